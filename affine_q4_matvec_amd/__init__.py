@@ -1,0 +1,285 @@
+"""Affine 4-bit matvec (q4mv) for AMD Instinct MI355X: Python binding.
+
+A thin ctypes layer over ``libq4mv.so`` (the C ABI in ``include/q4mv.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks and marshals torch tensors (device memory) and streams.  There
+is no CPU path: if the library is missing, importing this package fails.
+
+Names follow the C ABI: ``q4mv``, ``q4mv_add``, ``rmsq``, ``swq``,
+``q4_argmax``, ``q4_embed``, the stage queue ``Queue`` (``q4mv_queue``,
+``q4_stage``, ``q4mv_wait``) and graph capture ``Graph``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "FIXED", "FAST", "Q4Error", "Q4Matrix", "q4mv", "q4mv_add", "rmsq", "swq",
+    "q4_argmax", "q4_argmax_ws_bytes", "q4_embed", "Queue", "Graph", "q4_sync",
+    "library_path",
+]
+
+FIXED = 0
+FAST = 1
+Q4_OK, Q4_EINVAL, Q4_EHIP, Q4_ETIMEOUT, Q4_ESTATE, Q4_ENOMEM = 0, -1, -2, -3, -4, -5
+MAX_COLS = 32768
+MAX_RMSQ_N = 8192
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libq4mv.so")
+
+if not os.path.exists(library_path):
+    raise ImportError(
+        "libq4mv.so is not built (expected at %s); build it with "
+        "`python -c 'import __graft_entry__ as g; g.build()'`" % library_path)
+
+
+class _Mat(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("s", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_lib = ctypes.CDLL(library_path)
+_SIGS = {
+    "q4mv": ([ctypes.POINTER(_Mat), _vp, _vp, _vp, ctypes.c_int, _vp], ctypes.c_int),
+    "q4mv_add": ([ctypes.POINTER(_Mat), _vp, _vp, _vp, _vp, ctypes.c_int, _vp], ctypes.c_int),
+    "rmsq": ([_vp, _vp, _i32, ctypes.c_float, _vp, _vp, _vp], ctypes.c_int),
+    "swq": ([_vp, _i32, _vp, _vp, ctypes.c_int, _vp], ctypes.c_int),
+    "q4_argmax_ws_bytes": ([_i32], ctypes.c_size_t),
+    "q4_argmax": ([_vp, _i32, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+    "q4_embed": ([ctypes.POINTER(_Mat), _vp, _vp, _vp], ctypes.c_int),
+    "q4_queue_create": ([_vp, ctypes.c_int, ctypes.POINTER(_vp)], ctypes.c_int),
+    "q4_queue_destroy": ([_vp], ctypes.c_int),
+    "q4mv_queue": ([_vp, ctypes.POINTER(_Mat), _vp, _vp, _vp], ctypes.c_int),
+    "q4_stage": ([_vp], ctypes.c_int),
+    "q4mv_wait": ([_vp], ctypes.c_int),
+    "q4_capture_begin": ([_vp], ctypes.c_int),
+    "q4_capture_end": ([_vp, ctypes.POINTER(_vp)], ctypes.c_int),
+    "q4_graph_launch": ([_vp, _vp], ctypes.c_int),
+    "q4_graph_destroy": ([_vp], ctypes.c_int),
+    "q4_sync": ([_vp], ctypes.c_int),
+    "q4_strerror": ([ctypes.c_int], ctypes.c_char_p),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, call: str, code: int):
+        super().__init__("%s: %s (%d)" % (call, _lib.q4_strerror(code).decode(), code))
+        self.code = code
+
+
+def _check(call: str, code: int) -> None:
+    if code != Q4_OK:
+        raise Q4Error(call, code)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, numel: int | None, what: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % what)
+    if t.dtype != dtype or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor" % (what, dtype))
+    if numel is not None and t.numel() != numel:
+        raise ValueError("%s must hold %d values, not %d" % (what, numel, t.numel()))
+    return t.data_ptr()
+
+
+class Q4Matrix:
+    """An affine Q4 matrix on the GPU: ``q`` int32 view of packed codes
+    ``[rows, cols/8]`` (column 8j+k in bits 4k..4k+3 of word j), ``s`` and
+    ``b`` float32 ``[rows, cols/64]``."""
+
+    def __init__(self, q: torch.Tensor, s: torch.Tensor, b: torch.Tensor, rows: int, cols: int):
+        if cols % 64 or cols < 64 or rows < 1:
+            raise ValueError("rows >= 1 and cols a positive multiple of 64 required")
+        G = cols // 64
+        if q.dtype not in (torch.int32, torch.uint32):
+            raise ValueError("q must be a 32-bit integer tensor")
+        _dev(q.view(torch.int32), torch.int32, rows * cols // 8, "q")
+        _dev(s, torch.float32, rows * G, "s")
+        _dev(b, torch.float32, rows * G, "b")
+        self.q, self.s, self.b, self.rows, self.cols = q, s, b, rows, cols
+        self._c = _Mat(q.data_ptr(), s.data_ptr(), b.data_ptr(), rows, cols)
+
+    @classmethod
+    def from_host(cls, m: dict, device="cuda") -> "Q4Matrix":
+        """From numpy arrays ``{"q": uint32[rows, cols/8], "s", "b",
+        "rows", "cols"}`` (the layout above)."""
+        import numpy as np
+        q = torch.from_numpy(np.ascontiguousarray(m["q"]).view(np.int32)).to(device)
+        s = torch.from_numpy(np.ascontiguousarray(m["s"], dtype=np.float32)).to(device)
+        b = torch.from_numpy(np.ascontiguousarray(m["b"], dtype=np.float32)).to(device)
+        return cls(q, s, b, int(m["rows"]), int(m["cols"]))
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._c)
+
+
+def q4mv(w: Q4Matrix, x: torch.Tensor, xsum: torch.Tensor, y: torch.Tensor | None = None,
+         mode: int = FIXED, stream=None) -> torch.Tensor:
+    """``y = W x`` with the activation group sums ``xsum`` (see q4mv.h)."""
+    if y is None:
+        y = torch.empty(w.rows, dtype=torch.float32, device=x.device)
+    _check("q4mv", _lib.q4mv(w.ref, _dev(x, torch.float32, w.cols, "x"),
+                             _dev(xsum, torch.float32, w.cols // 64, "xsum"),
+                             _dev(y, torch.float32, w.rows, "y"), mode, _stream(stream)))
+    return y
+
+
+def q4mv_add(w: Q4Matrix, x: torch.Tensor, xsum: torch.Tensor, resid: torch.Tensor,
+             y: torch.Tensor | None = None, mode: int = FIXED, stream=None) -> torch.Tensor:
+    """``y = resid + W x`` (``y`` may be ``resid``)."""
+    if y is None:
+        y = torch.empty(w.rows, dtype=torch.float32, device=x.device)
+    _check("q4mv_add", _lib.q4mv_add(w.ref, _dev(x, torch.float32, w.cols, "x"),
+                                     _dev(xsum, torch.float32, w.cols // 64, "xsum"),
+                                     _dev(resid, torch.float32, w.rows, "resid"),
+                                     _dev(y, torch.float32, w.rows, "y"), mode, _stream(stream)))
+    return y
+
+
+def rmsq(h: torch.Tensor, w: torch.Tensor, eps: float, u: torch.Tensor | None = None,
+         usum: torch.Tensor | None = None, stream=None):
+    """RMS norm with weights plus group sums; returns ``(u, usum)``."""
+    n = h.numel()
+    if u is None:
+        u = torch.empty(n, dtype=torch.float32, device=h.device)
+    if usum is None:
+        usum = torch.empty(max(n // 64, 1), dtype=torch.float32, device=h.device)
+    _check("rmsq", _lib.rmsq(_dev(h, torch.float32, n, "h"), _dev(w, torch.float32, n, "w"), n,
+                             float(eps), _dev(u, torch.float32, n, "u"),
+                             _dev(usum, torch.float32, None, "usum"), _stream(stream)))
+    return u, usum
+
+
+def swq(a: torch.Tensor, n: int, o: torch.Tensor | None = None, osum: torch.Tensor | None = None,
+        mode: int = FIXED, stream=None):
+    """SwiGLU of ``a = [gate | up]`` plus group sums; returns ``(o, osum)``."""
+    if o is None:
+        o = torch.empty(n, dtype=torch.float32, device=a.device)
+    if osum is None:
+        osum = torch.empty(max(n // 64, 1), dtype=torch.float32, device=a.device)
+    _check("swq", _lib.swq(_dev(a, torch.float32, 2 * n, "a"), n, _dev(o, torch.float32, n, "o"),
+                           _dev(osum, torch.float32, None, "osum"), mode, _stream(stream)))
+    return o, osum
+
+
+def q4_argmax_ws_bytes(n: int) -> int:
+    return int(_lib.q4_argmax_ws_bytes(n))
+
+
+def q4_argmax(v: torch.Tensor, idx: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """Lowest index of the largest value (-1 on NaN), written on the device
+    into ``idx`` (int32[1])."""
+    n = v.numel()
+    if idx is None:
+        idx = torch.empty(1, dtype=torch.int32, device=v.device)
+    if ws is None:
+        ws = torch.empty((q4_argmax_ws_bytes(n) + 7) // 8, dtype=torch.int64, device=v.device)
+    _check("q4_argmax", _lib.q4_argmax(_dev(v, torch.float32, n, "v"), n,
+                                       _dev(idx, torch.int32, 1, "idx"),
+                                       _dev(ws, ws.dtype, None, "ws"), ws.numel() * ws.element_size(),
+                                       _stream(stream)))
+    return idx
+
+
+def q4_embed(w: Q4Matrix, tok: torch.Tensor, e: torch.Tensor | None = None,
+             stream=None) -> torch.Tensor:
+    """Dequantised row ``tok`` (device int32[1]) of ``w``."""
+    if e is None:
+        e = torch.empty(w.cols, dtype=torch.float32, device=tok.device)
+    _check("q4_embed", _lib.q4_embed(w.ref, _dev(tok, torch.int32, 1, "tok"),
+                                     _dev(e, torch.float32, w.cols, "e"), _stream(stream)))
+    return e
+
+
+def q4_sync(stream=None) -> None:
+    _check("q4_sync", _lib.q4_sync(_stream(stream)))
+
+
+class Queue:
+    """Stage queue over one stream: ``q4mv_queue`` adds a product to the open
+    stage, ``q4_stage`` closes it (grouped launches, no host wait),
+    ``q4mv_wait`` closes it and waits once.  The queue holds a reference to
+    every tensor it was given until ``q4mv_wait`` returns."""
+
+    def __init__(self, mode: int = FIXED, stream=None):
+        self._stream = _stream(stream)
+        self._h = ctypes.c_void_p()
+        _check("q4_queue_create", _lib.q4_queue_create(self._stream, mode, ctypes.byref(self._h)))
+        self._keep = []
+
+    def q4mv_queue(self, w: Q4Matrix, x: torch.Tensor, xsum: torch.Tensor, y: torch.Tensor) -> None:
+        _check("q4mv_queue", _lib.q4mv_queue(self._h, w.ref, _dev(x, torch.float32, w.cols, "x"),
+                                             _dev(xsum, torch.float32, w.cols // 64, "xsum"),
+                                             _dev(y, torch.float32, w.rows, "y")))
+        self._keep.append((w, x, xsum, y))
+
+    def q4_stage(self) -> None:
+        _check("q4_stage", _lib.q4_stage(self._h))
+
+    def q4mv_wait(self) -> None:
+        _check("q4mv_wait", _lib.q4mv_wait(self._h))
+        self._keep.clear()
+
+    def close(self) -> None:
+        if self._h:
+            _check("q4_queue_destroy", _lib.q4_queue_destroy(self._h))
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Graph:
+    """Records every library call issued on ``stream`` between ``begin`` and
+    ``end`` and replays it with ``launch``.  Keep the tensors the recorded
+    calls use alive (and at the same addresses) for the graph's lifetime."""
+
+    def __init__(self, stream: torch.cuda.Stream):
+        if not isinstance(stream, torch.cuda.Stream):
+            raise ValueError("capture needs a torch.cuda.Stream (not the null stream)")
+        self.stream = stream
+        self._h = ctypes.c_void_p()
+        self.keep = []
+
+    def begin(self) -> None:
+        _check("q4_capture_begin", _lib.q4_capture_begin(self.stream.cuda_stream))
+
+    def end(self) -> None:
+        _check("q4_capture_end", _lib.q4_capture_end(self.stream.cuda_stream, ctypes.byref(self._h)))
+
+    def launch(self, stream=None) -> None:
+        _check("q4_graph_launch", _lib.q4_graph_launch(self._h, _stream(stream or self.stream)))
+
+    def close(self) -> None:
+        if self._h:
+            _check("q4_graph_destroy", _lib.q4_graph_destroy(self._h))
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

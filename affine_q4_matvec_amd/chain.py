@@ -1,0 +1,128 @@
+"""A greedy decode chain built only from the library's calls.
+
+One step from token t (the chain has no other state):
+  h = embed(head, t)                                   (tied embedding)
+  per layer l:  u, us = rmsq(h, wn_l)
+                a     = [gate_l; up_l] u               (one q4mv over both)
+                m, ms = swq(a, inter)
+                h     = h + down_l m                   (q4mv_add, in place)
+  u, us = rmsq(h, wn_final);  logits = head u;  t' = argmax(logits)
+
+The token lives on the device: argmax writes it where the next step's embed
+reads it, so a step captured once as a graph can be replayed token after
+token with a single host wait (for reading the token) per step.
+
+This is the structure "Metal: queued rmsq, swq, gdn and atq kernels and a
+4-row q4mv, so a decode token is one command buffer with one wait" (#1440)
+describes for a whole decode token (Verification: one command buffer, one
+wait), restricted to the products, norms and SwiGLU the chain uses.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (FIXED, Graph, Q4Matrix, q4_argmax, q4_argmax_ws_bytes, q4_embed, q4mv,
+               q4mv_add, rmsq, swq)
+
+
+def _stack_rows(a: dict, b: dict) -> dict:
+    """[a; b] as one matrix: rows of a, then rows of b (same cols)."""
+    assert a["cols"] == b["cols"]
+    return {"q": np.concatenate([a["q"], b["q"]]), "s": np.concatenate([a["s"], b["s"]]),
+            "b": np.concatenate([a["b"], b["b"]]), "rows": a["rows"] + b["rows"],
+            "cols": a["cols"]}
+
+
+class DecodeChain:
+    def __init__(self, weights: dict, mode: int = FIXED, layers: int | None = None,
+                 device: str = "cuda"):
+        self.mode = mode
+        self.hidden = int(weights["hidden"])
+        self.inter = int(weights["inter"])
+        self.vocab = int(weights["vocab"])
+        self.eps = float(weights["eps"])
+        L = len(weights["layers"]) if layers is None else layers
+        f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+        self.layers = []
+        for lw in weights["layers"][:L]:
+            self.layers.append({
+                "wn": f32(lw["wn"]),
+                "gu": Q4Matrix.from_host(_stack_rows(lw["gate"], lw["up"]), device),
+                "down": Q4Matrix.from_host(lw["down"], device),
+            })
+        self.wn_final = f32(weights["wn_final"])
+        self.head = Q4Matrix.from_host(weights["head"], device)
+        z = lambda n, dt=torch.float32: torch.zeros(n, dtype=dt, device=device)
+        self.tok = z(1, torch.int32)
+        self.h = z(self.hidden)
+        self.u = z(self.hidden)
+        self.us = z(self.hidden // 64)
+        self.a = z(2 * self.inter)
+        self.m = z(self.inter)
+        self.ms = z(self.inter // 64)
+        self.logits = z(self.vocab)
+        self.ws = z((q4_argmax_ws_bytes(self.vocab) + 7) // 8, torch.int64)
+        self.graph = None
+
+    def bytes_per_token(self) -> int:
+        """Algorithmic bytes one step moves: weights and scales of every
+        product (codes cols/2, s and b 8 per group per row), plus the small
+        vectors each kernel reads and writes."""
+        def prod(w):
+            return w.rows * (w.cols // 2 + 8 * (w.cols // 64)) + 4 * (w.cols + w.cols // 64 + w.rows)
+        total = prod(self.head) + self.hidden * 2 + 4 * self.vocab  # embed row, argmax read
+        for lw in self.layers:
+            total += prod(lw["gu"]) + prod(lw["down"]) + 4 * self.hidden  # residual read
+            total += 4 * (3 * self.hidden + self.hidden // 64)             # rmsq
+            total += 4 * (3 * self.inter + self.inter // 64)               # swq
+        return total + 4 * (3 * self.hidden + self.hidden // 64)
+
+    def enqueue_step(self, stream) -> None:
+        """Every kernel of one step, in order, on `stream`."""
+        q4_embed(self.head, self.tok, self.h, stream=stream)
+        for lw in self.layers:
+            rmsq(self.h, lw["wn"], self.eps, self.u, self.us, stream=stream)
+            q4mv(lw["gu"], self.u, self.us, self.a, mode=self.mode, stream=stream)
+            swq(self.a, self.inter, self.m, self.ms, mode=self.mode, stream=stream)
+            q4mv_add(lw["down"], self.m, self.ms, self.h, self.h, mode=self.mode, stream=stream)
+        rmsq(self.h, self.wn_final, self.eps, self.u, self.us, stream=stream)
+        q4mv(self.head, self.u, self.us, self.logits, mode=self.mode, stream=stream)
+        q4_argmax(self.logits, self.tok, self.ws, stream=stream)
+
+    def capture(self, stream: torch.cuda.Stream) -> Graph:
+        g = Graph(stream)
+        g.begin()
+        try:
+            self.enqueue_step(stream)
+        finally:
+            g.end()
+        self.graph = g
+        return g
+
+    def set_token(self, t: int) -> None:
+        self.tok.fill_(int(t))
+
+    def run(self, tok0: int, steps: int, stream: torch.cuda.Stream, use_graph: bool = True,
+            on_step=None) -> list:
+        """Decodes `steps` tokens from `tok0`; returns them (host ints).
+        One host wait per token (to read it).  `on_step(i, chain)` runs
+        after token i is known, e.g. to read the logits."""
+        if use_graph and self.graph is None:
+            self.capture(stream)
+        with torch.cuda.stream(stream):
+            self.set_token(tok0)
+        out = []
+        pinned = torch.empty(1, dtype=torch.int32, pin_memory=True)
+        for i in range(steps):
+            if use_graph:
+                self.graph.launch(stream)
+            else:
+                self.enqueue_step(stream)
+            with torch.cuda.stream(stream):
+                pinned.copy_(self.tok, non_blocking=True)
+            stream.synchronize()
+            out.append(int(pinned[0]))
+            if on_step is not None:
+                on_step(i, self)
+        return out

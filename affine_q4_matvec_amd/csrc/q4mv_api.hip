@@ -1,0 +1,342 @@
+// C ABI of libq4mv.so (declared in include/q4mv.h): argument checks, the
+// stage queue, graph capture and status codes.  Every check runs before any
+// HIP call, so a rejected call touches neither the device nor the runtime.
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <chrono>
+#include <new>
+#include <vector>
+
+// Only the C ABI is exported; everything else is hidden (-fvisibility=hidden).
+#pragma GCC visibility push(default)
+#include "../../include/q4mv.h"
+#pragma GCC visibility pop
+#include "q4mv_internal.h"
+
+namespace {
+
+using q4::Prod;
+using q4::ProdGroup;
+using q4::Shape;
+
+constexpr int32_t kMaxRows = 1 << 30;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// [a, a+na) and [b, b+nb) (bytes) overlap?
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+bool env_flag(const char *name) {
+  const char *v = getenv(name);
+  return v && *v && strcmp(v, "0") != 0;
+}
+
+int check_mat(const q4_mat *w) {
+  if (!w || !w->q || !w->s || !w->b) return Q4_EINVAL;
+  if (w->rows < 1 || w->rows > kMaxRows) return Q4_EINVAL;
+  if (w->cols < 64 || w->cols % 64 != 0 || w->cols > Q4_MAX_COLS) return Q4_EINVAL;
+  if (!aligned(w->q, 16) || !aligned(w->s, 4) || !aligned(w->b, 4)) return Q4_EINVAL;
+  return Q4_OK;
+}
+
+// Checks one product and fills the kernel's view of it.
+int make_prod(const q4_mat *w, const float *x, const float *xsum, const float *resid, float *y,
+              Prod *out) {
+  int rc = check_mat(w);
+  if (rc != Q4_OK) return rc;
+  if (!x || !xsum || !y) return Q4_EINVAL;
+  if (!aligned(x, 16) || !aligned(xsum, 4) || !aligned(y, 4)) return Q4_EINVAL;
+  if (resid && !aligned(resid, 4)) return Q4_EINVAL;
+  const size_t G = (size_t)w->cols / 64;
+  const size_t ybytes = sizeof(float) * (size_t)w->rows;
+  if (overlap(y, ybytes, x, sizeof(float) * (size_t)w->cols) ||
+      overlap(y, ybytes, xsum, sizeof(float) * G) ||
+      overlap(y, ybytes, w->q, (size_t)w->rows * (size_t)w->cols / 2) ||
+      overlap(y, ybytes, w->s, sizeof(float) * G * (size_t)w->rows) ||
+      overlap(y, ybytes, w->b, sizeof(float) * G * (size_t)w->rows))
+    return Q4_EINVAL;
+  if (resid && resid != y && overlap(y, ybytes, resid, ybytes)) return Q4_EINVAL;
+  *out = Prod{w->q, w->s, w->b, x, xsum, resid, y, w->rows, w->cols};
+  return Q4_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_EHIP; }
+
+// Launches a list of products of one shape as grouped kernels (up to
+// kMaxGroup products per launch).
+int launch_products(const Prod *prods, int count, const Shape &sh, int mode, hipStream_t st) {
+  for (int at = 0; at < count; at += q4::kMaxGroup) {
+    ProdGroup g;
+    memset(&g, 0, sizeof(g));
+    g.n = count - at < q4::kMaxGroup ? count - at : q4::kMaxGroup;
+    g.wg_begin[0] = 0;
+    for (int i = 0; i < g.n; ++i) {
+      g.p[i] = prods[at + i];
+      g.wg_begin[i + 1] = g.wg_begin[i] + q4::workgroups_for(sh, prods[at + i].rows);
+    }
+    for (int i = g.n; i < q4::kMaxGroup; ++i) g.wg_begin[i + 1] = g.wg_begin[g.n];
+    const int rc = hip_status(q4::launch_q4mv_group(g, sh, mode, st));
+    if (rc != Q4_OK) return rc;
+  }
+  return Q4_OK;
+}
+
+}  // namespace
+
+struct q4_queue {
+  hipStream_t st = nullptr;
+  int mode = Q4_FIXED;
+  std::vector<Prod> stage;  // products of the open stage
+  bool debug = false;
+  bool trace = false;
+  // trace state: events around the work since the last wait
+  hipEvent_t ev_begin = nullptr, ev_end = nullptr;
+  bool began = false;
+  int products_since_wait = 0;
+  std::chrono::steady_clock::time_point wall_begin;
+};
+
+struct q4_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+namespace {
+
+// Launches the open stage: products grouped by kernel shape.
+int flush_stage(q4_queue *q) {
+  if (q->stage.empty()) return Q4_OK;
+  if (q->trace && !q->began) {
+    if (hipEventRecord(q->ev_begin, q->st) != hipSuccess) return Q4_EHIP;
+    q->began = true;
+    q->wall_begin = std::chrono::steady_clock::now();
+  }
+  std::vector<bool> done(q->stage.size(), false);
+  std::vector<Prod> same;
+  for (size_t i = 0; i < q->stage.size(); ++i) {
+    if (done[i]) continue;
+    const Shape sh = q4::shape_of(q->stage[i].cols);
+    same.clear();
+    for (size_t j = i; j < q->stage.size(); ++j) {
+      if (!done[j] && q4::shape_of(q->stage[j].cols) == sh) {
+        same.push_back(q->stage[j]);
+        done[j] = true;
+      }
+    }
+    const int rc = launch_products(same.data(), (int)same.size(), sh, q->mode, q->st);
+    if (rc != Q4_OK) return rc;
+  }
+  q->products_since_wait += (int)q->stage.size();
+  q->stage.clear();
+  return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4mv(const q4_mat *w, const float *x, const float *xsum, float *y, int mode, void *stream) {
+  return q4mv_add(w, x, xsum, nullptr, y, mode, stream);
+}
+
+int q4mv_add(const q4_mat *w, const float *x, const float *xsum, const float *resid, float *y,
+             int mode, void *stream) {
+  if (mode != Q4_FIXED && mode != Q4_FAST) return Q4_EINVAL;
+  Prod p;
+  const int rc = make_prod(w, x, xsum, resid, y, &p);
+  if (rc != Q4_OK) return rc;
+  return launch_products(&p, 1, q4::shape_of(p.cols), mode, static_cast<hipStream_t>(stream));
+}
+
+int rmsq(const float *h, const float *w, int32_t n, float eps, float *u, float *usum,
+         void *stream) {
+  if (!h || !w || !u || !usum) return Q4_EINVAL;
+  if (n < 64 || n % 64 != 0 || n > Q4_MAX_RMSQ_N) return Q4_EINVAL;
+  if (!aligned(h, 4) || !aligned(w, 4) || !aligned(u, 4) || !aligned(usum, 4)) return Q4_EINVAL;
+  const size_t nb = sizeof(float) * (size_t)n, gb = sizeof(float) * (size_t)(n / 64);
+  if (overlap(u, nb, h, nb) || overlap(u, nb, w, nb) || overlap(usum, gb, h, nb) ||
+      overlap(usum, gb, w, nb) || overlap(usum, gb, u, nb))
+    return Q4_EINVAL;
+  return hip_status(q4::launch_rmsq(h, w, n, eps, u, usum, static_cast<hipStream_t>(stream)));
+}
+
+int swq(const float *a, int32_t n, float *o, float *osum, int mode, void *stream) {
+  if (mode != Q4_FIXED && mode != Q4_FAST) return Q4_EINVAL;
+  if (!a || !o || !osum) return Q4_EINVAL;
+  if (n < 64 || n % 64 != 0 || n > (1 << 28)) return Q4_EINVAL;
+  if (!aligned(a, 4) || !aligned(o, 4) || !aligned(osum, 4)) return Q4_EINVAL;
+  const size_t ab = sizeof(float) * 2 * (size_t)n, nb = sizeof(float) * (size_t)n,
+               gb = sizeof(float) * (size_t)(n / 64);
+  if (overlap(o, nb, a, ab) || overlap(osum, gb, a, ab) || overlap(osum, gb, o, nb))
+    return Q4_EINVAL;
+  return hip_status(q4::launch_swq(a, n, o, osum, mode, static_cast<hipStream_t>(stream)));
+}
+
+size_t q4_argmax_ws_bytes(int32_t n) { return n < 1 ? 0 : q4::argmax_ws_bytes(n); }
+
+int q4_argmax(const float *v, int32_t n, int32_t *idx, void *ws, size_t ws_bytes, void *stream) {
+  if (!v || !idx || !ws || n < 1) return Q4_EINVAL;
+  if (!aligned(v, 4) || !aligned(idx, 4) || !aligned(ws, 8)) return Q4_EINVAL;
+  if (ws_bytes < q4::argmax_ws_bytes(n)) return Q4_EINVAL;
+  const size_t vb = sizeof(float) * (size_t)n;
+  if (overlap(idx, 4, v, vb) || overlap(ws, ws_bytes, v, vb) || overlap(ws, ws_bytes, idx, 4))
+    return Q4_EINVAL;
+  return hip_status(q4::launch_argmax(v, n, idx, ws, static_cast<hipStream_t>(stream)));
+}
+
+int q4_embed(const q4_mat *w, const int32_t *tok, float *e, void *stream) {
+  int rc = check_mat(w);
+  if (rc != Q4_OK) return rc;
+  if (!tok || !e || !aligned(tok, 4) || !aligned(e, 4)) return Q4_EINVAL;
+  if (overlap(e, sizeof(float) * (size_t)w->cols, tok, 4)) return Q4_EINVAL;
+  Prod p{w->q, w->s, w->b, nullptr, nullptr, nullptr, e, w->rows, w->cols};
+  return hip_status(q4::launch_embed(p, tok, e, static_cast<hipStream_t>(stream)));
+}
+
+int q4_queue_create(void *stream, int mode, q4_queue **out) {
+  if (!out || (mode != Q4_FIXED && mode != Q4_FAST)) return Q4_EINVAL;
+  *out = nullptr;
+  q4_queue *q = new (std::nothrow) q4_queue();
+  if (!q) return Q4_ENOMEM;
+  q->st = static_cast<hipStream_t>(stream);
+  q->mode = mode;
+  q->debug = env_flag("Q4MV_DEBUG_CHECKS");
+  q->trace = env_flag("Q4MV_TRACE");
+  if (q->trace) {
+    if (hipEventCreate(&q->ev_begin) != hipSuccess || hipEventCreate(&q->ev_end) != hipSuccess) {
+      if (q->ev_begin) (void)hipEventDestroy(q->ev_begin);
+      delete q;
+      return Q4_EHIP;
+    }
+  }
+  *out = q;
+  return Q4_OK;
+}
+
+int q4_queue_destroy(q4_queue *q) {
+  if (!q) return Q4_EINVAL;
+  int rc = Q4_OK;
+  if (q->ev_begin && hipEventDestroy(q->ev_begin) != hipSuccess) rc = Q4_EHIP;
+  if (q->ev_end && hipEventDestroy(q->ev_end) != hipSuccess) rc = Q4_EHIP;
+  delete q;
+  return rc;
+}
+
+int q4mv_queue(q4_queue *q, const q4_mat *w, const float *x, const float *xsum, float *y) {
+  if (!q) return Q4_EINVAL;
+  Prod p;
+  const int rc = make_prod(w, x, xsum, nullptr, y, &p);
+  if (rc != Q4_OK) return rc;
+  if (q->debug) {
+    // products of one stage may run concurrently: none may read another's y
+    const size_t yb = sizeof(float) * (size_t)p.rows;
+    for (const Prod &o : q->stage) {
+      const size_t ob = sizeof(float) * (size_t)o.rows;
+      if (overlap(p.y, yb, o.x, sizeof(float) * (size_t)o.cols) ||
+          overlap(p.y, yb, o.xs, sizeof(float) * (size_t)(o.cols / 64)) ||
+          overlap(o.y, ob, p.x, sizeof(float) * (size_t)p.cols) ||
+          overlap(o.y, ob, p.xs, sizeof(float) * (size_t)(p.cols / 64)) ||
+          overlap(o.y, ob, p.y, yb))
+        return Q4_EINVAL;
+    }
+  }
+  try {
+    q->stage.push_back(p);
+  } catch (...) {
+    return Q4_ENOMEM;
+  }
+  return Q4_OK;
+}
+
+int q4_stage(q4_queue *q) {
+  if (!q) return Q4_EINVAL;
+  return flush_stage(q);
+}
+
+int q4mv_wait(q4_queue *q) {
+  if (!q) return Q4_EINVAL;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(q->st, &cs) != hipSuccess) return Q4_EHIP;
+  if (cs != hipStreamCaptureStatusNone) return Q4_ESTATE;
+  int rc = flush_stage(q);
+  if (rc != Q4_OK) return rc;
+  if (q->trace && q->began) {
+    if (hipEventRecord(q->ev_end, q->st) != hipSuccess) return Q4_EHIP;
+  }
+  if (hipStreamSynchronize(q->st) != hipSuccess) return Q4_EHIP;
+  if (q->trace && q->began) {
+    float gpu_ms = 0.0f;
+    if (hipEventElapsedTime(&gpu_ms, q->ev_begin, q->ev_end) != hipSuccess) return Q4_EHIP;
+    const double wall_ms =
+        std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - q->wall_begin)
+            .count();
+    fprintf(stderr, "q4mv_wait: %d products, gpu %.3f ms, wall %.3f ms\n",
+            q->products_since_wait, gpu_ms, wall_ms);
+  }
+  q->began = false;
+  q->products_since_wait = 0;
+  return Q4_OK;
+}
+
+int q4_capture_begin(void *stream) {
+  if (!stream) return Q4_EINVAL;  // the null stream cannot be captured
+  return hip_status(
+      hipStreamBeginCapture(static_cast<hipStream_t>(stream), hipStreamCaptureModeRelaxed));
+}
+
+int q4_capture_end(void *stream, q4_graph **out) {
+  if (!stream || !out) return Q4_EINVAL;
+  *out = nullptr;
+  q4_graph *g = new (std::nothrow) q4_graph();
+  if (!g) return Q4_ENOMEM;
+  if (hipStreamEndCapture(static_cast<hipStream_t>(stream), &g->graph) != hipSuccess ||
+      !g->graph) {
+    delete g;
+    return Q4_EHIP;
+  }
+  if (hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(g->graph);
+    delete g;
+    return Q4_EHIP;
+  }
+  *out = g;
+  return Q4_OK;
+}
+
+int q4_graph_launch(q4_graph *g, void *stream) {
+  if (!g || !g->exec) return Q4_EINVAL;
+  return hip_status(hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)));
+}
+
+int q4_graph_destroy(q4_graph *g) {
+  if (!g) return Q4_EINVAL;
+  int rc = Q4_OK;
+  if (g->exec && hipGraphExecDestroy(g->exec) != hipSuccess) rc = Q4_EHIP;
+  if (g->graph && hipGraphDestroy(g->graph) != hipSuccess) rc = Q4_EHIP;
+  delete g;
+  return rc;
+}
+
+int q4_sync(void *stream) {
+  return hip_status(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+}
+
+const char *q4_strerror(int code) {
+  switch (code) {
+    case Q4_OK: return "ok";
+    case Q4_EINVAL: return "invalid argument (nothing was launched)";
+    case Q4_EHIP: return "HIP runtime error";
+    case Q4_ETIMEOUT: return "host wait timed out";
+    case Q4_ESTATE: return "call not legal in the current state (e.g. host wait during capture)";
+    case Q4_ENOMEM: return "host allocation failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal interface between the C ABI layer (q4mv_api.hip) and the kernels
+// (q4mv_kernels.hip).  Not installed; the public interface is include/q4mv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+// One product as the kernels see it.  All pointers are device pointers.
+struct Prod {
+  const uint32_t *q;  // [rows][cols/8] packed codes
+  const float *s;     // [rows][G] scales
+  const float *b;     // [rows][G] biases
+  const float *x;     // [cols] activations
+  const float *xs;    // [G] group sums of x
+  const float *res;   // [rows] residual added to the result, or nullptr
+  float *y;           // [rows] output
+  int32_t rows;
+  int32_t cols;
+};
+
+// Up to kMaxGroup products of one kernel shape, launched as one grid: the
+// workgroups [wg_begin[i], wg_begin[i+1]) work on product i.
+constexpr int kMaxGroup = 8;
+struct ProdGroup {
+  Prod p[kMaxGroup];
+  int32_t wg_begin[kMaxGroup + 1];
+  int32_t n;
+};
+
+// Kernel shape of a product: rows of at most 32 groups are covered by one
+// segment of `lpr` lanes of a wave (lpr = 2..64); wider rows are split into
+// `passes` 2048-column passes, one wave each, combined through LDS.
+struct Shape {
+  int32_t lpr;     // lanes per row segment (0 when split)
+  int32_t passes;  // waves per row for split rows (0 when segmented)
+  bool operator==(const Shape &o) const { return lpr == o.lpr && passes == o.passes; }
+};
+
+Shape shape_of(int32_t cols);
+// Workgroups a product of this shape gets in a launch.
+int32_t workgroups_for(const Shape &sh, int32_t rows);
+
+// Launchers.  They assume validated arguments and return the HIP status of
+// the launch.
+hipError_t launch_q4mv_group(const ProdGroup &g, const Shape &sh, int mode, hipStream_t st);
+hipError_t launch_rmsq(const float *h, const float *w, int32_t n, float eps, float *u,
+                       float *us, hipStream_t st);
+hipError_t launch_swq(const float *a, int32_t n, float *o, float *os, int mode,
+                      hipStream_t st);
+size_t argmax_ws_bytes(int32_t n);
+hipError_t launch_argmax(const float *v, int32_t n, int32_t *idx, void *ws, hipStream_t st);
+hipError_t launch_embed(const Prod &w, const int32_t *tok, float *e, hipStream_t st);
+
+}  // namespace q4

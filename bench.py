@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of the affine 4-bit matvec hot path on one MI355X.
+
+Headline: the 248320 x 2048 output head.  One step = rmsq of z (2048, eps
+1e-6) into x and its group sums, then q4mv of the head with them (fixed
+order).  Two weight copies alternate so that the 256 MB Infinity Cache
+cannot serve the 318.9 MB of weights of a step from the previous one.
+Inputs are resident in HBM before timing starts.
+
+value = algorithmic bytes of a step / time per step (GB/s, 1e9 B/s).
+roofline = the q4mv kernel alone: its algorithmic bytes / its average
+duration measured with HIP events around each launch, on the launch stream.
+
+Also reported: the 24-layer decode chain (rmsq -> [gate;up] q4mv -> swq ->
+down q4mv + residual, then rmsq -> head q4mv -> argmax), captured once as a
+HIP graph, in ms per token over 200 tokens; and the CPU oracle timed on the
+host's cores on the head workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "q4mv achieved HBM GB/s (% of peak) on 248320x2048 head; ms per decode chain"
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+ROWS, COLS = 248320, 2048
+
+
+def head_bytes(rows: int, cols: int) -> int:
+    """Algorithmic bytes of one q4mv: per row cols/2 of codes, 4 B of scale
+    and 4 B of bias per 64-column group, 4 B of output; once per product the
+    activations (4 cols B) and their group sums (4 cols/64 B)."""
+    G = cols // 64
+    return rows * (cols // 2 + 8 * G + 4) + 4 * cols + 4 * G
+
+
+def rmsq_bytes(n: int) -> int:
+    return 4 * (3 * n + n // 64)  # h, w in; u, group sums out
+
+
+def log(msg: str) -> None:
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    src = os.path.join(ROOT, "affine_q4_matvec_amd", "csrc", "q4mv_kernels.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(per_launch_alg_bytes: int):
+    """HBM bytes per q4mv head launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "q4mv_head_hbm_counters.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(seed: int):
+    """The CPU oracle on the head workload, all host cores (at most 16)."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(16, cores))
+    h = synth.head_inputs(seed=seed)
+    u, us = oracle.rmsq(h["z"], h["wn"], h["eps"])
+    best = None
+    t_end = time.perf_counter() + 20.0
+    reps = 0
+    while reps < 3 and (reps == 0 or time.perf_counter() < t_end):
+        t0 = time.perf_counter()
+        oracle.q4mv(h, u, us, nthreads=cores)
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+        reps += 1
+    del np
+    return {"value": round(head_bytes(ROWS, COLS) / best / 1e9, 3), "unit": "GB/s",
+            "cores": cores, "kind": "oracle",
+            "sample": "full 248320x2048 head q4mv (fixed order), rows split over %d threads, "
+                      "best of %d runs, %.2f s each" % (cores, reps, best)}
+
+
+def run_head(args, q4, torch, synth):
+    import numpy as np
+
+    log("generating head inputs (248320 x 2048, seed %d)" % args.seed)
+    h = synth.head_inputs(seed=args.seed)
+    W0 = q4.Q4Matrix.from_host(h)
+    # second copy at other addresses: same bytes, so every step's output is
+    # the same, but the cache cannot hold both copies
+    W1 = q4.Q4Matrix(W0.q.clone(), W0.s.clone(), W0.b.clone(), ROWS, COLS)
+    mats = [W0, W1]
+    z = torch.from_numpy(h["z"]).cuda()
+    wn = torch.from_numpy(h["wn"]).cuda()
+    eps = float(h["eps"])
+    x = torch.empty(COLS, device="cuda")
+    xs = torch.empty(COLS // 64, device="cuda")
+    y = torch.empty(ROWS, device="cuda")
+    mode = q4.FAST if args.mode == "fast" else q4.FIXED
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        q4.rmsq(z, wn, eps, x, xs, stream=stream)
+        q4.q4mv(mats[i % 2], x, xs, y, mode=mode, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    y_first = y.cpu().numpy().copy()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        q4.rmsq(z, wn, eps, x, xs, stream=stream)
+        starts[i].record(stream)
+        q4.q4mv(mats[i % 2], x, xs, y, mode=mode, stream=stream)
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    same = bool(np.array_equal(y.cpu().numpy().view(np.uint32), y_first.view(np.uint32)))
+    return total_ms / args.steps, sum(kern_ms) / len(kern_ms), sorted(kern_ms)[len(kern_ms) // 2], same
+
+
+def run_chain(args, q4, torch, synth):
+    import numpy as np
+
+    from affine_q4_matvec_amd.chain import DecodeChain
+
+    log("generating decode-chain weights (24 layers, seed %d)" % args.seed)
+    w = synth.chain_weights(seed=args.seed)
+    mode = q4.FAST if args.mode == "fast" else q4.FIXED
+    chain = DecodeChain(w, mode=mode)
+    del w
+    stream = torch.cuda.Stream()
+    chain.capture(stream)
+    # warm-up tokens (not timed)
+    chain.run(0, 3, stream)
+    torch.cuda.synchronize()
+    # (a) one host wait per token: replay, read the token, repeat
+    tok0 = chain_tok0(args.seed, synth)
+    t0 = time.perf_counter()
+    tokens = chain.run(tok0, args.chain_tokens, stream)
+    per_token_sync_ms = (time.perf_counter() - t0) * 1e3 / args.chain_tokens
+    # (b) device time of the same replays queued back to back (the token
+    # stays on the device, so the chain is the same)
+    chain.set_token(tok0)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.chain_tokens):
+        chain.graph.launch(stream)
+    e1.record(stream)
+    stream.synchronize()
+    gpu_ms = e0.elapsed_time(e1) / args.chain_tokens
+    last = int(chain.tok.cpu().numpy()[0])
+    golden = os.path.join(ROOT, "tests", "golden", "chain_seed%d.json" % args.seed)
+    match = None
+    if os.path.exists(golden):
+        ref = json.load(open(golden))
+        n = min(len(ref["tokens"]), len(tokens))
+        match = bool(ref["tokens"][:n] == tokens[:n])
+    bpt = chain.bytes_per_token()
+    del np
+    return {
+        "tokens": args.chain_tokens, "layers": len(chain.layers),
+        "ms_per_token_with_host_wait": round(per_token_sync_ms, 4),
+        "ms_per_token_gpu": round(gpu_ms, 4),
+        "algorithmic_bytes_per_token": bpt,
+        "gpu_GBps": round(bpt / (gpu_ms * 1e-3) / 1e9, 1),
+        "kernels_per_token": 1 + 4 * len(chain.layers) + 4,
+        "tokens_match_oracle_golden": match,
+        "queued_replays_reach_same_last_token": last == tokens[-1],
+        "distinct_tokens": len(set(tokens)),
+    }
+
+
+def chain_tok0(seed, synth):
+    return synth.randint(seed, "ch.tok0", synth.VOCAB)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--mode", choices=["fixed", "fast"], default="fixed")
+    ap.add_argument("--seed", type=int, default=20261202)
+    ap.add_argument("--chain-tokens", type=int, default=200)
+    ap.add_argument("--no-chain", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(asked for --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        return 2
+    if args.steps < 1:
+        print("--steps must be >= 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import affine_q4_matvec_amd as q4
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    step_ms, kern_ms, kern_med_ms, stable = run_head(args, q4, torch, synth)
+    qb = head_bytes(ROWS, COLS)
+    step_bytes = qb + rmsq_bytes(COLS)
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+    achieved = qb / (kern_ms * 1e-3) / 1e9
+    log("head: %.4f ms/step, q4mv %.4f ms avg (%.1f GB/s)" % (step_ms, kern_ms, achieved))
+    chain = None
+    if not args.no_chain:
+        chain = run_chain(args, q4, torch, synth)
+        log("chain: %s" % chain)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.seed)
+    traffic = measured_traffic(qb)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "output-head q4mv 248320x2048, group 64, 4-bit codes + fp32 scale/bias; "
+                        "x and group sums from rmsq(z~N(0,1), wn~N(1,0.1), eps 1e-6); "
+                        "step = rmsq + q4mv; 2 weight copies alternate",
+            "rows": ROWS, "cols": COLS, "group": 64, "mode": args.mode,
+            "step_bytes": step_bytes,
+            "output_bits_stable_across_steps": stable,
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+            "kernel": "q4mv_seg_kernel<64,R,fixed>" if args.mode == "fixed" else "q4mv_seg_kernel<64,R,fast>",
+            "algorithmic_bytes_per_launch": qb,
+            "avg_launch_ms": round(kern_ms, 5), "median_launch_ms": round(kern_med_ms, 5),
+        },
+        "decode_chain": chain,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

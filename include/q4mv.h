@@ -1,0 +1,192 @@
+/*
+ * q4mv.h -- C ABI of libq4mv.so: the affine 4-bit matvec (q4mv), its
+ * producers (rmsq, swq), the greedy-decode glue (argmax, embed), a
+ * stage queue with a single host wait, and whole-token graph capture,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations come from three pull-request pages of the Bend language
+ * repository (bendlang/bend):
+ *   [P1] "Metal: queued rmsq, swq, gdn and atq kernels and a 4-row q4mv, so
+ *        a decode token is one command buffer with one wait" (#1440)
+ *   [P2] "Array.q4go / Array.q4wait queue Metal Q4 products in one command
+ *        buffer and wait once on a flag" (#1437)
+ *   [P3] "Array.q4mv on Metal: one kernel thread per row for products of 4M
+ *        weights or more, bit-identical" (#1435)
+ *
+ * Conventions for every entry point
+ *   - Pointers named "device" must point to GPU memory of the current HIP
+ *     device; the caller allocates and owns every buffer, and must keep it
+ *     alive until the work that uses it has completed (for the queue: until
+ *     q4mv_wait returns -- the lifetime rule of [P2], Change).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only
+ *     enqueue work and return; they are legal inside stream capture, except
+ *     q4mv_wait, which waits on the host.
+ *   - Arguments are checked before anything is launched.  A bad argument
+ *     returns Q4_EINVAL and launches nothing; a failed launch returns
+ *     Q4_EHIP.  There is no CPU fallback and no size threshold.
+ *   - Outputs must not overlap inputs unless stated.
+ */
+#ifndef Q4MV_H
+#define Q4MV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define Q4_OK 0
+#define Q4_EINVAL (-1)   /* bad argument; nothing was launched            */
+#define Q4_EHIP (-2)     /* a HIP runtime call failed                     */
+#define Q4_ETIMEOUT (-3) /* a bounded host wait ran out of time           */
+#define Q4_ESTATE (-4)   /* call not legal now (e.g. host wait in capture) */
+#define Q4_ENOMEM (-5)   /* host allocation failed                        */
+
+/* Modes of q4mv and swq. */
+#define Q4_FIXED 0 /* fixed operation order: bit-identical to the reference */
+#define Q4_FAST 1  /* any order, fused multiply-add: relative error <= 1e-5 */
+
+/* Size limits of this build. */
+#define Q4_MAX_COLS 32768 /* q4mv: cols <= 32768 (512 groups)          */
+#define Q4_MAX_RMSQ_N 8192 /* rmsq: n <= 8192                          */
+
+/*
+ * One affine Q4 matrix ([P3] Why/Change: rows of 4-bit codes; [P1] Change:
+ * 64-value groups).  Layout (all device, row-major):
+ *   q : uint32[rows][cols/8]; column 8j+k is held in bits 4k..4k+3 of word
+ *       j of its row (low nibble first).  16-byte aligned.
+ *   s : float[rows][cols/64] scale of each 64-column group.  4-byte aligned.
+ *   b : float[rows][cols/64] bias of each group.          4-byte aligned.
+ * rows >= 1; cols a positive multiple of 64, at most Q4_MAX_COLS.
+ * Dequantised weight: W[r][c] = s[r][c/64] * q(r,c) + b[r][c/64].
+ */
+typedef struct q4_mat {
+  const uint32_t *q;
+  const float *s;
+  const float *b;
+  int32_t rows;
+  int32_t cols;
+} q4_mat;
+
+/*
+ * q4mv: y[r] = sum_g s[r,g] * (q[r,g] . x_g) + b[r,g] * xsum[g]
+ * ([P3] Change: the product itself; [P1] Change, rmsq bullet: the group
+ * sums it reads; [P1] Change, q4mv bullet: each row keeps a fixed
+ * summation tree).
+ *   w    : host pointer to the matrix descriptor (read during the call).
+ *   x    : device float[cols], 16-byte aligned.
+ *   xsum : device float[cols/64]; xsum[g] is the sum of x[64g..64g+63]
+ *          as emitted by rmsq/swq (an input: never recomputed).
+ *   y    : device float[rows]; must not overlap w, x or xsum.
+ *   mode : Q4_FIXED -- per row, p_i = q_i * x_i, d_g = T(p over the group),
+ *          t_g = (s*d_g) + (b*xsum_g) unfused, y = T(t over groups), with T
+ *          the canonical tree (split at the largest power of two below n);
+ *          bit-identical to the reference.  Q4_FAST -- reordered, fused;
+ *          |err| <= 1e-5*|y| + 1e-5*rms(y).
+ */
+int q4mv(const q4_mat *w, const float *x, const float *xsum, float *y, int mode,
+         void *stream);
+
+/*
+ * q4mv_add: y[r] = resid[r] + (W x)[r], the product of q4mv followed by one
+ * binary32 addition (a decode chain's residual, fused into the product's
+ * store).  resid: device float[rows]; it may be the same array as y.
+ */
+int q4mv_add(const q4_mat *w, const float *x, const float *xsum,
+             const float *resid, float *y, int mode, void *stream);
+
+/*
+ * rmsq: RMS norm with float weights plus the 64-value group sums that q4mv
+ * reads ([P1] Change, rmsq bullet; exact on the GPU there).
+ *   ss = T(h_i*h_i); rho = 1 / sqrt(ss/n + eps)  (correctly rounded);
+ *   u_i = (h_i*rho)*w_i;  usum[g] = T(u[64g..64g+63]).
+ *   h, w : device float[n];  u : device float[n];  usum : device float[n/64].
+ *   n a positive multiple of 64, at most Q4_MAX_RMSQ_N.  u may not overlap h.
+ */
+int rmsq(const float *h, const float *w, int32_t n, float eps, float *u,
+         float *usum, void *stream);
+
+/*
+ * swq: SwiGLU round(silu(a[i]) * a[n+i]) plus group sums ([P1] Change, swq
+ * bullet).
+ *   a    : device float[2n], gate in a[0..n), up in a[n..2n).
+ *   o    : device float[n];  osum : device float[n/64].
+ *   n a positive multiple of 64 (the n = 32 case the pages criticise is
+ *   Q4_EINVAL here, not a silently untouched o).
+ *   mode : Q4_FIXED -- binary64 silu a/(1+E(-a)) with E a fixed binary64
+ *          exp (Cody-Waite reduction by ln 2, degree-13 Taylor polynomial by
+ *          fused Horner, ldexp), one rounding of the binary64 product to
+ *          binary32; bit-identical to the reference.  Q4_FAST -- binary32.
+ */
+int swq(const float *a, int32_t n, float *o, float *osum, int mode,
+        void *stream);
+
+/*
+ * q4_argmax: greedy pick for a decode chain ([P1] Verification: greedy token
+ * ids).  *idx = lowest index of the largest value of v[0..n); -1 when any
+ * value is NaN.  -0 and +0 compare equal.
+ *   v   : device float[n], n >= 1.   idx : device int32[1].
+ *   ws  : device workspace of at least q4_argmax_ws_bytes(n) bytes, 8-byte
+ *         aligned, owned by the caller; calls that overlap in time must not
+ *         share it.
+ */
+size_t q4_argmax_ws_bytes(int32_t n);
+int q4_argmax(const float *v, int32_t n, int32_t *idx, void *ws,
+              size_t ws_bytes, void *stream);
+
+/*
+ * q4_embed: embedding lookup from a tied Q4 matrix: e[c] = (s[t,c/64] *
+ * q(t,c)) + b[t,c/64] with t = *tok read on the device (so a captured graph
+ * can feed argmax's output straight back).  A token outside [0, rows) fills
+ * e with quiet NaNs.  tok: device int32[1]; e: device float[cols].
+ */
+int q4_embed(const q4_mat *w, const int32_t *tok, float *e, void *stream);
+
+/*
+ * Stage queue ([P2] Change: q4go encodes products into one open concurrent
+ * command buffer and returns; q4wait commits and waits once).
+ * q4mv_queue appends a product to the current stage.  Products of one stage
+ * may run concurrently, so none may read another's y ([P2] Change).
+ * q4_stage closes the stage: its products are launched as grouped kernels
+ * (one launch per kernel shape) with no host wait; later stages are ordered
+ * after it on the queue's stream.  q4mv_wait closes the open stage and waits
+ * once on the host for all of it; every buffer the queue's products use
+ * must stay alive until it returns.  With env Q4MV_DEBUG_CHECKS=1,
+ * q4mv_queue rejects (Q4_EINVAL) a product whose y overlaps an input of
+ * another product of the same stage.  With env Q4MV_TRACE=1, q4mv_wait
+ * prints the product count, GPU time and wall time of each wait to stderr.
+ * A queue is used by one host thread at a time.
+ */
+typedef struct q4_queue q4_queue;
+int q4_queue_create(void *stream, int mode, q4_queue **out);
+int q4_queue_destroy(q4_queue *q);
+int q4mv_queue(q4_queue *q, const q4_mat *w, const float *x, const float *xsum,
+               float *y);
+int q4_stage(q4_queue *q);
+int q4mv_wait(q4_queue *q);
+
+/*
+ * Whole-token graph capture ([P1] Verification: a decode token encoded as
+ * one command buffer of 194 kernels and one wait).  Between
+ * q4_capture_begin and q4_capture_end every call on `stream` is recorded,
+ * not run; q4_graph_launch replays the recording on a stream.  No host wait
+ * may happen in between (q4mv_wait returns Q4_ESTATE).
+ */
+typedef struct q4_graph q4_graph;
+int q4_capture_begin(void *stream);
+int q4_capture_end(void *stream, q4_graph **out);
+int q4_graph_launch(q4_graph *g, void *stream);
+int q4_graph_destroy(q4_graph *g);
+
+/* Host wait for all work on `stream` (one hipStreamSynchronize). */
+int q4_sync(void *stream);
+
+/* Text of a status code. */
+const char *q4_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q4MV_H */

@@ -20,8 +20,14 @@ Generator (counter-based, machine independent):
 * 4-bit codes: word ``2j`` of a code tensor is the low half of draw ``j`` and
   word ``2j + 1`` the high half; every nibble of a word is one code, so codes
   are uniform over 0..15.
-* Bias of the affine Q4 matrices: ``RN32(-8 * s + N(0, 1e-3))`` in binary64,
-  where ``s`` is the binary32 scale of the same group.
+* Bias of the affine Q4 matrices: ``RN32(-c * s + N(0, 1e-3))`` in binary64,
+  where ``s`` is the binary32 scale of the same group and ``c`` the code
+  centre: 8 for the single products (as their configurations state), 7.5
+  for the decode chain's matrices (zero-mean dequantised weights).  With
+  c = 8 every uniform-code weight carries a -0.5 s offset; in a 24-layer
+  chain that rank-one drift dominates the residual stream, the head sees
+  almost the same input for every token and greedy decoding sits on one
+  token from the first step.
 """
 from __future__ import annotations
 
@@ -122,16 +128,17 @@ def codes_u32(seed: int, name: str, rows: int, cols: int) -> np.ndarray:
 
 
 def q4_matrix(seed: int, name: str, rows: int, cols: int,
-              s_lo: float = 0.001, s_hi: float = 0.02, b_std: float = 1e-3) -> dict:
+              s_lo: float = 0.001, s_hi: float = 0.02, b_std: float = 1e-3,
+              center: float = 8.0) -> dict:
     """An affine Q4 matrix: codes, fp32 scale U(s_lo, s_hi) and fp32 bias
-    RN32(-8 s + N(0, b_std)) per group of 64 columns."""
+    RN32(-center s + N(0, b_std)) per group of 64 columns."""
     if cols % GROUP:
         raise ValueError("cols must be a multiple of 64")
     G = cols // GROUP
     q = codes_u32(seed, name + ".q", rows, cols)
     s = uniform_f32(seed, name + ".s", (rows, G), s_lo, s_hi)
     noise = normal_f64(seed, name + ".b", rows * G).reshape(rows, G)
-    b = (-8.0 * s.astype(np.float64) + b_std * noise).astype(np.float32)
+    b = (-center * s.astype(np.float64) + b_std * noise).astype(np.float32)
     return {"q": q, "s": s, "b": b, "rows": rows, "cols": cols}
 
 
@@ -158,6 +165,7 @@ INTER = 6144
 VOCAB = 248320
 LAYERS = 24
 EPS = 1e-6
+CHAIN_CENTER = 7.5
 
 
 def small_product(seed: int = DEFAULT_SEED, rows: int = 13, cols: int = 128,
@@ -210,19 +218,20 @@ def chain_weights(seed: int = DEFAULT_SEED, layers: int = LAYERS, hidden: int = 
                   inter: int = INTER, vocab: int = VOCAB) -> dict:
     """Decode-chain weights: per layer an RMS-norm weight N(1, 0.1) and
     gate, up (inter x hidden) and down (hidden x inter) Q4 matrices; a final
-    norm weight; a vocab x hidden head, also used as the tied embedding."""
+    norm weight; a vocab x hidden head, also used as the tied embedding.
+    The Q4 matrices use the code centre 7.5 (zero-mean weights)."""
     lay = []
     for l in range(layers):
         lay.append({
             "wn": normal_f32(seed, "ch.l%d.wn" % l, (hidden,), 1.0, 0.1),
-            "gate": q4_matrix(seed, "ch.l%d.gate" % l, inter, hidden),
-            "up": q4_matrix(seed, "ch.l%d.up" % l, inter, hidden),
-            "down": q4_matrix(seed, "ch.l%d.down" % l, hidden, inter),
+            "gate": q4_matrix(seed, "ch.l%d.gate" % l, inter, hidden, center=CHAIN_CENTER),
+            "up": q4_matrix(seed, "ch.l%d.up" % l, inter, hidden, center=CHAIN_CENTER),
+            "down": q4_matrix(seed, "ch.l%d.down" % l, hidden, inter, center=CHAIN_CENTER),
         })
     return {
         "layers": lay,
         "wn_final": normal_f32(seed, "ch.wn_final", (hidden,), 1.0, 0.1),
-        "head": q4_matrix(seed, "ch.head", vocab, hidden),
+        "head": q4_matrix(seed, "ch.head", vocab, hidden, center=CHAIN_CENTER),
         "tok0": randint(seed, "ch.tok0", vocab),
         "eps": np.float32(EPS),
         "hidden": hidden, "inter": inter, "vocab": vocab,

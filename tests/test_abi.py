@@ -1,0 +1,123 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/q4mv.h declares, and rejects bad arguments before any HIP call
+(every call below returns Q4_EINVAL from the host-side checks)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4mv.h")
+LIB = os.path.join(ROOT, "affine_q4_matvec_amd", "libq4mv.so")
+
+EINVAL = -1
+
+
+class Mat(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("s", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^\s*(?:int|size_t|const char \*)\s*\**\s*(\w+)\s*\(", text, re.M)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        pytest.fail("libq4mv.so is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB)
+    lib.q4_strerror.restype = ctypes.c_char_p
+    lib.q4_argmax_ws_bytes.restype = ctypes.c_size_t
+    return lib
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) >= 18
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_only_the_c_abi_is_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    exported = {s for s in syms if not s.startswith("__hip_cuid")}
+    assert exported == set(declared_functions())
+
+
+# fake, never-dereferenced device addresses (16-byte aligned, disjoint)
+A = 0x7F0000000000
+B = 0x7F0010000000
+C = 0x7F0020000000
+D = 0x7F0030000000
+E = 0x7F0040000000
+F = 0x7F0050000000
+
+
+def mat(q=A, s=B, b=C, rows=8, cols=128):
+    return Mat(q, s, b, rows, cols)
+
+
+@pytest.mark.parametrize("m", [
+    mat(q=0), mat(s=0), mat(b=0), mat(rows=0), mat(rows=-3), mat(cols=0), mat(cols=100),
+    mat(cols=32), mat(cols=32768 + 64), mat(q=A + 4), mat(s=B + 2),
+])
+def test_q4mv_rejects_bad_matrix(L, m):
+    assert L.q4mv(ctypes.byref(m), ctypes.c_void_p(D), ctypes.c_void_p(E), ctypes.c_void_p(F), 0, None) == EINVAL
+
+
+def test_q4mv_rejects_bad_vectors_and_mode(L):
+    m = mat()
+    p = lambda v: ctypes.c_void_p(v)
+    assert L.q4mv(None, p(D), p(E), p(F), 0, None) == EINVAL
+    assert L.q4mv(ctypes.byref(m), None, p(E), p(F), 0, None) == EINVAL
+    assert L.q4mv(ctypes.byref(m), p(D + 4), p(E), p(F), 0, None) == EINVAL  # x not 16-B aligned
+    assert L.q4mv(ctypes.byref(m), p(D), p(E), p(F), 2, None) == EINVAL      # mode
+    assert L.q4mv(ctypes.byref(m), p(D), p(E), p(D + 64), 0, None) == EINVAL  # y overlaps x
+    assert L.q4mv(ctypes.byref(m), p(D), p(E), p(A + 16), 0, None) == EINVAL  # y overlaps q
+    # residual that partly overlaps y
+    assert L.q4mv_add(ctypes.byref(m), p(D), p(E), p(F + 4), p(F), 0, None) == EINVAL
+
+
+def test_producers_reject_bad_sizes(L):
+    p = lambda v: ctypes.c_void_p(v)
+    assert L.rmsq(p(A), p(B), 100, ctypes.c_float(1e-6), p(C), p(D), None) == EINVAL
+    assert L.rmsq(p(A), p(B), 8192 + 64, ctypes.c_float(1e-6), p(C), p(D), None) == EINVAL
+    assert L.rmsq(p(A), p(B), 2048, ctypes.c_float(1e-6), p(A + 64), p(D), None) == EINVAL
+    assert L.swq(p(A), 32, p(B), p(C), 0, None) == EINVAL  # n = 32 is an error
+    assert L.swq(p(A), 6144, p(A + 4), p(C), 0, None) == EINVAL  # o inside a
+    assert L.swq(p(A), 6144, p(B), p(C), 5, None) == EINVAL
+
+
+def test_argmax_and_embed_checks(L):
+    p = lambda v: ctypes.c_void_p(v)
+    need = L.q4_argmax_ws_bytes(248320)
+    assert 8 <= need <= 8 * 1024 and L.q4_argmax_ws_bytes(0) == 0
+    assert L.q4_argmax(p(A), 248320, p(B), p(C), need - 8, None) == EINVAL
+    assert L.q4_argmax(p(A), 0, p(B), p(C), need, None) == EINVAL
+    assert L.q4_argmax(p(A), 248320, p(B), p(C + 4), need, None) == EINVAL
+    m = mat()
+    assert L.q4_embed(ctypes.byref(m), None, p(D), None) == EINVAL
+    assert L.q4_embed(ctypes.byref(mat(cols=96)), p(E), p(D), None) == EINVAL
+
+
+def test_queue_and_graph_argument_checks(L):
+    assert L.q4_queue_create(None, 0, None) == EINVAL
+    out = ctypes.c_void_p()
+    assert L.q4_queue_create(None, 3, ctypes.byref(out)) == EINVAL
+    assert L.q4mv_queue(None, None, None, None, None) == EINVAL
+    assert L.q4_stage(None) == EINVAL and L.q4mv_wait(None) == EINVAL
+    assert L.q4_queue_destroy(None) == EINVAL
+    assert L.q4_capture_begin(None) == EINVAL
+    assert L.q4_capture_end(None, ctypes.byref(out)) == EINVAL
+    assert L.q4_graph_launch(None, None) == EINVAL and L.q4_graph_destroy(None) == EINVAL
+
+
+def test_strerror(L):
+    assert L.q4_strerror(0) == b"ok"
+    assert b"invalid" in L.q4_strerror(-1)
+    assert L.q4_strerror(12345) == b"unknown status"
