@@ -17,7 +17,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libq4mv.so")
-SOURCES = ["q4mv_kernels.hip", "q4mv_api.hip"]
+SOURCES = ["q4mv_kernels.hip", "producers.hip", "q4mv_api.hip"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -35,11 +35,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into affine_q4_matvec_amd/libq4mv.so."""
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every source into affine_q4_matvec_amd/libq4mv.so (or `out`;
+    `defines` are extra -D tunables)."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *FLAGS, "-o", tmp, *srcs]
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *FLAGS, *["-D" + d for d in defines], "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,15 +51,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
-def asm(out_path: str) -> str:
-    """Writes the gfx950 assembly of the kernels (for inspection)."""
+def asm(out_path: str, source: str = "q4mv_kernels.hip") -> str:
+    """Writes the gfx950 assembly of one source (for inspection)."""
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-ffp-contract=off",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "--cuda-device-only", "-S", "-o", out_path, os.path.join(CSRC, "q4mv_kernels.hip")]
+           "--cuda-device-only", "-S", "-o", out_path, os.path.join(CSRC, source)]
     subprocess.run(cmd, check=True, capture_output=True)
     return out_path
 

@@ -69,16 +69,31 @@ int make_prod(const q4_mat *w, const float *x, const float *xsum, const float *r
 int hip_status(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_EHIP; }
 
 // Launches a list of products of one shape as grouped kernels (up to
-// kMaxGroup products per launch).
+// kMaxGroup products per launch).  When the products of a launch together
+// want more workgroups than fit on the device at once, each one's share is
+// cut in proportion (at least one workgroup each).
 int launch_products(const Prod *prods, int count, const Shape &sh, int mode, hipStream_t st) {
+  const int cap = q4::resident_capacity(sh, mode);
   for (int at = 0; at < count; at += q4::kMaxGroup) {
     ProdGroup g;
     memset(&g, 0, sizeof(g));
     g.n = count - at < q4::kMaxGroup ? count - at : q4::kMaxGroup;
+    int32_t want[q4::kMaxGroup];
+    long long total = 0;
+    for (int i = 0; i < g.n; ++i) {
+      want[i] = q4::workgroups_for(sh, prods[at + i].rows, mode);
+      total += want[i];
+    }
+    if (cap > 0 && total > cap) {
+      for (int i = 0; i < g.n; ++i) {
+        const long long w = (long long)want[i] * cap / total;
+        want[i] = (int32_t)(w < 1 ? 1 : w);
+      }
+    }
     g.wg_begin[0] = 0;
     for (int i = 0; i < g.n; ++i) {
       g.p[i] = prods[at + i];
-      g.wg_begin[i + 1] = g.wg_begin[i] + q4::workgroups_for(sh, prods[at + i].rows);
+      g.wg_begin[i + 1] = g.wg_begin[i] + want[i];
     }
     for (int i = g.n; i < q4::kMaxGroup; ++i) g.wg_begin[i + 1] = g.wg_begin[g.n];
     const int rc = hip_status(q4::launch_q4mv_group(g, sh, mode, st));

@@ -1,0 +1,295 @@
+// Device helpers shared by the q4mv kernels (gfx950, wave64).
+//
+// Compiled with -ffp-contract=off: every float expression is the exact
+// sequence of IEEE binary32 operations it spells.
+//
+// The fixed summation tree T(v[0..n)) splits at the largest power of two
+// below n ("a fixed tree order": "Metal: queued rmsq, swq, gdn and atq
+// kernels and a 4-row q4mv, so a decode token is one command buffer with one
+// wait" (#1440), Change, q4mv bullet).  T equals a balanced pairwise tree
+// over the next power of two >= n whose missing leaves are -0.0 (x + -0.0 ==
+// x for every x, including +-0), so a lane butterfly with -0.0 padding
+// reproduces it for any n, and T over n leaves equals T over the sums of
+// aligned blocks of any power-of-two size.  IEEE addition is commutative, so
+// which lane of a butterfly pair adds which operand does not change a bit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q4mv_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace q4 {
+namespace dev {
+
+constexpr int kWave = 64;
+constexpr float kNegZero = -0.0f;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// DPP controls of the gfx9 family.
+constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- 7-i within 8 lanes
+constexpr int kDppRowMirror = 0x140;      // lane i <- 15-i within 16 lanes
+constexpr int kDppRowBcast15 = 0x142;     // lane 15 of row k -> row k+1
+constexpr int kDppRowBcast31 = 0x143;     // lane 31 -> rows 2 and 3
+
+// Buffer resource (gfx9 format): raw byte addressing, no stride; loads past
+// num_records bytes return zero.
+constexpr int kBufferFlags = 0x00020000;
+// Cache policy of the streaming code loads: non-temporal.
+constexpr int kAuxNonTemporal = 2;
+
+// Index of the wave in its workgroup, as a wave-uniform (scalar) value: the
+// compiler cannot prove threadIdx.x / 64 uniform by itself, and addresses
+// built from a value it thinks divergent turn every buffer load into a loop.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// -0.0 in a register the compiler cannot rematerialise (it would rebuild
+// the constant with one instruction at every use).
+__device__ __forceinline__ int neg_zero_reg() {
+  int v = __float_as_int(kNegZero);
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// DPP move limited to the rows in ROW_MASK; lanes of the other rows read
+// `old` (-0.0, the additive identity of the tree).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_rows(float v, int old) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(old, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum of the group terms of one row segment of LPR lanes (every group term
+// held identically by a lane pair).  All lanes of the segment must run it.
+// After each step every aligned block of 2^k lanes holds one value, so a
+// mirror within 8 (16) lanes pairs blocks 4 (8) lanes apart, like xor 4 (8).
+template <int LPR>
+__device__ __forceinline__ float segment_sum(float t) {
+  if constexpr (LPR >= 4) t = t + dpp<kDppQuadXor2>(t);
+  if constexpr (LPR >= 8) t = t + dpp<kDppRowHalfMirror>(t);
+  if constexpr (LPR >= 16) t = t + dpp<kDppRowMirror>(t);
+  if constexpr (LPR >= 32) t = t + __shfl_xor(t, 16);
+  if constexpr (LPR >= 64) t = t + __shfl_xor(t, 32);
+  return t;
+}
+
+// Sum over the 32 lane pairs of a wave, valid in lane 63 only.  The first
+// three steps leave each 16-lane row R_k uniform; row_bcast15 adds R0 into
+// row 1 and R2 into row 3; row_bcast31 adds (R0+R1) into row 3:
+// ((R0+R1)+(R2+R3)), the balanced tree over the four rows.
+// `negz` holds -0.0 (neg_zero_reg()).
+__device__ __forceinline__ float wave_sum_lane63(float t, int negz) {
+  t = t + dpp<kDppQuadXor2>(t);
+  t = t + dpp<kDppRowHalfMirror>(t);
+  t = t + dpp<kDppRowMirror>(t);
+  t = t + dpp_rows<kDppRowBcast15, 0xA>(t, negz);
+  t = t + dpp_rows<kDppRowBcast31, 0xC>(t, negz);
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// Codes -> products.  Word bits 4k..4k+3 hold code k; p_k = code_k * x_k.
+// ---------------------------------------------------------------------------
+
+// Plain decode: every code converted to binary32 exactly.
+__device__ __forceinline__ float word_tree(uint32_t w, const float *xk) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
+  const float p0 = (float)(lo & 0xFFu) * xk[0];
+  const float p1 = (float)(hi & 0xFFu) * xk[1];
+  const float p2 = (float)((lo >> 8) & 0xFFu) * xk[2];
+  const float p3 = (float)((hi >> 8) & 0xFFu) * xk[3];
+  const float p4 = (float)((lo >> 16) & 0xFFu) * xk[4];
+  const float p5 = (float)((hi >> 16) & 0xFFu) * xk[5];
+  const float p6 = (float)(lo >> 24) * xk[6];
+  const float p7 = (float)(hi >> 24) * xk[7];
+  return ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7));
+}
+
+// Pair decode: a byte 0x0q read as an 8-bit float (4 exponent bits, 3
+// mantissa bits) is exactly q * u for q = 0..15, where u (2^-9 in the OCP
+// format, 2^-10 in the FNUZ one) is the value of byte 0x01: 0x01..0x07 are
+// subnormals m*u and 0x08..0x0F the first binade (8+m)*u.  One
+// v_cvt_pk_f32_fp8 decodes two codes.  With activations pre-scaled to
+// x' = x / u (exact: a power-of-two scale that cannot overflow while
+// |x| < 2^118), (q u) * x' equals q * x as a real number, so its rounding
+// is the rounding of q * x: the same bits as the plain decode.
+__device__ __forceinline__ float fp8_unit() {
+  const f32x2 one = __builtin_amdgcn_cvt_pk_f32_fp8(0x0101, false);
+  return one.x;
+}
+
+__device__ __forceinline__ float word_tree_pairs(uint32_t w, const float *xk) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+  const f32x2 c02 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+  const f32x2 c46 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+  const f32x2 c13 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+  const f32x2 c57 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  const float p0 = c02.x * xk[0];
+  const float p1 = c13.x * xk[1];
+  const float p2 = c02.y * xk[2];
+  const float p3 = c13.y * xk[3];
+  const float p4 = c46.x * xk[4];
+  const float p5 = c57.x * xk[5];
+  const float p6 = c46.y * xk[6];
+  const float p7 = c57.y * xk[7];
+  return ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7));
+}
+
+// Tree of one lane's 32-code chunk (four words, contiguous columns).
+template <bool PAIRS>
+__device__ __forceinline__ float chunk_tree(u32x4 c, const float *xv) {
+  if constexpr (PAIRS) {
+    return (word_tree_pairs(c.x, xv) + word_tree_pairs(c.y, xv + 8)) +
+           (word_tree_pairs(c.z, xv + 16) + word_tree_pairs(c.w, xv + 24));
+  } else {
+    return (word_tree(c.x, xv) + word_tree(c.y, xv + 8)) +
+           (word_tree(c.z, xv + 16) + word_tree(c.w, xv + 24));
+  }
+}
+
+// Q4_FAST: the chunk's dot product accumulated with fused multiply-adds.
+template <bool PAIRS>
+__device__ __forceinline__ float chunk_dot_fast(u32x4 c, const float *xv) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  float acc = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t lo = w[k] & 0x0F0F0F0Fu;
+    const uint32_t hi = (w[k] >> 4) & 0x0F0F0F0Fu;
+    const float *xk = xv + 8 * k;
+    if constexpr (PAIRS) {
+      const f32x2 c02 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+      const f32x2 c46 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+      const f32x2 c13 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+      const f32x2 c57 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+      acc = fmaf(c02.x, xk[0], acc);
+      acc = fmaf(c13.x, xk[1], acc);
+      acc = fmaf(c02.y, xk[2], acc);
+      acc = fmaf(c13.y, xk[3], acc);
+      acc = fmaf(c46.x, xk[4], acc);
+      acc = fmaf(c57.x, xk[5], acc);
+      acc = fmaf(c46.y, xk[6], acc);
+      acc = fmaf(c57.y, xk[7], acc);
+    } else {
+      acc = fmaf((float)(lo & 0xFFu), xk[0], acc);
+      acc = fmaf((float)(hi & 0xFFu), xk[1], acc);
+      acc = fmaf((float)((lo >> 8) & 0xFFu), xk[2], acc);
+      acc = fmaf((float)((hi >> 8) & 0xFFu), xk[3], acc);
+      acc = fmaf((float)((lo >> 16) & 0xFFu), xk[4], acc);
+      acc = fmaf((float)((hi >> 16) & 0xFFu), xk[5], acc);
+      acc = fmaf((float)(lo >> 24), xk[6], acc);
+      acc = fmaf((float)(hi >> 24), xk[7], acc);
+    }
+  }
+  return acc;
+}
+
+// Group term of a lane (the lane pair 2g, 2g+1 holds group g):
+//   fixed: d = T(pair's chunk trees); t = (s*d) + (b*xs); both lanes of the
+//          pair end with the same t
+//   fast : each lane adds s*dot (+ b*xs on the even lane), then the pair is
+//          summed, so both lanes again hold the group's term.
+template <bool FAST, bool PAIRS>
+__device__ __forceinline__ float group_term(u32x4 c, const float *xv, float sv, float bv,
+                                            float xsv, bool active, bool odd) {
+  if constexpr (!FAST) {
+    float L = chunk_tree<PAIRS>(c, xv);
+    L = active ? L : kNegZero;
+    const float d = L + dpp<kDppQuadXor1>(L);
+    const float sd = sv * d;
+    const float bx = bv * xsv;
+    const float t = sd + bx;
+    return active ? t : kNegZero;
+  } else {
+    const float acc = chunk_dot_fast<PAIRS>(c, xv);
+    float t = fmaf(sv, acc, odd ? 0.0f : bv * xsv);
+    t = active ? t : 0.0f;
+    return t + dpp<kDppQuadXor1>(t);
+  }
+}
+
+// Picks product i of a group with constant indices only (a dynamic index
+// into the kernel-argument struct would spill it to scratch).
+__device__ __forceinline__ void select_product(const ProdGroup &grp, Prod &P, int &lw, int &nwg) {
+  const int bid = blockIdx.x;
+  int pi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i)
+    if (i < grp.n && bid >= grp.wg_begin[i]) pi = i;
+#pragma unroll
+  for (int i = 0; i < kMaxGroup; ++i) {
+    if (i == pi) {
+      P = grp.p[i];
+      lw = bid - grp.wg_begin[i];
+      nwg = grp.wg_begin[i + 1] - grp.wg_begin[i];
+    }
+  }
+}
+
+// The 32 activations of chunk `chunk` (columns 32 chunk .. 32 chunk + 31)
+// and the group sum of its group.  Inactive lanes get zeros.
+__device__ __forceinline__ void load_x_chunk(const Prod &P, int chunk, bool active, float *xv,
+                                             float &xsv) {
+  if (active) {
+    const float4 *xp = reinterpret_cast<const float4 *>(P.x + 32 * chunk);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 v = xp[k];
+      xv[4 * k + 0] = v.x;
+      xv[4 * k + 1] = v.y;
+      xv[4 * k + 2] = v.z;
+      xv[4 * k + 3] = v.w;
+    }
+    xsv = P.xs[chunk >> 1];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) xv[k] = 0.0f;
+    xsv = 0.0f;
+  }
+}
+
+// Pre-scales the lane's activations for the pair decode when every
+// activation of the wave is below 2^118 in magnitude (NaN counts as large);
+// returns whether the wave may use the pair decode.
+__device__ __forceinline__ bool prescale_for_pairs(float *xv) {
+  bool large = false;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) large |= !(__builtin_fabsf(xv[k]) < 0x1p118f);
+  if (__any(large)) return false;
+  const float scale = 1.0f / fp8_unit();  // 2^9 or 2^10, exact
+#pragma unroll
+  for (int k = 0; k < 32; ++k) xv[k] = xv[k] * scale;
+  return true;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           kBufferFlags);
+}
+
+__device__ __forceinline__ u32x4 load_codes(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                            uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kAuxNonTemporal);
+}
+
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+}  // namespace dev
+}  // namespace q4

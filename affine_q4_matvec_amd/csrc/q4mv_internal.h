@@ -29,18 +29,26 @@ struct ProdGroup {
   int32_t n;
 };
 
-// Kernel shape of a product: rows of at most 32 groups are covered by one
-// segment of `lpr` lanes of a wave (lpr = 2..64); wider rows are split into
-// `passes` 2048-column passes, one wave each, combined through LDS.
+// Kernel shape of a product: rows of exactly 32 groups (2048 columns) take
+// one wave each (row64); rows of fewer groups are covered by one segment of
+// `lpr` lanes of a wave (lpr = 2..64); wider rows are split into `passes`
+// 2048-column passes, one wave each, combined through LDS.
 struct Shape {
-  int32_t lpr;     // lanes per row segment (0 when split)
-  int32_t passes;  // waves per row for split rows (0 when segmented)
-  bool operator==(const Shape &o) const { return lpr == o.lpr && passes == o.passes; }
+  enum Kind : int32_t { kRow64 = 0, kSeg = 1, kSplit = 2 };
+  int32_t kind;
+  int32_t lpr;     // lanes per row segment (seg)
+  int32_t passes;  // waves per row (split)
+  bool operator==(const Shape &o) const {
+    return kind == o.kind && lpr == o.lpr && passes == o.passes;
+  }
 };
 
 Shape shape_of(int32_t cols);
-// Workgroups a product of this shape gets in a launch.
-int32_t workgroups_for(const Shape &sh, int32_t rows);
+// Workgroups a product of this shape gets when launched alone.
+int32_t workgroups_for(const Shape &sh, int32_t rows, int mode);
+// Workgroups of this shape that fit on the current device at once (0: no
+// limit from occupancy).
+int32_t resident_capacity(const Shape &sh, int mode);
 
 // Launchers.  They assume validated arguments and return the HIP status of
 // the launch.

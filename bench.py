@@ -52,8 +52,11 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
-    src = os.path.join(ROOT, "affine_q4_matvec_amd", "csrc", "q4mv_kernels.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    """Hash of the q4mv kernel sources (the counters are only valid for them)."""
+    h = hashlib.sha256()
+    for name in ("q4mv_kernels.hip", "q4mv_device.h"):
+        h.update(open(os.path.join(ROOT, "affine_q4_matvec_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(per_launch_alg_bytes: int):
@@ -214,6 +217,9 @@ def main() -> int:
     ap.add_argument("--chain-tokens", type=int, default=200)
     ap.add_argument("--no-chain", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
+                         "kernel that scales the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -234,6 +240,16 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = 1 << 28  # 2^28 floats = 1 GiB
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 5}))
+        return 0
     step_ms, kern_ms, kern_med_ms, stable = run_head(args, q4, torch, synth)
     qb = head_bytes(ROWS, COLS)
     step_bytes = qb + rmsq_bytes(COLS)
@@ -271,7 +287,7 @@ def main() -> int:
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-            "kernel": "q4mv_seg_kernel<64,R,fixed>" if args.mode == "fixed" else "q4mv_seg_kernel<64,R,fast>",
+            "kernel": "q4mv_row64_kernel<4,%s>" % ("false" if args.mode == "fixed" else "true"),
             "algorithmic_bytes_per_launch": qb,
             "avg_launch_ms": round(kern_ms, 5), "median_launch_ms": round(kern_med_ms, 5),
         },

@@ -103,19 +103,41 @@ def test_q4mv_tree_order_adversarial():
             assert_bits_equal(run_q4mv(m2, x, xs), oracle.q4mv(m2, x, xs), "%d %s" % (c2048, case))
 
 
-def test_q4mv_special_values():
-    """Zeros of both signs, subnormal activations, huge activations."""
-    rows, cols = 16, 2048
-    m = synth.small_product(seed=3, rows=rows, cols=cols, name="spec")
+@pytest.mark.parametrize("cols", [128, 2048, 6144])
+def test_q4mv_special_values(cols):
+    """Zeros of both signs and subnormal activations (pair decode), and
+    activations of 2^118 and more, which send a wave to the plain decode."""
+    rows = 16
+    m = synth.small_product(seed=3, rows=rows, cols=cols, name="spec%d" % cols)
     x = m["x"].copy()
-    x[:64] = 0.0
-    x[64:128] = -0.0
-    x[128:192] = np.float32(1e-40)   # binary32 subnormals
-    x[192:256] = np.float32(-3e-39)
-    x[256] = np.float32(1e37)
-    x[300] = np.float32(-2e36)
+    x[:32] = 0.0
+    x[32:64] = -0.0
+    x[64:96] = np.float32(1e-40)   # binary32 subnormals
+    x[96:128] = np.float32(-3e-39)
     xs = oracle.group_sums(x)
-    assert_bits_equal(run_q4mv(m, x, xs), oracle.q4mv(m, x, xs), "special values")
+    assert_bits_equal(run_q4mv(m, x, xs), oracle.q4mv(m, x, xs), "small values %d" % cols)
+    for big in (np.float32(2.0**118), np.float32(1e37), np.float32(-3.4e38)):
+        xb = x.copy()
+        xb[cols - 5] = big
+        xs = oracle.group_sums(xb)
+        assert_bits_equal(run_q4mv(m, xb, xs), oracle.q4mv(m, xb, xs), "large %r %d" % (big, cols))
+    xb = x.copy()
+    xb[cols // 2] = np.float32(2.0**117)  # largest scale the pair decode keeps
+    xs = oracle.group_sums(xb)
+    assert_bits_equal(run_q4mv(m, xb, xs), oracle.q4mv(m, xb, xs), "2^117 %d" % cols)
+
+
+def test_q4mv_nan_and_inf_propagate():
+    rows, cols = 8, 2048
+    m = synth.small_product(seed=4, rows=rows, cols=cols, name="nan")
+    for bad in (np.inf, -np.inf, np.nan):
+        x = m["x"].copy()
+        x[700] = bad
+        xs = oracle.group_sums(x)
+        got, want = run_q4mv(m, x, xs), oracle.q4mv(m, x, xs)
+        assert np.array_equal(np.isnan(got), np.isnan(want))
+        ok = ~np.isnan(want)
+        assert_bits_equal(got[ok], want[ok], "non-NaN outputs with %r" % bad)
 
 
 def test_q4mv_add_residual():
