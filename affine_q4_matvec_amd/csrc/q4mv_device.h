@@ -4,9 +4,10 @@
 // sequence of IEEE binary32 operations it spells.
 //
 // The fixed summation tree T(v[0..n)) splits at the largest power of two
-// below n ("a fixed tree order": "Metal: queued rmsq, swq, gdn and atq
-// kernels and a 4-row q4mv, so a decode token is one command buffer with one
-// wait" (#1440), Change, q4mv bullet).  T equals a balanced pairwise tree
+// below n: the reading taken of the fixed order the pages name for q4mv's
+// sums ("Metal: queued rmsq, swq, gdn and atq kernels and a 4-row q4mv, so a
+// decode token is one command buffer with one wait" (#1440), Change, q4mv
+// bullet).  T equals a balanced pairwise tree
 // over the next power of two >= n whose missing leaves are -0.0 (x + -0.0 ==
 // x for every x, including +-0), so a lane butterfly with -0.0 padding
 // reproduces it for any n, and T over n leaves equals T over the sums of

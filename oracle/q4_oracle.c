@@ -16,10 +16,12 @@
  * Sources (bendlang/bend pull requests, as quoted in the source pages):
  *  - "Array.q4mv on Metal: one kernel thread per row ..." (#1435), Why and
  *    Change: the product is an affine 4-bit matvec over rows of packed codes.
- *  - "Metal: queued rmsq, swq, gdn and atq kernels and a 4-row q4mv" (#1440),
- *    Change: rmsq is an RMS norm with F32 weights that also emits the
- *    64-value group sums q4mv reads; swq is SwiGLU round(silu(a[i])*a[n+i])
- *    plus group sums; q4mv keeps "a fixed tree order" for its sums.
+ *  - "Metal: queued rmsq, swq, gdn and atq kernels and a 4-row q4mv, so a
+ *    decode token is one command buffer with one wait" (#1440), Change:
+ *    rmsq is an RMS norm with binary32 weights that also produces the
+ *    per-64-column group sums q4mv consumes; swq is SwiGLU (silu of each
+ *    gate value times its up value, rounded) with group sums; q4mv sums
+ *    each row in a fixed order that the pages name but never print.
  *  - The pages never print the summation tree, the nibble order or the
  *    precision of swq.  The readings taken here (canonical tree T, low
  *    nibble first, swq in binary64 with one rounding to binary32, exp by a
@@ -36,8 +38,8 @@
 #define GROUP 64
 
 /* ------------------------------------------------------------------------
- * Canonical summation tree T (the reading of "a fixed tree order", #1436's
- * title as quoted on the #1440 page, Change).
+ * Canonical summation tree T: the reading taken of the fixed summation
+ * order that #1436's title (cited on the #1440 page, Change) names.
  *   T(v[0..1)) = v[0]
  *   T(v[0..n)) = T(v[0..m)) + T(v[m..n)),  m = largest power of two < n
  * Every '+' is one binary32 addition.
@@ -58,8 +60,8 @@ float orc_tree(const float *v, int64_t n) {
 
 /* ------------------------------------------------------------------------
  * Group sums of an activation vector: xs[g] = T(x[64g .. 64g+63]).
- * These are the "64-value group sums that Array.q4mv reads" (#1440, Change,
- * rmsq bullet).  n must be a multiple of 64.
+ * These are the group sums the producers hand to q4mv (#1440, Change, rmsq
+ * bullet).  n must be a multiple of 64.
  * ---------------------------------------------------------------------- */
 void orc_group_sums(const float *x, int64_t n, float *xs) {
     for (int64_t g = 0; g < n / GROUP; ++g) xs[g] = orc_tree(x + g * GROUP, GROUP);
@@ -186,8 +188,8 @@ int orc_rmsq(const float *h, const float *w, int64_t n, float eps,
 
 /* ------------------------------------------------------------------------
  * exp in binary64 by a fixed method, so that every implementation that
- * follows the same steps gets the same bits (the pages trace swq's Metal
- * mismatch to "Metal's exp", #1440 Change):
+ * follows the same steps gets the same bits (the pages put swq's Metal
+ * mismatch down to Metal's exp, #1440 Change):
  *   t >= 710  -> +inf ;  t <= -746 -> +0 ;  NaN -> NaN
  *   k = rint(t * INV_LN2)                      (nearest, ties to even)
  *   r = (t - k*LN2_HI) - k*LN2_LO              (Cody-Waite reduction)
@@ -222,8 +224,8 @@ double orc_exp(double t) {
 }
 
 /* ------------------------------------------------------------------------
- * swq: SwiGLU over a = [gate (n) | up (n)], "round(silu(a[i]) * a[n+i])"
- * plus group sums (#1440, Change, swq bullet).  Reading: the product is
+ * swq: SwiGLU over a = [gate (n) | up (n)]: silu of each gate value times
+ * its up value, rounded, plus group sums (#1440, Change, swq bullet).  Reading: the product is
  * formed in binary64 and rounded once to binary32:
  *   sig_i = a_i / (1 + E(-a_i))                 (binary64)
  *   o_i   = RN32(sig_i * a_{n+i})               (binary64 product, one
