@@ -17,7 +17,8 @@ import os
 import torch
 
 __all__ = [
-    "FIXED", "FAST", "Q4Error", "Q4Matrix", "q4mv", "q4mv_add", "rmsq", "swq",
+    "FIXED", "FAST", "Q4Error", "Q4Matrix", "q4mv", "q4mv_add", "q4mv_norm",
+    "q4mv_norm_swiglu", "q4mv_norm_argmax", "q4mv_argmax_ws_bytes", "rmsq", "swq",
     "q4_argmax", "q4_argmax_ws_bytes", "q4_embed", "Queue", "Graph", "q4_sync",
     "library_path",
 ]
@@ -48,6 +49,13 @@ _lib = ctypes.CDLL(library_path)
 _SIGS = {
     "q4mv": ([ctypes.POINTER(_Mat), _vp, _vp, _vp, ctypes.c_int, _vp], ctypes.c_int),
     "q4mv_add": ([ctypes.POINTER(_Mat), _vp, _vp, _vp, _vp, ctypes.c_int, _vp], ctypes.c_int),
+    "q4mv_norm": ([ctypes.POINTER(_Mat), _vp, _vp, ctypes.c_float, _vp, _vp, _vp, ctypes.c_int, _vp],
+                  ctypes.c_int),
+    "q4mv_norm_swiglu": ([ctypes.POINTER(_Mat), _vp, _vp, ctypes.c_float, _vp, ctypes.c_int, _vp],
+                         ctypes.c_int),
+    "q4mv_argmax_ws_bytes": ([], ctypes.c_size_t),
+    "q4mv_norm_argmax": ([ctypes.POINTER(_Mat), _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
+                          ctypes.c_size_t, ctypes.c_int, _vp], ctypes.c_int),
     "rmsq": ([_vp, _vp, _i32, ctypes.c_float, _vp, _vp, _vp], ctypes.c_int),
     "swq": ([_vp, _i32, _vp, _vp, ctypes.c_int, _vp], ctypes.c_int),
     "q4_argmax_ws_bytes": ([_i32], ctypes.c_size_t),
@@ -132,27 +140,84 @@ class Q4Matrix:
         return ctypes.byref(self._c)
 
 
-def q4mv(w: Q4Matrix, x: torch.Tensor, xsum: torch.Tensor, y: torch.Tensor | None = None,
+def _opt(t, dtype, numel, what):
+    return None if t is None else _dev(t, dtype, numel, what)
+
+
+def q4mv(w: Q4Matrix, x: torch.Tensor, xsum: torch.Tensor | None, y: torch.Tensor | None = None,
          mode: int = FIXED, stream=None) -> torch.Tensor:
-    """``y = W x`` with the activation group sums ``xsum`` (see q4mv.h)."""
+    """``y = W x`` with the activation group sums ``xsum`` (None: formed in
+    the kernel); see q4mv.h."""
     if y is None:
         y = torch.empty(w.rows, dtype=torch.float32, device=x.device)
     _check("q4mv", _lib.q4mv(w.ref, _dev(x, torch.float32, w.cols, "x"),
-                             _dev(xsum, torch.float32, w.cols // 64, "xsum"),
+                             _opt(xsum, torch.float32, w.cols // 64, "xsum"),
                              _dev(y, torch.float32, w.rows, "y"), mode, _stream(stream)))
     return y
 
 
-def q4mv_add(w: Q4Matrix, x: torch.Tensor, xsum: torch.Tensor, resid: torch.Tensor,
+def q4mv_add(w: Q4Matrix, x: torch.Tensor, xsum: torch.Tensor | None, resid: torch.Tensor,
              y: torch.Tensor | None = None, mode: int = FIXED, stream=None) -> torch.Tensor:
     """``y = resid + W x`` (``y`` may be ``resid``)."""
     if y is None:
         y = torch.empty(w.rows, dtype=torch.float32, device=x.device)
     _check("q4mv_add", _lib.q4mv_add(w.ref, _dev(x, torch.float32, w.cols, "x"),
-                                     _dev(xsum, torch.float32, w.cols // 64, "xsum"),
+                                     _opt(xsum, torch.float32, w.cols // 64, "xsum"),
                                      _dev(resid, torch.float32, w.rows, "resid"),
                                      _dev(y, torch.float32, w.rows, "y"), mode, _stream(stream)))
     return y
+
+
+def q4mv_norm(w: Q4Matrix, h: torch.Tensor, wn: torch.Tensor, eps: float,
+              y: torch.Tensor | None = None, u: torch.Tensor | None = None,
+              usum: torch.Tensor | None = None, mode: int = FIXED, stream=None) -> torch.Tensor:
+    """``y = W rmsq(h, wn)`` in one kernel (2048 columns); optionally also
+    writes rmsq's ``u`` and ``usum``."""
+    if y is None:
+        y = torch.empty(w.rows, dtype=torch.float32, device=h.device)
+    _check("q4mv_norm", _lib.q4mv_norm(w.ref, _dev(h, torch.float32, w.cols, "h"),
+                                       _dev(wn, torch.float32, w.cols, "wn"), float(eps),
+                                       _dev(y, torch.float32, w.rows, "y"),
+                                       _opt(u, torch.float32, w.cols, "u"),
+                                       _opt(usum, torch.float32, w.cols // 64, "usum"),
+                                       mode, _stream(stream)))
+    return y
+
+
+def q4mv_norm_swiglu(w: Q4Matrix, h: torch.Tensor, wn: torch.Tensor, eps: float,
+                     m: torch.Tensor | None = None, mode: int = FIXED,
+                     stream=None) -> torch.Tensor:
+    """``m = swq(W rmsq(h, wn))`` for a matrix of interleaved (gate, up)
+    rows, in one kernel."""
+    if m is None:
+        m = torch.empty(w.rows // 2, dtype=torch.float32, device=h.device)
+    _check("q4mv_norm_swiglu",
+           _lib.q4mv_norm_swiglu(w.ref, _dev(h, torch.float32, w.cols, "h"),
+                                 _dev(wn, torch.float32, w.cols, "wn"), float(eps),
+                                 _dev(m, torch.float32, w.rows // 2, "m"), mode, _stream(stream)))
+    return m
+
+
+def q4mv_argmax_ws_bytes() -> int:
+    return int(_lib.q4mv_argmax_ws_bytes())
+
+
+def q4mv_norm_argmax(w: Q4Matrix, h: torch.Tensor, wn: torch.Tensor, eps: float,
+                     y: torch.Tensor, idx: torch.Tensor, state: torch.Tensor | None = None,
+                     mode: int = FIXED, stream=None) -> torch.Tensor:
+    """``y = W rmsq(h, wn)`` and ``idx[0] = argmax(y)``: the product kernel
+    plus one small reduction kernel; ``state`` is the key workspace
+    (allocated when None)."""
+    if state is None:
+        state = torch.empty((q4mv_argmax_ws_bytes() + 7) // 8, dtype=torch.int64, device=h.device)
+    _check("q4mv_norm_argmax",
+           _lib.q4mv_norm_argmax(w.ref, _dev(h, torch.float32, w.cols, "h"),
+                                 _dev(wn, torch.float32, w.cols, "wn"), float(eps),
+                                 _dev(y, torch.float32, w.rows, "y"),
+                                 _dev(idx, torch.int32, 1, "idx"),
+                                 _dev(state, state.dtype, None, "state"),
+                                 state.numel() * state.element_size(), mode, _stream(stream)))
+    return idx
 
 
 def rmsq(h: torch.Tensor, w: torch.Tensor, eps: float, u: torch.Tensor | None = None,

@@ -8,6 +8,13 @@ One step from token t (the chain has no other state):
                 h     = h + down_l m                   (q4mv_add, in place)
   u, us = rmsq(h, wn_final);  logits = head u;  t' = argmax(logits)
 
+Two ways to run it, with the same bits:
+  fused=False  the steps as listed: 1 + 4 per layer + 4 kernels
+  fused=True   rmsq in the products' prologues, SwiGLU in the gate/up
+               product's epilogue (gate and up rows interleaved), the down
+               product forming its group sums, argmax's first half in the
+               head product's epilogue: 1 + 2 per layer + 2 kernels
+
 The token lives on the device: argmax writes it where the next step's embed
 reads it, so a step captured once as a graph can be replayed token after
 token with a single host wait (for reading the token) per step.
@@ -23,7 +30,7 @@ import numpy as np
 import torch
 
 from . import (FIXED, Graph, Q4Matrix, q4_argmax, q4_argmax_ws_bytes, q4_embed, q4mv,
-               q4mv_add, rmsq, swq)
+               q4mv_add, q4mv_argmax_ws_bytes, q4mv_norm_argmax, q4mv_norm_swiglu, rmsq, swq)
 
 
 def _stack_rows(a: dict, b: dict) -> dict:
@@ -34,10 +41,19 @@ def _stack_rows(a: dict, b: dict) -> dict:
             "cols": a["cols"]}
 
 
+def _interleave_rows(a: dict, b: dict) -> dict:
+    """Rows a0, b0, a1, b1, ... (same shape)."""
+    assert a["cols"] == b["cols"] and a["rows"] == b["rows"]
+    il = lambda x, y: np.stack([x, y], axis=1).reshape(2 * x.shape[0], *x.shape[1:])
+    return {"q": il(a["q"], b["q"]), "s": il(a["s"], b["s"]), "b": il(a["b"], b["b"]),
+            "rows": 2 * a["rows"], "cols": a["cols"]}
+
+
 class DecodeChain:
     def __init__(self, weights: dict, mode: int = FIXED, layers: int | None = None,
-                 device: str = "cuda"):
+                 device: str = "cuda", fused: bool = True):
         self.mode = mode
+        self.fused = fused
         self.hidden = int(weights["hidden"])
         self.inter = int(weights["inter"])
         self.vocab = int(weights["vocab"])
@@ -46,9 +62,10 @@ class DecodeChain:
         f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
         self.layers = []
         for lw in weights["layers"][:L]:
+            gu = (_interleave_rows if fused else _stack_rows)(lw["gate"], lw["up"])
             self.layers.append({
                 "wn": f32(lw["wn"]),
-                "gu": Q4Matrix.from_host(_stack_rows(lw["gate"], lw["up"]), device),
+                "gu": Q4Matrix.from_host(gu, device),
                 "down": Q4Matrix.from_host(lw["down"], device),
             })
         self.wn_final = f32(weights["wn_final"])
@@ -63,7 +80,14 @@ class DecodeChain:
         self.ms = z(self.inter // 64)
         self.logits = z(self.vocab)
         self.ws = z((q4_argmax_ws_bytes(self.vocab) + 7) // 8, torch.int64)
+        self.amax_ws = z((q4mv_argmax_ws_bytes() + 7) // 8, torch.int64)
         self.graph = None
+        # the copies and fills above ran on the current stream; the chain may
+        # run on another one
+        torch.cuda.synchronize()
+
+    def kernels_per_token(self) -> int:
+        return 3 + 2 * len(self.layers) if self.fused else 5 + 4 * len(self.layers)
 
     def bytes_per_token(self) -> int:
         """Algorithmic bytes one step moves: weights and scales of every
@@ -81,6 +105,14 @@ class DecodeChain:
     def enqueue_step(self, stream) -> None:
         """Every kernel of one step, in order, on `stream`."""
         q4_embed(self.head, self.tok, self.h, stream=stream)
+        if self.fused:
+            for lw in self.layers:
+                q4mv_norm_swiglu(lw["gu"], self.h, lw["wn"], self.eps, self.m, mode=self.mode,
+                                 stream=stream)
+                q4mv_add(lw["down"], self.m, None, self.h, self.h, mode=self.mode, stream=stream)
+            q4mv_norm_argmax(self.head, self.h, self.wn_final, self.eps, self.logits, self.tok,
+                             self.amax_ws, mode=self.mode, stream=stream)
+            return
         for lw in self.layers:
             rmsq(self.h, lw["wn"], self.eps, self.u, self.us, stream=stream)
             q4mv(lw["gu"], self.u, self.us, self.a, mode=self.mode, stream=stream)

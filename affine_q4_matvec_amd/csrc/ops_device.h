@@ -1,0 +1,172 @@
+// Device building blocks shared by the standalone producer kernels and the
+// fused q4mv prologues/epilogues: the same code runs in both, so a fused
+// stage produces the bits of the separate one.
+//
+// rmsq and swq follow "Metal: queued rmsq, swq, gdn and atq kernels and a
+// 4-row q4mv, so a decode token is one command buffer with one wait"
+// (#1440), Change (rmsq and swq bullets); greedy argmax its Verification
+// (greedy token ids).  Compiled with -ffp-contract=off.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#pragma clang fp contract(off)
+
+namespace q4 {
+namespace ops {
+
+constexpr int kWave = 64;
+constexpr float kNegZero = -0.0f;
+
+__device__ __forceinline__ float tree8(const float *v) {
+  return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+}
+
+// RMS norm of n values with weights, plus group sums, by one workgroup of
+// blockDim.x = max(64, P/8) threads (P = next power of two >= n, n % 64 ==
+// 0, at most 1024 threads).  Thread t owns the contiguous slots [8t, 8t+8);
+// slots >= n hold -0.0, so the lane and wave butterflies give the canonical
+// tree over the n squares:
+//   ss = T(h*h); ms = ss / n; rho = 1 / sqrt(ms + eps)  (correctly rounded);
+//   u_i = (h_i * rho) * w_i; us_g = T(u[64g .. 64g+63]).
+
+// The first half: rho, in every thread.  The thread's 8 slots of h and of
+// w are loaded together up front (hv, wv) so that their latencies overlap.
+// red is LDS scratch of 17 floats; every thread of the workgroup must call
+// it (two barriers).
+__device__ __forceinline__ float rmsq_rho(const float *__restrict__ h,
+                                          const float *__restrict__ w, int n, float eps,
+                                          float *red, float *hv, float *wv) {
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = t / kWave;
+  const int nw = blockDim.x / kWave;
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int i = 8 * t + k;
+    hv[k] = i < n ? h[i] : 0.0f;
+    wv[k] = i < n ? w[i] : 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = 8 * t + k < n ? hv[k] * hv[k] : kNegZero;
+  float s = tree8(v);
+#pragma unroll
+  for (int m = 1; m < kWave; m *= 2) s = s + __shfl_xor(s, m);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  if (t == 0) {
+    // balanced tree over the (power-of-two many) wave sums
+    for (int m = 1; m < nw; m *= 2)
+      for (int i = 0; i < nw; i += 2 * m) red[i] = red[i] + red[i + m];
+    red[16] = red[0];
+  }
+  __syncthreads();
+  const float ms = red[16] / (float)n;
+  return 1.0f / sqrtf(ms + eps);
+}
+
+// One normalised value: (h * rho) * w.
+__device__ __forceinline__ float rmsq_value(float h, float rho, float w) {
+  const float hr = h * rho;
+  return hr * w;
+}
+
+// The second half: u for the thread's 8 slots and the group sums (8
+// threads per group), stored at u[i + PAD * (i / 32)] (PAD = 0: plain; 4:
+// the padded LDS layout whose 32-value runs start on distinct banks).  u and
+// us may point to global or LDS memory.
+template <int PAD>
+__device__ __forceinline__ void rmsq_u(int n, float rho, const float *hv, const float *wv,
+                                       float *u, float *us) {
+  const int t = threadIdx.x;
+  float uv[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int i = 8 * t + k;
+    uv[k] = i < n ? rmsq_value(hv[k], rho, wv[k]) : kNegZero;
+    if (i < n) u[i + (i >> 5) * PAD] = uv[k];
+  }
+  float gsum = tree8(uv);
+  gsum = gsum + __shfl_xor(gsum, 1);
+  gsum = gsum + __shfl_xor(gsum, 2);
+  gsum = gsum + __shfl_xor(gsum, 4);
+  if ((t & 7) == 0 && 8 * t < n) us[t >> 3] = gsum;
+}
+
+__device__ __forceinline__ void rmsq_block(const float *__restrict__ h,
+                                           const float *__restrict__ w, int n, float eps,
+                                           float *u, float *us, float *red) {
+  float hv[8], wv[8];
+  const float rho = rmsq_rho(h, w, n, eps, red, hv, wv);
+  rmsq_u<0>(n, rho, hv, wv, u, us);
+}
+
+// exp in binary64 by a fixed method (every implementation that follows the
+// same steps gets the same bits):
+//   k = rint(t * INV_LN2); r = (t - k*LN2_HI) - k*LN2_LO;
+//   p = sum_{j<=13} r^j / j! by fused Horner; E = ldexp(p, k);
+//   E = +inf for t >= 710, +0 for t <= -746, NaN for NaN.
+// INV_LN2 = RN64(1/ln 2); LN2_HI = ln 2 truncated to 32 significant bits;
+// LN2_LO = RN64(ln 2 - LN2_HI); 1/j! correctly rounded.
+__device__ __forceinline__ double fixed_exp(double t) {
+  if (t != t) return t;
+  if (t >= 710.0) return __builtin_inf();
+  if (t <= -746.0) return 0.0;
+  const double inv_ln2 = 0x1.71547652b82fep+0;
+  const double ln2_hi = 0x1.62e42fee00000p-1;
+  const double ln2_lo = 0x1.a39ef35793c76p-33;
+  const double k = rint(t * inv_ln2);
+  const double hi = t - k * ln2_hi;
+  const double lo = k * ln2_lo;
+  const double r = hi - lo;
+  double p = 1.0 / 6227020800.0;  // 1/13!
+  p = fma(p, r, 1.0 / 479001600.0);
+  p = fma(p, r, 1.0 / 39916800.0);
+  p = fma(p, r, 1.0 / 3628800.0);
+  p = fma(p, r, 1.0 / 362880.0);
+  p = fma(p, r, 1.0 / 40320.0);
+  p = fma(p, r, 1.0 / 5040.0);
+  p = fma(p, r, 1.0 / 720.0);
+  p = fma(p, r, 1.0 / 120.0);
+  p = fma(p, r, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return ldexp(p, (int)k);
+}
+
+// One SwiGLU output.  Fixed: silu in binary64, a / (1 + E(-a)), times up in
+// binary64, rounded once to binary32.  Fast: binary32 with the hardware exp.
+template <bool FAST>
+__device__ __forceinline__ float swiglu_value(float gate, float up) {
+  if constexpr (!FAST) {
+    const double g = (double)gate;
+    const double sig = g / (1.0 + fixed_exp(-g));
+    return (float)(sig * (double)up);
+  } else {
+    return gate / (1.0f + __expf(-gate)) * up;
+  }
+}
+
+// 64-bit key ordered by (value, -index): the largest key is the lowest index
+// of the largest value; -0 and +0 compare equal; NaN maps to the largest key.
+constexpr unsigned long long kNanKey = ~0ull;
+
+__device__ __forceinline__ unsigned long long argmax_key(float v, int i) {
+  if (v != v) return kNanKey;
+  uint32_t u = __float_as_uint(v);
+  if (v == 0.0f) u = 0u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (unsigned long long)(~(uint32_t)i);
+}
+
+__device__ __forceinline__ int32_t argmax_index(unsigned long long key) {
+  return key == kNanKey ? -1 : (int32_t)(~(uint32_t)(key & 0xFFFFFFFFull));
+}
+
+}  // namespace ops
+}  // namespace q4

@@ -45,24 +45,36 @@ int check_mat(const q4_mat *w) {
   return Q4_OK;
 }
 
-// Checks one product and fills the kernel's view of it.
+// Does the output range [p, p + bytes) overlap the matrix arrays?
+bool overlaps_mat(const void *p, size_t bytes, const q4_mat *w) {
+  const size_t G = (size_t)w->cols / 64;
+  return overlap(p, bytes, w->q, (size_t)w->rows * (size_t)w->cols / 2) ||
+         overlap(p, bytes, w->s, sizeof(float) * G * (size_t)w->rows) ||
+         overlap(p, bytes, w->b, sizeof(float) * G * (size_t)w->rows);
+}
+
+// Checks one product and fills the kernel's view of it.  xsum may be null
+// (the kernel then forms the group sums of x).
 int make_prod(const q4_mat *w, const float *x, const float *xsum, const float *resid, float *y,
               Prod *out) {
   int rc = check_mat(w);
   if (rc != Q4_OK) return rc;
-  if (!x || !xsum || !y) return Q4_EINVAL;
-  if (!aligned(x, 16) || !aligned(xsum, 4) || !aligned(y, 4)) return Q4_EINVAL;
+  if (!x || !y) return Q4_EINVAL;
+  if (!aligned(x, 16) || !aligned(y, 4) || (xsum && !aligned(xsum, 4))) return Q4_EINVAL;
   if (resid && !aligned(resid, 4)) return Q4_EINVAL;
   const size_t G = (size_t)w->cols / 64;
   const size_t ybytes = sizeof(float) * (size_t)w->rows;
   if (overlap(y, ybytes, x, sizeof(float) * (size_t)w->cols) ||
-      overlap(y, ybytes, xsum, sizeof(float) * G) ||
-      overlap(y, ybytes, w->q, (size_t)w->rows * (size_t)w->cols / 2) ||
-      overlap(y, ybytes, w->s, sizeof(float) * G * (size_t)w->rows) ||
-      overlap(y, ybytes, w->b, sizeof(float) * G * (size_t)w->rows))
+      (xsum && overlap(y, ybytes, xsum, sizeof(float) * G)) || overlaps_mat(y, ybytes, w))
     return Q4_EINVAL;
   if (resid && resid != y && overlap(y, ybytes, resid, ybytes)) return Q4_EINVAL;
   *out = Prod{w->q, w->s, w->b, x, xsum, resid, y, w->rows, w->cols};
+  return Q4_OK;
+}
+
+// Checks the inputs of an rmsq prologue over n values.
+int check_norm_inputs(const float *h, const float *wn) {
+  if (!h || !wn || !aligned(h, 16) || !aligned(wn, 16)) return Q4_EINVAL;
   return Q4_OK;
 }
 
@@ -72,7 +84,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_EHIP; }
 // kMaxGroup products per launch).  When the products of a launch together
 // want more workgroups than fit on the device at once, each one's share is
 // cut in proportion (at least one workgroup each).
-int launch_products(const Prod *prods, int count, const Shape &sh, int mode, hipStream_t st) {
+int launch_products(const Prod *prods, int count, const Shape &sh, int mode, hipStream_t st,
+                    const q4::Extra &ex = q4::Extra{}) {
+  if (!q4::shape_supported(sh)) return Q4_EINVAL;
   const int cap = q4::resident_capacity(sh, mode);
   for (int at = 0; at < count; at += q4::kMaxGroup) {
     ProdGroup g;
@@ -96,7 +110,7 @@ int launch_products(const Prod *prods, int count, const Shape &sh, int mode, hip
       g.wg_begin[i + 1] = g.wg_begin[i] + want[i];
     }
     for (int i = g.n; i < q4::kMaxGroup; ++i) g.wg_begin[i + 1] = g.wg_begin[g.n];
-    const int rc = hip_status(q4::launch_q4mv_group(g, sh, mode, st));
+    const int rc = hip_status(q4::launch_q4mv_group(g, sh, mode, ex, st));
     if (rc != Q4_OK) return rc;
   }
   return Q4_OK;
@@ -124,6 +138,10 @@ struct q4_graph {
 
 namespace {
 
+Shape prod_shape(const Prod &p) {
+  return q4::shape_of(p.cols, p.xs ? q4::kProX : q4::kProXsum);
+}
+
 // Launches the open stage: products grouped by kernel shape.
 int flush_stage(q4_queue *q) {
   if (q->stage.empty()) return Q4_OK;
@@ -136,10 +154,10 @@ int flush_stage(q4_queue *q) {
   std::vector<Prod> same;
   for (size_t i = 0; i < q->stage.size(); ++i) {
     if (done[i]) continue;
-    const Shape sh = q4::shape_of(q->stage[i].cols);
+    const Shape sh = prod_shape(q->stage[i]);
     same.clear();
     for (size_t j = i; j < q->stage.size(); ++j) {
-      if (!done[j] && q4::shape_of(q->stage[j].cols) == sh) {
+      if (!done[j] && prod_shape(q->stage[j]) == sh) {
         same.push_back(q->stage[j]);
         done[j] = true;
       }
@@ -166,7 +184,105 @@ int q4mv_add(const q4_mat *w, const float *x, const float *xsum, const float *re
   Prod p;
   const int rc = make_prod(w, x, xsum, resid, y, &p);
   if (rc != Q4_OK) return rc;
-  return launch_products(&p, 1, q4::shape_of(p.cols), mode, static_cast<hipStream_t>(stream));
+  return launch_products(&p, 1, prod_shape(p), mode, static_cast<hipStream_t>(stream));
+}
+
+int q4mv_norm(const q4_mat *w, const float *h, const float *wn, float eps, float *y, float *u,
+              float *usum, int mode, void *stream) {
+  if (mode != Q4_FIXED && mode != Q4_FAST) return Q4_EINVAL;
+  int rc = check_mat(w);
+  if (rc != Q4_OK) return rc;
+  if ((rc = check_norm_inputs(h, wn)) != Q4_OK) return rc;
+  if (!y || !aligned(y, 4) || (!u) != (!usum)) return Q4_EINVAL;
+  if (u && (!aligned(u, 16) || !aligned(usum, 4))) return Q4_EINVAL;
+  const size_t n = (size_t)w->cols, ybytes = sizeof(float) * (size_t)w->rows;
+  const size_t nb = sizeof(float) * n, gb = sizeof(float) * (n / 64);
+  if (overlap(y, ybytes, h, nb) || overlap(y, ybytes, wn, nb) || overlaps_mat(y, ybytes, w))
+    return Q4_EINVAL;
+  if (u && (overlap(u, nb, h, nb) || overlap(u, nb, wn, nb) || overlap(u, nb, y, ybytes) ||
+            overlap(usum, gb, h, nb) || overlap(usum, gb, wn, nb) || overlap(usum, gb, u, nb) ||
+            overlap(usum, gb, y, ybytes) || overlaps_mat(u, nb, w) || overlaps_mat(usum, gb, w)))
+    return Q4_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (w->cols != 2048) {
+    // no fused kernel for this width: the norm, then the product
+    if (!u) return Q4_EINVAL;
+    if (w->cols > Q4_MAX_RMSQ_N) return Q4_EINVAL;
+    rc = rmsq(h, wn, w->cols, eps, u, usum, stream);
+    if (rc != Q4_OK) return rc;
+    return q4mv(w, u, usum, y, mode, stream);
+  }
+  Prod p{w->q, w->s, w->b, nullptr, nullptr, nullptr, y, w->rows, w->cols};
+  q4::Extra ex{};
+  ex.h = h;
+  ex.wn = wn;
+  ex.eps = eps;
+  ex.u_out = u;
+  ex.us_out = usum;
+  return launch_products(&p, 1, q4::shape_of(w->cols, q4::kProNorm, q4::kEpiStore), mode, st, ex);
+}
+
+int q4mv_norm_swiglu(const q4_mat *w, const float *h, const float *wn, float eps, float *m,
+                     int mode, void *stream) {
+  if (mode != Q4_FIXED && mode != Q4_FAST) return Q4_EINVAL;
+  int rc = check_mat(w);
+  if (rc != Q4_OK) return rc;
+  if ((rc = check_norm_inputs(h, wn)) != Q4_OK) return rc;
+  if (w->cols != 2048 || w->rows % 2 != 0) return Q4_EINVAL;
+  if (!m || !aligned(m, 4)) return Q4_EINVAL;
+  const size_t nb = sizeof(float) * 2048, mb = sizeof(float) * (size_t)(w->rows / 2);
+  if (overlap(m, mb, h, nb) || overlap(m, mb, wn, nb) || overlaps_mat(m, mb, w)) return Q4_EINVAL;
+  Prod p{w->q, w->s, w->b, nullptr, nullptr, nullptr, nullptr, w->rows, w->cols};
+  q4::Extra ex{};
+  ex.h = h;
+  ex.wn = wn;
+  ex.eps = eps;
+  ex.m_out = m;
+  return launch_products(&p, 1, q4::shape_of(2048, q4::kProNorm, q4::kEpiSwiglu), mode,
+                         static_cast<hipStream_t>(stream), ex);
+}
+
+// One 8-byte key per workgroup of the fused argmax launch.
+constexpr int32_t kArgmaxMaxWorkgroups = 4096;
+
+size_t q4mv_argmax_ws_bytes(void) { return sizeof(unsigned long long) * kArgmaxMaxWorkgroups; }
+
+int q4mv_norm_argmax(const q4_mat *w, const float *h, const float *wn, float eps, float *y,
+                     int32_t *idx, void *ws, size_t ws_bytes, int mode, void *stream) {
+  if (mode != Q4_FIXED && mode != Q4_FAST) return Q4_EINVAL;
+  int rc = check_mat(w);
+  if (rc != Q4_OK) return rc;
+  if ((rc = check_norm_inputs(h, wn)) != Q4_OK) return rc;
+  if (w->cols != 2048) return Q4_EINVAL;
+  if (!y || !idx || !ws || !aligned(y, 4) || !aligned(idx, 4) || !aligned(ws, 8))
+    return Q4_EINVAL;
+  if (ws_bytes < sizeof(unsigned long long)) return Q4_EINVAL;
+  const size_t nb = sizeof(float) * 2048, yb = sizeof(float) * (size_t)w->rows;
+  if (overlap(y, yb, h, nb) || overlap(y, yb, wn, nb) || overlaps_mat(y, yb, w) ||
+      overlap(idx, 4, y, yb) || overlap(idx, 4, h, nb) || overlap(idx, 4, wn, nb) ||
+      overlap(ws, ws_bytes, y, yb) || overlap(ws, ws_bytes, idx, 4) ||
+      overlap(ws, ws_bytes, h, nb) || overlap(ws, ws_bytes, wn, nb) || overlaps_mat(idx, 4, w) ||
+      overlaps_mat(ws, ws_bytes, w))
+    return Q4_EINVAL;
+  const Shape sh = q4::shape_of(2048, q4::kProNorm, q4::kEpiArgmax);
+  long long nwg = q4::workgroups_for(sh, w->rows, mode);
+  const long long slots = (long long)(ws_bytes / sizeof(unsigned long long));
+  if (nwg > slots) nwg = slots;
+  if (nwg > kArgmaxMaxWorkgroups) nwg = kArgmaxMaxWorkgroups;
+  ProdGroup g;
+  memset(&g, 0, sizeof(g));
+  g.n = 1;
+  g.p[0] = Prod{w->q, w->s, w->b, nullptr, nullptr, nullptr, y, w->rows, w->cols};
+  for (int i = 1; i <= q4::kMaxGroup; ++i) g.wg_begin[i] = (int32_t)nwg;
+  q4::Extra ex{};
+  ex.h = h;
+  ex.wn = wn;
+  ex.eps = eps;
+  ex.amax = static_cast<unsigned long long *>(ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = hip_status(q4::launch_q4mv_group(g, sh, mode, ex, st));
+  if (rc != Q4_OK) return rc;
+  return hip_status(q4::launch_argmax_final(ex.amax, (int32_t)nwg, idx, st));
 }
 
 int rmsq(const float *h, const float *w, int32_t n, float eps, float *u, float *usum,
@@ -254,9 +370,9 @@ int q4mv_queue(q4_queue *q, const q4_mat *w, const float *x, const float *xsum, 
     for (const Prod &o : q->stage) {
       const size_t ob = sizeof(float) * (size_t)o.rows;
       if (overlap(p.y, yb, o.x, sizeof(float) * (size_t)o.cols) ||
-          overlap(p.y, yb, o.xs, sizeof(float) * (size_t)(o.cols / 64)) ||
+          (o.xs && overlap(p.y, yb, o.xs, sizeof(float) * (size_t)(o.cols / 64))) ||
           overlap(o.y, ob, p.x, sizeof(float) * (size_t)p.cols) ||
-          overlap(o.y, ob, p.xs, sizeof(float) * (size_t)(p.cols / 64)) ||
+          (p.xs && overlap(o.y, ob, p.xs, sizeof(float) * (size_t)(p.cols / 64))) ||
           overlap(o.y, ob, p.y, yb))
         return Q4_EINVAL;
     }

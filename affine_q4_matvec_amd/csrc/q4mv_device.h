@@ -242,28 +242,6 @@ __device__ __forceinline__ void select_product(const ProdGroup &grp, Prod &P, in
   }
 }
 
-// The 32 activations of chunk `chunk` (columns 32 chunk .. 32 chunk + 31)
-// and the group sum of its group.  Inactive lanes get zeros.
-__device__ __forceinline__ void load_x_chunk(const Prod &P, int chunk, bool active, float *xv,
-                                             float &xsv) {
-  if (active) {
-    const float4 *xp = reinterpret_cast<const float4 *>(P.x + 32 * chunk);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float4 v = xp[k];
-      xv[4 * k + 0] = v.x;
-      xv[4 * k + 1] = v.y;
-      xv[4 * k + 2] = v.z;
-      xv[4 * k + 3] = v.w;
-    }
-    xsv = P.xs[chunk >> 1];
-  } else {
-#pragma unroll
-    for (int k = 0; k < 32; ++k) xv[k] = 0.0f;
-    xsv = 0.0f;
-  }
-}
-
 // Pre-scales the lane's activations for the pair decode when every
 // activation of the wave is below 2^118 in magnitude (NaN counts as large);
 // returns whether the wave may use the pair decode.

@@ -29,21 +29,45 @@ struct ProdGroup {
   int32_t n;
 };
 
+// Stages fused into a product's kernel.
+constexpr int kProX = 0;      // x and its group sums are inputs
+constexpr int kProXsum = 1;   // x is an input, its group sums formed in the kernel
+constexpr int kProNorm = 2;   // x = rmsq(h, wn) formed in the kernel (2048 columns)
+constexpr int kEpiStore = 0;  // y[r] = (res[r] +) row sum
+constexpr int kEpiSwiglu = 1; // (gate, up) row pairs -> m[r/2] = SwiGLU
+constexpr int kEpiArgmax = 2; // y stored, and one argmax key per workgroup
+
+// Inputs and outputs of the fused stages (unused fields are ignored).
+struct Extra {
+  const float *h;            // kProNorm: [cols] values to normalise
+  const float *wn;           // kProNorm: [cols] norm weights
+  float eps;                 // kProNorm
+  float *u_out;              // kProNorm, optional: [cols] normalised x
+  float *us_out;             //   and its [cols/64] group sums
+  float *m_out;              // kEpiSwiglu: [rows/2]
+  unsigned long long *amax;  // kEpiArgmax: [workgroups] one key per workgroup
+};
+
 // Kernel shape of a product: rows of exactly 32 groups (2048 columns) take
 // one wave each (row64); rows of fewer groups are covered by one segment of
 // `lpr` lanes of a wave (lpr = 2..64); wider rows are split into `passes`
-// 2048-column passes, one wave each, combined through LDS.
+// 2048-column passes, one wave each, combined through LDS.  `pro` and `epi`
+// name the fused stages (kProNorm and the epilogues other than kEpiStore
+// exist for row64 only).
 struct Shape {
   enum Kind : int32_t { kRow64 = 0, kSeg = 1, kSplit = 2 };
   int32_t kind;
   int32_t lpr;     // lanes per row segment (seg)
   int32_t passes;  // waves per row (split)
+  int32_t pro;
+  int32_t epi;
   bool operator==(const Shape &o) const {
-    return kind == o.kind && lpr == o.lpr && passes == o.passes;
+    return kind == o.kind && lpr == o.lpr && passes == o.passes && pro == o.pro && epi == o.epi;
   }
 };
 
-Shape shape_of(int32_t cols);
+Shape shape_of(int32_t cols, int pro = kProX, int epi = kEpiStore);
+bool shape_supported(const Shape &sh);
 // Workgroups a product of this shape gets when launched alone.
 int32_t workgroups_for(const Shape &sh, int32_t rows, int mode);
 // Workgroups of this shape that fit on the current device at once (0: no
@@ -52,13 +76,17 @@ int32_t resident_capacity(const Shape &sh, int mode);
 
 // Launchers.  They assume validated arguments and return the HIP status of
 // the launch.
-hipError_t launch_q4mv_group(const ProdGroup &g, const Shape &sh, int mode, hipStream_t st);
+hipError_t launch_q4mv_group(const ProdGroup &g, const Shape &sh, int mode, const Extra &ex,
+                             hipStream_t st);
 hipError_t launch_rmsq(const float *h, const float *w, int32_t n, float eps, float *u,
                        float *us, hipStream_t st);
 hipError_t launch_swq(const float *a, int32_t n, float *o, float *os, int mode,
                       hipStream_t st);
 size_t argmax_ws_bytes(int32_t n);
 hipError_t launch_argmax(const float *v, int32_t n, int32_t *idx, void *ws, hipStream_t st);
+// The last step of an argmax: the largest of `nkeys` keys -> *idx.
+hipError_t launch_argmax_final(const unsigned long long *keys, int32_t nkeys, int32_t *idx,
+                               hipStream_t st);
 hipError_t launch_embed(const Prod &w, const int32_t *tok, float *e, hipStream_t st);
 
 }  // namespace q4

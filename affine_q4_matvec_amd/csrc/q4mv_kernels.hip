@@ -12,27 +12,34 @@
 // Three kernel shapes, all reading each code byte from HBM once:
 //   row64  rows of exactly 2048 columns (32 groups): one wave per row,
 //          lane l owns columns [32l, 32l+32) and keeps their activations in
-//          registers across all rows it visits (the pages' "4-row" sharing of
+//          registers across all rows it visits (the pages' 4-row sharing of
 //          one activation group by several rows, taken to every row of the
 //          wave); one 16-byte buffer load per lane and row.
 //   seg    rows of at most 31 groups: 64/LPR row segments of LPR lanes.
 //   split  rows of more than 32 groups: one wave per 2048-column pass, pass
 //          sums combined through LDS with the tree over passes.
+//
+// Fused stages (one kernel instead of two or three; same bits as the
+// separate kernels, because the same code computes them):
+//   prologue kProXsum    the group sums of x are formed in the kernel (each
+//                        lane pair: T over its 32 + 32 activations)
+//   prologue kProNorm    x = rmsq(h, wn): the workgroup forms rho, each lane
+//                        its own 32 normalised activations and group sum
+//   epilogue kEpiSwiglu  rows come in (gate, up) pairs; the pair's outputs
+//                        go through swq's SwiGLU into m[r/2]
+//   epilogue kEpiArgmax  greedy argmax of y: each workgroup writes the key
+//                        of its best row; a one-workgroup kernel picks the
+//                        largest key
 #include <atomic>
 
+#include "ops_device.h"
 #include "q4mv_device.h"
 
 #ifndef Q4_ROW64_R
 #define Q4_ROW64_R 4  // rows per wave iteration (loads in flight per lane)
 #endif
 #ifndef Q4_ROW64_MAX_WG
-#define Q4_ROW64_MAX_WG 2048  // workgroups of 4 waves (grid-stride beyond)
-#endif
-#ifndef Q4_ROW64_PREFETCH
-#define Q4_ROW64_PREFETCH 0  // issue the next block's loads before summing
-#endif
-#ifndef Q4_ROW64_INTERLEAVE
-#define Q4_ROW64_INTERLEAVE 1  // round-robin row blocks instead of ranges
+#define Q4_ROW64_MAX_WG 2048  // cap when the occupancy query is unavailable
 #endif
 #ifndef Q4_ROW64_OCC_PCT
 #define Q4_ROW64_OCC_PCT 100  // share of the resident workgroups launched
@@ -54,6 +61,43 @@ using namespace dev;
 
 constexpr int kSegR = 4;
 constexpr int kThreads = 256;
+static_assert(Q4_ROW64_R % 2 == 0, "the SwiGLU epilogue pairs rows within a block");
+
+// Group sum of the lane pair's 64 activations: T over the lane's 32
+// (balanced) plus the partner's 32.
+__device__ __forceinline__ float pair_group_sum(const float *xv) {
+  const float L =
+      (ops::tree8(xv) + ops::tree8(xv + 8)) + (ops::tree8(xv + 16) + ops::tree8(xv + 24));
+  return L + dpp<kDppQuadXor1>(L);
+}
+
+__device__ __forceinline__ void load_x_values(const float *x, bool active, float *xv) {
+  if (active) {
+    const float4 *xp = reinterpret_cast<const float4 *>(x);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 v = xp[k];
+      xv[4 * k + 0] = v.x;
+      xv[4 * k + 1] = v.y;
+      xv[4 * k + 2] = v.z;
+      xv[4 * k + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) xv[k] = 0.0f;
+  }
+}
+
+// Activations of `chunk` and its group sum for prologues kProX / kProXsum.
+template <int PRO>
+__device__ __forceinline__ void chunk_inputs(const Prod &P, int chunk, bool active, float *xv,
+                                             float &xsv) {
+  load_x_values(P.x + 32 * chunk, active, xv);
+  if constexpr (PRO == kProXsum)
+    xsv = pair_group_sum(xv);
+  else
+    xsv = active ? P.xs[chunk >> 1] : 0.0f;
+}
 
 // ---------------------------------------------------------------------------
 // row64
@@ -81,102 +125,163 @@ __device__ __forceinline__ void row64_load(const Prod &P, int r0, int nrows, uin
   }
 }
 
-// Sums the rows of a loaded block and stores them (lane 63 holds the sums).
-template <int R, bool FAST, bool PAIRS>
-__device__ __forceinline__ void row64_finish(const Prod &P, int r0, int nrows, const float *xv,
-                                             float xsv, int lane, const Row64Block<R> &blk) {
+// (gate, up) pairs waiting for their SwiGLU: lane k of a wave holds pair k
+// of the current batch.  The pairs come out of the row sums one or two per
+// block, but the SwiGLU costs the same instructions for 1 pair as for 64, so
+// a wave evaluates them in batches of up to 64.
+struct SwigluBatch {
+  float gate = 0.0f, up = 0.0f;
+  int out = -1;  // index into m, -1 for an empty slot
+  int count = 0; // pairs held (wave-uniform)
+};
+
+template <bool FAST>
+__device__ __forceinline__ void swiglu_flush(const Extra &ex, SwigluBatch &b) {
+  if (b.count == 0) return;
+  if (b.out >= 0) ex.m_out[b.out] = ops::swiglu_value<FAST>(b.gate, b.up);
+  b.out = -1;
+  b.count = 0;
+}
+
+// Appends the pair (gate, up) for m[out], both held by lane 63, to slot
+// b.count (lane b.count takes them).
+template <bool FAST>
+__device__ __forceinline__ void swiglu_push(const Extra &ex, SwigluBatch &b, int lane, float gate,
+                                            float up, int out) {
+  const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gate), kWave - 1));
+  const float u = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(up), kWave - 1));
+  const bool mine = lane == b.count;
+  b.gate = mine ? g : b.gate;
+  b.up = mine ? u : b.up;
+  b.out = mine ? out : b.out;
+  b.count = b.count + 1;
+  if (b.count == kWave) swiglu_flush<FAST>(ex, b);
+}
+
+// Blocks of R rows dealt round-robin to the waves: r0, r0 + stride, ...
+// Each block is loaded at the top of its iteration (issuing the next
+// block's loads while summing the current one would keep two blocks of
+// registers live); with PRELOAD, `a` holds the first block's loads on entry.
+// Greedy pick over the rows a wave has summed.
+struct RunningMax {
+  float value = 0.0f;
+  int index = -1;  // -1: no row yet
+  bool nan = false;
+  __device__ unsigned long long key() const {
+    if (nan) return ops::kNanKey;
+    return index < 0 ? 0ull : ops::argmax_key(value, index);
+  }
+};
+
+template <int R, bool FAST, bool PAIRS, int EPI, bool PRELOAD>
+__device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, const float *xv,
+                                           float xsv, int lane, int r0, int stride,
+                                           Row64Block<R> &a, RunningMax &best) {
+  const uint32_t voff_q = 16u * lane;
+  const uint32_t voff_g = 4u * (lane >> 1);
+  const int end = P.rows;
   const bool odd = lane & 1;
   const int negz = neg_zero_reg();
-  float tot[R];
+  SwigluBatch batch;
+  for (int r = r0; r < end; r += stride) {
+    const int nrows = min(R, end - r);
+    if (!PRELOAD || r != r0) row64_load<R>(P, r, nrows, voff_q, voff_g, a);
+    float tot[R];
 #pragma unroll
-  for (int j = 0; j < R; ++j)
-    tot[j] = wave_sum_lane63(
-        group_term<FAST, PAIRS>(blk.cw[j], xv, blk.sv[j], blk.bv[j], xsv, true, odd), negz);
-  if (lane == kWave - 1) {
+    for (int j = 0; j < R; ++j)
+      tot[j] = wave_sum_lane63(
+          group_term<FAST, PAIRS>(a.cw[j], xv, a.sv[j], a.bv[j], xsv, true, odd), negz);
+    if constexpr (EPI == kEpiSwiglu) {
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      if (j < nrows) {
-        float v = tot[j];
-        if (P.res) v = P.res[r0 + j] + v;
-        P.y[r0 + j] = v;
+      for (int j = 0; j + 1 < R; j += 2)
+        if (j + 1 < nrows) swiglu_push<FAST>(ex, batch, lane, tot[j], tot[j + 1], (r + j) >> 1);
+    } else if (lane == kWave - 1) {
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        if (j < nrows) {
+          float v = tot[j];
+          if (P.res) v = P.res[r + j] + v;
+          P.y[r + j] = v;
+          if constexpr (EPI == kEpiArgmax) {
+            // rows arrive in increasing order: strictly greater keeps the
+            // lowest index of equal values (and -0 == +0)
+            const bool gt = (v > best.value) || best.index < 0;
+            best.value = gt ? v : best.value;
+            best.index = gt ? r + j : best.index;
+            best.nan |= v != v;
+          }
+        }
       }
     }
   }
+  if constexpr (EPI == kEpiSwiglu) swiglu_flush<FAST>(ex, batch);
 }
 
-// Rows [begin, end) in blocks of R, or (interleaved) blocks first,
-// first + step, ... of R rows.  With PREFETCH the loads of the next block
-// are issued before the current block is summed (two register sets used in
-// turn, so no copies).
-template <int R, bool FAST, bool PAIRS>
-__device__ __forceinline__ void row64_rows(const Prod &P, const float *xv, float xsv, int lane,
-                                           int begin, int end, int stride) {
-  const uint32_t voff_q = 16u * lane;
-  const uint32_t voff_g = 4u * (lane >> 1);
-  auto count = [&](int r0) { return min(R, end - r0); };
-#if Q4_ROW64_PREFETCH
-  Row64Block<R> a, b;
-  int r0 = begin;
-  if (r0 >= end) return;
-  row64_load<R>(P, r0, count(r0), voff_q, voff_g, a);
-  while (true) {
-    const int r1 = r0 + stride;
-    if (r1 < end) row64_load<R>(P, r1, count(r1), voff_q, voff_g, b);
-    row64_finish<R, FAST, PAIRS>(P, r0, count(r0), xv, xsv, lane, a);
-    if (r1 >= end) break;
-    const int r2 = r1 + stride;
-    if (r2 < end) row64_load<R>(P, r2, count(r2), voff_q, voff_g, a);
-    row64_finish<R, FAST, PAIRS>(P, r1, count(r1), xv, xsv, lane, b);
-    if (r2 >= end) break;
-    r0 = r2;
-  }
-#else
-  for (int r0 = begin; r0 < end; r0 += stride) {
-    Row64Block<R> a;
-    row64_load<R>(P, r0, count(r0), voff_q, voff_g, a);
-    row64_finish<R, FAST, PAIRS>(P, r0, count(r0), xv, xsv, lane, a);
-  }
-#endif
-}
-
-// Rows [begin, end) of part `k` when `rows` are split into `parts` balanced
-// contiguous ranges.
-__device__ __forceinline__ void balanced_range(int rows, int k, int parts, int &begin, int &end) {
-  begin = (int)(((long long)rows * k) / parts);
-  end = (int)(((long long)rows * (k + 1)) / parts);
-}
-
-template <int R, bool FAST>
-__global__ __launch_bounds__(kThreads) void q4mv_row64_kernel(ProdGroup grp) {
+// PRELOAD: issue the first block's loads before the activations are formed
+// (for launches where every wave has one block: the loads' latency then
+// overlaps the prologue).  Without it the kernel needs fewer registers.
+template <int R, bool FAST, int PRO, int EPI, bool PRELOAD>
+__global__ __launch_bounds__(kThreads) void q4mv_row64_kernel(ProdGroup grp, Extra ex) {
   Prod P;
   int lw = 0, nwg = 1;
   select_product(grp, P, lw, nwg);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = wave_index();
   const int wpg = kThreads / kWave;
+  const int first = (lw * wpg + wave) * R, stride = nwg * wpg * R;
+
+  Row64Block<R> a;
+  if (PRELOAD && first < P.rows)
+    row64_load<R>(P, first, min(R, P.rows - first), 16u * lane, 4u * (lane >> 1), a);
+
   float xv[32];
   float xsv;
-  load_x_chunk(P, lane, true, xv, xsv);
-#if Q4_ROW64_INTERLEAVE
-  // blocks of R rows dealt round-robin to the waves
-  const int begin = (lw * wpg + wave) * R, end = P.rows, stride = nwg * wpg * R;
-#else
-  // each wave streams one contiguous, balanced range of rows
-  int begin, end;
-  balanced_range(P.rows, lw * wpg + wave, nwg * wpg, begin, end);
-  const int stride = R;
-#endif
+  if constexpr (PRO == kProNorm) {
+    // rmsq over the workgroup into LDS (4 floats of padding after every 32,
+    // so that the lanes' 16-byte reads of their 32 values hit distinct banks)
+    __shared__ float red[17];
+    __shared__ float su[2048 + 2048 / 8];
+    __shared__ float sus[32];
+    float hv[8], wv[8];
+    const float rho = ops::rmsq_rho(ex.h, ex.wn, 2048, ex.eps, red, hv, wv);
+    ops::rmsq_u<4>(2048, rho, hv, wv, su, sus);
+    __syncthreads();
+    if (lw == 0 && ex.u_out) {  // the first workgroup also publishes u
+      for (int i = threadIdx.x; i < 2048; i += kThreads) ex.u_out[i] = su[i + (i >> 5) * 4];
+      if (threadIdx.x < 32) ex.us_out[threadIdx.x] = sus[threadIdx.x];
+    }
+    load_x_values(su + 36 * lane, true, xv);
+    xsv = sus[lane >> 1];
+  } else {
+    chunk_inputs<PRO>(P, lane, true, xv, xsv);
+  }
+
+  RunningMax best;
   if (prescale_for_pairs(xv))
-    row64_rows<R, FAST, true>(P, xv, xsv, lane, begin, end, stride);
+    row64_rows<R, FAST, true, EPI, PRELOAD>(P, ex, xv, xsv, lane, first, stride, a, best);
   else
-    row64_rows<R, FAST, false>(P, xv, xsv, lane, begin, end, stride);
+    row64_rows<R, FAST, false, EPI, PRELOAD>(P, ex, xv, xsv, lane, first, stride, a, best);
+
+  if constexpr (EPI == kEpiArgmax) {
+    // one key per workgroup; a second kernel reduces them (a single counter
+    // or maximum shared by every workgroup would serialise their atomics)
+    __shared__ unsigned long long wbest[kThreads / kWave];
+    if (lane == kWave - 1) wbest[wave] = best.key();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long k = wbest[0];
+#pragma unroll
+      for (int i = 1; i < kThreads / kWave; ++i) k = wbest[i] > k ? wbest[i] : k;
+      ex.amax[lw] = k;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
 // seg: rows of at most 31 groups.  A wave holds 64/LPR row segments of LPR
 // lanes; lane `chunk` of a segment owns columns [32 chunk, 32 chunk + 32).
 // ---------------------------------------------------------------------------
-template <int LPR, int R, bool FAST>
+template <int LPR, int R, bool FAST, int PRO>
 __global__ __launch_bounds__(kThreads) void q4mv_seg_kernel(ProdGroup grp) {
   Prod P;
   int lw = 0, nwg = 1;
@@ -196,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void q4mv_seg_kernel(ProdGroup grp) {
 
   float xv[32];
   float xsv;
-  load_x_chunk(P, chunk, active, xv, xsv);
+  chunk_inputs<PRO>(P, chunk, active, xv, xsv);
 
   const int waves_total = nwg * wpg;
   for (int rb = lw * wpg + wave; rb * RB < P.rows; rb += waves_total) {
@@ -239,40 +344,51 @@ __global__ __launch_bounds__(kThreads) void q4mv_seg_kernel(ProdGroup grp) {
 // first wave combines a row's pass sums with a -0-padded balanced tree over
 // PP = next power of two >= passes, which is T over the passes.
 // ---------------------------------------------------------------------------
-template <int PP, int R, bool FAST, bool PAIRS>
-__device__ __forceinline__ void split_rows(const Prod &P, const float *xv, float xsv, int lane,
-                                           int wave, int passes, int lw, int nwg,
-                                           float (*part)[16]) {
+template <int R>
+struct SplitBlock {
+  u32x4 cw[R];
+  float sv[R], bv[R];
+};
+
+template <int R>
+__device__ __forceinline__ void split_load(const Prod &P, int r0, int nrows, uint32_t voff_q,
+                                           uint32_t voff_g, SplitBlock<R> &blk) {
   const int G = P.cols >> 6;
   const uint32_t row_bytes = (uint32_t)P.cols / 2;
   const uint32_t group_bytes = 4u * G;
+  const auto qr = buffer(P.q + (size_t)r0 * (P.cols >> 3), nrows * row_bytes);
+  const auto sr = buffer(P.s + (size_t)r0 * G, nrows * group_bytes);
+  const auto br = buffer(P.b + (size_t)r0 * G, nrows * group_bytes);
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    blk.cw[j] = load_codes(qr, voff_q, j * row_bytes);
+    blk.sv[j] = load_f32(sr, voff_g, j * group_bytes);
+    blk.bv[j] = load_f32(br, voff_g, j * group_bytes);
+  }
+}
+
+template <int PP, int R, bool FAST, bool PAIRS>
+__device__ __forceinline__ void split_rows(const Prod &P, const float *xv, float xsv, int lane,
+                                           int wave, int passes, int begin, int end,
+                                           SplitBlock<R> &a, float (*part)[16]) {
+  const int G = P.cols >> 6;
   const int chunk = wave * kWave + lane;
   const bool active = chunk < 2 * G;
   const bool odd = lane & 1;
   const uint32_t voff_q = 16u * chunk;
   const uint32_t voff_g = 4u * (chunk >> 1);
-  int begin, end;  // one contiguous, balanced range of rows per workgroup
-  balanced_range(P.rows, lw, nwg, begin, end);
+  const int negz = neg_zero_reg();
+  // `a` holds the loads of the first block on entry
   for (int r0 = begin; r0 < end; r0 += R) {
     const int nrows = min(R, end - r0);
-    const auto qr = buffer(P.q + (size_t)r0 * (P.cols >> 3), nrows * row_bytes);
-    const auto sr = buffer(P.s + (size_t)r0 * G, nrows * group_bytes);
-    const auto br = buffer(P.b + (size_t)r0 * G, nrows * group_bytes);
-    u32x4 cw[R];
-    float sv[R], bv[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      cw[j] = load_codes(qr, voff_q, j * row_bytes);
-      sv[j] = load_f32(sr, voff_g, j * group_bytes);
-      bv[j] = load_f32(br, voff_g, j * group_bytes);
-    }
-    const int negz = neg_zero_reg();
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const float tot = wave_sum_lane63(
-          group_term<FAST, PAIRS>(cw[j], xv, sv[j], bv[j], xsv, active, odd), negz);
+          group_term<FAST, PAIRS>(a.cw[j], xv, a.sv[j], a.bv[j], xsv, active, odd), negz);
       if (lane == kWave - 1) part[j][wave] = tot;
     }
+    const int r1 = r0 + R;
+    if (r1 < end) split_load<R>(P, r1, min(R, end - r1), voff_q, voff_g, a);
     __syncthreads();
     if (wave == 0 && lane < R) {
       float v[PP];
@@ -292,7 +408,14 @@ __device__ __forceinline__ void split_rows(const Prod &P, const float *xv, float
   }
 }
 
-template <int PP, int R, bool FAST>
+// Rows [begin, end) of part `k` when `rows` are split into `parts` balanced
+// contiguous ranges.
+__device__ __forceinline__ void balanced_range(int rows, int k, int parts, int &begin, int &end) {
+  begin = (int)(((long long)rows * k) / parts);
+  end = (int)(((long long)rows * (k + 1)) / parts);
+}
+
+template <int PP, int R, bool FAST, int PRO>
 __global__ __launch_bounds__(1024) void q4mv_split_kernel(ProdGroup grp) {
   Prod P;
   int lw = 0, nwg = 1;
@@ -303,9 +426,17 @@ __global__ __launch_bounds__(1024) void q4mv_split_kernel(ProdGroup grp) {
   const int passes = blockDim.x / kWave;
   const int chunk = wave * kWave + lane;
   const bool active = chunk < 2 * G;
+  int begin, end;  // one contiguous, balanced range of rows per workgroup
+  balanced_range(P.rows, lw, nwg, begin, end);
+
+  // the first block's loads go out before the activations are ready
+  SplitBlock<R> a;
+  if (begin < end)
+    split_load<R>(P, begin, min(R, end - begin), 16u * chunk, 4u * (chunk >> 1), a);
+
   float xv[32];
   float xsv;
-  load_x_chunk(P, chunk, active, xv, xsv);
+  chunk_inputs<PRO>(P, chunk, active, xv, xsv);
   // one decode choice for the whole workgroup (the loop has barriers)
   bool large = false;
 #pragma unroll
@@ -315,9 +446,9 @@ __global__ __launch_bounds__(1024) void q4mv_split_kernel(ProdGroup grp) {
     const float scale = 1.0f / fp8_unit();
 #pragma unroll
     for (int k = 0; k < 32; ++k) xv[k] = xv[k] * scale;
-    split_rows<PP, R, FAST, true>(P, xv, xsv, lane, wave, passes, lw, nwg, part);
+    split_rows<PP, R, FAST, true>(P, xv, xsv, lane, wave, passes, begin, end, a, part);
   } else {
-    split_rows<PP, R, FAST, false>(P, xv, xsv, lane, wave, passes, lw, nwg, part);
+    split_rows<PP, R, FAST, false>(P, xv, xsv, lane, wave, passes, begin, end, a, part);
   }
 }
 
@@ -327,56 +458,97 @@ int next_pow2(int v) {
   return p;
 }
 
-template <bool FAST>
+template <bool FAST, int PRO>
 hipError_t launch_seg(const ProdGroup &g, int lpr, hipStream_t st) {
   const dim3 grid(g.wg_begin[g.n]), block(kThreads);
   switch (lpr) {
-    case 2: hipLaunchKernelGGL((q4mv_seg_kernel<2, kSegR, FAST>), grid, block, 0, st, g); break;
-    case 4: hipLaunchKernelGGL((q4mv_seg_kernel<4, kSegR, FAST>), grid, block, 0, st, g); break;
-    case 8: hipLaunchKernelGGL((q4mv_seg_kernel<8, kSegR, FAST>), grid, block, 0, st, g); break;
-    case 16: hipLaunchKernelGGL((q4mv_seg_kernel<16, kSegR, FAST>), grid, block, 0, st, g); break;
-    case 32: hipLaunchKernelGGL((q4mv_seg_kernel<32, kSegR, FAST>), grid, block, 0, st, g); break;
-    case 64: hipLaunchKernelGGL((q4mv_seg_kernel<64, kSegR, FAST>), grid, block, 0, st, g); break;
+    case 2: hipLaunchKernelGGL((q4mv_seg_kernel<2, kSegR, FAST, PRO>), grid, block, 0, st, g); break;
+    case 4: hipLaunchKernelGGL((q4mv_seg_kernel<4, kSegR, FAST, PRO>), grid, block, 0, st, g); break;
+    case 8: hipLaunchKernelGGL((q4mv_seg_kernel<8, kSegR, FAST, PRO>), grid, block, 0, st, g); break;
+    case 16: hipLaunchKernelGGL((q4mv_seg_kernel<16, kSegR, FAST, PRO>), grid, block, 0, st, g); break;
+    case 32: hipLaunchKernelGGL((q4mv_seg_kernel<32, kSegR, FAST, PRO>), grid, block, 0, st, g); break;
+    case 64: hipLaunchKernelGGL((q4mv_seg_kernel<64, kSegR, FAST, PRO>), grid, block, 0, st, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <bool FAST>
+template <bool FAST, int PRO>
 hipError_t launch_split(const ProdGroup &g, int passes, hipStream_t st) {
   const dim3 grid(g.wg_begin[g.n]), block(kWave * passes);
   switch (next_pow2(passes)) {
-    case 2: hipLaunchKernelGGL((q4mv_split_kernel<2, Q4_SPLIT_R, FAST>), grid, block, 0, st, g); break;
-    case 4: hipLaunchKernelGGL((q4mv_split_kernel<4, Q4_SPLIT_R, FAST>), grid, block, 0, st, g); break;
-    case 8: hipLaunchKernelGGL((q4mv_split_kernel<8, Q4_SPLIT_R, FAST>), grid, block, 0, st, g); break;
-    case 16: hipLaunchKernelGGL((q4mv_split_kernel<16, Q4_SPLIT_R, FAST>), grid, block, 0, st, g); break;
+    case 2: hipLaunchKernelGGL((q4mv_split_kernel<2, Q4_SPLIT_R, FAST, PRO>), grid, block, 0, st, g); break;
+    case 4: hipLaunchKernelGGL((q4mv_split_kernel<4, Q4_SPLIT_R, FAST, PRO>), grid, block, 0, st, g); break;
+    case 8: hipLaunchKernelGGL((q4mv_split_kernel<8, Q4_SPLIT_R, FAST, PRO>), grid, block, 0, st, g); break;
+    case 16: hipLaunchKernelGGL((q4mv_split_kernel<16, Q4_SPLIT_R, FAST, PRO>), grid, block, 0, st, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <bool FAST>
-hipError_t launch_row64(const ProdGroup &g, hipStream_t st) {
-  hipLaunchKernelGGL((q4mv_row64_kernel<Q4_ROW64_R, FAST>), dim3(g.wg_begin[g.n]), dim3(kThreads),
-                     0, st, g);
+template <bool FAST, int PRO, int EPI>
+hipError_t launch_row64(const ProdGroup &g, bool preload, const Extra &ex, hipStream_t st) {
+  if (preload)
+    hipLaunchKernelGGL((q4mv_row64_kernel<Q4_ROW64_R, FAST, PRO, EPI, true>),
+                       dim3(g.wg_begin[g.n]), dim3(kThreads), 0, st, g, ex);
+  else
+    hipLaunchKernelGGL((q4mv_row64_kernel<Q4_ROW64_R, FAST, PRO, EPI, false>),
+                       dim3(g.wg_begin[g.n]), dim3(kThreads), 0, st, g, ex);
   return hipGetLastError();
 }
 
-// Workgroups of a kernel (with `block` threads) that fit on the current
-// device at once: its occupancy per compute unit times the compute units.
-// Queried once per device and kernel slot, then cached.
-constexpr int kMaxDevices = 64;
-constexpr int kKernelSlots = 2;  // row64 fixed, row64 fast
-std::atomic<int> g_resident[kMaxDevices][kKernelSlots];
+// The row64 variants: prologue x epilogue pairs that exist.
+#define Q4_ROW64_VARIANTS(X) \
+  X(kProX, kEpiStore)        \
+  X(kProXsum, kEpiStore)     \
+  X(kProNorm, kEpiStore)     \
+  X(kProNorm, kEpiSwiglu)    \
+  X(kProNorm, kEpiArgmax)
 
-int resident_workgroups(const void *kernel, int slot, int block) {
+template <bool FAST, bool PRELOAD>
+const void *row64_ptr(int pro, int epi) {
+#define Q4_PTR_CASE(P_, E_) \
+  if (pro == P_ && epi == E_)   \
+    return reinterpret_cast<const void *>(&q4mv_row64_kernel<Q4_ROW64_R, FAST, P_, E_, PRELOAD>);
+  Q4_ROW64_VARIANTS(Q4_PTR_CASE)
+#undef Q4_PTR_CASE
+  return nullptr;
+}
+
+// One block per wave or fewer: preload.
+bool row64_single_pass(const ProdGroup &g) {
+  for (int i = 0; i < g.n; ++i) {
+    const long long waves = (long long)(g.wg_begin[i + 1] - g.wg_begin[i]) * (kThreads / kWave);
+    if ((long long)g.p[i].rows > waves * Q4_ROW64_R) return false;
+  }
+  return true;
+}
+
+template <bool FAST>
+hipError_t dispatch_row64(const ProdGroup &g, const Shape &sh, const Extra &ex, hipStream_t st) {
+  const bool preload = row64_single_pass(g);
+#define Q4_LAUNCH_CASE(P_, E_) \
+  if (sh.pro == P_ && sh.epi == E_) return launch_row64<FAST, P_, E_>(g, preload, ex, st);
+  Q4_ROW64_VARIANTS(Q4_LAUNCH_CASE)
+#undef Q4_LAUNCH_CASE
+  return hipErrorInvalidValue;
+}
+
+// Workgroups of a row64 kernel variant that fit on the current device at
+// once: its occupancy per compute unit times the compute units, queried
+// once per device and variant.
+constexpr int kMaxDevices = 64;
+constexpr int kVariantSlots = 2 * 2 * 3 * 3;  // mode x preload x prologue x epilogue
+std::atomic<int> g_resident[kMaxDevices][kVariantSlots];
+
+int resident_workgroups(const void *kernel, int slot) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (dev < 0 || dev >= kMaxDevices) return 0;
+  if (dev < 0 || dev >= kMaxDevices || slot < 0 || slot >= kVariantSlots) return 0;
   const int cached = g_resident[dev][slot].load(std::memory_order_relaxed);
   if (cached > 0) return cached;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   int v = (per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
@@ -393,33 +565,49 @@ int32_t clamp_wg(long long need, long long cap) {
 
 }  // namespace
 
-Shape shape_of(int32_t cols) {
+Shape shape_of(int32_t cols, int pro, int epi) {
   const int G = cols / 64;
-  if (G == 32) return Shape{Shape::kRow64, 64, 0};
+  if (G == 32) return Shape{Shape::kRow64, 64, 0, pro, epi};
   if (G < 32) {
     int lpr = next_pow2(2 * G);
-    return Shape{Shape::kSeg, lpr < 2 ? 2 : lpr, 0};
+    return Shape{Shape::kSeg, lpr < 2 ? 2 : lpr, 0, pro, epi};
   }
-  return Shape{Shape::kSplit, 0, (G + 31) / 32};
+  return Shape{Shape::kSplit, 0, (G + 31) / 32, pro, epi};
+}
+
+bool shape_supported(const Shape &sh) {
+  if (sh.kind == Shape::kRow64) return true;
+  return sh.epi == kEpiStore && sh.pro != kProNorm;
+}
+
+// Resident workgroups of the row64 variant for this shape and mode.
+int32_t row64_capacity(const Shape &sh, int mode, bool preload) {
+  const bool fast = mode != 0;
+  const void *k = fast ? (preload ? row64_ptr<true, true>(sh.pro, sh.epi)
+                                  : row64_ptr<true, false>(sh.pro, sh.epi))
+                       : (preload ? row64_ptr<false, true>(sh.pro, sh.epi)
+                                  : row64_ptr<false, false>(sh.pro, sh.epi));
+  if (!k) return 0;
+  return resident_workgroups(k, 18 * (fast ? 1 : 0) + 9 * (preload ? 1 : 0) + 3 * sh.pro + sh.epi);
 }
 
 int32_t resident_capacity(const Shape &sh, int mode) {
-  const bool fast = mode != 0;
   if (sh.kind != Shape::kRow64) return 0;  // no cap from occupancy
-  const void *k = fast ? reinterpret_cast<const void *>(&q4mv_row64_kernel<Q4_ROW64_R, true>)
-                       : reinterpret_cast<const void *>(&q4mv_row64_kernel<Q4_ROW64_R, false>);
-  return resident_workgroups(k, fast ? 1 : 0, kThreads);
+  return row64_capacity(sh, mode, false);
 }
 
 int32_t workgroups_for(const Shape &sh, int32_t rows, int mode) {
   const int wpg = kThreads / kWave;
   switch (sh.kind) {
     case Shape::kRow64: {
-      // at most what fits on the device at once (no second round of
-      // workgroups), at least R rows per wave
-      const int cap = resident_capacity(sh, mode);
-      return clamp_wg((rows + wpg * Q4_ROW64_R - 1) / (wpg * Q4_ROW64_R),
-                      cap > 0 ? cap : Q4_ROW64_MAX_WG);
+      // one block of R rows per wave if that fits on the device at once
+      // (the preloading variant then runs); otherwise as many workgroups as
+      // fit at once, none waiting for a second round
+      const long long need = (rows + wpg * Q4_ROW64_R - 1) / (wpg * Q4_ROW64_R);
+      const int cap_pre = row64_capacity(sh, mode, true);
+      if (cap_pre > 0 && need <= cap_pre) return clamp_wg(need, cap_pre);
+      const int cap = row64_capacity(sh, mode, false);
+      return clamp_wg(need, cap > 0 ? cap : Q4_ROW64_MAX_WG);
     }
     case Shape::kSeg: {
       const long long per_wg = (long long)wpg * kSegR * (kWave / sh.lpr);
@@ -430,12 +618,24 @@ int32_t workgroups_for(const Shape &sh, int32_t rows, int mode) {
   }
 }
 
-hipError_t launch_q4mv_group(const ProdGroup &g, const Shape &sh, int mode, hipStream_t st) {
+hipError_t launch_q4mv_group(const ProdGroup &g, const Shape &sh, int mode, const Extra &ex,
+                             hipStream_t st) {
+  if (!shape_supported(sh)) return hipErrorInvalidValue;
   const bool fast = mode != 0;
   switch (sh.kind) {
-    case Shape::kRow64: return fast ? launch_row64<true>(g, st) : launch_row64<false>(g, st);
-    case Shape::kSeg: return fast ? launch_seg<true>(g, sh.lpr, st) : launch_seg<false>(g, sh.lpr, st);
-    default: return fast ? launch_split<true>(g, sh.passes, st) : launch_split<false>(g, sh.passes, st);
+    case Shape::kRow64:
+      return fast ? dispatch_row64<true>(g, sh, ex, st) : dispatch_row64<false>(g, sh, ex, st);
+    case Shape::kSeg:
+      if (sh.pro == kProXsum)
+        return fast ? launch_seg<true, kProXsum>(g, sh.lpr, st)
+                    : launch_seg<false, kProXsum>(g, sh.lpr, st);
+      return fast ? launch_seg<true, kProX>(g, sh.lpr, st) : launch_seg<false, kProX>(g, sh.lpr, st);
+    default:
+      if (sh.pro == kProXsum)
+        return fast ? launch_split<true, kProXsum>(g, sh.passes, st)
+                    : launch_split<false, kProXsum>(g, sh.passes, st);
+      return fast ? launch_split<true, kProX>(g, sh.passes, st)
+                  : launch_split<false, kProX>(g, sh.passes, st);
   }
 }
 

@@ -8,10 +8,11 @@ cannot serve the 318.9 MB of weights of a step from the previous one.
 Inputs are resident in HBM before timing starts.
 
 value = algorithmic bytes of a step / time per step (GB/s, 1e9 B/s), the
-steps timed back to back by one pair of HIP events.
+steps timed back to back by one pair of HIP events on the launch stream.
 roofline = the q4mv kernel alone: its algorithmic bytes / its average
 duration, from one pair of HIP events around the same number of q4mv
-launches issued back to back on the launch stream.
+launches issued back to back on the launch stream.  Also reported: rmsq fused
+into the product's prologue (one kernel per step).
 
 Also reported: the 24-layer decode chain (rmsq -> [gate;up] q4mv -> swq ->
 down q4mv + residual, then rmsq -> head q4mv -> argmax), captured once as a
@@ -49,6 +50,13 @@ def rmsq_bytes(n: int) -> int:
     return 4 * (3 * n + n // 64)  # h, w in; u, group sums out
 
 
+def norm_head_bytes(rows: int, cols: int) -> int:
+    """Algorithmic bytes of y = W rmsq(z, wn) in one kernel: the product's
+    per-row bytes, plus z and wn (4 cols B each) instead of x and its sums."""
+    G = cols // 64
+    return rows * (cols // 2 + 8 * G + 4) + 8 * cols
+
+
 def log(msg: str) -> None:
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
@@ -56,7 +64,7 @@ def log(msg: str) -> None:
 def kernel_source_hash() -> str:
     """Hash of the q4mv kernel sources (the counters are only valid for them)."""
     h = hashlib.sha256()
-    for name in ("q4mv_kernels.hip", "q4mv_device.h"):
+    for name in ("q4mv_kernels.hip", "q4mv_device.h", "ops_device.h"):
         h.update(open(os.path.join(ROOT, "affine_q4_matvec_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
@@ -124,37 +132,36 @@ def run_head(args, q4, torch, synth):
     stream = torch.cuda.current_stream()
 
     def step(i):
+        # the standalone rmsq, then the product (2 kernels)
         q4.rmsq(z, wn, eps, x, xs, stream=stream)
         q4.q4mv(mats[i % 2], x, xs, y, mode=mode, stream=stream)
+
+    def timed(fn, n):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     y_first = y.cpu().numpy().copy()
-
-    # (1) the timed steps: rmsq + q4mv back to back, one event pair around all
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_begin.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    step_ms = t_begin.elapsed_time(t_end) / args.steps
+    # the timed steps, back to back, one event pair around all of them
+    step_ms = timed(step, args.steps)
     same = bool(np.array_equal(y.cpu().numpy().view(np.uint32), y_first.view(np.uint32)))
-
-    # (2) the q4mv kernel alone: the same launches back to back (no event
-    # between them, which would itself add a gap), one event pair around all
-    k_begin = torch.cuda.Event(enable_timing=True)
-    k_end = torch.cuda.Event(enable_timing=True)
-    k_begin.record(stream)
-    for i in range(args.steps):
-        q4.q4mv(mats[i % 2], x, xs, y, mode=mode, stream=stream)
-    k_end.record(stream)
+    # the q4mv kernel alone: the same launches back to back (an event between
+    # launches would itself add a gap)
+    kern_ms = timed(lambda i: q4.q4mv(mats[i % 2], x, xs, y, mode=mode, stream=stream), args.steps)
+    # for reference: rmsq fused into the product's prologue (one kernel)
+    fused_ms = timed(lambda i: q4.q4mv_norm(mats[i % 2], z, wn, eps, y, mode=mode, stream=stream),
+                     args.steps)
     torch.cuda.synchronize()
-    kern_ms = k_begin.elapsed_time(k_end) / args.steps
-    return step_ms, kern_ms, same
+    same = same and bool(np.array_equal(y.cpu().numpy().view(np.uint32), y_first.view(np.uint32)))
+    return step_ms, kern_ms, fused_ms, same
 
 
 def run_chain(args, q4, torch, synth):
@@ -204,7 +211,8 @@ def run_chain(args, q4, torch, synth):
         "ms_per_token_gpu": round(gpu_ms, 4),
         "algorithmic_bytes_per_token": bpt,
         "gpu_GBps": round(bpt / (gpu_ms * 1e-3) / 1e9, 1),
-        "kernels_per_token": 1 + 4 * len(chain.layers) + 4,
+        "kernels_per_token": chain.kernels_per_token(),
+        "fused": chain.fused,
         "tokens_match_oracle_golden": match,
         "queued_replays_reach_same_last_token": last == tokens[-1],
         "distinct_tokens": len(set(tokens)),
@@ -258,12 +266,13 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 5}))
         return 0
-    step_ms, kern_ms, stable = run_head(args, q4, torch, synth)
+    step_ms, kern_ms, fused_ms, stable = run_head(args, q4, torch, synth)
     qb = head_bytes(ROWS, COLS)
     step_bytes = qb + rmsq_bytes(COLS)
     value = step_bytes / (step_ms * 1e-3) / 1e9
     achieved = qb / (kern_ms * 1e-3) / 1e9
-    log("head: %.4f ms/step, q4mv %.4f ms avg (%.1f GB/s)" % (step_ms, kern_ms, achieved))
+    log("head: %.4f ms/step; q4mv %.4f ms (%.1f GB/s); fused rmsq+q4mv %.4f ms"
+        % (step_ms, kern_ms, achieved, fused_ms))
     chain = None
     if not args.no_chain:
         chain = run_chain(args, q4, torch, synth)
@@ -286,16 +295,19 @@ def main() -> int:
         "config": {
             "workload": "output-head q4mv 248320x2048, group 64, 4-bit codes + fp32 scale/bias; "
                         "x and group sums from rmsq(z~N(0,1), wn~N(1,0.1), eps 1e-6); "
-                        "step = rmsq + q4mv; 2 weight copies alternate",
+                        "step = rmsq kernel + q4mv kernel; 2 weight copies alternate",
             "rows": ROWS, "cols": COLS, "group": 64, "mode": args.mode,
             "step_bytes": step_bytes,
             "output_bits_stable_across_steps": stable,
+            "fused_rmsq_q4mv_ms": round(fused_ms, 5),
+            "fused_rmsq_q4mv_GBps": round(norm_head_bytes(ROWS, COLS) / (fused_ms * 1e-3) / 1e9, 1),
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-            "kernel": "q4mv_row64_kernel<4,%s>" % ("false" if args.mode == "fixed" else "true"),
+            "kernel": "q4mv_row64_kernel<4,%s,kProX,kEpiStore,no preload>" % (
+                "false" if args.mode == "fixed" else "true"),
             "algorithmic_bytes_per_launch": qb,
             "avg_launch_ms": round(kern_ms, 5),
             "timing": "HIP events around %d back-to-back launches on the launch stream" % args.steps,

@@ -78,7 +78,9 @@ typedef struct q4_mat {
  *   w    : host pointer to the matrix descriptor (read during the call).
  *   x    : device float[cols], 16-byte aligned.
  *   xsum : device float[cols/64]; xsum[g] is the sum of x[64g..64g+63]
- *          as emitted by rmsq/swq (an input: never recomputed).
+ *          as emitted by rmsq/swq (an input: never recomputed).  NULL asks
+ *          the kernel to form the group sums of x itself with the same
+ *          tree rmsq and swq use (same bits as passing them).
  *   y    : device float[rows]; must not overlap w, x or xsum.
  *   mode : Q4_FIXED -- per row, p_i = q_i * x_i, d_g = T(p over the group),
  *          t_g = (s*d_g) + (b*xsum_g) unfused, y = T(t over groups), with T
@@ -98,6 +100,41 @@ int q4mv_add(const q4_mat *w, const float *x, const float *xsum,
              const float *resid, float *y, int mode, void *stream);
 
 /*
+ * Fused stages ([P1] Change: rmsq, swq and the 4-row q4mv as one queued
+ * sequence; [P1] Verification: one command buffer per token).  Each gives
+ * the bits of the separate calls it replaces; each needs cols == 2048.
+ *
+ * q4mv_norm: y = W rmsq(h, wn)  (rmsq's arithmetic in the product's
+ *   prologue).  h, wn: device float[cols], 16-byte aligned.  u, usum:
+ *   optional outputs (both or neither; float[cols] 16-byte aligned and
+ *   float[cols/64]) receiving rmsq's u and group sums.  For cols != 2048 it
+ *   runs rmsq into u, usum (then required) and q4mv: two launches.
+ */
+int q4mv_norm(const q4_mat *w, const float *h, const float *wn, float eps, float *y, float *u,
+              float *usum, int mode, void *stream);
+
+/*
+ * q4mv_norm_swiglu: m = swq(W rmsq(h, wn)) for a matrix whose rows come in
+ *   (gate, up) pairs: row 2i is gate row i, row 2i+1 up row i.  m: device
+ *   float[rows/2]; rows even; cols == 2048.  The group sums of m are not
+ *   written: pass xsum = NULL to the product that reads m.
+ */
+int q4mv_norm_swiglu(const q4_mat *w, const float *h, const float *wn, float eps, float *m,
+                     int mode, void *stream);
+
+/*
+ * q4mv_norm_argmax: y = W rmsq(h, wn) and *idx = q4_argmax(y) (cols ==
+ *   2048): the product kernel also leaves the key of each workgroup's best
+ *   row in ws, and one small kernel picks the largest.  ws: device
+ *   workspace, 8-byte aligned, of q4mv_argmax_ws_bytes() bytes (fewer bytes
+ *   limit the product to one workgroup per 8 bytes); no initialisation
+ *   needed.  Calls that overlap in time must not share it.
+ */
+size_t q4mv_argmax_ws_bytes(void);
+int q4mv_norm_argmax(const q4_mat *w, const float *h, const float *wn, float eps, float *y,
+                     int32_t *idx, void *ws, size_t ws_bytes, int mode, void *stream);
+
+/*
  * rmsq: RMS norm with float weights plus the 64-value group sums that q4mv
  * reads ([P1] Change, rmsq bullet; exact on the GPU there).
  *   ss = T(h_i*h_i); rho = 1 / sqrt(ss/n + eps)  (correctly rounded);
@@ -109,8 +146,8 @@ int rmsq(const float *h, const float *w, int32_t n, float eps, float *u,
          float *usum, void *stream);
 
 /*
- * swq: SwiGLU round(silu(a[i]) * a[n+i]) plus group sums ([P1] Change, swq
- * bullet).
+ * swq: SwiGLU, o[i] = silu(a[i]) times a[n+i], rounded, plus group sums
+ * ([P1] Change, swq bullet).
  *   a    : device float[2n], gate in a[0..n), up in a[n..2n).
  *   o    : device float[n];  osum : device float[n/64].
  *   n a positive multiple of 64 (the n = 32 case the pages criticise is
