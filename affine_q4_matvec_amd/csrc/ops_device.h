@@ -32,24 +32,15 @@ __device__ __forceinline__ float tree8(const float *v) {
 //   ss = T(h*h); ms = ss / n; rho = 1 / sqrt(ms + eps)  (correctly rounded);
 //   u_i = (h_i * rho) * w_i; us_g = T(u[64g .. 64g+63]).
 
-// The first half: rho, in every thread.  The thread's 8 slots of h and of
-// w are loaded together up front (hv, wv) so that their latencies overlap.
-// red is LDS scratch of 17 floats; every thread of the workgroup must call
-// it (two barriers).
-__device__ __forceinline__ float rmsq_rho(const float *__restrict__ h,
-                                          const float *__restrict__ w, int n, float eps,
-                                          float *red, float *hv, float *wv) {
+// The first half: rho, in every thread, from the thread's 8 slots of h
+// already in registers (hv; slots >= n must hold 0).  red is LDS scratch of
+// 17 floats; every thread of the workgroup must call it (two barriers).
+__device__ __forceinline__ float rmsq_rho_regs(const float *hv, int n, float eps, float *red) {
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1);
   const int wave = t / kWave;
   const int nw = blockDim.x / kWave;
   float v[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int i = 8 * t + k;
-    hv[k] = i < n ? h[i] : 0.0f;
-    wv[k] = i < n ? w[i] : 0.0f;
-  }
 #pragma unroll
   for (int k = 0; k < 8; ++k) v[k] = 8 * t + k < n ? hv[k] * hv[k] : kNegZero;
   float s = tree8(v);
@@ -66,6 +57,21 @@ __device__ __forceinline__ float rmsq_rho(const float *__restrict__ h,
   __syncthreads();
   const float ms = red[16] / (float)n;
   return 1.0f / sqrtf(ms + eps);
+}
+
+// The same, loading the thread's 8 slots of h and of w together up front
+// (hv, wv) so that their latencies overlap.
+__device__ __forceinline__ float rmsq_rho(const float *__restrict__ h,
+                                          const float *__restrict__ w, int n, float eps,
+                                          float *red, float *hv, float *wv) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int i = 8 * t + k;
+    hv[k] = i < n ? h[i] : 0.0f;
+    wv[k] = i < n ? w[i] : 0.0f;
+  }
+  return rmsq_rho_regs(hv, n, eps, red);
 }
 
 // One normalised value: (h * rho) * w.

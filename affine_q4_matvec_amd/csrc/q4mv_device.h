@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ops_device.h"
 #include "q4mv_internal.h"
 
 #pragma clang fp contract(off)
@@ -270,5 +271,67 @@ __device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t vof
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
+// Group sum of the lane pair's 64 activations: T over the lane's 32
+// (balanced) plus the partner's 32.
+__device__ __forceinline__ float pair_group_sum(const float *xv) {
+  const float L =
+      (ops::tree8(xv) + ops::tree8(xv + 8)) + (ops::tree8(xv + 16) + ops::tree8(xv + 24));
+  return L + dpp<kDppQuadXor1>(L);
+}
+
+__device__ __forceinline__ void load_x_values(const float *x, bool active, float *xv) {
+  if (active) {
+    const float4 *xp = reinterpret_cast<const float4 *>(x);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 v = xp[k];
+      xv[4 * k + 0] = v.x;
+      xv[4 * k + 1] = v.y;
+      xv[4 * k + 2] = v.z;
+      xv[4 * k + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) xv[k] = 0.0f;
+  }
+}
+
+// (gate, up) pairs waiting for their SwiGLU: lane k of a wave holds pair k
+// of the current batch.  The pairs come out of the row sums one or two per
+// block, but the SwiGLU costs the same instructions for 1 pair as for 64, so
+// a wave evaluates them in batches of up to 64.
+struct SwigluBatch {
+  float gate = 0.0f, up = 0.0f;
+  int out = -1;  // index into m, -1 for an empty slot
+  int count = 0; // pairs held (wave-uniform)
+};
+
+template <bool FAST>
+__device__ __forceinline__ void swiglu_flush(float *m_out, SwigluBatch &b) {
+  if (b.count == 0) return;
+  if (b.out >= 0) m_out[b.out] = ops::swiglu_value<FAST>(b.gate, b.up);
+  b.out = -1;
+  b.count = 0;
+}
+
+// Appends the pair (gate, up) for m[out], both held by lane 63, to slot
+// b.count (lane b.count takes them).
+template <bool FAST>
+__device__ __forceinline__ void swiglu_push(float *m_out, SwigluBatch &b, int lane, float gate,
+                                            float up, int out) {
+  const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gate), kWave - 1));
+  const float u = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(up), kWave - 1));
+  const bool mine = lane == b.count;
+  b.gate = mine ? g : b.gate;
+  b.up = mine ? u : b.up;
+  b.out = mine ? out : b.out;
+  b.count = b.count + 1;
+  if (b.count == kWave) swiglu_flush<FAST>(m_out, b);
+}
+
+// Blocks of R rows dealt round-robin to the waves: r0, r0 + stride, ...
+// Each block is loaded at the top of its iteration (issuing the next
+// block's loads while summing the current one would keep two blocks of
+// registers live); with PRELOAD, `a` holds the first block's loads on entry.
 }  // namespace dev
 }  // namespace q4

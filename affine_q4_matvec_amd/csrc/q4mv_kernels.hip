@@ -63,31 +63,6 @@ constexpr int kSegR = 4;
 constexpr int kThreads = 256;
 static_assert(Q4_ROW64_R % 2 == 0, "the SwiGLU epilogue pairs rows within a block");
 
-// Group sum of the lane pair's 64 activations: T over the lane's 32
-// (balanced) plus the partner's 32.
-__device__ __forceinline__ float pair_group_sum(const float *xv) {
-  const float L =
-      (ops::tree8(xv) + ops::tree8(xv + 8)) + (ops::tree8(xv + 16) + ops::tree8(xv + 24));
-  return L + dpp<kDppQuadXor1>(L);
-}
-
-__device__ __forceinline__ void load_x_values(const float *x, bool active, float *xv) {
-  if (active) {
-    const float4 *xp = reinterpret_cast<const float4 *>(x);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float4 v = xp[k];
-      xv[4 * k + 0] = v.x;
-      xv[4 * k + 1] = v.y;
-      xv[4 * k + 2] = v.z;
-      xv[4 * k + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 32; ++k) xv[k] = 0.0f;
-  }
-}
-
 // Activations of `chunk` and its group sum for prologues kProX / kProXsum.
 template <int PRO>
 __device__ __forceinline__ void chunk_inputs(const Prod &P, int chunk, bool active, float *xv,
@@ -125,43 +100,6 @@ __device__ __forceinline__ void row64_load(const Prod &P, int r0, int nrows, uin
   }
 }
 
-// (gate, up) pairs waiting for their SwiGLU: lane k of a wave holds pair k
-// of the current batch.  The pairs come out of the row sums one or two per
-// block, but the SwiGLU costs the same instructions for 1 pair as for 64, so
-// a wave evaluates them in batches of up to 64.
-struct SwigluBatch {
-  float gate = 0.0f, up = 0.0f;
-  int out = -1;  // index into m, -1 for an empty slot
-  int count = 0; // pairs held (wave-uniform)
-};
-
-template <bool FAST>
-__device__ __forceinline__ void swiglu_flush(const Extra &ex, SwigluBatch &b) {
-  if (b.count == 0) return;
-  if (b.out >= 0) ex.m_out[b.out] = ops::swiglu_value<FAST>(b.gate, b.up);
-  b.out = -1;
-  b.count = 0;
-}
-
-// Appends the pair (gate, up) for m[out], both held by lane 63, to slot
-// b.count (lane b.count takes them).
-template <bool FAST>
-__device__ __forceinline__ void swiglu_push(const Extra &ex, SwigluBatch &b, int lane, float gate,
-                                            float up, int out) {
-  const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gate), kWave - 1));
-  const float u = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(up), kWave - 1));
-  const bool mine = lane == b.count;
-  b.gate = mine ? g : b.gate;
-  b.up = mine ? u : b.up;
-  b.out = mine ? out : b.out;
-  b.count = b.count + 1;
-  if (b.count == kWave) swiglu_flush<FAST>(ex, b);
-}
-
-// Blocks of R rows dealt round-robin to the waves: r0, r0 + stride, ...
-// Each block is loaded at the top of its iteration (issuing the next
-// block's loads while summing the current one would keep two blocks of
-// registers live); with PRELOAD, `a` holds the first block's loads on entry.
 // Greedy pick over the rows a wave has summed.
 struct RunningMax {
   float value = 0.0f;
@@ -194,7 +132,7 @@ __device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, const
     if constexpr (EPI == kEpiSwiglu) {
 #pragma unroll
       for (int j = 0; j + 1 < R; j += 2)
-        if (j + 1 < nrows) swiglu_push<FAST>(ex, batch, lane, tot[j], tot[j + 1], (r + j) >> 1);
+        if (j + 1 < nrows) swiglu_push<FAST>(ex.m_out, batch, lane, tot[j], tot[j + 1], (r + j) >> 1);
     } else if (lane == kWave - 1) {
 #pragma unroll
       for (int j = 0; j < R; ++j) {
@@ -214,7 +152,7 @@ __device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, const
       }
     }
   }
-  if constexpr (EPI == kEpiSwiglu) swiglu_flush<FAST>(ex, batch);
+  if constexpr (EPI == kEpiSwiglu) swiglu_flush<FAST>(ex.m_out, batch);
 }
 
 // PRELOAD: issue the first block's loads before the activations are formed
