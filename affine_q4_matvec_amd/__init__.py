@@ -20,6 +20,7 @@ __all__ = [
     "FIXED", "FAST", "Q4Error", "Q4Matrix", "q4mv", "q4mv_add", "q4mv_norm",
     "q4mv_norm_swiglu", "q4mv_norm_argmax", "q4mv_argmax_ws_bytes", "rmsq", "swq",
     "q4_argmax", "q4_argmax_ws_bytes", "q4_embed", "Queue", "Graph", "q4_sync",
+    "MlpLayer", "q4_decode_layers", "q4_decode_layers_ws_bytes", "q4_decode_layers_status",
     "library_path",
 ]
 
@@ -28,6 +29,7 @@ FAST = 1
 Q4_OK, Q4_EINVAL, Q4_EHIP, Q4_ETIMEOUT, Q4_ESTATE, Q4_ENOMEM = 0, -1, -2, -3, -4, -5
 MAX_COLS = 32768
 MAX_RMSQ_N = 8192
+MAX_DECODE_LAYERS = 32
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libq4mv.so")
@@ -41,6 +43,10 @@ if not os.path.exists(library_path):
 class _Mat(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("s", ctypes.c_void_p), ("b", ctypes.c_void_p),
                 ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+class _MlpLayer(ctypes.Structure):
+    _fields_ = [("gate_up", _Mat), ("down", _Mat), ("wn", ctypes.c_void_p)]
 
 
 _vp = ctypes.c_void_p
@@ -61,6 +67,11 @@ _SIGS = {
     "q4_argmax_ws_bytes": ([_i32], ctypes.c_size_t),
     "q4_argmax": ([_vp, _i32, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "q4_embed": ([ctypes.POINTER(_Mat), _vp, _vp, _vp], ctypes.c_int),
+    "q4_decode_layers_ws_bytes": ([], ctypes.c_size_t),
+    "q4_decode_layers": ([ctypes.POINTER(_Mat), _vp, ctypes.POINTER(_MlpLayer), _i32,
+                          ctypes.c_float, _vp, _vp, ctypes.c_size_t, ctypes.c_int, _vp],
+                         ctypes.c_int),
+    "q4_decode_layers_status": ([_vp, _vp], ctypes.c_int),
     "q4_queue_create": ([_vp, ctypes.c_int, ctypes.POINTER(_vp)], ctypes.c_int),
     "q4_queue_destroy": ([_vp], ctypes.c_int),
     "q4mv_queue": ([_vp, ctypes.POINTER(_Mat), _vp, _vp, _vp], ctypes.c_int),
@@ -274,6 +285,45 @@ def q4_embed(w: Q4Matrix, tok: torch.Tensor, e: torch.Tensor | None = None,
     _check("q4_embed", _lib.q4_embed(w.ref, _dev(tok, torch.int32, 1, "tok"),
                                      _dev(e, torch.float32, w.cols, "e"), _stream(stream)))
     return e
+
+
+class MlpLayer:
+    """One MLP layer for ``q4_decode_layers``: ``gate_up`` (rows 2*inter,
+    2048 columns, gate row i at 2i and up row i at 2i+1), ``down`` (2048
+    rows, inter columns) and the norm weights ``wn`` (float32[2048])."""
+
+    def __init__(self, gate_up: Q4Matrix, down: Q4Matrix, wn: torch.Tensor):
+        _dev(wn, torch.float32, 2048, "wn")
+        self.gate_up, self.down, self.wn = gate_up, down, wn
+        self._c = _MlpLayer(gate_up._c, down._c, wn.data_ptr())
+
+
+def q4_decode_layers_ws_bytes() -> int:
+    return int(_lib.q4_decode_layers_ws_bytes())
+
+
+def q4_decode_layers(emb: Q4Matrix, tok: torch.Tensor, layers: list, eps: float,
+                     h: torch.Tensor, ws: torch.Tensor, mode: int = FIXED,
+                     stream=None) -> torch.Tensor:
+    """``h = embed(emb, tok)``, then per layer ``h += down swq(gate_up
+    rmsq(h, wn))``, in one persistent kernel.  ``ws`` is its workspace of
+    ``q4_decode_layers_ws_bytes()`` bytes (zero-filled before first use,
+    e.g. ``torch.zeros``)."""
+    if not layers:
+        raise ValueError("at least one layer required")
+    arr = (_MlpLayer * len(layers))(*[L._c for L in layers])
+    _check("q4_decode_layers",
+           _lib.q4_decode_layers(emb.ref, _dev(tok, torch.int32, 1, "tok"), arr, len(layers),
+                                 float(eps), _dev(h, torch.float32, 2048, "h"),
+                                 _dev(ws, ws.dtype, None, "ws"), ws.numel() * ws.element_size(),
+                                 mode, _stream(stream)))
+    return h
+
+
+def q4_decode_layers_status(ws: torch.Tensor, stream=None) -> int:
+    """Host wait; Q4_OK, or Q4_ETIMEOUT when a wait of the persistent
+    kernel ran out (the workspace is then cleared)."""
+    return int(_lib.q4_decode_layers_status(_dev(ws, ws.dtype, None, "ws"), _stream(stream)))
 
 
 def q4_sync(stream=None) -> None:

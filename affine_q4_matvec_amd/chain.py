@@ -8,12 +8,14 @@ One step from token t (the chain has no other state):
                 h     = h + down_l m                   (q4mv_add, in place)
   u, us = rmsq(h, wn_final);  logits = head u;  t' = argmax(logits)
 
-Two ways to run it, with the same bits:
-  fused=False  the steps as listed: 1 + 4 per layer + 4 kernels
-  fused=True   rmsq in the products' prologues, SwiGLU in the gate/up
-               product's epilogue (gate and up rows interleaved), the down
-               product forming its group sums, argmax's first half in the
-               head product's epilogue: 1 + 2 per layer + 2 kernels
+Three ways to run it, with the same bits:
+  fused=False      the steps as listed: 1 + 4 per layer + 4 kernels
+  fused=True       rmsq in the products' prologues, SwiGLU in the gate/up
+                   product's epilogue (gate and up rows interleaved), the
+                   down product forming its group sums, argmax's first half
+                   in the head product's epilogue: 1 + 2 per layer + 2 kernels
+  persistent=True  the embedding and every layer in one persistent kernel
+                   (q4_decode_layers), then the fused head: 3 kernels
 
 The token lives on the device: argmax writes it where the next step's embed
 reads it, so a step captured once as a graph can be replayed token after
@@ -29,8 +31,9 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (FIXED, Graph, Q4Matrix, q4_argmax, q4_argmax_ws_bytes, q4_embed, q4mv,
-               q4mv_add, q4mv_argmax_ws_bytes, q4mv_norm_argmax, q4mv_norm_swiglu, rmsq, swq)
+from . import (FIXED, Graph, MlpLayer, Q4Matrix, q4_argmax, q4_argmax_ws_bytes,
+               q4_decode_layers, q4_decode_layers_ws_bytes, q4_embed, q4mv, q4mv_add,
+               q4mv_argmax_ws_bytes, q4mv_norm_argmax, q4mv_norm_swiglu, rmsq, swq)
 
 
 def _stack_rows(a: dict, b: dict) -> dict:
@@ -51,9 +54,10 @@ def _interleave_rows(a: dict, b: dict) -> dict:
 
 class DecodeChain:
     def __init__(self, weights: dict, mode: int = FIXED, layers: int | None = None,
-                 device: str = "cuda", fused: bool = True):
+                 device: str = "cuda", fused: bool = True, persistent: bool = False):
         self.mode = mode
-        self.fused = fused
+        self.persistent = persistent
+        self.fused = fused or persistent
         self.hidden = int(weights["hidden"])
         self.inter = int(weights["inter"])
         self.vocab = int(weights["vocab"])
@@ -62,7 +66,7 @@ class DecodeChain:
         f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
         self.layers = []
         for lw in weights["layers"][:L]:
-            gu = (_interleave_rows if fused else _stack_rows)(lw["gate"], lw["up"])
+            gu = (_interleave_rows if self.fused else _stack_rows)(lw["gate"], lw["up"])
             self.layers.append({
                 "wn": f32(lw["wn"]),
                 "gu": Q4Matrix.from_host(gu, device),
@@ -81,12 +85,16 @@ class DecodeChain:
         self.logits = z(self.vocab)
         self.ws = z((q4_argmax_ws_bytes(self.vocab) + 7) // 8, torch.int64)
         self.amax_ws = z((q4mv_argmax_ws_bytes() + 7) // 8, torch.int64)
+        self.mlp = [MlpLayer(lw["gu"], lw["down"], lw["wn"]) for lw in self.layers]
+        self.stack_ws = z((q4_decode_layers_ws_bytes() + 7) // 8, torch.int64)
         self.graph = None
         # the copies and fills above ran on the current stream; the chain may
         # run on another one
         torch.cuda.synchronize()
 
     def kernels_per_token(self) -> int:
+        if self.persistent:
+            return 3
         return 3 + 2 * len(self.layers) if self.fused else 5 + 4 * len(self.layers)
 
     def bytes_per_token(self) -> int:
@@ -104,6 +112,12 @@ class DecodeChain:
 
     def enqueue_step(self, stream) -> None:
         """Every kernel of one step, in order, on `stream`."""
+        if self.persistent:
+            q4_decode_layers(self.head, self.tok, self.mlp, self.eps, self.h, self.stack_ws,
+                             mode=self.mode, stream=stream)
+            q4mv_norm_argmax(self.head, self.h, self.wn_final, self.eps, self.logits, self.tok,
+                             self.amax_ws, mode=self.mode, stream=stream)
+            return
         q4_embed(self.head, self.tok, self.h, stream=stream)
         if self.fused:
             for lw in self.layers:

@@ -1,0 +1,432 @@
+// The MLP layers of one decode step as a single persistent launch (gfx950).
+//
+// A decode token runs rmsq, the gate/up product, swq and the down product
+// of every layer in order ("Metal: queued rmsq, swq, gdn and atq kernels and
+// a 4-row q4mv, so a decode token is one command buffer with one wait"
+// (#1440), Change and Verification).  Launched one kernel per stage, each
+// stage pays a launch and the cold start of its loads; here one grid of
+// resident workgroups (one per compute unit) runs every stage:
+//
+//   h = embed(tok)                          (each workgroup, from the weights)
+//   per layer:  u = rmsq(h, wn)              (each workgroup, into LDS)
+//               m = SwiGLU([gate; up] u)     (rows in (gate, up) pairs)
+//               h = h + down m               (m staged in LDS per workgroup)
+//
+// Dataflow instead of grid barriers.  Every value one workgroup hands to
+// another (m of each layer, h between layers) is stored as a 64-bit word:
+// the float's bits and a 32-bit tag naming the call and the stage that
+// produced it, with one device-scope store (the sc1 cache policy: written
+// through to the memory side, where device-scope loads read it).  A
+// consumer polls the words it needs with device-scope 64-bit loads until
+// each carries the expected tag: the wait and the data arrive in the same
+// load, and no cache write-back, invalidation or barrier is needed.  (On
+// this device a grid barrier built on the memory model's agent-scope
+// fences costs about 10 us, a fence-free one about 4 us; a dependent
+// device-scope load about 2 us.)
+//
+// Tags: call c (each workgroup counts its calls in a word of its own in the
+// workspace; the grid has the same size in every call, so after a
+// completed call all counters agree) gives m of layer l the tag
+// 64 c + 2 l + 1 and h after layer l the tag 64 c + 2 l + 2 (at most 32
+// layers).  m and h alternate between two buffers each by layer; with that,
+// no word is overwritten while a reader may still need it.  Writing m of
+// layer l + 2 needs h after layer l + 1 complete, and writing h after layer
+// l + 2 needs m of layer l + 2 complete, hence h after layer l + 1; h after
+// layer l + 1 is complete only when every workgroup (each owns at least one
+// row) has finished layer l + 1's down stage, which follows its reads of m
+// of layer l and of h after layer l.
+//
+// Every wait is bounded by spin_ticks of the wall clock; a wait that runs
+// out sets the error word, and every workgroup leaves at its next wait, so
+// the grid always drains.  On an otherwise idle device every workgroup of
+// the launch is resident.
+//
+// The weights of a stage do not depend on the previous one, so every wave
+// issues the loads of its next stage's rows right after the first loads of
+// its current wait (issued after them, so that the wait does not include
+// them: a wave's loads complete in issue order for its wait counter).
+//
+// Every value is computed by the same code as the per-stage kernels (rmsq
+// and SwiGLU from ops_device.h, group terms and row trees from
+// q4mv_device.h), so the result has the bits of the unfused chain.
+#include "ops_device.h"
+#include "q4mv_device.h"
+#include "q4mv_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace q4 {
+namespace {
+
+using namespace dev;
+
+constexpr int kThreads = 512;   // 8 waves: two per SIMD, up to 256 registers each
+constexpr int kWaves = kThreads / kWave;
+constexpr int kCols = 2048;     // width of h: the gate/up rows and the down output
+constexpr int kGuPairs = 3;     // (gate, up) row pairs per block
+constexpr int kGuR = 2 * kGuPairs;
+constexpr int kChunkStride = 36;  // LDS floats per 32-value chunk (4 of padding)
+
+template <int NP>
+struct alignas(16) Lds {
+  float x[NP * 64 * kChunkStride];  // activations: u (stage A) or m (stage B)
+  float xs[NP * 32];                // their group sums
+  float red[17];
+};
+
+struct GuBlock {
+  u32x4 cw[kGuR];
+  float sv[kGuR], bv[kGuR];
+};
+
+template <int NP>
+struct DownRow {
+  u32x4 cw[NP];
+  float sv[NP], bv[NP];
+};
+
+// Rows 2 p0 .. 2 p0 + 2 np - 1 (np <= kGuPairs pairs); the buffer's size
+// makes the loads of the rows past them return zero without a memory access.
+__device__ __forceinline__ void load_gu(const DecodeLayer &L, int p0, int np, int lane,
+                                        GuBlock &a) {
+  const size_t r0 = 2 * (size_t)p0;
+  const auto qr = buffer(L.gq + r0 * 256, 2 * np * 1024);
+  const auto sr = buffer(L.gs + r0 * 32, 2 * np * 128);
+  const auto br = buffer(L.gb + r0 * 32, 2 * np * 128);
+#pragma unroll
+  for (int j = 0; j < kGuR; ++j) {
+    a.cw[j] = load_codes(qr, 16u * lane, j * 1024);
+    a.sv[j] = load_f32(sr, 4u * (lane >> 1), j * 128);
+    a.bv[j] = load_f32(br, 4u * (lane >> 1), j * 128);
+  }
+}
+
+// Row r of the down matrix: pass p covers columns [2048 p, 2048 p + 2048).
+template <int NP>
+__device__ __forceinline__ void load_down(const DecodeLayer &L, int r, int lane, DownRow<NP> &d) {
+  const auto qr = buffer(L.dq + (size_t)r * (NP * 256), NP * 1024);
+  const auto sr = buffer(L.ds + (size_t)r * (NP * 32), NP * 128);
+  const auto br = buffer(L.db + (size_t)r * (NP * 32), NP * 128);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    d.cw[p] = load_codes(qr, 16u * lane, p * 1024);
+    d.sv[p] = load_f32(sr, 4u * (lane >> 1), p * 128);
+    d.bv[p] = load_f32(br, 4u * (lane >> 1), p * 128);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Device-scope words
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t load_word(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_word(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_tagged(uint64_t *p, float v, uint32_t tag) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Polls the N tagged words at p until each carries `tag`; their floats go to
+// v.  False when the wait ran out (the error word is then set) or another
+// workgroup's did.
+template <int N>
+__device__ __forceinline__ bool poll_tagged(const uint64_t *p, uint32_t tag, float *v,
+                                            uint32_t *err, long long spin_ticks) {
+  const long long t0 = wall_clock64();
+  for (int it = 1;; ++it) {
+    bool ready = true;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const uint64_t w = __hip_atomic_load(p + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      v[k] = __uint_as_float((uint32_t)w);
+      ready &= (uint32_t)(w >> 32) == tag;
+    }
+    if (ready) return true;
+    if ((it & 63) == 0 && load_word(err) != 0) return false;
+    if (wall_clock64() - t0 > spin_ticks) {
+      store_word(err, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Keeps the compiler from moving memory accesses across this point (the
+// weight loads of the next stage stay behind the loads of the current wait).
+__device__ __forceinline__ void issue_order() { asm volatile("" ::: "memory"); }
+
+// One gate/up block of np pairs: the row sums, then each (gate, up) pair
+// goes into the wave's SwiGLU batch (m[p0 + i]).
+template <bool FAST, bool PAIRS, class Store>
+__device__ __forceinline__ void gu_block(const GuBlock &a, const float *xv, float xsv, int lane,
+                                         int p0, int np, const Store &store, SwigluBatch &batch,
+                                         int negz) {
+  const bool odd = lane & 1;
+#pragma unroll
+  for (int i = 0; i < kGuPairs; ++i) {
+    if (i < np) {
+      const float g = wave_sum_lane63(
+          group_term<FAST, PAIRS>(a.cw[2 * i], xv, a.sv[2 * i], a.bv[2 * i], xsv, true, odd), negz);
+      const float u = wave_sum_lane63(
+          group_term<FAST, PAIRS>(a.cw[2 * i + 1], xv, a.sv[2 * i + 1], a.bv[2 * i + 1], xsv, true,
+                                  odd),
+          negz);
+      swiglu_push<FAST>(store, batch, lane, g, u, p0 + i);
+    }
+  }
+}
+
+// Stage A over the wave's pairs [pb, pe) in blocks of kGuPairs; `a` holds
+// the first block's loads.
+template <bool FAST, bool PAIRS, class Store>
+__device__ __forceinline__ void gu_stage(const DecodeLayer &L, const float *xv, float xsv, int lane,
+                                         int pb, int pe, GuBlock &a, const Store &store) {
+  const int negz = neg_zero_reg();
+  SwigluBatch batch;
+  for (int p = pb; p < pe; p += kGuPairs) {
+    const int np = min(kGuPairs, pe - p);
+    if (p != pb) load_gu(L, p, np, lane, a);
+    gu_block<FAST, PAIRS>(a, xv, xsv, lane, p, np, store, batch, negz);
+  }
+  swiglu_flush<FAST>(store, batch);
+}
+
+// Stage B: the wave's down row from `d` and the activations in LDS: T over
+// each pass's 32 group terms, then the -0-padded balanced tree over the
+// passes (T over all groups); valid in lane 63.
+template <int NP, bool FAST, bool PAIRS>
+__device__ __forceinline__ float down_row(const Lds<NP> &S, int lane, const DownRow<NP> &d) {
+  constexpr int PP = NP == 1 ? 1 : NP == 2 ? 2 : 4;
+  const int negz = neg_zero_reg();
+  const bool odd = lane & 1;
+  float v[PP];
+#pragma unroll
+  for (int p = 0; p < PP; ++p) {
+    if (p < NP) {
+      float xv[32];
+      load_x_values(S.x + (p * 64 + lane) * kChunkStride, true, xv);
+      const float xsv = S.xs[p * 32 + (lane >> 1)];
+      v[p] = wave_sum_lane63(group_term<FAST, PAIRS>(d.cw[p], xv, d.sv[p], d.bv[p], xsv, true, odd),
+                             negz);
+      issue_order();  // one pass's activations in registers at a time
+    } else {
+      v[p] = kNegZero;
+    }
+  }
+#pragma unroll
+  for (int w = 1; w < PP; w *= 2)
+#pragma unroll
+    for (int i = 0; i < PP; i += 2 * w) v[i] = v[i] + v[i + w];
+  return v[0];
+}
+
+// e[c] of the embedding row tk (the embed kernel's arithmetic; NaN for a
+// token outside the vocabulary).
+__device__ __forceinline__ float embed_value(const DecodeArgs &A, int tk, int c) {
+  if (tk < 0 || tk >= A.vocab) return __builtin_nanf("");
+  const uint32_t word = A.eq[(size_t)tk * 256 + (c >> 3)];
+  const float code = (float)((word >> (4 * (c & 7))) & 15u);
+  const float sq = A.es[(size_t)tk * 32 + (c >> 6)] * code;
+  return sq + A.eb[(size_t)tk * 32 + (c >> 6)];
+}
+
+template <bool FAST, int NP>
+__global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
+  __shared__ Lds<NP> S;
+  const int nwg = gridDim.x;
+  const int wg = blockIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = wave_index();
+  uint32_t *err = A.ctl + kDecodeErrorWord;
+  if (__syncthreads_or(load_word(err) != 0)) return;
+  const uint32_t call = load_word(A.ctl + wg);
+  const uint32_t tag0 = call << 6;
+
+  // wave gw = wave * nwg + wg (consecutive gw on different compute units)
+  // takes a balanced contiguous range of the inter (gate, up) pairs and
+  // the down row gw (the launch has at least 2048 waves)
+  const int gw = wave * nwg + wg;
+  const int stride = kWaves * nwg;
+  const int pb = (int)(((long long)A.inter * gw) / stride);
+  const int pe = (int)(((long long)A.inter * (gw + 1)) / stride);
+  const int row = gw;
+  const bool has_row = row < kCols;
+  const bool mine = 8 * t < kCols;  // threads 0..255 own 8 values of h each
+  const int tk = *A.tok;
+
+  GuBlock a;
+  DownRow<NP> d;
+  if (pb < pe) load_gu(A.layer[0], pb, min(kGuPairs, pe - pb), lane, a);
+  // the residual of the wave's row (lane 63): h before the layer
+  float res = has_row && lane == kWave - 1 ? embed_value(A, tk, row) : 0.0f;
+
+  for (int l = 0; l < A.nlayers; ++l) {
+    const DecodeLayer &L = A.layer[l];
+    uint64_t *mq = A.mq + (size_t)(l & 1) * A.inter;
+
+    // ---- stage A: u = rmsq(h, wn) in LDS; m = SwiGLU of the gate/up rows
+    float hv[8], wv[8];
+    bool ok = true;
+    if (mine) {
+      if (l == 0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) hv[k] = embed_value(A, tk, 8 * t + k);
+      } else {
+        ok = poll_tagged<8>(A.hq + (size_t)((l - 1) & 1) * kCols + 8 * t, tag0 + 2 * l, hv, err,
+                            A.spin_ticks);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) wv[k] = L.wn[8 * t + k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) hv[k] = wv[k] = 0.0f;
+    }
+    issue_order();
+    if (has_row) load_down<NP>(L, row, lane, d);
+    if (!__syncthreads_and(ok)) return;
+    const float rho = ops::rmsq_rho_regs(hv, kCols, A.eps, S.red);
+    ops::rmsq_u<4>(kCols, rho, hv, wv, S.x, S.xs);
+    __syncthreads();
+    {
+      float xv[32];
+      load_x_values(S.x + kChunkStride * lane, true, xv);
+      const float xsv = S.xs[lane >> 1];
+      const uint32_t tag = tag0 + 2 * l + 1;
+      const auto store_m = [mq, tag](int i, float v) { store_tagged(mq + i, v, tag); };
+      if (pb < pe) {
+        if (prescale_for_pairs(xv))
+          gu_stage<FAST, true>(L, xv, xsv, lane, pb, pe, a, store_m);
+        else
+          gu_stage<FAST, false>(L, xv, xsv, lane, pb, pe, a, store_m);
+      }
+    }
+
+    // ---- stage B: m and its group sums into LDS; h = h + down m
+    // chunk c = 8 consecutive values of m; chunks t and t + kThreads
+    constexpr int kChunks = NP * kCols / 8;
+    float xm[2][8];
+    ok = true;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int c = t + r * kThreads;
+      if (c < kChunks) ok &= poll_tagged<8>(mq + 8 * c, tag0 + 2 * l + 1, xm[r], err, A.spin_ticks);
+    }
+    issue_order();
+    if (l + 1 < A.nlayers && pb < pe)
+      load_gu(A.layer[l + 1], pb, min(kGuPairs, pe - pb), lane, a);
+    if (!__syncthreads_and(ok)) return;
+    // group sums: T over each chunk, then over 8 chunks by a butterfly
+    // (the balanced tree over the group's 64 values)
+    bool large = false;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int c = t + r * kThreads;
+      if (r * kThreads < kChunks) {  // uniform per round: 8 aligned chunks per group
+        float g = c < kChunks ? ops::tree8(xm[r]) : 0.0f;
+        g = g + __shfl_xor(g, 1);
+        g = g + __shfl_xor(g, 2);
+        g = g + __shfl_xor(g, 4);
+        if (c < kChunks && (c & 7) == 0) S.xs[c >> 3] = g;
+        if (c < kChunks) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) large |= !(__builtin_fabsf(xm[r][k]) < 0x1p118f);
+        }
+      }
+    }
+    // pre-scaled for the pair decode unless some value of the workgroup is
+    // large
+    const bool pairs = !__syncthreads_or(large);
+    {
+      const float scale = pairs ? 1.0f / fp8_unit() : 1.0f;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int c = t + r * kThreads;
+        if (c < kChunks) {
+          // value i of m sits at i + 4 (i / 32) in the padded layout
+          float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * c + 4 * (c >> 2));
+          dst[0] = make_float4(xm[r][0] * scale, xm[r][1] * scale, xm[r][2] * scale,
+                               xm[r][3] * scale);
+          dst[1] = make_float4(xm[r][4] * scale, xm[r][5] * scale, xm[r][6] * scale,
+                               xm[r][7] * scale);
+        }
+      }
+    }
+    __syncthreads();
+    if (has_row) {
+      const float v = pairs ? down_row<NP, FAST, true>(S, lane, d)
+                            : down_row<NP, FAST, false>(S, lane, d);
+      if (lane == kWave - 1) {
+        res = res + v;
+        if (l + 1 < A.nlayers)
+          store_tagged(A.hq + (size_t)(l & 1) * kCols + row, res, tag0 + 2 * l + 2);
+        else
+          A.h[row] = res;
+      }
+    }
+    // the next stage A writes S.x (all reads of it above are done)
+    __syncthreads();
+  }
+  if (t == 0) store_word(A.ctl + wg, call + 1);
+}
+
+template <bool FAST, int NP>
+const void *kernel_ptr() {
+  return reinterpret_cast<const void *>(&decode_layers_kernel<FAST, NP>);
+}
+
+const void *decode_kernel(int mode, int np) {
+  const bool fast = mode != 0;
+  switch (np) {
+    case 1: return fast ? kernel_ptr<true, 1>() : kernel_ptr<false, 1>();
+    case 2: return fast ? kernel_ptr<true, 2>() : kernel_ptr<false, 2>();
+    case 3: return fast ? kernel_ptr<true, 3>() : kernel_ptr<false, 3>();
+    case 4: return fast ? kernel_ptr<true, 4>() : kernel_ptr<false, 4>();
+    default: return nullptr;
+  }
+}
+
+}  // namespace
+
+int32_t decode_layers_grid(int mode, int32_t inter) {
+  const void *k = decode_kernel(mode, inter / kCols);
+  if (!k || inter % kCols) return 0;
+  int dev = 0, per_cu = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  // one workgroup per compute unit, and a wave for every down row
+  if (per_cu < 1 || cus * kWaves < kCols || cus > kDecodeMaxGroups) return 0;
+  return cus;
+}
+
+hipError_t launch_decode_layers(const DecodeArgs &a, int mode, hipStream_t st) {
+  const int np = a.inter / kCols;
+  const int32_t grid = decode_layers_grid(mode, a.inter);
+  if (grid < 1) return hipErrorInvalidValue;
+  const dim3 g(grid), b(kThreads);
+#define Q4_DECODE_CASE(NP_)                                                           \
+  case NP_:                                                                           \
+    if (mode != 0)                                                                    \
+      hipLaunchKernelGGL((decode_layers_kernel<true, NP_>), g, b, 0, st, a);          \
+    else                                                                              \
+      hipLaunchKernelGGL((decode_layers_kernel<false, NP_>), g, b, 0, st, a);         \
+    break;
+  switch (np) {
+    Q4_DECODE_CASE(1)
+    Q4_DECODE_CASE(2)
+    Q4_DECODE_CASE(3)
+    Q4_DECODE_CASE(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef Q4_DECODE_CASE
+  return hipGetLastError();
+}
+
+}  // namespace q4

@@ -330,6 +330,92 @@ int q4_embed(const q4_mat *w, const int32_t *tok, float *e, void *stream) {
   return hip_status(q4::launch_embed(p, tok, e, static_cast<hipStream_t>(stream)));
 }
 
+size_t q4_decode_layers_ws_bytes(void) { return q4::kDecodeWsBytes; }
+
+int q4_decode_layers(const q4_mat *emb, const int32_t *tok, const q4_mlp_layer *layers,
+                     int32_t nlayers, float eps, float *h, void *ws, size_t ws_bytes, int mode,
+                     void *stream) {
+  if (mode != Q4_FIXED && mode != Q4_FAST) return Q4_EINVAL;
+  int rc = check_mat(emb);
+  if (rc != Q4_OK) return rc;
+  if (emb->cols != 2048) return Q4_EINVAL;
+  if (!layers || nlayers < 1 || nlayers > Q4_MAX_DECODE_LAYERS) return Q4_EINVAL;
+  if (!tok || !aligned(tok, 4) || !h || !aligned(h, 4)) return Q4_EINVAL;
+  if (!ws || !aligned(ws, 16) || ws_bytes < q4::kDecodeWsBytes) return Q4_EINVAL;
+  const int32_t inter = layers[0].down.cols;
+  if (inter < 2048 || inter % 2048 != 0 || inter > q4::kDecodeMaxInter) return Q4_EINVAL;
+  const size_t hb = sizeof(float) * 2048;
+  // h and ws are written: they may overlap nothing else
+  const void *outs[2] = {h, ws};
+  const size_t outb[2] = {hb, q4::kDecodeWsBytes};
+  if (overlap(h, hb, ws, q4::kDecodeWsBytes)) return Q4_EINVAL;
+  for (int i = 0; i < 2; ++i)
+    if (overlaps_mat(outs[i], outb[i], emb) || overlap(outs[i], outb[i], tok, 4)) return Q4_EINVAL;
+  q4::DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  for (int l = 0; l < nlayers; ++l) {
+    const q4_mlp_layer &L = layers[l];
+    if (check_mat(&L.gate_up) != Q4_OK || check_mat(&L.down) != Q4_OK) return Q4_EINVAL;
+    if (L.gate_up.cols != 2048 || L.gate_up.rows != 2 * inter) return Q4_EINVAL;
+    if (L.down.rows != 2048 || L.down.cols != inter) return Q4_EINVAL;
+    if (!L.wn || !aligned(L.wn, 4)) return Q4_EINVAL;
+    for (int i = 0; i < 2; ++i)
+      if (overlaps_mat(outs[i], outb[i], &L.gate_up) || overlaps_mat(outs[i], outb[i], &L.down) ||
+          overlap(outs[i], outb[i], L.wn, hb))
+        return Q4_EINVAL;
+    a.layer[l] = q4::DecodeLayer{L.gate_up.q, L.gate_up.s, L.gate_up.b, L.wn,
+                                 L.down.q,    L.down.s,    L.down.b};
+  }
+  a.nlayers = nlayers;
+  a.inter = inter;
+  a.eq = emb->q;
+  a.es = emb->s;
+  a.eb = emb->b;
+  a.vocab = emb->rows;
+  a.tok = tok;
+  a.h = h;
+  char *w = static_cast<char *>(ws);
+  a.hq = reinterpret_cast<uint64_t *>(w + q4::kDecodeHqOffset);
+  a.mq = reinterpret_cast<uint64_t *>(w + q4::kDecodeMqOffset);
+  a.ctl = reinterpret_cast<uint32_t *>(w + q4::kDecodeCtlOffset);
+  a.eps = eps;
+  // bound of one wait: Q4_DECODE_TIMEOUT_MS (default 2000, at most 60000)
+  // of the device's constant wall clock; a negative value makes every wait
+  // that does not find its data at the first look run out (a test of that
+  // path)
+  long long ms = 2000;
+  if (const char *v = getenv("Q4_DECODE_TIMEOUT_MS")) ms = atoll(v);
+  if (ms > 60000) ms = 60000;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return Q4_EHIP;
+  a.spin_ticks = ms < 0 ? -1 : ms * (long long)(khz > 0 ? khz : 100000);
+  if (q4::decode_layers_grid(mode, inter) < 1) return Q4_EINVAL;  // too few compute units
+  return hip_status(q4::launch_decode_layers(a, mode, static_cast<hipStream_t>(stream)));
+}
+
+int q4_decode_layers_status(void *ws, void *stream) {
+  if (!ws || !aligned(ws, 16)) return Q4_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return Q4_EHIP;
+  if (cs != hipStreamCaptureStatusNone) return Q4_ESTATE;
+  if (hipStreamSynchronize(st) != hipSuccess) return Q4_EHIP;
+  uint32_t err = 0;
+  const char *ctl = static_cast<const char *>(ws) + q4::kDecodeCtlOffset;
+  if (hipMemcpy(&err, ctl + 4 * q4::kDecodeErrorWord, sizeof(err), hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return Q4_EHIP;
+  if (err == 0) return Q4_OK;
+  // the tagged words and the call counter are left in an unknown state:
+  // clear the whole workspace for reuse
+  if (hipMemsetAsync(ws, 0, q4::kDecodeWsBytes, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return Q4_EHIP;
+  return Q4_ETIMEOUT;
+}
+
 int q4_queue_create(void *stream, int mode, q4_queue **out) {
   if (!out || (mode != Q4_FIXED && mode != Q4_FAST)) return Q4_EINVAL;
   *out = nullptr;
@@ -463,7 +549,7 @@ const char *q4_strerror(int code) {
     case Q4_OK: return "ok";
     case Q4_EINVAL: return "invalid argument (nothing was launched)";
     case Q4_EHIP: return "HIP runtime error";
-    case Q4_ETIMEOUT: return "host wait timed out";
+    case Q4_ETIMEOUT: return "a bounded wait timed out";
     case Q4_ESTATE: return "call not legal in the current state (e.g. host wait during capture)";
     case Q4_ENOMEM: return "host allocation failed";
     default: return "unknown status";

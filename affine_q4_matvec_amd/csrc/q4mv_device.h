@@ -306,19 +306,20 @@ struct SwigluBatch {
   int count = 0; // pairs held (wave-uniform)
 };
 
-template <bool FAST>
-__device__ __forceinline__ void swiglu_flush(float *m_out, SwigluBatch &b) {
+// `store(i, v)` writes output i (plain or tagged stores, by the caller).
+template <bool FAST, class Store>
+__device__ __forceinline__ void swiglu_flush(const Store &store, SwigluBatch &b) {
   if (b.count == 0) return;
-  if (b.out >= 0) m_out[b.out] = ops::swiglu_value<FAST>(b.gate, b.up);
+  if (b.out >= 0) store(b.out, ops::swiglu_value<FAST>(b.gate, b.up));
   b.out = -1;
   b.count = 0;
 }
 
 // Appends the pair (gate, up) for m[out], both held by lane 63, to slot
 // b.count (lane b.count takes them).
-template <bool FAST>
-__device__ __forceinline__ void swiglu_push(float *m_out, SwigluBatch &b, int lane, float gate,
-                                            float up, int out) {
+template <bool FAST, class Store>
+__device__ __forceinline__ void swiglu_push(const Store &store, SwigluBatch &b, int lane,
+                                            float gate, float up, int out) {
   const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gate), kWave - 1));
   const float u = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(up), kWave - 1));
   const bool mine = lane == b.count;
@@ -326,7 +327,7 @@ __device__ __forceinline__ void swiglu_push(float *m_out, SwigluBatch &b, int la
   b.up = mine ? u : b.up;
   b.out = mine ? out : b.out;
   b.count = b.count + 1;
-  if (b.count == kWave) swiglu_flush<FAST>(m_out, b);
+  if (b.count == kWave) swiglu_flush<FAST>(store, b);
 }
 
 // Blocks of R rows dealt round-robin to the waves: r0, r0 + stride, ...

@@ -89,4 +89,42 @@ hipError_t launch_argmax_final(const unsigned long long *keys, int32_t nkeys, in
                                hipStream_t st);
 hipError_t launch_embed(const Prod &w, const int32_t *tok, float *e, hipStream_t st);
 
+// The MLP layers of a decode step in one persistent launch (decode_layers.hip).
+constexpr int kMaxDecodeLayers = 32;
+struct DecodeLayer {
+  const uint32_t *gq;  // gate/up rows interleaved: [2*inter][256] codes
+  const float *gs, *gb;
+  const float *wn;     // [2048] norm weights
+  const uint32_t *dq;  // down: [2048][inter/8] codes
+  const float *ds, *db;
+};
+struct DecodeArgs {
+  DecodeLayer layer[kMaxDecodeLayers];
+  int32_t nlayers;
+  int32_t inter;        // 2048, 4096, 6144 or 8192
+  const uint32_t *eq;   // embedding rows: [vocab][256] codes
+  const float *es, *eb;
+  int32_t vocab;
+  const int32_t *tok;   // [1] token read on the device
+  float *h;             // [2048] hidden state after the last layer (output)
+  uint64_t *hq;         // workspace: [2][2048] tagged h between layers, by parity
+  uint64_t *mq;         // workspace: [2][inter] tagged m, by layer parity
+  uint32_t *ctl;        // workspace: call counters and error word
+  float eps;
+  long long spin_ticks; // bound of one wait in wall-clock ticks
+};
+// Workspace layout (bytes): two tagged h buffers, two tagged m buffers of
+// the widest inter, then the control words: one call counter per workgroup (at most
+// kDecodeMaxGroups) and the error word on a 128-byte line of its own.
+constexpr int kDecodeMaxInter = 8192;
+constexpr int kDecodeMaxGroups = 1024;
+constexpr size_t kDecodeHqOffset = 0;
+constexpr size_t kDecodeMqOffset = 2 * 8 * 2048;
+constexpr size_t kDecodeCtlOffset = kDecodeMqOffset + 2 * 8 * (size_t)kDecodeMaxInter;
+constexpr int kDecodeErrorWord = kDecodeMaxGroups + 32;
+constexpr size_t kDecodeWsBytes = kDecodeCtlOffset + 4 * (kDecodeErrorWord + 32);
+// Workgroups of the persistent launch for this mode and width (0: none fit).
+int32_t decode_layers_grid(int mode, int32_t inter);
+hipError_t launch_decode_layers(const DecodeArgs &a, int mode, hipStream_t st);
+
 }  // namespace q4

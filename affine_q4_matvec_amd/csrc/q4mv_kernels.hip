@@ -121,6 +121,8 @@ __device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, const
   const bool odd = lane & 1;
   const int negz = neg_zero_reg();
   SwigluBatch batch;
+  float *m_out = ex.m_out;
+  const auto store_m = [m_out](int i, float v) { m_out[i] = v; };
   for (int r = r0; r < end; r += stride) {
     const int nrows = min(R, end - r);
     if (!PRELOAD || r != r0) row64_load<R>(P, r, nrows, voff_q, voff_g, a);
@@ -132,7 +134,7 @@ __device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, const
     if constexpr (EPI == kEpiSwiglu) {
 #pragma unroll
       for (int j = 0; j + 1 < R; j += 2)
-        if (j + 1 < nrows) swiglu_push<FAST>(ex.m_out, batch, lane, tot[j], tot[j + 1], (r + j) >> 1);
+        if (j + 1 < nrows) swiglu_push<FAST>(store_m, batch, lane, tot[j], tot[j + 1], (r + j) >> 1);
     } else if (lane == kWave - 1) {
 #pragma unroll
       for (int j = 0; j < R; ++j) {
@@ -152,7 +154,7 @@ __device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, const
       }
     }
   }
-  if constexpr (EPI == kEpiSwiglu) swiglu_flush<FAST>(ex.m_out, batch);
+  if constexpr (EPI == kEpiSwiglu) swiglu_flush<FAST>(store_m, batch);
 }
 
 // PRELOAD: issue the first block's loads before the activations are formed

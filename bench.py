@@ -16,8 +16,10 @@ into the product's prologue (one kernel per step).
 
 Also reported: the 24-layer decode chain (rmsq -> [gate;up] q4mv -> swq ->
 down q4mv + residual, then rmsq -> head q4mv -> argmax), captured once as a
-HIP graph, in ms per token over 200 tokens; and the CPU oracle timed on the
-host's cores on the head workload.
+HIP graph, in ms per token over 200 tokens, for two engines: the fused
+per-stage kernels (2 per layer) and the persistent layer kernel (one launch
+for all layers); and the CPU oracle timed on the host's cores on the head
+workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -164,28 +166,17 @@ def run_head(args, q4, torch, synth):
     return step_ms, kern_ms, fused_ms, same
 
 
-def run_chain(args, q4, torch, synth):
-    import numpy as np
-
-    from affine_q4_matvec_amd.chain import DecodeChain
-
-    log("generating decode-chain weights (24 layers, seed %d)" % args.seed)
-    w = synth.chain_weights(seed=args.seed)
-    mode = q4.FAST if args.mode == "fast" else q4.FIXED
-    chain = DecodeChain(w, mode=mode)
-    del w
+def time_chain(args, q4, torch, chain, tok0):
+    """Token rate of one decode-chain engine: (a) with one host wait per
+    token, (b) device time of the same captured step replayed back to back."""
     stream = torch.cuda.Stream()
     chain.capture(stream)
-    # warm-up tokens (not timed)
-    chain.run(0, 3, stream)
+    chain.run(0, 3, stream)  # warm-up tokens (not timed)
     torch.cuda.synchronize()
-    # (a) one host wait per token: replay, read the token, repeat
-    tok0 = chain_tok0(args.seed, synth)
     t0 = time.perf_counter()
     tokens = chain.run(tok0, args.chain_tokens, stream)
     per_token_sync_ms = (time.perf_counter() - t0) * 1e3 / args.chain_tokens
-    # (b) device time of the same replays queued back to back (the token
-    # stays on the device, so the chain is the same)
+    # the token stays on the device, so the queued replays decode the same chain
     chain.set_token(tok0)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -204,18 +195,41 @@ def run_chain(args, q4, torch, synth):
         n = min(len(ref["tokens"]), len(tokens))
         match = bool(ref["tokens"][:n] == tokens[:n])
     bpt = chain.bytes_per_token()
-    del np
-    return {
-        "tokens": args.chain_tokens, "layers": len(chain.layers),
+    out = {
         "ms_per_token_with_host_wait": round(per_token_sync_ms, 4),
         "ms_per_token_gpu": round(gpu_ms, 4),
-        "algorithmic_bytes_per_token": bpt,
         "gpu_GBps": round(bpt / (gpu_ms * 1e-3) / 1e9, 1),
         "kernels_per_token": chain.kernels_per_token(),
-        "fused": chain.fused,
         "tokens_match_oracle_golden": match,
         "queued_replays_reach_same_last_token": last == tokens[-1],
         "distinct_tokens": len(set(tokens)),
+    }
+    if chain.persistent:
+        out["barrier_status_ok"] = q4.q4_decode_layers_status(chain.stack_ws) == q4.Q4_OK
+    return out, bpt
+
+
+def run_chain(args, q4, torch, synth):
+    from affine_q4_matvec_amd.chain import DecodeChain
+
+    log("generating decode-chain weights (24 layers, seed %d)" % args.seed)
+    w = synth.chain_weights(seed=args.seed)
+    mode = q4.FAST if args.mode == "fast" else q4.FIXED
+    tok0 = chain_tok0(args.seed, synth)
+    engines, bpt = {}, None
+    for name in ("fused", "persistent"):
+        chain = DecodeChain(w, mode=mode, persistent=(name == "persistent"))
+        engines[name], bpt = time_chain(args, q4, torch, chain, tok0)
+        log("chain %s: %s" % (name, engines[name]))
+        del chain
+        torch.cuda.synchronize()
+    best = min(engines, key=lambda k: engines[k]["ms_per_token_gpu"])
+    return {
+        "tokens": args.chain_tokens, "layers": len(w["layers"]),
+        "algorithmic_bytes_per_token": bpt,
+        "best_engine": best,
+        "best_ms_per_token_gpu": engines[best]["ms_per_token_gpu"],
+        "engines": engines,
     }
 
 
@@ -276,7 +290,6 @@ def main() -> int:
     chain = None
     if not args.no_chain:
         chain = run_chain(args, q4, torch, synth)
-        log("chain: %s" % chain)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.seed)
     traffic = measured_traffic(qb)
     out = {

@@ -40,7 +40,7 @@ extern "C" {
 #define Q4_OK 0
 #define Q4_EINVAL (-1)   /* bad argument; nothing was launched            */
 #define Q4_EHIP (-2)     /* a HIP runtime call failed                     */
-#define Q4_ETIMEOUT (-3) /* a bounded host wait ran out of time           */
+#define Q4_ETIMEOUT (-3) /* a bounded wait (host or device) ran out       */
 #define Q4_ESTATE (-4)   /* call not legal now (e.g. host wait in capture) */
 #define Q4_ENOMEM (-5)   /* host allocation failed                        */
 
@@ -51,6 +51,7 @@ extern "C" {
 /* Size limits of this build. */
 #define Q4_MAX_COLS 32768 /* q4mv: cols <= 32768 (512 groups)          */
 #define Q4_MAX_RMSQ_N 8192 /* rmsq: n <= 8192                          */
+#define Q4_MAX_DECODE_LAYERS 32 /* q4_decode_layers: layers per call    */
 
 /*
  * One affine Q4 matrix ([P3] Why/Change: rows of 4-bit codes; [P1] Change:
@@ -180,6 +181,62 @@ int q4_argmax(const float *v, int32_t n, int32_t *idx, void *ws,
  * e with quiet NaNs.  tok: device int32[1]; e: device float[cols].
  */
 int q4_embed(const q4_mat *w, const int32_t *tok, float *e, void *stream);
+
+/*
+ * The MLP layers of a decode token as one persistent kernel ([P1] Change:
+ * rmsq, swq and the 4-row q4mv queued for a whole decode token; [P1]
+ * Verification: one command buffer and one wait per token).  Computes
+ *   h = e_tok  (the q4_embed row of *tok)
+ *   for each layer:  h = h + down * swq(gate_up * rmsq(h, wn))
+ * with the bits of the separate calls: q4_embed, then per layer
+ * q4mv_norm_swiglu(gate_up, h, wn, eps, m) and q4mv_add(down, m, NULL, h, h).
+ * One launch of one workgroup per compute unit (the device needs at least
+ * 256 of them); the stages hand their outputs to each other through tagged
+ * words in the workspace that the consumers poll, with no grid barrier, and
+ * each wave loads its next stage's weights before it waits.
+ *
+ *   emb     : host pointer to the embedding matrix (cols == 2048), the
+ *             decode head's tied weights.  A token outside [0, rows) makes
+ *             h NaN.
+ *   tok     : device int32[1], read on the device.
+ *   layers  : host array of nlayers (1..Q4_MAX_DECODE_LAYERS) descriptors,
+ *             read during the call.  gate_up: rows 2*inter, cols 2048, gate
+ *             row i at row 2i and up row i at row 2i+1.  down: rows 2048,
+ *             cols inter; inter (taken from layers[0].down.cols) is 2048,
+ *             4096, 6144 or 8192 and the same in every layer.  wn: device
+ *             float[2048].
+ *   h       : device float[2048]: the output (its prior contents are not
+ *             read).
+ *   ws      : device workspace of q4_decode_layers_ws_bytes() bytes (about
+ *             145 KB), 16-byte aligned, zero-filled before its first use;
+ *             each call leaves it ready for the next.  Calls that overlap in
+ *             time must not share it, and no other kernel should hold the
+ *             device's compute units while this one runs.
+ * h and ws must not overlap each other or any input.  Each wait for another
+ * workgroup's output is bounded (env Q4_DECODE_TIMEOUT_MS, default 2000, at
+ * most 60000; negative: no waiting at all, for tests of this path): when
+ * one runs out, every workgroup leaves the kernel and h is undefined;
+ * q4_decode_layers_status reports it.  A workspace whose error word is set
+ * makes the kernel return at once until the status call clears it.
+ * Q4_EINVAL also when the device has fewer than 256 compute units.
+ */
+typedef struct q4_mlp_layer {
+  q4_mat gate_up;
+  q4_mat down;
+  const float *wn;
+} q4_mlp_layer;
+size_t q4_decode_layers_ws_bytes(void);
+int q4_decode_layers(const q4_mat *emb, const int32_t *tok, const q4_mlp_layer *layers,
+                     int32_t nlayers, float eps, float *h, void *ws, size_t ws_bytes, int mode,
+                     void *stream);
+
+/*
+ * Waits for `stream` on the host, then returns Q4_ETIMEOUT if a wait of a
+ * q4_decode_layers call using `ws` ran out since the workspace was last
+ * cleared (and clears the whole workspace), else Q4_OK.  Q4_ESTATE during
+ * capture.
+ */
+int q4_decode_layers_status(void *ws, void *stream);
 
 /*
  * Stage queue ([P2] Change: q4go encodes products into one open concurrent

@@ -197,12 +197,10 @@ def fnv1a32(arr) -> int:
     return int(lib().orc_fnv1a32(arr.ctypes.data, arr.nbytes))
 
 
-def chain_step(w: dict, tok: int, nthreads: int = 1, layers: int | None = None):
-    """One decode-chain step from token ``tok``:
-    h = embed(head, tok); per layer: u = rmsq(h, wn); a = [gate u | up u];
-    m = swq(a); h = h + down m; then u = rmsq(h, wn_final),
-    logits = head u, next token = argmax(logits).
-    Returns ``(logits, next_token)``."""
+def chain_hidden(w: dict, tok: int, nthreads: int = 1, layers: int | None = None) -> np.ndarray:
+    """The hidden state after the embedding and the MLP layers of one
+    decode-chain step: h = embed(head, tok); per layer: u = rmsq(h, wn);
+    a = [gate u | up u]; m = swq(a); h = h + down m."""
     L = len(w["layers"]) if layers is None else layers
     inter = w["inter"]
     h = embed(w["head"], tok)
@@ -214,6 +212,14 @@ def chain_step(w: dict, tok: int, nthreads: int = 1, layers: int | None = None):
         a[inter:] = q4mv(lw["up"], u, us, nthreads)
         m, ms = swq(a, inter)
         h = add(h, q4mv(lw["down"], m, ms, nthreads))
+    return h
+
+
+def chain_step(w: dict, tok: int, nthreads: int = 1, layers: int | None = None):
+    """One decode-chain step from token ``tok``: the hidden state of
+    ``chain_hidden``, then u = rmsq(h, wn_final), logits = head u, next
+    token = argmax(logits).  Returns ``(logits, next_token)``."""
+    h = chain_hidden(w, tok, nthreads, layers)
     u, us = rmsq(h, w["wn_final"], w["eps"])
     logits = q4mv(w["head"], u, us, nthreads)
     return logits, argmax(logits)

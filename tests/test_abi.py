@@ -121,3 +121,54 @@ def test_strerror(L):
     assert L.q4_strerror(0) == b"ok"
     assert b"invalid" in L.q4_strerror(-1)
     assert L.q4_strerror(12345) == b"unknown status"
+
+
+class MlpLayer(ctypes.Structure):
+    _fields_ = [("gate_up", Mat), ("down", Mat), ("wn", ctypes.c_void_p)]
+
+
+def test_decode_layers_argument_checks(L):
+    p = lambda v: ctypes.c_void_p(v)
+    L.q4_decode_layers_ws_bytes.restype = ctypes.c_size_t
+    wsb = L.q4_decode_layers_ws_bytes()
+    assert 16 * 1024 <= wsb <= 256 * 1024
+    G = 0x7F1000000000  # a further disjoint region for the layer arrays
+    emb = mat(rows=4096, cols=2048)
+
+    def layers(n=2, inter=6144):
+        arr = (MlpLayer * n)()
+        for i in range(n):
+            base = G + i * 0x100000000
+            arr[i].gate_up = Mat(base, base + 0x10000000, base + 0x20000000, 2 * inter, 2048)
+            arr[i].down = Mat(base + 0x30000000, base + 0x40000000, base + 0x50000000, 2048, inter)
+            arr[i].wn = base + 0x60000000
+        return arr
+
+    def call(e=emb, tok=D, arr=None, n=2, h=E, ws=F, wsb=wsb, mode=0):
+        arr = layers(n) if arr is None else arr
+        return L.q4_decode_layers(ctypes.byref(e), p(tok), arr, n, ctypes.c_float(1e-6), p(h),
+                                  p(ws), ctypes.c_size_t(wsb), mode, None)
+
+    assert call(n=0) == EINVAL
+    assert call(n=33, arr=layers(33)) == EINVAL
+    assert call(e=mat(rows=4096, cols=1024)) == EINVAL          # embedding width
+    assert call(arr=layers(2, inter=3000)) == EINVAL            # inter not a multiple of 2048
+    assert call(arr=layers(2, inter=10240)) == EINVAL           # inter too wide
+    bad = layers(2)
+    bad[1].down = Mat(G + 0x130000000, G + 0x140000000, G + 0x150000000, 2048, 4096)
+    assert call(arr=bad) == EINVAL                              # inter differs between layers
+    bad = layers(2)
+    bad[0].gate_up = Mat(G, G + 0x10000000, G + 0x20000000, 6144, 2048)
+    assert call(arr=bad) == EINVAL                              # gate_up rows != 2 inter
+    bad = layers(2)
+    bad[1].wn = 0
+    assert call(arr=bad) == EINVAL                              # no norm weights
+    assert call(h=E + 2) == EINVAL                              # h misaligned
+    assert call(h=F + 1024) == EINVAL                           # h inside ws
+    assert call(ws=F + 8) == EINVAL                             # ws misaligned
+    assert call(wsb=wsb - 8) == EINVAL                          # ws too small
+    assert call(tok=0) == EINVAL
+    assert call(mode=2) == EINVAL
+    assert call(h=G + 0x30000000 + 64) == EINVAL                # h inside a down matrix
+    assert call(ws=G + 0x60000000 - 64) == EINVAL               # ws over the norm weights
+    assert L.q4_decode_layers_status(None, None) == EINVAL

@@ -55,7 +55,7 @@ def test_queue_product_set_two_layers_bit_exact():
 
 
 def test_queue_full_product_set_one_wait():
-    """configs[3]: 24 layers x 7 products + head, 97 stages, one host wait."""
+    """24 layers x 7 products + head, 97 stages, one host wait."""
     q4 = lib()
     ps = synth.product_set()
     assert ps["stages"] == 97 and len(ps["products"]) == 169
@@ -147,13 +147,14 @@ def oracle_chain(w, tok, steps, layers=None):
     return toks, logits
 
 
-def test_chain_two_layers_every_step_bit_exact():
+@pytest.mark.parametrize("persistent", [False, True])
+def test_chain_two_layers_every_step_bit_exact(persistent):
     DecodeChain = chain_cls()
     w = synth.chain_weights(seed=7, layers=2, vocab=8192)
     want_toks, want_logits = oracle_chain(w, w["tok0"], 12)
     assert len(set(want_toks)) > 3
     for use_graph in (False, True):
-        chain = DecodeChain(w)
+        chain = DecodeChain(w, persistent=persistent)
         got_logits = []
         toks = chain.run(w["tok0"], 12, torch.cuda.Stream(), use_graph=use_graph,
                          on_step=lambda i, c: got_logits.append(host(c.logits)))
@@ -198,15 +199,16 @@ def test_chain_full_depth_first_steps_bit_exact():
         assert_bits_equal(got[i], want_logits[i], "full chain logits step %d" % i)
 
 
-def test_chain_200_tokens_against_oracle_golden():
-    """configs[4]: 200 greedy steps in one captured graph; every token and
-    every step's logits hash equal the oracle's (tests/golden, written by
-    tests/golden/make_chain_golden.py from the oracle only)."""
+@pytest.mark.parametrize("persistent", [False, True])
+def test_chain_200_tokens_against_oracle_golden(persistent):
+    """200 greedy steps of the 24-layer chain in one captured graph; every
+    token and every step's logits hash equal the oracle's (tests/golden,
+    written by tests/golden/make_chain_golden.py from the oracle only)."""
     DecodeChain = chain_cls()
     ref = json.load(open(GOLDEN))
     w = synth.chain_weights(seed=ref["seed"])
     assert w["tok0"] == ref["tok0"]
-    chain = DecodeChain(w)
+    chain = DecodeChain(w, persistent=persistent)
     hashes = []
     toks = chain.run(ref["tok0"], len(ref["tokens"]), torch.cuda.Stream(),
                      on_step=lambda i, c: hashes.append(oracle.fnv1a32(host(c.logits))))

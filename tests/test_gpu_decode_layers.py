@@ -1,0 +1,181 @@
+"""GPU parity of the persistent decode-layers kernel (q4_decode_layers):
+the embedding and every MLP layer of a decode step in one launch whose
+workgroups hand m and h to each other through tagged words, against the
+oracle's separate steps (bit-exact in fixed mode), against the per-stage
+kernels in fast mode, inside a captured graph, and its bounded waits."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_bits_equal, dev, host, lib
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = 16
+
+
+def mlp_layers(q4, w, n=None):
+    from affine_q4_matvec_amd.chain import _interleave_rows
+    out = []
+    for lw in w["layers"][:n]:
+        gu = q4.Q4Matrix.from_host(_interleave_rows(lw["gate"], lw["up"]))
+        out.append(q4.MlpLayer(gu, q4.Q4Matrix.from_host(lw["down"]), dev(lw["wn"])))
+    return out
+
+
+def new_ws(q4):
+    return torch.zeros((q4.q4_decode_layers_ws_bytes() + 7) // 8, dtype=torch.int64,
+                       device="cuda")
+
+
+ERROR_WORD = (163840 + 4 * (1024 + 32)) // 4  # int32 index of the error word in the workspace
+
+
+def run_layers(q4, emb, layers, w, tok, mode=0, ws=None):
+    t = torch.tensor([tok], dtype=torch.int32, device="cuda")
+    h = torch.full((2048,), 7.0, device="cuda")
+    if ws is None:
+        ws = new_ws(q4)
+    q4.q4_decode_layers(emb, t, layers, w["eps"], h, ws, mode=mode)
+    assert q4.q4_decode_layers_status(ws) == q4.Q4_OK
+    return host(h), ws
+
+
+@pytest.mark.parametrize("inter,nlayers", [(2048, 1), (4096, 2), (6144, 3), (8192, 2)])
+def test_decode_layers_bit_exact(inter, nlayers):
+    q4 = lib()
+    w = synth.chain_weights(seed=40 + inter // 2048, layers=nlayers, inter=inter, vocab=3000)
+    emb = q4.Q4Matrix.from_host(w["head"])
+    layers = mlp_layers(q4, w)
+    ws = None
+    for tok in (w["tok0"], 0, 2999):
+        want = oracle.chain_hidden(w, tok, NTHREADS)
+        got, ws = run_layers(q4, emb, layers, w, tok, ws=ws)
+        print("decode_layers inter=%d layers=%d tok=%d" % (inter, nlayers, tok), flush=True)
+        assert_bits_equal(got, want, "h inter=%d layers=%d tok=%d" % (inter, nlayers, tok))
+
+
+def test_decode_layers_token_out_of_range_gives_nan():
+    q4 = lib()
+    w = synth.chain_weights(seed=45, layers=1, vocab=500)
+    emb = q4.Q4Matrix.from_host(w["head"])
+    got, _ = run_layers(q4, emb, mlp_layers(q4, w), w, 500)
+    assert np.all(np.isnan(got))
+    got, _ = run_layers(q4, emb, mlp_layers(q4, w), w, -1)
+    assert np.all(np.isnan(got))
+
+
+def test_decode_layers_fast_mode_equals_stage_kernels():
+    """Fast mode: the same code as the per-stage fused kernels, so the same
+    bits as q4mv_norm_swiglu + q4mv_add in fast mode; and within the fast
+    mode's error of the fixed result."""
+    q4 = lib()
+    w = synth.chain_weights(seed=46, layers=4, vocab=2000)
+    emb = q4.Q4Matrix.from_host(w["head"])
+    layers = mlp_layers(q4, w)
+    tok = w["tok0"]
+    got, _ = run_layers(q4, emb, layers, w, tok, mode=q4.FAST)
+    t = torch.tensor([tok], dtype=torch.int32, device="cuda")
+    h = q4.q4_embed(emb, t)
+    m = torch.empty(w["inter"], device="cuda")
+    for L in layers:
+        q4.q4mv_norm_swiglu(L.gate_up, h, L.wn, w["eps"], m, mode=q4.FAST)
+        q4.q4mv_add(L.down, m, None, h, h, mode=q4.FAST)
+    torch.cuda.synchronize()
+    assert_bits_equal(got, host(h), "fast decode_layers vs fast stage kernels")
+    want = oracle.chain_hidden(w, tok, NTHREADS)
+    err = np.abs(got.astype(np.float64) - want)
+    assert err.max() <= 1e-4 * np.sqrt(np.mean(want.astype(np.float64) ** 2)), err.max()
+
+
+def test_decode_layers_full_depth_matches_oracle():
+    """24 layers of 2048 x 6144 (the decode chain's layer stack)."""
+    q4 = lib()
+    w = synth.chain_weights(vocab=4096)
+    emb = q4.Q4Matrix.from_host(w["head"])
+    layers = mlp_layers(q4, w)
+    want = oracle.chain_hidden(w, w["tok0"], NTHREADS)
+    got, ws = run_layers(q4, emb, layers, w, w["tok0"])
+    assert_bits_equal(got, want, "h after 24 layers")
+    # repeated calls reuse the workspace (the barrier words return to rest)
+    for _ in range(3):
+        again, ws = run_layers(q4, emb, layers, w, w["tok0"], ws=ws)
+        assert_bits_equal(again, want, "h after 24 layers, again")
+
+
+def test_decode_layers_in_graph_replays():
+    q4 = lib()
+    w = synth.chain_weights(seed=47, layers=3, vocab=3000)
+    emb = q4.Q4Matrix.from_host(w["head"])
+    layers = mlp_layers(q4, w)
+    s = torch.cuda.Stream()
+    t = torch.zeros(1, dtype=torch.int32, device="cuda")
+    h = torch.empty(2048, device="cuda")
+    ws = new_ws(q4)
+    torch.cuda.synchronize()
+    g = q4.Graph(s)
+    g.begin()
+    try:
+        q4.q4_decode_layers(emb, t, layers, w["eps"], h, ws, stream=s)
+    finally:
+        g.end()
+    other = synth.small_product(seed=48, rows=200, cols=2048, name="between")
+    W = q4.Q4Matrix.from_host(other)
+    for tok in (5, 2999, 1234):
+        t.fill_(tok)
+        torch.cuda.synchronize()
+        g.launch(s)
+        s.synchronize()
+        assert_bits_equal(host(h), oracle.chain_hidden(w, tok, NTHREADS), "graph tok %d" % tok)
+        q4.q4mv(W, dev(other["x"]), None)  # eager work between replays
+        torch.cuda.synchronize()
+    assert q4.q4_decode_layers_status(ws) == q4.Q4_OK
+    g.close()
+
+
+def test_decode_layers_error_word_stops_the_kernel_and_is_cleared():
+    """A workspace whose error word is set: every workgroup returns at once,
+    the status call reports it and clears the workspace, the next call is
+    correct."""
+    q4 = lib()
+    w = synth.chain_weights(seed=49, layers=2, vocab=1000)
+    emb = q4.Q4Matrix.from_host(w["head"])
+    layers = mlp_layers(q4, w)
+    t = torch.tensor([3], dtype=torch.int32, device="cuda")
+    h = torch.full((2048,), 7.0, device="cuda")
+    ws = new_ws(q4)
+    ws.view(torch.int32)[ERROR_WORD] = 1
+    q4.q4_decode_layers(emb, t, layers, w["eps"], h, ws)
+    assert q4.q4_decode_layers_status(ws) == q4.Q4_ETIMEOUT
+    assert np.all(host(h) == 7.0)  # nothing ran
+    assert int(np.abs(host(ws)).max()) == 0  # cleared
+    got, _ = run_layers(q4, emb, layers, w, 3, ws=ws)
+    assert_bits_equal(got, oracle.chain_hidden(w, 3, NTHREADS), "after a cleared error")
+
+
+def test_decode_layers_wait_timeout_is_reported_and_cleared():
+    """No waiting allowed (bound set from the host): the first thread that
+    does not find its data at the first look sets the error word, every
+    workgroup leaves at its next wait, and the status call reports it.  (A
+    run can only escape this if every workgroup found every value it needs
+    already written; the 12 layers make that out of reach.)"""
+    q4 = lib()
+    w = synth.chain_weights(seed=50, layers=12, vocab=1000)
+    emb = q4.Q4Matrix.from_host(w["head"])
+    layers = mlp_layers(q4, w)
+    t = torch.tensor([3], dtype=torch.int32, device="cuda")
+    h = torch.empty(2048, device="cuda")
+    ws = new_ws(q4)
+    os.environ["Q4_DECODE_TIMEOUT_MS"] = "-1"
+    try:
+        q4.q4_decode_layers(emb, t, layers, w["eps"], h, ws)
+    finally:
+        del os.environ["Q4_DECODE_TIMEOUT_MS"]
+    assert q4.q4_decode_layers_status(ws) == q4.Q4_ETIMEOUT
+    assert int(np.abs(host(ws)).max()) == 0
+    got, _ = run_layers(q4, emb, layers[:2], {**w, "layers": w["layers"][:2]}, 3, ws=ws)
+    assert_bits_equal(got, oracle.chain_hidden(w, 3, NTHREADS, layers=2), "after a timeout")

@@ -156,7 +156,7 @@ def test_q4mv_add_residual():
 
 
 def test_q4mv_4096x2048_400_calls_hash():
-    """configs[1]: 400 calls, every output identical to the oracle; the FNV-1a
+    """4096 x 2048, 400 calls: every output identical to the oracle; the FNV-1a
     hash of the last output's bits equals the oracle's."""
     q4 = lib()
     m = synth.small_product(seed=synth.DEFAULT_SEED, rows=4096, cols=2048, name="c1")
@@ -174,7 +174,7 @@ def test_q4mv_4096x2048_400_calls_hash():
 
 
 def test_q4mv_head_248320x2048_full():
-    """configs[2]: the output head with x from rmsq; every row bit-exact."""
+    """The 248320 x 2048 output head with x from rmsq; every row bit-exact."""
     q4 = lib()
     h = synth.head_inputs()
     u, us = oracle.rmsq(h["z"], h["wn"], h["eps"])
