@@ -7,16 +7,18 @@
 // stage pays a launch and the cold start of its loads; here one grid of
 // resident workgroups (one per compute unit) runs every stage:
 //
-//   h = embed(tok)                          (each workgroup, from the weights)
-//   per layer:  u = rmsq(h, wn)              (each workgroup, into LDS)
+//   h = embed(tok)                          (each wave, from the weights)
+//   per layer:  u = rmsq(h, wn)              (each wave, in registers)
 //               m = SwiGLU([gate; up] u)     (rows in (gate, up) pairs)
 //               h = h + down m               (m staged in LDS per workgroup)
 //
 // Dataflow instead of grid barriers.  Every value one workgroup hands to
 // another (m of each layer, h between layers) is stored as a 64-bit word:
 // the float's bits and a 32-bit tag naming the call and the stage that
-// produced it, with one device-scope store (the sc1 cache policy: written
-// through to the memory side, where device-scope loads read it).  A
+// produced it, with device-scope stores (the sc1 cache policy: written
+// through to the memory side, where device-scope loads read it), in
+// kDecodeCopies copies of which each workgroup reads one (a cache line that
+// the whole grid polls at once serialises its readers).  A
 // consumer polls the words it needs with device-scope 64-bit loads until
 // each carries the expected tag: the wait and the data arrive in the same
 // load, and no cache write-back, invalidation or barrier is needed.  (On
@@ -42,9 +44,12 @@
 // the launch is resident.
 //
 // The weights of a stage do not depend on the previous one, so every wave
-// issues the loads of its next stage's rows right after the first loads of
-// its current wait (issued after them, so that the wait does not include
-// them: a wave's loads complete in issue order for its wait counter).
+// loads its next stage's rows ahead: the down row right after the wait for
+// h, the next layer's gate/up rows right after its gate/up products.  A
+// wave's loads complete in issue order for its wait counter, so a wait
+// issued after a prefetch also waits for the prefetch; the order above puts
+// each prefetch before the wait that is long anyway (for m), never before
+// the wait for h.
 //
 // Every value is computed by the same code as the per-stage kernels (rmsq
 // and SwiGLU from ops_device.h, group terms and row trees from
@@ -69,9 +74,8 @@ constexpr int kChunkStride = 36;  // LDS floats per 32-value chunk (4 of padding
 
 template <int NP>
 struct alignas(16) Lds {
-  float x[NP * 64 * kChunkStride];  // activations: u (stage A) or m (stage B)
-  float xs[NP * 32];                // their group sums
-  float red[17];
+  float x[NP * 64 * kChunkStride];  // h (stage A) or m (stage B)
+  float xs[NP * 32];                // the group sums of m
 };
 
 struct GuBlock {
@@ -259,6 +263,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
   const bool has_row = row < kCols;
   const bool mine = 8 * t < kCols;  // threads 0..255 own 8 values of h each
   const int tk = *A.tok;
+  const int copy = wg % kDecodeCopies;  // the copy of m and h this workgroup reads
 
   GuBlock a;
   DownRow<NP> d;
@@ -268,37 +273,56 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
 
   for (int l = 0; l < A.nlayers; ++l) {
     const DecodeLayer &L = A.layer[l];
-    uint64_t *mq = A.mq + (size_t)(l & 1) * A.inter;
+    uint64_t *mq = A.mq + (size_t)(l & 1) * kDecodeCopies * kDecodeMaxInter;  // copy 0
 
-    // ---- stage A: u = rmsq(h, wn) in LDS; m = SwiGLU of the gate/up rows
-    float hv[8], wv[8];
+    // ---- stage A: x = rmsq(h, wn), each wave for itself (lane l: columns
+    // [32 l, 32 l + 32)); m = SwiGLU of the gate/up rows
     bool ok = true;
-    if (mine) {
-      if (l == 0) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) hv[k] = embed_value(A, tk, 8 * t + k);
-      } else {
-        ok = poll_tagged<8>(A.hq + (size_t)((l - 1) & 1) * kCols + 8 * t, tag0 + 2 * l, hv, err,
-                            A.spin_ticks);
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) wv[k] = L.wn[8 * t + k];
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) hv[k] = wv[k] = 0.0f;
+    float wv[32];
+    load_x_values(L.wn + 32 * lane, true, wv);
+    if (l > 0 && mine) {
+      // threads 0..255 fetch h (8 values each) into LDS, value i at
+      // i + 4 (i / 32)
+      float hv[8];
+      ok = poll_tagged<8>(A.hq + ((size_t)((l - 1) & 1) * kDecodeCopies + copy) * kCols + 8 * t,
+                          tag0 + 2 * l, hv, err, A.spin_ticks);
+      float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * t + 4 * (t >> 2));
+      dst[0] = make_float4(hv[0], hv[1], hv[2], hv[3]);
+      dst[1] = make_float4(hv[4], hv[5], hv[6], hv[7]);
     }
     issue_order();
     if (has_row) load_down<NP>(L, row, lane, d);
-    if (!__syncthreads_and(ok)) return;
-    const float rho = ops::rmsq_rho_regs(hv, kCols, A.eps, S.red);
-    ops::rmsq_u<4>(kCols, rho, hv, wv, S.x, S.xs);
-    __syncthreads();
+    float hv[32];
+    if (l == 0) {
+      // the embedding row of the token (the embed kernel's arithmetic)
+      const bool valid = tk >= 0 && tk < A.vocab;
+      const size_t er = valid ? (size_t)tk : 0;
+      const float sg = valid ? A.es[er * 32 + (lane >> 1)] : 0.0f;
+      const float bg = valid ? A.eb[er * 32 + (lane >> 1)] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t word = valid ? A.eq[er * 256 + 4 * lane + j] : 0u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float sq = sg * (float)((word >> (4 * i)) & 15u);
+          hv[8 * j + i] = valid ? sq + bg : __builtin_nanf("");
+        }
+      }
+    } else {
+      if (!__syncthreads_and(ok)) return;
+      load_x_values(S.x + kChunkStride * lane, true, hv);
+    }
     {
+      const float rho = ops::rmsq_rho_wave2048(hv, A.eps);
       float xv[32];
-      load_x_values(S.x + kChunkStride * lane, true, xv);
-      const float xsv = S.xs[lane >> 1];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) xv[k] = ops::rmsq_value(hv[k], rho, wv[k]);
+      const float xsv = pair_group_sum(xv);
       const uint32_t tag = tag0 + 2 * l + 1;
-      const auto store_m = [mq, tag](int i, float v) { store_tagged(mq + i, v, tag); };
+      const auto store_m = [mq, tag](int i, float v) {
+#pragma unroll
+        for (int c = 0; c < kDecodeCopies; ++c) store_tagged(mq + c * kDecodeMaxInter + i, v, tag);
+      };
       if (pb < pe) {
         if (prescale_for_pairs(xv))
           gu_stage<FAST, true>(L, xv, xsv, lane, pb, pe, a, store_m);
@@ -307,19 +331,27 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
       }
     }
 
+    // the next layer's gate/up rows: issued before this wave's next wait for
+    // m, which they would otherwise delay in the wait for h after it
+    if (l + 1 < A.nlayers && pb < pe)
+      load_gu(A.layer[l + 1], pb, min(kGuPairs, pe - pb), lane, a);
+    issue_order();
+
     // ---- stage B: m and its group sums into LDS; h = h + down m
     // chunk c = 8 consecutive values of m; chunks t and t + kThreads
     constexpr int kChunks = NP * kCols / 8;
     float xm[2][8];
     ok = true;
+    // the workgroup polls only once all its waves are done with stage A (a
+    // poll that starts early only adds traffic at the lines being polled)
+    __syncthreads();
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int c = t + r * kThreads;
-      if (c < kChunks) ok &= poll_tagged<8>(mq + 8 * c, tag0 + 2 * l + 1, xm[r], err, A.spin_ticks);
+      if (c < kChunks)
+        ok &= poll_tagged<8>(mq + (size_t)copy * kDecodeMaxInter + 8 * c, tag0 + 2 * l + 1, xm[r],
+                             err, A.spin_ticks);
     }
-    issue_order();
-    if (l + 1 < A.nlayers && pb < pe)
-      load_gu(A.layer[l + 1], pb, min(kGuPairs, pe - pb), lane, a);
     if (!__syncthreads_and(ok)) return;
     // group sums: T over each chunk, then over 8 chunks by a butterfly
     // (the balanced tree over the group's 64 values)
@@ -364,7 +396,10 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
       if (lane == kWave - 1) {
         res = res + v;
         if (l + 1 < A.nlayers)
-          store_tagged(A.hq + (size_t)(l & 1) * kCols + row, res, tag0 + 2 * l + 2);
+#pragma unroll
+          for (int c = 0; c < kDecodeCopies; ++c)
+            store_tagged(A.hq + ((size_t)(l & 1) * kDecodeCopies + c) * kCols + row, res,
+                         tag0 + 2 * l + 2);
         else
           A.h[row] = res;
       }

@@ -32,6 +32,12 @@ __device__ __forceinline__ float tree8(const float *v) {
 //   ss = T(h*h); ms = ss / n; rho = 1 / sqrt(ms + eps)  (correctly rounded);
 //   u_i = (h_i * rho) * w_i; us_g = T(u[64g .. 64g+63]).
 
+// rho from the sum of squares ss of the n values.
+__device__ __forceinline__ float rmsq_rho_from_ss(float ss, int n, float eps) {
+  const float ms = ss / (float)n;
+  return 1.0f / sqrtf(ms + eps);
+}
+
 // The first half: rho, in every thread, from the thread's 8 slots of h
 // already in registers (hv; slots >= n must hold 0).  red is LDS scratch of
 // 17 floats; every thread of the workgroup must call it (two barriers).
@@ -55,8 +61,7 @@ __device__ __forceinline__ float rmsq_rho_regs(const float *hv, int n, float eps
     red[16] = red[0];
   }
   __syncthreads();
-  const float ms = red[16] / (float)n;
-  return 1.0f / sqrtf(ms + eps);
+  return rmsq_rho_from_ss(red[16], n, eps);
 }
 
 // The same, loading the thread's 8 slots of h and of w together up front
@@ -72,6 +77,19 @@ __device__ __forceinline__ float rmsq_rho(const float *__restrict__ h,
     wv[k] = i < n ? w[i] : 0.0f;
   }
   return rmsq_rho_regs(hv, n, eps, red);
+}
+
+// rho of 2048 values by one wave without LDS: lane l holds values
+// [32 l, 32 l + 32) in hv.  The same tree as rmsq_rho_regs (the balanced
+// tree over the 2048 squares in index order), so the same bits.
+__device__ __forceinline__ float rmsq_rho_wave2048(const float *hv, float eps) {
+  float sq[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) sq[k] = hv[k] * hv[k];
+  float s = (tree8(sq) + tree8(sq + 8)) + (tree8(sq + 16) + tree8(sq + 24));
+#pragma unroll
+  for (int m = 1; m < kWave; m *= 2) s = s + __shfl_xor(s, m);
+  return rmsq_rho_from_ss(s, 2048, eps);
 }
 
 // One normalised value: (h * rho) * w.

@@ -358,7 +358,7 @@ int q4_decode_layers(const q4_mat *emb, const int32_t *tok, const q4_mlp_layer *
     if (check_mat(&L.gate_up) != Q4_OK || check_mat(&L.down) != Q4_OK) return Q4_EINVAL;
     if (L.gate_up.cols != 2048 || L.gate_up.rows != 2 * inter) return Q4_EINVAL;
     if (L.down.rows != 2048 || L.down.cols != inter) return Q4_EINVAL;
-    if (!L.wn || !aligned(L.wn, 4)) return Q4_EINVAL;
+    if (!L.wn || !aligned(L.wn, 16)) return Q4_EINVAL;
     for (int i = 0; i < 2; ++i)
       if (overlaps_mat(outs[i], outb[i], &L.gate_up) || overlaps_mat(outs[i], outb[i], &L.down) ||
           overlap(outs[i], outb[i], L.wn, hb))

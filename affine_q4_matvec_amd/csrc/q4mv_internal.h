@@ -107,20 +107,25 @@ struct DecodeArgs {
   int32_t vocab;
   const int32_t *tok;   // [1] token read on the device
   float *h;             // [2048] hidden state after the last layer (output)
-  uint64_t *hq;         // workspace: [2][2048] tagged h between layers, by parity
-  uint64_t *mq;         // workspace: [2][inter] tagged m, by layer parity
+  uint64_t *hq;         // workspace: [2][copies][2048] tagged h between layers
+  uint64_t *mq;         // workspace: [2][copies][max inter] tagged m
   uint32_t *ctl;        // workspace: call counters and error word
   float eps;
   long long spin_ticks; // bound of one wait in wall-clock ticks
 };
-// Workspace layout (bytes): two tagged h buffers, two tagged m buffers of
-// the widest inter, then the control words: one call counter per workgroup (at most
+// Workspace layout (bytes): tagged h and tagged m of the widest inter, each
+// twice (by layer parity) in kDecodeCopies copies, then the control words: one call counter per workgroup (at most
 // kDecodeMaxGroups) and the error word on a 128-byte line of its own.
 constexpr int kDecodeMaxInter = 8192;
 constexpr int kDecodeMaxGroups = 1024;
+// Each tagged value is written in kDecodeCopies copies; workgroup i reads
+// copy i % kDecodeCopies, so that each cache line is polled by a fraction
+// of the grid only.
+constexpr int kDecodeCopies = 8;
 constexpr size_t kDecodeHqOffset = 0;
-constexpr size_t kDecodeMqOffset = 2 * 8 * 2048;
-constexpr size_t kDecodeCtlOffset = kDecodeMqOffset + 2 * 8 * (size_t)kDecodeMaxInter;
+constexpr size_t kDecodeMqOffset = 2 * kDecodeCopies * 8 * 2048;
+constexpr size_t kDecodeCtlOffset =
+    kDecodeMqOffset + 2 * kDecodeCopies * 8 * (size_t)kDecodeMaxInter;
 constexpr int kDecodeErrorWord = kDecodeMaxGroups + 32;
 constexpr size_t kDecodeWsBytes = kDecodeCtlOffset + 4 * (kDecodeErrorWord + 32);
 // Workgroups of the persistent launch for this mode and width (0: none fit).

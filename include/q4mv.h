@@ -204,11 +204,11 @@ int q4_embed(const q4_mat *w, const int32_t *tok, float *e, void *stream);
  *             row i at row 2i and up row i at row 2i+1.  down: rows 2048,
  *             cols inter; inter (taken from layers[0].down.cols) is 2048,
  *             4096, 6144 or 8192 and the same in every layer.  wn: device
- *             float[2048].
+ *             float[2048], 16-byte aligned.
  *   h       : device float[2048]: the output (its prior contents are not
  *             read).
  *   ws      : device workspace of q4_decode_layers_ws_bytes() bytes (about
- *             145 KB), 16-byte aligned, zero-filled before its first use;
+ *             1.3 MB), 16-byte aligned, zero-filled before its first use;
  *             each call leaves it ready for the next.  Calls that overlap in
  *             time must not share it, and no other kernel should hold the
  *             device's compute units while this one runs.

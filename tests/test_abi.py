@@ -131,7 +131,7 @@ def test_decode_layers_argument_checks(L):
     p = lambda v: ctypes.c_void_p(v)
     L.q4_decode_layers_ws_bytes.restype = ctypes.c_size_t
     wsb = L.q4_decode_layers_ws_bytes()
-    assert 16 * 1024 <= wsb <= 256 * 1024
+    assert 16 * 1024 <= wsb <= 4 * 1024 * 1024
     G = 0x7F1000000000  # a further disjoint region for the layer arrays
     emb = mat(rows=4096, cols=2048)
 

@@ -32,7 +32,6 @@ def new_ws(q4):
                        device="cuda")
 
 
-ERROR_WORD = (163840 + 4 * (1024 + 32)) // 4  # int32 index of the error word in the workspace
 
 
 def run_layers(q4, emb, layers, w, tok, mode=0, ws=None):
@@ -148,7 +147,8 @@ def test_decode_layers_error_word_stops_the_kernel_and_is_cleared():
     t = torch.tensor([3], dtype=torch.int32, device="cuda")
     h = torch.full((2048,), 7.0, device="cuda")
     ws = new_ws(q4)
-    ws.view(torch.int32)[ERROR_WORD] = 1
+    # the error word: 32 words before the end of the workspace
+    ws.view(torch.int32)[q4.q4_decode_layers_ws_bytes() // 4 - 32] = 1
     q4.q4_decode_layers(emb, t, layers, w["eps"], h, ws)
     assert q4.q4_decode_layers_status(ws) == q4.Q4_ETIMEOUT
     assert np.all(host(h) == 7.0)  # nothing ran
