@@ -102,6 +102,38 @@ __device__ __forceinline__ float wave_sum_lane63(float t, int negz) {
   return t;
 }
 
+// The sums of four rows at once, each row's group terms held as for
+// wave_sum_lane63 (lane pairs identical).  Within each 16-lane row the
+// steps xor 2 and the two mirrors leave R_jk, the sum over row k's lanes,
+// in every lane of row k of register j; the gfx950 lane swaps then combine
+// the 16-lane rows across the four registers: v_permlane16_swap of
+// registers (0, 1) gives [R00, R10, R02, R12] and [R01, R11, R03, R13],
+// whose sum holds R_j0 + R_j1 and R_j2 + R_j3; v_permlane32_swap of the
+// two sums gathers each row's two halves into one 16-lane row.  Row j's
+// total, ((R_j0 + R_j1) + (R_j2 + R_j3)) as in wave_sum_lane63, ends in
+// lanes [16 j, 16 j + 16).  Three swaps and three adds replace the eight
+// broadcast instructions per row of wave_sum_lane63.
+__device__ __forceinline__ float swap_sum16(float a, float b) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ float quad_row_sums(float t0, float t1, float t2, float t3) {
+  float t[4] = {t0, t1, t2, t3};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    t[j] = t[j] + dpp<kDppQuadXor2>(t[j]);
+    t[j] = t[j] + dpp<kDppRowHalfMirror>(t[j]);
+    t[j] = t[j] + dpp<kDppRowMirror>(t[j]);
+  }
+  const float x = swap_sum16(t[0], t[1]);
+  const float y = swap_sum16(t[2], t[3]);
+  const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false,
+                                                  false);
+  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Codes -> products.  Word bits 4k..4k+3 hold code k; p_k = code_k * x_k.
 // ---------------------------------------------------------------------------

@@ -45,7 +45,7 @@
 #define Q4_ROW64_OCC_PCT 100  // share of the resident workgroups launched
 #endif
 #ifndef Q4_SPLIT_R
-#define Q4_SPLIT_R 4
+#define Q4_SPLIT_R 4  // a multiple of 4
 #endif
 #ifndef Q4_SPLIT_MAX_WG
 #define Q4_SPLIT_MAX_WG 2048
@@ -61,7 +61,7 @@ using namespace dev;
 
 constexpr int kSegR = 4;
 constexpr int kThreads = 256;
-static_assert(Q4_ROW64_R % 2 == 0, "the SwiGLU epilogue pairs rows within a block");
+static_assert(Q4_ROW64_R % 4 == 0, "rows are reduced four at a time");
 
 // Activations of `chunk` and its group sum for prologues kProX / kProXsum.
 template <int PRO>
@@ -119,32 +119,50 @@ __device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, const
   const uint32_t voff_g = 4u * (lane >> 1);
   const int end = P.rows;
   const bool odd = lane & 1;
-  const int negz = neg_zero_reg();
   SwigluBatch batch;
   float *m_out = ex.m_out;
   const auto store_m = [m_out](int i, float v) { m_out[i] = v; };
+  // lane 16 j + 15 holds row j of each quad of the block
+  const int jq = lane >> 4;
+  const bool holder = (lane & 15) == 15;
   for (int r = r0; r < end; r += stride) {
     const int nrows = min(R, end - r);
     if (!PRELOAD || r != r0) row64_load<R>(P, r, nrows, voff_q, voff_g, a);
-    float tot[R];
+    float tq[R / 4];
 #pragma unroll
-    for (int j = 0; j < R; ++j)
-      tot[j] = wave_sum_lane63(
-          group_term<FAST, PAIRS>(a.cw[j], xv, a.sv[j], a.bv[j], xsv, true, odd), negz);
+    for (int q = 0; q < R / 4; ++q) {
+      float gt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        gt[j] = group_term<FAST, PAIRS>(a.cw[4 * q + j], xv, a.sv[4 * q + j], a.bv[4 * q + j], xsv,
+                                        true, odd);
+      tq[q] = quad_row_sums(gt[0], gt[1], gt[2], gt[3]);
+    }
     if constexpr (EPI == kEpiSwiglu) {
+      // pairs (gate, up) = rows (4q + 2i, 4q + 2i + 1): lanes 32 i + 15, 32 i + 31
 #pragma unroll
-      for (int j = 0; j + 1 < R; j += 2)
-        if (j + 1 < nrows) swiglu_push<FAST>(store_m, batch, lane, tot[j], tot[j + 1], (r + j) >> 1);
-    } else if (lane == kWave - 1) {
+      for (int q = 0; q < R / 4; ++q) {
 #pragma unroll
-      for (int j = 0; j < R; ++j) {
+        for (int i = 0; i < 2; ++i) {
+          if (4 * q + 2 * i + 1 < nrows) {
+            const int b = __float_as_int(tq[q]);
+            const float g = __int_as_float(__builtin_amdgcn_readlane(b, 32 * i + 15));
+            const float u = __int_as_float(__builtin_amdgcn_readlane(b, 32 * i + 31));
+            swiglu_push<FAST>(store_m, batch, lane, g, u, (r + 4 * q + 2 * i) >> 1);
+          }
+        }
+      }
+    } else if (holder) {
+#pragma unroll
+      for (int q = 0; q < R / 4; ++q) {
+        const int j = 4 * q + jq;
         if (j < nrows) {
-          float v = tot[j];
+          float v = tq[q];
           if (P.res) v = P.res[r + j] + v;
           P.y[r + j] = v;
           if constexpr (EPI == kEpiArgmax) {
-            // rows arrive in increasing order: strictly greater keeps the
-            // lowest index of equal values (and -0 == +0)
+            // a lane's rows arrive in increasing order: strictly greater
+            // keeps the lowest index of equal values (and -0 == +0)
             const bool gt = (v > best.value) || best.index < 0;
             best.value = gt ? v : best.value;
             best.index = gt ? r + j : best.index;
@@ -206,7 +224,13 @@ __global__ __launch_bounds__(kThreads) void q4mv_row64_kernel(ProdGroup grp, Ext
     // one key per workgroup; a second kernel reduces them (a single counter
     // or maximum shared by every workgroup would serialise their atomics)
     __shared__ unsigned long long wbest[kThreads / kWave];
-    if (lane == kWave - 1) wbest[wave] = best.key();
+    // the best of the four holder lanes (other lanes hold key 0)
+    unsigned long long k = best.key();
+    unsigned long long o = __shfl_xor(k, 16);
+    k = o > k ? o : k;
+    o = __shfl_xor(k, 32);
+    k = o > k ? o : k;
+    if (lane == kWave - 1) wbest[wave] = k;
     __syncthreads();
     if (threadIdx.x == 0) {
       unsigned long long k = wbest[0];
@@ -317,15 +341,19 @@ __device__ __forceinline__ void split_rows(const Prod &P, const float *xv, float
   const bool odd = lane & 1;
   const uint32_t voff_q = 16u * chunk;
   const uint32_t voff_g = 4u * (chunk >> 1);
-  const int negz = neg_zero_reg();
   // `a` holds the loads of the first block on entry
   for (int r0 = begin; r0 < end; r0 += R) {
     const int nrows = min(R, end - r0);
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const float tot = wave_sum_lane63(
-          group_term<FAST, PAIRS>(a.cw[j], xv, a.sv[j], a.bv[j], xsv, active, odd), negz);
-      if (lane == kWave - 1) part[j][wave] = tot;
+    for (int q = 0; q < R / 4; ++q) {
+      float gt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        gt[j] = group_term<FAST, PAIRS>(a.cw[4 * q + j], xv, a.sv[4 * q + j], a.bv[4 * q + j], xsv,
+                                        active, odd);
+      // row 4 q + j's pass sum in lanes [16 j, 16 j + 16)
+      const float tq = quad_row_sums(gt[0], gt[1], gt[2], gt[3]);
+      if ((lane & 15) == 15) part[4 * q + (lane >> 4)][wave] = tq;
     }
     const int r1 = r0 + R;
     if (r1 < end) split_load<R>(P, r1, min(R, end - r1), voff_q, voff_g, a);
