@@ -21,7 +21,7 @@ __all__ = [
     "q4mv_norm_swiglu", "q4mv_norm_argmax", "q4mv_argmax_ws_bytes", "rmsq", "swq",
     "q4_argmax", "q4_argmax_ws_bytes", "q4_embed", "Queue", "Graph", "q4_sync",
     "MlpLayer", "q4_decode_layers", "q4_decode_layers_ws_bytes", "q4_decode_layers_status",
-    "library_path",
+    "Mailbox", "library_path",
 ]
 
 FIXED = 0
@@ -81,6 +81,11 @@ _SIGS = {
     "q4_capture_end": ([_vp, ctypes.POINTER(_vp)], ctypes.c_int),
     "q4_graph_launch": ([_vp, _vp], ctypes.c_int),
     "q4_graph_destroy": ([_vp], ctypes.c_int),
+    "q4_mailbox_create": ([_i32, ctypes.POINTER(_vp)], ctypes.c_int),
+    "q4_mailbox_destroy": ([_vp], ctypes.c_int),
+    "q4_mailbox_post": ([_vp, _vp, _vp], ctypes.c_int),
+    "q4_mailbox_wait": ([_vp, ctypes.c_uint32, _vp, _i32], ctypes.c_int),
+    "q4_mailbox_seq": ([_vp], ctypes.c_uint32),
     "q4_sync": ([_vp], ctypes.c_int),
     "q4_strerror": ([ctypes.c_int], ctypes.c_char_p),
 }
@@ -324,6 +329,44 @@ def q4_decode_layers_status(ws: torch.Tensor, stream=None) -> int:
     """Host wait; Q4_OK, or Q4_ETIMEOUT when a wait of the persistent
     kernel ran out (the workspace is then cleared)."""
     return int(_lib.q4_decode_layers_status(_dev(ws, ws.dtype, None, "ws"), _stream(stream)))
+
+
+class Mailbox:
+    """Pinned host mailbox of ``n`` int32 values: ``post`` enqueues a
+    one-thread kernel that copies device values into it and publishes the
+    next sequence number; ``wait`` spins on the host until the number
+    reaches ``target`` (the host waits on a flag, not on the stream)."""
+
+    def __init__(self, n: int):
+        h = _vp()
+        _check("q4_mailbox_create", _lib.q4_mailbox_create(int(n), ctypes.byref(h)))
+        self._h = h
+        self.n = int(n)
+        self._buf = (ctypes.c_int32 * self.n)()
+
+    def post(self, vals: torch.Tensor, stream=None) -> None:
+        _check("q4_mailbox_post", _lib.q4_mailbox_post(self._h, _dev(vals, torch.int32, self.n,
+                                                                       "vals"), _stream(stream)))
+
+    def wait(self, target: int, timeout_ms: int = 2000) -> list:
+        _check("q4_mailbox_wait", _lib.q4_mailbox_wait(self._h, int(target) & 0xFFFFFFFF,
+                                                       ctypes.byref(self._buf), int(timeout_ms)))
+        return list(self._buf)
+
+    @property
+    def seq(self) -> int:
+        return int(_lib.q4_mailbox_seq(self._h))
+
+    def close(self) -> None:
+        if self._h:
+            _lib.q4_mailbox_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def q4_sync(stream=None) -> None:

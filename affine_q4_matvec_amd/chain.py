@@ -31,7 +31,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (FIXED, Graph, MlpLayer, Q4Matrix, q4_argmax, q4_argmax_ws_bytes,
+from . import (FIXED, Graph, Mailbox, MlpLayer, Q4Matrix, q4_argmax, q4_argmax_ws_bytes,
                q4_decode_layers, q4_decode_layers_ws_bytes, q4_embed, q4mv, q4mv_add,
                q4mv_argmax_ws_bytes, q4mv_norm_argmax, q4mv_norm_swiglu, rmsq, swq)
 
@@ -88,6 +88,7 @@ class DecodeChain:
         self.mlp = [MlpLayer(lw["gu"], lw["down"], lw["wn"]) for lw in self.layers]
         self.stack_ws = z((q4_decode_layers_ws_bytes() + 7) // 8, torch.int64)
         self.graph = None
+        self.mailbox = None
         # the copies and fills above ran on the current stream; the chain may
         # run on another one
         torch.cuda.synchronize()
@@ -137,10 +138,15 @@ class DecodeChain:
         q4_argmax(self.logits, self.tok, self.ws, stream=stream)
 
     def capture(self, stream: torch.cuda.Stream) -> Graph:
+        """One step as a graph; it ends with a post of the new token to the
+        chain's mailbox (the host can wait on that instead of the stream)."""
+        if self.mailbox is None:
+            self.mailbox = Mailbox(1)
         g = Graph(stream)
         g.begin()
         try:
             self.enqueue_step(stream)
+            self.mailbox.post(self.tok, stream=stream)
         finally:
             g.end()
         self.graph = g
@@ -150,25 +156,40 @@ class DecodeChain:
         self.tok.fill_(int(t))
 
     def run(self, tok0: int, steps: int, stream: torch.cuda.Stream, use_graph: bool = True,
-            on_step=None) -> list:
+            on_step=None, wait: str = "stream") -> list:
         """Decodes `steps` tokens from `tok0`; returns them (host ints).
-        One host wait per token (to read it).  `on_step(i, chain)` runs
-        after token i is known, e.g. to read the logits."""
+        One host wait per token, to read it: wait="stream" copies the token
+        to pinned memory and synchronises the stream; wait="mailbox" (graph
+        only) spins on the mailbox that the graph's last kernel fills.
+        `on_step(i, chain)` runs after token i is known, e.g. to read the
+        logits."""
         if use_graph and self.graph is None:
             self.capture(stream)
+        if wait == "mailbox" and not use_graph:
+            raise ValueError("the mailbox wait needs the captured graph")
         with torch.cuda.stream(stream):
             self.set_token(tok0)
         out = []
         pinned = torch.empty(1, dtype=torch.int32, pin_memory=True)
+        if wait == "mailbox":
+            stream.synchronize()  # earlier posts have all landed
+        target = self.mailbox.seq if self.mailbox is not None else 0
         for i in range(steps):
             if use_graph:
                 self.graph.launch(stream)
             else:
                 self.enqueue_step(stream)
-            with torch.cuda.stream(stream):
-                pinned.copy_(self.tok, non_blocking=True)
-            stream.synchronize()
-            out.append(int(pinned[0]))
+            if wait == "mailbox":
+                target += 1
+                out.append(self.mailbox.wait(target)[0])
+            else:
+                with torch.cuda.stream(stream):
+                    pinned.copy_(self.tok, non_blocking=True)
+                stream.synchronize()
+                out.append(int(pinned[0]))
             if on_step is not None:
+                stream.synchronize()
                 on_step(i, self)
+        if wait == "mailbox":
+            stream.synchronize()
         return out

@@ -110,6 +110,22 @@ __global__ __launch_bounds__(256) void embed_kernel(Prod w, const int32_t *__res
   e[c] = sq + w.b[(size_t)t * G + (c >> 6)];
 }
 
+// ---------------------------------------------------------------------------
+// mailbox: copies n int32 values into pinned host memory, then publishes the
+// next sequence number there (one thread; system-scope release, so a host
+// that reads the new number also reads the values).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void mailbox_kernel(const int32_t *__restrict__ vals, int n,
+                                                     int32_t *host_vals, uint32_t *host_seq,
+                                                     uint32_t *dev_count) {
+  if (threadIdx.x != 0) return;
+  for (int i = 0; i < n; ++i)
+    __hip_atomic_store(host_vals + i, vals[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  const uint32_t seq = *dev_count + 1u;
+  *dev_count = seq;
+  __hip_atomic_store(host_seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 int next_pow2(int v) {
   int p = 1;
   while (p < v) p *= 2;
@@ -158,6 +174,13 @@ hipError_t launch_argmax(const float *v, int32_t n, int32_t *idx, void *ws, hipS
 hipError_t launch_argmax_final(const unsigned long long *keys, int32_t nkeys, int32_t *idx,
                                hipStream_t st) {
   hipLaunchKernelGGL(argmax_final_kernel, dim3(1), dim3(256), 0, st, keys, nkeys, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_mailbox(const int32_t *vals, int32_t n, int32_t *host_vals, uint32_t *host_seq,
+                          uint32_t *dev_count, hipStream_t st) {
+  hipLaunchKernelGGL(mailbox_kernel, dim3(1), dim3(64), 0, st, vals, n, host_vals, host_seq,
+                     dev_count);
   return hipGetLastError();
 }
 

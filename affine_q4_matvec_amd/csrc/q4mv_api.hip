@@ -131,6 +131,15 @@ struct q4_queue {
   std::chrono::steady_clock::time_point wall_begin;
 };
 
+struct q4_mailbox {
+  int32_t n = 0;
+  int32_t *host_vals = nullptr;   // pinned, coherent host memory (mapped)
+  uint32_t *host_seq = nullptr;
+  int32_t *dev_vals_view = nullptr;  // device addresses of the same memory
+  uint32_t *dev_seq_view = nullptr;
+  uint32_t *dev_count = nullptr;  // device memory: posts executed
+};
+
 struct q4_graph {
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
@@ -538,6 +547,70 @@ int q4_graph_destroy(q4_graph *g) {
   if (g->graph && hipGraphDestroy(g->graph) != hipSuccess) rc = Q4_EHIP;
   delete g;
   return rc;
+}
+
+int q4_mailbox_create(int32_t nvals, q4_mailbox **out) {
+  if (!out || nvals < 1 || nvals > Q4_MAILBOX_MAX_VALUES) return Q4_EINVAL;
+  *out = nullptr;
+  q4_mailbox *mb = new (std::nothrow) q4_mailbox();
+  if (!mb) return Q4_ENOMEM;
+  mb->n = nvals;
+  void *host = nullptr;
+  // 64 bytes for the sequence number, then the values
+  const size_t bytes = 64 + sizeof(int32_t) * (size_t)nvals;
+  if (hipHostMalloc(&host, bytes, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess) {
+    delete mb;
+    return Q4_EHIP;
+  }
+  memset(host, 0, bytes);
+  mb->host_seq = static_cast<uint32_t *>(host);
+  mb->host_vals = reinterpret_cast<int32_t *>(static_cast<char *>(host) + 64);
+  void *dview = nullptr;
+  if (hipHostGetDevicePointer(&dview, host, 0) != hipSuccess ||
+      hipMalloc(&mb->dev_count, sizeof(uint32_t)) != hipSuccess ||
+      hipMemset(mb->dev_count, 0, sizeof(uint32_t)) != hipSuccess) {
+    if (mb->dev_count) (void)hipFree(mb->dev_count);
+    (void)hipHostFree(host);
+    delete mb;
+    return Q4_EHIP;
+  }
+  mb->dev_seq_view = static_cast<uint32_t *>(dview);
+  mb->dev_vals_view = reinterpret_cast<int32_t *>(static_cast<char *>(dview) + 64);
+  *out = mb;
+  return Q4_OK;
+}
+
+int q4_mailbox_destroy(q4_mailbox *mb) {
+  if (!mb) return Q4_EINVAL;
+  int rc = Q4_OK;
+  if (hipFree(mb->dev_count) != hipSuccess) rc = Q4_EHIP;
+  if (hipHostFree(mb->host_seq) != hipSuccess) rc = Q4_EHIP;
+  delete mb;
+  return rc;
+}
+
+int q4_mailbox_post(q4_mailbox *mb, const int32_t *vals, void *stream) {
+  if (!mb || !vals || !aligned(vals, 4)) return Q4_EINVAL;
+  return hip_status(q4::launch_mailbox(vals, mb->n, mb->dev_vals_view, mb->dev_seq_view,
+                                       mb->dev_count, static_cast<hipStream_t>(stream)));
+}
+
+int q4_mailbox_wait(q4_mailbox *mb, uint32_t target, int32_t *vals, int32_t timeout_ms) {
+  if (!mb || timeout_ms < 0) return Q4_EINVAL;
+  const auto t0 = std::chrono::steady_clock::now();
+  const auto limit = std::chrono::milliseconds(timeout_ms);
+  for (uint64_t spin = 0;; ++spin) {
+    const uint32_t seq = __atomic_load_n(mb->host_seq, __ATOMIC_ACQUIRE);
+    if ((int32_t)(seq - target) >= 0) break;
+    if ((spin & 1023) == 1023 && std::chrono::steady_clock::now() - t0 > limit) return Q4_ETIMEOUT;
+  }
+  if (vals)
+    for (int32_t i = 0; i < mb->n; ++i) vals[i] = __atomic_load_n(mb->host_vals + i, __ATOMIC_RELAXED);
+  return Q4_OK;
+}
+
+uint32_t q4_mailbox_seq(const q4_mailbox *mb) {
+  return mb ? __atomic_load_n(mb->host_seq, __ATOMIC_ACQUIRE) : 0u;
 }
 
 int q4_sync(void *stream) {

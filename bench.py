@@ -168,7 +168,8 @@ def run_head(args, q4, torch, synth):
 
 def time_chain(args, q4, torch, chain, tok0):
     """Token rate of one decode-chain engine: (a) with one host wait per
-    token, (b) device time of the same captured step replayed back to back."""
+    token on the stream, (b) device time of the same captured step replayed
+    back to back, (c) with one host wait per token on a pinned mailbox."""
     stream = torch.cuda.Stream()
     chain.capture(stream)
     chain.run(0, 3, stream)  # warm-up tokens (not timed)
@@ -195,8 +196,14 @@ def time_chain(args, q4, torch, chain, tok0):
         n = min(len(ref["tokens"]), len(tokens))
         match = bool(ref["tokens"][:n] == tokens[:n])
     bpt = chain.bytes_per_token()
+    # (c) one host wait per token on the mailbox the graph's last kernel fills
+    t0 = time.perf_counter()
+    mtokens = chain.run(tok0, args.chain_tokens, stream, wait="mailbox")
+    per_token_mailbox_ms = (time.perf_counter() - t0) * 1e3 / args.chain_tokens
     out = {
         "ms_per_token_with_host_wait": round(per_token_sync_ms, 4),
+        "ms_per_token_with_mailbox_wait": round(per_token_mailbox_ms, 4),
+        "mailbox_tokens_equal": mtokens == tokens,
         "ms_per_token_gpu": round(gpu_ms, 4),
         "gpu_GBps": round(bpt / (gpu_ms * 1e-3) / 1e9, 1),
         "kernels_per_token": chain.kernels_per_token(),

@@ -274,6 +274,36 @@ int q4_capture_end(void *stream, q4_graph **out);
 int q4_graph_launch(q4_graph *g, void *stream);
 int q4_graph_destroy(q4_graph *g);
 
+/*
+ * Mailbox: a host wait on a flag instead of on the stream ([P2] Change: the
+ * host waits once on a flag that the last queued work sets).  A mailbox is
+ * pinned, coherent host memory holding n int32 values and a sequence
+ * number, plus a device counter.
+ *   q4_mailbox_create : n in 1..Q4_MAILBOX_MAX_VALUES; allocates (not for
+ *                       use during capture).
+ *   q4_mailbox_post   : enqueues on `stream` one single-thread kernel that
+ *                       copies vals (device int32[n]) into the mailbox and
+ *                       then publishes the next sequence number (the
+ *                       number of posts executed so far).  Legal inside
+ *                       stream capture: every replay posts once.
+ *   q4_mailbox_wait   : spins on the host until the sequence number reaches
+ *                       `target` (compared modulo 2^32), then copies the
+ *                       values into vals (host int32[n], NULL to skip).
+ *                       Q4_ETIMEOUT after timeout_ms milliseconds (a fault or
+ *                       an error on the stream is reported by q4_sync, not
+ *                       here).
+ *   q4_mailbox_seq    : the sequence number now (0 before the first post).
+ * Posts on one mailbox must be ordered (one stream).  The caller keeps vals
+ * alive until the post has run.
+ */
+#define Q4_MAILBOX_MAX_VALUES 1024
+typedef struct q4_mailbox q4_mailbox;
+int q4_mailbox_create(int32_t nvals, q4_mailbox **out);
+int q4_mailbox_destroy(q4_mailbox *mb);
+int q4_mailbox_post(q4_mailbox *mb, const int32_t *vals, void *stream);
+int q4_mailbox_wait(q4_mailbox *mb, uint32_t target, int32_t *vals, int32_t timeout_ms);
+uint32_t q4_mailbox_seq(const q4_mailbox *mb);
+
 /* Host wait for all work on `stream` (one hipStreamSynchronize). */
 int q4_sync(void *stream);
 

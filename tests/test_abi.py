@@ -21,7 +21,7 @@ class Mat(ctypes.Structure):
 
 def declared_functions():
     text = open(HEADER).read()
-    return re.findall(r"^\s*(?:int|size_t|const char \*)\s*\**\s*(\w+)\s*\(", text, re.M)
+    return re.findall(r"^\s*(?:int|size_t|uint32_t|const char \*)\s*\**\s*(\w+)\s*\(", text, re.M)
 
 
 @pytest.fixture(scope="module")
@@ -172,3 +172,15 @@ def test_decode_layers_argument_checks(L):
     assert call(h=G + 0x30000000 + 64) == EINVAL                # h inside a down matrix
     assert call(ws=G + 0x60000000 - 64) == EINVAL               # ws over the norm weights
     assert L.q4_decode_layers_status(None, None) == EINVAL
+
+
+def test_mailbox_argument_checks(L):
+    out = ctypes.c_void_p()
+    assert L.q4_mailbox_create(0, ctypes.byref(out)) == EINVAL
+    assert L.q4_mailbox_create(1025, ctypes.byref(out)) == EINVAL
+    assert L.q4_mailbox_create(4, None) == EINVAL
+    assert L.q4_mailbox_destroy(None) == EINVAL
+    assert L.q4_mailbox_post(None, ctypes.c_void_p(A), None) == EINVAL
+    assert L.q4_mailbox_wait(None, 1, None, 10) == EINVAL
+    L.q4_mailbox_seq.restype = ctypes.c_uint32
+    assert L.q4_mailbox_seq(None) == 0
