@@ -26,6 +26,7 @@ __all__ = [
 
 FIXED = 0
 FAST = 1
+WAIT_STREAM, WAIT_MAILBOX = 0, 1
 Q4_OK, Q4_EINVAL, Q4_EHIP, Q4_ETIMEOUT, Q4_ESTATE, Q4_ENOMEM = 0, -1, -2, -3, -4, -5
 MAX_COLS = 32768
 MAX_RMSQ_N = 8192
@@ -81,6 +82,7 @@ _SIGS = {
     "q4_capture_end": ([_vp, ctypes.POINTER(_vp)], ctypes.c_int),
     "q4_graph_launch": ([_vp, _vp], ctypes.c_int),
     "q4_graph_destroy": ([_vp], ctypes.c_int),
+    "q4_queue_set_wait": ([_vp, ctypes.c_int, _i32], ctypes.c_int),
     "q4_mailbox_create": ([_i32, ctypes.POINTER(_vp)], ctypes.c_int),
     "q4_mailbox_destroy": ([_vp], ctypes.c_int),
     "q4_mailbox_post": ([_vp, _vp, _vp], ctypes.c_int),
@@ -393,6 +395,11 @@ class Queue:
 
     def q4_stage(self) -> None:
         _check("q4_stage", _lib.q4_stage(self._h))
+
+    def set_wait(self, how: int, timeout_ms: int = 10000) -> None:
+        """WAIT_STREAM (hipStreamSynchronize) or WAIT_MAILBOX (spin on a
+        pinned flag that a one-thread kernel sets after the last stage)."""
+        _check("q4_queue_set_wait", _lib.q4_queue_set_wait(self._h, int(how), int(timeout_ms)))
 
     def q4mv_wait(self) -> None:
         _check("q4mv_wait", _lib.q4mv_wait(self._h))

@@ -118,6 +118,15 @@ int launch_products(const Prod *prods, int count, const Shape &sh, int mode, hip
 
 }  // namespace
 
+struct q4_mailbox {
+  int32_t n = 0;
+  int32_t *host_vals = nullptr;   // pinned, coherent host memory (mapped)
+  uint32_t *host_seq = nullptr;
+  int32_t *dev_vals_view = nullptr;  // device addresses of the same memory
+  uint32_t *dev_seq_view = nullptr;
+  uint32_t *dev_count = nullptr;  // device memory: posts executed
+};
+
 struct q4_queue {
   hipStream_t st = nullptr;
   int mode = Q4_FIXED;
@@ -129,15 +138,10 @@ struct q4_queue {
   bool began = false;
   int products_since_wait = 0;
   std::chrono::steady_clock::time_point wall_begin;
-};
-
-struct q4_mailbox {
-  int32_t n = 0;
-  int32_t *host_vals = nullptr;   // pinned, coherent host memory (mapped)
-  uint32_t *host_seq = nullptr;
-  int32_t *dev_vals_view = nullptr;  // device addresses of the same memory
-  uint32_t *dev_seq_view = nullptr;
-  uint32_t *dev_count = nullptr;  // device memory: posts executed
+  // Q4_WAIT_MAILBOX: the wait spins on this mailbox instead of the stream
+  q4_mailbox *mailbox = nullptr;
+  uint32_t posted = 0;
+  int32_t timeout_ms = 0;
 };
 
 struct q4_graph {
@@ -448,10 +452,32 @@ int q4_queue_create(void *stream, int mode, q4_queue **out) {
 int q4_queue_destroy(q4_queue *q) {
   if (!q) return Q4_EINVAL;
   int rc = Q4_OK;
+  if (q->mailbox && q4_mailbox_destroy(q->mailbox) != Q4_OK) rc = Q4_EHIP;
   if (q->ev_begin && hipEventDestroy(q->ev_begin) != hipSuccess) rc = Q4_EHIP;
   if (q->ev_end && hipEventDestroy(q->ev_end) != hipSuccess) rc = Q4_EHIP;
   delete q;
   return rc;
+}
+
+int q4_queue_set_wait(q4_queue *q, int how, int32_t timeout_ms) {
+  if (!q || (how != Q4_WAIT_STREAM && how != Q4_WAIT_MAILBOX) || timeout_ms < 0) return Q4_EINVAL;
+  if (how == Q4_WAIT_STREAM) {
+    if (q->mailbox) {
+      // posts still in flight write into the mailbox: let them land first
+      if (hipStreamSynchronize(q->st) != hipSuccess) return Q4_EHIP;
+      const int rc = q4_mailbox_destroy(q->mailbox);
+      q->mailbox = nullptr;
+      if (rc != Q4_OK) return rc;
+    }
+    return Q4_OK;
+  }
+  if (!q->mailbox) {
+    const int rc = q4_mailbox_create(1, &q->mailbox);
+    if (rc != Q4_OK) return rc;
+    q->posted = 0;
+  }
+  q->timeout_ms = timeout_ms;
+  return Q4_OK;
 }
 
 int q4mv_queue(q4_queue *q, const q4_mat *w, const float *x, const float *xsum, float *y) {
@@ -495,7 +521,18 @@ int q4mv_wait(q4_queue *q) {
   if (q->trace && q->began) {
     if (hipEventRecord(q->ev_end, q->st) != hipSuccess) return Q4_EHIP;
   }
-  if (hipStreamSynchronize(q->st) != hipSuccess) return Q4_EHIP;
+  if (q->mailbox) {
+    // a one-thread kernel after the last stage publishes the next number
+    const int32_t *any = reinterpret_cast<const int32_t *>(q->mailbox->dev_count);
+    rc = q4_mailbox_post(q->mailbox, any, q->st);
+    if (rc != Q4_OK) return rc;
+    rc = q4_mailbox_wait(q->mailbox, ++q->posted, nullptr, q->timeout_ms);
+    if (rc != Q4_OK) return rc;
+  } else if (hipStreamSynchronize(q->st) != hipSuccess) {
+    return Q4_EHIP;
+  }
+  if (q->trace && q->began && q->mailbox && hipEventSynchronize(q->ev_end) != hipSuccess)
+    return Q4_EHIP;
   if (q->trace && q->began) {
     float gpu_ms = 0.0f;
     if (hipEventElapsedTime(&gpu_ms, q->ev_begin, q->ev_end) != hipSuccess) return Q4_EHIP;

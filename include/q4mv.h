@@ -256,6 +256,19 @@ int q4_decode_layers_status(void *ws, void *stream);
 typedef struct q4_queue q4_queue;
 int q4_queue_create(void *stream, int mode, q4_queue **out);
 int q4_queue_destroy(q4_queue *q);
+
+/*
+ * How q4mv_wait waits ([P2] Change: q4wait waits on a flag).  Q4_WAIT_STREAM
+ * (the default): hipStreamSynchronize.  Q4_WAIT_MAILBOX: q4mv_wait enqueues
+ * a mailbox post (below) after the last stage and spins on the host until
+ * it lands, at most timeout_ms milliseconds (then Q4_ETIMEOUT; errors of the
+ * stream itself are reported by q4_sync).  Switching to Q4_WAIT_MAILBOX
+ * allocates the queue's mailbox; switching back waits for the stream and
+ * frees it.
+ */
+#define Q4_WAIT_STREAM 0
+#define Q4_WAIT_MAILBOX 1
+int q4_queue_set_wait(q4_queue *q, int how, int32_t timeout_ms);
 int q4mv_queue(q4_queue *q, const q4_mat *w, const float *x, const float *xsum,
                float *y);
 int q4_stage(q4_queue *q);

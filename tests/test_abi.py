@@ -184,3 +184,7 @@ def test_mailbox_argument_checks(L):
     assert L.q4_mailbox_wait(None, 1, None, 10) == EINVAL
     L.q4_mailbox_seq.restype = ctypes.c_uint32
     assert L.q4_mailbox_seq(None) == 0
+
+
+def test_queue_set_wait_checks(L):
+    assert L.q4_queue_set_wait(None, 0, 10) == EINVAL

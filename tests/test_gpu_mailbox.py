@@ -68,3 +68,38 @@ def test_chain_mailbox_wait_golden_tokens():
     assert toks == ref["tokens"][:40]
     again = chain.run(ref["tok0"], 5, s, wait="stream")
     assert again == ref["tokens"][:5]
+
+
+def test_queue_waits_on_mailbox():
+    """q4mv_wait on a mailbox: the product set of two layers, one wait,
+    every product bit-exact; switching back to the stream wait works."""
+    import numpy as np
+    import oracle
+    from gpu_util import assert_bits_equal, dev, host
+    q4 = lib()
+    ps = synth.product_set(seed=5, layers=2, vocab=4096)
+    xs_host = {c: oracle.group_sums(x) for c, x in ps["x"].items()}
+    xd = {c: dev(x) for c, x in ps["x"].items()}
+    xsd = {c: dev(v) for c, v in xs_host.items()}
+    queue = q4.Queue()
+    queue.set_wait(q4.WAIT_MAILBOX, timeout_ms=5000)
+    for rep in range(2):
+        keep = []
+        stage = 0
+        for m in ps["products"]:
+            if m["stage"] != stage:
+                queue.q4_stage()
+                stage = m["stage"]
+            W = q4.Q4Matrix.from_host(m)
+            y = torch.full((m["rows"],), 7.0, device="cuda")
+            queue.q4mv_queue(W, xd[m["cols"]], xsd[m["cols"]], y)
+            keep.append((m, W, y))
+        torch.cuda.synchronize()  # the uploads above ran on torch's stream
+        queue.q4mv_wait()
+        for m, W, y in keep[-3:]:
+            got = host(y)
+            idx = np.unique(np.linspace(0, m["rows"] - 1, 64).astype(np.int64))
+            assert_bits_equal(got[idx], oracle.q4mv_sample(m, ps["x"][m["cols"]],
+                                                           xs_host[m["cols"]], idx), m["name"])
+        queue.set_wait(q4.WAIT_STREAM if rep == 0 else q4.WAIT_MAILBOX)
+    queue.close()
