@@ -61,7 +61,11 @@ using namespace dev;
 
 constexpr int kSegR = 4;
 constexpr int kThreads = 256;
-static_assert(Q4_ROW64_R % 4 == 0, "rows are reduced four at a time");
+static_assert(Q4_ROW64_R == 1 || Q4_ROW64_R % 2 == 0, "rows per block: 1 or even");
+// The SwiGLU epilogue takes (gate, up) row pairs within a block: not with
+// one row per block (a build for measurements only; the fused call then
+// returns Q4_EINVAL).
+constexpr bool kRow64Swiglu = Q4_ROW64_R % 2 == 0;
 
 // Activations of `chunk` and its group sum for prologues kProX / kProXsum.
 template <int PRO>
@@ -122,42 +126,52 @@ __device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, const
   SwigluBatch batch;
   float *m_out = ex.m_out;
   const auto store_m = [m_out](int i, float v) { m_out[i] = v; };
-  // lane 16 j + 15 holds row j of each quad of the block
-  const int jq = lane >> 4;
-  const bool holder = (lane & 15) == 15;
+  // R a multiple of 4: four rows reduced at once, row j of a quad ending in
+  // lane 16 j + 15; otherwise each row on its own, ending in lane 63
+  constexpr bool kQuad = R % 4 == 0;
+  constexpr int kSums = kQuad ? R / 4 : R;
+  const int jq = kQuad ? lane >> 4 : 0;
+  const bool holder = kQuad ? (lane & 15) == 15 : lane == kWave - 1;
+  const int negz = neg_zero_reg();
   for (int r = r0; r < end; r += stride) {
     const int nrows = min(R, end - r);
     if (!PRELOAD || r != r0) row64_load<R>(P, r, nrows, voff_q, voff_g, a);
-    float tq[R / 4];
-#pragma unroll
-    for (int q = 0; q < R / 4; ++q) {
-      float gt[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        gt[j] = group_term<FAST, PAIRS>(a.cw[4 * q + j], xv, a.sv[4 * q + j], a.bv[4 * q + j], xsv,
-                                        true, odd);
-      tq[q] = quad_row_sums(gt[0], gt[1], gt[2], gt[3]);
-    }
-    if constexpr (EPI == kEpiSwiglu) {
-      // pairs (gate, up) = rows (4q + 2i, 4q + 2i + 1): lanes 32 i + 15, 32 i + 31
+    float tq[kSums];
+    if constexpr (kQuad) {
 #pragma unroll
       for (int q = 0; q < R / 4; ++q) {
+        float gt[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          if (4 * q + 2 * i + 1 < nrows) {
-            const int b = __float_as_int(tq[q]);
-            const float g = __int_as_float(__builtin_amdgcn_readlane(b, 32 * i + 15));
-            const float u = __int_as_float(__builtin_amdgcn_readlane(b, 32 * i + 31));
-            swiglu_push<FAST>(store_m, batch, lane, g, u, (r + 4 * q + 2 * i) >> 1);
-          }
+        for (int j = 0; j < 4; ++j)
+          gt[j] = group_term<FAST, PAIRS>(a.cw[4 * q + j], xv, a.sv[4 * q + j], a.bv[4 * q + j],
+                                          xsv, true, odd);
+        tq[q] = quad_row_sums(gt[0], gt[1], gt[2], gt[3]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < R; ++j)
+        tq[j] = wave_sum_lane63(
+            group_term<FAST, PAIRS>(a.cw[j], xv, a.sv[j], a.bv[j], xsv, true, odd), negz);
+    }
+    if constexpr (EPI == kEpiSwiglu) {
+      // (gate, up) = rows (2i, 2i + 1) of the block
+#pragma unroll
+      for (int i = 0; 2 * i + 1 < R; ++i) {
+        if (2 * i + 1 < nrows) {
+          const int jg = 2 * i, ju = 2 * i + 1;
+          const int bg = __float_as_int(tq[kQuad ? jg / 4 : jg]);
+          const int bu = __float_as_int(tq[kQuad ? ju / 4 : ju]);
+          const float g = __int_as_float(__builtin_amdgcn_readlane(bg, kQuad ? 16 * (jg % 4) + 15 : 63));
+          const float u = __int_as_float(__builtin_amdgcn_readlane(bu, kQuad ? 16 * (ju % 4) + 15 : 63));
+          swiglu_push<FAST>(store_m, batch, lane, g, u, (r + jg) >> 1);
         }
       }
     } else if (holder) {
 #pragma unroll
-      for (int q = 0; q < R / 4; ++q) {
-        const int j = 4 * q + jq;
+      for (int k = 0; k < kSums; ++k) {
+        const int j = kQuad ? 4 * k + jq : k;
         if (j < nrows) {
-          float v = tq[q];
+          float v = tq[k];
           if (P.res) v = P.res[r + j] + v;
           P.y[r + j] = v;
           if constexpr (EPI == kEpiArgmax) {
@@ -544,7 +558,7 @@ Shape shape_of(int32_t cols, int pro, int epi) {
 }
 
 bool shape_supported(const Shape &sh) {
-  if (sh.kind == Shape::kRow64) return true;
+  if (sh.kind == Shape::kRow64) return sh.epi != kEpiSwiglu || kRow64Swiglu;
   return sh.epi == kEpiStore && sh.pro != kProNorm;
 }
 
