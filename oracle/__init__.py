@@ -72,6 +72,9 @@ def lib():
         L.orc_add.argtypes = [_f32p, _f32p, _f32p, _i64]
         L.orc_add.restype = None
         L.orc_fnv1a32.argtypes = [ctypes.c_void_p, _i64]
+        L.orc_atq.argtypes = [_f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_float, _f32p,
+                              _f32p, _f32p, _f32p, _i64, _i64, _i64, _i64, _f32p, _f32p]
+        L.orc_atq.restype = ctypes.c_int
         L.orc_fnv1a32.restype = ctypes.c_uint32
         _lib = L
     return _lib
@@ -195,6 +198,35 @@ def add(a, b) -> np.ndarray:
 def fnv1a32(arr) -> int:
     arr = np.ascontiguousarray(arr)
     return int(lib().orc_fnv1a32(arr.ctypes.data, arr.nbytes))
+
+
+ATQ_D = 128
+
+
+def atq(q, g, k, v, wq, wk, eps, cos, sin, kcache, vcache, pos: int):
+    """One decode token of gated attention over key/value caches (the
+    readings in q4_oracle.c): writes row ``pos`` of ``kcache`` and
+    ``vcache`` (float32 [hkv, max_pos, 128], updated in place) and returns
+    ``(o, os)`` for ``hq = q.size / 128`` query heads."""
+    q, g, k, v = (_f32(a).ravel() for a in (q, g, k, v))
+    wq, wk, cos, sin = (_f32(a).ravel() for a in (wq, wk, cos, sin))
+    if not (kcache.dtype == np.float32 and kcache.flags.c_contiguous and
+            vcache.dtype == np.float32 and vcache.flags.c_contiguous):
+        raise ValueError("caches must be C-contiguous float32 arrays")
+    hq, hkv = q.size // ATQ_D, k.size // ATQ_D
+    max_pos = kcache.shape[1]
+    if kcache.shape != (hkv, max_pos, ATQ_D) or vcache.shape != kcache.shape:
+        raise ValueError("caches must be [hkv, max_pos, 128]")
+    if g.size != q.size or v.size != k.size or wq.size != ATQ_D or wk.size != ATQ_D:
+        raise ValueError("shape mismatch")
+    if cos.size != ATQ_D // 2 or sin.size != ATQ_D // 2:
+        raise ValueError("rotation tables hold 64 values")
+    o = np.empty(q.size, np.float32)
+    os_ = np.empty(q.size // GROUP, np.float32)
+    if lib().orc_atq(q, g, k, v, wq, wk, float(np.float32(eps)), cos, sin, kcache, vcache,
+                     int(pos), int(max_pos), hq, hkv, o, os_) != 0:
+        raise ValueError("atq: heads or position outside the readings")
+    return o, os_
 
 
 def chain_hidden(w: dict, tok: int, nthreads: int = 1, layers: int | None = None) -> np.ndarray:

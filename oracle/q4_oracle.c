@@ -294,3 +294,90 @@ uint32_t orc_fnv1a32(const void *data, int64_t nbytes) {
     }
     return h;
 }
+
+/* ------------------------------------------------------------------------
+ * atq: one decode token of gated attention over key and value caches
+ * ("Metal: queued rmsq, swq, gdn and atq kernels ..." (#1440), Change, atq
+ * bullet: q/k RMS norm and rotation, the new k/v into the caches, scores,
+ * softmax, weighted values, sigmoid gate and group sums; one threadgroup per
+ * query head; a group of query heads shares one key/value head).  The
+ * pages give no formulas; the readings (listed with the design notes):
+ *   D = 128 values per head; hq query heads, hkv key/value heads with
+ *   hq % hkv == 0; query head h uses key/value head h / (hq / hkv).
+ *   qn = rmsq(q_h, wq), kn = rmsq(k_j, wk)     (rmsq's definition over D)
+ *   rotation by the position's table c_i, s_i (i < D/2), pairing dims i
+ *   and i + D/2 (a = x_i, b = x_{i+D/2}):
+ *     r_i       = (a * c_i) - (b * s_i)
+ *     r_{i+D/2} = (a * s_i) + (b * c_i)
+ *   caches (rows of D floats, [hkv][max_pos][D]): K[j][pos] = rotated kn,
+ *   V[j][pos] = v_j
+ *   score   s_t = T(qr_i * K[j][t]_i, i < D) * SCALE, t = 0..pos,
+ *           SCALE = RN32(1/sqrt(D))
+ *   m = the largest s_t; e_t = RN32(E(s_t - m)), the difference in binary32,
+ *   E the fixed binary64 exp above
+ *   Z = T(e_0 .. e_pos)
+ *   w_i = T(e_t * V[j][t]_i, t = 0..pos) / Z
+ *   o_i = w_i * RN32(1 / (1 + E(-g_i)))      (the sigmoid in binary64)
+ *   os  = T over each 64 values of o
+ * Returns 0, or -1 for shapes outside these readings.
+ * ---------------------------------------------------------------------- */
+#define ATQ_D 128
+
+static void atq_rotate(const float *x, const float *c, const float *s, float *r) {
+    for (int i = 0; i < ATQ_D / 2; ++i) {
+        const float a = x[i], b = x[i + ATQ_D / 2];
+        const float ac = a * c[i], bs = b * s[i];
+        const float as = a * s[i], bc = b * c[i];
+        r[i] = ac - bs;
+        r[i + ATQ_D / 2] = as + bc;
+    }
+}
+
+int orc_atq(const float *q, const float *g, const float *k, const float *v,
+            const float *wq, const float *wk, float eps, const float *cs,
+            const float *sn, float *kc, float *vc, int64_t pos, int64_t max_pos,
+            int64_t hq, int64_t hkv, float *o, float *os) {
+    if (hq < 1 || hkv < 1 || hq % hkv != 0 || pos < 0 || pos >= max_pos) return -1;
+    const int64_t group = hq / hkv;
+    const int64_t n = pos + 1;
+    const float scale = (float)(1.0 / sqrt((double)ATQ_D));
+    float kn[ATQ_D], knu[2], qn[ATQ_D], qnu[2], qr[ATQ_D];
+    float *prod = (float *)malloc(sizeof(float) * ATQ_D);
+    float *sc = (float *)malloc(sizeof(float) * (size_t)n);
+    float *ev = (float *)malloc(sizeof(float) * (size_t)n);
+    /* the new key and value rows of every key/value head */
+    for (int64_t j = 0; j < hkv; ++j) {
+        orc_rmsq(k + j * ATQ_D, wk, ATQ_D, eps, kn, knu);
+        atq_rotate(kn, cs, sn, kc + (j * max_pos + pos) * ATQ_D);
+        memcpy(vc + (j * max_pos + pos) * ATQ_D, v + j * ATQ_D, sizeof(float) * ATQ_D);
+    }
+    for (int64_t h = 0; h < hq; ++h) {
+        const int64_t j = h / group;
+        orc_rmsq(q + h * ATQ_D, wq, ATQ_D, eps, qn, qnu);
+        atq_rotate(qn, cs, sn, qr);
+        const float *K = kc + j * max_pos * ATQ_D;
+        const float *V = vc + j * max_pos * ATQ_D;
+        float m = 0.0f;
+        for (int64_t t = 0; t < n; ++t) {
+            for (int i = 0; i < ATQ_D; ++i) prod[i] = qr[i] * K[t * ATQ_D + i];
+            sc[t] = orc_tree(prod, ATQ_D) * scale;
+            if (t == 0 || sc[t] > m) m = sc[t];
+        }
+        for (int64_t t = 0; t < n; ++t) ev[t] = (float)orc_exp((double)(sc[t] - m));
+        const float z = orc_tree(ev, n);
+        float *wv = (float *)malloc(sizeof(float) * (size_t)n);
+        for (int i = 0; i < ATQ_D; ++i) {
+            for (int64_t t = 0; t < n; ++t) wv[t] = ev[t] * V[t * ATQ_D + i];
+            const float w = orc_tree(wv, n) / z;
+            const double gi = (double)g[h * ATQ_D + i];
+            const float sig = (float)(1.0 / (1.0 + orc_exp(-gi)));
+            o[h * ATQ_D + i] = w * sig;
+        }
+        free(wv);
+    }
+    orc_group_sums(o, hq * ATQ_D, os);
+    free(prod);
+    free(sc);
+    free(ev);
+    return 0;
+}

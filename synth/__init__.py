@@ -236,3 +236,44 @@ def chain_weights(seed: int = DEFAULT_SEED, layers: int = LAYERS, hidden: int = 
         "eps": np.float32(EPS),
         "hidden": hidden, "inter": inter, "vocab": vocab,
     }
+
+
+ATQ_D = 128
+ATQ_HQ = 16       # query heads of the 2048-wide Q product
+ATQ_HKV = 4       # key/value heads of the 512-wide K and V products
+ATQ_MAX_POS = 4096
+ROPE_BASE = 10000.0
+
+
+def rope_table(pos: int, d: int = ATQ_D, base: float = ROPE_BASE):
+    """The rotation table of position ``pos``: cos and sin of
+    pos * base^(-2i/d), i < d/2, rounded to binary32 (an input of the
+    attention step, like the activations)."""
+    i = np.arange(d // 2, dtype=np.float64)
+    ang = float(pos) * np.power(base, -2.0 * i / d)
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def atq_inputs(seed: int = DEFAULT_SEED, pos: int = 204, hq: int = ATQ_HQ, hkv: int = ATQ_HKV,
+               max_pos: int = ATQ_MAX_POS) -> dict:
+    """One decode token of the attention step at position ``pos``: q, gate
+    (hq x 128) and k, v (hkv x 128) ~ N(0, 1); norm weights wq, wk ~
+    N(1, 0.1); the position's rotation table; key and value caches
+    [hkv, max_pos, 128] whose rows below ``pos`` hold N(0, 1) values (the
+    earlier tokens) and zeros above."""
+    kc = np.zeros((hkv, max_pos, ATQ_D), np.float32)
+    vc = np.zeros((hkv, max_pos, ATQ_D), np.float32)
+    if pos > 0:
+        kc[:, :pos] = normal_f32(seed, "atq.kcache", (hkv, pos, ATQ_D), 0.0, 1.0)
+        vc[:, :pos] = normal_f32(seed, "atq.vcache", (hkv, pos, ATQ_D), 0.0, 1.0)
+    c, s = rope_table(pos)
+    return {
+        "q": normal_f32(seed, "atq.q", (hq * ATQ_D,), 0.0, 1.0),
+        "g": normal_f32(seed, "atq.g", (hq * ATQ_D,), 0.0, 1.0),
+        "k": normal_f32(seed, "atq.k", (hkv * ATQ_D,), 0.0, 1.0),
+        "v": normal_f32(seed, "atq.v", (hkv * ATQ_D,), 0.0, 1.0),
+        "wq": normal_f32(seed, "atq.wq", (ATQ_D,), 1.0, 0.1),
+        "wk": normal_f32(seed, "atq.wk", (ATQ_D,), 1.0, 0.1),
+        "cos": c, "sin": s, "kcache": kc, "vcache": vc, "pos": pos,
+        "eps": np.float32(EPS), "hq": hq, "hkv": hkv, "max_pos": max_pos,
+    }

@@ -499,3 +499,173 @@ def test_chain_step_against_binary64_forward():
         # the next step depends only on the token: resuming reproduces it
         assert oracle.chain_step(w, tok)[1] == nxt
         tok = nxt
+
+
+# ---------------------------------------------------------------------------
+# atq: the attention step (readings in oracle/q4_oracle.c), pinned against an
+# independent binary64 forward pass and against closed forms
+# ---------------------------------------------------------------------------
+def _atq_run(a):
+    kc, vc = a["kcache"].copy(), a["vcache"].copy()
+    o, os_ = oracle.atq(a["q"], a["g"], a["k"], a["v"], a["wq"], a["wk"], a["eps"], a["cos"],
+                        a["sin"], kc, vc, a["pos"])
+    return o, os_, kc, vc
+
+
+def _atq_ref64(a):
+    D = 128
+    hq, hkv, pos = a["hq"], a["hkv"], a["pos"]
+    grp = hq // hkv
+    eps = float(a["eps"])
+    c, s = a["cos"].astype(np.float64), a["sin"].astype(np.float64)
+
+    def norm(x, w):
+        x = x.astype(np.float64)
+        return x / np.sqrt(np.mean(x * x) + eps) * w.astype(np.float64)
+
+    def rot(x):
+        lo, hi = x[:D // 2], x[D // 2:]
+        return np.concatenate([lo * c - hi * s, lo * s + hi * c])
+
+    K = a["kcache"].astype(np.float64).copy()
+    V = a["vcache"].astype(np.float64).copy()
+    for j in range(hkv):
+        K[j, pos] = rot(norm(a["k"][j * D:(j + 1) * D], a["wk"]))
+        V[j, pos] = a["v"][j * D:(j + 1) * D]
+    o = np.empty(hq * D)
+    for h in range(hq):
+        j = h // grp
+        qr = rot(norm(a["q"][h * D:(h + 1) * D], a["wq"]))
+        sc = K[j, :pos + 1] @ qr / np.sqrt(D)
+        p = np.exp(sc - sc.max())
+        w = (p @ V[j, :pos + 1]) / p.sum()
+        g = a["g"][h * D:(h + 1) * D].astype(np.float64)
+        o[h * D:(h + 1) * D] = w / (1.0 + np.exp(-g))
+    return o, K, V
+
+
+@pytest.mark.parametrize("pos,hq,hkv", [(0, 16, 4), (1, 16, 4), (63, 4, 2), (204, 16, 4),
+                                        (300, 2, 2)])
+def test_atq_matches_binary64_forward(pos, hq, hkv):
+    a = synth.atq_inputs(seed=61 + pos, pos=pos, hq=hq, hkv=hkv, max_pos=512)
+    o, os_, kc, vc = _atq_run(a)
+    o64, K64, V64 = _atq_ref64(a)
+    scale = np.sqrt(np.mean(o64 ** 2))
+    assert np.max(np.abs(o - o64)) <= 2e-5 * scale, np.max(np.abs(o - o64)) / scale
+    # the new cache rows; every other row untouched
+    assert np.max(np.abs(kc[:, pos] - K64[:, pos])) <= 1e-5
+    assert np.array_equal(vc[:, pos], a["v"].reshape(hkv, 128))
+    keep = np.ones(512, bool)
+    keep[pos] = False
+    assert np.array_equal(kc[:, keep], a["kcache"][:, keep])
+    assert np.array_equal(vc[:, keep], a["vcache"][:, keep])
+    # group sums of o
+    assert np.array_equal(os_, oracle.group_sums(o))
+
+
+def test_atq_first_position_is_gated_value():
+    """One position: the softmax weight is E(0) = 1 exactly, Z = 1, so o is
+    the new value times the sigmoid of the gate."""
+    a = synth.atq_inputs(seed=71, pos=0, max_pos=8)
+    o, _, _, _ = _atq_run(a)
+    v = a["v"].reshape(4, 128)
+    sig = (1.0 / (1.0 + np.exp(-a["g"].astype(np.float64)))).astype(np.float32)
+    want = np.repeat(v, 4, axis=0).ravel() * sig
+    # the sigmoid may differ from libm's in its last bit
+    assert np.max(np.abs(o - want) / np.maximum(np.abs(want), 1e-30)) <= 2.5e-7
+    # values 1: o is the gate's sigmoid itself, taken in binary64 and rounded
+    # once to binary32.  libm's binary64 exp is within an ulp of the fixed
+    # exp, far below binary32's rounding step, so the bits agree (a sigmoid
+    # evaluated in binary32 differs in a good share of them)
+    a["v"] = np.ones_like(a["v"])
+    o, _, _, _ = _atq_run(a)
+    sig = (1.0 / (1.0 + np.exp(-a["g"].astype(np.float64)))).astype(np.float32)
+    assert np.array_equal(o, sig)
+
+
+def test_atq_equal_keys_weighted_sum_is_the_tree():
+    """All keys equal (so every weight is exactly 1 and Z is the count) and
+    a saturated gate (sigmoid exactly 1): o is T over the value column
+    divided by the count, bit for bit."""
+    pos = 37
+    a = synth.atq_inputs(seed=72, pos=pos, max_pos=64)
+    # the generator's normals sit on a 2^-16 grid, where any summation order
+    # is exact; scaling by RN32(1/3) fills the significands, so the order of
+    # the value sum shows in the bits
+    third = np.float32(1.0 / 3.0)
+    a["vcache"] = a["vcache"] * third
+    a["v"] = a["v"] * third
+    # the key the step writes at position pos, copied into every earlier row
+    first = dict(a, pos=0, kcache=np.zeros_like(a["kcache"]), vcache=np.zeros_like(a["vcache"]))
+    _, _, k0, _ = _atq_run(first)
+    a["kcache"][:, :pos] = k0[:, :1]
+    a["g"] = np.full_like(a["g"], 40.0)
+    o, _, kc, vc = _atq_run(a)
+    assert np.array_equal(kc[:, :pos + 1], np.repeat(k0[:, :1], pos + 1, axis=1))
+    for h in range(16):
+        j = h // 4
+        col = np.array([oracle.tree(vc[j, :pos + 1, i]) for i in range(128)], np.float32)
+        want = col / np.float32(pos + 1)
+        assert np.array_equal(o[h * 128:(h + 1) * 128].view(np.uint32), want.view(np.uint32)), h
+
+
+def test_atq_unit_values_give_unit_output():
+    """Every value 1 and a saturated gate: the weighted sum and Z are the
+    same tree over the same weights, so o is exactly 1 at every position
+    count, whatever the scores."""
+    for pos in (1, 6, 37, 200):
+        a = synth.atq_inputs(seed=75 + pos, pos=pos, max_pos=256)
+        a["vcache"][:, :pos] = 1.0
+        a["v"] = np.ones_like(a["v"])
+        a["g"] = np.full_like(a["g"], 40.0)
+        o, _, _, _ = _atq_run(a)
+        assert np.array_equal(o, np.ones_like(o)), pos
+
+
+def test_atq_score_is_the_tree_of_products():
+    """A score whose terms cancel only in the canonical tree order.  With
+    eps = 0, q = 1 and wq = 1 the normed query is exactly 1; an identity
+    rotation (c = 1, s = 0) keeps it; so the score of an earlier key row is
+    T(row) * SCALE.  Row [2^30, 1 x 63, -2^30, 1 x 63]: T loses every 1
+    against the 2^30 in each half and returns 0 (a left-to-right sum gives
+    63).  The new key is zero (wk = 0), so both scores are 0, both weights
+    E(0) = 1, and o = (V_0 + V_1) / 2 exactly."""
+    a = synth.atq_inputs(seed=79, pos=1, hq=4, hkv=2, max_pos=4)
+    a["eps"] = np.float32(0.0)
+    a["q"] = np.ones_like(a["q"])
+    a["wq"] = np.ones_like(a["wq"])
+    a["k"] = np.ones_like(a["k"])
+    a["wk"] = np.zeros_like(a["wk"])
+    a["cos"] = np.ones_like(a["cos"])
+    a["sin"] = np.zeros_like(a["sin"])
+    a["g"] = np.full_like(a["g"], 40.0)
+    row = np.ones(128, np.float32)
+    row[0], row[64] = 2.0 ** 30, -(2.0 ** 30)
+    a["kcache"][:, 0] = row
+    # value rows on a coarse grid so that (V_0 + V_1) / 2 is exact
+    a["vcache"][:, 0] = np.round(a["vcache"][:, 0] * 8) / 8
+    a["v"] = np.round(a["v"] * 8) / 8
+    o, _, kc, _ = _atq_run(a)
+    assert np.array_equal(kc[:, 1].view(np.uint32), np.zeros((2, 128), np.uint32))
+    mean = (a["vcache"][:, 0] + a["v"].reshape(2, 128)) / np.float32(2.0)
+    want = np.repeat(mean, 2, axis=0).ravel()
+    assert np.array_equal(o, want)
+
+
+def test_atq_large_scores_stay_finite():
+    a = synth.atq_inputs(seed=73, pos=100, max_pos=128)
+    a["wq"] = a["wq"] * np.float32(30.0)  # scores ~ 30x larger
+    o, _, _, _ = _atq_run(a)
+    o64, _, _ = _atq_ref64(a)
+    assert np.all(np.isfinite(o))
+    assert np.max(np.abs(o - o64)) <= 1e-4 * np.sqrt(np.mean(o64 ** 2))
+
+
+def test_atq_rejects_shapes_outside_the_readings():
+    a = synth.atq_inputs(seed=74, pos=3, hq=4, hkv=4, max_pos=8)
+    with pytest.raises(ValueError):
+        oracle.atq(a["q"], a["g"], a["k"][:3 * 128], a["v"][:3 * 128], a["wq"], a["wk"],
+                   a["eps"], a["cos"], a["sin"], a["kcache"][:3].copy(), a["vcache"][:3].copy(), 3)
+    with pytest.raises(ValueError):
+        oracle.atq(a["q"], a["g"], a["k"], a["v"], a["wq"], a["wk"], a["eps"], a["cos"],
+                   a["sin"], a["kcache"], a["vcache"], 8)
