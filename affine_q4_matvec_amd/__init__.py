@@ -31,6 +31,8 @@ Q4_OK, Q4_EINVAL, Q4_EHIP, Q4_ETIMEOUT, Q4_ESTATE, Q4_ENOMEM = 0, -1, -2, -3, -4
 MAX_COLS = 32768
 MAX_RMSQ_N = 8192
 MAX_DECODE_LAYERS = 32
+ATQ_D = 128
+ATQ_MAX_POS = 4096
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libq4mv.so")
@@ -73,6 +75,9 @@ _SIGS = {
                           ctypes.c_float, _vp, _vp, ctypes.c_size_t, ctypes.c_int, _vp],
                          ctypes.c_int),
     "q4_decode_layers_status": ([_vp, _vp], ctypes.c_int),
+    "q4_atq_ws_bytes": ([_i32, _i32], ctypes.c_size_t),
+    "q4_atq": ([_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _i32, _i32,
+                _i32, _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "q4_queue_create": ([_vp, ctypes.c_int, ctypes.POINTER(_vp)], ctypes.c_int),
     "q4_queue_destroy": ([_vp], ctypes.c_int),
     "q4mv_queue": ([_vp, ctypes.POINTER(_Mat), _vp, _vp, _vp], ctypes.c_int),
@@ -331,6 +336,36 @@ def q4_decode_layers_status(ws: torch.Tensor, stream=None) -> int:
     """Host wait; Q4_OK, or Q4_ETIMEOUT when a wait of the persistent
     kernel ran out (the workspace is then cleared)."""
     return int(_lib.q4_decode_layers_status(_dev(ws, ws.dtype, None, "ws"), _stream(stream)))
+
+
+def q4_atq_ws_bytes(hq: int, hkv: int) -> int:
+    """Workspace bytes of ``q4_atq`` for these head counts (0: outside the
+    limits)."""
+    return int(_lib.q4_atq_ws_bytes(int(hq), int(hkv)))
+
+
+def q4_atq(q: torch.Tensor, g: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+           wq: torch.Tensor, wk: torch.Tensor, eps: float, rope_cos: torch.Tensor,
+           rope_sin: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, pos: int,
+           o: torch.Tensor, osum: torch.Tensor, ws: torch.Tensor, stream=None) -> torch.Tensor:
+    """Gated attention of one decode token: writes row ``pos`` of the
+    ``[hkv, max_pos, 128]`` caches and ``o`` (``hq * 128`` values) with its
+    group sums ``osum`` (``hq * 2``).  ``ws``: ``q4_atq_ws_bytes(hq, hkv)``
+    bytes, 256-byte aligned (any fresh torch allocation is)."""
+    if kcache.dim() != 3 or kcache.shape[2] != ATQ_D or vcache.shape != kcache.shape:
+        raise ValueError("caches must be [hkv, max_pos, 128]")
+    hkv, max_pos = int(kcache.shape[0]), int(kcache.shape[1])
+    hq = q.numel() // ATQ_D
+    f = torch.float32
+    _check("q4_atq", _lib.q4_atq(
+        _dev(q, f, hq * ATQ_D, "q"), _dev(g, f, hq * ATQ_D, "g"), _dev(k, f, hkv * ATQ_D, "k"),
+        _dev(v, f, hkv * ATQ_D, "v"), _dev(wq, f, ATQ_D, "wq"), _dev(wk, f, ATQ_D, "wk"),
+        float(eps), _dev(rope_cos, f, ATQ_D // 2, "rope_cos"),
+        _dev(rope_sin, f, ATQ_D // 2, "rope_sin"), _dev(kcache, f, None, "kcache"),
+        _dev(vcache, f, None, "vcache"), int(pos), max_pos, hq, hkv,
+        _dev(o, f, hq * ATQ_D, "o"), _dev(osum, f, hq * 2, "osum"),
+        _dev(ws, ws.dtype, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+    return o
 
 
 class Mailbox:

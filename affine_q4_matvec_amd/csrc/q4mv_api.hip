@@ -429,6 +429,63 @@ int q4_decode_layers_status(void *ws, void *stream) {
   return Q4_ETIMEOUT;
 }
 
+size_t q4_atq_ws_bytes(int32_t hq, int32_t hkv) {
+  if (hq < 1 || hq > q4::kAtqMaxHeads || hkv < 1 || hq % hkv != 0 ||
+      hq / hkv > q4::kAtqMaxGroup)
+    return 0;
+  q4::AtqWs L;
+  q4::atq_ws_layout(hq, hkv, &L);
+  return L.bytes;
+}
+
+int q4_atq(const float *q, const float *g, const float *k, const float *v, const float *wq,
+           const float *wk, float eps, const float *rope_cos, const float *rope_sin,
+           float *kcache, float *vcache, int32_t pos, int32_t max_pos, int32_t hq, int32_t hkv,
+           float *o, float *osum, void *ws, size_t ws_bytes, void *stream) {
+  const size_t need = q4_atq_ws_bytes(hq, hkv);
+  if (need == 0) return Q4_EINVAL;
+  if (max_pos < 1 || max_pos > q4::kAtqMaxPos || pos < 0 || pos >= max_pos) return Q4_EINVAL;
+  const float *in16[5] = {q, k, v, wq, wk};
+  for (int i = 0; i < 5; ++i)
+    if (!in16[i] || !aligned(in16[i], 16)) return Q4_EINVAL;
+  if (!g || !aligned(g, 4) || !rope_cos || !aligned(rope_cos, 4) || !rope_sin ||
+      !aligned(rope_sin, 4))
+    return Q4_EINVAL;
+  if (!kcache || !vcache || !aligned(kcache, 16) || !aligned(vcache, 16)) return Q4_EINVAL;
+  if (!o || !aligned(o, 4) || !osum || !aligned(osum, 4)) return Q4_EINVAL;
+  if (!ws || !aligned(ws, 256) || ws_bytes < need) return Q4_EINVAL;
+  const size_t D = q4::kAtqD;
+  const size_t qb = sizeof(float) * (size_t)hq * D, kb = sizeof(float) * (size_t)hkv * D;
+  const size_t cb = sizeof(float) * (size_t)hkv * (size_t)max_pos * D;
+  const size_t wb = sizeof(float) * D, rb = sizeof(float) * D / 2;
+  // written: the caches, o, osum and the workspace; they overlap nothing
+  const void *outs[5] = {kcache, vcache, o, osum, ws};
+  const size_t outb[5] = {cb, cb, qb, sizeof(float) * (size_t)hq * 2, need};
+  const void *ins[8] = {q, g, k, v, wq, wk, rope_cos, rope_sin};
+  const size_t inb[8] = {qb, qb, kb, kb, wb, wb, rb, rb};
+  for (int i = 0; i < 5; ++i) {
+    for (int m = i + 1; m < 5; ++m)
+      if (overlap(outs[i], outb[i], outs[m], outb[m])) return Q4_EINVAL;
+    for (int m = 0; m < 8; ++m)
+      if (overlap(outs[i], outb[i], ins[m], inb[m])) return Q4_EINVAL;
+  }
+  q4::AtqWs L;
+  q4::atq_ws_layout(hq, hkv, &L);
+  char *w = static_cast<char *>(ws);
+  q4::AtqArgs a;
+  a.q = q; a.g = g; a.k = k; a.v = v; a.wq = wq; a.wk = wk;
+  a.cs = rope_cos; a.sn = rope_sin;
+  a.kc = kcache; a.vc = vcache; a.o = o; a.os = osum;
+  a.sc = reinterpret_cast<float *>(w + L.sc);
+  a.cmax = reinterpret_cast<float *>(w + L.cmax);
+  a.zp = reinterpret_cast<float *>(w + L.zp);
+  a.wp = reinterpret_cast<float *>(w + L.wp);
+  a.cnt = reinterpret_cast<uint32_t *>(w + L.cnt);
+  a.eps = eps;
+  a.pos = pos; a.max_pos = max_pos; a.hq = hq; a.hkv = hkv;
+  return hip_status(q4::launch_atq(a, static_cast<hipStream_t>(stream)));
+}
+
 int q4_queue_create(void *stream, int mode, q4_queue **out) {
   if (!out || (mode != Q4_FIXED && mode != Q4_FAST)) return Q4_EINVAL;
   *out = nullptr;

@@ -135,4 +135,35 @@ constexpr size_t kDecodeWsBytes = kDecodeCtlOffset + 4 * (kDecodeErrorWord + 32)
 int32_t decode_layers_grid(int mode, int32_t inter);
 hipError_t launch_decode_layers(const DecodeArgs &a, int mode, hipStream_t st);
 
+// Gated attention of one decode token (atq.hip).  Caches are float
+// [hkv][max_pos][128]; positions are worked on in aligned chunks of 64.
+constexpr int kAtqD = 128;
+constexpr int kAtqChunk = 64;
+constexpr int kAtqMaxPos = 4096;
+constexpr int kAtqMaxChunks = kAtqMaxPos / kAtqChunk;
+constexpr int kAtqMaxGroup = 8;   // query heads per key/value head
+constexpr int kAtqMaxHeads = 128; // query heads
+struct AtqArgs {
+  const float *q, *g;    // [hq][128]
+  const float *k, *v;    // [hkv][128]
+  const float *wq, *wk;  // [128] norm weights
+  const float *cs, *sn;  // [64] rotation table of the position
+  float *kc, *vc;        // [hkv][max_pos][128] caches; row pos is written
+  float *o;              // [hq][128]
+  float *os;             // [hq][2] group sums of o
+  float *sc;             // workspace: [hq][kAtqMaxPos] scores
+  float *cmax;           // workspace: [hq][kAtqMaxChunks] chunk maxima
+  float *zp;             // workspace: [hq][kAtqMaxChunks] chunk sums of weights
+  float *wp;             // workspace: [hq][kAtqMaxChunks][128] chunk value sums
+  uint32_t *cnt;         // workspace: [hkv] arrival counters
+  float eps;
+  int32_t pos, max_pos, hq, hkv;
+};
+// Byte offsets of the workspace arrays for hq query and hkv key/value heads.
+struct AtqWs {
+  size_t sc, cmax, zp, wp, cnt, bytes;
+};
+void atq_ws_layout(int32_t hq, int32_t hkv, AtqWs *out);
+hipError_t launch_atq(const AtqArgs &a, hipStream_t st);
+
 }  // namespace q4

@@ -239,6 +239,47 @@ int q4_decode_layers(const q4_mat *emb, const int32_t *tok, const q4_mlp_layer *
 int q4_decode_layers_status(void *ws, void *stream);
 
 /*
+ * Gated attention of one decode token over key/value caches ([P1] Change,
+ * atq bullet: q/k RMS norm and rotation, the new key and value written to
+ * the caches, scores, softmax, weighted values, sigmoid gate and group sums;
+ * query heads in groups that share a key/value head).  The pages state no
+ * formulas; the operations as read, D = 128, G = hq / hkv, query head h
+ * using key/value head j = h / G, n = pos + 1:
+ *   qn = rmsq(q_h, wq), kn = rmsq(k_j, wk)          (rmsq over 128 values)
+ *   rotate(x)_i      = (x_i c_i) - (x_{i+64} s_i)      i < 64, with
+ *   rotate(x)_{i+64} = (x_i s_i) + (x_{i+64} c_i)      c = rope_cos, s = rope_sin
+ *   kcache[j][pos] = rotate(kn), vcache[j][pos] = v_j
+ *   s_t = T(rotate(qn) * kcache[j][t]) * RN32(1/sqrt(128)),  t < n
+ *   e_t = RN32(E(s_t - max_t s_t))   (E: the fixed binary64 exp of swq)
+ *   o_h = (T(e_t * vcache[j][t] over t) / T(e)) * RN32(1 / (1 + E(-g_h)))
+ *   osum[2h + b] = T(o_h[64b .. 64b+63])
+ * with T the canonical tree of q4mv; bit-identical to the reference.
+ *
+ *   q, g    : device float[hq][128] query and gate; q 16-byte aligned.
+ *   k, v    : device float[hkv][128] new key and value, 16-byte aligned.
+ *   wq, wk  : device float[128] norm weights, 16-byte aligned.
+ *   rope_cos, rope_sin : device float[64], the position's rotation table.
+ *   kcache, vcache : device float[hkv][max_pos][128], 16-byte aligned; rows
+ *             below pos are read, row pos is written, others untouched.
+ *   pos     : 0 <= pos < max_pos <= Q4_ATQ_MAX_POS.
+ *   hq, hkv : 1 <= hkv, hq % hkv == 0, hq / hkv <= 8, hq <= 128.
+ *   o       : device float[hq][128]; osum: device float[hq][2].
+ *   ws      : device workspace of q4_atq_ws_bytes(hq, hkv) bytes, 256-byte
+ *             aligned, contents irrelevant.  Calls that overlap in time must
+ *             not share it.
+ * Two launches on `stream`; every output and the workspace must overlap no
+ * other argument.  Inputs are assumed finite (a NaN score makes the
+ * position of the maximum, and so the output, unspecified).
+ * q4_atq_ws_bytes returns 0 for head counts outside the limits above.
+ */
+#define Q4_ATQ_MAX_POS 4096
+size_t q4_atq_ws_bytes(int32_t hq, int32_t hkv);
+int q4_atq(const float *q, const float *g, const float *k, const float *v, const float *wq,
+           const float *wk, float eps, const float *rope_cos, const float *rope_sin,
+           float *kcache, float *vcache, int32_t pos, int32_t max_pos, int32_t hq, int32_t hkv,
+           float *o, float *osum, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Stage queue ([P2] Change: q4go encodes products into one open concurrent
  * command buffer and returns; q4wait commits and waits once).
  * q4mv_queue appends a product to the current stage.  Products of one stage

@@ -188,3 +188,39 @@ def test_mailbox_argument_checks(L):
 
 def test_queue_set_wait_checks(L):
     assert L.q4_queue_set_wait(None, 0, 10) == EINVAL
+
+
+def test_atq_argument_checks(L):
+    L.q4_atq_ws_bytes.restype = ctypes.c_size_t
+    assert L.q4_atq_ws_bytes(16, 4) > 16 * 4096 * 4
+    for hq, hkv in ((0, 1), (16, 0), (16, 3), (18, 2), (256, 32), (129, 129)):
+        assert L.q4_atq_ws_bytes(hq, hkv) == 0, (hq, hkv)
+    wsb = L.q4_atq_ws_bytes(16, 4)
+    H = 0x7F0100000000
+    f = ctypes.c_float
+    base = dict(q=A, g=B, k=C, v=C + 0x100000, wq=C + 0x200000, wk=C + 0x300000,
+                cs=C + 0x400000, sn=C + 0x500000, kc=D, vc=E, pos=204, max_pos=4096, hq=16,
+                hkv=4, o=F, os=F + 0x100000, ws=H, wsb=wsb)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        p = ctypes.c_void_p
+        return L.q4_atq(p(a["q"]), p(a["g"]), p(a["k"]), p(a["v"]), p(a["wq"]), p(a["wk"]),
+                        f(1e-6), p(a["cs"]), p(a["sn"]), p(a["kc"]), p(a["vc"]), a["pos"],
+                        a["max_pos"], a["hq"], a["hkv"], p(a["o"]), p(a["os"]), p(a["ws"]),
+                        ctypes.c_size_t(a["wsb"]), None)
+
+    assert call(pos=-1) == EINVAL
+    assert call(pos=4096) == EINVAL                 # pos == max_pos
+    assert call(max_pos=4097, pos=0) == EINVAL      # cache longer than the limit
+    assert call(hq=16, hkv=3) == EINVAL             # heads not in groups
+    assert call(hq=32, hkv=2) == EINVAL             # 16 queries per key/value head
+    assert call(q=0) == EINVAL
+    assert call(q=A + 4) == EINVAL                  # q misaligned
+    assert call(kc=D + 8) == EINVAL                 # cache misaligned
+    assert call(ws=H + 16) == EINVAL                # workspace misaligned
+    assert call(wsb=wsb - 4) == EINVAL              # workspace too small
+    assert call(vc=D + 4096 * 512) == EINVAL        # value cache inside the key cache
+    assert call(o=A + 512) == EINVAL                # o over q
+    assert call(ws=D) == EINVAL                     # workspace over the key cache
+    assert call(os=C + 0x400000) == EINVAL          # osum over the rotation table
