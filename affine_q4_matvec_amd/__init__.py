@@ -76,7 +76,7 @@ _SIGS = {
                          ctypes.c_int),
     "q4_decode_layers_status": ([_vp, _vp], ctypes.c_int),
     "q4_atq_ws_bytes": ([_i32, _i32], ctypes.c_size_t),
-    "q4_atq": ([_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _i32, _i32,
+    "q4_atq": ([_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _i32,
                 _i32, _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "q4_queue_create": ([_vp, ctypes.c_int, ctypes.POINTER(_vp)], ctypes.c_int),
     "q4_queue_destroy": ([_vp], ctypes.c_int),
@@ -346,23 +346,27 @@ def q4_atq_ws_bytes(hq: int, hkv: int) -> int:
 
 def q4_atq(q: torch.Tensor, g: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
            wq: torch.Tensor, wk: torch.Tensor, eps: float, rope_cos: torch.Tensor,
-           rope_sin: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, pos: int,
-           o: torch.Tensor, osum: torch.Tensor, ws: torch.Tensor, stream=None) -> torch.Tensor:
-    """Gated attention of one decode token: writes row ``pos`` of the
+           rope_sin: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+           pos: torch.Tensor, o: torch.Tensor, osum: torch.Tensor, ws: torch.Tensor,
+           stream=None) -> torch.Tensor:
+    """Gated attention of one decode token at the position held in ``pos``
+    (device int32[1], read on the device): writes that row of the
     ``[hkv, max_pos, 128]`` caches and ``o`` (``hq * 128`` values) with its
-    group sums ``osum`` (``hq * 2``).  ``ws``: ``q4_atq_ws_bytes(hq, hkv)``
+    group sums ``osum`` (``hq * 2``).  ``rope_cos``/``rope_sin``: the
+    ``[max_pos, 64]`` rotation tables.  ``ws``: ``q4_atq_ws_bytes(hq, hkv)``
     bytes, 256-byte aligned (any fresh torch allocation is)."""
     if kcache.dim() != 3 or kcache.shape[2] != ATQ_D or vcache.shape != kcache.shape:
         raise ValueError("caches must be [hkv, max_pos, 128]")
     hkv, max_pos = int(kcache.shape[0]), int(kcache.shape[1])
     hq = q.numel() // ATQ_D
     f = torch.float32
+    rn = max_pos * (ATQ_D // 2)
     _check("q4_atq", _lib.q4_atq(
         _dev(q, f, hq * ATQ_D, "q"), _dev(g, f, hq * ATQ_D, "g"), _dev(k, f, hkv * ATQ_D, "k"),
         _dev(v, f, hkv * ATQ_D, "v"), _dev(wq, f, ATQ_D, "wq"), _dev(wk, f, ATQ_D, "wk"),
-        float(eps), _dev(rope_cos, f, ATQ_D // 2, "rope_cos"),
-        _dev(rope_sin, f, ATQ_D // 2, "rope_sin"), _dev(kcache, f, None, "kcache"),
-        _dev(vcache, f, None, "vcache"), int(pos), max_pos, hq, hkv,
+        float(eps), _dev(rope_cos, f, rn, "rope_cos"), _dev(rope_sin, f, rn, "rope_sin"),
+        _dev(kcache, f, None, "kcache"), _dev(vcache, f, None, "vcache"),
+        _dev(pos, torch.int32, 1, "pos"), max_pos, hq, hkv,
         _dev(o, f, hq * ATQ_D, "o"), _dev(osum, f, hq * 2, "osum"),
         _dev(ws, ws.dtype, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
     return o

@@ -19,9 +19,14 @@
 // with T the canonical tree (the balanced tree over the next power of two
 // with -0 in the empty slots).  Compiled with -ffp-contract=off.
 //
+// The position is read from device memory (a captured graph replays the
+// same launches token after token), with the rotation table's row of that
+// position.
+//
 // Layout of the work (MI355X-first rather than one workgroup per query
 // head): the positions are cut into aligned chunks of 64, and a grid of
-// (chunks x key/value heads) workgroups runs twice.
+// (chunks of the whole cache x key/value heads) workgroups runs twice; the
+// workgroups past the position leave at once.
 //   scores kernel:  each workgroup normalises and rotates the G queries of
 //     its head group (and, in the chunk holding pos, the new key, which it
 //     writes to the caches with the new value), reads each key row of its
@@ -89,10 +94,16 @@ __global__ __launch_bounds__(kThreads) void atq_scores_kernel(AtqArgs a) {
   const int c = blockIdx.x;  // chunk of positions
   const int j = blockIdx.y;  // key/value head
   const int G = a.hq / a.hkv;
-  const int n = a.pos + 1;
-  const bool owns_pos = c == a.pos / kC;
   // the weights kernel's arrival counter of this head group starts at zero
   if (c == 0 && t == 0) a.cnt[j] = 0u;
+  const int pos = *a.pos;
+  // outside the cache (the weights kernel then writes NaN) or past the
+  // position: nothing to do
+  if (pos < 0 || pos >= a.max_pos || c > pos / kC) return;
+  const int n = pos + 1;
+  const bool owns_pos = c == pos / kC;
+  const float *cs = a.cs + (size_t)pos * (kD / 2);
+  const float *sn = a.sn + (size_t)pos * (kD / 2);
 
   // 16 lanes per row, 8 values per lane: rows r < G are the queries of
   // heads j*G + r; row G is the new key, in the workgroup owning pos only
@@ -111,14 +122,14 @@ __global__ __launch_bounds__(kThreads) void atq_scores_kernel(AtqArgs a) {
     const int i0 = 8 * (l & 7);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      ct[k] = a.cs[i0 + k];
-      st[k] = a.sn[i0 + k];
+      ct[k] = cs[i0 + k];
+      st[k] = sn[i0 + k];
     }
   }
 #pragma unroll
   for (int pass = 0; pass < kC / 16; ++pass) {
     const int tp = c * kC + 16 * pass + r;
-    if (tp < n && tp != a.pos) load8(a.kc + ((size_t)j * a.max_pos + tp) * kD + 8 * l, kv[pass]);
+    if (tp < n && tp != pos) load8(a.kc + ((size_t)j * a.max_pos + tp) * kD + 8 * l, kv[pass]);
   }
   if (active) {
     float sq[8];
@@ -147,8 +158,8 @@ __global__ __launch_bounds__(kThreads) void atq_scores_kernel(AtqArgs a) {
       rot[r][i] = rv[k];
     }
     if (r == G) {
-      float *kd = a.kc + ((size_t)j * a.max_pos + a.pos) * kD + 8 * l;
-      float *vd = a.vc + ((size_t)j * a.max_pos + a.pos) * kD + 8 * l;
+      float *kd = a.kc + ((size_t)j * a.max_pos + pos) * kD + 8 * l;
+      float *vd = a.vc + ((size_t)j * a.max_pos + pos) * kD + 8 * l;
       const float *vs = a.v + (size_t)j * kD + 8 * l;
       reinterpret_cast<float4 *>(kd)[0] = make_float4(rv[0], rv[1], rv[2], rv[3]);
       reinterpret_cast<float4 *>(kd)[1] = make_float4(rv[4], rv[5], rv[6], rv[7]);
@@ -173,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void atq_scores_kernel(AtqArgs a) {
   for (int pass = 0; pass < kC / 16; ++pass) {
     const int tp = c * kC + 16 * pass + r;
     if (tp < n) {  // uniform over the 16 lanes of the position
-      if (tp == a.pos) {
+      if (tp == pos) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) kv[pass][k] = rot[G][8 * l + k];
       }
@@ -216,8 +227,17 @@ __global__ __launch_bounds__(kThreads) void atq_weights_kernel(AtqArgs a) {
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int c = blockIdx.x, j = blockIdx.y;
   const int G = a.hq / a.hkv;
-  const int n = a.pos + 1;
-  const int nchunk = (n + kC - 1) / kC;
+  const int pos = *a.pos;
+  if (pos < 0 || pos >= a.max_pos) {  // no such cache row: o and osum are NaN
+    if (c == 0) {
+      for (int idx = t; idx < G * kD; idx += kThreads) a.o[(size_t)j * G * kD + idx] = NAN;
+      if (t < 2 * G) a.os[(size_t)j * G * 2 + t] = NAN;
+    }
+    return;
+  }
+  if (c > pos / kC) return;
+  const int n = pos + 1;
+  const int nchunk = pos / kC + 1;
   const int i = t & (kD - 1), half = t / kD;
   const int p0 = c * kC + 32 * half;
   const int tp = c * kC + lane;
@@ -338,8 +358,9 @@ void atq_ws_layout(int32_t hq, int32_t hkv, AtqWs *out) {
 }
 
 hipError_t launch_atq(const AtqArgs &a, hipStream_t st) {
-  const int nchunk = (a.pos + 1 + kAtqChunk - 1) / kAtqChunk;
-  const dim3 grid(nchunk, a.hkv);
+  // one workgroup per chunk of the whole cache: the position is read on the
+  // device, and the workgroups past it leave at once
+  const dim3 grid((a.max_pos + kAtqChunk - 1) / kAtqChunk, a.hkv);
   hipLaunchKernelGGL(atq_scores_kernel, grid, dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

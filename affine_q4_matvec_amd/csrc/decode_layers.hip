@@ -57,6 +57,7 @@
 #include "ops_device.h"
 #include "q4mv_device.h"
 #include "q4mv_internal.h"
+#include "tagged_device.h"
 
 #pragma clang fp contract(off)
 
@@ -116,47 +117,6 @@ __device__ __forceinline__ void load_down(const DecodeLayer &L, int r, int lane,
     d.cw[p] = load_codes(qr, 16u * lane, p * 1024);
     d.sv[p] = load_f32(sr, 4u * (lane >> 1), p * 128);
     d.bv[p] = load_f32(br, 4u * (lane >> 1), p * 128);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Device-scope words
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t load_word(const uint32_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void store_word(uint32_t *p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void store_tagged(uint64_t *p, float v, uint32_t tag) {
-  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Polls the N tagged words at p until each carries `tag`; their floats go to
-// v.  False when the wait ran out (the error word is then set) or another
-// workgroup's did.
-template <int N>
-__device__ __forceinline__ bool poll_tagged(const uint64_t *p, uint32_t tag, float *v,
-                                            uint32_t *err, long long spin_ticks) {
-  const long long t0 = wall_clock64();
-  for (int it = 1;; ++it) {
-    bool ready = true;
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-      const uint64_t w = __hip_atomic_load(p + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      v[k] = __uint_as_float((uint32_t)w);
-      ready &= (uint32_t)(w >> 32) == tag;
-    }
-    if (ready) return true;
-    if ((it & 63) == 0 && load_word(err) != 0) return false;
-    if (wall_clock64() - t0 > spin_ticks) {
-      store_word(err, 1u);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(1);
   }
 }
 

@@ -440,11 +440,11 @@ size_t q4_atq_ws_bytes(int32_t hq, int32_t hkv) {
 
 int q4_atq(const float *q, const float *g, const float *k, const float *v, const float *wq,
            const float *wk, float eps, const float *rope_cos, const float *rope_sin,
-           float *kcache, float *vcache, int32_t pos, int32_t max_pos, int32_t hq, int32_t hkv,
-           float *o, float *osum, void *ws, size_t ws_bytes, void *stream) {
+           float *kcache, float *vcache, const int32_t *pos, int32_t max_pos, int32_t hq,
+           int32_t hkv, float *o, float *osum, void *ws, size_t ws_bytes, void *stream) {
   const size_t need = q4_atq_ws_bytes(hq, hkv);
   if (need == 0) return Q4_EINVAL;
-  if (max_pos < 1 || max_pos > q4::kAtqMaxPos || pos < 0 || pos >= max_pos) return Q4_EINVAL;
+  if (max_pos < 1 || max_pos > q4::kAtqMaxPos || !pos || !aligned(pos, 4)) return Q4_EINVAL;
   const float *in16[5] = {q, k, v, wq, wk};
   for (int i = 0; i < 5; ++i)
     if (!in16[i] || !aligned(in16[i], 16)) return Q4_EINVAL;
@@ -457,16 +457,16 @@ int q4_atq(const float *q, const float *g, const float *k, const float *v, const
   const size_t D = q4::kAtqD;
   const size_t qb = sizeof(float) * (size_t)hq * D, kb = sizeof(float) * (size_t)hkv * D;
   const size_t cb = sizeof(float) * (size_t)hkv * (size_t)max_pos * D;
-  const size_t wb = sizeof(float) * D, rb = sizeof(float) * D / 2;
+  const size_t wb = sizeof(float) * D, rb = sizeof(float) * (size_t)max_pos * D / 2;
   // written: the caches, o, osum and the workspace; they overlap nothing
   const void *outs[5] = {kcache, vcache, o, osum, ws};
   const size_t outb[5] = {cb, cb, qb, sizeof(float) * (size_t)hq * 2, need};
-  const void *ins[8] = {q, g, k, v, wq, wk, rope_cos, rope_sin};
-  const size_t inb[8] = {qb, qb, kb, kb, wb, wb, rb, rb};
+  const void *ins[9] = {q, g, k, v, wq, wk, rope_cos, rope_sin, pos};
+  const size_t inb[9] = {qb, qb, kb, kb, wb, wb, rb, rb, sizeof(int32_t)};
   for (int i = 0; i < 5; ++i) {
     for (int m = i + 1; m < 5; ++m)
       if (overlap(outs[i], outb[i], outs[m], outb[m])) return Q4_EINVAL;
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < 9; ++m)
       if (overlap(outs[i], outb[i], ins[m], inb[m])) return Q4_EINVAL;
   }
   q4::AtqWs L;
@@ -481,8 +481,9 @@ int q4_atq(const float *q, const float *g, const float *k, const float *v, const
   a.zp = reinterpret_cast<float *>(w + L.zp);
   a.wp = reinterpret_cast<float *>(w + L.wp);
   a.cnt = reinterpret_cast<uint32_t *>(w + L.cnt);
+  a.pos = pos;
   a.eps = eps;
-  a.pos = pos; a.max_pos = max_pos; a.hq = hq; a.hkv = hkv;
+  a.max_pos = max_pos; a.hq = hq; a.hkv = hkv;
   return hip_status(q4::launch_atq(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -147,7 +147,7 @@ struct AtqArgs {
   const float *q, *g;    // [hq][128]
   const float *k, *v;    // [hkv][128]
   const float *wq, *wk;  // [128] norm weights
-  const float *cs, *sn;  // [64] rotation table of the position
+  const float *cs, *sn;  // [max_pos][64] rotation tables, row pos used
   float *kc, *vc;        // [hkv][max_pos][128] caches; row pos is written
   float *o;              // [hq][128]
   float *os;             // [hq][2] group sums of o
@@ -156,8 +156,9 @@ struct AtqArgs {
   float *zp;             // workspace: [hq][kAtqMaxChunks] chunk sums of weights
   float *wp;             // workspace: [hq][kAtqMaxChunks][128] chunk value sums
   uint32_t *cnt;         // workspace: [hkv] arrival counters
+  const int32_t *pos;    // [1] the token's position, read on the device
   float eps;
-  int32_t pos, max_pos, hq, hkv;
+  int32_t max_pos, hq, hkv;
 };
 // Byte offsets of the workspace arrays for hq query and hkv key/value heads.
 struct AtqWs {

@@ -1,0 +1,55 @@
+// Device-scope words for handing values between the workgroups of one
+// launch without fences: a 64-bit word holds a float's bits and a 32-bit
+// tag naming the call and stage that produced it, stored and loaded with
+// device-scope (agent) atomics, i.e. with the sc1 cache policy that writes
+// through to the memory side where device-scope loads read it.  A consumer
+// polls until the tag is the expected one: the wait and the data arrive in
+// the same load, and no cache write-back or invalidation is needed.  Every
+// wait is bounded by a number of wall-clock ticks; one that runs out sets an
+// error word that the other waits also give up on.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+__device__ __forceinline__ uint32_t load_word(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_word(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_tagged(uint64_t *p, float v, uint32_t tag) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Polls the N tagged words at p until each carries `tag`; their floats go to
+// v.  False when the wait ran out (the error word is then set) or another
+// wait did.
+template <int N>
+__device__ __forceinline__ bool poll_tagged(const uint64_t *p, uint32_t tag, float *v,
+                                            uint32_t *err, long long spin_ticks) {
+  const long long t0 = wall_clock64();
+  for (int it = 1;; ++it) {
+    bool ready = true;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const uint64_t w = __hip_atomic_load(p + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      v[k] = __uint_as_float((uint32_t)w);
+      ready &= (uint32_t)(w >> 32) == tag;
+    }
+    if (ready) return true;
+    if ((it & 63) == 0 && load_word(err) != 0) return false;
+    if (wall_clock64() - t0 > spin_ticks) {
+      store_word(err, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+}  // namespace q4

@@ -18,8 +18,8 @@ Also reported: the 24-layer decode chain (rmsq -> [gate;up] q4mv -> swq ->
 down q4mv + residual, then rmsq -> head q4mv -> argmax), captured once as a
 HIP graph, in ms per token over 200 tokens, for two engines: the fused
 per-stage kernels (2 per layer) and the persistent layer kernel (one launch
-for all layers); and the CPU oracle timed on the host's cores on the head
-workload.
+for all layers); the attention step at positions 204 and 4095 of a 4096
+cache; and the CPU oracle timed on the host's cores on the head workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -240,6 +240,64 @@ def run_chain(args, q4, torch, synth):
     }
 
 
+def atq_bytes(n: int, hq: int, hkv: int) -> int:
+    """Algorithmic bytes of one attention step over n positions: every key
+    and value row of the cache read once (the new key row is formed, not
+    read), q, gate, new k and v, the two norm weights and the position's
+    table row read, the new cache rows, o and its group sums written."""
+    row = 128 * 4
+    reads = row * ((n - 1) * hkv + n * hkv + 2 * hq + 2 * hkv + 2 + 1)
+    writes = row * (2 * hkv + hq) + 8 * hq
+    return reads + writes
+
+
+def run_atq(args, q4, torch, synth):
+    """The attention step (16 query heads, 4 key/value heads, cache of
+    4096 positions) at positions 204 and 4095: K launches back to back
+    between one pair of HIP events, each checked against the first
+    launch's bits."""
+    import numpy as np
+
+    out = {}
+    stream = torch.cuda.current_stream()
+    for pos in (204, 4095):
+        a = synth.atq_inputs(seed=args.seed, pos=pos, max_pos=4096)
+        t = {n: torch.from_numpy(np.ascontiguousarray(a[n])).cuda()
+             for n in ("q", "g", "k", "v", "wq", "wk", "cos_tab", "sin_tab", "kcache", "vcache")}
+        p = torch.tensor([pos], dtype=torch.int32, device="cuda")
+        o = torch.empty(16 * 128, device="cuda")
+        os_ = torch.empty(32, device="cuda")
+        ws = torch.empty(q4.q4_atq_ws_bytes(16, 4) // 4 + 64, device="cuda")
+
+        def call():
+            q4.q4_atq(t["q"], t["g"], t["k"], t["v"], t["wq"], t["wk"], float(a["eps"]),
+                      t["cos_tab"], t["sin_tab"], t["kcache"], t["vcache"], p, o, os_, ws,
+                      stream=stream)
+
+        call()
+        torch.cuda.synchronize()
+        first = o.cpu().numpy().view(np.uint32).copy()
+        for _ in range(args.warmup):
+            call()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            call()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) / args.steps * 1e3
+        nb = atq_bytes(pos + 1, 16, 4)
+        out["pos%d" % pos] = {
+            "us_per_call": round(us, 2), "algorithmic_bytes": nb,
+            "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+            "bits_stable": bool(np.array_equal(o.cpu().numpy().view(np.uint32), first)),
+        }
+        log("atq pos %d: %.2f us per call (%.1f GB/s)" % (pos, us, nb / (us * 1e-6) / 1e9))
+    out["config"] = "hq 16, hkv 4, head dim 128, float caches [4, 4096, 128], fixed order"
+    return out
+
+
 def chain_tok0(seed, synth):
     return synth.randint(seed, "ch.tok0", synth.VOCAB)
 
@@ -254,6 +312,7 @@ def main() -> int:
     ap.add_argument("--chain-tokens", type=int, default=200)
     ap.add_argument("--no-chain", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-atq", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
                          "kernel that scales the HBM byte counters)")
@@ -297,6 +356,7 @@ def main() -> int:
     chain = None
     if not args.no_chain:
         chain = run_chain(args, q4, torch, synth)
+    atq = None if args.no_atq else run_atq(args, q4, torch, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.seed)
     traffic = measured_traffic(qb)
     out = {
@@ -333,6 +393,7 @@ def main() -> int:
             "timing": "HIP events around %d back-to-back launches on the launch stream" % args.steps,
         },
         "decode_chain": chain,
+        "attention_step": atq,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

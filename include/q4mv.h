@@ -258,16 +258,21 @@ int q4_decode_layers_status(void *ws, void *stream);
  *   q, g    : device float[hq][128] query and gate; q 16-byte aligned.
  *   k, v    : device float[hkv][128] new key and value, 16-byte aligned.
  *   wq, wk  : device float[128] norm weights, 16-byte aligned.
- *   rope_cos, rope_sin : device float[64], the position's rotation table.
+ *   rope_cos, rope_sin : device float[max_pos][64], the rotation tables
+ *             of every position; row pos is read.
  *   kcache, vcache : device float[hkv][max_pos][128], 16-byte aligned; rows
  *             below pos are read, row pos is written, others untouched.
- *   pos     : 0 <= pos < max_pos <= Q4_ATQ_MAX_POS.
+ *   pos     : device int32[1], the token's position, read on the device (so
+ *             that a captured graph can be replayed token after token).  A
+ *             position outside [0, max_pos) writes no cache row and fills o
+ *             and osum with quiet NaNs.  max_pos <= Q4_ATQ_MAX_POS.
  *   hq, hkv : 1 <= hkv, hq % hkv == 0, hq / hkv <= 8, hq <= 128.
  *   o       : device float[hq][128]; osum: device float[hq][2].
  *   ws      : device workspace of q4_atq_ws_bytes(hq, hkv) bytes, 256-byte
  *             aligned, contents irrelevant.  Calls that overlap in time must
  *             not share it.
- * Two launches on `stream`; every output and the workspace must overlap no
+ * Two launches on `stream`, of max_pos/64 x hkv workgroups each (those
+ * past the position leave at once); every output and the workspace must overlap no
  * other argument.  Inputs are assumed finite (a NaN score makes the
  * position of the maximum, and so the output, unspecified).
  * q4_atq_ws_bytes returns 0 for head counts outside the limits above.
@@ -276,8 +281,8 @@ int q4_decode_layers_status(void *ws, void *stream);
 size_t q4_atq_ws_bytes(int32_t hq, int32_t hkv);
 int q4_atq(const float *q, const float *g, const float *k, const float *v, const float *wq,
            const float *wk, float eps, const float *rope_cos, const float *rope_sin,
-           float *kcache, float *vcache, int32_t pos, int32_t max_pos, int32_t hq, int32_t hkv,
-           float *o, float *osum, void *ws, size_t ws_bytes, void *stream);
+           float *kcache, float *vcache, const int32_t *pos, int32_t max_pos, int32_t hq,
+           int32_t hkv, float *o, float *osum, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Stage queue ([P2] Change: q4go encodes products into one open concurrent

@@ -254,11 +254,20 @@ def rope_table(pos: int, d: int = ATQ_D, base: float = ROPE_BASE):
     return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
 
 
+def rope_tables(max_pos: int, d: int = ATQ_D, base: float = ROPE_BASE):
+    """The rotation tables of positions 0 .. max_pos-1 as [max_pos, d/2]
+    arrays (row p is ``rope_table(p)``)."""
+    i = np.arange(d // 2, dtype=np.float64)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * np.power(base, -2.0 * i / d)[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 def atq_inputs(seed: int = DEFAULT_SEED, pos: int = 204, hq: int = ATQ_HQ, hkv: int = ATQ_HKV,
                max_pos: int = ATQ_MAX_POS) -> dict:
     """One decode token of the attention step at position ``pos``: q, gate
     (hq x 128) and k, v (hkv x 128) ~ N(0, 1); norm weights wq, wk ~
-    N(1, 0.1); the position's rotation table; key and value caches
+    N(1, 0.1); the position's rotation table (and the tables of every
+    position of the cache); key and value caches
     [hkv, max_pos, 128] whose rows below ``pos`` hold N(0, 1) values (the
     earlier tokens) and zeros above."""
     kc = np.zeros((hkv, max_pos, ATQ_D), np.float32)
@@ -267,6 +276,7 @@ def atq_inputs(seed: int = DEFAULT_SEED, pos: int = 204, hq: int = ATQ_HQ, hkv: 
         kc[:, :pos] = normal_f32(seed, "atq.kcache", (hkv, pos, ATQ_D), 0.0, 1.0)
         vc[:, :pos] = normal_f32(seed, "atq.vcache", (hkv, pos, ATQ_D), 0.0, 1.0)
     c, s = rope_table(pos)
+    ct, st = rope_tables(max_pos)
     return {
         "q": normal_f32(seed, "atq.q", (hq * ATQ_D,), 0.0, 1.0),
         "g": normal_f32(seed, "atq.g", (hq * ATQ_D,), 0.0, 1.0),
@@ -274,6 +284,7 @@ def atq_inputs(seed: int = DEFAULT_SEED, pos: int = 204, hq: int = ATQ_HQ, hkv: 
         "v": normal_f32(seed, "atq.v", (hkv * ATQ_D,), 0.0, 1.0),
         "wq": normal_f32(seed, "atq.wq", (ATQ_D,), 1.0, 0.1),
         "wk": normal_f32(seed, "atq.wk", (ATQ_D,), 1.0, 0.1),
-        "cos": c, "sin": s, "kcache": kc, "vcache": vc, "pos": pos,
+        "cos": c, "sin": s, "cos_tab": ct, "sin_tab": st,
+        "kcache": kc, "vcache": vc, "pos": pos,
         "eps": np.float32(EPS), "hq": hq, "hkv": hkv, "max_pos": max_pos,
     }

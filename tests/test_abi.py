@@ -199,20 +199,23 @@ def test_atq_argument_checks(L):
     H = 0x7F0100000000
     f = ctypes.c_float
     base = dict(q=A, g=B, k=C, v=C + 0x100000, wq=C + 0x200000, wk=C + 0x300000,
-                cs=C + 0x400000, sn=C + 0x500000, kc=D, vc=E, pos=204, max_pos=4096, hq=16,
+                cs=C + 0x400000, sn=C + 0x500000, kc=D, vc=E, pos=C + 0x600000, max_pos=4096, hq=16,
                 hkv=4, o=F, os=F + 0x100000, ws=H, wsb=wsb)
 
     def call(**kw):
         a = dict(base, **kw)
         p = ctypes.c_void_p
         return L.q4_atq(p(a["q"]), p(a["g"]), p(a["k"]), p(a["v"]), p(a["wq"]), p(a["wk"]),
-                        f(1e-6), p(a["cs"]), p(a["sn"]), p(a["kc"]), p(a["vc"]), a["pos"],
+                        f(1e-6), p(a["cs"]), p(a["sn"]), p(a["kc"]), p(a["vc"]), p(a["pos"]),
                         a["max_pos"], a["hq"], a["hkv"], p(a["o"]), p(a["os"]), p(a["ws"]),
                         ctypes.c_size_t(a["wsb"]), None)
 
-    assert call(pos=-1) == EINVAL
-    assert call(pos=4096) == EINVAL                 # pos == max_pos
-    assert call(max_pos=4097, pos=0) == EINVAL      # cache longer than the limit
+    assert call(pos=0) == EINVAL                    # no position
+    assert call(pos=C + 0x600002) == EINVAL         # position misaligned
+    assert call(max_pos=4097) == EINVAL             # cache longer than the limit
+    assert call(max_pos=0) == EINVAL
+    assert call(o=C + 0x600000) == EINVAL           # o over the position
+    assert call(o=C + 0x500000 + 4096 * 256 - 4) == EINVAL   # o over the end of the sin table
     assert call(hq=16, hkv=3) == EINVAL             # heads not in groups
     assert call(hq=32, hkv=2) == EINVAL             # 16 queries per key/value head
     assert call(q=0) == EINVAL

@@ -4,7 +4,8 @@ attention over key/value caches, bit for bit against the oracle's orc_atq
 span one to 64 chunks of 64 with ragged last chunks, head groupings from
 1 to 8 queries per key/value head, cache lengths that are not multiples of
 the chunk, a key row whose terms cancel only in the canonical order,
-consecutive tokens that grow the caches in place, and graph replays."""
+consecutive tokens that grow the caches in place, graph replays at
+positions read on the device, and positions outside the cache."""
 import numpy as np
 import pytest
 import torch
@@ -28,15 +29,20 @@ class Dev:
     def __init__(self, a):
         self.q, self.g, self.k, self.v = (dev(a[n]) for n in ("q", "g", "k", "v"))
         self.wq, self.wk = dev(a["wq"]), dev(a["wk"])
-        self.cs, self.sn = dev(a["cos"]), dev(a["sin"])
+        # the tables of every position; the token's row is the one in a
+        # (which a test may have replaced)
+        ct, st = a["cos_tab"].copy(), a["sin_tab"].copy()
+        ct[a["pos"]], st[a["pos"]] = a["cos"], a["sin"]
+        self.cs, self.sn = dev(ct), dev(st)
+        self.pos = torch.tensor([a["pos"]], dtype=torch.int32, device="cuda")
         self.kc, self.vc = dev(a["kcache"]), dev(a["vcache"])
         self.o = torch.full((a["hq"] * 128,), 7.0, device="cuda")
         self.os = torch.full((a["hq"] * 2,), 7.0, device="cuda")
         self.eps = float(a["eps"])
 
-    def run(self, q4, pos, ws, stream=None):
+    def run(self, q4, ws, stream=None):
         q4.q4_atq(self.q, self.g, self.k, self.v, self.wq, self.wk, self.eps, self.cs, self.sn,
-                  self.kc, self.vc, pos, self.o, self.os, ws, stream)
+                  self.kc, self.vc, self.pos, self.o, self.os, ws, stream)
 
 
 def oracle_run(a):
@@ -61,7 +67,7 @@ def test_atq_bit_exact_positions(pos):
     print("atq pos %d" % pos, flush=True)
     a = synth.atq_inputs(seed=100 + pos, pos=pos, max_pos=4096)
     d = Dev(a)
-    d.run(q4, pos, new_ws(q4, 16, 4))
+    d.run(q4, new_ws(q4, 16, 4))
     check(a, d, "pos %d" % pos)
 
 
@@ -71,7 +77,7 @@ def test_atq_head_groups(hq, hkv):
     print("atq hq %d hkv %d" % (hq, hkv), flush=True)
     a = synth.atq_inputs(seed=200 + hq, pos=300, hq=hq, hkv=hkv, max_pos=512)
     d = Dev(a)
-    d.run(q4, 300, new_ws(q4, hq, hkv))
+    d.run(q4, new_ws(q4, hq, hkv))
     check(a, d, "hq %d hkv %d" % (hq, hkv))
 
 
@@ -80,7 +86,7 @@ def test_atq_ragged_cache_length(pos):
     q4 = lib()
     a = synth.atq_inputs(seed=300 + pos, pos=pos, max_pos=100)
     d = Dev(a)
-    d.run(q4, pos, new_ws(q4, 16, 4))
+    d.run(q4, new_ws(q4, 16, 4))
     check(a, d, "max_pos 100 pos %d" % pos)
 
 
@@ -99,7 +105,7 @@ def test_atq_cancelling_key_row():
     row[0], row[64] = 2.0 ** 30, -(2.0 ** 30)
     a["kcache"][:, 0] = row
     d = Dev(a)
-    d.run(q4, 1, new_ws(q4, 4, 2))
+    d.run(q4, new_ws(q4, 4, 2))
     check(a, d, "cancelling key")
 
 
@@ -118,9 +124,8 @@ def test_atq_consecutive_tokens_grow_the_cache():
         for n in ("q", "g", "k", "v"):
             b[n] = t[n]
             getattr(d, n).copy_(dev(t[n]))
-        d.cs.copy_(dev(t["cos"]))
-        d.sn.copy_(dev(t["sin"]))
-        d.run(q4, pos, ws)
+        d.pos.fill_(pos)
+        d.run(q4, ws)
         o, os_ = oracle.atq(b["q"], b["g"], b["k"], b["v"], b["wq"], b["wk"], b["eps"], b["cos"],
                             b["sin"], kc, vc, pos)
         torch.cuda.synchronize()
@@ -131,11 +136,11 @@ def test_atq_consecutive_tokens_grow_the_cache():
 
 
 def test_atq_in_graph_replays():
-    """One captured q4_atq replayed with new inputs copied in between, with
+    """One captured q4_atq replayed at positions 204, 205 and 64 (the
+    position is read on the device), with new inputs copied in between, and
     eager work and host synchronisations between the replays."""
     q4 = lib()
-    pos = 204
-    a = synth.atq_inputs(seed=500, pos=pos, max_pos=512)
+    a = synth.atq_inputs(seed=500, pos=204, max_pos=512)
     d = Dev(a)
     ws = new_ws(q4, 16, 4)
     s = torch.cuda.Stream()
@@ -143,21 +148,38 @@ def test_atq_in_graph_replays():
     g = q4.Graph(s)
     g.begin()
     try:
-        d.run(q4, pos, ws, stream=s)
+        d.run(q4, ws, stream=s)
     finally:
         g.end()
-    for seed in (501, 502, 503):
+    for seed, pos in ((501, 204), (502, 205), (503, 64)):
         t = synth.atq_inputs(seed=seed, pos=pos, max_pos=512)
         for n in ("q", "g", "k", "v"):
             getattr(d, n).copy_(dev(t[n]))
         d.kc.copy_(dev(t["kcache"]))
         d.vc.copy_(dev(t["vcache"]))
+        d.pos.fill_(pos)
         torch.cuda.synchronize()
         g.launch(s)
         s.synchronize()
-        b = dict(a, **{n: t[n] for n in ("q", "g", "k", "v", "kcache", "vcache")})
-        check(b, d, "replay seed %d" % seed)
+        b = dict(a, pos=pos, cos=t["cos"], sin=t["sin"],
+                 **{n: t[n] for n in ("q", "g", "k", "v", "kcache", "vcache")})
+        check(b, d, "replay seed %d pos %d" % (seed, pos))
         # eager work between replays: the same step outside the graph
-        d.run(q4, pos, new_ws(q4, 16, 4))
+        d.run(q4, new_ws(q4, 16, 4))
         torch.cuda.synchronize()
     g.close()
+
+
+@pytest.mark.parametrize("pos", [-1, 100])
+def test_atq_position_outside_the_cache(pos):
+    """A position outside [0, max_pos): no cache row written, o and osum
+    NaN."""
+    q4 = lib()
+    a = synth.atq_inputs(seed=600, pos=50, max_pos=100)
+    d = Dev(a)
+    d.pos.fill_(pos)
+    d.run(q4, new_ws(q4, 16, 4))
+    torch.cuda.synchronize()
+    assert np.all(np.isnan(host(d.o))) and np.all(np.isnan(host(d.os)))
+    assert_bits_equal(host(d.kc).ravel(), a["kcache"].ravel(), "kcache untouched")
+    assert_bits_equal(host(d.vc).ravel(), a["vcache"].ravel(), "vcache untouched")

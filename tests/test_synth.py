@@ -51,3 +51,13 @@ def test_workload_shapes():
     assert w["head"]["q"].shape == (300, 16) and 0 <= w["tok0"] < 300
     h = synth.head_inputs(seed=1, rows=10, cols=2048)
     assert h["q"].shape == (10, 256) and h["z"].shape == (2048,)
+
+
+def test_rope_tables_rows_are_the_position_tables():
+    ct, st = synth.rope_tables(300)
+    assert ct.shape == (300, 64) and st.shape == (300, 64)
+    for p in (0, 1, 204, 299):
+        c, s = synth.rope_table(p)
+        assert np.array_equal(ct[p], c) and np.array_equal(st[p], s)
+    assert np.array_equal(ct[0], np.ones(64, np.float32))
+    assert np.array_equal(st[0], np.zeros(64, np.float32))
