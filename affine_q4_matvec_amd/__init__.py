@@ -78,6 +78,7 @@ _SIGS = {
     "q4_atq_ws_bytes": ([_i32, _i32], ctypes.c_size_t),
     "q4_atq": ([_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _i32,
                 _i32, _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+    "q4_atq_status": ([_vp, _i32, _i32, _vp], ctypes.c_int),
     "q4_queue_create": ([_vp, ctypes.c_int, ctypes.POINTER(_vp)], ctypes.c_int),
     "q4_queue_destroy": ([_vp], ctypes.c_int),
     "q4mv_queue": ([_vp, ctypes.POINTER(_Mat), _vp, _vp, _vp], ctypes.c_int),
@@ -354,7 +355,9 @@ def q4_atq(q: torch.Tensor, g: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     ``[hkv, max_pos, 128]`` caches and ``o`` (``hq * 128`` values) with its
     group sums ``osum`` (``hq * 2``).  ``rope_cos``/``rope_sin``: the
     ``[max_pos, 64]`` rotation tables.  ``ws``: ``q4_atq_ws_bytes(hq, hkv)``
-    bytes, 256-byte aligned (any fresh torch allocation is)."""
+    bytes, 256-byte aligned (any fresh torch allocation is), zero-filled
+    before its first use (e.g. ``torch.zeros``) and kept for calls of one
+    shape."""
     if kcache.dim() != 3 or kcache.shape[2] != ATQ_D or vcache.shape != kcache.shape:
         raise ValueError("caches must be [hkv, max_pos, 128]")
     hkv, max_pos = int(kcache.shape[0]), int(kcache.shape[1])
@@ -370,6 +373,13 @@ def q4_atq(q: torch.Tensor, g: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _dev(o, f, hq * ATQ_D, "o"), _dev(osum, f, hq * 2, "osum"),
         _dev(ws, ws.dtype, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
     return o
+
+
+def q4_atq_status(ws: torch.Tensor, hq: int, hkv: int, stream=None) -> int:
+    """Host wait; Q4_OK, or Q4_ETIMEOUT when a wait of q4_atq ran out (the
+    workspace is then cleared)."""
+    return int(_lib.q4_atq_status(_dev(ws, ws.dtype, None, "ws"), int(hq), int(hkv),
+                                  _stream(stream)))
 
 
 class Mailbox:

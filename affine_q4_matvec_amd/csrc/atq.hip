@@ -19,58 +19,80 @@
 // with T the canonical tree (the balanced tree over the next power of two
 // with -0 in the empty slots).  Compiled with -ffp-contract=off.
 //
-// The position is read from device memory (a captured graph replays the
-// same launches token after token), with the rotation table's row of that
-// position.
-//
-// Layout of the work (MI355X-first rather than one workgroup per query
-// head): the positions are cut into aligned chunks of 64, and a grid of
-// (chunks of the whole cache x key/value heads) workgroups runs twice; the
-// workgroups past the position leave at once.
-//   scores kernel:  each workgroup normalises and rotates the G queries of
-//     its head group (and, in the chunk holding pos, the new key, which it
-//     writes to the caches with the new value), reads each key row of its
-//     chunk once for all G queries, and writes the scores and each query's
-//     chunk maximum.
-//   weights kernel: each workgroup takes the largest score from the chunk
-//     maxima, forms its chunk's weights, the chunk's sum of weights and of
-//     weighted value rows (each value row read once for all G queries), and
-//     writes them; the last workgroup of the head group to arrive (a device
-//     counter, no waiting) adds up the chunks and applies the gate.
-// A chunk of 64 aligned positions is a subtree of the canonical tree over
-// the n positions, and the chunks' tree (64 slots, -0 in the unused ones)
-// is the rest of it: every sum has the bits of T over the n terms.
+// One launch of (spans of 256 positions of the whole cache) x (query
+// heads) workgroups of 1024 threads; the position is read from device
+// memory (a captured graph replays the same launch token after token), and
+// the workgroups past it leave at once.  Workgroup (c, h) works on query
+// head h over positions [256 c, 256 c + 256) (one workgroup per query head
+// rather than per head group: a group's work on one compute unit made the
+// arithmetic, not the loads, the bound; the G queries of a group read the
+// same key and value rows, the later ones from the caches):
+//   - every global load is issued first: its query, the new key and the
+//     norm weights, the position's table row, and the key and value rows of
+//     its span;
+//   - norms and rotations into LDS; in the workgroup holding pos the new
+//     key is formed (its own loads take the new rows from the inputs) and
+//     the group's first query head writes the new cache rows;
+//   - scores (16 lanes per position, DPP row sums), the span's largest
+//     score;
+//   - with more than one span, the span maxima are exchanged through tagged
+//     device-scope words and each workgroup takes the largest;
+//   - weights e and the span's sums T(e) and T(e V) (256 aligned positions:
+//     a subtree of the canonical tree; each thread sums 8 positions of 4
+//     value columns, the lanes 32 apart add neighbouring blocks, LDS the
+//     16 blocks of 16);
+//   - one span: the workgroup finishes o itself; more: the span sums are
+//     published as tagged words and workgroup (0, h) polls them all at
+//     once, adds them up in a 16-slot balanced tree (-0 in the unused
+//     slots, the rest of the canonical tree) and applies the gate.
+// At position 204 of a 4096 cache this is one busy workgroup per query
+// head and no exchange at all; at 4095, 16 per head.  The exchanges follow
+// the tagged-word protocol of tagged_device.h (no fences, no grid barrier):
+// every workgroup publishes its maximum before it waits for any, so the
+// waits of a head end once its (at most 16) workgroups are resident.
+// Each workgroup counts its calls in a word of its own, which gives the
+// call's tag.
 #include <math.h>
 
 #include "ops_device.h"
+#include "q4mv_device.h"
 #include "q4mv_internal.h"
+#include "tagged_device.h"
 
 #pragma clang fp contract(off)
 
 namespace q4 {
 namespace {
 
-using namespace ops;
+using ops::fixed_exp;
+using ops::rmsq_rho_from_ss;
+using ops::rmsq_value;
+using ops::tree8;
+using dev::dpp;
+using dev::kDppQuadXor1;
+using dev::kNegZero;
+using dev::kWave;
+using dev::segment_sum;
 
 constexpr int kD = kAtqD;
-constexpr int kC = kAtqChunk;
-constexpr int kMaxG = kAtqMaxGroup;
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+constexpr int kSpan = kAtqSpan;
+constexpr int kMaxSpans = kAtqMaxSpans;
+constexpr int kThreads = 1024;
 constexpr float kScale = 0x1.6a09e6p-4f;  // RN32(1 / sqrt(128))
+static_assert(kMaxSpans == 16, "two tree8 levels over the spans");
+static_assert(kSpan == 256, "4 passes of 64 positions; 32 blocks of 8");
 
-// Sum over the 16 lanes of an aligned 16-lane group, as the balanced tree
-// over the lanes' values in lane order (every lane gets it).
+// The balanced tree over the 16 lanes of an aligned 16-lane row, in lane
+// order, in every lane of the row (xor 1 by quad permutation, then xor 2
+// and the two mirrors).
 __device__ __forceinline__ float sum16(float s) {
-#pragma unroll
-  for (int m = 1; m < 16; m *= 2) s = s + __shfl_xor(s, m);
-  return s;
+  s = s + dpp<kDppQuadXor1>(s);
+  return segment_sum<16>(s);
 }
 
 __device__ __forceinline__ float sum64(float s) {
-#pragma unroll
-  for (int m = 1; m < kWave; m *= 2) s = s + __shfl_xor(s, m);
-  return s;
+  s = s + dpp<kDppQuadXor1>(s);
+  return segment_sum<64>(s);
 }
 
 __device__ __forceinline__ float max64(float s) {
@@ -86,285 +108,284 @@ __device__ __forceinline__ void load8(const float *p, float *v) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-__global__ __launch_bounds__(kThreads) void atq_scores_kernel(AtqArgs a) {
-  __shared__ float un[kMaxG + 1][kD];   // normed rows (queries, then the new key)
-  __shared__ float rot[kMaxG + 1][kD];  // rotated rows
-  __shared__ float wmax[kWaves][kMaxG];
-  const int t = threadIdx.x;
-  const int c = blockIdx.x;  // chunk of positions
-  const int j = blockIdx.y;  // key/value head
-  const int G = a.hq / a.hkv;
-  // the weights kernel's arrival counter of this head group starts at zero
-  if (c == 0 && t == 0) a.cnt[j] = 0u;
-  const int pos = *a.pos;
-  // outside the cache (the weights kernel then writes NaN) or past the
-  // position: nothing to do
-  if (pos < 0 || pos >= a.max_pos || c > pos / kC) return;
-  const int n = pos + 1;
-  const bool owns_pos = c == pos / kC;
-  const float *cs = a.cs + (size_t)pos * (kD / 2);
-  const float *sn = a.sn + (size_t)pos * (kD / 2);
+__device__ __forceinline__ float gate_value(float g) {
+  return (float)(1.0 / (1.0 + fixed_exp(-(double)g)));
+}
 
-  // 16 lanes per row, 8 values per lane: rows r < G are the queries of
-  // heads j*G + r; row G is the new key, in the workgroup owning pos only
-  const int r = t >> 4, l = t & 15;
-  const bool active = r < G || (r == G && owns_pos);
-  // every global load up front, so that their latencies overlap: this
-  // lane's slice of its row and norm weights, of the rotation table, and
-  // of the key rows of its four positions (16 positions per pass)
-  float xv[8], wv[8], ct[8], st[8];
-  float kv[kC / 16][8];
-  if (active) {
-    const float *x = r < G ? a.q + (size_t)(j * G + r) * kD : a.k + (size_t)j * kD;
-    const float *w = r < G ? a.wq : a.wk;
-    load8(x + 8 * l, xv);
-    load8(w + 8 * l, wv);
-    const int i0 = 8 * (l & 7);
+// The tagged span sums 1 .. nspan-1 of one output column (wp: stride
+// 128 words) and of the weights (zp), all loaded in each round; slots from
+// nspan on are -0.  False when the wait ran out or another wait did.
+__device__ __forceinline__ bool poll_spans(const uint64_t *wp, const uint64_t *zp, int nspan,
+                                           uint32_t tag, float *ws, float *zs, uint32_t *err,
+                                           long long spin_ticks) {
+  const long long t0 = wall_clock64();
+  for (int it = 1;; ++it) {
+    bool ready = true;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      ct[k] = cs[i0 + k];
-      st[k] = sn[i0 + k];
+    for (int sp = 1; sp < kMaxSpans; ++sp) {
+      ws[sp] = kNegZero;
+      zs[sp] = kNegZero;
+      if (sp < nspan) {
+        const uint64_t w = __hip_atomic_load(wp + (size_t)sp * kD, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t z = __hip_atomic_load(zp + sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ws[sp] = __uint_as_float((uint32_t)w);
+        zs[sp] = __uint_as_float((uint32_t)z);
+        ready &= (uint32_t)(w >> 32) == tag && (uint32_t)(z >> 32) == tag;
+      }
     }
+    if (ready) return true;
+    if ((it & 63) == 0 && load_word(err) != 0) return false;
+    if (wall_clock64() - t0 > spin_ticks) {
+      store_word(err, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
   }
+}
+
+struct Lds {
+  float un[2][kD];     // normed rows: the query, then the new key
+  float rot[2][kD];    // rotated rows
+  float s[kSpan];      // scores of the span
+  float e[kSpan];      // weights of the span
+  float part[16][kD];  // value sums over 16 positions
+  float wsum[4];       // weight sums over 64 positions
+  float m;             // largest score
+  float z;             // the span's weight sum
+};
+
+__global__ __launch_bounds__(kThreads) void atq_kernel(AtqArgs a) {
+  __shared__ Lds S;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = dev::wave_index();
+  const int c = blockIdx.x, h = blockIdx.y;
+  const int G = a.hq / a.hkv, j = h / G;
+  uint32_t *err = a.ctl + kAtqErrorWord;
+  uint32_t *mine = a.ctl + h * kMaxSpans + c;
+  // the control words and the position, loaded together
+  const uint32_t e0 = load_word(err);
+  const uint32_t tag = load_word(mine) + 1;
+  const int pos = *a.pos;
+  if (__syncthreads_or(e0 != 0)) return;
+  const bool valid = pos >= 0 && pos < a.max_pos;
+  const int nspan = valid ? pos / kSpan + 1 : 0;
+  if (c >= nspan) {
+    if (!valid && c == 0) {  // no such cache row: o and osum are NaN
+      if (t < kD) a.o[(size_t)h * kD + t] = NAN;
+      if (t < 2) a.os[(size_t)h * 2 + t] = NAN;
+    }
+    __syncthreads();
+    if (t == 0) store_word(mine, tag);
+    return;
+  }
+  const int n = pos + 1;
+  const int base = c * kSpan;
+  const bool owns_pos = pos / kSpan == c;
+  // the new cache rows are written by the first query head of the group
+  const bool writes_rows = owns_pos && h % G == 0;
+
+  // ---- every global load first -------------------------------------------
+  // row 0: the query of head h; row 1: the new key and value (workgroup
+  // holding pos only); 16 lanes per row, 8 values per lane
+  const int r = t >> 4, l = t & 15;
+  const bool nrow = r == 0 || (r == 1 && owns_pos);
+  float xv[8], wv[8], ct[8], st[8], nv[8];
+  if (nrow) {
+    const float *x = r == 0 ? a.q + (size_t)h * kD : a.k + (size_t)j * kD;
+    load8(x + 8 * l, xv);
+    load8((r == 0 ? a.wq : a.wk) + 8 * l, wv);
+    load8(a.cs + (size_t)pos * (kD / 2) + 8 * (l & 7), ct);
+    load8(a.sn + (size_t)pos * (kD / 2) + 8 * (l & 7), st);
+    if (r == 1 && writes_rows) load8(a.v + (size_t)j * kD + 8 * l, nv);
+  }
+  // key rows: position base + 64 pass + r (r < 64), dims [8 l, 8 l + 8)
+  float kv[kSpan / 64][8];
 #pragma unroll
-  for (int pass = 0; pass < kC / 16; ++pass) {
-    const int tp = c * kC + 16 * pass + r;
+  for (int pass = 0; pass < kSpan / 64; ++pass) {
+    const int tp = base + 64 * pass + r;
     if (tp < n && tp != pos) load8(a.kc + ((size_t)j * a.max_pos + tp) * kD + 8 * l, kv[pass]);
   }
-  if (active) {
+  // value columns [4 cq, 4 cq + 4) of positions pb .. pb + 7 (the new row
+  // from v)
+  const int cq = t & 31, pg = t >> 5;
+  const int pb = base + 8 * pg;
+  float4 vv[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int p = pb + k;
+    vv[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (p < n)
+      vv[k] = reinterpret_cast<const float4 *>(
+          p == pos ? a.v + (size_t)j * kD : a.vc + ((size_t)j * a.max_pos + p) * kD)[cq];
+  }
+  // the gate of output t (t < 128), needed by workgroup 0
+  const bool out_t = t < kD;
+  const float gv = c == 0 && out_t ? a.g[(size_t)h * kD + t] : 0.0f;
+
+  // ---- norms and rotations -------------------------------------------------
+  if (nrow) {
     float sq[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) sq[k] = xv[k] * xv[k];
     const float rho = rmsq_rho_from_ss(sum16(tree8(sq)), kD, a.eps);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) un[r][8 * l + k] = rmsq_value(xv[k], rho, wv[k]);
+    for (int k = 0; k < 8; ++k) S.un[r][8 * l + k] = rmsq_value(xv[k], rho, wv[k]);
   }
   __syncthreads();
-  if (active) {
+  if (nrow) {
     float rv[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int i = 8 * l + k;
-      if (l < 8) {  // i < 64: the first of the pair
-        const float A = un[r][i], B = un[r][i + kD / 2];
+      const int d = 8 * l + k;
+      if (l < 8) {  // d < 64: the first of the pair
+        const float A = S.un[r][d], B = S.un[r][d + kD / 2];
         const float ac = A * ct[k], bs = B * st[k];
         rv[k] = ac - bs;
       } else {
-        const int i2 = i - kD / 2;
-        const float A = un[r][i2], B = un[r][i];
+        const float A = S.un[r][d - kD / 2], B = S.un[r][d];
         const float as = A * st[k], bc = B * ct[k];
         rv[k] = as + bc;
       }
-      rot[r][i] = rv[k];
+      S.rot[r][d] = rv[k];
     }
-    if (r == G) {
-      float *kd = a.kc + ((size_t)j * a.max_pos + pos) * kD + 8 * l;
-      float *vd = a.vc + ((size_t)j * a.max_pos + pos) * kD + 8 * l;
-      const float *vs = a.v + (size_t)j * kD + 8 * l;
-      reinterpret_cast<float4 *>(kd)[0] = make_float4(rv[0], rv[1], rv[2], rv[3]);
-      reinterpret_cast<float4 *>(kd)[1] = make_float4(rv[4], rv[5], rv[6], rv[7]);
-      reinterpret_cast<float4 *>(vd)[0] = reinterpret_cast<const float4 *>(vs)[0];
-      reinterpret_cast<float4 *>(vd)[1] = reinterpret_cast<const float4 *>(vs)[1];
+    if (r == 1 && writes_rows) {  // the new cache rows
+      float4 *kd = reinterpret_cast<float4 *>(a.kc + ((size_t)j * a.max_pos + pos) * kD + 8 * l);
+      float4 *vd = reinterpret_cast<float4 *>(a.vc + ((size_t)j * a.max_pos + pos) * kD + 8 * l);
+      kd[0] = make_float4(rv[0], rv[1], rv[2], rv[3]);
+      kd[1] = make_float4(rv[4], rv[5], rv[6], rv[7]);
+      vd[0] = make_float4(nv[0], nv[1], nv[2], nv[3]);
+      vd[1] = make_float4(nv[4], nv[5], nv[6], nv[7]);
     }
   }
   __syncthreads();
 
-  // scores: 16 lanes per position, 16 positions per pass, 4 passes
-  float qv[kMaxG][8];
-  float mx[kMaxG];
+  // ---- scores ---------------------------------------------------------------
+  float qv[8];
 #pragma unroll
-  for (int gi = 0; gi < kMaxG; ++gi) {
-    mx[gi] = -INFINITY;
-    if (gi < G) {
+  for (int k = 0; k < 8; ++k) qv[k] = S.rot[0][8 * l + k];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) qv[gi][k] = rot[gi][8 * l + k];
-    }
-  }
-#pragma unroll
-  for (int pass = 0; pass < kC / 16; ++pass) {
-    const int tp = c * kC + 16 * pass + r;
+  for (int pass = 0; pass < kSpan / 64; ++pass) {
+    const int tp = base + 64 * pass + r;
     if (tp < n) {  // uniform over the 16 lanes of the position
       if (tp == pos) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) kv[pass][k] = rot[G][8 * l + k];
+        for (int k = 0; k < 8; ++k) kv[pass][k] = S.rot[1][8 * l + k];
       }
+      float pr[8];
 #pragma unroll
-      for (int gi = 0; gi < kMaxG; ++gi) {
-        if (gi < G) {
-          float pr[8];
-#pragma unroll
-          for (int k = 0; k < 8; ++k) pr[k] = qv[gi][k] * kv[pass][k];
-          const float s = sum16(tree8(pr)) * kScale;
-          if (l == gi) a.sc[(size_t)(j * G + gi) * kAtqMaxPos + tp] = s;
-          mx[gi] = fmaxf(mx[gi], s);
-        }
-      }
-    }
-  }
-  const int lane = t & (kWave - 1), wave = t / kWave;
-#pragma unroll
-  for (int gi = 0; gi < kMaxG; ++gi) {
-    if (gi < G) {
-      float m = fmaxf(mx[gi], __shfl_xor(mx[gi], 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      if (lane == 0) wmax[wave][gi] = m;
+      for (int k = 0; k < 8; ++k) pr[k] = qv[k] * kv[pass][k];
+      const float sc = sum16(tree8(pr)) * kScale;
+      if (l == 0) S.s[64 * pass + r] = sc;
     }
   }
   __syncthreads();
-  if (t < G) {
-    float m = wmax[0][t];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, wmax[w][t]);
-    a.cmax[(size_t)(j * G + t) * kAtqMaxChunks + c] = m;
-  }
-}
 
-__global__ __launch_bounds__(kThreads) void atq_weights_kernel(AtqArgs a) {
-  __shared__ float eS[kMaxG][kC];
-  __shared__ float part[kMaxG][kD];
-  __shared__ float zS[kMaxG];
-  __shared__ int last;
-  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
-  const int c = blockIdx.x, j = blockIdx.y;
-  const int G = a.hq / a.hkv;
-  const int pos = *a.pos;
-  if (pos < 0 || pos >= a.max_pos) {  // no such cache row: o and osum are NaN
-    if (c == 0) {
-      for (int idx = t; idx < G * kD; idx += kThreads) a.o[(size_t)j * G * kD + idx] = NAN;
-      if (t < 2 * G) a.os[(size_t)j * G * 2 + t] = NAN;
+  // ---- the largest score (wave 0) -------------------------------------------
+  bool ok = true;
+  if (wave == 0) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kSpan / 64; ++k)
+      if (base + 64 * k + lane < n) m = fmaxf(m, S.s[64 * k + lane]);
+    m = max64(m);
+    if (nspan > 1) {
+      uint64_t *mx = a.mx + (size_t)h * kMaxSpans;
+      if (lane == 0) store_tagged(mx + c, m, tag);
+      float o = -INFINITY;
+      if (lane < nspan) ok = poll_tagged<1>(mx + lane, tag, &o, err, a.spin_ticks);
+      m = max64(o);
     }
-    return;
+    if (lane == 0) S.m = m;
   }
-  if (c > pos / kC) return;
-  const int n = pos + 1;
-  const int nchunk = pos / kC + 1;
-  const int i = t & (kD - 1), half = t / kD;
-  const int p0 = c * kC + 32 * half;
-  const int tp = c * kC + lane;
+  if (__syncthreads_or(!ok)) return;
 
-  // every global load up front: this thread's column of 32 value rows
-  // (thread = column i, half of the chunk), and per query of this wave
-  // the chunk maxima and the score of position tp
-  float vv[32];
-#pragma unroll
-  for (int k = 0; k < 32; ++k)
-    vv[k] = p0 + k < n ? a.vc[((size_t)j * a.max_pos + p0 + k) * kD + i] : 0.0f;
-  constexpr int kPerWave = kMaxG / kWaves;
-  float cm[kPerWave], sv[kPerWave];
-#pragma unroll
-  for (int u = 0; u < kPerWave; ++u) {
-    const int gi = wave + kWaves * u;
-    cm[u] = -INFINITY;
-    sv[u] = 0.0f;
-    if (gi < G) {
-      if (lane < nchunk) cm[u] = a.cmax[(size_t)(j * G + gi) * kAtqMaxChunks + lane];
-      if (tp < n) sv[u] = a.sc[(size_t)(j * G + gi) * kAtqMaxPos + tp];
+  // ---- weights e and their sums over 64 positions (waves 0..3) --------------
+  if (t < kSpan) {
+    float e = kNegZero;
+    if (base + t < n) {
+      const float d = S.s[t] - S.m;
+      e = (float)fixed_exp((double)d);
     }
-  }
-  // the chunk's weights e (lane = position) from the largest score, and
-  // their sum
-#pragma unroll
-  for (int u = 0; u < kPerWave; ++u) {
-    const int gi = wave + kWaves * u;
-    if (gi < G) {  // uniform per wave
-      const float m = max64(cm[u]);
-      float e = kNegZero;
-      if (tp < n) {
-        const float d = sv[u] - m;
-        e = (float)fixed_exp((double)d);
-      }
-      eS[gi][lane] = e;
-      const float z = sum64(e);
-      if (lane == 0) a.zp[(size_t)(j * G + gi) * kAtqMaxChunks + c] = z;
-    }
+    S.e[t] = e;
+    const float z = sum64(e);
+    if (lane == 0) S.wsum[wave] = z;
   }
   __syncthreads();
-  // the chunk's weighted value sums
-  float own[kMaxG];
+  // the span's weighted value sums: 8 positions of 4 columns per thread, then
+  // the lanes 32 apart (blocks 2w and 2w + 1 of wave w) give 16 positions
+  {
+    float w4[4];
 #pragma unroll
-  for (int gi = 0; gi < kMaxG; ++gi) {
-    own[gi] = 0.0f;
-    if (gi < G) {
-      float pr[32];
-#pragma unroll
-      for (int k = 0; k < 32; ++k) pr[k] = p0 + k < n ? eS[gi][32 * half + k] * vv[k] : kNegZero;
-      own[gi] = (tree8(pr) + tree8(pr + 8)) + (tree8(pr + 16) + tree8(pr + 24));
-      if (half == 1) part[gi][i] = own[gi];
-    }
-  }
-  __syncthreads();
-  if (half == 0) {
-#pragma unroll
-    for (int gi = 0; gi < kMaxG; ++gi)
-      if (gi < G)
-        a.wp[((size_t)(j * G + gi) * kAtqMaxChunks + c) * kD + i] = own[gi] + part[gi][i];
-  }
-
-  // the last workgroup of the head group to arrive adds up the chunks
-  __threadfence();
-  __syncthreads();
-  if (t == 0)
-    last = __hip_atomic_fetch_add(a.cnt + j, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-           (uint32_t)(nchunk - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  for (int gi = wave; gi < G; gi += kWaves) {
-    const float z = lane < nchunk ? a.zp[(size_t)(j * G + gi) * kAtqMaxChunks + lane] : kNegZero;
-    const float zz = sum64(z);
-    if (lane == 0) zS[gi] = zz;
-  }
-  __syncthreads();
-  for (int idx = t; idx < G * kD; idx += kThreads) {  // uniform per wave
-    const int gi = idx / kD, ii = idx & (kD - 1);
-    const size_t hrow = (size_t)(j * G + gi);
-    const float *wp = a.wp + hrow * kAtqMaxChunks * kD + ii;
-    float blk[8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      float v8[8];
+    for (int col = 0; col < 4; ++col) {
+      float pr[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int cc = 8 * b + k;
-        v8[k] = cc < nchunk ? wp[(size_t)cc * kD] : kNegZero;
+        const float vk = col == 0 ? vv[k].x : col == 1 ? vv[k].y : col == 2 ? vv[k].z : vv[k].w;
+        pr[k] = pb + k < n ? S.e[8 * pg + k] * vk : kNegZero;
       }
-      blk[b] = tree8(v8);
+      const float b8 = tree8(pr);
+      w4[col] = b8 + __shfl_xor(b8, 32);
     }
-    const float w = tree8(blk) / zS[gi];
-    const double gv = (double)a.g[hrow * kD + ii];
-    const float sig = (float)(1.0 / (1.0 + fixed_exp(-gv)));
-    const float ov = w * sig;
-    a.o[hrow * kD + ii] = ov;
-    const float s = sum64(ov);
-    if (lane == 0) a.os[hrow * 2 + ii / 64] = s;
+    if (lane < 32)
+      *reinterpret_cast<float4 *>(&S.part[wave][4 * cq]) = make_float4(w4[0], w4[1], w4[2], w4[3]);
   }
+  if (t == 0) S.z = (S.wsum[0] + S.wsum[1]) + (S.wsum[2] + S.wsum[3]);
+  __syncthreads();
+
+  // ---- the span's sums; o (workgroup 0) --------------------------------------
+  if (out_t) {
+    const int i = t;
+    float pq[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) pq[k] = S.part[k][i];
+    float w = tree8(pq) + tree8(pq + 8), z = S.z;
+    if (nspan > 1) {
+      uint64_t *wp = a.wp + (size_t)h * kMaxSpans * kD + i;
+      uint64_t *zp = a.zp + (size_t)h * kMaxSpans;
+      if (c > 0) {
+        store_tagged(wp + (size_t)c * kD, w, tag);
+        if (i == 0) store_tagged(zp + c, z, tag);
+      } else {
+        // every span's sums, polled together
+        float ws[kMaxSpans], zs[kMaxSpans];
+        ok = poll_spans(wp, zp, nspan, tag, ws, zs, err, a.spin_ticks);
+        ws[0] = w;
+        zs[0] = z;
+        w = tree8(ws) + tree8(ws + 8);
+        z = tree8(zs) + tree8(zs + 8);
+      }
+    }
+    if (c == 0 && ok) {
+      const float ov = (w / z) * gate_value(gv);
+      a.o[(size_t)h * kD + i] = ov;
+      const float s = sum64(ov);  // the wave holds 64 consecutive values
+      if (lane == 0) a.os[(size_t)h * 2 + i / 64] = s;
+    }
+  }
+  if (__syncthreads_or(!ok)) return;
+  if (t == 0) store_word(mine, tag);
 }
 
 }  // namespace
 
 void atq_ws_layout(int32_t hq, int32_t hkv, AtqWs *out) {
+  (void)hkv;
   size_t at = 0;
   auto take = [&at](size_t bytes) {
     const size_t p = at;
     at += (bytes + 255) & ~(size_t)255;
     return p;
   };
-  out->sc = take(sizeof(float) * (size_t)hq * kAtqMaxPos);
-  out->cmax = take(sizeof(float) * (size_t)hq * kAtqMaxChunks);
-  out->zp = take(sizeof(float) * (size_t)hq * kAtqMaxChunks);
-  out->wp = take(sizeof(float) * (size_t)hq * kAtqMaxChunks * kAtqD);
-  out->cnt = take(sizeof(uint32_t) * (size_t)hkv);
+  out->mx = take(sizeof(uint64_t) * (size_t)hq * kAtqMaxSpans);
+  out->zp = take(sizeof(uint64_t) * (size_t)hq * kAtqMaxSpans);
+  out->wp = take(sizeof(uint64_t) * (size_t)hq * kAtqMaxSpans * kAtqD);
+  out->ctl = take(sizeof(uint32_t) * (size_t)(kAtqErrorWord + 32));
   out->bytes = at;
 }
 
 hipError_t launch_atq(const AtqArgs &a, hipStream_t st) {
-  // one workgroup per chunk of the whole cache: the position is read on the
-  // device, and the workgroups past it leave at once
-  const dim3 grid((a.max_pos + kAtqChunk - 1) / kAtqChunk, a.hkv);
-  hipLaunchKernelGGL(atq_scores_kernel, grid, dim3(kThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(atq_weights_kernel, grid, dim3(kThreads), 0, st, a);
+  const dim3 grid((a.max_pos + kAtqSpan - 1) / kAtqSpan, a.hq);
+  hipLaunchKernelGGL(atq_kernel, grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -80,6 +80,42 @@ int check_norm_inputs(const float *h, const float *wn) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_EHIP; }
 
+// Bound of one device-side wait (the persistent layers kernel, the
+// attention step's exchanges): Q4_DECODE_TIMEOUT_MS (default 2000, at most
+// 60000) of the device's constant wall clock; a negative value makes every
+// wait that does not find its data at the first look run out (a test of
+// that path).
+int wait_ticks(long long *ticks) {
+  long long ms = 2000;
+  if (const char *v = getenv("Q4_DECODE_TIMEOUT_MS")) ms = atoll(v);
+  if (ms > 60000) ms = 60000;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return Q4_EHIP;
+  *ticks = ms < 0 ? -1 : ms * (long long)(khz > 0 ? khz : 100000);
+  return Q4_OK;
+}
+
+// Host wait on `stream`, then the error word at byte offset err_off of a
+// workspace: Q4_OK, or Q4_ETIMEOUT after clearing the first `clear` bytes
+// of the workspace (a wait ran out and left its words in an unknown state).
+int ws_status(void *ws, size_t err_off, size_t clear, void *stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return Q4_EHIP;
+  if (cs != hipStreamCaptureStatusNone) return Q4_ESTATE;
+  if (hipStreamSynchronize(st) != hipSuccess) return Q4_EHIP;
+  uint32_t err = 0;
+  if (hipMemcpy(&err, static_cast<const char *>(ws) + err_off, sizeof(err),
+                hipMemcpyDeviceToHost) != hipSuccess)
+    return Q4_EHIP;
+  if (err == 0) return Q4_OK;
+  if (hipMemsetAsync(ws, 0, clear, st) != hipSuccess || hipStreamSynchronize(st) != hipSuccess)
+    return Q4_EHIP;
+  return Q4_ETIMEOUT;
+}
+
 // Launches a list of products of one shape as grouped kernels (up to
 // kMaxGroup products per launch).  When the products of a launch together
 // want more workgroups than fit on the device at once, each one's share is
@@ -392,41 +428,15 @@ int q4_decode_layers(const q4_mat *emb, const int32_t *tok, const q4_mlp_layer *
   a.mq = reinterpret_cast<uint64_t *>(w + q4::kDecodeMqOffset);
   a.ctl = reinterpret_cast<uint32_t *>(w + q4::kDecodeCtlOffset);
   a.eps = eps;
-  // bound of one wait: Q4_DECODE_TIMEOUT_MS (default 2000, at most 60000)
-  // of the device's constant wall clock; a negative value makes every wait
-  // that does not find its data at the first look run out (a test of that
-  // path)
-  long long ms = 2000;
-  if (const char *v = getenv("Q4_DECODE_TIMEOUT_MS")) ms = atoll(v);
-  if (ms > 60000) ms = 60000;
-  int dev = 0, khz = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
-    return Q4_EHIP;
-  a.spin_ticks = ms < 0 ? -1 : ms * (long long)(khz > 0 ? khz : 100000);
+  if (wait_ticks(&a.spin_ticks) != Q4_OK) return Q4_EHIP;
   if (q4::decode_layers_grid(mode, inter) < 1) return Q4_EINVAL;  // too few compute units
   return hip_status(q4::launch_decode_layers(a, mode, static_cast<hipStream_t>(stream)));
 }
 
 int q4_decode_layers_status(void *ws, void *stream) {
   if (!ws || !aligned(ws, 16)) return Q4_EINVAL;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return Q4_EHIP;
-  if (cs != hipStreamCaptureStatusNone) return Q4_ESTATE;
-  if (hipStreamSynchronize(st) != hipSuccess) return Q4_EHIP;
-  uint32_t err = 0;
-  const char *ctl = static_cast<const char *>(ws) + q4::kDecodeCtlOffset;
-  if (hipMemcpy(&err, ctl + 4 * q4::kDecodeErrorWord, sizeof(err), hipMemcpyDeviceToHost) !=
-      hipSuccess)
-    return Q4_EHIP;
-  if (err == 0) return Q4_OK;
-  // the tagged words and the call counter are left in an unknown state:
-  // clear the whole workspace for reuse
-  if (hipMemsetAsync(ws, 0, q4::kDecodeWsBytes, st) != hipSuccess ||
-      hipStreamSynchronize(st) != hipSuccess)
-    return Q4_EHIP;
-  return Q4_ETIMEOUT;
+  return ws_status(ws, q4::kDecodeCtlOffset + 4 * (size_t)q4::kDecodeErrorWord,
+                   q4::kDecodeWsBytes, stream);
 }
 
 size_t q4_atq_ws_bytes(int32_t hq, int32_t hkv) {
@@ -476,15 +486,23 @@ int q4_atq(const float *q, const float *g, const float *k, const float *v, const
   a.q = q; a.g = g; a.k = k; a.v = v; a.wq = wq; a.wk = wk;
   a.cs = rope_cos; a.sn = rope_sin;
   a.kc = kcache; a.vc = vcache; a.o = o; a.os = osum;
-  a.sc = reinterpret_cast<float *>(w + L.sc);
-  a.cmax = reinterpret_cast<float *>(w + L.cmax);
-  a.zp = reinterpret_cast<float *>(w + L.zp);
-  a.wp = reinterpret_cast<float *>(w + L.wp);
-  a.cnt = reinterpret_cast<uint32_t *>(w + L.cnt);
+  a.mx = reinterpret_cast<uint64_t *>(w + L.mx);
+  a.zp = reinterpret_cast<uint64_t *>(w + L.zp);
+  a.wp = reinterpret_cast<uint64_t *>(w + L.wp);
+  a.ctl = reinterpret_cast<uint32_t *>(w + L.ctl);
+  if (wait_ticks(&a.spin_ticks) != Q4_OK) return Q4_EHIP;
   a.pos = pos;
   a.eps = eps;
   a.max_pos = max_pos; a.hq = hq; a.hkv = hkv;
   return hip_status(q4::launch_atq(a, static_cast<hipStream_t>(stream)));
+}
+
+int q4_atq_status(void *ws, int32_t hq, int32_t hkv, void *stream) {
+  const size_t need = q4_atq_ws_bytes(hq, hkv);
+  if (need == 0 || !ws || !aligned(ws, 256)) return Q4_EINVAL;
+  q4::AtqWs L;
+  q4::atq_ws_layout(hq, hkv, &L);
+  return ws_status(ws, L.ctl + 4 * (size_t)q4::kAtqErrorWord, need, stream);
 }
 
 int q4_queue_create(void *stream, int mode, q4_queue **out) {

@@ -136,13 +136,16 @@ int32_t decode_layers_grid(int mode, int32_t inter);
 hipError_t launch_decode_layers(const DecodeArgs &a, int mode, hipStream_t st);
 
 // Gated attention of one decode token (atq.hip).  Caches are float
-// [hkv][max_pos][128]; positions are worked on in aligned chunks of 64.
+// [hkv][max_pos][128]; positions are worked on in aligned spans of 256.
 constexpr int kAtqD = 128;
-constexpr int kAtqChunk = 64;
+constexpr int kAtqSpan = 256;
 constexpr int kAtqMaxPos = 4096;
-constexpr int kAtqMaxChunks = kAtqMaxPos / kAtqChunk;
+constexpr int kAtqMaxSpans = kAtqMaxPos / kAtqSpan;
 constexpr int kAtqMaxGroup = 8;   // query heads per key/value head
 constexpr int kAtqMaxHeads = 128; // query heads
+// Control words: one call counter per workgroup ([hkv][kAtqMaxSpans]), then
+// the error word on a 128-byte line of its own.
+constexpr int kAtqErrorWord = kAtqMaxHeads * kAtqMaxSpans + 32;
 struct AtqArgs {
   const float *q, *g;    // [hq][128]
   const float *k, *v;    // [hkv][128]
@@ -151,18 +154,18 @@ struct AtqArgs {
   float *kc, *vc;        // [hkv][max_pos][128] caches; row pos is written
   float *o;              // [hq][128]
   float *os;             // [hq][2] group sums of o
-  float *sc;             // workspace: [hq][kAtqMaxPos] scores
-  float *cmax;           // workspace: [hq][kAtqMaxChunks] chunk maxima
-  float *zp;             // workspace: [hq][kAtqMaxChunks] chunk sums of weights
-  float *wp;             // workspace: [hq][kAtqMaxChunks][128] chunk value sums
-  uint32_t *cnt;         // workspace: [hkv] arrival counters
+  uint64_t *mx;          // workspace: [hq][kAtqMaxSpans] tagged span maxima
+  uint64_t *zp;          // workspace: [hq][kAtqMaxSpans] tagged span weight sums
+  uint64_t *wp;          // workspace: [hq][kAtqMaxSpans][128] tagged span value sums
+  uint32_t *ctl;         // workspace: call counters and the error word
   const int32_t *pos;    // [1] the token's position, read on the device
   float eps;
   int32_t max_pos, hq, hkv;
+  long long spin_ticks;  // bound of one wait in wall-clock ticks
 };
-// Byte offsets of the workspace arrays for hq query and hkv key/value heads.
+// Byte offsets of the workspace arrays for hq query heads.
 struct AtqWs {
-  size_t sc, cmax, zp, wp, cnt, bytes;
+  size_t mx, zp, wp, ctl, bytes;
 };
 void atq_ws_layout(int32_t hq, int32_t hkv, AtqWs *out);
 hipError_t launch_atq(const AtqArgs &a, hipStream_t st);

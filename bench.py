@@ -267,7 +267,7 @@ def run_atq(args, q4, torch, synth):
         p = torch.tensor([pos], dtype=torch.int32, device="cuda")
         o = torch.empty(16 * 128, device="cuda")
         os_ = torch.empty(32, device="cuda")
-        ws = torch.empty(q4.q4_atq_ws_bytes(16, 4) // 4 + 64, device="cuda")
+        ws = torch.zeros(q4.q4_atq_ws_bytes(16, 4) // 4 + 64, device="cuda")
 
         def call():
             q4.q4_atq(t["q"], t["g"], t["k"], t["v"], t["wq"], t["wk"], float(a["eps"]),

@@ -269,13 +269,20 @@ int q4_decode_layers_status(void *ws, void *stream);
  *   hq, hkv : 1 <= hkv, hq % hkv == 0, hq / hkv <= 8, hq <= 128.
  *   o       : device float[hq][128]; osum: device float[hq][2].
  *   ws      : device workspace of q4_atq_ws_bytes(hq, hkv) bytes, 256-byte
- *             aligned, contents irrelevant.  Calls that overlap in time must
- *             not share it.
- * Two launches on `stream`, of max_pos/64 x hkv workgroups each (those
- * past the position leave at once); every output and the workspace must overlap no
- * other argument.  Inputs are assumed finite (a NaN score makes the
- * position of the maximum, and so the output, unspecified).
- * q4_atq_ws_bytes returns 0 for head counts outside the limits above.
+ *             aligned, zero-filled before its first use; each call leaves
+ *             it ready for the next call of the same hq, hkv and max_pos
+ *             (zero-fill it again before a call of another shape).  Calls
+ *             that overlap in time must not share it.
+ * One launch on `stream` of (max_pos/256 rounded up) x hq workgroups; those
+ * past the position leave at once.  Past 256 positions the workgroups of a
+ * query head hand span maxima and sums to each other through tagged words
+ * in the workspace; each such wait is bounded like q4_decode_layers' (env
+ * Q4_DECODE_TIMEOUT_MS); when one runs out, o is undefined and
+ * q4_atq_status reports it (and clears the workspace).  Every output and
+ * the workspace must overlap no other argument.  Inputs are assumed finite
+ * (a NaN score makes the position of the maximum, and so the output,
+ * unspecified).  q4_atq_ws_bytes returns 0 for head counts outside the
+ * limits above.
  */
 #define Q4_ATQ_MAX_POS 4096
 size_t q4_atq_ws_bytes(int32_t hq, int32_t hkv);
@@ -283,6 +290,9 @@ int q4_atq(const float *q, const float *g, const float *k, const float *v, const
            const float *wk, float eps, const float *rope_cos, const float *rope_sin,
            float *kcache, float *vcache, const int32_t *pos, int32_t max_pos, int32_t hq,
            int32_t hkv, float *o, float *osum, void *ws, size_t ws_bytes, void *stream);
+/* Host wait on `stream`; Q4_OK, or Q4_ETIMEOUT when a wait of q4_atq ran
+ * out since the last status call (the workspace is then zero-filled). */
+int q4_atq_status(void *ws, int32_t hq, int32_t hkv, void *stream);
 
 /*
  * Stage queue ([P2] Change: q4go encodes products into one open concurrent

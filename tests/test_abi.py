@@ -227,3 +227,6 @@ def test_atq_argument_checks(L):
     assert call(o=A + 512) == EINVAL                # o over q
     assert call(ws=D) == EINVAL                     # workspace over the key cache
     assert call(os=C + 0x400000) == EINVAL          # osum over the rotation table
+    assert L.q4_atq_status(None, 16, 4, None) == EINVAL
+    assert L.q4_atq_status(ctypes.c_void_p(H), 16, 3, None) == EINVAL
+    assert L.q4_atq_status(ctypes.c_void_p(H + 16), 16, 4, None) == EINVAL

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 def new_ws(q4, hq, hkv):
     n = q4.q4_atq_ws_bytes(hq, hkv)
     assert n > 0
-    return torch.empty((n + 255) // 256 * 64, dtype=torch.float32, device="cuda")
+    return torch.zeros((n + 255) // 256 * 64, dtype=torch.float32, device="cuda")
 
 
 class Dev:
@@ -61,14 +61,16 @@ def check(a, d, what):
     assert_bits_equal(host(d.vc).ravel(), vc.ravel(), what + " vcache")
 
 
-@pytest.mark.parametrize("pos", [0, 1, 63, 64, 65, 204, 1000, 4095])
+@pytest.mark.parametrize("pos", [0, 1, 63, 64, 204, 255, 256, 257, 1000, 4095])
 def test_atq_bit_exact_positions(pos):
     q4 = lib()
     print("atq pos %d" % pos, flush=True)
     a = synth.atq_inputs(seed=100 + pos, pos=pos, max_pos=4096)
     d = Dev(a)
-    d.run(q4, new_ws(q4, 16, 4))
+    ws = new_ws(q4, 16, 4)
+    d.run(q4, ws)
     check(a, d, "pos %d" % pos)
+    assert q4.q4_atq_status(ws, 16, 4) == q4.Q4_OK
 
 
 @pytest.mark.parametrize("hq,hkv", [(2, 2), (8, 1), (4, 4), (16, 2), (24, 3), (128, 16)])
@@ -183,3 +185,26 @@ def test_atq_position_outside_the_cache(pos):
     assert np.all(np.isnan(host(d.o))) and np.all(np.isnan(host(d.os)))
     assert_bits_equal(host(d.kc).ravel(), a["kcache"].ravel(), "kcache untouched")
     assert_bits_equal(host(d.vc).ravel(), a["vcache"].ravel(), "vcache untouched")
+
+
+def test_atq_bounded_waits_report_and_recover():
+    """With the wait bound at zero (Q4_DECODE_TIMEOUT_MS < 0) the span
+    exchanges of position 4095 give up at their first look: the status call
+    reports Q4_ETIMEOUT and clears the workspace, and the next call with
+    the normal bound is bit-exact."""
+    import os
+    q4 = lib()
+    a = synth.atq_inputs(seed=700, pos=4095, max_pos=4096)
+    d = Dev(a)
+    ws = new_ws(q4, 16, 4)
+    os.environ["Q4_DECODE_TIMEOUT_MS"] = "-1"
+    try:
+        d.run(q4, ws)
+    finally:
+        del os.environ["Q4_DECODE_TIMEOUT_MS"]
+    assert q4.q4_atq_status(ws, 16, 4) == q4.Q4_ETIMEOUT
+    d.kc.copy_(dev(a["kcache"]))
+    d.vc.copy_(dev(a["vcache"]))
+    d.run(q4, ws)
+    check(a, d, "after a timeout")
+    assert q4.q4_atq_status(ws, 16, 4) == q4.Q4_OK
