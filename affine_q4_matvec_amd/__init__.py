@@ -79,6 +79,7 @@ _SIGS = {
     "q4_atq": ([_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _i32,
                 _i32, _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "q4_atq_status": ([_vp, _i32, _i32, _vp], ctypes.c_int),
+    "q4_pos_advance": ([_vp, _vp], ctypes.c_int),
     "q4_queue_create": ([_vp, ctypes.c_int, ctypes.POINTER(_vp)], ctypes.c_int),
     "q4_queue_destroy": ([_vp], ctypes.c_int),
     "q4mv_queue": ([_vp, ctypes.POINTER(_Mat), _vp, _vp, _vp], ctypes.c_int),
@@ -380,6 +381,13 @@ def q4_atq_status(ws: torch.Tensor, hq: int, hkv: int, stream=None) -> int:
     workspace is then cleared)."""
     return int(_lib.q4_atq_status(_dev(ws, ws.dtype, None, "ws"), int(hq), int(hkv),
                                   _stream(stream)))
+
+
+def q4_pos_advance(pos: torch.Tensor, stream=None) -> torch.Tensor:
+    """``pos += 1`` on the device (int32[1])."""
+    _check("q4_pos_advance", _lib.q4_pos_advance(_dev(pos, torch.int32, 1, "pos"),
+                                                 _stream(stream)))
+    return pos
 
 
 class Mailbox:

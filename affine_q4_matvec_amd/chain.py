@@ -8,7 +8,8 @@ One step from token t (the chain has no other state):
                 h     = h + down_l m                   (q4mv_add, in place)
   u, us = rmsq(h, wn_final);  logits = head u;  t' = argmax(logits)
 
-Three ways to run it, with the same bits:
+Three ways to run it, with the same bits (and, in AttnDecodeChain below,
+the same chain with an attention block in every layer):
   fused=False      the steps as listed: 1 + 4 per layer + 4 kernels
   fused=True       rmsq in the products' prologues, SwiGLU in the gate/up
                    product's epilogue (gate and up rows interleaved), the
@@ -31,9 +32,10 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (FIXED, Graph, Mailbox, MlpLayer, Q4Matrix, q4_argmax, q4_argmax_ws_bytes,
-               q4_decode_layers, q4_decode_layers_ws_bytes, q4_embed, q4mv, q4mv_add,
-               q4mv_argmax_ws_bytes, q4mv_norm_argmax, q4mv_norm_swiglu, rmsq, swq)
+from . import (ATQ_D, FIXED, Graph, Mailbox, MlpLayer, Q4Matrix, q4_argmax, q4_argmax_ws_bytes,
+               q4_atq, q4_atq_ws_bytes, q4_decode_layers, q4_decode_layers_ws_bytes, q4_embed,
+               q4_pos_advance, q4mv, q4mv_add, q4mv_argmax_ws_bytes, q4mv_norm, q4mv_norm_argmax,
+               q4mv_norm_swiglu, rmsq, swq)
 
 
 def _stack_rows(a: dict, b: dict) -> dict:
@@ -193,3 +195,119 @@ class DecodeChain:
         if wait == "mailbox":
             stream.synchronize()
         return out
+
+
+class AttnDecodeChain(DecodeChain):
+    """The decode chain with an attention block in every layer, on the fused
+    per-stage kernels.  One step from token t at position p:
+
+      h = embed(head, t)
+      per layer l:  [q; g; k; v] = qgkv_l rmsq(h, wa_l)     (q4mv_norm)
+                    o, os = atq(q, g, k, v, ..., caches_l, p)  (q4_atq)
+                    h = h + O_l o                            (q4mv_add)
+                    m = swq([gate_l; up_l] rmsq(h, wn_l))    (q4mv_norm_swiglu)
+                    h = h + down_l m                         (q4mv_add)
+      t' = argmax(head rmsq(h, wn_final));  p = p + 1
+
+    Token and position live on the device, so one captured step is
+    replayed token after token; 2 + 5 per layer + 1 kernels.  The
+    attention block is the product set's Q/K/V/O stages given their
+    dataflow (the gate rows are an addition: the attention step gates its
+    output)."""
+
+    def __init__(self, weights: dict, mode: int = FIXED, layers: int | None = None,
+                 device: str = "cuda"):
+        self.mode = mode
+        self.persistent = False
+        self.fused = True
+        self.hidden = int(weights["hidden"])
+        self.inter = int(weights["inter"])
+        self.vocab = int(weights["vocab"])
+        self.eps = float(weights["eps"])
+        self.hq, self.hkv = int(weights["hq"]), int(weights["hkv"])
+        self.max_pos = int(weights["max_pos"])
+        L = len(weights["layers"]) if layers is None else layers
+        f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+        z = lambda *n, dt=torch.float32: torch.zeros(*n, dtype=dt, device=device)
+        self.layers = []
+        for lw in weights["layers"][:L]:
+            self.layers.append({
+                "wa": f32(lw["wa"]), "wq": f32(lw["wq"]), "wk": f32(lw["wk"]),
+                "qgkv": Q4Matrix.from_host(lw["qgkv"], device),
+                "o": Q4Matrix.from_host(lw["o"], device),
+                "wn": f32(lw["wn"]),
+                "gu": Q4Matrix.from_host(_interleave_rows(lw["gate"], lw["up"]), device),
+                "down": Q4Matrix.from_host(lw["down"], device),
+                "kc": z(self.hkv, self.max_pos, ATQ_D),
+                "vc": z(self.hkv, self.max_pos, ATQ_D),
+            })
+        self.wn_final = f32(weights["wn_final"])
+        self.head = Q4Matrix.from_host(weights["head"], device)
+        self.cos_tab, self.sin_tab = f32(weights["cos_tab"]), f32(weights["sin_tab"])
+        self.tok = z(1, dt=torch.int32)
+        self.pos = z(1, dt=torch.int32)
+        self.h = z(self.hidden)
+        D = ATQ_D
+        self.y = z((2 * self.hq + 2 * self.hkv) * D)
+        hq, hkv = self.hq, self.hkv
+        self.q, self.g = self.y[:hq * D], self.y[hq * D:2 * hq * D]
+        self.k = self.y[2 * hq * D:2 * hq * D + hkv * D]
+        self.v = self.y[2 * hq * D + hkv * D:]
+        self.o = z(hq * D)
+        self.os = z(hq * 2)
+        self.m = z(self.inter)
+        self.logits = z(self.vocab)
+        self.amax_ws = z((q4mv_argmax_ws_bytes() + 7) // 8, dt=torch.int64)
+        self.atq_ws = z((q4_atq_ws_bytes(hq, hkv) + 7) // 8, dt=torch.int64)
+        self.graph = None
+        self.mailbox = None
+        torch.cuda.synchronize()
+
+    def kernels_per_token(self) -> int:
+        return 3 + 5 * len(self.layers)
+
+    def bytes_per_token(self) -> int:
+        """Algorithmic bytes at position 0: every product's weights and
+        scales plus the small vectors (the caches grow by 2 rows per layer
+        per token and are read once per step: 1 KiB per position and layer
+        per key/value head, not counted here)."""
+        def prod(w):
+            return w.rows * (w.cols // 2 + 8 * (w.cols // 64)) + 4 * (w.cols + w.cols // 64 + w.rows)
+        total = prod(self.head) + self.hidden * 2 + 4 * self.vocab
+        for lw in self.layers:
+            total += prod(lw["qgkv"]) + prod(lw["o"]) + prod(lw["gu"]) + prod(lw["down"])
+            total += 8 * self.hidden + 4 * (3 * self.hidden)  # residual reads, norms
+        return total
+
+    def set_position(self, p: int, clear_caches: bool = True) -> None:
+        """Position of the next step (caches cleared by default: a new
+        sequence)."""
+        self.pos.fill_(int(p))
+        if clear_caches:
+            for lw in self.layers:
+                lw["kc"].zero_()
+                lw["vc"].zero_()
+
+    def enqueue_step(self, stream) -> None:
+        q4_embed(self.head, self.tok, self.h, stream=stream)
+        for lw in self.layers:
+            q4mv_norm(lw["qgkv"], self.h, lw["wa"], self.eps, self.y, mode=self.mode, stream=stream)
+            q4_atq(self.q, self.g, self.k, self.v, lw["wq"], lw["wk"], self.eps, self.cos_tab,
+                   self.sin_tab, lw["kc"], lw["vc"], self.pos, self.o, self.os, self.atq_ws,
+                   stream=stream)
+            q4mv_add(lw["o"], self.o, self.os, self.h, self.h, mode=self.mode, stream=stream)
+            q4mv_norm_swiglu(lw["gu"], self.h, lw["wn"], self.eps, self.m, mode=self.mode,
+                             stream=stream)
+            q4mv_add(lw["down"], self.m, None, self.h, self.h, mode=self.mode, stream=stream)
+        q4mv_norm_argmax(self.head, self.h, self.wn_final, self.eps, self.logits, self.tok,
+                         self.amax_ws, mode=self.mode, stream=stream)
+        q4_pos_advance(self.pos, stream=stream)
+
+    def run(self, tok0: int, steps: int, stream: torch.cuda.Stream, use_graph: bool = True,
+            on_step=None, wait: str = "stream", pos0: int = 0) -> list:
+        """As DecodeChain.run, from position `pos0` with empty caches."""
+        if pos0 + steps > self.max_pos:
+            raise ValueError("the caches hold %d positions" % self.max_pos)
+        with torch.cuda.stream(stream):
+            self.set_position(pos0)
+        return super().run(tok0, steps, stream, use_graph=use_graph, on_step=on_step, wait=wait)

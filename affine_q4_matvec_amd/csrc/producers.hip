@@ -126,6 +126,12 @@ __global__ __launch_bounds__(64) void mailbox_kernel(const int32_t *__restrict__
   __hip_atomic_store(host_seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// One thread: *pos += 1 (a decode chain's position, advanced inside its
+// captured graph after the token's last attention step).
+__global__ __launch_bounds__(64) void pos_advance_kernel(int32_t *pos) {
+  if (threadIdx.x == 0) *pos = *pos + 1;
+}
+
 int next_pow2(int v) {
   int p = 1;
   while (p < v) p *= 2;
@@ -181,6 +187,11 @@ hipError_t launch_mailbox(const int32_t *vals, int32_t n, int32_t *host_vals, ui
                           uint32_t *dev_count, hipStream_t st) {
   hipLaunchKernelGGL(mailbox_kernel, dim3(1), dim3(64), 0, st, vals, n, host_vals, host_seq,
                      dev_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_pos_advance(int32_t *pos, hipStream_t st) {
+  hipLaunchKernelGGL(pos_advance_kernel, dim3(1), dim3(64), 0, st, pos);
   return hipGetLastError();
 }
 

@@ -497,6 +497,11 @@ int q4_atq(const float *q, const float *g, const float *k, const float *v, const
   return hip_status(q4::launch_atq(a, static_cast<hipStream_t>(stream)));
 }
 
+int q4_pos_advance(int32_t *pos, void *stream) {
+  if (!pos || !aligned(pos, 4)) return Q4_EINVAL;
+  return hip_status(q4::launch_pos_advance(pos, static_cast<hipStream_t>(stream)));
+}
+
 int q4_atq_status(void *ws, int32_t hq, int32_t hkv, void *stream) {
   const size_t need = q4_atq_ws_bytes(hq, hkv);
   if (need == 0 || !ws || !aligned(ws, 256)) return Q4_EINVAL;

@@ -88,6 +88,7 @@ hipError_t launch_argmax(const float *v, int32_t n, int32_t *idx, void *ws, hipS
 hipError_t launch_argmax_final(const unsigned long long *keys, int32_t nkeys, int32_t *idx,
                                hipStream_t st);
 hipError_t launch_embed(const Prod &w, const int32_t *tok, float *e, hipStream_t st);
+hipError_t launch_pos_advance(int32_t *pos, hipStream_t st);
 // One thread: host_vals[0..n) = vals[0..n), then *host_seq = ++*dev_count.
 hipError_t launch_mailbox(const int32_t *vals, int32_t n, int32_t *host_vals, uint32_t *host_seq,
                           uint32_t *dev_count, hipStream_t st);

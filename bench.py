@@ -19,7 +19,9 @@ down q4mv + residual, then rmsq -> head q4mv -> argmax), captured once as a
 HIP graph, in ms per token over 200 tokens, for two engines: the fused
 per-stage kernels (2 per layer) and the persistent layer kernel (one launch
 for all layers); the attention step at positions 204 and 4095 of a 4096
-cache; and the CPU oracle timed on the host's cores on the head workload.
+cache; the chain with an attention block in every layer (fused stages,
+200 tokens from position 0); and the CPU oracle timed on the host's cores
+on the head workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -298,6 +300,62 @@ def run_atq(args, q4, torch, synth):
     return out
 
 
+def run_attn_chain(args, q4, torch, synth):
+    """The decode chain with an attention block in every layer (fused
+    per-stage kernels, 5 per layer), one captured graph per token from
+    position 0 with empty caches: ms per token with the mailbox wait, and
+    the device time of the same number of queued replays."""
+    from affine_q4_matvec_amd.chain import AttnDecodeChain
+
+    log("generating the chain with attention (24 layers, seed %d)" % args.seed)
+    w = synth.attn_chain_weights(seed=args.seed)
+    mode = q4.FAST if args.mode == "fast" else q4.FIXED
+    chain = AttnDecodeChain(w, mode=mode)
+    tok0 = int(w["tok0"])
+    steps = min(args.chain_tokens, chain.max_pos)
+    stream = torch.cuda.Stream()
+    chain.capture(stream)
+    chain.run(0, 3, stream)  # warm-up tokens (not timed)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tokens = chain.run(tok0, steps, stream, wait="mailbox")
+    per_token_ms = (time.perf_counter() - t0) * 1e3 / steps
+    with torch.cuda.stream(stream):
+        chain.set_token(tok0)
+        chain.set_position(0)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        chain.graph.launch(stream)
+    e1.record(stream)
+    stream.synchronize()
+    gpu_ms = e0.elapsed_time(e1) / steps
+    last = int(chain.tok.cpu().numpy()[0])
+    golden = os.path.join(ROOT, "tests", "golden", "attn_chain_seed%d.json" % args.seed)
+    match = None
+    if os.path.exists(golden) and mode == q4.FIXED:
+        ref = json.load(open(golden))
+        n = min(len(ref["tokens"]), len(tokens))
+        match = bool(ref["tokens"][:n] == tokens[:n])
+    out = {
+        "tokens": steps, "layers": len(chain.layers), "positions": "0..%d" % (steps - 1),
+        "ms_per_token_with_mailbox_wait": round(per_token_ms, 4),
+        "ms_per_token_gpu": round(gpu_ms, 4),
+        "kernels_per_token": chain.kernels_per_token(),
+        "algorithmic_bytes_per_token_at_pos0": chain.bytes_per_token(),
+        "tokens_match_oracle_golden_prefix": match,
+        "queued_replays_reach_same_last_token": last == tokens[-1],
+        "distinct_tokens": len(set(tokens)),
+        "attention_waits_ok": q4.q4_atq_status(chain.atq_ws, chain.hq, chain.hkv, stream) == q4.Q4_OK,
+    }
+    log("attention chain: %s" % out)
+    del chain
+    torch.cuda.synchronize()
+    return out
+
+
 def chain_tok0(seed, synth):
     return synth.randint(seed, "ch.tok0", synth.VOCAB)
 
@@ -357,6 +415,7 @@ def main() -> int:
     if not args.no_chain:
         chain = run_chain(args, q4, torch, synth)
     atq = None if args.no_atq else run_atq(args, q4, torch, synth)
+    attn_chain = None if (args.no_chain or args.no_atq) else run_attn_chain(args, q4, torch, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.seed)
     traffic = measured_traffic(qb)
     out = {
@@ -394,6 +453,7 @@ def main() -> int:
         },
         "decode_chain": chain,
         "attention_step": atq,
+        "attention_chain": attn_chain,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

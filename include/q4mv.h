@@ -295,6 +295,14 @@ int q4_atq(const float *q, const float *g, const float *k, const float *v, const
 int q4_atq_status(void *ws, int32_t hq, int32_t hkv, void *stream);
 
 /*
+ * q4_pos_advance: *pos += 1 on the device (one thread), so that a decode
+ * token captured once as a graph moves its attention steps to the next
+ * position on every replay ([P1] Verification: one command buffer per
+ * token, replayed token after token here).  pos: device int32[1].
+ */
+int q4_pos_advance(int32_t *pos, void *stream);
+
+/*
  * Stage queue ([P2] Change: q4go encodes products into one open concurrent
  * command buffer and returns; q4wait commits and waits once).
  * q4mv_queue appends a product to the current stage.  Products of one stage

@@ -247,6 +247,54 @@ def chain_hidden(w: dict, tok: int, nthreads: int = 1, layers: int | None = None
     return h
 
 
+def attn_caches(w: dict, layers: int | None = None):
+    """Empty key and value caches of an attention chain: one float32
+    [hkv, max_pos, 128] pair per layer."""
+    L = len(w["layers"]) if layers is None else layers
+    shape = (w["hkv"], w["max_pos"], ATQ_D)
+    return ([np.zeros(shape, np.float32) for _ in range(L)],
+            [np.zeros(shape, np.float32) for _ in range(L)])
+
+
+def attn_chain_hidden(w: dict, tok: int, pos: int, kc: list, vc: list, nthreads: int = 1,
+                      layers: int | None = None) -> np.ndarray:
+    """The hidden state of one decode step of a chain with attention, at
+    position ``pos`` (the caches ``kc``, ``vc`` get row ``pos`` of every
+    layer): h = embed(head, tok); per layer: u = rmsq(h, wa); [q; g; k; v]
+    = qgkv u; o = atq(q, g, k, v, ...); h = h + O o; then the MLP block of
+    ``chain_hidden``."""
+    L = len(w["layers"]) if layers is None else layers
+    hq, hkv, D = w["hq"], w["hkv"], ATQ_D
+    inter = w["inter"]
+    h = embed(w["head"], tok)
+    for l in range(L):
+        lw = w["layers"][l]
+        u, us = rmsq(h, lw["wa"], w["eps"])
+        y = q4mv(lw["qgkv"], u, us, nthreads)
+        q, g = y[:hq * D], y[hq * D:2 * hq * D]
+        k, v = y[2 * hq * D:2 * hq * D + hkv * D], y[2 * hq * D + hkv * D:]
+        o, os_ = atq(q, g, k, v, lw["wq"], lw["wk"], w["eps"], w["cos_tab"][pos],
+                     w["sin_tab"][pos], kc[l], vc[l], pos)
+        h = add(h, q4mv(lw["o"], o, os_, nthreads))
+        u, us = rmsq(h, lw["wn"], w["eps"])
+        a = np.empty(2 * inter, np.float32)
+        a[:inter] = q4mv(lw["gate"], u, us, nthreads)
+        a[inter:] = q4mv(lw["up"], u, us, nthreads)
+        m, ms = swq(a, inter)
+        h = add(h, q4mv(lw["down"], m, ms, nthreads))
+    return h
+
+
+def attn_chain_step(w: dict, tok: int, pos: int, kc: list, vc: list, nthreads: int = 1,
+                    layers: int | None = None):
+    """One step of the chain with attention: ``attn_chain_hidden``, then
+    the final norm, the head and argmax.  Returns ``(logits, next_token)``."""
+    h = attn_chain_hidden(w, tok, pos, kc, vc, nthreads, layers)
+    u, us = rmsq(h, w["wn_final"], w["eps"])
+    logits = q4mv(w["head"], u, us, nthreads)
+    return logits, argmax(logits)
+
+
 def chain_step(w: dict, tok: int, nthreads: int = 1, layers: int | None = None):
     """One decode-chain step from token ``tok``: the hidden state of
     ``chain_hidden``, then u = rmsq(h, wn_final), logits = head u, next

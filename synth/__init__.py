@@ -288,3 +288,25 @@ def atq_inputs(seed: int = DEFAULT_SEED, pos: int = 204, hq: int = ATQ_HQ, hkv: 
         "kcache": kc, "vcache": vc, "pos": pos,
         "eps": np.float32(EPS), "hq": hq, "hkv": hkv, "max_pos": max_pos,
     }
+
+
+def attn_chain_weights(seed: int = DEFAULT_SEED, layers: int = LAYERS, hidden: int = HIDDEN,
+                       inter: int = INTER, vocab: int = VOCAB, hq: int = ATQ_HQ,
+                       hkv: int = ATQ_HKV, max_pos: int = 256) -> dict:
+    """Decode-chain weights with an attention block in every layer: the MLP
+    chain's weights (``chain_weights``), plus per layer an RMS-norm weight
+    wa ~ N(1, 0.1), the [Q; gate; K; V] matrix ((2 hq + 2 hkv) * 128 rows x
+    hidden), the query and key norm weights wq, wk ~ N(1, 0.1) (128 each)
+    and O (hidden x hq * 128), all Q4 matrices with the chain's code centre;
+    and the rotation tables of ``max_pos`` positions."""
+    w = chain_weights(seed, layers, hidden, inter, vocab)
+    rows = (2 * hq + 2 * hkv) * ATQ_D
+    for l, lw in enumerate(w["layers"]):
+        lw["wa"] = normal_f32(seed, "ach.l%d.wa" % l, (hidden,), 1.0, 0.1)
+        lw["qgkv"] = q4_matrix(seed, "ach.l%d.qgkv" % l, rows, hidden, center=CHAIN_CENTER)
+        lw["wq"] = normal_f32(seed, "ach.l%d.wq" % l, (ATQ_D,), 1.0, 0.1)
+        lw["wk"] = normal_f32(seed, "ach.l%d.wk" % l, (ATQ_D,), 1.0, 0.1)
+        lw["o"] = q4_matrix(seed, "ach.l%d.o" % l, hidden, hq * ATQ_D, center=CHAIN_CENTER)
+    w["cos_tab"], w["sin_tab"] = rope_tables(max_pos)
+    w.update(hq=hq, hkv=hkv, max_pos=max_pos)
+    return w

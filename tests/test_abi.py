@@ -228,5 +228,7 @@ def test_atq_argument_checks(L):
     assert call(ws=D) == EINVAL                     # workspace over the key cache
     assert call(os=C + 0x400000) == EINVAL          # osum over the rotation table
     assert L.q4_atq_status(None, 16, 4, None) == EINVAL
+    assert L.q4_pos_advance(None, None) == EINVAL
+    assert L.q4_pos_advance(ctypes.c_void_p(A + 2), None) == EINVAL
     assert L.q4_atq_status(ctypes.c_void_p(H), 16, 3, None) == EINVAL
     assert L.q4_atq_status(ctypes.c_void_p(H + 16), 16, 4, None) == EINVAL

@@ -669,3 +669,61 @@ def test_atq_rejects_shapes_outside_the_readings():
     with pytest.raises(ValueError):
         oracle.atq(a["q"], a["g"], a["k"], a["v"], a["wq"], a["wk"], a["eps"], a["cos"],
                    a["sin"], a["kcache"], a["vcache"], 8)
+
+
+# ---------------------------------------------------------------------------
+# the decode chain with attention, composed from the pieces above
+# ---------------------------------------------------------------------------
+def test_attn_chain_steps_against_binary64_forward():
+    """Four steps (positions 0..3) of a 2-layer chain with attention against
+    an independent binary64 forward pass that keeps its own caches."""
+    w = synth.attn_chain_weights(seed=23, layers=2, hidden=128, inter=192, vocab=1000, hq=2,
+                                 hkv=1, max_pos=8)
+    D, hq, hkv = 128, 2, 1
+
+    def deq(m):
+        c = unpack_codes(m["q"], m["cols"]).astype(np.float64)
+        g = np.arange(m["cols"]) // 64
+        return c * m["s"][:, g].astype(np.float64) + m["b"][:, g].astype(np.float64)
+
+    def norm(x, wt):
+        return x / math.sqrt(np.mean(x * x) + 1e-6) * wt.astype(np.float64)
+
+    def rot(x, pos):
+        c, s = w["cos_tab"][pos].astype(np.float64), w["sin_tab"][pos].astype(np.float64)
+        lo, hi = x[:D // 2], x[D // 2:]
+        return np.concatenate([lo * c - hi * s, lo * s + hi * c])
+
+    kc, vc = oracle.attn_caches(w)
+    K64 = [np.zeros((hkv, 8, D)) for _ in range(2)]
+    V64 = [np.zeros((hkv, 8, D)) for _ in range(2)]
+    tok = w["tok0"]
+    for pos in range(4):
+        logits, nxt = oracle.attn_chain_step(w, tok, pos, kc, vc)
+        h = deq(w["head"])[tok]
+        for l, lw in enumerate(w["layers"]):
+            y = deq(lw["qgkv"]) @ norm(h, lw["wa"])
+            q, g = y[:hq * D], y[hq * D:2 * hq * D]
+            k, v = y[2 * hq * D:2 * hq * D + hkv * D], y[2 * hq * D + hkv * D:]
+            K64[l][0, pos] = rot(norm(k, lw["wk"]), pos)
+            V64[l][0, pos] = v
+            o = np.empty(hq * D)
+            for hh in range(hq):
+                qr = rot(norm(q[hh * D:(hh + 1) * D], lw["wq"]), pos)
+                sc = K64[l][0, :pos + 1] @ qr / math.sqrt(D)
+                p = np.exp(sc - sc.max())
+                o[hh * D:(hh + 1) * D] = (p @ V64[l][0, :pos + 1]) / p.sum() / (
+                    1 + np.exp(-g[hh * D:(hh + 1) * D]))
+            h = h + deq(lw["o"]) @ o
+            u = norm(h, lw["wn"])
+            a1, a2 = deq(lw["gate"]) @ u, deq(lw["up"]) @ u
+            h = h + deq(lw["down"]) @ (a1 / (1 + np.exp(-a1)) * a2)
+        ref = deq(w["head"]) @ norm(h, w["wn_final"])
+        assert np.max(np.abs(logits - ref)) < 1e-4 * (np.max(np.abs(ref)) + 1), pos
+        top2 = np.sort(ref)[-2:]
+        if top2[1] - top2[0] > 1e-3:
+            assert nxt == int(np.argmax(ref))
+        # the caches hold the rotated keys and the values of every position so far
+        assert np.max(np.abs(kc[0][0, :pos + 1] - K64[0][0, :pos + 1])) < 1e-4 * np.max(
+            np.abs(K64[0][0, :pos + 1]))
+        tok = nxt
