@@ -165,7 +165,11 @@ def run_head(args, q4, torch, synth):
                      args.steps)
     torch.cuda.synchronize()
     same = same and bool(np.array_equal(y.cpu().numpy().view(np.uint32), y_first.view(np.uint32)))
-    return step_ms, kern_ms, fused_ms, same
+    # for reference: the q4mv kernel in the other mode, timed the same way
+    other = q4.FIXED if mode == q4.FAST else q4.FAST
+    other_ms = timed(lambda i: q4.q4mv(mats[i % 2], x, xs, y, mode=other, stream=stream),
+                     args.steps)
+    return step_ms, kern_ms, fused_ms, same, other_ms
 
 
 def time_chain(args, q4, torch, chain, tok0):
@@ -404,7 +408,7 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 5}))
         return 0
-    step_ms, kern_ms, fused_ms, stable = run_head(args, q4, torch, synth)
+    step_ms, kern_ms, fused_ms, stable, other_ms = run_head(args, q4, torch, synth)
     qb = head_bytes(ROWS, COLS)
     step_bytes = qb + rmsq_bytes(COLS)
     value = step_bytes / (step_ms * 1e-3) / 1e9
@@ -450,6 +454,15 @@ def main() -> int:
             "algorithmic_bytes_per_launch": qb,
             "avg_launch_ms": round(kern_ms, 5),
             "timing": "HIP events around %d back-to-back launches on the launch stream" % args.steps,
+            "other_mode": {
+                "mode": "fast" if args.mode == "fixed" else "fixed",
+                "avg_launch_ms": round(other_ms, 5),
+                "achieved": round(qb / (other_ms * 1e-3) / 1e9, 1),
+                "frac": round(qb / (other_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            },
+            "fixed_order_note": "the fixed order is bound by VALU issue (26.2M wave instructions "
+                                "per launch; about 53 us with the weights L2-resident): "
+                                "profiles/q4mv_head_248320x2048_valu_counters.md",
         },
         "decode_chain": chain,
         "attention_step": atq,
