@@ -71,3 +71,26 @@ def test_attn_chain_24_layers_golden_tokens():
                      on_step=lambda i, c: hashes.append(oracle.fnv1a32(host(c.logits))))
     assert toks == g["tokens"]
     assert hashes == g["logits_fnv1a32"]
+
+
+def test_attn_chain_past_one_span():
+    """Three steps at positions 700..702 of a 1024-position cache (earlier
+    rows zero, as the oracle's fresh caches): the attention step's span
+    exchanges run inside the captured graph."""
+    from affine_q4_matvec_amd.chain import AttnDecodeChain
+    w = synth.attn_chain_weights(seed=33, layers=2, vocab=4096, max_pos=1024)
+    chain = AttnDecodeChain(w)
+    s = torch.cuda.Stream()
+    kc, vc = oracle.attn_caches(w)
+    want, tok = [], w["tok0"]
+    for pos in range(700, 703):
+        logits, tok = oracle.attn_chain_step(w, tok, pos, kc, vc, nthreads=NTHREADS)
+        want.append((tok, logits))
+    got = []
+    toks = chain.run(w["tok0"], 3, s, pos0=700, on_step=lambda i, c: got.append(host(c.logits)))
+    assert toks == [t for t, _ in want]
+    for i, (_, logits) in enumerate(want):
+        assert_bits_equal(got[i], logits, "step %d logits" % i)
+    for l, lw in enumerate(chain.layers):
+        assert_bits_equal(host(lw["kc"]).ravel(), kc[l].ravel(), "layer %d kcache" % l)
+    assert lib().q4_atq_status(chain.atq_ws, w["hq"], w["hkv"], s) == lib().Q4_OK
