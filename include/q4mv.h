@@ -258,6 +258,7 @@ int q4_decode_layers_status(void *ws, void *stream);
  *   q, g    : device float[hq][128] query and gate; q 16-byte aligned.
  *   k, v    : device float[hkv][128] new key and value, 16-byte aligned.
  *   wq, wk  : device float[128] norm weights, 16-byte aligned.
+ *   eps     : the epsilon of both norms (as rmsq's).
  *   rope_cos, rope_sin : device float[max_pos][64], the rotation tables
  *             of every position; row pos is read.
  *   kcache, vcache : device float[hkv][max_pos][128], 16-byte aligned; rows
@@ -278,7 +279,8 @@ int q4_decode_layers_status(void *ws, void *stream);
  * query head hand span maxima and sums to each other through tagged words
  * in the workspace; each such wait is bounded like q4_decode_layers' (env
  * Q4_DECODE_TIMEOUT_MS); when one runs out, o is undefined and
- * q4_atq_status reports it (and clears the workspace).  Every output and
+ * q4_atq_status reports it (and clears the workspace); until then, calls
+ * with that workspace return at once without writing.  Every output and
  * the workspace must overlap no other argument.  Inputs are assumed finite
  * (a NaN score makes the position of the maximum, and so the output,
  * unspecified).  q4_atq_ws_bytes returns 0 for head counts outside the
