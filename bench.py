@@ -100,20 +100,20 @@ def cpu_baseline(seed: int):
     cores = max(1, min(16, cores))
     h = synth.head_inputs(seed=seed)
     u, us = oracle.rmsq(h["z"], h["wn"], h["eps"])
-    best = None
-    t_end = time.perf_counter() + 20.0
-    reps = 0
-    while reps < 3 and (reps == 0 or time.perf_counter() < t_end):
+    # about 10 s of CPU work: whole-head products repeated (at least 3, at
+    # most 200), the median run reported
+    times = []
+    t_end = time.perf_counter() + 10.0
+    while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 200):
         t0 = time.perf_counter()
         oracle.q4mv(h, u, us, nthreads=cores)
-        dt = time.perf_counter() - t0
-        best = dt if best is None else min(best, dt)
-        reps += 1
-    del np
-    return {"value": round(head_bytes(ROWS, COLS) / best / 1e9, 3), "unit": "GB/s",
+        times.append(time.perf_counter() - t0)
+    med = float(np.median(times))
+    return {"value": round(head_bytes(ROWS, COLS) / med / 1e9, 3), "unit": "GB/s",
             "cores": cores, "kind": "oracle",
             "sample": "full 248320x2048 head q4mv (fixed order), rows split over %d threads, "
-                      "best of %d runs, %.2f s each" % (cores, reps, best)}
+                      "%d runs in %.1f s, median %.3f s (best %.3f s)"
+                      % (cores, len(times), sum(times), med, min(times))}
 
 
 def run_head(args, q4, torch, synth):
