@@ -54,9 +54,7 @@
 // Every value is computed by the same code as the per-stage kernels (rmsq
 // and SwiGLU from ops_device.h, group terms and row trees from
 // q4mv_device.h), so the result has the bits of the unfused chain.
-#include "ops_device.h"
-#include "q4mv_device.h"
-#include "q4mv_internal.h"
+#include "decode_device.h"
 #include "tagged_device.h"
 
 #pragma clang fp contract(off)
@@ -65,129 +63,7 @@ namespace q4 {
 namespace {
 
 using namespace dev;
-
-constexpr int kThreads = 512;   // 8 waves: two per SIMD, up to 256 registers each
-constexpr int kWaves = kThreads / kWave;
-constexpr int kCols = 2048;     // width of h: the gate/up rows and the down output
-constexpr int kGuPairs = 3;     // (gate, up) row pairs per block
-constexpr int kGuR = 2 * kGuPairs;
-constexpr int kChunkStride = 36;  // LDS floats per 32-value chunk (4 of padding)
-
-template <int NP>
-struct alignas(16) Lds {
-  float x[NP * 64 * kChunkStride];  // h (stage A) or m (stage B)
-  float xs[NP * 32];                // the group sums of m
-};
-
-struct GuBlock {
-  u32x4 cw[kGuR];
-  float sv[kGuR], bv[kGuR];
-};
-
-template <int NP>
-struct DownRow {
-  u32x4 cw[NP];
-  float sv[NP], bv[NP];
-};
-
-// Rows 2 p0 .. 2 p0 + 2 np - 1 (np <= kGuPairs pairs); the buffer's size
-// makes the loads of the rows past them return zero without a memory access.
-__device__ __forceinline__ void load_gu(const DecodeLayer &L, int p0, int np, int lane,
-                                        GuBlock &a) {
-  const size_t r0 = 2 * (size_t)p0;
-  const auto qr = buffer(L.gq + r0 * 256, 2 * np * 1024);
-  const auto sr = buffer(L.gs + r0 * 32, 2 * np * 128);
-  const auto br = buffer(L.gb + r0 * 32, 2 * np * 128);
-#pragma unroll
-  for (int j = 0; j < kGuR; ++j) {
-    a.cw[j] = load_codes(qr, 16u * lane, j * 1024);
-    a.sv[j] = load_f32(sr, 4u * (lane >> 1), j * 128);
-    a.bv[j] = load_f32(br, 4u * (lane >> 1), j * 128);
-  }
-}
-
-// Row r of the down matrix: pass p covers columns [2048 p, 2048 p + 2048).
-template <int NP>
-__device__ __forceinline__ void load_down(const DecodeLayer &L, int r, int lane, DownRow<NP> &d) {
-  const auto qr = buffer(L.dq + (size_t)r * (NP * 256), NP * 1024);
-  const auto sr = buffer(L.ds + (size_t)r * (NP * 32), NP * 128);
-  const auto br = buffer(L.db + (size_t)r * (NP * 32), NP * 128);
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    d.cw[p] = load_codes(qr, 16u * lane, p * 1024);
-    d.sv[p] = load_f32(sr, 4u * (lane >> 1), p * 128);
-    d.bv[p] = load_f32(br, 4u * (lane >> 1), p * 128);
-  }
-}
-
-// Keeps the compiler from moving memory accesses across this point (the
-// weight loads of the next stage stay behind the loads of the current wait).
-__device__ __forceinline__ void issue_order() { asm volatile("" ::: "memory"); }
-
-// One gate/up block of np pairs: the row sums, then each (gate, up) pair
-// goes into the wave's SwiGLU batch (m[p0 + i]).
-template <bool FAST, bool PAIRS, class Store>
-__device__ __forceinline__ void gu_block(const GuBlock &a, const float *xv, float xsv, int lane,
-                                         int p0, int np, const Store &store, SwigluBatch &batch,
-                                         int negz) {
-  const bool odd = lane & 1;
-#pragma unroll
-  for (int i = 0; i < kGuPairs; ++i) {
-    if (i < np) {
-      const float g = wave_sum_lane63(
-          group_term<FAST, PAIRS>(a.cw[2 * i], xv, a.sv[2 * i], a.bv[2 * i], xsv, true, odd), negz);
-      const float u = wave_sum_lane63(
-          group_term<FAST, PAIRS>(a.cw[2 * i + 1], xv, a.sv[2 * i + 1], a.bv[2 * i + 1], xsv, true,
-                                  odd),
-          negz);
-      swiglu_push<FAST>(store, batch, lane, g, u, p0 + i);
-    }
-  }
-}
-
-// Stage A over the wave's pairs [pb, pe) in blocks of kGuPairs; `a` holds
-// the first block's loads.
-template <bool FAST, bool PAIRS, class Store>
-__device__ __forceinline__ void gu_stage(const DecodeLayer &L, const float *xv, float xsv, int lane,
-                                         int pb, int pe, GuBlock &a, const Store &store) {
-  const int negz = neg_zero_reg();
-  SwigluBatch batch;
-  for (int p = pb; p < pe; p += kGuPairs) {
-    const int np = min(kGuPairs, pe - p);
-    if (p != pb) load_gu(L, p, np, lane, a);
-    gu_block<FAST, PAIRS>(a, xv, xsv, lane, p, np, store, batch, negz);
-  }
-  swiglu_flush<FAST>(store, batch);
-}
-
-// Stage B: the wave's down row from `d` and the activations in LDS: T over
-// each pass's 32 group terms, then the -0-padded balanced tree over the
-// passes (T over all groups); valid in lane 63.
-template <int NP, bool FAST, bool PAIRS>
-__device__ __forceinline__ float down_row(const Lds<NP> &S, int lane, const DownRow<NP> &d) {
-  constexpr int PP = NP == 1 ? 1 : NP == 2 ? 2 : 4;
-  const int negz = neg_zero_reg();
-  const bool odd = lane & 1;
-  float v[PP];
-#pragma unroll
-  for (int p = 0; p < PP; ++p) {
-    if (p < NP) {
-      float xv[32];
-      load_x_values(S.x + (p * 64 + lane) * kChunkStride, true, xv);
-      const float xsv = S.xs[p * 32 + (lane >> 1)];
-      v[p] = wave_sum_lane63(group_term<FAST, PAIRS>(d.cw[p], xv, d.sv[p], d.bv[p], xsv, true, odd),
-                             negz);
-      issue_order();  // one pass's activations in registers at a time
-    } else {
-      v[p] = kNegZero;
-    }
-  }
-#pragma unroll
-  for (int w = 1; w < PP; w *= 2)
-#pragma unroll
-    for (int i = 0; i < PP; i += 2 * w) v[i] = v[i] + v[i + w];
-  return v[0];
-}
+using namespace decode;
 
 // e[c] of the embedding row tk (the embed kernel's arithmetic; NaN for a
 // token outside the vocabulary).
