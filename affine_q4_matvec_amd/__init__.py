@@ -52,6 +52,12 @@ class _MlpLayer(ctypes.Structure):
     _fields_ = [("gate_up", _Mat), ("down", _Mat), ("wn", ctypes.c_void_p)]
 
 
+class _AttnBlock(ctypes.Structure):
+    _fields_ = [("qgkv", _Mat), ("o", _Mat), ("wa", ctypes.c_void_p), ("wq", ctypes.c_void_p),
+                ("wk", ctypes.c_void_p), ("kcache", ctypes.c_void_p),
+                ("vcache", ctypes.c_void_p), ("hkv", ctypes.c_int32), ("mlp", _MlpLayer)]
+
+
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _lib = ctypes.CDLL(library_path)
@@ -80,6 +86,10 @@ _SIGS = {
                 _i32, _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "q4_atq_status": ([_vp, _i32, _i32, _vp], ctypes.c_int),
     "q4_pos_advance": ([_vp, _vp], ctypes.c_int),
+    "q4_decode_block_ws_bytes": ([], ctypes.c_size_t),
+    "q4_decode_block": ([ctypes.POINTER(_AttnBlock), ctypes.c_float, _vp, _vp, _i32, _vp, _vp, _vp,
+                         ctypes.c_size_t, ctypes.c_int, _vp], ctypes.c_int),
+    "q4_decode_block_status": ([_vp, _vp], ctypes.c_int),
     "q4_queue_create": ([_vp, ctypes.c_int, ctypes.POINTER(_vp)], ctypes.c_int),
     "q4_queue_destroy": ([_vp], ctypes.c_int),
     "q4mv_queue": ([_vp, ctypes.POINTER(_Mat), _vp, _vp, _vp], ctypes.c_int),
@@ -381,6 +391,51 @@ def q4_atq_status(ws: torch.Tensor, hq: int, hkv: int, stream=None) -> int:
     workspace is then cleared)."""
     return int(_lib.q4_atq_status(_dev(ws, ws.dtype, None, "ws"), int(hq), int(hkv),
                                   _stream(stream)))
+
+
+BLOCK_MAX_POS = 256
+
+
+class AttnBlock:
+    """One decoder layer's weights and caches for q4_decode_block: the
+    [Q; gate; K; V] and O matrices, the attention, query and key norm
+    weights, the caches ``[hkv, max_pos, 128]`` and the MLP layer."""
+
+    def __init__(self, qgkv: Q4Matrix, o: Q4Matrix, wa: torch.Tensor, wq: torch.Tensor,
+                 wk: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, mlp: "MlpLayer"):
+        f = torch.float32
+        self._keep = (qgkv, o, wa, wq, wk, kcache, vcache, mlp)
+        self.kcache, self.vcache = kcache, vcache
+        self._c = _AttnBlock(qgkv._c, o._c, _dev(wa, f, 2048, "wa"), _dev(wq, f, ATQ_D, "wq"),
+                             _dev(wk, f, ATQ_D, "wk"), _dev(kcache, f, None, "kcache"),
+                             _dev(vcache, f, None, "vcache"), int(kcache.shape[0]), mlp._c)
+
+
+def q4_decode_block_ws_bytes() -> int:
+    return int(_lib.q4_decode_block_ws_bytes())
+
+
+def q4_decode_block(blk: AttnBlock, eps: float, h: torch.Tensor, pos: torch.Tensor,
+                    rope_cos: torch.Tensor, rope_sin: torch.Tensor, ws: torch.Tensor,
+                    mode: int = FIXED, stream=None) -> torch.Tensor:
+    """One decoder layer (attention block and MLP block) in one persistent
+    launch: ``h`` (2048 values) is read and written in place; the caches
+    get row ``pos``.  ``ws``: ``q4_decode_block_ws_bytes()`` bytes,
+    zero-filled before first use."""
+    max_pos = int(blk.kcache.shape[1])
+    f = torch.float32
+    rn = max_pos * (ATQ_D // 2)
+    _check("q4_decode_block", _lib.q4_decode_block(
+        ctypes.byref(blk._c), float(eps), _dev(h, f, 2048, "h"), _dev(pos, torch.int32, 1, "pos"),
+        max_pos, _dev(rope_cos, f, rn, "rope_cos"), _dev(rope_sin, f, rn, "rope_sin"),
+        _dev(ws, ws.dtype, None, "ws"), ws.numel() * ws.element_size(), mode, _stream(stream)))
+    return h
+
+
+def q4_decode_block_status(ws: torch.Tensor, stream=None) -> int:
+    """Host wait; Q4_OK, or Q4_ETIMEOUT when a wait of q4_decode_block ran
+    out (the workspace is then cleared)."""
+    return int(_lib.q4_decode_block_status(_dev(ws, ws.dtype, None, "ws"), _stream(stream)))
 
 
 def q4_pos_advance(pos: torch.Tensor, stream=None) -> torch.Tensor:

@@ -17,7 +17,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libq4mv.so")
-SOURCES = ["q4mv_kernels.hip", "producers.hip", "decode_layers.hip", "atq.hip", "q4mv_api.hip"]
+SOURCES = ["q4mv_kernels.hip", "producers.hip", "decode_layers.hip", "decode_block.hip", "atq.hip",
+           "q4mv_api.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

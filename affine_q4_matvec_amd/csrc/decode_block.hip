@@ -1,0 +1,536 @@
+// One decoder layer of a decode token, attention block and MLP block, in
+// one persistent launch (gfx950): "Metal: queued rmsq, swq, gdn and atq
+// kernels and a 4-row q4mv, so a decode token is one command buffer with
+// one wait" (#1440), Change (the rmsq, q4mv, atq and swq stages queued for
+// a whole token) and Verification (one command buffer, one wait).  The
+// same layer as the separate calls
+//   y = q4mv_norm(qgkv, h, wa)            [q; gate; k; v] = y
+//   o = q4_atq(q, gate, k, v, ...)        (16 query heads of 128)
+//   h = q4mv_add(O, o, osum, h)
+//   m = q4mv_norm_swiglu(gate_up, h, wn); h = q4mv_add(down, m, NULL, h)
+// with their bits, in one grid of one workgroup per compute unit whose
+// stages hand their outputs to each other through tagged words (the
+// protocol of tagged_device.h, as in the persistent MLP layers):
+//   stage Q    every wave: rmsq(h, wa) for itself, its 2..4 rows of
+//              [Q; gate; K; V]                    -> tagged q, gate, k, v
+//   stage ATQ  workgroups 0..15, one query head each: the attention step
+//              over one span of at most 256 positions; the head's new
+//              key and value rows, if it is its group's first head; the
+//              key and value cache rows are loaded before the wait
+//                                                  -> tagged o, osum
+//   stage O    every wave: one O row + the residual -> tagged h
+//   stage A    every wave: rmsq(h, wn), its (gate, up) pairs, SwiGLU
+//                                                  -> tagged m
+//   stage B    every wave: one down row + the residual -> h (plain store)
+// Each hand-off buffer is written once per launch; the tags name the call
+// (a counter per workgroup) and the stage.  Every wait is bounded; one that
+// runs out sets the error word and every workgroup leaves at its next
+// wait.  Compiled with -ffp-contract=off.
+#include <math.h>
+
+#include "decode_device.h"
+#include "tagged_device.h"
+
+#pragma clang fp contract(off)
+
+namespace q4 {
+namespace {
+
+using namespace dev;
+using namespace decode;
+
+constexpr int kD = kAtqD;
+constexpr int kHeads = kBlockHeads;
+constexpr float kScale = 0x1.6a09e6p-4f;  // RN32(1 / sqrt(128))
+constexpr int kQRowsPerWave = kBlockQRows / kCols;  // rows of [Q; gate; K; V] per wave, at most
+static_assert(kThreads == 512, "the attention stage's thread layout");
+static_assert(kBlockMaxPos == 256, "8 passes of 32 positions; 16 blocks of 16");
+
+struct QBlock {
+  u32x4 cw[kQRowsPerWave];
+  float sv[kQRowsPerWave], bv[kQRowsPerWave];
+};
+
+struct Row {
+  u32x4 cw;
+  float sv, bv;
+};
+
+__device__ __forceinline__ void load_qrows(const DecodeBlockArgs &A, int r0, int nrows, int lane,
+                                           QBlock &a) {
+  const auto qr = buffer(A.qq + (size_t)r0 * 256, nrows * 1024);
+  const auto sr = buffer(A.qs + (size_t)r0 * 32, nrows * 128);
+  const auto br = buffer(A.qb + (size_t)r0 * 32, nrows * 128);
+#pragma unroll
+  for (int j = 0; j < kQRowsPerWave; ++j) {
+    a.cw[j] = load_codes(qr, 16u * lane, j * 1024);
+    a.sv[j] = load_f32(sr, 4u * (lane >> 1), j * 128);
+    a.bv[j] = load_f32(br, 4u * (lane >> 1), j * 128);
+  }
+}
+
+__device__ __forceinline__ void load_orow(const DecodeBlockArgs &A, int r, int lane, Row &d) {
+  const auto qr = buffer(A.oq + (size_t)r * 256, 1024);
+  const auto sr = buffer(A.os + (size_t)r * 32, 128);
+  const auto br = buffer(A.ob + (size_t)r * 32, 128);
+  d.cw = load_codes(qr, 16u * lane, 0);
+  d.sv = load_f32(sr, 4u * (lane >> 1), 0);
+  d.bv = load_f32(br, 4u * (lane >> 1), 0);
+}
+
+__device__ __forceinline__ void load8(const float *p, float *v) {
+  const float4 a = reinterpret_cast<const float4 *>(p)[0];
+  const float4 b = reinterpret_cast<const float4 *>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// The balanced tree over the 16 lanes of an aligned 16-lane row, in every
+// lane of the row.
+__device__ __forceinline__ float sum16(float s) {
+  s = s + dpp<kDppQuadXor1>(s);
+  return segment_sum<16>(s);
+}
+
+__device__ __forceinline__ float sum64(float s) {
+  s = s + dpp<kDppQuadXor1>(s);
+  return segment_sum<64>(s);
+}
+
+__device__ __forceinline__ float max64(float s) {
+#pragma unroll
+  for (int m = 1; m < kWave; m *= 2) s = fmaxf(s, __shfl_xor(s, m));
+  return s;
+}
+
+struct AttnLds {
+  float in[4][kD];          // q, gate, k, v of the head
+  float un[2][kD];          // normed q, k
+  float rot[2][kD];         // rotated q, k
+  float s[kBlockMaxPos];    // scores
+  float e[kBlockMaxPos];    // weights
+  float part[16][kD];       // value sums over 16 positions
+  float wsum[4];            // weight sums over 64 positions
+  float m;                  // largest score
+};
+
+// Stages m (or o) into LDS for a down (or O) row: `vals` are this thread's
+// chunks (8 values each, chunk c of the padded layout), the group sums
+// are written by the caller.  Returns whether the pair decode may be used.
+template <int NP>
+__device__ __forceinline__ bool stage_rows_input(Lds<NP> &L, const float (*vals)[8], int nchunks) {
+  bool large = false;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int c = threadIdx.x + r * kThreads;
+    if (c < nchunks)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) large |= !(__builtin_fabsf(vals[r][k]) < 0x1p118f);
+  }
+  const bool pairs = !__syncthreads_or(large);
+  const float scale = pairs ? 1.0f / fp8_unit() : 1.0f;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int c = threadIdx.x + r * kThreads;
+    if (c < nchunks) {
+      float4 *dst = reinterpret_cast<float4 *>(L.x + 8 * c + 4 * (c >> 2));
+      dst[0] = make_float4(vals[r][0] * scale, vals[r][1] * scale, vals[r][2] * scale,
+                           vals[r][3] * scale);
+      dst[1] = make_float4(vals[r][4] * scale, vals[r][5] * scale, vals[r][6] * scale,
+                           vals[r][7] * scale);
+    }
+  }
+  return pairs;
+}
+
+template <bool FAST, int NP>
+__global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs A) {
+  __shared__ Lds<NP> S;  // h (stage A) or m (stage B)
+  __shared__ Lds<1> SO;  // o (stage O)
+  __shared__ AttnLds T;
+  const int nwg = gridDim.x;
+  const int wg = blockIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1);
+  const int wave = wave_index();
+  uint32_t *err = A.ctl + kBlockErrorWord;
+  if (__syncthreads_or(load_word(err) != 0)) return;
+  const uint32_t call = load_word(A.ctl + wg);
+  const uint32_t tag = call << 3;  // + 1 q/gate/k/v, + 2 o, + 3 h after attention, + 4 m
+  const int gw = wave * nwg + wg;
+  const int stride = kWaves * nwg;
+  const int row = gw;
+  const bool has_row = row < kCols;
+  const bool mine = 8 * t < kCols;
+  const int copy = wg % kDecodeCopies;
+  const int G = kHeads / A.hkv;
+  const int nq = 2 * kCols + 2 * A.hkv * kD;
+  const int qb = (int)(((long long)nq * gw) / stride);
+  const int qe = (int)(((long long)nq * (gw + 1)) / stride);
+  const int pb = (int)(((long long)A.inter * gw) / stride);
+  const int pe = (int)(((long long)A.inter * (gw + 1)) / stride);
+  const int pos = *A.pos;
+  const bool pos_ok = pos >= 0 && pos < A.max_pos;
+  const int n = pos_ok ? pos + 1 : 0;
+  const int negz = neg_zero_reg();
+  const bool odd = lane & 1;
+
+  // ---- stage Q --------------------------------------------------------------
+  QBlock qa;
+  if (qb < qe) load_qrows(A, qb, qe - qb, lane, qa);
+  float hv[32], wv[32];
+  load_x_values(A.h + 32 * lane, true, hv);
+  load_x_values(A.wa + 32 * lane, true, wv);
+  // the residual of the wave's row (lane 63): h before the layer
+  float res = has_row && lane == kWave - 1 ? A.h[row] : 0.0f;
+  {
+    const float rho = ops::rmsq_rho_wave2048(hv, A.eps);
+    float xv[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) xv[k] = ops::rmsq_value(hv[k], rho, wv[k]);
+    const float xsv = pair_group_sum(xv);
+    const bool pairs = prescale_for_pairs(xv);
+#pragma unroll
+    for (int i = 0; i < kQRowsPerWave; ++i) {
+      if (qb + i < qe) {  // uniform per wave
+        const float tv = pairs ? group_term<FAST, true>(qa.cw[i], xv, qa.sv[i], qa.bv[i], xsv, true, odd)
+                               : group_term<FAST, false>(qa.cw[i], xv, qa.sv[i], qa.bv[i], xsv, true, odd);
+        const float v = wave_sum_lane63(tv, negz);
+        if (lane == kWave - 1)
+#pragma unroll
+          for (int c = 0; c < kDecodeCopies; ++c)
+            store_tagged(A.qv + (size_t)c * kBlockQRows + qb + i, v, tag + 1);
+      }
+    }
+  }
+  Row od;
+  if (has_row) load_orow(A, row, lane, od);
+  issue_order();
+
+  // ---- stage ATQ (workgroups 0..15, one query head each) --------------------
+  if (wg < kHeads) {
+    const int hd = wg, j = hd / G;
+    const int r = t >> 4, l = t & 15;  // scores: 32 positions per pass
+    // the cache rows below pos, loaded before the wait
+    float kv[8][8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int tp = 32 * p + r;
+      if (tp < n && tp != pos) load8(A.kc + ((size_t)j * A.max_pos + tp) * kD + 8 * l, kv[p]);
+    }
+    const int cq = t & 31, pg = t >> 5;  // values: 4 columns x 16 positions
+    float v0[16], v1[16], v2[16], v3[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int p = 16 * pg + k;
+      float4 f = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (p < n && p != pos)
+        f = reinterpret_cast<const float4 *>(A.vc + ((size_t)j * A.max_pos + p) * kD)[cq];
+      v0[k] = f.x;
+      v1[k] = f.y;
+      v2[k] = f.z;
+      v3[k] = f.w;
+    }
+    float nw[8], ct[8], st[8];
+    if (t < 32) {
+      load8((r == 0 ? A.wq : A.wk) + 8 * l, nw);
+      const int pr = pos_ok ? pos : 0;
+      load8(A.cs + (size_t)pr * (kD / 2) + 8 * (l & 7), ct);
+      load8(A.sn + (size_t)pr * (kD / 2) + 8 * (l & 7), st);
+    }
+    // q, gate (rows of this head), k, v (rows of its key/value head)
+    {
+      const int part = t / kD, i = t % kD;
+      const int src = part == 0   ? kD * hd + i
+                      : part == 1 ? kCols + kD * hd + i
+                      : part == 2 ? 2 * kCols + kD * j + i
+                                  : 2 * kCols + kD * A.hkv + kD * j + i;
+      float v = 0.0f;
+      const bool ok =
+          poll_tagged<1>(A.qv + (size_t)copy * kBlockQRows + src, tag + 1, &v, err, A.spin_ticks);
+      T.in[part][i] = v;
+      if (!__syncthreads_and(ok)) return;
+    }
+    // rmsq of q (row 0) and k (row 1), then the rotation
+    if (t < 32) {
+      float x[8], sq[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        x[k] = T.in[r == 0 ? 0 : 2][8 * l + k];
+        sq[k] = x[k] * x[k];
+      }
+      const float rho = ops::rmsq_rho_from_ss(sum16(ops::tree8(sq)), kD, A.eps);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) T.un[r][8 * l + k] = ops::rmsq_value(x[k], rho, nw[k]);
+    }
+    __syncthreads();
+    if (t < 32) {
+      float rv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int d = 8 * l + k;
+        if (l < 8) {
+          const float a = T.un[r][d], b = T.un[r][d + kD / 2];
+          const float ac = a * ct[k], bs = b * st[k];
+          rv[k] = ac - bs;
+        } else {
+          const float a = T.un[r][d - kD / 2], b = T.un[r][d];
+          const float as = a * st[k], bc = b * ct[k];
+          rv[k] = as + bc;
+        }
+        T.rot[r][d] = rv[k];
+      }
+      if (r == 1 && hd % G == 0 && pos_ok) {  // the new cache rows
+        float4 *kd = reinterpret_cast<float4 *>(A.kc + ((size_t)j * A.max_pos + pos) * kD + 8 * l);
+        float4 *vd = reinterpret_cast<float4 *>(A.vc + ((size_t)j * A.max_pos + pos) * kD + 8 * l);
+        kd[0] = make_float4(rv[0], rv[1], rv[2], rv[3]);
+        kd[1] = make_float4(rv[4], rv[5], rv[6], rv[7]);
+        const float *nv = T.in[3] + 8 * l;
+        vd[0] = make_float4(nv[0], nv[1], nv[2], nv[3]);
+        vd[1] = make_float4(nv[4], nv[5], nv[6], nv[7]);
+      }
+    }
+    __syncthreads();
+    // scores
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int tp = 32 * p + r;
+      if (tp < n) {  // uniform over the 16 lanes of the position
+        float pr[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          pr[k] = T.rot[0][8 * l + k] * (tp == pos ? T.rot[1][8 * l + k] : kv[p][k]);
+        const float sc = sum16(ops::tree8(pr)) * kScale;
+        if (l == 0) T.s[tp] = sc;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (64 * k + lane < n) m = fmaxf(m, T.s[64 * k + lane]);
+      m = max64(m);
+      if (lane == 0) T.m = m;
+    }
+    __syncthreads();
+    if (t < kBlockMaxPos) {
+      float e = kNegZero;
+      if (t < n) {
+        const float d = T.s[t] - T.m;
+        e = (float)ops::fixed_exp((double)d);
+      }
+      T.e[t] = e;
+      const float z = sum64(e);
+      if (lane == 0) T.wsum[wave] = z;
+    }
+    __syncthreads();
+    // the weighted value sums over 16 positions of 4 columns (the new row,
+    // at pos, from the inputs)
+    {
+      const int kp = pos - 16 * pg;  // the new row's slot in this thread's block, if any
+      if (kp >= 0 && kp < 16) {
+        const float4 nv = *reinterpret_cast<const float4 *>(&T.in[3][4 * cq]);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          if (k == kp) {
+            v0[k] = nv.x;
+            v1[k] = nv.y;
+            v2[k] = nv.z;
+            v3[k] = nv.w;
+          }
+        }
+      }
+      float ek[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) ek[k] = T.e[16 * pg + k];
+      const auto block16 = [&](const float *vc) {
+        float pr[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) pr[k] = 16 * pg + k < n ? ek[k] * vc[k] : kNegZero;
+        return ops::tree8(pr) + ops::tree8(pr + 8);
+      };
+      *reinterpret_cast<float4 *>(&T.part[pg][4 * cq]) =
+          make_float4(block16(v0), block16(v1), block16(v2), block16(v3));
+    }
+    __syncthreads();
+    if (t < kD) {
+      float pq[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) pq[k] = T.part[k][t];
+      const float w = ops::tree8(pq) + ops::tree8(pq + 8);
+      const float z = (T.wsum[0] + T.wsum[1]) + (T.wsum[2] + T.wsum[3]);
+      const double gd = (double)T.in[1][t];
+      const float sig = (float)(1.0 / (1.0 + ops::fixed_exp(-gd)));
+      const float ov = pos_ok ? (w / z) * sig : __builtin_nanf("");
+      const float gsum = sum64(ov);  // waves 0 and 1: the head's two groups
+#pragma unroll
+      for (int c = 0; c < kDecodeCopies; ++c) {
+        uint64_t *o = A.ov + (size_t)c * kBlockORows;
+        store_tagged(o + kD * hd + t, ov, tag + 2);
+        if (lane == 0) store_tagged(o + kCols + 2 * hd + wave, gsum, tag + 2);
+      }
+    }
+  }
+
+  // ---- stage O: h = h + O o ---------------------------------------------------
+  GuBlock a;
+  if (pb < pe) load_gu(A.mlp, pb, min(kGuPairs, pe - pb), lane, a);
+  issue_order();
+  {
+    float ov[2][8];
+    // the wait for the attention stage is long: wave 0 alone polls (the
+    // group sums of every head) until it ends, then every thread takes its
+    // words
+    bool ok = wave != 0 || await_words(A.ov + (size_t)copy * kBlockORows + kCols, 2 * kHeads,
+                                       tag + 2, err, A.spin_ticks);
+    if (!__syncthreads_and(ok)) return;
+    if (mine)
+      ok = poll_tagged<8>(A.ov + (size_t)copy * kBlockORows + 8 * t, tag + 2, ov[0], err,
+                          A.spin_ticks);
+    if (t >= 256 && t < 260)  // the 32 group sums, 8 per thread
+      ok = poll_tagged<8>(A.ov + (size_t)copy * kBlockORows + kCols + 8 * (t - 256), tag + 2,
+                          ov[1], err, A.spin_ticks);
+    if (!__syncthreads_and(ok)) return;
+    if (t >= 256 && t < 260)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) SO.xs[8 * (t - 256) + k] = ov[1][k];
+    // stage_rows_input looks at chunks t and t + 512 only: chunk t is this
+    // thread's 8 values of o
+    float vals[2][8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      vals[0][k] = mine ? ov[0][k] : 0.0f;
+      vals[1][k] = 0.0f;
+    }
+    const bool pairs = stage_rows_input<1>(SO, vals, kCols / 8);
+    __syncthreads();
+    if (has_row) {
+      Lds<1> &L = SO;
+      float xv[32];
+      load_x_values(L.x + lane * kChunkStride, true, xv);
+      const float xsv = L.xs[lane >> 1];
+      const float tv = pairs ? group_term<FAST, true>(od.cw, xv, od.sv, od.bv, xsv, true, odd)
+                             : group_term<FAST, false>(od.cw, xv, od.sv, od.bv, xsv, true, odd);
+      const float v = wave_sum_lane63(tv, negz);
+      if (lane == kWave - 1) {
+        res = res + v;
+#pragma unroll
+        for (int c = 0; c < kDecodeCopies; ++c)
+          store_tagged(A.hv + (size_t)c * kCols + row, res, tag + 3);
+      }
+    }
+  }
+
+  // ---- stage A: m = SwiGLU([gate; up] rmsq(h, wn)) --------------------------
+  load_x_values(A.mlp.wn + 32 * lane, true, wv);
+  {
+    bool ok = true;
+    if (mine) {
+      float h8[8];
+      ok = poll_tagged<8>(A.hv + (size_t)copy * kCols + 8 * t, tag + 3, h8, err, A.spin_ticks);
+      float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * t + 4 * (t >> 2));
+      dst[0] = make_float4(h8[0], h8[1], h8[2], h8[3]);
+      dst[1] = make_float4(h8[4], h8[5], h8[6], h8[7]);
+    }
+    issue_order();
+    DownRow<NP> d;
+    if (has_row) load_down<NP>(A.mlp, row, lane, d);
+    if (!__syncthreads_and(ok)) return;
+    load_x_values(S.x + kChunkStride * lane, true, hv);
+    {
+      const float rho = ops::rmsq_rho_wave2048(hv, A.eps);
+      float xv[32];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) xv[k] = ops::rmsq_value(hv[k], rho, wv[k]);
+      const float xsv = pair_group_sum(xv);
+      uint64_t *mq = A.mq;
+      const uint32_t tm = tag + 4;
+      const auto store_m = [mq, tm](int i, float v) {
+#pragma unroll
+        for (int c = 0; c < kDecodeCopies; ++c) store_tagged(mq + c * kDecodeMaxInter + i, v, tm);
+      };
+      if (pb < pe) {
+        if (prescale_for_pairs(xv))
+          gu_stage<FAST, true>(A.mlp, xv, xsv, lane, pb, pe, a, store_m);
+        else
+          gu_stage<FAST, false>(A.mlp, xv, xsv, lane, pb, pe, a, store_m);
+      }
+    }
+
+    // ---- stage B: h = h + down m ---------------------------------------------
+    constexpr int kChunks = NP * kCols / 8;
+    float xm[2][8];
+    ok = true;
+    __syncthreads();  // every wave of the workgroup is done with stage A
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int c = t + rr * kThreads;
+      if (c < kChunks)
+        ok &= poll_tagged<8>(A.mq + (size_t)copy * kDecodeMaxInter + 8 * c, tag + 4, xm[rr], err,
+                             A.spin_ticks);
+    }
+    if (!__syncthreads_and(ok)) return;
+    // group sums: T over each chunk, then over 8 chunks by a butterfly
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int c = t + rr * kThreads;
+      if (rr * kThreads < kChunks) {  // uniform per round
+        float gs = c < kChunks ? ops::tree8(xm[rr]) : 0.0f;
+        gs = gs + __shfl_xor(gs, 1);
+        gs = gs + __shfl_xor(gs, 2);
+        gs = gs + __shfl_xor(gs, 4);
+        if (c < kChunks && (c & 7) == 0) S.xs[c >> 3] = gs;
+      }
+    }
+    const bool pairs = stage_rows_input<NP>(S, xm, kChunks);
+    __syncthreads();
+    if (has_row) {
+      const float v = pairs ? down_row<NP, FAST, true>(S, lane, d) : down_row<NP, FAST, false>(S, lane, d);
+      if (lane == kWave - 1) A.h[row] = res + v;
+    }
+  }
+  __syncthreads();
+  if (t == 0) store_word(A.ctl + wg, call + 1);
+}
+
+template <bool FAST, int NP>
+const void *kernel_ptr() {
+  return reinterpret_cast<const void *>(&decode_block_kernel<FAST, NP>);
+}
+
+const void *block_kernel(int mode, int np) {
+  const bool fast = mode != 0;
+  switch (np) {
+    case 1: return fast ? kernel_ptr<true, 1>() : kernel_ptr<false, 1>();
+    case 2: return fast ? kernel_ptr<true, 2>() : kernel_ptr<false, 2>();
+    case 3: return fast ? kernel_ptr<true, 3>() : kernel_ptr<false, 3>();
+    case 4: return fast ? kernel_ptr<true, 4>() : kernel_ptr<false, 4>();
+    default: return nullptr;
+  }
+}
+
+}  // namespace
+
+int32_t decode_block_grid(int mode, int32_t inter) {
+  const void *k = block_kernel(mode, inter / kCols);
+  if (!k || inter % kCols) return 0;
+  int dev = 0, per_cu = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  // one workgroup per compute unit, a wave for every O and down row
+  if (per_cu < 1 || cus * kWaves < kCols || cus > kDecodeMaxGroups) return 0;
+  return cus;
+}
+
+hipError_t launch_decode_block(const DecodeBlockArgs &a, int mode, hipStream_t st) {
+  const int32_t grid = decode_block_grid(mode, a.inter);
+  const void *k = block_kernel(mode, a.inter / kCols);
+  if (grid < 1 || !k) return hipErrorInvalidValue;
+  void *args[] = {const_cast<DecodeBlockArgs *>(&a)};
+  return hipLaunchKernel(k, dim3(grid), dim3(kThreads), args, 0, st);
+}
+
+}  // namespace q4

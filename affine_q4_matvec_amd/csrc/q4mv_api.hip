@@ -497,6 +497,80 @@ int q4_atq(const float *q, const float *g, const float *k, const float *v, const
   return hip_status(q4::launch_atq(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t q4_decode_block_ws_bytes(void) { return q4::kBlockWsBytes; }
+
+int q4_decode_block(const q4_attn_block *blk, float eps, float *h, const int32_t *pos,
+                    int32_t max_pos, const float *rope_cos, const float *rope_sin, void *ws,
+                    size_t ws_bytes, int mode, void *stream) {
+  if (mode != Q4_FIXED && mode != Q4_FAST) return Q4_EINVAL;
+  if (!blk) return Q4_EINVAL;
+  const int32_t hkv = blk->hkv;
+  if (hkv < 1 || hkv > q4::kBlockHeads || q4::kBlockHeads % hkv != 0) return Q4_EINVAL;
+  if (check_mat(&blk->qgkv) != Q4_OK || check_mat(&blk->o) != Q4_OK) return Q4_EINVAL;
+  if (blk->qgkv.cols != 2048 || blk->qgkv.rows != (2 * q4::kBlockHeads + 2 * hkv) * q4::kAtqD)
+    return Q4_EINVAL;
+  if (blk->o.rows != 2048 || blk->o.cols != 2048) return Q4_EINVAL;
+  const q4_mlp_layer &L = blk->mlp;
+  if (check_mat(&L.gate_up) != Q4_OK || check_mat(&L.down) != Q4_OK) return Q4_EINVAL;
+  const int32_t inter = L.down.cols;
+  if (inter < 2048 || inter % 2048 != 0 || inter > q4::kDecodeMaxInter) return Q4_EINVAL;
+  if (L.gate_up.cols != 2048 || L.gate_up.rows != 2 * inter || L.down.rows != 2048)
+    return Q4_EINVAL;
+  const float *in16[6] = {blk->wa, blk->wq, blk->wk, L.wn, rope_cos, rope_sin};
+  for (int i = 0; i < 6; ++i)
+    if (!in16[i] || !aligned(in16[i], 16)) return Q4_EINVAL;
+  if (!blk->kcache || !blk->vcache || !aligned(blk->kcache, 16) || !aligned(blk->vcache, 16))
+    return Q4_EINVAL;
+  if (!h || !aligned(h, 16) || !pos || !aligned(pos, 4)) return Q4_EINVAL;
+  if (max_pos < 1 || max_pos > q4::kBlockMaxPos) return Q4_EINVAL;
+  if (!ws || !aligned(ws, 16) || ws_bytes < q4::kBlockWsBytes) return Q4_EINVAL;
+  const size_t D = q4::kAtqD;
+  const size_t hb = sizeof(float) * 2048, wb = sizeof(float) * D;
+  const size_t cb = sizeof(float) * (size_t)hkv * (size_t)max_pos * D;
+  const size_t rb = sizeof(float) * (size_t)max_pos * D / 2;
+  // written: h (in place), the caches, the workspace
+  const void *outs[4] = {h, blk->kcache, blk->vcache, ws};
+  const size_t outb[4] = {hb, cb, cb, q4::kBlockWsBytes};
+  const void *ins[7] = {blk->wa, blk->wq, blk->wk, L.wn, rope_cos, rope_sin, pos};
+  const size_t inb[7] = {hb, wb, wb, hb, rb, rb, sizeof(int32_t)};
+  const q4_mat *mats[4] = {&blk->qgkv, &blk->o, &L.gate_up, &L.down};
+  for (int i = 0; i < 4; ++i) {
+    for (int m = i + 1; m < 4; ++m)
+      if (overlap(outs[i], outb[i], outs[m], outb[m])) return Q4_EINVAL;
+    for (int m = 0; m < 7; ++m)
+      if (overlap(outs[i], outb[i], ins[m], inb[m])) return Q4_EINVAL;
+    for (int m = 0; m < 4; ++m)
+      if (overlaps_mat(outs[i], outb[i], mats[m])) return Q4_EINVAL;
+  }
+  q4::DecodeBlockArgs a;
+  memset(&a, 0, sizeof(a));
+  a.qq = blk->qgkv.q; a.qs = blk->qgkv.s; a.qb = blk->qgkv.b;
+  a.oq = blk->o.q; a.os = blk->o.s; a.ob = blk->o.b;
+  a.wa = blk->wa; a.wq = blk->wq; a.wk = blk->wk;
+  a.kc = blk->kcache; a.vc = blk->vcache;
+  a.cs = rope_cos; a.sn = rope_sin; a.pos = pos;
+  a.max_pos = max_pos; a.hkv = hkv;
+  a.mlp = q4::DecodeLayer{L.gate_up.q, L.gate_up.s, L.gate_up.b, L.wn, L.down.q, L.down.s, L.down.b};
+  a.inter = inter;
+  a.h = h;
+  char *w = static_cast<char *>(ws);
+  a.qv = reinterpret_cast<uint64_t *>(w + q4::kBlockQvOffset);
+  a.ov = reinterpret_cast<uint64_t *>(w + q4::kBlockOvOffset);
+  a.hv = reinterpret_cast<uint64_t *>(w + q4::kBlockHvOffset);
+  a.mq = reinterpret_cast<uint64_t *>(w + q4::kBlockMqOffset);
+  a.ctl = reinterpret_cast<uint32_t *>(w + q4::kBlockCtlOffset);
+  a.eps = eps;
+  if (wait_ticks(&a.spin_ticks) != Q4_OK) return Q4_EHIP;
+  if (q4::decode_block_grid(mode, inter) < 1) return Q4_EINVAL;  // too few compute units
+  return hip_status(q4::launch_decode_block(a, mode, static_cast<hipStream_t>(stream)));
+}
+
+int q4_decode_block_status(void *ws, void *stream) {
+  if (!ws || !aligned(ws, 16)) return Q4_EINVAL;
+  return ws_status(ws, q4::kBlockCtlOffset + 4 * (size_t)q4::kBlockErrorWord, q4::kBlockWsBytes,
+                   stream);
+}
+
 int q4_pos_advance(int32_t *pos, void *stream) {
   if (!pos || !aligned(pos, 4)) return Q4_EINVAL;
   return hip_status(q4::launch_pos_advance(pos, static_cast<hipStream_t>(stream)));

@@ -52,4 +52,18 @@ __device__ __forceinline__ bool poll_tagged(const uint64_t *p, uint32_t tag, flo
   }
 }
 
+// The first half of a long wait: lanes [0, n) of the calling wave poll the
+// n consecutive words at p until each carries `tag` (their values are not
+// kept); the caller's workgroup barrier holds its other waves meanwhile.  A
+// waiting workgroup then sends one narrow load per round instead of one
+// per thread, which leaves the memory side to the workgroups still at
+// work.  It proves nothing about other words: the caller still polls every
+// word it takes, which by then has mostly arrived.
+__device__ __forceinline__ bool await_words(const uint64_t *p, int n, uint32_t tag, uint32_t *err,
+                                            long long spin_ticks) {
+  const int lane = threadIdx.x & 63;
+  float v;
+  return lane >= n || poll_tagged<1>(p + lane, tag, &v, err, spin_ticks);
+}
+
 }  // namespace q4

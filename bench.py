@@ -19,9 +19,9 @@ down q4mv + residual, then rmsq -> head q4mv -> argmax), captured once as a
 HIP graph, in ms per token over 200 tokens, for two engines: the fused
 per-stage kernels (2 per layer) and the persistent layer kernel (one launch
 for all layers); the attention step at positions 204 and 4095 of a 4096
-cache; the chain with an attention block in every layer (fused stages,
-200 tokens from position 0); and the CPU oracle timed on the host's cores
-on the head workload.
+cache; the chain with an attention block in every layer (200 tokens from
+position 0; fused stages, and one persistent launch per layer); and the
+CPU oracle timed on the host's cores on the head workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -316,19 +316,10 @@ def run_atq(args, q4, torch, synth):
     return out
 
 
-def run_attn_chain(args, q4, torch, synth):
-    """The decode chain with an attention block in every layer (fused
-    per-stage kernels, 5 per layer), one captured graph per token from
-    position 0 with empty caches: ms per token with the mailbox wait, and
-    the device time of the same number of queued replays."""
-    from affine_q4_matvec_amd.chain import AttnDecodeChain
-
-    log("generating the chain with attention (24 layers, seed %d)" % args.seed)
-    w = synth.attn_chain_weights(seed=args.seed)
-    mode = q4.FAST if args.mode == "fast" else q4.FIXED
-    chain = AttnDecodeChain(w, mode=mode)
-    tok0 = int(w["tok0"])
-    steps = min(args.chain_tokens, chain.max_pos)
+def time_attn_chain(args, q4, torch, chain, tok0, steps):
+    """One engine of the chain with attention: ms per token with the
+    mailbox wait, and the device time of the same number of queued
+    replays, from position 0 with empty caches."""
     stream = torch.cuda.Stream()
     chain.capture(stream)
     chain.run(0, 3, stream)  # warm-up tokens (not timed)
@@ -349,27 +340,51 @@ def run_attn_chain(args, q4, torch, synth):
     stream.synchronize()
     gpu_ms = e0.elapsed_time(e1) / steps
     last = int(chain.tok.cpu().numpy()[0])
-    golden = os.path.join(ROOT, "tests", "golden", "attn_chain_seed%d.json" % args.seed)
-    match = None
-    if os.path.exists(golden) and mode == q4.FIXED:
-        ref = json.load(open(golden))
-        n = min(len(ref["tokens"]), len(tokens))
-        match = bool(ref["tokens"][:n] == tokens[:n])
     out = {
-        "tokens": steps, "layers": len(chain.layers), "positions": "0..%d" % (steps - 1),
         "ms_per_token_with_mailbox_wait": round(per_token_ms, 4),
         "ms_per_token_gpu": round(gpu_ms, 4),
         "kernels_per_token": chain.kernels_per_token(),
-        "algorithmic_bytes_per_token_at_pos0": chain.bytes_per_token(),
-        "tokens_match_oracle_golden_prefix": match,
         "queued_replays_reach_same_last_token": last == tokens[-1],
         "distinct_tokens": len(set(tokens)),
         "attention_waits_ok": q4.q4_atq_status(chain.atq_ws, chain.hq, chain.hkv, stream) == q4.Q4_OK,
     }
-    log("attention chain: %s" % out)
-    del chain
-    torch.cuda.synchronize()
-    return out
+    if chain.persistent:
+        out["block_waits_ok"] = q4.q4_decode_block_status(chain.block_ws, stream) == q4.Q4_OK
+    return out, tokens
+
+
+def run_attn_chain(args, q4, torch, synth):
+    """The decode chain with an attention block in every layer, two
+    engines: the fused per-stage kernels (5 per layer) and one persistent
+    launch per layer (q4_decode_block); one captured graph per token from
+    position 0 with empty caches."""
+    from affine_q4_matvec_amd.chain import AttnDecodeChain
+
+    log("generating the chain with attention (24 layers, seed %d)" % args.seed)
+    w = synth.attn_chain_weights(seed=args.seed)
+    mode = q4.FAST if args.mode == "fast" else q4.FIXED
+    tok0 = int(w["tok0"])
+    steps = min(args.chain_tokens, int(w["max_pos"]))
+    golden = os.path.join(ROOT, "tests", "golden", "attn_chain_seed%d.json" % args.seed)
+    ref = json.load(open(golden)) if os.path.exists(golden) and mode == q4.FIXED else None
+    engines = {}
+    for name in ("fused", "persistent"):
+        chain = AttnDecodeChain(w, mode=mode, persistent=(name == "persistent"))
+        r, tokens = time_attn_chain(args, q4, torch, chain, tok0, steps)
+        if ref is not None:
+            n = min(len(ref["tokens"]), len(tokens))
+            r["tokens_match_oracle_golden_prefix"] = bool(ref["tokens"][:n] == tokens[:n])
+        engines[name] = r
+        log("attention chain %s: %s" % (name, r))
+        del chain
+        torch.cuda.synchronize()
+    best = min(engines, key=lambda k: engines[k]["ms_per_token_gpu"])
+    return {
+        "tokens": steps, "layers": len(w["layers"]), "positions": "0..%d" % (steps - 1),
+        "best_engine": best,
+        "best_ms_per_token_gpu": engines[best]["ms_per_token_gpu"],
+        "engines": engines,
+    }
 
 
 def chain_tok0(seed, synth):

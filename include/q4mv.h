@@ -297,6 +297,56 @@ int q4_atq(const float *q, const float *g, const float *k, const float *v, const
 int q4_atq_status(void *ws, int32_t hq, int32_t hkv, void *stream);
 
 /*
+ * One decoder layer of a decode token, the attention block and the MLP
+ * block, in one persistent launch ([P1] Change: rmsq, q4mv, atq and swq
+ * queued for a whole token; Verification: one command buffer and one wait).
+ * Computes, with the bits of the separate calls,
+ *   y = q4mv_norm(qgkv, h, wa)           [q; gate; k; v] = y
+ *   q4_atq(q, gate, k, v, wq, wk, eps, rope_cos, rope_sin, kcache, vcache,
+ *          pos, max_pos, 16, hkv, o, osum)
+ *   h = q4mv_add(o_mat, o, osum, h)
+ *   m = q4mv_norm_swiglu(mlp.gate_up, h, mlp.wn); h = q4mv_add(mlp.down, m, NULL, h)
+ * in one grid of one workgroup per compute unit (at least 256) whose stages
+ * hand their outputs to each other through tagged words in the workspace,
+ * with bounded waits (as q4_decode_layers).
+ *
+ *   blk->qgkv : rows (32 + 2 hkv) * 128, cols 2048: the 16 query heads'
+ *               rows, the 16 gate heads' rows, hkv key heads', hkv value
+ *               heads'.
+ *   blk->o    : rows 2048, cols 2048 (16 heads of 128 in).
+ *   blk->wa   : device float[2048] attention norm weights; wq, wk: float[128];
+ *               all 16-byte aligned.
+ *   blk->kcache, vcache : device float[hkv][max_pos][128], 16-byte aligned.
+ *   blk->hkv  : 1, 2, 4, 8 or 16 key/value heads.
+ *   blk->mlp  : as for q4_decode_layers (inter 2048..8192).
+ *   h         : device float[2048], 16-byte aligned, read and written.
+ *   pos       : device int32[1]; max_pos <= Q4_BLOCK_MAX_POS (one span);
+ *               rope_cos, rope_sin: device float[max_pos][64], 16-byte
+ *               aligned.  A position outside [0, max_pos) makes h NaN.
+ *   ws        : q4_decode_block_ws_bytes() bytes (about 1.3 MB), 16-byte
+ *               aligned, zero-filled before first use; one call at a time.
+ * q4_decode_block_status waits on the stream and reports a wait that ran
+ * out (Q4_ETIMEOUT, after clearing the workspace).
+ */
+#define Q4_BLOCK_MAX_POS 256
+typedef struct q4_attn_block {
+  q4_mat qgkv;
+  q4_mat o;
+  const float *wa;
+  const float *wq;
+  const float *wk;
+  float *kcache;
+  float *vcache;
+  int32_t hkv;
+  q4_mlp_layer mlp;
+} q4_attn_block;
+size_t q4_decode_block_ws_bytes(void);
+int q4_decode_block(const q4_attn_block *blk, float eps, float *h, const int32_t *pos,
+                    int32_t max_pos, const float *rope_cos, const float *rope_sin, void *ws,
+                    size_t ws_bytes, int mode, void *stream);
+int q4_decode_block_status(void *ws, void *stream);
+
+/*
  * q4_pos_advance: *pos += 1 on the device (one thread), so that a decode
  * token captured once as a graph moves its attention steps to the next
  * position on every replay ([P1] Verification: one command buffer per

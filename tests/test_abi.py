@@ -232,3 +232,75 @@ def test_atq_argument_checks(L):
     assert L.q4_pos_advance(ctypes.c_void_p(A + 2), None) == EINVAL
     assert L.q4_atq_status(ctypes.c_void_p(H), 16, 3, None) == EINVAL
     assert L.q4_atq_status(ctypes.c_void_p(H + 16), 16, 4, None) == EINVAL
+
+
+class AttnBlock(ctypes.Structure):
+    _fields_ = [("qgkv", Mat), ("o", Mat), ("wa", ctypes.c_void_p), ("wq", ctypes.c_void_p),
+                ("wk", ctypes.c_void_p), ("kcache", ctypes.c_void_p), ("vcache", ctypes.c_void_p),
+                ("hkv", ctypes.c_int32), ("mlp", MlpLayer)]
+
+
+def test_decode_block_argument_checks(L):
+    L.q4_decode_block_ws_bytes.restype = ctypes.c_size_t
+    wsb = L.q4_decode_block_ws_bytes()
+    assert 256 * 1024 <= wsb <= 4 * 1024 * 1024
+    G = 0x7F2000000000
+    slot = lambda i: G + i * 0x10000000  # disjoint 256 MiB regions
+    base = dict(hkv=4, qrows=(32 + 8) * 128, qcols=2048, orows=2048, inter=6144, gu_rows=12288,
+                wa=slot(9), wq=slot(10), wk=slot(11), kc=slot(12), vc=slot(13), wn=slot(14),
+                h=slot(15), pos=slot(16), max_pos=256, cs=slot(17), sn=slot(18), ws=slot(19),
+                wsb=wsb, mode=0)
+
+    def block(a):
+        b = AttnBlock()
+        b.qgkv = Mat(slot(0), slot(1), slot(2), a["qrows"], a["qcols"])
+        b.o = Mat(slot(3), slot(4), slot(5), a["orows"], 2048)
+        b.wa, b.wq, b.wk = a["wa"], a["wq"], a["wk"]
+        b.kcache, b.vcache, b.hkv = a["kc"], a["vc"], a["hkv"]
+        b.mlp.gate_up = Mat(slot(6), slot(6) + 0x8000000, slot(7), a["gu_rows"], 2048)
+        b.mlp.down = Mat(slot(8), slot(8) + 0x8000000, slot(7) + 0x8000000, 2048, a["inter"])
+        b.mlp.wn = a["wn"]
+        return b
+
+    def call(blk=True, **kw):
+        a = dict(base, **kw)
+        p = ctypes.c_void_p
+        b = ctypes.byref(block(a)) if blk else None
+        return L.q4_decode_block(b, ctypes.c_float(1e-6), p(a["h"]), p(a["pos"]), a["max_pos"],
+                                 p(a["cs"]), p(a["sn"]), p(a["ws"]), ctypes.c_size_t(a["wsb"]),
+                                 a["mode"], None)
+
+    import torch
+    if torch.cuda.device_count() == 0:
+        # the unchanged arguments pass every check and fail at the first HIP
+        # call, so each rejection below comes from the change it makes
+        assert call() not in (EINVAL, 0)
+    assert call(mode=2) == EINVAL
+    assert call(blk=False) == EINVAL
+    for hkv in (0, 3, 32):
+        assert call(hkv=hkv) == EINVAL, hkv
+    assert call(hkv=2) == EINVAL                        # [Q; gate; K; V] rows are those of 4
+    assert call(qcols=1024) == EINVAL
+    assert call(orows=4096) == EINVAL
+    assert call(inter=3000, gu_rows=6000) == EINVAL     # not a multiple of 2048
+    assert call(inter=10240, gu_rows=20480) == EINVAL   # wider than the limit
+    assert call(gu_rows=6144) == EINVAL                 # gate/up rows != 2 inter
+    assert call(wa=0) == EINVAL
+    assert call(wq=slot(10) + 4) == EINVAL              # norm weights misaligned
+    assert call(kc=slot(12) + 8) == EINVAL              # cache misaligned
+    assert call(h=slot(15) + 4) == EINVAL
+    assert call(pos=0) == EINVAL
+    assert call(pos=slot(16) + 2) == EINVAL
+    assert call(max_pos=0) == EINVAL
+    assert call(max_pos=257) == EINVAL                  # longer than one span
+    assert call(cs=0) == EINVAL
+    assert call(ws=slot(19) + 8) == EINVAL
+    assert call(wsb=wsb - 16) == EINVAL
+    assert call(vc=slot(12) + 4096) == EINVAL           # value cache inside the key cache
+    assert call(h=slot(19) + 1024) == EINVAL            # h inside the workspace
+    assert call(kc=slot(17) + 64) == EINVAL             # key cache over the cos table
+    assert call(ws=slot(3) + 4096) == EINVAL            # workspace over the O codes
+    assert call(h=slot(8) + 64) == EINVAL               # h inside the down codes
+    assert call(pos=slot(15) + 64) == EINVAL            # position inside h
+    assert L.q4_decode_block_status(None, None) == EINVAL
+    assert L.q4_decode_block_status(ctypes.c_void_p(slot(19) + 4), None) == EINVAL

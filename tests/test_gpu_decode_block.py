@@ -1,0 +1,121 @@
+"""GPU parity of the persistent decoder layer (q4_decode_block: the
+attention block and the MLP block of one layer in one launch whose stages
+hand their outputs to each other through tagged words), driven through
+AttnDecodeChain(persistent=True): step by step and as graph replays
+against the oracle's attn_chain_step, bit for bit, for 1 to 16 key/value
+heads; 64 tokens of the 24-layer chain against the oracle's golden file;
+its bounded waits; a position outside the cache."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_bits_equal, dev, host, lib
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = 16
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "attn_chain_seed20261202.json")
+
+
+def oracle_steps(w, steps, pos0=0):
+    kc, vc = oracle.attn_caches(w)
+    out, tok = [], w["tok0"]
+    for pos in range(pos0, pos0 + steps):
+        logits, tok = oracle.attn_chain_step(w, tok, pos, kc, vc, nthreads=NTHREADS)
+        out.append((tok, logits))
+    return out, kc, vc
+
+
+@pytest.mark.parametrize("hkv,use_graph", [(4, False), (4, True), (1, True), (2, False),
+                                           (16, True)])
+def test_block_chain_bit_exact(hkv, use_graph):
+    from affine_q4_matvec_amd.chain import AttnDecodeChain
+    print("decode block: 2 layers, hkv %d, graph %s" % (hkv, use_graph), flush=True)
+    w = synth.attn_chain_weights(seed=40 + hkv, layers=2, vocab=4096, hkv=hkv, max_pos=32)
+    want, kc, vc = oracle_steps(w, 5)
+    chain = AttnDecodeChain(w, persistent=True)
+    s = torch.cuda.Stream()
+    got = []
+    toks = chain.run(w["tok0"], 5, s, use_graph=use_graph,
+                     on_step=lambda i, c: got.append(host(c.logits)))
+    for i, (_, logits) in enumerate(want):
+        assert_bits_equal(got[i], logits, "step %d logits" % i)
+    assert toks == [t for t, _ in want]
+    for l, lw in enumerate(chain.layers):
+        assert_bits_equal(host(lw["kc"]).ravel(), kc[l].ravel(), "layer %d kcache" % l)
+        assert_bits_equal(host(lw["vc"]).ravel(), vc[l].ravel(), "layer %d vcache" % l)
+    assert lib().q4_decode_block_status(chain.block_ws, s) == lib().Q4_OK
+
+
+def test_block_chain_late_positions():
+    """Steps at positions 250..254 of a 256-position cache (the whole span)."""
+    from affine_q4_matvec_amd.chain import AttnDecodeChain
+    w = synth.attn_chain_weights(seed=45, layers=2, vocab=4096, max_pos=256)
+    want, kc, _ = oracle_steps(w, 5, pos0=250)
+    chain = AttnDecodeChain(w, persistent=True)
+    s = torch.cuda.Stream()
+    got = []
+    toks = chain.run(w["tok0"], 5, s, pos0=250, on_step=lambda i, c: got.append(host(c.logits)))
+    for i, (_, logits) in enumerate(want):
+        assert_bits_equal(got[i], logits, "step %d logits" % i)
+    assert toks == [t for t, _ in want]
+    assert_bits_equal(host(chain.layers[1]["kc"]).ravel(), kc[1].ravel(), "layer 1 kcache")
+
+
+def test_block_chain_24_layers_golden_tokens():
+    from affine_q4_matvec_amd.chain import AttnDecodeChain
+    g = json.load(open(GOLDEN))
+    print("decode block, 24 layers, %d golden tokens" % len(g["tokens"]), flush=True)
+    w = synth.attn_chain_weights(seed=g["seed"])
+    chain = AttnDecodeChain(w, persistent=True)
+    s = torch.cuda.Stream()
+    hashes = []
+    toks = chain.run(g["tok0"], len(g["tokens"]), s, wait="mailbox",
+                     on_step=lambda i, c: hashes.append(oracle.fnv1a32(host(c.logits))))
+    assert toks == g["tokens"]
+    assert hashes == g["logits_fnv1a32"]
+    assert lib().q4_decode_block_status(chain.block_ws, s) == lib().Q4_OK
+
+
+def test_block_waits_report_and_recover():
+    """With the wait bound at zero the hand-offs give up at their first
+    look: the status call reports Q4_ETIMEOUT and clears the workspace; the
+    next step with the normal bound is bit-exact."""
+    from affine_q4_matvec_amd.chain import AttnDecodeChain
+    q4 = lib()
+    w = synth.attn_chain_weights(seed=46, layers=2, vocab=4096, max_pos=16)
+    want, _, _ = oracle_steps(w, 1)
+    chain = AttnDecodeChain(w, persistent=True)
+    s = torch.cuda.Stream()
+    os.environ["Q4_DECODE_TIMEOUT_MS"] = "-1"
+    try:
+        chain.run(w["tok0"], 1, s, use_graph=False)
+    finally:
+        del os.environ["Q4_DECODE_TIMEOUT_MS"]
+    assert q4.q4_decode_block_status(chain.block_ws, s) == q4.Q4_ETIMEOUT
+    got = []
+    toks = chain.run(w["tok0"], 1, s, use_graph=False,
+                     on_step=lambda i, c: got.append(host(c.logits)))
+    assert toks == [want[0][0]]
+    assert_bits_equal(got[0], want[0][1], "after a timeout")
+    assert q4.q4_decode_block_status(chain.block_ws, s) == q4.Q4_OK
+
+
+def test_block_position_outside_the_cache():
+    from affine_q4_matvec_amd.chain import AttnDecodeChain
+    q4 = lib()
+    w = synth.attn_chain_weights(seed=47, layers=1, vocab=4096, max_pos=16)
+    chain = AttnDecodeChain(w, persistent=True)
+    h = dev(np.ones(2048, np.float32))
+    pos = torch.tensor([16], dtype=torch.int32, device="cuda")
+    q4.q4_decode_block(chain.layers[0]["blk"], chain.eps, h, pos, chain.cos_tab, chain.sin_tab,
+                       chain.block_ws)
+    assert q4.q4_decode_block_status(chain.block_ws) == q4.Q4_OK
+    assert np.all(np.isnan(host(h)))
+    assert not np.any(host(chain.layers[0]["kc"]))  # no cache row written
