@@ -21,7 +21,9 @@ __all__ = [
     "q4mv_norm_swiglu", "q4mv_norm_argmax", "q4mv_argmax_ws_bytes", "rmsq", "swq",
     "q4_argmax", "q4_argmax_ws_bytes", "q4_embed", "Queue", "Graph", "q4_sync",
     "MlpLayer", "q4_decode_layers", "q4_decode_layers_ws_bytes", "q4_decode_layers_status",
-    "Mailbox", "library_path",
+    "Mailbox", "library_path", "q4_atq", "q4_atq_ws_bytes", "q4_atq_status", "q4_pos_advance",
+    "AttnBlock", "BlockStack", "q4_decode_block", "q4_decode_blocks", "q4_decode_block_ws_bytes",
+    "q4_decode_block_status",
 ]
 
 FIXED = 0
@@ -90,6 +92,11 @@ _SIGS = {
     "q4_decode_block": ([ctypes.POINTER(_AttnBlock), ctypes.c_float, _vp, _vp, _i32, _vp, _vp, _vp,
                          ctypes.c_size_t, ctypes.c_int, _vp], ctypes.c_int),
     "q4_decode_block_status": ([_vp, _vp], ctypes.c_int),
+    "q4_block_stack_create": ([ctypes.POINTER(_AttnBlock), _i32, _i32, ctypes.POINTER(_vp)],
+                              ctypes.c_int),
+    "q4_block_stack_destroy": ([_vp], ctypes.c_int),
+    "q4_decode_blocks": ([_vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                          ctypes.c_int, _vp], ctypes.c_int),
     "q4_queue_create": ([_vp, ctypes.c_int, ctypes.POINTER(_vp)], ctypes.c_int),
     "q4_queue_destroy": ([_vp], ctypes.c_int),
     "q4mv_queue": ([_vp, ctypes.POINTER(_Mat), _vp, _vp, _vp], ctypes.c_int),
@@ -394,6 +401,7 @@ def q4_atq_status(ws: torch.Tensor, hq: int, hkv: int, stream=None) -> int:
 
 
 BLOCK_MAX_POS = 256
+BLOCK_MAX_LAYERS = 32
 
 
 class AttnBlock:
@@ -428,6 +436,52 @@ def q4_decode_block(blk: AttnBlock, eps: float, h: torch.Tensor, pos: torch.Tens
     _check("q4_decode_block", _lib.q4_decode_block(
         ctypes.byref(blk._c), float(eps), _dev(h, f, 2048, "h"), _dev(pos, torch.int32, 1, "pos"),
         max_pos, _dev(rope_cos, f, rn, "rope_cos"), _dev(rope_sin, f, rn, "rope_sin"),
+        _dev(ws, ws.dtype, None, "ws"), ws.numel() * ws.element_size(), mode, _stream(stream)))
+    return h
+
+
+class BlockStack:
+    """Decoder layers for one persistent launch (``q4_decode_blocks``): the
+    layers' pointers are copied once to a table in device memory (a
+    synchronous copy, so not under stream capture).  Holds references to
+    the layers, whose arrays must outlive it."""
+
+    def __init__(self, blocks: list):
+        blocks = list(blocks)
+        if not blocks:
+            raise ValueError("no layers")
+        self.blocks = blocks
+        self.max_pos = int(blocks[0].kcache.shape[1])
+        arr = (_AttnBlock * len(blocks))(*[b._c for b in blocks])
+        h = _vp()
+        _check("q4_block_stack_create",
+               _lib.q4_block_stack_create(arr, len(blocks), self.max_pos, ctypes.byref(h)))
+        self._h = h
+
+    def close(self) -> None:
+        if self._h is not None and self._h.value:
+            _check("q4_block_stack_destroy", _lib.q4_block_stack_destroy(self._h))
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def q4_decode_blocks(stack: BlockStack, eps: float, h: torch.Tensor, pos: torch.Tensor,
+                     rope_cos: torch.Tensor, rope_sin: torch.Tensor, ws: torch.Tensor,
+                     mode: int = FIXED, stream=None) -> torch.Tensor:
+    """Every layer of ``stack`` in one persistent launch, with the bits of
+    ``q4_decode_block`` called once per layer: ``h`` is read and written in
+    place; each layer's caches get row ``pos``.  ``ws`` as for
+    ``q4_decode_block``."""
+    f = torch.float32
+    rn = stack.max_pos * (ATQ_D // 2)
+    _check("q4_decode_blocks", _lib.q4_decode_blocks(
+        stack._h, float(eps), _dev(h, f, 2048, "h"), _dev(pos, torch.int32, 1, "pos"),
+        _dev(rope_cos, f, rn, "rope_cos"), _dev(rope_sin, f, rn, "rope_sin"),
         _dev(ws, ws.dtype, None, "ws"), ws.numel() * ws.element_size(), mode, _stream(stream)))
     return h
 

@@ -32,11 +32,11 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (ATQ_D, BLOCK_MAX_POS, FIXED, AttnBlock, Graph, Mailbox, MlpLayer, Q4Matrix,
-               q4_argmax, q4_argmax_ws_bytes, q4_atq, q4_atq_ws_bytes, q4_decode_block,
-               q4_decode_block_ws_bytes, q4_decode_layers, q4_decode_layers_ws_bytes, q4_embed,
-               q4_pos_advance, q4mv, q4mv_add, q4mv_argmax_ws_bytes, q4mv_norm, q4mv_norm_argmax,
-               q4mv_norm_swiglu, rmsq, swq)
+from . import (ATQ_D, BLOCK_MAX_LAYERS, BLOCK_MAX_POS, FIXED, AttnBlock, BlockStack, Graph,
+               Mailbox, MlpLayer, Q4Matrix, q4_argmax, q4_argmax_ws_bytes, q4_atq,
+               q4_atq_ws_bytes, q4_decode_block_ws_bytes, q4_decode_blocks, q4_decode_layers,
+               q4_decode_layers_ws_bytes, q4_embed, q4_pos_advance, q4mv, q4mv_add,
+               q4mv_argmax_ws_bytes, q4mv_norm, q4mv_norm_argmax, q4mv_norm_swiglu, rmsq, swq)
 
 
 def _stack_rows(a: dict, b: dict) -> dict:
@@ -214,9 +214,9 @@ class AttnDecodeChain(DecodeChain):
     replayed token after token; 2 + 5 per layer + 1 kernels.  The
     attention block is the product set's Q/K/V/O stages given their
     dataflow (the gate rows are an addition: the attention step gates its
-    output).  persistent=True runs each layer as one persistent launch
-    (q4_decode_block, caches of at most 256 positions): 1 + 1 per layer + 3
-    kernels, the same bits."""
+    output).  persistent=True runs every layer in one persistent launch
+    (q4_decode_blocks over stacks of at most 32 layers, caches of at most
+    256 positions): 4 kernels for up to 32 layers, the same bits."""
 
     def __init__(self, weights: dict, mode: int = FIXED, layers: int | None = None,
                  device: str = "cuda", persistent: bool = False):
@@ -268,13 +268,18 @@ class AttnDecodeChain(DecodeChain):
             for lw in self.layers:
                 lw["blk"] = AttnBlock(lw["qgkv"], lw["o"], lw["wa"], lw["wq"], lw["wk"], lw["kc"],
                                       lw["vc"], MlpLayer(lw["gu"], lw["down"], lw["wn"]))
+            blks = [lw["blk"] for lw in self.layers]
+            self.stacks = [BlockStack(blks[i:i + BLOCK_MAX_LAYERS])
+                           for i in range(0, len(blks), BLOCK_MAX_LAYERS)]
             self.block_ws = z((q4_decode_block_ws_bytes() + 7) // 8, dt=torch.int64)
         self.graph = None
         self.mailbox = None
         torch.cuda.synchronize()
 
     def kernels_per_token(self) -> int:
-        return (4 if self.persistent else 3) + (1 if self.persistent else 5) * len(self.layers)
+        if self.persistent:
+            return 3 + len(self.stacks)
+        return 3 + 5 * len(self.layers)
 
     def bytes_per_token(self) -> int:
         """Algorithmic bytes at position 0: every product's weights and
@@ -301,9 +306,9 @@ class AttnDecodeChain(DecodeChain):
     def enqueue_step(self, stream) -> None:
         q4_embed(self.head, self.tok, self.h, stream=stream)
         if self.persistent:
-            for lw in self.layers:
-                q4_decode_block(lw["blk"], self.eps, self.h, self.pos, self.cos_tab, self.sin_tab,
-                                self.block_ws, mode=self.mode, stream=stream)
+            for st in self.stacks:
+                q4_decode_blocks(st, self.eps, self.h, self.pos, self.cos_tab, self.sin_tab,
+                                 self.block_ws, mode=self.mode, stream=stream)
             q4mv_norm_argmax(self.head, self.h, self.wn_final, self.eps, self.logits, self.tok,
                              self.amax_ws, mode=self.mode, stream=stream)
             q4_pos_advance(self.pos, stream=stream)

@@ -1,9 +1,9 @@
-// One decoder layer of a decode token, attention block and MLP block, in
-// one persistent launch (gfx950): "Metal: queued rmsq, swq, gdn and atq
+// Decoder layers of a decode token, attention block and MLP block, in one
+// persistent launch (gfx950): "Metal: queued rmsq, swq, gdn and atq
 // kernels and a 4-row q4mv, so a decode token is one command buffer with
 // one wait" (#1440), Change (the rmsq, q4mv, atq and swq stages queued for
-// a whole token) and Verification (one command buffer, one wait).  The
-// same layer as the separate calls
+// a whole token) and Verification (one command buffer, one wait).  Each
+// layer is the same as the separate calls
 //   y = q4mv_norm(qgkv, h, wa)            [q; gate; k; v] = y
 //   o = q4_atq(q, gate, k, v, ...)        (16 query heads of 128)
 //   h = q4mv_add(O, o, osum, h)
@@ -21,11 +21,13 @@
 //   stage O    every wave: one O row + the residual -> tagged h
 //   stage A    every wave: rmsq(h, wn), its (gate, up) pairs, SwiGLU
 //                                                  -> tagged m
-//   stage B    every wave: one down row + the residual -> h (plain store)
-// Each hand-off buffer is written once per launch; the tags name the call
-// (a counter per workgroup) and the stage.  Every wait is bounded; one that
-// runs out sets the error word and every workgroup leaves at its next
-// wait.  Compiled with -ffp-contract=off.
+//   stage B    every wave: one down row + the residual -> tagged h for the
+//              next layer's stage Q, or h (plain store) after the last
+// The weights of a wave's next rows are loaded before the wait that
+// precedes them (the next layer's Q rows before the wait for m).  The
+// tags name the call (a counter per workgroup), the layer and the stage.
+// Every wait is bounded; one that runs out sets the error word and every
+// workgroup leaves at its next wait.  Compiled with -ffp-contract=off.
 #include <math.h>
 
 #include "decode_device.h"
@@ -56,11 +58,11 @@ struct Row {
   float sv, bv;
 };
 
-__device__ __forceinline__ void load_qrows(const DecodeBlockArgs &A, int r0, int nrows, int lane,
+__device__ __forceinline__ void load_qrows(const BlockLayer &Y, int r0, int nrows, int lane,
                                            QBlock &a) {
-  const auto qr = buffer(A.qq + (size_t)r0 * 256, nrows * 1024);
-  const auto sr = buffer(A.qs + (size_t)r0 * 32, nrows * 128);
-  const auto br = buffer(A.qb + (size_t)r0 * 32, nrows * 128);
+  const auto qr = buffer(Y.qq + (size_t)r0 * 256, nrows * 1024);
+  const auto sr = buffer(Y.qs + (size_t)r0 * 32, nrows * 128);
+  const auto br = buffer(Y.qb + (size_t)r0 * 32, nrows * 128);
 #pragma unroll
   for (int j = 0; j < kQRowsPerWave; ++j) {
     a.cw[j] = load_codes(qr, 16u * lane, j * 1024);
@@ -69,10 +71,10 @@ __device__ __forceinline__ void load_qrows(const DecodeBlockArgs &A, int r0, int
   }
 }
 
-__device__ __forceinline__ void load_orow(const DecodeBlockArgs &A, int r, int lane, Row &d) {
-  const auto qr = buffer(A.oq + (size_t)r * 256, 1024);
-  const auto sr = buffer(A.os + (size_t)r * 32, 128);
-  const auto br = buffer(A.ob + (size_t)r * 32, 128);
+__device__ __forceinline__ void load_orow(const BlockLayer &Y, int r, int lane, Row &d) {
+  const auto qr = buffer(Y.oq + (size_t)r * 256, 1024);
+  const auto sr = buffer(Y.os + (size_t)r * 32, 128);
+  const auto br = buffer(Y.ob + (size_t)r * 32, 128);
   d.cw = load_codes(qr, 16u * lane, 0);
   d.sv = load_f32(sr, 4u * (lane >> 1), 0);
   d.bv = load_f32(br, 4u * (lane >> 1), 0);
@@ -105,6 +107,7 @@ __device__ __forceinline__ float max64(float s) {
 
 struct AttnLds {
   float in[4][kD];          // q, gate, k, v of the head
+  float tab[3 * kD];        // q and k norm weights, then the rotation's cos and sin
   float un[2][kD];          // normed q, k
   float rot[2][kD];         // rotated q, k
   float s[kBlockMaxPos];    // scores
@@ -143,25 +146,78 @@ __device__ __forceinline__ bool stage_rows_input(Lds<NP> &L, const float (*vals)
   return pairs;
 }
 
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// The tags of layer l in call `call`: + 1 .. + 5 name the stage.
+__device__ __forceinline__ uint32_t stage_tag(uint32_t call, int l) {
+  return (call << 8) | ((uint32_t)l << 3);
+}
+
+// The layer table as the kernel reads it: the same layout as BlockLayer,
+// with pointers typed as global ones, so that loads through them are
+// global (or buffer) loads rather than flat loads of the generic address
+// space.
+#define Q4_GLOBAL __attribute__((address_space(1)))
+struct GlobalLayer {
+  const uint32_t Q4_GLOBAL *qq;
+  const float Q4_GLOBAL *qs, *qb;
+  const uint32_t Q4_GLOBAL *oq;
+  const float Q4_GLOBAL *os, *ob;
+  const float Q4_GLOBAL *wa, *wq, *wk;
+  float Q4_GLOBAL *kc, *vc;
+  const uint32_t Q4_GLOBAL *gq;
+  const float Q4_GLOBAL *gs, *gb, *wn;
+  const uint32_t Q4_GLOBAL *dq;
+  const float Q4_GLOBAL *ds, *db;
+};
+static_assert(sizeof(GlobalLayer) == sizeof(BlockLayer), "one layout");
+
+// Layer l: from the device layer table, else the one layer of the arguments.
+__device__ __forceinline__ BlockLayer layer_at(const DecodeBlockArgs &A, int l) {
+  GlobalLayer g;
+  if (A.layers) {
+    g = reinterpret_cast<const GlobalLayer *>(A.layers)[l];
+  } else {
+    const BlockLayer &o = A.one;
+    g = GlobalLayer{(const uint32_t Q4_GLOBAL *)o.qq, (const float Q4_GLOBAL *)o.qs,
+                    (const float Q4_GLOBAL *)o.qb, (const uint32_t Q4_GLOBAL *)o.oq,
+                    (const float Q4_GLOBAL *)o.os, (const float Q4_GLOBAL *)o.ob,
+                    (const float Q4_GLOBAL *)o.wa, (const float Q4_GLOBAL *)o.wq,
+                    (const float Q4_GLOBAL *)o.wk, (float Q4_GLOBAL *)o.kc,
+                    (float Q4_GLOBAL *)o.vc, (const uint32_t Q4_GLOBAL *)o.mlp.gq,
+                    (const float Q4_GLOBAL *)o.mlp.gs, (const float Q4_GLOBAL *)o.mlp.gb,
+                    (const float Q4_GLOBAL *)o.mlp.wn, (const uint32_t Q4_GLOBAL *)o.mlp.dq,
+                    (const float Q4_GLOBAL *)o.mlp.ds, (const float Q4_GLOBAL *)o.mlp.db};
+  }
+  BlockLayer y;
+  y.qq = (const uint32_t *)g.qq; y.qs = (const float *)g.qs; y.qb = (const float *)g.qb;
+  y.oq = (const uint32_t *)g.oq; y.os = (const float *)g.os; y.ob = (const float *)g.ob;
+  y.wa = (const float *)g.wa; y.wq = (const float *)g.wq; y.wk = (const float *)g.wk;
+  y.kc = (float *)g.kc; y.vc = (float *)g.vc;
+  y.mlp = DecodeLayer{(const uint32_t *)g.gq, (const float *)g.gs, (const float *)g.gb,
+                      (const float *)g.wn, (const uint32_t *)g.dq, (const float *)g.ds,
+                      (const float *)g.db};
+  return y;
+}
+
 template <bool FAST, int NP>
 __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs A) {
   __shared__ Lds<NP> S;  // h (stage A) or m (stage B)
-  __shared__ Lds<1> SO;  // o (stage O)
+  __shared__ Lds<1> SO;  // h between layers (stage Q) or o (stage O)
   __shared__ AttnLds T;
   const int nwg = gridDim.x;
   const int wg = blockIdx.x;
-  const int t = threadIdx.x;
-  const int lane = t & (kWave - 1);
   const int wave = wave_index();
   uint32_t *err = A.ctl + kBlockErrorWord;
   if (__syncthreads_or(load_word(err) != 0)) return;
   const uint32_t call = load_word(A.ctl + wg);
-  const uint32_t tag = call << 3;  // + 1 q/gate/k/v, + 2 o, + 3 h after attention, + 4 m
   const int gw = wave * nwg + wg;
   const int stride = kWaves * nwg;
   const int row = gw;
   const bool has_row = row < kCols;
-  const bool mine = 8 * t < kCols;
   const int copy = wg % kDecodeCopies;
   const int G = kHeads / A.hkv;
   const int nq = 2 * kCols + 2 * A.hkv * kD;
@@ -173,325 +229,382 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
   const bool pos_ok = pos >= 0 && pos < A.max_pos;
   const int n = pos_ok ? pos + 1 : 0;
   const int negz = neg_zero_reg();
-  const bool odd = lane & 1;
-
-  // ---- stage Q --------------------------------------------------------------
+  // the residual of the wave's row (lane 63): h before the first layer,
+  // carried from layer to layer
+  const int lane0 = threadIdx.x & (kWave - 1);
+  float res = has_row && lane0 == kWave - 1 ? A.h[row] : 0.0f;
   QBlock qa;
-  if (qb < qe) load_qrows(A, qb, qe - qb, lane, qa);
-  float hv[32], wv[32];
-  load_x_values(A.h + 32 * lane, true, hv);
-  load_x_values(A.wa + 32 * lane, true, wv);
-  // the residual of the wave's row (lane 63): h before the layer
-  float res = has_row && lane == kWave - 1 ? A.h[row] : 0.0f;
-  {
-    const float rho = ops::rmsq_rho_wave2048(hv, A.eps);
-    float xv[32];
-#pragma unroll
-    for (int k = 0; k < 32; ++k) xv[k] = ops::rmsq_value(hv[k], rho, wv[k]);
-    const float xsv = pair_group_sum(xv);
-    const bool pairs = prescale_for_pairs(xv);
-#pragma unroll
-    for (int i = 0; i < kQRowsPerWave; ++i) {
-      if (qb + i < qe) {  // uniform per wave
-        const float tv = pairs ? group_term<FAST, true>(qa.cw[i], xv, qa.sv[i], qa.bv[i], xsv, true, odd)
-                               : group_term<FAST, false>(qa.cw[i], xv, qa.sv[i], qa.bv[i], xsv, true, odd);
-        const float v = wave_sum_lane63(tv, negz);
-        if (lane == kWave - 1)
-#pragma unroll
-          for (int c = 0; c < kDecodeCopies; ++c)
-            store_tagged(A.qv + (size_t)c * kBlockQRows + qb + i, v, tag + 1);
-      }
-    }
-  }
-  Row od;
-  if (has_row) load_orow(A, row, lane, od);
-  issue_order();
+  if (qb < qe) load_qrows(layer_at(A, 0), qb, qe - qb, lane0, qa);
 
-  // ---- stage ATQ (workgroups 0..15, one query head each) --------------------
-  if (wg < kHeads) {
-    const int hd = wg, j = hd / G;
-    const int r = t >> 4, l = t & 15;  // scores: 32 positions per pass
-    // the cache rows below pos, loaded before the wait
-    float kv[8][8];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int tp = 32 * p + r;
-      if (tp < n && tp != pos) load8(A.kc + ((size_t)j * A.max_pos + tp) * kD + 8 * l, kv[p]);
-    }
-    const int cq = t & 31, pg = t >> 5;  // values: 4 columns x 16 positions
-    float v0[16], v1[16], v2[16], v3[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int p = 16 * pg + k;
-      float4 f = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if (p < n && p != pos)
-        f = reinterpret_cast<const float4 *>(A.vc + ((size_t)j * A.max_pos + p) * kD)[cq];
-      v0[k] = f.x;
-      v1[k] = f.y;
-      v2[k] = f.z;
-      v3[k] = f.w;
-    }
-    float nw[8], ct[8], st[8];
-    if (t < 32) {
-      load8((r == 0 ? A.wq : A.wk) + 8 * l, nw);
-      const int pr = pos_ok ? pos : 0;
-      load8(A.cs + (size_t)pr * (kD / 2) + 8 * (l & 7), ct);
-      load8(A.sn + (size_t)pr * (kD / 2) + 8 * (l & 7), st);
-    }
-    // q, gate (rows of this head), k, v (rows of its key/value head)
-    {
-      const int part = t / kD, i = t % kD;
-      const int src = part == 0   ? kD * hd + i
-                      : part == 1 ? kCols + kD * hd + i
-                      : part == 2 ? 2 * kCols + kD * j + i
-                                  : 2 * kCols + kD * A.hkv + kD * j + i;
-      float v = 0.0f;
-      const bool ok =
-          poll_tagged<1>(A.qv + (size_t)copy * kBlockQRows + src, tag + 1, &v, err, A.spin_ticks);
-      T.in[part][i] = v;
+  for (int l = 0; l < A.nlayers; ++l) {
+    // the thread index, opaque to the optimiser: the addresses and table
+    // loads derived from it stay in the layer instead of being hoisted out
+    // of the loop and held in registers through every stage
+    const int t = opaque(threadIdx.x);
+    const int lane = t & (kWave - 1);
+    const bool mine = 8 * t < kCols;
+    const bool odd = lane & 1;
+    const BlockLayer Y = layer_at(A, l);
+    // + 1 q/gate/k/v, + 2 o, + 3 h after attention, + 4 m, + 5 h after the layer
+    const uint32_t tag = stage_tag(call, l);
+
+    // ---- stage Q --------------------------------------------------------------
+    float hv[32], wv[32];
+    load_x_values(Y.wa + 32 * lane, true, wv);
+    if (l == 0) {
+      load_x_values(A.h + 32 * lane, true, hv);
+    } else {
+      // h after the previous layer: threads 0..255 fetch 8 values each
+      bool ok = true;
+      if (mine) {
+        float h8[8];
+        ok = poll_tagged<8>(A.hb + (size_t)copy * kCols + 8 * t, stage_tag(call, l - 1) + 5, h8,
+                            err, A.spin_ticks);
+        float4 *dst = reinterpret_cast<float4 *>(SO.x + 8 * t + 4 * (t >> 2));
+        dst[0] = make_float4(h8[0], h8[1], h8[2], h8[3]);
+        dst[1] = make_float4(h8[4], h8[5], h8[6], h8[7]);
+      }
       if (!__syncthreads_and(ok)) return;
+      load_x_values(SO.x + kChunkStride * lane, true, hv);
     }
-    // rmsq of q (row 0) and k (row 1), then the rotation
-    if (t < 32) {
-      float x[8], sq[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        x[k] = T.in[r == 0 ? 0 : 2][8 * l + k];
-        sq[k] = x[k] * x[k];
-      }
-      const float rho = ops::rmsq_rho_from_ss(sum16(ops::tree8(sq)), kD, A.eps);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) T.un[r][8 * l + k] = ops::rmsq_value(x[k], rho, nw[k]);
-    }
-    __syncthreads();
-    if (t < 32) {
-      float rv[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int d = 8 * l + k;
-        if (l < 8) {
-          const float a = T.un[r][d], b = T.un[r][d + kD / 2];
-          const float ac = a * ct[k], bs = b * st[k];
-          rv[k] = ac - bs;
-        } else {
-          const float a = T.un[r][d - kD / 2], b = T.un[r][d];
-          const float as = a * st[k], bc = b * ct[k];
-          rv[k] = as + bc;
-        }
-        T.rot[r][d] = rv[k];
-      }
-      if (r == 1 && hd % G == 0 && pos_ok) {  // the new cache rows
-        float4 *kd = reinterpret_cast<float4 *>(A.kc + ((size_t)j * A.max_pos + pos) * kD + 8 * l);
-        float4 *vd = reinterpret_cast<float4 *>(A.vc + ((size_t)j * A.max_pos + pos) * kD + 8 * l);
-        kd[0] = make_float4(rv[0], rv[1], rv[2], rv[3]);
-        kd[1] = make_float4(rv[4], rv[5], rv[6], rv[7]);
-        const float *nv = T.in[3] + 8 * l;
-        vd[0] = make_float4(nv[0], nv[1], nv[2], nv[3]);
-        vd[1] = make_float4(nv[4], nv[5], nv[6], nv[7]);
-      }
-    }
-    __syncthreads();
-    // scores
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int tp = 32 * p + r;
-      if (tp < n) {  // uniform over the 16 lanes of the position
-        float pr[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          pr[k] = T.rot[0][8 * l + k] * (tp == pos ? T.rot[1][8 * l + k] : kv[p][k]);
-        const float sc = sum16(ops::tree8(pr)) * kScale;
-        if (l == 0) T.s[tp] = sc;
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (64 * k + lane < n) m = fmaxf(m, T.s[64 * k + lane]);
-      m = max64(m);
-      if (lane == 0) T.m = m;
-    }
-    __syncthreads();
-    if (t < kBlockMaxPos) {
-      float e = kNegZero;
-      if (t < n) {
-        const float d = T.s[t] - T.m;
-        e = (float)ops::fixed_exp((double)d);
-      }
-      T.e[t] = e;
-      const float z = sum64(e);
-      if (lane == 0) T.wsum[wave] = z;
-    }
-    __syncthreads();
-    // the weighted value sums over 16 positions of 4 columns (the new row,
-    // at pos, from the inputs)
-    {
-      const int kp = pos - 16 * pg;  // the new row's slot in this thread's block, if any
-      if (kp >= 0 && kp < 16) {
-        const float4 nv = *reinterpret_cast<const float4 *>(&T.in[3][4 * cq]);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          if (k == kp) {
-            v0[k] = nv.x;
-            v1[k] = nv.y;
-            v2[k] = nv.z;
-            v3[k] = nv.w;
-          }
-        }
-      }
-      float ek[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) ek[k] = T.e[16 * pg + k];
-      const auto block16 = [&](const float *vc) {
-        float pr[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) pr[k] = 16 * pg + k < n ? ek[k] * vc[k] : kNegZero;
-        return ops::tree8(pr) + ops::tree8(pr + 8);
-      };
-      *reinterpret_cast<float4 *>(&T.part[pg][4 * cq]) =
-          make_float4(block16(v0), block16(v1), block16(v2), block16(v3));
-    }
-    __syncthreads();
-    if (t < kD) {
-      float pq[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) pq[k] = T.part[k][t];
-      const float w = ops::tree8(pq) + ops::tree8(pq + 8);
-      const float z = (T.wsum[0] + T.wsum[1]) + (T.wsum[2] + T.wsum[3]);
-      const double gd = (double)T.in[1][t];
-      const float sig = (float)(1.0 / (1.0 + ops::fixed_exp(-gd)));
-      const float ov = pos_ok ? (w / z) * sig : __builtin_nanf("");
-      const float gsum = sum64(ov);  // waves 0 and 1: the head's two groups
-#pragma unroll
-      for (int c = 0; c < kDecodeCopies; ++c) {
-        uint64_t *o = A.ov + (size_t)c * kBlockORows;
-        store_tagged(o + kD * hd + t, ov, tag + 2);
-        if (lane == 0) store_tagged(o + kCols + 2 * hd + wave, gsum, tag + 2);
-      }
-    }
-  }
-
-  // ---- stage O: h = h + O o ---------------------------------------------------
-  GuBlock a;
-  if (pb < pe) load_gu(A.mlp, pb, min(kGuPairs, pe - pb), lane, a);
-  issue_order();
-  {
-    float ov[2][8];
-    // the wait for the attention stage is long: wave 0 alone polls (the
-    // group sums of every head) until it ends, then every thread takes its
-    // words
-    bool ok = wave != 0 || await_words(A.ov + (size_t)copy * kBlockORows + kCols, 2 * kHeads,
-                                       tag + 2, err, A.spin_ticks);
-    if (!__syncthreads_and(ok)) return;
-    if (mine)
-      ok = poll_tagged<8>(A.ov + (size_t)copy * kBlockORows + 8 * t, tag + 2, ov[0], err,
-                          A.spin_ticks);
-    if (t >= 256 && t < 260)  // the 32 group sums, 8 per thread
-      ok = poll_tagged<8>(A.ov + (size_t)copy * kBlockORows + kCols + 8 * (t - 256), tag + 2,
-                          ov[1], err, A.spin_ticks);
-    if (!__syncthreads_and(ok)) return;
-    if (t >= 256 && t < 260)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) SO.xs[8 * (t - 256) + k] = ov[1][k];
-    // stage_rows_input looks at chunks t and t + 512 only: chunk t is this
-    // thread's 8 values of o
-    float vals[2][8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      vals[0][k] = mine ? ov[0][k] : 0.0f;
-      vals[1][k] = 0.0f;
-    }
-    const bool pairs = stage_rows_input<1>(SO, vals, kCols / 8);
-    __syncthreads();
-    if (has_row) {
-      Lds<1> &L = SO;
-      float xv[32];
-      load_x_values(L.x + lane * kChunkStride, true, xv);
-      const float xsv = L.xs[lane >> 1];
-      const float tv = pairs ? group_term<FAST, true>(od.cw, xv, od.sv, od.bv, xsv, true, odd)
-                             : group_term<FAST, false>(od.cw, xv, od.sv, od.bv, xsv, true, odd);
-      const float v = wave_sum_lane63(tv, negz);
-      if (lane == kWave - 1) {
-        res = res + v;
-#pragma unroll
-        for (int c = 0; c < kDecodeCopies; ++c)
-          store_tagged(A.hv + (size_t)c * kCols + row, res, tag + 3);
-      }
-    }
-  }
-
-  // ---- stage A: m = SwiGLU([gate; up] rmsq(h, wn)) --------------------------
-  load_x_values(A.mlp.wn + 32 * lane, true, wv);
-  {
-    bool ok = true;
-    if (mine) {
-      float h8[8];
-      ok = poll_tagged<8>(A.hv + (size_t)copy * kCols + 8 * t, tag + 3, h8, err, A.spin_ticks);
-      float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * t + 4 * (t >> 2));
-      dst[0] = make_float4(h8[0], h8[1], h8[2], h8[3]);
-      dst[1] = make_float4(h8[4], h8[5], h8[6], h8[7]);
-    }
-    issue_order();
-    DownRow<NP> d;
-    if (has_row) load_down<NP>(A.mlp, row, lane, d);
-    if (!__syncthreads_and(ok)) return;
-    load_x_values(S.x + kChunkStride * lane, true, hv);
     {
       const float rho = ops::rmsq_rho_wave2048(hv, A.eps);
       float xv[32];
 #pragma unroll
       for (int k = 0; k < 32; ++k) xv[k] = ops::rmsq_value(hv[k], rho, wv[k]);
       const float xsv = pair_group_sum(xv);
-      uint64_t *mq = A.mq;
-      const uint32_t tm = tag + 4;
-      const auto store_m = [mq, tm](int i, float v) {
+      const bool pairs = prescale_for_pairs(xv);
 #pragma unroll
-        for (int c = 0; c < kDecodeCopies; ++c) store_tagged(mq + c * kDecodeMaxInter + i, v, tm);
-      };
-      if (pb < pe) {
-        if (prescale_for_pairs(xv))
-          gu_stage<FAST, true>(A.mlp, xv, xsv, lane, pb, pe, a, store_m);
-        else
-          gu_stage<FAST, false>(A.mlp, xv, xsv, lane, pb, pe, a, store_m);
+      for (int i = 0; i < kQRowsPerWave; ++i) {
+        if (qb + i < qe) {  // uniform per wave
+          const float tv =
+              pairs ? group_term<FAST, true>(qa.cw[i], xv, qa.sv[i], qa.bv[i], xsv, true, odd)
+                    : group_term<FAST, false>(qa.cw[i], xv, qa.sv[i], qa.bv[i], xsv, true, odd);
+          const float v = wave_sum_lane63(tv, negz);
+          if (lane == kWave - 1)
+#pragma unroll
+            for (int c = 0; c < kDecodeCopies; ++c)
+              store_tagged(A.qv + (size_t)c * kBlockQRows + qb + i, v, tag + 1);
+        }
+      }
+    }
+    // (zero-initialised: a value loaded under a condition would otherwise
+    // be carried from the previous layer and held through every stage)
+    Row od{};
+    if (has_row) load_orow(Y, row, lane, od);
+    issue_order();
+
+    // ---- stage ATQ (workgroups 0..15, one query head each) --------------------
+    if (wg < kHeads) {
+      const int hd = wg, j = hd / G;
+      const int r = t >> 4, lq = t & 15;  // scores: 32 positions per pass
+      // the norm weights and the rotation table's row, for LDS below
+      float tv = 0.0f;
+      if (t < 2 * kD) {
+        tv = (t < kD ? Y.wq : Y.wk)[t % kD];
+      } else if (t < 3 * kD) {
+        const int pr = pos_ok ? pos : 0;
+        tv = (t < 5 * kD / 2 ? A.cs : A.sn)[(size_t)pr * (kD / 2) + t % (kD / 2)];
+      }
+      // the cache rows below n, loaded before the wait (bounded buffer
+      // loads: zeros from n on; row pos is stale here and not used)
+      const size_t hb = (size_t)j * A.max_pos * kD;
+      const auto kr = buffer(Y.kc + hb, (uint32_t)n * kD * 4u);
+      const auto vr = buffer(Y.vc + hb, (uint32_t)n * kD * 4u);
+      float kv[8][8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const uint32_t off = 4u * (uint32_t)((32 * p + r) * kD + 8 * lq);
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
+        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(kr, off + 16u, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          kv[p][k] = __uint_as_float(a[k]);
+          kv[p][k + 4] = __uint_as_float(b[k]);
+        }
+      }
+      const int cq = t & 31, pg = t >> 5;  // values: 4 columns x 16 positions
+      float v0[16], v1[16], v2[16], v3[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t off = 4u * (uint32_t)((16 * pg + k) * kD + 4 * cq);
+        const u32x4 f = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
+        v0[k] = __uint_as_float(f[0]);
+        v1[k] = __uint_as_float(f[1]);
+        v2[k] = __uint_as_float(f[2]);
+        v3[k] = __uint_as_float(f[3]);
+      }
+      if (t < 3 * kD) T.tab[t] = tv;  // waits for these loads only, not the cache rows
+      // q, gate (rows of this head), k, v (rows of its key/value head)
+      {
+        const int part = t / kD, i = t % kD;
+        const int src = part == 0   ? kD * hd + i
+                        : part == 1 ? kCols + kD * hd + i
+                        : part == 2 ? 2 * kCols + kD * j + i
+                                    : 2 * kCols + kD * A.hkv + kD * j + i;
+        float v = 0.0f;
+        const bool ok =
+            poll_tagged<1>(A.qv + (size_t)copy * kBlockQRows + src, tag + 1, &v, err, A.spin_ticks);
+        T.in[part][i] = v;
+        if (!__syncthreads_and(ok)) return;
+      }
+      // rmsq of q (row 0) and k (row 1), then the rotation
+      if (t < 32) {
+        float x[8], sq[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          x[k] = T.in[r == 0 ? 0 : 2][8 * lq + k];
+          sq[k] = x[k] * x[k];
+        }
+        const float rho = ops::rmsq_rho_from_ss(sum16(ops::tree8(sq)), kD, A.eps);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          T.un[r][8 * lq + k] = ops::rmsq_value(x[k], rho, T.tab[kD * r + 8 * lq + k]);
+      }
+      __syncthreads();
+      if (t < 32) {
+        const float *ct = T.tab + 2 * kD + 8 * (lq & 7), *st = ct + kD / 2;
+        float rv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int d = 8 * lq + k;
+          if (lq < 8) {
+            const float a = T.un[r][d], b = T.un[r][d + kD / 2];
+            const float ac = a * ct[k], bs = b * st[k];
+            rv[k] = ac - bs;
+          } else {
+            const float a = T.un[r][d - kD / 2], b = T.un[r][d];
+            const float as = a * st[k], bc = b * ct[k];
+            rv[k] = as + bc;
+          }
+          T.rot[r][d] = rv[k];
+        }
+        if (r == 1 && hd % G == 0 && pos_ok) {  // the new cache rows
+          const size_t at = ((size_t)j * A.max_pos + pos) * kD + 8 * lq;
+          float4 *kd = reinterpret_cast<float4 *>(Y.kc + at);
+          float4 *vd = reinterpret_cast<float4 *>(Y.vc + at);
+          kd[0] = make_float4(rv[0], rv[1], rv[2], rv[3]);
+          kd[1] = make_float4(rv[4], rv[5], rv[6], rv[7]);
+          const float *nv = T.in[3] + 8 * lq;
+          vd[0] = make_float4(nv[0], nv[1], nv[2], nv[3]);
+          vd[1] = make_float4(nv[4], nv[5], nv[6], nv[7]);
+        }
+      }
+      __syncthreads();
+      // scores
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int tp = 32 * p + r;
+        if (tp < n) {  // uniform over the 16 lanes of the position
+          float pr[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            pr[k] = T.rot[0][8 * lq + k] * (tp == pos ? T.rot[1][8 * lq + k] : kv[p][k]);
+          const float sc = sum16(ops::tree8(pr)) * kScale;
+          if (lq == 0) T.s[tp] = sc;
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (64 * k + lane < n) m = fmaxf(m, T.s[64 * k + lane]);
+        m = max64(m);
+        if (lane == 0) T.m = m;
+      }
+      __syncthreads();
+      if (t < kBlockMaxPos) {
+        float e = kNegZero;
+        if (t < n) {
+          const float d = T.s[t] - T.m;
+          e = (float)ops::fixed_exp((double)d);
+        }
+        T.e[t] = e;
+        const float z = sum64(e);
+        if (lane == 0) T.wsum[wave] = z;
+      }
+      __syncthreads();
+      // the weighted value sums over 16 positions of 4 columns (the new row,
+      // at pos, from the inputs)
+      {
+        const int kp = pos - 16 * pg;  // the new row's slot in this thread's block, if any
+        if (kp >= 0 && kp < 16) {
+          const float4 nv = *reinterpret_cast<const float4 *>(&T.in[3][4 * cq]);
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            if (k == kp) {
+              v0[k] = nv.x;
+              v1[k] = nv.y;
+              v2[k] = nv.z;
+              v3[k] = nv.w;
+            }
+          }
+        }
+        float ek[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) ek[k] = T.e[16 * pg + k];
+        const auto block16 = [&](const float *vc) {
+          float pr[16];
+#pragma unroll
+          for (int k = 0; k < 16; ++k) pr[k] = 16 * pg + k < n ? ek[k] * vc[k] : kNegZero;
+          return ops::tree8(pr) + ops::tree8(pr + 8);
+        };
+        *reinterpret_cast<float4 *>(&T.part[pg][4 * cq]) =
+            make_float4(block16(v0), block16(v1), block16(v2), block16(v3));
+      }
+      __syncthreads();
+      if (t < kD) {
+        float pq[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) pq[k] = T.part[k][t];
+        const float w = ops::tree8(pq) + ops::tree8(pq + 8);
+        const float z = (T.wsum[0] + T.wsum[1]) + (T.wsum[2] + T.wsum[3]);
+        const double gd = (double)T.in[1][t];
+        const float sig = (float)(1.0 / (1.0 + ops::fixed_exp(-gd)));
+        const float ov = pos_ok ? (w / z) * sig : __builtin_nanf("");
+        const float gsum = sum64(ov);  // waves 0 and 1: the head's two groups
+#pragma unroll
+        for (int c = 0; c < kDecodeCopies; ++c) {
+          uint64_t *o = A.ov + (size_t)c * kBlockORows;
+          store_tagged(o + kD * hd + t, ov, tag + 2);
+          if (lane == 0) store_tagged(o + kCols + 2 * hd + wave, gsum, tag + 2);
+        }
       }
     }
 
-    // ---- stage B: h = h + down m ---------------------------------------------
-    constexpr int kChunks = NP * kCols / 8;
-    float xm[2][8];
-    ok = true;
-    __syncthreads();  // every wave of the workgroup is done with stage A
+    // ---- stage O: h = h + O o ---------------------------------------------------
+    GuBlock a{};
+    if (pb < pe) load_gu(Y.mlp, pb, min(kGuPairs, pe - pb), lane, a);
+    issue_order();
+    {
+      float ov[2][8] = {};
+      // the wait for the attention stage is long: wave 0 alone polls (the
+      // group sums of every head) until it ends, then every thread takes its
+      // words
+      bool ok = wave != 0 || await_words(A.ov + (size_t)copy * kBlockORows + kCols, 2 * kHeads,
+                                         tag + 2, err, A.spin_ticks);
+      if (!__syncthreads_and(ok)) return;
+      if (mine)
+        ok = poll_tagged<8>(A.ov + (size_t)copy * kBlockORows + 8 * t, tag + 2, ov[0], err,
+                            A.spin_ticks);
+      if (t >= 256 && t < 260)  // the 32 group sums, 8 per thread
+        ok = poll_tagged<8>(A.ov + (size_t)copy * kBlockORows + kCols + 8 * (t - 256), tag + 2,
+                            ov[1], err, A.spin_ticks);
+      if (!__syncthreads_and(ok)) return;
+      if (t >= 256 && t < 260)
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int c = t + rr * kThreads;
-      if (c < kChunks)
-        ok &= poll_tagged<8>(A.mq + (size_t)copy * kDecodeMaxInter + 8 * c, tag + 4, xm[rr], err,
-                             A.spin_ticks);
-    }
-    if (!__syncthreads_and(ok)) return;
-    // group sums: T over each chunk, then over 8 chunks by a butterfly
+        for (int k = 0; k < 8; ++k) SO.xs[8 * (t - 256) + k] = ov[1][k];
+      // stage_rows_input looks at chunks t and t + 512 only: chunk t is this
+      // thread's 8 values of o
+      float vals[2][8];
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int c = t + rr * kThreads;
-      if (rr * kThreads < kChunks) {  // uniform per round
-        float gs = c < kChunks ? ops::tree8(xm[rr]) : 0.0f;
-        gs = gs + __shfl_xor(gs, 1);
-        gs = gs + __shfl_xor(gs, 2);
-        gs = gs + __shfl_xor(gs, 4);
-        if (c < kChunks && (c & 7) == 0) S.xs[c >> 3] = gs;
+      for (int k = 0; k < 8; ++k) {
+        vals[0][k] = mine ? ov[0][k] : 0.0f;
+        vals[1][k] = 0.0f;
+      }
+      const bool pairs = stage_rows_input<1>(SO, vals, kCols / 8);
+      __syncthreads();
+      if (has_row) {
+        Lds<1> &L = SO;
+        float xv[32];
+        load_x_values(L.x + lane * kChunkStride, true, xv);
+        const float xsv = L.xs[lane >> 1];
+        const float tv = pairs ? group_term<FAST, true>(od.cw, xv, od.sv, od.bv, xsv, true, odd)
+                               : group_term<FAST, false>(od.cw, xv, od.sv, od.bv, xsv, true, odd);
+        const float v = wave_sum_lane63(tv, negz);
+        if (lane == kWave - 1) {
+          res = res + v;
+#pragma unroll
+          for (int c = 0; c < kDecodeCopies; ++c)
+            store_tagged(A.hv + (size_t)c * kCols + row, res, tag + 3);
+        }
       }
     }
-    const bool pairs = stage_rows_input<NP>(S, xm, kChunks);
-    __syncthreads();
-    if (has_row) {
-      const float v = pairs ? down_row<NP, FAST, true>(S, lane, d) : down_row<NP, FAST, false>(S, lane, d);
-      if (lane == kWave - 1) A.h[row] = res + v;
+
+    // ---- stage A: m = SwiGLU([gate; up] rmsq(h, wn)) --------------------------
+    load_x_values(Y.mlp.wn + 32 * lane, true, wv);
+    {
+      bool ok = true;
+      if (mine) {
+        float h8[8];
+        ok = poll_tagged<8>(A.hv + (size_t)copy * kCols + 8 * t, tag + 3, h8, err, A.spin_ticks);
+        float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * t + 4 * (t >> 2));
+        dst[0] = make_float4(h8[0], h8[1], h8[2], h8[3]);
+        dst[1] = make_float4(h8[4], h8[5], h8[6], h8[7]);
+      }
+      issue_order();
+      DownRow<NP> d{};
+      if (has_row) load_down<NP>(Y.mlp, row, lane, d);
+      if (!__syncthreads_and(ok)) return;
+      load_x_values(S.x + kChunkStride * lane, true, hv);
+      {
+        const float rho = ops::rmsq_rho_wave2048(hv, A.eps);
+        float xv[32];
+#pragma unroll
+        for (int k = 0; k < 32; ++k) xv[k] = ops::rmsq_value(hv[k], rho, wv[k]);
+        const float xsv = pair_group_sum(xv);
+        uint64_t *mq = A.mq;
+        const uint32_t tm = tag + 4;
+        const auto store_m = [mq, tm](int i, float v) {
+#pragma unroll
+          for (int c = 0; c < kDecodeCopies; ++c) store_tagged(mq + c * kDecodeMaxInter + i, v, tm);
+        };
+        if (pb < pe) {
+          if (prescale_for_pairs(xv))
+            gu_stage<FAST, true>(Y.mlp, xv, xsv, lane, pb, pe, a, store_m);
+          else
+            gu_stage<FAST, false>(Y.mlp, xv, xsv, lane, pb, pe, a, store_m);
+        }
+      }
+
+      // ---- stage B: h = h + down m ---------------------------------------------
+      constexpr int kChunks = NP * kCols / 8;
+      float xm[2][8] = {};
+      ok = true;
+      __syncthreads();  // every wave of the workgroup is done with stage A
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int c = t + rr * kThreads;
+        if (c < kChunks)
+          ok &= poll_tagged<8>(A.mq + (size_t)copy * kDecodeMaxInter + 8 * c, tag + 4, xm[rr], err,
+                               A.spin_ticks);
+      }
+      if (!__syncthreads_and(ok)) return;
+      // group sums: T over each chunk, then over 8 chunks by a butterfly
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int c = t + rr * kThreads;
+        if (rr * kThreads < kChunks) {  // uniform per round
+          float gs = c < kChunks ? ops::tree8(xm[rr]) : 0.0f;
+          gs = gs + __shfl_xor(gs, 1);
+          gs = gs + __shfl_xor(gs, 2);
+          gs = gs + __shfl_xor(gs, 4);
+          if (c < kChunks && (c & 7) == 0) S.xs[c >> 3] = gs;
+        }
+      }
+      const bool pairs = stage_rows_input<NP>(S, xm, kChunks);
+      __syncthreads();
+      if (has_row) {
+        const float v =
+            pairs ? down_row<NP, FAST, true>(S, lane, d) : down_row<NP, FAST, false>(S, lane, d);
+        if (lane == kWave - 1) {
+          res = res + v;
+          if (l + 1 < A.nlayers) {
+#pragma unroll
+            for (int c = 0; c < kDecodeCopies; ++c)
+              store_tagged(A.hb + (size_t)c * kCols + row, res, tag + 5);
+          } else {
+            A.h[row] = res;
+          }
+        }
+      }
     }
-  }
+    // the next layer's [Q; gate; K; V] rows, in flight during the wait for h
+    if (l + 1 < A.nlayers && qb < qe) load_qrows(layer_at(A, l + 1), qb, qe - qb, lane, qa);
+  }  // layers
   __syncthreads();
-  if (t == 0) store_word(A.ctl + wg, call + 1);
+  if (threadIdx.x == 0) store_word(A.ctl + wg, call + 1);
 }
 
 template <bool FAST, int NP>

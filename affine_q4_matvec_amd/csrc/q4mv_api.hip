@@ -499,70 +499,224 @@ int q4_atq(const float *q, const float *g, const float *k, const float *v, const
 
 size_t q4_decode_block_ws_bytes(void) { return q4::kBlockWsBytes; }
 
-int q4_decode_block(const q4_attn_block *blk, float eps, float *h, const int32_t *pos,
-                    int32_t max_pos, const float *rope_cos, const float *rope_sin, void *ws,
-                    size_t ws_bytes, int mode, void *stream) {
-  if (mode != Q4_FIXED && mode != Q4_FAST) return Q4_EINVAL;
-  if (!blk) return Q4_EINVAL;
-  const int32_t hkv = blk->hkv;
+namespace {
+
+size_t cache_bytes(const q4_attn_block &b, int32_t max_pos) {
+  return sizeof(float) * (size_t)b.hkv * (size_t)max_pos * q4::kAtqD;
+}
+
+// The checks of one block that do not depend on the call: shapes,
+// alignment, and its two caches apart.  Sets *inter.
+int check_block(const q4_attn_block &b, int32_t max_pos, int32_t *inter) {
+  const int32_t hkv = b.hkv;
   if (hkv < 1 || hkv > q4::kBlockHeads || q4::kBlockHeads % hkv != 0) return Q4_EINVAL;
-  if (check_mat(&blk->qgkv) != Q4_OK || check_mat(&blk->o) != Q4_OK) return Q4_EINVAL;
-  if (blk->qgkv.cols != 2048 || blk->qgkv.rows != (2 * q4::kBlockHeads + 2 * hkv) * q4::kAtqD)
+  if (check_mat(&b.qgkv) != Q4_OK || check_mat(&b.o) != Q4_OK) return Q4_EINVAL;
+  if (b.qgkv.cols != 2048 || b.qgkv.rows != (2 * q4::kBlockHeads + 2 * hkv) * q4::kAtqD)
     return Q4_EINVAL;
-  if (blk->o.rows != 2048 || blk->o.cols != 2048) return Q4_EINVAL;
-  const q4_mlp_layer &L = blk->mlp;
+  if (b.o.rows != 2048 || b.o.cols != 2048) return Q4_EINVAL;
+  const q4_mlp_layer &L = b.mlp;
   if (check_mat(&L.gate_up) != Q4_OK || check_mat(&L.down) != Q4_OK) return Q4_EINVAL;
-  const int32_t inter = L.down.cols;
-  if (inter < 2048 || inter % 2048 != 0 || inter > q4::kDecodeMaxInter) return Q4_EINVAL;
-  if (L.gate_up.cols != 2048 || L.gate_up.rows != 2 * inter || L.down.rows != 2048)
+  const int32_t in = L.down.cols;
+  if (in < 2048 || in % 2048 != 0 || in > q4::kDecodeMaxInter) return Q4_EINVAL;
+  if (L.gate_up.cols != 2048 || L.gate_up.rows != 2 * in || L.down.rows != 2048)
     return Q4_EINVAL;
-  const float *in16[6] = {blk->wa, blk->wq, blk->wk, L.wn, rope_cos, rope_sin};
-  for (int i = 0; i < 6; ++i)
-    if (!in16[i] || !aligned(in16[i], 16)) return Q4_EINVAL;
-  if (!blk->kcache || !blk->vcache || !aligned(blk->kcache, 16) || !aligned(blk->vcache, 16))
+  const float *w[4] = {b.wa, b.wq, b.wk, L.wn};
+  for (int i = 0; i < 4; ++i)
+    if (!w[i] || !aligned(w[i], 16)) return Q4_EINVAL;
+  if (!b.kcache || !b.vcache || !aligned(b.kcache, 16) || !aligned(b.vcache, 16))
     return Q4_EINVAL;
-  if (!h || !aligned(h, 16) || !pos || !aligned(pos, 4)) return Q4_EINVAL;
   if (max_pos < 1 || max_pos > q4::kBlockMaxPos) return Q4_EINVAL;
-  if (!ws || !aligned(ws, 16) || ws_bytes < q4::kBlockWsBytes) return Q4_EINVAL;
-  const size_t D = q4::kAtqD;
-  const size_t hb = sizeof(float) * 2048, wb = sizeof(float) * D;
-  const size_t cb = sizeof(float) * (size_t)hkv * (size_t)max_pos * D;
-  const size_t rb = sizeof(float) * (size_t)max_pos * D / 2;
-  // written: h (in place), the caches, the workspace
-  const void *outs[4] = {h, blk->kcache, blk->vcache, ws};
-  const size_t outb[4] = {hb, cb, cb, q4::kBlockWsBytes};
-  const void *ins[7] = {blk->wa, blk->wq, blk->wk, L.wn, rope_cos, rope_sin, pos};
-  const size_t inb[7] = {hb, wb, wb, hb, rb, rb, sizeof(int32_t)};
-  const q4_mat *mats[4] = {&blk->qgkv, &blk->o, &L.gate_up, &L.down};
-  for (int i = 0; i < 4; ++i) {
-    for (int m = i + 1; m < 4; ++m)
-      if (overlap(outs[i], outb[i], outs[m], outb[m])) return Q4_EINVAL;
-    for (int m = 0; m < 7; ++m)
-      if (overlap(outs[i], outb[i], ins[m], inb[m])) return Q4_EINVAL;
-    for (int m = 0; m < 4; ++m)
-      if (overlaps_mat(outs[i], outb[i], mats[m])) return Q4_EINVAL;
+  const size_t cb = cache_bytes(b, max_pos);
+  if (overlap(b.kcache, cb, b.vcache, cb)) return Q4_EINVAL;
+  *inter = in;
+  return Q4_OK;
+}
+
+// Does [p, p + bytes) overlap an array that the block only reads?
+bool overlaps_weights(const void *p, size_t bytes, const q4_attn_block &b) {
+  const size_t hb = sizeof(float) * 2048, wb = sizeof(float) * q4::kAtqD;
+  return overlap(p, bytes, b.wa, hb) || overlap(p, bytes, b.wq, wb) ||
+         overlap(p, bytes, b.wk, wb) || overlap(p, bytes, b.mlp.wn, hb) ||
+         overlaps_mat(p, bytes, &b.qgkv) || overlaps_mat(p, bytes, &b.o) ||
+         overlaps_mat(p, bytes, &b.mlp.gate_up) || overlaps_mat(p, bytes, &b.mlp.down);
+}
+
+// Does [p, p + bytes) overlap any array of the block?
+bool overlaps_block(const void *p, size_t bytes, const q4_attn_block &b, int32_t max_pos) {
+  const size_t cb = cache_bytes(b, max_pos);
+  return overlap(p, bytes, b.kcache, cb) || overlap(p, bytes, b.vcache, cb) ||
+         overlaps_weights(p, bytes, b);
+}
+
+// Each block's caches (written) overlap no other array of any block.
+int check_caches(const q4_attn_block *b, int32_t n, int32_t max_pos) {
+  for (int32_t i = 0; i < n; ++i) {
+    const size_t cb = cache_bytes(b[i], max_pos);
+    for (int32_t j = 0; j < n; ++j) {
+      if (overlaps_weights(b[i].kcache, cb, b[j]) || overlaps_weights(b[i].vcache, cb, b[j]))
+        return Q4_EINVAL;
+      if (j != i && (overlaps_block(b[i].kcache, cb, b[j], max_pos) ||
+                     overlaps_block(b[i].vcache, cb, b[j], max_pos)))
+        return Q4_EINVAL;
+    }
   }
+  return Q4_OK;
+}
+
+// The arguments of one call: h and the workspace (written) overlap nothing
+// else; the caches overlap none of the call's inputs.
+int check_block_call(const q4_attn_block *b, int32_t n, int32_t max_pos, const float *h,
+                     const int32_t *pos, const float *cs, const float *sn, const void *ws,
+                     size_t ws_bytes) {
+  if (!h || !aligned(h, 16) || !pos || !aligned(pos, 4)) return Q4_EINVAL;
+  if (!cs || !sn || !aligned(cs, 16) || !aligned(sn, 16)) return Q4_EINVAL;
+  if (!ws || !aligned(ws, 16) || ws_bytes < q4::kBlockWsBytes) return Q4_EINVAL;
+  const size_t hb = sizeof(float) * 2048, wsb = q4::kBlockWsBytes;
+  const size_t rb = sizeof(float) * (size_t)max_pos * q4::kAtqD / 2;
+  if (overlap(h, hb, ws, wsb)) return Q4_EINVAL;
+  const void *ins[3] = {cs, sn, pos};
+  const size_t inb[3] = {rb, rb, sizeof(int32_t)};
+  for (int m = 0; m < 3; ++m)
+    if (overlap(h, hb, ins[m], inb[m]) || overlap(ws, wsb, ins[m], inb[m])) return Q4_EINVAL;
+  for (int32_t i = 0; i < n; ++i) {
+    if (overlaps_block(h, hb, b[i], max_pos) || overlaps_block(ws, wsb, b[i], max_pos))
+      return Q4_EINVAL;
+    const size_t cb = cache_bytes(b[i], max_pos);
+    for (int m = 0; m < 3; ++m)
+      if (overlap(b[i].kcache, cb, ins[m], inb[m]) || overlap(b[i].vcache, cb, ins[m], inb[m]))
+        return Q4_EINVAL;
+  }
+  return Q4_OK;
+}
+
+q4::BlockLayer block_layer(const q4_attn_block &b) {
+  q4::BlockLayer y;
+  y.qq = b.qgkv.q; y.qs = b.qgkv.s; y.qb = b.qgkv.b;
+  y.oq = b.o.q; y.os = b.o.s; y.ob = b.o.b;
+  y.wa = b.wa; y.wq = b.wq; y.wk = b.wk;
+  y.kc = b.kcache; y.vc = b.vcache;
+  const q4_mlp_layer &L = b.mlp;
+  y.mlp = q4::DecodeLayer{L.gate_up.q, L.gate_up.s, L.gate_up.b, L.wn, L.down.q, L.down.s, L.down.b};
+  return y;
+}
+
+int launch_blocks(const q4::BlockLayer &one, const q4::BlockLayer *table, int32_t n, int32_t hkv,
+                  int32_t inter, int32_t max_pos, float eps, float *h, const int32_t *pos,
+                  const float *cs, const float *sn, void *ws, int mode, void *stream) {
   q4::DecodeBlockArgs a;
   memset(&a, 0, sizeof(a));
-  a.qq = blk->qgkv.q; a.qs = blk->qgkv.s; a.qb = blk->qgkv.b;
-  a.oq = blk->o.q; a.os = blk->o.s; a.ob = blk->o.b;
-  a.wa = blk->wa; a.wq = blk->wq; a.wk = blk->wk;
-  a.kc = blk->kcache; a.vc = blk->vcache;
-  a.cs = rope_cos; a.sn = rope_sin; a.pos = pos;
-  a.max_pos = max_pos; a.hkv = hkv;
-  a.mlp = q4::DecodeLayer{L.gate_up.q, L.gate_up.s, L.gate_up.b, L.wn, L.down.q, L.down.s, L.down.b};
-  a.inter = inter;
+  a.one = one;
+  a.layers = table;
+  a.nlayers = n;
+  a.cs = cs; a.sn = sn; a.pos = pos;
+  a.max_pos = max_pos; a.hkv = hkv; a.inter = inter;
   a.h = h;
   char *w = static_cast<char *>(ws);
   a.qv = reinterpret_cast<uint64_t *>(w + q4::kBlockQvOffset);
   a.ov = reinterpret_cast<uint64_t *>(w + q4::kBlockOvOffset);
   a.hv = reinterpret_cast<uint64_t *>(w + q4::kBlockHvOffset);
   a.mq = reinterpret_cast<uint64_t *>(w + q4::kBlockMqOffset);
+  a.hb = reinterpret_cast<uint64_t *>(w + q4::kBlockHbOffset);
   a.ctl = reinterpret_cast<uint32_t *>(w + q4::kBlockCtlOffset);
   a.eps = eps;
   if (wait_ticks(&a.spin_ticks) != Q4_OK) return Q4_EHIP;
   if (q4::decode_block_grid(mode, inter) < 1) return Q4_EINVAL;  // too few compute units
   return hip_status(q4::launch_decode_block(a, mode, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+struct q4_block_stack {
+  // host copy, for the checks of each call (a plain array: a template
+  // instantiated on the public type would be exported)
+  q4_attn_block *blocks = nullptr;
+  int32_t n = 0;
+  q4::BlockLayer *table = nullptr;  // device copy of the layers' arrays
+  int32_t max_pos = 0, inter = 0;
+  ~q4_block_stack() { delete[] blocks; }
+};
+
+int q4_decode_block(const q4_attn_block *blk, float eps, float *h, const int32_t *pos,
+                    int32_t max_pos, const float *rope_cos, const float *rope_sin, void *ws,
+                    size_t ws_bytes, int mode, void *stream) {
+  if (mode != Q4_FIXED && mode != Q4_FAST) return Q4_EINVAL;
+  if (!blk) return Q4_EINVAL;
+  int32_t inter = 0;
+  if (check_block(*blk, max_pos, &inter) != Q4_OK || check_caches(blk, 1, max_pos) != Q4_OK ||
+      check_block_call(blk, 1, max_pos, h, pos, rope_cos, rope_sin, ws, ws_bytes) != Q4_OK)
+    return Q4_EINVAL;
+  return launch_blocks(block_layer(*blk), nullptr, 1, blk->hkv, inter, max_pos, eps, h, pos,
+                       rope_cos, rope_sin, ws, mode, stream);
+}
+
+int q4_block_stack_create(const q4_attn_block *blocks, int32_t nlayers, int32_t max_pos,
+                          q4_block_stack **out) {
+  if (!out) return Q4_EINVAL;
+  *out = nullptr;
+  if (!blocks || nlayers < 1 || nlayers > q4::kBlockMaxLayers) return Q4_EINVAL;
+  int32_t inter = 0;
+  for (int32_t i = 0; i < nlayers; ++i) {
+    int32_t in = 0;
+    if (check_block(blocks[i], max_pos, &in) != Q4_OK) return Q4_EINVAL;
+    if (i > 0 && (in != inter || blocks[i].hkv != blocks[0].hkv)) return Q4_EINVAL;
+    inter = in;
+  }
+  if (check_caches(blocks, nlayers, max_pos) != Q4_OK) return Q4_EINVAL;
+  q4_block_stack *s = new (std::nothrow) q4_block_stack();
+  if (!s) return Q4_ENOMEM;
+  std::vector<q4::BlockLayer> host;
+  try {
+    host.resize(nlayers);
+  } catch (...) {
+    delete s;
+    return Q4_ENOMEM;
+  }
+  s->blocks = new (std::nothrow) q4_attn_block[nlayers];
+  if (!s->blocks) {
+    delete s;
+    return Q4_ENOMEM;
+  }
+  s->n = nlayers;
+  for (int32_t i = 0; i < nlayers; ++i) {
+    s->blocks[i] = blocks[i];
+    host[i] = block_layer(blocks[i]);
+  }
+  const size_t bytes = sizeof(q4::BlockLayer) * (size_t)nlayers;
+  if (hipMalloc(&s->table, bytes) != hipSuccess) {
+    delete s;
+    return Q4_EHIP;
+  }
+  if (hipMemcpy(s->table, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(s->table);
+    delete s;
+    return Q4_EHIP;
+  }
+  s->max_pos = max_pos;
+  s->inter = inter;
+  *out = s;
+  return Q4_OK;
+}
+
+int q4_block_stack_destroy(q4_block_stack *s) {
+  if (!s) return Q4_EINVAL;
+  const hipError_t e = hipFree(s->table);
+  delete s;
+  return hip_status(e);
+}
+
+int q4_decode_blocks(const q4_block_stack *s, float eps, float *h, const int32_t *pos,
+                     const float *rope_cos, const float *rope_sin, void *ws, size_t ws_bytes,
+                     int mode, void *stream) {
+  if (mode != Q4_FIXED && mode != Q4_FAST) return Q4_EINVAL;
+  if (!s) return Q4_EINVAL;
+  const int32_t n = s->n;
+  if (check_block_call(s->blocks, n, s->max_pos, h, pos, rope_cos, rope_sin, ws, ws_bytes) !=
+      Q4_OK)
+    return Q4_EINVAL;
+  q4::BlockLayer none;
+  memset(&none, 0, sizeof(none));
+  return launch_blocks(none, s->table, n, s->blocks[0].hkv, s->inter, s->max_pos, eps, h, pos,
+                       rope_cos, rope_sin, ws, mode, stream);
 }
 
 int q4_decode_block_status(void *ws, void *stream) {

@@ -136,14 +136,16 @@ constexpr size_t kDecodeWsBytes = kDecodeCtlOffset + 4 * (kDecodeErrorWord + 32)
 int32_t decode_layers_grid(int mode, int32_t inter);
 hipError_t launch_decode_layers(const DecodeArgs &a, int mode, hipStream_t st);
 
-// One decoder layer (attention block and MLP block) in one persistent
-// launch (decode_block.hip): 16 query heads of 128 (hq * 128 = 2048), hkv
-// key/value heads dividing 16, one span of at most 256 positions.
+// Decoder layers (attention block and MLP block), one or several in one
+// persistent launch (decode_block.hip): 16 query heads of 128 (hq * 128 =
+// 2048), hkv key/value heads dividing 16, one span of at most 256
+// positions.
 constexpr int kBlockHeads = 16;
 constexpr int kBlockMaxPos = 256;
 constexpr int kBlockQRows = 8192;         // rows of [Q; gate; K; V], at most (hkv = 16)
 constexpr int kBlockORows = 2048 + 64;    // o and its 32 group sums (padded)
-struct DecodeBlockArgs {
+// One decoder layer's arrays.
+struct BlockLayer {
   const uint32_t *qq;  // [Q; gate; K; V] codes: [(32 + 2 hkv) * 128][256]
   const float *qs, *qb;
   const uint32_t *oq;  // O: [2048][256] codes
@@ -151,25 +153,37 @@ struct DecodeBlockArgs {
   const float *wa;     // [2048] attention norm weights
   const float *wq, *wk;  // [128] query and key norm weights
   float *kc, *vc;      // [hkv][max_pos][128] caches; row pos is written
+  DecodeLayer mlp;     // gate/up rows interleaved, down, MLP norm weights
+};
+constexpr int kBlockMaxLayers = 32;
+struct DecodeBlockArgs {
+  BlockLayer one;             // the layer, when `layers` is null
+  const BlockLayer *layers;   // device table [nlayers], or null
+  int32_t nlayers;            // 1 .. kBlockMaxLayers
   const float *cs, *sn;  // [max_pos][64] rotation tables
   const int32_t *pos;  // [1] the token's position
   int32_t max_pos, hkv;
-  DecodeLayer mlp;     // gate/up rows interleaved, down, MLP norm weights
   int32_t inter;
   float *h;            // [2048] hidden state: read at the start, written at the end
   uint64_t *qv;        // workspace: [copies][kBlockQRows] tagged q, gate, k, v
   uint64_t *ov;        // workspace: [copies][kBlockORows] tagged o and its group sums
   uint64_t *hv;        // workspace: [copies][2048] tagged h after the attention block
   uint64_t *mq;        // workspace: [copies][kDecodeMaxInter] tagged m
+  uint64_t *hb;        // workspace: [copies][2048] tagged h between layers
   uint32_t *ctl;       // workspace: call counters and the error word
   float eps;
   long long spin_ticks;
 };
+// Each hand-off buffer serves every layer of a launch: a workgroup writes
+// layer l + 1's values of a buffer only after every workgroup has passed
+// its read of layer l's (each stage waits on outputs of every workgroup's
+// previous stage, around the whole layer).
 constexpr size_t kBlockQvOffset = 0;
 constexpr size_t kBlockOvOffset = kBlockQvOffset + 8 * (size_t)kDecodeCopies * kBlockQRows;
 constexpr size_t kBlockHvOffset = kBlockOvOffset + 8 * (size_t)kDecodeCopies * kBlockORows;
 constexpr size_t kBlockMqOffset = kBlockHvOffset + 8 * (size_t)kDecodeCopies * 2048;
-constexpr size_t kBlockCtlOffset = kBlockMqOffset + 8 * (size_t)kDecodeCopies * kDecodeMaxInter;
+constexpr size_t kBlockHbOffset = kBlockMqOffset + 8 * (size_t)kDecodeCopies * kDecodeMaxInter;
+constexpr size_t kBlockCtlOffset = kBlockHbOffset + 8 * (size_t)kDecodeCopies * 2048;
 constexpr int kBlockErrorWord = kDecodeMaxGroups + 32;
 constexpr size_t kBlockWsBytes = kBlockCtlOffset + 4 * (kBlockErrorWord + 32);
 int32_t decode_block_grid(int mode, int32_t inter);

@@ -323,8 +323,11 @@ int q4_atq_status(void *ws, int32_t hq, int32_t hkv, void *stream);
  *   pos       : device int32[1]; max_pos <= Q4_BLOCK_MAX_POS (one span);
  *               rope_cos, rope_sin: device float[max_pos][64], 16-byte
  *               aligned.  A position outside [0, max_pos) makes h NaN.
- *   ws        : q4_decode_block_ws_bytes() bytes (about 1.3 MB), 16-byte
+ *   ws        : q4_decode_block_ws_bytes() bytes (about 1.5 MB), 16-byte
  *               aligned, zero-filled before first use; one call at a time.
+ * Errors: Q4_EINVAL for a shape, alignment or limit above, or when an
+ * array that the call writes (h, the caches, ws) overlaps another of its
+ * arrays; nothing is launched then.
  * q4_decode_block_status waits on the stream and reports a wait that ran
  * out (Q4_ETIMEOUT, after clearing the workspace).
  */
@@ -345,6 +348,34 @@ int q4_decode_block(const q4_attn_block *blk, float eps, float *h, const int32_t
                     int32_t max_pos, const float *rope_cos, const float *rope_sin, void *ws,
                     size_t ws_bytes, int mode, void *stream);
 int q4_decode_block_status(void *ws, void *stream);
+
+/*
+ * Several decoder layers of a decode token in one persistent launch
+ * ([P1] Change and Verification, as q4_decode_block): layer l + 1 takes h
+ * from layer l through tagged words, and each workgroup loads its rows of
+ * the next layer before it waits for the values they multiply.  The result
+ * has the bits of q4_decode_block called once per layer, in order.
+ *
+ * q4_block_stack_create checks the layers (each as q4_decode_block does;
+ * all with the same hkv and inter; no cache overlapping another layer's
+ * arrays) and copies their pointers to a table in device memory, with a
+ * synchronous copy: not a call for stream capture.  The arrays stay owned
+ * by the caller and must outlive the stack.  1 <= nlayers <=
+ * Q4_BLOCK_MAX_LAYERS; every cache holds max_pos positions.
+ * q4_decode_blocks runs every layer of the stack on h (read, then written
+ * with the last layer's output); pos, rope tables and ws as for
+ * q4_decode_block (the same workspace size and status call).  Errors as
+ * for q4_decode_block, Q4_ENOMEM or Q4_EHIP from create.
+ * q4_block_stack_destroy frees the table (after the device is idle).
+ */
+#define Q4_BLOCK_MAX_LAYERS 32
+typedef struct q4_block_stack q4_block_stack;
+int q4_block_stack_create(const q4_attn_block *blocks, int32_t nlayers, int32_t max_pos,
+                          q4_block_stack **out);
+int q4_block_stack_destroy(q4_block_stack *s);
+int q4_decode_blocks(const q4_block_stack *s, float eps, float *h, const int32_t *pos,
+                     const float *rope_cos, const float *rope_sin, void *ws, size_t ws_bytes,
+                     int mode, void *stream);
 
 /*
  * q4_pos_advance: *pos += 1 on the device (one thread), so that a decode

@@ -304,3 +304,51 @@ def test_decode_block_argument_checks(L):
     assert call(pos=slot(15) + 64) == EINVAL            # position inside h
     assert L.q4_decode_block_status(None, None) == EINVAL
     assert L.q4_decode_block_status(ctypes.c_void_p(slot(19) + 4), None) == EINVAL
+
+
+def test_block_stack_argument_checks(L):
+    """q4_block_stack_create rejects bad layer sets before any HIP call."""
+    G = 0x7F3000000000
+    slot = lambda i: G + i * 0x10000000
+
+    def block(base, hkv=4, inter=6144, kc=None, vc=None):
+        b = AttnBlock()
+        b.qgkv = Mat(slot(base), slot(base + 1), slot(base + 2), (32 + 2 * hkv) * 128, 2048)
+        b.o = Mat(slot(base + 3), slot(base + 4), slot(base + 5), 2048, 2048)
+        b.wa, b.wq, b.wk = slot(base + 6), slot(base + 7), slot(base + 8)
+        b.kcache = slot(base + 9) if kc is None else kc
+        b.vcache = slot(base + 10) if vc is None else vc
+        b.hkv = hkv
+        b.mlp.gate_up = Mat(slot(base + 11), slot(base + 12), slot(base + 13), 2 * inter, 2048)
+        b.mlp.down = Mat(slot(base + 14), slot(base + 15), slot(base + 16), 2048, inter)
+        b.mlp.wn = slot(base + 17)
+        return b
+
+    def create(blocks, n=None, max_pos=256):
+        arr = (AttnBlock * len(blocks))(*blocks)
+        out = ctypes.c_void_p()
+        return L.q4_block_stack_create(arr, len(blocks) if n is None else n, max_pos,
+                                       ctypes.byref(out))
+
+    two = lambda **kw: [block(0), block(20, **kw)]
+    import torch
+    if torch.cuda.device_count() == 0:
+        # a valid set passes every check and fails at the first HIP call
+        assert create(two()) not in (EINVAL, 0)
+    assert create(two(), n=0) == EINVAL
+    assert create([block(20 * i) for i in range(33)]) == EINVAL      # more than 32 layers
+    assert create(two(hkv=2)) == EINVAL                               # hkv differs
+    assert create(two(inter=4096)) == EINVAL                          # inter differs
+    assert create(two(kc=slot(9) + 4096)) == EINVAL                   # caches of two layers overlap
+    assert create(two(vc=slot(3))) == EINVAL                          # a cache over layer 0's O codes
+    assert create(two(), max_pos=0) == EINVAL
+    assert create(two(), max_pos=257) == EINVAL
+    assert create([block(0, hkv=3)]) == EINVAL
+    assert L.q4_block_stack_create(None, 1, 16, ctypes.byref(ctypes.c_void_p())) == EINVAL
+    arr = (AttnBlock * 1)(block(0))
+    assert L.q4_block_stack_create(arr, 1, 16, None) == EINVAL
+    assert L.q4_block_stack_destroy(None) == EINVAL
+    f = ctypes.c_float(1e-6)
+    p = ctypes.c_void_p
+    assert L.q4_decode_blocks(None, f, p(A), p(B), p(C), p(D), p(E), ctypes.c_size_t(1 << 21), 0,
+                              None) == EINVAL

@@ -1,10 +1,12 @@
-"""GPU parity of the persistent decoder layer (q4_decode_block: the
-attention block and the MLP block of one layer in one launch whose stages
-hand their outputs to each other through tagged words), driven through
-AttnDecodeChain(persistent=True): step by step and as graph replays
-against the oracle's attn_chain_step, bit for bit, for 1 to 16 key/value
-heads; 64 tokens of the 24-layer chain against the oracle's golden file;
-its bounded waits; a position outside the cache."""
+"""GPU parity of the persistent decoder layers (q4_decode_blocks and
+q4_decode_block: the attention block and the MLP block of every layer in
+one launch whose stages hand their outputs to each other through tagged
+words), driven through AttnDecodeChain(persistent=True): step by step and
+as graph replays against the oracle's attn_chain_step, bit for bit, for 1
+to 16 key/value heads; 64 tokens of the 24-layer chain against the
+oracle's golden file; the hidden state after a stack of layers and after
+single-layer launches against the oracle's; the bounded waits; positions
+outside the cache."""
 import json
 import os
 
@@ -119,3 +121,64 @@ def test_block_position_outside_the_cache():
     assert q4.q4_decode_block_status(chain.block_ws) == q4.Q4_OK
     assert np.all(np.isnan(host(h)))
     assert not np.any(host(chain.layers[0]["kc"]))  # no cache row written
+
+
+def test_stack_and_single_layer_calls_against_oracle_hidden():
+    """Three layers, three steps: the hidden state after every layer, from
+    one q4_decode_blocks launch and from three q4_decode_block launches,
+    each against the oracle's attn_chain_hidden bit for bit, and the caches
+    of both against the oracle's."""
+    from affine_q4_matvec_amd.chain import AttnDecodeChain
+    q4 = lib()
+    print("decode blocks: stack of 3 layers vs 3 single-layer launches", flush=True)
+    w = synth.attn_chain_weights(seed=48, layers=3, vocab=4096, hkv=2, max_pos=24)
+    toks = [5, 17, 4000]
+    kc, vc = oracle.attn_caches(w)
+    want = [oracle.attn_chain_hidden(w, t, p, kc, vc, nthreads=NTHREADS)
+            for p, t in enumerate(toks)]
+    chain = AttnDecodeChain(w, persistent=True)
+    assert len(chain.stacks) == 1
+    zc = lambda: torch.zeros_like(chain.layers[0]["kc"])
+    single = []
+    for lw in chain.layers:
+        single.append(q4.AttnBlock(lw["qgkv"], lw["o"], lw["wa"], lw["wq"], lw["wk"], zc(), zc(),
+                                   q4.MlpLayer(lw["gu"], lw["down"], lw["wn"])))
+    ws2 = torch.zeros_like(chain.block_ws)
+    s = torch.cuda.Stream()
+    for p, t in enumerate(toks):
+        tok = torch.tensor([t], dtype=torch.int32, device="cuda")
+        pos = torch.tensor([p], dtype=torch.int32, device="cuda")
+        h1 = torch.empty(2048, device="cuda")
+        h2 = torch.empty(2048, device="cuda")
+        q4.q4_embed(chain.head, tok, h1, stream=s)
+        q4.q4_embed(chain.head, tok, h2, stream=s)
+        q4.q4_decode_blocks(chain.stacks[0], chain.eps, h1, pos, chain.cos_tab, chain.sin_tab,
+                            chain.block_ws, stream=s)
+        for blk in single:
+            q4.q4_decode_block(blk, chain.eps, h2, pos, chain.cos_tab, chain.sin_tab, ws2,
+                               stream=s)
+        s.synchronize()
+        assert_bits_equal(host(h1), want[p], "stack, step %d" % p)
+        assert_bits_equal(host(h2), want[p], "single layers, step %d" % p)
+    for l in range(3):
+        for name, kt, vt in (("stack", chain.layers[l]["kc"], chain.layers[l]["vc"]),
+                             ("single", single[l].kcache, single[l].vcache)):
+            assert_bits_equal(host(kt).ravel(), kc[l].ravel(), "%s layer %d kcache" % (name, l))
+            assert_bits_equal(host(vt).ravel(), vc[l].ravel(), "%s layer %d vcache" % (name, l))
+    assert q4.q4_decode_block_status(chain.block_ws, s) == q4.Q4_OK
+    assert q4.q4_decode_block_status(ws2, s) == q4.Q4_OK
+
+
+def test_stack_position_outside_the_cache():
+    from affine_q4_matvec_amd.chain import AttnDecodeChain
+    q4 = lib()
+    w = synth.attn_chain_weights(seed=49, layers=2, vocab=4096, max_pos=16)
+    chain = AttnDecodeChain(w, persistent=True)
+    h = dev(np.ones(2048, np.float32))
+    pos = torch.tensor([-1], dtype=torch.int32, device="cuda")
+    q4.q4_decode_blocks(chain.stacks[0], chain.eps, h, pos, chain.cos_tab, chain.sin_tab,
+                        chain.block_ws)
+    assert q4.q4_decode_block_status(chain.block_ws) == q4.Q4_OK
+    assert np.all(np.isnan(host(h)))
+    for lw in chain.layers:
+        assert not np.any(host(lw["kc"])) and not np.any(host(lw["vc"]))
