@@ -19,8 +19,8 @@
 //              key and value cache rows are loaded before the wait
 //                                                  -> tagged o, osum
 //   stage O    every wave: one O row + the residual -> tagged h
-//   stage A    every wave: rmsq(h, wn), its (gate, up) pairs, SwiGLU
-//                                                  -> tagged m
+//   stage A    rmsq(h, wn) once per workgroup (workgroup_rmsq); every
+//              wave: its (gate, up) pairs, SwiGLU   -> tagged m
 //   stage B    every wave: one down row + the residual -> tagged h for the
 //              next layer's stage Q, or h (plain store) after the last
 // The weights of a wave's next rows are loaded before the wait that
@@ -249,25 +249,28 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
     const uint32_t tag = stage_tag(call, l);
 
     // ---- stage Q --------------------------------------------------------------
-    float hv[32], wv[32];
-    load_x_values(Y.wa + 32 * lane, true, wv);
-    if (l == 0) {
-      load_x_values(A.h + 32 * lane, true, hv);
-    } else {
-      // h after the previous layer: threads 0..255 fetch 8 values each
-      bool ok = true;
-      if (mine) {
-        float h8[8];
-        ok = poll_tagged<8>(A.hb + (size_t)copy * kCols + 8 * t, stage_tag(call, l - 1) + 5, h8,
-                            err, A.spin_ticks);
-        float4 *dst = reinterpret_cast<float4 *>(SO.x + 8 * t + 4 * (t >> 2));
-        dst[0] = make_float4(h8[0], h8[1], h8[2], h8[3]);
-        dst[1] = make_float4(h8[4], h8[5], h8[6], h8[7]);
-      }
-      if (!__syncthreads_and(ok)) return;
-      load_x_values(SO.x + kChunkStride * lane, true, hv);
-    }
+    // x = rmsq(h, wa), each wave for itself: h is the layer's input, or the
+    // previous layer's tagged output staged in LDS.  (Forming it once per
+    // workgroup, as stage A does, measured slower in this stage, which
+    // leads to the attention stage.)
     {
+      float hv[32], wv[32];
+      load_x_values(Y.wa + 32 * lane, true, wv);
+      if (l == 0) {
+        load_x_values(A.h + 32 * lane, true, hv);
+      } else {
+        bool ok = true;
+        if (mine) {
+          float h8[8];
+          ok = poll_tagged<8>(A.hb + (size_t)copy * kCols + 8 * t, stage_tag(call, l - 1) + 5, h8,
+                              err, A.spin_ticks);
+          float4 *dst = reinterpret_cast<float4 *>(SO.x + 8 * t + 4 * (t >> 2));
+          dst[0] = make_float4(h8[0], h8[1], h8[2], h8[3]);
+          dst[1] = make_float4(h8[4], h8[5], h8[6], h8[7]);
+        }
+        if (!__syncthreads_and(ok)) return;
+        load_x_values(SO.x + kChunkStride * lane, true, hv);
+      }
       const float rho = ops::rmsq_rho_wave2048(hv, A.eps);
       float xv[32];
 #pragma unroll
@@ -523,27 +526,22 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
     }
 
     // ---- stage A: m = SwiGLU([gate; up] rmsq(h, wn)) --------------------------
-    load_x_values(Y.mlp.wn + 32 * lane, true, wv);
     {
+      // x = rmsq(h, wn) over the workgroup: threads 0..255 take 8 columns
       bool ok = true;
+      float h8[8] = {}, w8[8] = {};
       if (mine) {
-        float h8[8];
+        load8(Y.mlp.wn + 8 * t, w8);
         ok = poll_tagged<8>(A.hv + (size_t)copy * kCols + 8 * t, tag + 3, h8, err, A.spin_ticks);
-        float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * t + 4 * (t >> 2));
-        dst[0] = make_float4(h8[0], h8[1], h8[2], h8[3]);
-        dst[1] = make_float4(h8[4], h8[5], h8[6], h8[7]);
       }
       issue_order();
       DownRow<NP> d{};
       if (has_row) load_down<NP>(Y.mlp, row, lane, d);
-      if (!__syncthreads_and(ok)) return;
-      load_x_values(S.x + kChunkStride * lane, true, hv);
+      const int rq = workgroup_rmsq(S, h8, w8, A.eps, ok);
+      if (rq < 0) return;
       {
-        const float rho = ops::rmsq_rho_wave2048(hv, A.eps);
         float xv[32];
-#pragma unroll
-        for (int k = 0; k < 32; ++k) xv[k] = ops::rmsq_value(hv[k], rho, wv[k]);
-        const float xsv = pair_group_sum(xv);
+        const float xsv = load_rmsq_x(S, lane, rq != 0, xv);
         uint64_t *mq = A.mq;
         const uint32_t tm = tag + 4;
         const auto store_m = [mq, tm](int i, float v) {
@@ -551,7 +549,7 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
           for (int c = 0; c < kDecodeCopies; ++c) store_tagged(mq + c * kDecodeMaxInter + i, v, tm);
         };
         if (pb < pe) {
-          if (prescale_for_pairs(xv))
+          if (rq != 0)
             gu_stage<FAST, true>(Y.mlp, xv, xsv, lane, pb, pe, a, store_m);
           else
             gu_stage<FAST, false>(Y.mlp, xv, xsv, lane, pb, pe, a, store_m);

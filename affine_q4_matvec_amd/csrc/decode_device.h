@@ -25,9 +25,72 @@ constexpr int kChunkStride = 36;  // LDS floats per 32-value chunk (4 of padding
 
 template <int NP>
 struct alignas(16) Lds {
-  float x[NP * 64 * kChunkStride];  // h (stage A) or m (stage B)
-  float xs[NP * 32];                // the group sums of m
+  float x[NP * 64 * kChunkStride];  // x = rmsq(h) (stage A) or m (stage B)
+  float xs[NP * 32];                // their group sums
+  float red[kWaves];                // the waves' sums of squares
 };
+
+// rmsq of h over the workgroup, with the arithmetic and tree of the rmsq
+// kernel (ops_device.h), so the bits of every wave forming it alone:
+// threads 0..255 hold h and the weights of columns [8t, 8t+8) (h8, w8);
+// the sum of squares goes over the 64 lanes of each wave, then every
+// thread adds the 8 wave sums in the balanced tree.  x goes to L.x in the
+// row stages' padded layout, its group sums to L.xs.  Returns -1 when `ok`
+// is false in any thread (a wait gave up), else 1 when every |x| < 2^118
+// (the pair decode may be used; the callers scale x as they load it), else
+// 0.  Two workgroup barriers; L must be free (every earlier reader past a
+// barrier).
+template <int NP>
+__device__ __forceinline__ int workgroup_rmsq(Lds<NP> &L, const float *h8, const float *w8,
+                                              float eps, bool ok) {
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1), wave = t / kWave;
+  const bool mine = 8 * t < kCols;
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = mine ? h8[k] * h8[k] : kNegZero;
+  float s = ops::tree8(v);
+#pragma unroll
+  for (int m = 1; m < kWave; m *= 2) s = s + __shfl_xor(s, m);
+  if (lane == 0) L.red[wave] = s;
+  if (!__syncthreads_and(ok)) return -1;
+  const float *r = L.red;
+  static_assert(kWaves == 8, "the tree over the wave sums");
+  const float ss = ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
+  const float rho = ops::rmsq_rho_from_ss(ss, kCols, eps);
+  float u[8];
+  bool large = false;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    u[k] = mine ? ops::rmsq_value(h8[k], rho, w8[k]) : kNegZero;
+    large |= mine && !(__builtin_fabsf(u[k]) < 0x1p118f);
+  }
+  if (mine) {
+    float4 *dst = reinterpret_cast<float4 *>(L.x + 8 * t + 4 * (t >> 2));
+    dst[0] = make_float4(u[0], u[1], u[2], u[3]);
+    dst[1] = make_float4(u[4], u[5], u[6], u[7]);
+  }
+  float g = ops::tree8(u);
+  g = g + __shfl_xor(g, 1);
+  g = g + __shfl_xor(g, 2);
+  g = g + __shfl_xor(g, 4);
+  if (mine && (t & 7) == 0) L.xs[t >> 3] = g;
+  return __syncthreads_or(large) ? 0 : 1;
+}
+
+// A wave's 32 values of x from L (lane l: columns [32 l, 32 l + 32)) and
+// the group sum of its lane pair, scaled for the pair decode if `pairs`
+// (the scaling of prescale_for_pairs).
+template <int NP>
+__device__ __forceinline__ float load_rmsq_x(const Lds<NP> &L, int lane, bool pairs, float *xv) {
+  load_x_values(L.x + kChunkStride * lane, true, xv);
+  if (pairs) {
+    const float scale = 1.0f / fp8_unit();
+#pragma unroll
+    for (int k = 0; k < 32; ++k) xv[k] = xv[k] * scale;
+  }
+  return L.xs[lane >> 1];
+}
 
 struct GuBlock {
   u32x4 cw[kGuR];

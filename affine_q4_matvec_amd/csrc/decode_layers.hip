@@ -7,8 +7,8 @@
 // stage pays a launch and the cold start of its loads; here one grid of
 // resident workgroups (one per compute unit) runs every stage:
 //
-//   h = embed(tok)                          (each wave, from the weights)
-//   per layer:  u = rmsq(h, wn)              (each wave, in registers)
+//   h = embed(tok)                          (8 columns per thread, from the weights)
+//   per layer:  u = rmsq(h, wn)              (once per workgroup, into LDS)
 //               m = SwiGLU([gate; up] u)     (rows in (gate, up) pairs)
 //               h = h + down m               (m staged in LDS per workgroup)
 //
@@ -111,56 +111,49 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
     const DecodeLayer &L = A.layer[l];
     uint64_t *mq = A.mq + (size_t)(l & 1) * kDecodeCopies * kDecodeMaxInter;  // copy 0
 
-    // ---- stage A: x = rmsq(h, wn), each wave for itself (lane l: columns
-    // [32 l, 32 l + 32)); m = SwiGLU of the gate/up rows
+    // ---- stage A: x = rmsq(h, wn) over the workgroup (threads 0..255: 8
+    // columns each); m = SwiGLU of the gate/up rows
     bool ok = true;
-    float wv[32];
-    load_x_values(L.wn + 32 * lane, true, wv);
-    if (l > 0 && mine) {
-      // threads 0..255 fetch h (8 values each) into LDS, value i at
-      // i + 4 (i / 32)
-      float hv[8];
-      ok = poll_tagged<8>(A.hq + ((size_t)((l - 1) & 1) * kDecodeCopies + copy) * kCols + 8 * t,
-                          tag0 + 2 * l, hv, err, A.spin_ticks);
-      float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * t + 4 * (t >> 2));
-      dst[0] = make_float4(hv[0], hv[1], hv[2], hv[3]);
-      dst[1] = make_float4(hv[4], hv[5], hv[6], hv[7]);
+    float h8[8] = {}, w8[8] = {};  // (zero: not carried from layer to layer)
+    if (mine) {
+      const float4 *wp = reinterpret_cast<const float4 *>(L.wn + 8 * t);
+      const float4 w0 = wp[0], w1 = wp[1];
+      w8[0] = w0.x; w8[1] = w0.y; w8[2] = w0.z; w8[3] = w0.w;
+      w8[4] = w1.x; w8[5] = w1.y; w8[6] = w1.z; w8[7] = w1.w;
     }
-    issue_order();
-    if (has_row) load_down<NP>(L, row, lane, d);
-    float hv[32];
     if (l == 0) {
       // the embedding row of the token (the embed kernel's arithmetic)
-      const bool valid = tk >= 0 && tk < A.vocab;
-      const size_t er = valid ? (size_t)tk : 0;
-      const float sg = valid ? A.es[er * 32 + (lane >> 1)] : 0.0f;
-      const float bg = valid ? A.eb[er * 32 + (lane >> 1)] : 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t word = valid ? A.eq[er * 256 + 4 * lane + j] : 0u;
+      if (mine) {
+        const bool valid = tk >= 0 && tk < A.vocab;
+        const size_t er = valid ? (size_t)tk : 0;
+        const float sg = valid ? A.es[er * 32 + (t >> 3)] : 0.0f;
+        const float bg = valid ? A.eb[er * 32 + (t >> 3)] : 0.0f;
+        const uint32_t word = valid ? A.eq[er * 256 + t] : 0u;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float sq = sg * (float)((word >> (4 * i)) & 15u);
-          hv[8 * j + i] = valid ? sq + bg : __builtin_nanf("");
+          h8[i] = valid ? sq + bg : __builtin_nanf("");
         }
       }
-    } else {
-      if (!__syncthreads_and(ok)) return;
-      load_x_values(S.x + kChunkStride * lane, true, hv);
+    } else if (mine) {
+      // h after the previous layer, 8 values per thread
+      ok = poll_tagged<8>(A.hq + ((size_t)((l - 1) & 1) * kDecodeCopies + copy) * kCols + 8 * t,
+                          tag0 + 2 * l, h8, err, A.spin_ticks);
     }
+    issue_order();
+    if (has_row) load_down<NP>(L, row, lane, d);
     {
-      const float rho = ops::rmsq_rho_wave2048(hv, A.eps);
+      const int rq = workgroup_rmsq(S, h8, w8, A.eps, ok);
+      if (rq < 0) return;
       float xv[32];
-#pragma unroll
-      for (int k = 0; k < 32; ++k) xv[k] = ops::rmsq_value(hv[k], rho, wv[k]);
-      const float xsv = pair_group_sum(xv);
+      const float xsv = load_rmsq_x(S, lane, rq != 0, xv);
       const uint32_t tag = tag0 + 2 * l + 1;
       const auto store_m = [mq, tag](int i, float v) {
 #pragma unroll
         for (int c = 0; c < kDecodeCopies; ++c) store_tagged(mq + c * kDecodeMaxInter + i, v, tag);
       };
       if (pb < pe) {
-        if (prescale_for_pairs(xv))
+        if (rq != 0)
           gu_stage<FAST, true>(L, xv, xsv, lane, pb, pe, a, store_m);
         else
           gu_stage<FAST, false>(L, xv, xsv, lane, pb, pe, a, store_m);

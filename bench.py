@@ -355,9 +355,9 @@ def time_attn_chain(args, q4, torch, chain, tok0, steps):
 
 def run_attn_chain(args, q4, torch, synth):
     """The decode chain with an attention block in every layer, two
-    engines: the fused per-stage kernels (5 per layer) and one persistent
-    launch per layer (q4_decode_block); one captured graph per token from
-    position 0 with empty caches."""
+    engines: the fused per-stage kernels (5 per layer) and every layer in
+    one persistent launch (q4_decode_blocks); one captured graph per token
+    from position 0 with empty caches."""
     from affine_q4_matvec_amd.chain import AttnDecodeChain
 
     log("generating the chain with attention (24 layers, seed %d)" % args.seed)
