@@ -182,3 +182,50 @@ def test_stack_position_outside_the_cache():
     assert np.all(np.isnan(host(h)))
     for lw in chain.layers:
         assert not np.any(host(lw["kc"])) and not np.any(host(lw["vc"]))
+
+
+@pytest.mark.parametrize("inter", [2048, 4096, 8192])
+def test_block_chain_other_widths(inter):
+    """The kernel's other MLP widths (1, 2 and 4 passes per down row): two
+    layers, three steps against the oracle bit for bit."""
+    from affine_q4_matvec_amd.chain import AttnDecodeChain
+    print("decode blocks: inter %d" % inter, flush=True)
+    w = synth.attn_chain_weights(seed=50 + inter // 2048, layers=2, vocab=4096, inter=inter,
+                                 max_pos=16)
+    want, kc, _ = oracle_steps(w, 3)
+    chain = AttnDecodeChain(w, persistent=True)
+    s = torch.cuda.Stream()
+    got = []
+    toks = chain.run(w["tok0"], 3, s, on_step=lambda i, c: got.append(host(c.logits)))
+    for i, (_, logits) in enumerate(want):
+        assert_bits_equal(got[i], logits, "inter %d step %d logits" % (inter, i))
+    assert toks == [t for t, _ in want]
+    assert_bits_equal(host(chain.layers[1]["kc"]).ravel(), kc[1].ravel(), "layer 1 kcache")
+    assert lib().q4_decode_block_status(chain.block_ws, s) == lib().Q4_OK
+
+
+def test_block_chain_fast_mode_equals_stage_kernels():
+    """Fast mode: the rows use the per-stage kernels' fast code and the
+    attention step its one order, so the persistent engine decodes the same
+    bits as the per-stage kernels in fast mode; and its logits stay within
+    the fast order's error of the oracle's."""
+    from affine_q4_matvec_amd.chain import AttnDecodeChain
+    q4 = lib()
+    w = synth.attn_chain_weights(seed=54, layers=3, vocab=4096, max_pos=16)
+    want, _, _ = oracle_steps(w, 4)
+    s = torch.cuda.Stream()
+    logits = {}
+    toks = {}
+    for persistent in (False, True):
+        chain = AttnDecodeChain(w, mode=q4.FAST, persistent=persistent)
+        got = []
+        toks[persistent] = chain.run(w["tok0"], 4, s,
+                                     on_step=lambda i, c: got.append(host(c.logits)))
+        logits[persistent] = got
+    for i in range(4):
+        assert_bits_equal(logits[True][i], logits[False][i], "fast step %d" % i)
+    assert toks[True] == toks[False]
+    # the first step starts from the same token as the oracle's
+    ref = want[0][1].astype(np.float64)
+    err = np.abs(logits[True][0].astype(np.float64) - ref)
+    assert err.max() <= 1e-4 * np.sqrt(np.mean(ref ** 2)), err.max()
