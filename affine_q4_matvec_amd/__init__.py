@@ -400,7 +400,7 @@ def q4_atq_status(ws: torch.Tensor, hq: int, hkv: int, stream=None) -> int:
                                   _stream(stream)))
 
 
-BLOCK_MAX_POS = 256
+BLOCK_MAX_POS = 4096
 BLOCK_MAX_LAYERS = 32
 
 

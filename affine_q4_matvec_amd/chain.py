@@ -216,7 +216,7 @@ class AttnDecodeChain(DecodeChain):
     dataflow (the gate rows are an addition: the attention step gates its
     output).  persistent=True runs every layer in one persistent launch
     (q4_decode_blocks over stacks of at most 32 layers, caches of at most
-    256 positions): 4 kernels for up to 32 layers, the same bits."""
+    4096 positions): 4 kernels for up to 32 layers, the same bits."""
 
     def __init__(self, weights: dict, mode: int = FIXED, layers: int | None = None,
                  device: str = "cuda", persistent: bool = False):

@@ -112,37 +112,6 @@ __device__ __forceinline__ float gate_value(float g) {
   return (float)(1.0 / (1.0 + fixed_exp(-(double)g)));
 }
 
-// The tagged span sums 1 .. nspan-1 of one output column (wp: stride
-// 128 words) and of the weights (zp), all loaded in each round; slots from
-// nspan on are -0.  False when the wait ran out or another wait did.
-__device__ __forceinline__ bool poll_spans(const uint64_t *wp, const uint64_t *zp, int nspan,
-                                           uint32_t tag, float *ws, float *zs, uint32_t *err,
-                                           long long spin_ticks) {
-  const long long t0 = wall_clock64();
-  for (int it = 1;; ++it) {
-    bool ready = true;
-#pragma unroll
-    for (int sp = 1; sp < kMaxSpans; ++sp) {
-      ws[sp] = kNegZero;
-      zs[sp] = kNegZero;
-      if (sp < nspan) {
-        const uint64_t w = __hip_atomic_load(wp + (size_t)sp * kD, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t z = __hip_atomic_load(zp + sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ws[sp] = __uint_as_float((uint32_t)w);
-        zs[sp] = __uint_as_float((uint32_t)z);
-        ready &= (uint32_t)(w >> 32) == tag && (uint32_t)(z >> 32) == tag;
-      }
-    }
-    if (ready) return true;
-    if ((it & 63) == 0 && load_word(err) != 0) return false;
-    if (wall_clock64() - t0 > spin_ticks) {
-      store_word(err, 1u);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-}
 
 struct Lds {
   float un[2][kD];     // normed rows: the query, then the new key
@@ -348,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void atq_kernel(AtqArgs a) {
       } else {
         // every span's sums, polled together
         float ws[kMaxSpans], zs[kMaxSpans];
-        ok = poll_spans(wp, zp, nspan, tag, ws, zs, err, a.spin_ticks);
+        ok = poll_span_sums<kMaxSpans>(wp, kD, zp, nspan, tag, ws, zs, err, a.spin_ticks);
         ws[0] = w;
         zs[0] = z;
         w = tree8(ws) + tree8(ws + 8);

@@ -13,11 +13,14 @@
 // protocol of tagged_device.h, as in the persistent MLP layers):
 //   stage Q    every wave: rmsq(h, wa) for itself, its 2..4 rows of
 //              [Q; gate; K; V]                    -> tagged q, gate, k, v
-//   stage ATQ  workgroups 0..15, one query head each: the attention step
-//              over one span of at most 256 positions; the head's new
-//              key and value rows, if it is its group's first head; the
-//              key and value cache rows are loaded before the wait
-//                                                  -> tagged o, osum
+//   stage ATQ  one workgroup per query head and 256-position span up to
+//              the position (16 to 256 workgroups): the attention step of
+//              atq_kernel (scores, the span maxima exchanged as tagged
+//              words, weights, the span sums gathered by span 0 of the
+//              head, which forms o); the head's new key and value rows are
+//              written by the span holding the position, if the head is
+//              its group's first; the span's cache rows are loaded before
+//              the wait                             -> tagged o, osum
 //   stage O    every wave: one O row + the residual -> tagged h
 //   stage A    rmsq(h, wn) once per workgroup (workgroup_rmsq); every
 //              wave: its (gate, up) pairs, SwiGLU   -> tagged m
@@ -46,7 +49,7 @@ constexpr int kHeads = kBlockHeads;
 constexpr float kScale = 0x1.6a09e6p-4f;  // RN32(1 / sqrt(128))
 constexpr int kQRowsPerWave = kBlockQRows / kCols;  // rows of [Q; gate; K; V] per wave, at most
 static_assert(kThreads == 512, "the attention stage's thread layout");
-static_assert(kBlockMaxPos == 256, "8 passes of 32 positions; 16 blocks of 16");
+static_assert(kBlockSpan == 256, "8 passes of 32 positions; 16 blocks of 16");
 
 struct QBlock {
   u32x4 cw[kQRowsPerWave];
@@ -110,8 +113,8 @@ struct AttnLds {
   float tab[3 * kD];        // q and k norm weights, then the rotation's cos and sin
   float un[2][kD];          // normed q, k
   float rot[2][kD];         // rotated q, k
-  float s[kBlockMaxPos];    // scores
-  float e[kBlockMaxPos];    // weights
+  float s[kBlockSpan];      // scores of the span
+  float e[kBlockSpan];      // weights of the span
   float part[16][kD];       // value sums over 16 positions
   float wsum[4];            // weight sums over 64 positions
   float m;                  // largest score
@@ -297,9 +300,21 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
     if (has_row) load_orow(Y, row, lane, od);
     issue_order();
 
-    // ---- stage ATQ (workgroups 0..15, one query head each) --------------------
-    if (wg < kHeads) {
-      const int hd = wg, j = hd / G;
+    // ---- stage ATQ (one workgroup per query head and 256-position span) ------
+    // Task i = ((c hkv + j) G + g): head j G + g of key/value head j over
+    // positions [256 c, 256 c + 256), for the spans up to pos; span 0 of
+    // each head gathers the others' sums and forms o.  Workgroup w runs on
+    // XCD w % 8 and takes task (w % 8) (nwg / 8) + w / 8, so that the G
+    // heads that read the same cache rows share an XCD and its L2.
+    const int nspan = pos_ok ? pos / kBlockSpan + 1 : 1;
+    const int per_xcd = nwg / kXcds;
+    const int task = wg < kXcds * per_xcd ? (wg % kXcds) * per_xcd + wg / kXcds : nwg;
+    if (task < kHeads * nspan) {
+      const int g = task % G, jc = task / G;
+      const int j = jc % A.hkv, c = jc / A.hkv, hd = j * G + g;
+      const int p0 = kBlockSpan * c;           // the span's first position
+      const int pn = min(n - p0, kBlockSpan);  // its positions below n (none for a bad pos)
+      const bool owns_pos = pos_ok && pos / kBlockSpan == c;
       const int r = t >> 4, lq = t & 15;  // scores: 32 positions per pass
       // the norm weights and the rotation table's row, for LDS below
       float tv = 0.0f;
@@ -309,11 +324,12 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
         const int pr = pos_ok ? pos : 0;
         tv = (t < 5 * kD / 2 ? A.cs : A.sn)[(size_t)pr * (kD / 2) + t % (kD / 2)];
       }
-      // the cache rows below n, loaded before the wait (bounded buffer
-      // loads: zeros from n on; row pos is stale here and not used)
-      const size_t hb = (size_t)j * A.max_pos * kD;
-      const auto kr = buffer(Y.kc + hb, (uint32_t)n * kD * 4u);
-      const auto vr = buffer(Y.vc + hb, (uint32_t)n * kD * 4u);
+      // the span's cache rows below n, loaded before the wait (bounded
+      // buffer loads: zeros from n on; row pos is stale here and not used)
+      const size_t hb = ((size_t)j * A.max_pos + p0) * kD;
+      const uint32_t span_bytes = (uint32_t)max(pn, 0) * kD * 4u;
+      const auto kr = buffer(Y.kc + hb, span_bytes);
+      const auto vr = buffer(Y.vc + hb, span_bytes);
       float kv[8][8];
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
@@ -382,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
           }
           T.rot[r][d] = rv[k];
         }
-        if (r == 1 && hd % G == 0 && pos_ok) {  // the new cache rows
+        if (r == 1 && hd % G == 0 && owns_pos) {  // the new cache rows
           const size_t at = ((size_t)j * A.max_pos + pos) * kD + 8 * lq;
           float4 *kd = reinterpret_cast<float4 *>(Y.kc + at);
           float4 *vd = reinterpret_cast<float4 *>(Y.vc + at);
@@ -398,28 +414,38 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
         const int tp = 32 * p + r;
-        if (tp < n) {  // uniform over the 16 lanes of the position
+        if (tp < pn) {  // uniform over the 16 lanes of the position
+          const bool at_pos = p0 + tp == pos;
           float pr[8];
 #pragma unroll
           for (int k = 0; k < 8; ++k)
-            pr[k] = T.rot[0][8 * lq + k] * (tp == pos ? T.rot[1][8 * lq + k] : kv[p][k]);
+            pr[k] = T.rot[0][8 * lq + k] * (at_pos ? T.rot[1][8 * lq + k] : kv[p][k]);
           const float sc = sum16(ops::tree8(pr)) * kScale;
           if (lq == 0) T.s[tp] = sc;
         }
       }
       __syncthreads();
+      // the largest score: of the span, then over the head's spans
+      bool ok = true;
       if (wave == 0) {
         float m = -INFINITY;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          if (64 * k + lane < n) m = fmaxf(m, T.s[64 * k + lane]);
+          if (64 * k + lane < pn) m = fmaxf(m, T.s[64 * k + lane]);
         m = max64(m);
+        if (nspan > 1) {
+          uint64_t *mx = A.mx + (size_t)hd * kBlockMaxSpans;
+          if (lane == 0) store_tagged(mx + c, m, tag + 6);
+          float o = -INFINITY;
+          if (lane < nspan) ok = poll_tagged<1>(mx + lane, tag + 6, &o, err, A.spin_ticks);
+          m = max64(o);
+        }
         if (lane == 0) T.m = m;
       }
-      __syncthreads();
-      if (t < kBlockMaxPos) {
+      if (__syncthreads_or(!ok)) return;
+      if (t < kBlockSpan) {
         float e = kNegZero;
-        if (t < n) {
+        if (t < pn) {
           const float d = T.s[t] - T.m;
           e = (float)ops::fixed_exp((double)d);
         }
@@ -431,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
       // the weighted value sums over 16 positions of 4 columns (the new row,
       // at pos, from the inputs)
       {
-        const int kp = pos - 16 * pg;  // the new row's slot in this thread's block, if any
+        const int kp = pos - p0 - 16 * pg;  // the new row's slot in this thread's block, if any
         if (kp >= 0 && kp < 16) {
           const float4 nv = *reinterpret_cast<const float4 *>(&T.in[3][4 * cq]);
 #pragma unroll
@@ -450,26 +476,48 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
         const auto block16 = [&](const float *vc) {
           float pr[16];
 #pragma unroll
-          for (int k = 0; k < 16; ++k) pr[k] = 16 * pg + k < n ? ek[k] * vc[k] : kNegZero;
+          for (int k = 0; k < 16; ++k) pr[k] = 16 * pg + k < pn ? ek[k] * vc[k] : kNegZero;
           return ops::tree8(pr) + ops::tree8(pr + 8);
         };
         *reinterpret_cast<float4 *>(&T.part[pg][4 * cq]) =
             make_float4(block16(v0), block16(v1), block16(v2), block16(v3));
       }
       __syncthreads();
+      float w = 0.0f, z = 0.0f;  // output column t's value sum and the weight sum
       if (t < kD) {
         float pq[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) pq[k] = T.part[k][t];
-        const float w = ops::tree8(pq) + ops::tree8(pq + 8);
-        const float z = (T.wsum[0] + T.wsum[1]) + (T.wsum[2] + T.wsum[3]);
+        w = ops::tree8(pq) + ops::tree8(pq + 8);
+        z = (T.wsum[0] + T.wsum[1]) + (T.wsum[2] + T.wsum[3]);
+        if (nspan > 1) {
+          // the spans' sums: T over the positions is the balanced tree over
+          // 16 span slots (-0 past the last span) of the spans' trees
+          uint64_t *wp = A.wp + (size_t)hd * kBlockMaxSpans * kD + t;
+          uint64_t *zp = A.zp + (size_t)hd * kBlockMaxSpans;
+          if (c > 0) {
+            store_tagged(wp + (size_t)c * kD, w, tag + 7);
+            if (t == 0) store_tagged(zp + c, z, tag + 7);
+          } else {
+            float ws[kBlockMaxSpans], zs[kBlockMaxSpans];
+            ok = poll_span_sums<kBlockMaxSpans>(wp, kD, zp, nspan, tag + 7, ws, zs, err,
+                                                A.spin_ticks);
+            ws[0] = w;
+            zs[0] = z;
+            w = ops::tree8(ws) + ops::tree8(ws + 8);
+            z = ops::tree8(zs) + ops::tree8(zs + 8);
+          }
+        }
+      }
+      if (__syncthreads_or(!ok)) return;
+      if (c == 0 && t < kD) {
         const double gd = (double)T.in[1][t];
         const float sig = (float)(1.0 / (1.0 + ops::fixed_exp(-gd)));
         const float ov = pos_ok ? (w / z) * sig : __builtin_nanf("");
         const float gsum = sum64(ov);  // waves 0 and 1: the head's two groups
 #pragma unroll
-        for (int c = 0; c < kDecodeCopies; ++c) {
-          uint64_t *o = A.ov + (size_t)c * kBlockORows;
+        for (int cp = 0; cp < kDecodeCopies; ++cp) {
+          uint64_t *o = A.ov + (size_t)cp * kBlockORows;
           store_tagged(o + kD * hd + t, ov, tag + 2);
           if (lane == 0) store_tagged(o + kCols + 2 * hd + wave, gsum, tag + 2);
         }
@@ -631,8 +679,11 @@ int32_t decode_block_grid(int mode, int32_t inter) {
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  // one workgroup per compute unit, a wave for every O and down row
-  if (per_cu < 1 || cus * kWaves < kCols || cus > kDecodeMaxGroups) return 0;
+  // one workgroup per compute unit, a wave for every O and down row, a
+  // workgroup for every head and span of the attention stage
+  if (per_cu < 1 || cus * kWaves < kCols || cus < kBlockHeads * kBlockMaxSpans ||
+      cus > kDecodeMaxGroups)
+    return 0;
   return cus;
 }
 

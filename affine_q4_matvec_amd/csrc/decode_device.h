@@ -22,6 +22,7 @@ constexpr int kCols = 2048;     // width of h: the gate/up rows and the down out
 constexpr int kGuPairs = 3;     // (gate, up) row pairs per block
 constexpr int kGuR = 2 * kGuPairs;
 constexpr int kChunkStride = 36;  // LDS floats per 32-value chunk (4 of padding)
+constexpr int kXcds = 8;          // MI355X: workgroup w is dispatched to XCD w % 8
 
 template <int NP>
 struct alignas(16) Lds {

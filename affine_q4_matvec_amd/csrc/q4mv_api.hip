@@ -617,6 +617,9 @@ int launch_blocks(const q4::BlockLayer &one, const q4::BlockLayer *table, int32_
   a.hv = reinterpret_cast<uint64_t *>(w + q4::kBlockHvOffset);
   a.mq = reinterpret_cast<uint64_t *>(w + q4::kBlockMqOffset);
   a.hb = reinterpret_cast<uint64_t *>(w + q4::kBlockHbOffset);
+  a.mx = reinterpret_cast<uint64_t *>(w + q4::kBlockMxOffset);
+  a.zp = reinterpret_cast<uint64_t *>(w + q4::kBlockZpOffset);
+  a.wp = reinterpret_cast<uint64_t *>(w + q4::kBlockWpOffset);
   a.ctl = reinterpret_cast<uint32_t *>(w + q4::kBlockCtlOffset);
   a.eps = eps;
   if (wait_ticks(&a.spin_ticks) != Q4_OK) return Q4_EHIP;

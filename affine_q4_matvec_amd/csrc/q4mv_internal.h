@@ -138,10 +138,12 @@ hipError_t launch_decode_layers(const DecodeArgs &a, int mode, hipStream_t st);
 
 // Decoder layers (attention block and MLP block), one or several in one
 // persistent launch (decode_block.hip): 16 query heads of 128 (hq * 128 =
-// 2048), hkv key/value heads dividing 16, one span of at most 256
-// positions.
+// 2048), hkv key/value heads dividing 16, caches of up to 16 spans of 256
+// positions (one workgroup per head and span).
 constexpr int kBlockHeads = 16;
-constexpr int kBlockMaxPos = 256;
+constexpr int kBlockSpan = 256;
+constexpr int kBlockMaxSpans = 16;
+constexpr int kBlockMaxPos = kBlockSpan * kBlockMaxSpans;
 constexpr int kBlockQRows = 8192;         // rows of [Q; gate; K; V], at most (hkv = 16)
 constexpr int kBlockORows = 2048 + 64;    // o and its 32 group sums (padded)
 // One decoder layer's arrays.
@@ -170,6 +172,9 @@ struct DecodeBlockArgs {
   uint64_t *hv;        // workspace: [copies][2048] tagged h after the attention block
   uint64_t *mq;        // workspace: [copies][kDecodeMaxInter] tagged m
   uint64_t *hb;        // workspace: [copies][2048] tagged h between layers
+  uint64_t *mx;        // workspace: [heads][spans] tagged span maxima
+  uint64_t *zp;        // workspace: [heads][spans] tagged span weight sums
+  uint64_t *wp;        // workspace: [heads][spans][128] tagged span value sums
   uint32_t *ctl;       // workspace: call counters and the error word
   float eps;
   long long spin_ticks;
@@ -183,7 +188,11 @@ constexpr size_t kBlockOvOffset = kBlockQvOffset + 8 * (size_t)kDecodeCopies * k
 constexpr size_t kBlockHvOffset = kBlockOvOffset + 8 * (size_t)kDecodeCopies * kBlockORows;
 constexpr size_t kBlockMqOffset = kBlockHvOffset + 8 * (size_t)kDecodeCopies * 2048;
 constexpr size_t kBlockHbOffset = kBlockMqOffset + 8 * (size_t)kDecodeCopies * kDecodeMaxInter;
-constexpr size_t kBlockCtlOffset = kBlockHbOffset + 8 * (size_t)kDecodeCopies * 2048;
+constexpr size_t kBlockMxOffset = kBlockHbOffset + 8 * (size_t)kDecodeCopies * 2048;
+constexpr size_t kBlockZpOffset = kBlockMxOffset + 8 * (size_t)kBlockHeads * kBlockMaxSpans;
+constexpr size_t kBlockWpOffset = kBlockZpOffset + 8 * (size_t)kBlockHeads * kBlockMaxSpans;
+constexpr size_t kBlockCtlOffset =
+    kBlockWpOffset + 8 * (size_t)kBlockHeads * kBlockMaxSpans * 128;
 constexpr int kBlockErrorWord = kDecodeMaxGroups + 32;
 constexpr size_t kBlockWsBytes = kBlockCtlOffset + 4 * (kBlockErrorWord + 32);
 int32_t decode_block_grid(int mode, int32_t inter);

@@ -316,20 +316,20 @@ def run_atq(args, q4, torch, synth):
     return out
 
 
-def time_attn_chain(args, q4, torch, chain, tok0, steps):
+def time_attn_chain(args, q4, torch, chain, tok0, steps, pos0=0):
     """One engine of the chain with attention: ms per token with the
     mailbox wait, and the device time of the same number of queued
-    replays, from position 0 with empty caches."""
+    replays, from position pos0 with empty caches."""
     stream = torch.cuda.Stream()
     chain.capture(stream)
     chain.run(0, 3, stream)  # warm-up tokens (not timed)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    tokens = chain.run(tok0, steps, stream, wait="mailbox")
+    tokens = chain.run(tok0, steps, stream, wait="mailbox", pos0=pos0)
     per_token_ms = (time.perf_counter() - t0) * 1e3 / steps
     with torch.cuda.stream(stream):
         chain.set_token(tok0)
-        chain.set_position(0)
+        chain.set_position(pos0)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -379,11 +379,34 @@ def run_attn_chain(args, q4, torch, synth):
         del chain
         torch.cuda.synchronize()
     best = min(engines, key=lambda k: engines[k]["ms_per_token_gpu"])
+    # the same engines at the end of a cache of 4096 positions (16 spans of
+    # 256 per head): both must decode the same tokens
+    long_pos = 4096
+    w = dict(w)  # the same weights, rotation tables of 4096 positions
+    w["cos_tab"], w["sin_tab"] = synth.rope_tables(long_pos)
+    w["max_pos"] = long_pos
+    pos0 = long_pos - steps
+    long_engines, long_tokens = {}, {}
+    for name in ("fused", "persistent"):
+        chain = AttnDecodeChain(w, mode=mode, persistent=(name == "persistent"))
+        r, long_tokens[name] = time_attn_chain(args, q4, torch, chain, tok0, steps, pos0=pos0)
+        long_engines[name] = r
+        log("attention chain %s, positions %d..%d: %s" % (name, pos0, long_pos - 1, r))
+        del chain
+        torch.cuda.synchronize()
+    long_best = min(long_engines, key=lambda k: long_engines[k]["ms_per_token_gpu"])
     return {
         "tokens": steps, "layers": len(w["layers"]), "positions": "0..%d" % (steps - 1),
         "best_engine": best,
         "best_ms_per_token_gpu": engines[best]["ms_per_token_gpu"],
         "engines": engines,
+        "long_cache": {
+            "max_pos": long_pos, "positions": "%d..%d" % (pos0, long_pos - 1),
+            "best_engine": long_best,
+            "best_ms_per_token_gpu": long_engines[long_best]["ms_per_token_gpu"],
+            "tokens_equal_across_engines": long_tokens["fused"] == long_tokens["persistent"],
+            "engines": long_engines,
+        },
     }
 
 

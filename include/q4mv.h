@@ -320,10 +320,11 @@ int q4_atq_status(void *ws, int32_t hq, int32_t hkv, void *stream);
  *   blk->hkv  : 1, 2, 4, 8 or 16 key/value heads.
  *   blk->mlp  : as for q4_decode_layers (inter 2048..8192).
  *   h         : device float[2048], 16-byte aligned, read and written.
- *   pos       : device int32[1]; max_pos <= Q4_BLOCK_MAX_POS (one span);
+ *   pos       : device int32[1]; max_pos <= Q4_BLOCK_MAX_POS (16 spans of
+ *               256 positions; one workgroup per query head and span);
  *               rope_cos, rope_sin: device float[max_pos][64], 16-byte
  *               aligned.  A position outside [0, max_pos) makes h NaN.
- *   ws        : q4_decode_block_ws_bytes() bytes (about 1.5 MB), 16-byte
+ *   ws        : q4_decode_block_ws_bytes() bytes (about 1.6 MB), 16-byte
  *               aligned, zero-filled before first use; one call at a time.
  * Errors: Q4_EINVAL for a shape, alignment or limit above, or when an
  * array that the call writes (h, the caches, ws) overlaps another of its
@@ -331,7 +332,7 @@ int q4_atq_status(void *ws, int32_t hq, int32_t hkv, void *stream);
  * q4_decode_block_status waits on the stream and reports a wait that ran
  * out (Q4_ETIMEOUT, after clearing the workspace).
  */
-#define Q4_BLOCK_MAX_POS 256
+#define Q4_BLOCK_MAX_POS 4096
 typedef struct q4_attn_block {
   q4_mat qgkv;
   q4_mat o;

@@ -292,7 +292,7 @@ def test_decode_block_argument_checks(L):
     assert call(pos=0) == EINVAL
     assert call(pos=slot(16) + 2) == EINVAL
     assert call(max_pos=0) == EINVAL
-    assert call(max_pos=257) == EINVAL                  # longer than one span
+    assert call(max_pos=4097) == EINVAL                 # longer than 16 spans
     assert call(cs=0) == EINVAL
     assert call(ws=slot(19) + 8) == EINVAL
     assert call(wsb=wsb - 16) == EINVAL
@@ -342,7 +342,7 @@ def test_block_stack_argument_checks(L):
     assert create(two(kc=slot(9) + 4096)) == EINVAL                   # caches of two layers overlap
     assert create(two(vc=slot(3))) == EINVAL                          # a cache over layer 0's O codes
     assert create(two(), max_pos=0) == EINVAL
-    assert create(two(), max_pos=257) == EINVAL
+    assert create(two(), max_pos=4097) == EINVAL
     assert create([block(0, hkv=3)]) == EINVAL
     assert L.q4_block_stack_create(None, 1, 16, ctypes.byref(ctypes.c_void_p())) == EINVAL
     arr = (AttnBlock * 1)(block(0))

@@ -229,3 +229,26 @@ def test_block_chain_fast_mode_equals_stage_kernels():
     ref = want[0][1].astype(np.float64)
     err = np.abs(logits[True][0].astype(np.float64) - ref)
     assert err.max() <= 1e-4 * np.sqrt(np.mean(ref ** 2)), err.max()
+
+
+@pytest.mark.parametrize("max_pos,pos0,hkv", [(1024, 254, 4), (1024, 766, 1), (4096, 4092, 4)])
+def test_block_chain_several_spans(max_pos, pos0, hkv):
+    """Caches of 4 and 16 spans of 256 positions: one workgroup per head
+    and span, the span maxima and sums exchanged as tagged words, steps
+    that cross from one span into the next, against the oracle bit for
+    bit."""
+    from affine_q4_matvec_amd.chain import AttnDecodeChain
+    print("decode blocks: max_pos %d from %d, hkv %d" % (max_pos, pos0, hkv), flush=True)
+    w = synth.attn_chain_weights(seed=60 + hkv, layers=2, vocab=4096, hkv=hkv, max_pos=max_pos)
+    want, kc, vc = oracle_steps(w, 4, pos0=pos0)
+    chain = AttnDecodeChain(w, persistent=True)
+    s = torch.cuda.Stream()
+    got = []
+    toks = chain.run(w["tok0"], 4, s, pos0=pos0, on_step=lambda i, c: got.append(host(c.logits)))
+    for i, (_, logits) in enumerate(want):
+        assert_bits_equal(got[i], logits, "pos %d logits" % (pos0 + i))
+    assert toks == [t for t, _ in want]
+    for l in range(2):
+        assert_bits_equal(host(chain.layers[l]["kc"]).ravel(), kc[l].ravel(), "layer %d kcache" % l)
+        assert_bits_equal(host(chain.layers[l]["vc"]).ravel(), vc[l].ravel(), "layer %d vcache" % l)
+    assert lib().q4_decode_block_status(chain.block_ws, s) == lib().Q4_OK
