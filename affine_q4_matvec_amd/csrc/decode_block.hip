@@ -116,6 +116,8 @@ struct AttnLds {
   float s[kBlockSpan];      // scores of the span
   float e[kBlockSpan];      // weights of the span
   float part[16][kD];       // value sums over 16 positions
+  float sw[kBlockMaxSpans][kD];  // the spans' value sums (span 0 of a head)
+  float sz[kBlockMaxSpans];      // the spans' weight sums
   float wsum[4];            // weight sums over 64 positions
   float m;                  // largest score
 };
@@ -490,26 +492,46 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
         for (int k = 0; k < 16; ++k) pq[k] = T.part[k][t];
         w = ops::tree8(pq) + ops::tree8(pq + 8);
         z = (T.wsum[0] + T.wsum[1]) + (T.wsum[2] + T.wsum[3]);
-        if (nspan > 1) {
-          // the spans' sums: T over the positions is the balanced tree over
-          // 16 span slots (-0 past the last span) of the spans' trees
-          uint64_t *wp = A.wp + (size_t)hd * kBlockMaxSpans * kD + t;
-          uint64_t *zp = A.zp + (size_t)hd * kBlockMaxSpans;
-          if (c > 0) {
-            store_tagged(wp + (size_t)c * kD, w, tag + 7);
-            if (t == 0) store_tagged(zp + c, z, tag + 7);
-          } else {
-            float ws[kBlockMaxSpans], zs[kBlockMaxSpans];
-            ok = poll_span_sums<kBlockMaxSpans>(wp, kD, zp, nspan, tag + 7, ws, zs, err,
-                                                A.spin_ticks);
-            ws[0] = w;
-            zs[0] = z;
-            w = ops::tree8(ws) + ops::tree8(ws + 8);
-            z = ops::tree8(zs) + ops::tree8(zs + 8);
+      }
+      if (nspan > 1) {
+        // the spans' sums: T over the positions is the balanced tree over
+        // 16 span slots (-0 past the last span) of the spans' trees
+        uint64_t *wp = A.wp + (size_t)hd * kBlockMaxSpans * kD;
+        uint64_t *zp = A.zp + (size_t)hd * kBlockMaxSpans;
+        if (c > 0) {
+          if (t < kD) store_tagged(wp + (size_t)c * kD + t, w, tag + 7);
+          if (t == 0) store_tagged(zp + c, z, tag + 7);
+        } else {
+          // span 0 gathers them with every thread: column t % 128 of the
+          // spans 1 + 4 q .. 4 + 4 q (q = t / 128), and the weight sum of
+          // span t (t < 16), into LDS
+          const int i = t % kD, sp0 = 1 + 4 * (t / kD);
+          float v4[4];
+          ok = poll_tagged_strided<4>(wp + (size_t)sp0 * kD + i, kD, min(4, nspan - sp0),
+                                      tag + 7, v4, err, A.spin_ticks);
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (sp0 + k < kBlockMaxSpans) T.sw[sp0 + k][i] = v4[k];
+          if (t > 0 && t < kBlockMaxSpans) {
+            float zv = kNegZero;
+            if (t < nspan) ok &= poll_tagged<1>(zp + t, tag + 7, &zv, err, A.spin_ticks);
+            T.sz[t] = zv;
           }
+          if (t < kD) T.sw[0][t] = w;
+          if (t == 0) T.sz[0] = z;
         }
       }
       if (__syncthreads_or(!ok)) return;
+      if (nspan > 1 && c == 0 && t < kD) {
+        float ws[kBlockMaxSpans], zs[kBlockMaxSpans];
+#pragma unroll
+        for (int sp = 0; sp < kBlockMaxSpans; ++sp) {
+          ws[sp] = T.sw[sp][t];
+          zs[sp] = T.sz[sp];
+        }
+        w = ops::tree8(ws) + ops::tree8(ws + 8);
+        z = ops::tree8(zs) + ops::tree8(zs + 8);
+      }
       if (c == 0 && t < kD) {
         const double gd = (double)T.in[1][t];
         const float sig = (float)(1.0 / (1.0 + ops::fixed_exp(-gd)));

@@ -52,6 +52,35 @@ __device__ __forceinline__ bool poll_tagged(const uint64_t *p, uint32_t tag, flo
   }
 }
 
+// Polls the words p[k * stride], k < count (count <= N), until each
+// carries `tag`; v[k] gets their floats and v[k] = -0 from count on.
+template <int N>
+__device__ __forceinline__ bool poll_tagged_strided(const uint64_t *p, size_t stride, int count,
+                                                    uint32_t tag, float *v, uint32_t *err,
+                                                    long long spin_ticks) {
+  const long long t0 = wall_clock64();
+  for (int it = 1;; ++it) {
+    bool ready = true;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      v[k] = -0.0f;
+      if (k < count) {
+        const uint64_t w =
+            __hip_atomic_load(p + (size_t)k * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v[k] = __uint_as_float((uint32_t)w);
+        ready &= (uint32_t)(w >> 32) == tag;
+      }
+    }
+    if (ready) return true;
+    if ((it & 63) == 0 && load_word(err) != 0) return false;
+    if (wall_clock64() - t0 > spin_ticks) {
+      store_word(err, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 // The span sums of one attention head: w at wp[sp * stride] and z at zp[sp]
 // for the spans sp = 1 .. nspan - 1, all polled in each round; ws[0], zs[0]
 // are left to the caller and the slots from nspan to N - 1 are -0 (the
