@@ -119,6 +119,8 @@ struct Lds {
   float s[kSpan];      // scores of the span
   float e[kSpan];      // weights of the span
   float part[16][kD];  // value sums over 16 positions
+  float sw[kMaxSpans][kD];  // the spans' value sums (workgroup 0 of a head)
+  float sz[kMaxSpans];      // the spans' weight sums
   float wsum[4];       // weight sums over 64 positions
   float m;             // largest score
   float z;             // the span's weight sum
@@ -302,29 +304,55 @@ __global__ __launch_bounds__(kThreads) void atq_kernel(AtqArgs a) {
   __syncthreads();
 
   // ---- the span's sums; o (workgroup 0) --------------------------------------
+  float w = 0.0f, z = 0.0f;  // output column t's value sum and the weight sum
   if (out_t) {
-    const int i = t;
     float pq[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) pq[k] = S.part[k][i];
-    float w = tree8(pq) + tree8(pq + 8), z = S.z;
-    if (nspan > 1) {
-      uint64_t *wp = a.wp + (size_t)h * kMaxSpans * kD + i;
-      uint64_t *zp = a.zp + (size_t)h * kMaxSpans;
-      if (c > 0) {
-        store_tagged(wp + (size_t)c * kD, w, tag);
-        if (i == 0) store_tagged(zp + c, z, tag);
-      } else {
-        // every span's sums, polled together
-        float ws[kMaxSpans], zs[kMaxSpans];
-        ok = poll_span_sums<kMaxSpans>(wp, kD, zp, nspan, tag, ws, zs, err, a.spin_ticks);
-        ws[0] = w;
-        zs[0] = z;
-        w = tree8(ws) + tree8(ws + 8);
-        z = tree8(zs) + tree8(zs + 8);
+    for (int k = 0; k < 16; ++k) pq[k] = S.part[k][t];
+    w = tree8(pq) + tree8(pq + 8);
+    z = S.z;
+  }
+  if (nspan > 1) {
+    uint64_t *wp = a.wp + (size_t)h * kMaxSpans * kD;
+    uint64_t *zp = a.zp + (size_t)h * kMaxSpans;
+    if (c > 0) {
+      if (out_t) store_tagged(wp + (size_t)c * kD + t, w, tag);
+      if (t == 0) store_tagged(zp + c, z, tag);
+    } else {
+      // every thread polls: column t % 128 of the spans 1 + 2 q, 2 + 2 q
+      // (q = t / 128), and the weight sum of span t (t < 16), into LDS
+      const int i = t % kD, sp0 = 1 + 2 * (t / kD);
+      float v2[2];
+      ok = poll_tagged_strided<2>(wp + (size_t)sp0 * kD + i, kD, min(2, nspan - sp0), tag, v2,
+                                  err, a.spin_ticks);
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        if (sp0 + k < kMaxSpans) S.sw[sp0 + k][i] = v2[k];
+      if (t > 0 && t < kMaxSpans) {
+        float zv = kNegZero;
+        if (t < nspan) ok &= poll_tagged<1>(zp + t, tag, &zv, err, a.spin_ticks);
+        S.sz[t] = zv;
       }
+      if (out_t) S.sw[0][t] = w;
+      if (t == 0) S.sz[0] = z;
     }
-    if (c == 0 && ok) {
+  }
+  if (__syncthreads_or(!ok)) return;
+  if (out_t) {
+    const int i = t;
+    if (nspan > 1 && c == 0) {
+      // T over the positions: the balanced tree over 16 span slots (-0 past
+      // the last span) of the spans' trees
+      float ws[kMaxSpans], zs[kMaxSpans];
+#pragma unroll
+      for (int sp = 0; sp < kMaxSpans; ++sp) {
+        ws[sp] = S.sw[sp][i];
+        zs[sp] = S.sz[sp];
+      }
+      w = tree8(ws) + tree8(ws + 8);
+      z = tree8(zs) + tree8(zs + 8);
+    }
+    if (c == 0) {
       const float ov = (w / z) * gate_value(gv);
       a.o[(size_t)h * kD + i] = ov;
       const float s = sum64(ov);  // the wave holds 64 consecutive values

@@ -81,41 +81,6 @@ __device__ __forceinline__ bool poll_tagged_strided(const uint64_t *p, size_t st
   }
 }
 
-// The span sums of one attention head: w at wp[sp * stride] and z at zp[sp]
-// for the spans sp = 1 .. nspan - 1, all polled in each round; ws[0], zs[0]
-// are left to the caller and the slots from nspan to N - 1 are -0 (the
-// padding of a balanced tree over N slots).
-template <int N>
-__device__ __forceinline__ bool poll_span_sums(const uint64_t *wp, size_t stride,
-                                               const uint64_t *zp, int nspan, uint32_t tag,
-                                               float *ws, float *zs, uint32_t *err,
-                                               long long spin_ticks) {
-  const long long t0 = wall_clock64();
-  for (int it = 1;; ++it) {
-    bool ready = true;
-#pragma unroll
-    for (int sp = 1; sp < N; ++sp) {
-      ws[sp] = -0.0f;
-      zs[sp] = -0.0f;
-      if (sp < nspan) {
-        const uint64_t w =
-            __hip_atomic_load(wp + (size_t)sp * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t z = __hip_atomic_load(zp + sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ws[sp] = __uint_as_float((uint32_t)w);
-        zs[sp] = __uint_as_float((uint32_t)z);
-        ready &= (uint32_t)(w >> 32) == tag && (uint32_t)(z >> 32) == tag;
-      }
-    }
-    if (ready) return true;
-    if ((it & 63) == 0 && load_word(err) != 0) return false;
-    if (wall_clock64() - t0 > spin_ticks) {
-      store_word(err, 1u);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-}
-
 // The first half of a long wait: lanes [0, n) of the calling wave poll the
 // n consecutive words at p until each carries `tag` (their values are not
 // kept); the caller's workgroup barrier holds its other waves meanwhile.  A
