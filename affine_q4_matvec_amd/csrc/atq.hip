@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void atq_kernel(AtqArgs a) {
       // (q = t / 128), and the weight sum of span t (t < 16), into LDS
       const int i = t % kD, sp0 = 1 + 2 * (t / kD);
       float v2[2];
-      ok = poll_tagged_strided<2>(wp + (size_t)sp0 * kD + i, kD, min(2, nspan - sp0), tag, v2,
+      ok = poll_tagged_groups<1, 2>(wp + (size_t)sp0 * kD + i, kD, min(2, nspan - sp0), tag, v2,
                                   err, a.spin_ticks);
 #pragma unroll
       for (int k = 0; k < 2; ++k)

@@ -507,7 +507,7 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
           // span t (t < 16), into LDS
           const int i = t % kD, sp0 = 1 + 4 * (t / kD);
           float v4[4];
-          ok = poll_tagged_strided<4>(wp + (size_t)sp0 * kD + i, kD, min(4, nspan - sp0),
+          ok = poll_tagged_groups<1, 4>(wp + (size_t)sp0 * kD + i, kD, min(4, nspan - sp0),
                                       tag + 7, v4, err, A.spin_ticks);
 #pragma unroll
           for (int k = 0; k < 4; ++k)
@@ -629,8 +629,10 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
       // ---- stage B: h = h + down m ---------------------------------------------
       constexpr int kChunks = NP * kCols / 8;
       float xm[2][8] = {};
-      ok = true;
       __syncthreads();  // every wave of the workgroup is done with stage A
+      // (one chunk at a time: polling both in the same rounds doubles the
+      // polled traffic while the wait lasts, which measured slower)
+      ok = true;
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
         const int c = t + rr * kThreads;

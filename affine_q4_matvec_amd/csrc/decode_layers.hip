@@ -170,10 +170,12 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
     // chunk c = 8 consecutive values of m; chunks t and t + kThreads
     constexpr int kChunks = NP * kCols / 8;
     float xm[2][8];
-    ok = true;
     // the workgroup polls only once all its waves are done with stage A (a
     // poll that starts early only adds traffic at the lines being polled)
     __syncthreads();
+    // (one chunk at a time: polling both in the same rounds doubles the
+    // polled traffic while the wait lasts, which measured slower)
+    ok = true;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int c = t + r * kThreads;

@@ -52,23 +52,28 @@ __device__ __forceinline__ bool poll_tagged(const uint64_t *p, uint32_t tag, flo
   }
 }
 
-// Polls the words p[k * stride], k < count (count <= N), until each
-// carries `tag`; v[k] gets their floats and v[k] = -0 from count on.
-template <int N>
-__device__ __forceinline__ bool poll_tagged_strided(const uint64_t *p, size_t stride, int count,
-                                                    uint32_t tag, float *v, uint32_t *err,
-                                                    long long spin_ticks) {
+// Polls `groups` (at most M) groups of N consecutive words, group g at
+// p + g * stride, in one round each time, until every word carries `tag`;
+// v[N g + k] gets word k of group g, and -0 for the groups from `groups`
+// on.
+template <int N, int M>
+__device__ __forceinline__ bool poll_tagged_groups(const uint64_t *p, size_t stride, int groups,
+                                                   uint32_t tag, float *v, uint32_t *err,
+                                                   long long spin_ticks) {
   const long long t0 = wall_clock64();
   for (int it = 1;; ++it) {
     bool ready = true;
 #pragma unroll
-    for (int k = 0; k < N; ++k) {
-      v[k] = -0.0f;
-      if (k < count) {
-        const uint64_t w =
-            __hip_atomic_load(p + (size_t)k * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v[k] = __uint_as_float((uint32_t)w);
-        ready &= (uint32_t)(w >> 32) == tag;
+    for (int g = 0; g < M; ++g) {
+#pragma unroll
+      for (int k = 0; k < N; ++k) {
+        v[N * g + k] = -0.0f;
+        if (g < groups) {
+          const uint64_t w = __hip_atomic_load(p + (size_t)g * stride + k, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+          v[N * g + k] = __uint_as_float((uint32_t)w);
+          ready &= (uint32_t)(w >> 32) == tag;
+        }
       }
     }
     if (ready) return true;
