@@ -27,10 +27,11 @@
 //   stage B    every wave: one down row + the residual -> tagged h for the
 //              next layer's stage Q, or h (plain store) after the last
 // The weights of a wave's next rows are loaded before the wait that
-// precedes them (the next layer's Q rows before the wait for m).  The
+// precedes them (the next layer's Q rows before the wait for its h).  The
 // tags name the call (a counter per workgroup), the layer and the stage.
 // Every wait is bounded; one that runs out sets the error word and every
-// workgroup leaves at its next wait.  Compiled with -ffp-contract=off.
+// workgroup leaves at its next wait.  Compiled with -ffp-contract=off, and
+// with machine-level loop-invariant code motion off (build.py).
 #include <math.h>
 
 #include "decode_device.h"
@@ -151,12 +152,14 @@ __device__ __forceinline__ bool stage_rows_input(Lds<NP> &L, const float (*vals)
   return pairs;
 }
 
+// v, through an empty asm the optimiser cannot see through.
 __device__ __forceinline__ int opaque(int v) {
   asm volatile("" : "+v"(v));
   return v;
 }
 
-// The tags of layer l in call `call`: + 1 .. + 5 name the stage.
+// The tags of layer l in call `call`: + 1 .. + 7 name the stage (and the
+// attention stage's two exchanges between spans).
 __device__ __forceinline__ uint32_t stage_tag(uint32_t call, int l) {
   return (call << 8) | ((uint32_t)l << 3);
 }
@@ -210,7 +213,7 @@ __device__ __forceinline__ BlockLayer layer_at(const DecodeBlockArgs &A, int l) 
 
 template <bool FAST, int NP>
 __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs A) {
-  __shared__ Lds<NP> S;  // h (stage A) or m (stage B)
+  __shared__ Lds<NP> S;  // x = rmsq(h) (stage A) or m (stage B)
   __shared__ Lds<1> SO;  // h between layers (stage Q) or o (stage O)
   __shared__ AttnLds T;
   const int nwg = gridDim.x;
@@ -250,7 +253,8 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
     const bool mine = 8 * t < kCols;
     const bool odd = lane & 1;
     const BlockLayer Y = layer_at(A, l);
-    // + 1 q/gate/k/v, + 2 o, + 3 h after attention, + 4 m, + 5 h after the layer
+    // + 1 q/gate/k/v, + 2 o, + 3 h after attention, + 4 m, + 5 h after the
+    // layer, + 6 span maxima, + 7 span sums
     const uint32_t tag = stage_tag(call, l);
 
     // ---- stage Q --------------------------------------------------------------
