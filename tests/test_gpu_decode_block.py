@@ -231,7 +231,8 @@ def test_block_chain_fast_mode_equals_stage_kernels():
     assert err.max() <= 1e-4 * np.sqrt(np.mean(ref ** 2)), err.max()
 
 
-@pytest.mark.parametrize("max_pos,pos0,hkv", [(1024, 254, 4), (1024, 766, 1), (4096, 4092, 4)])
+@pytest.mark.parametrize("max_pos,pos0,hkv", [(1024, 254, 4), (1024, 766, 1), (2048, 1790, 16),
+                                             (4096, 4092, 4)])
 def test_block_chain_several_spans(max_pos, pos0, hkv):
     """Caches of 4 and 16 spans of 256 positions: one workgroup per head
     and span, the span maxima and sums exchanged as tagged words, steps
