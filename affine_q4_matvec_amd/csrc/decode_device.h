@@ -138,25 +138,47 @@ __device__ __forceinline__ void load_down(const DecodeLayer &L, int r, int lane,
 // weight loads of the next stage stay behind the loads of the current wait).
 __device__ __forceinline__ void issue_order() { asm volatile("" ::: "memory"); }
 
-// One gate/up block of np pairs: the row sums, then each (gate, up) pair
-// goes into the wave's SwiGLU batch (m[p0 + i]).
+// Appends the pair (gate, up) for m[out], the same in every lane, to the
+// wave's SwiGLU batch (swiglu_push of q4mv_device.h for values already
+// read from their lane).
+template <bool FAST, class Store>
+__device__ __forceinline__ void swiglu_push_uniform(const Store &store, SwigluBatch &b, int lane,
+                                                    float g, float u, int out) {
+  const bool mine = lane == b.count;
+  b.gate = mine ? g : b.gate;
+  b.up = mine ? u : b.up;
+  b.out = mine ? out : b.out;
+  b.count = b.count + 1;
+  if (b.count == kWave) swiglu_flush<FAST>(store, b);
+}
+
+// One gate/up block of np pairs: the group terms of all its rows, then the
+// row sums (rows 0..3 together by quad_row_sums, row j ending in lanes
+// [16 j, 16 j + 16); rows 4 and 5 in lane 63: the same tree as
+// wave_sum_lane63), then each (gate, up) pair goes into the wave's SwiGLU
+// batch (m[p0 + i]).
 template <bool FAST, bool PAIRS, class Store>
 __device__ __forceinline__ void gu_block(const GuBlock &a, const float *xv, float xsv, int lane,
                                          int p0, int np, const Store &store, SwigluBatch &batch,
                                          int negz) {
+  static_assert(kGuR == 6, "four rows by quad_row_sums, two by wave_sum_lane63");
   const bool odd = lane & 1;
+  float t[kGuR];
 #pragma unroll
-  for (int i = 0; i < kGuPairs; ++i) {
-    if (i < np) {
-      const float g = wave_sum_lane63(
-          group_term<FAST, PAIRS>(a.cw[2 * i], xv, a.sv[2 * i], a.bv[2 * i], xsv, true, odd), negz);
-      const float u = wave_sum_lane63(
-          group_term<FAST, PAIRS>(a.cw[2 * i + 1], xv, a.sv[2 * i + 1], a.bv[2 * i + 1], xsv, true,
-                                  odd),
-          negz);
-      swiglu_push<FAST>(store, batch, lane, g, u, p0 + i);
-    }
-  }
+  for (int j = 0; j < kGuR; ++j)
+    t[j] = j < 2 * np ? group_term<FAST, PAIRS>(a.cw[j], xv, a.sv[j], a.bv[j], xsv, true, odd)
+                      : kNegZero;
+  const float q = quad_row_sums(t[0], t[1], t[2], t[3]);
+  const float r4 = wave_sum_lane63(t[4], negz);
+  const float r5 = wave_sum_lane63(t[5], negz);
+  const auto at = [](float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+  };
+  const float g[kGuPairs] = {at(q, 15), at(q, 47), at(r4, kWave - 1)};
+  const float u[kGuPairs] = {at(q, 31), at(q, kWave - 1), at(r5, kWave - 1)};
+#pragma unroll
+  for (int i = 0; i < kGuPairs; ++i)
+    if (i < np) swiglu_push_uniform<FAST>(store, batch, lane, g[i], u[i], p0 + i);
 }
 
 // Stage A over the wave's pairs [pb, pe) in blocks of kGuPairs; `a` holds
