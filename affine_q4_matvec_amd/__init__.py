@@ -412,6 +412,11 @@ class AttnBlock:
     def __init__(self, qgkv: Q4Matrix, o: Q4Matrix, wa: torch.Tensor, wq: torch.Tensor,
                  wk: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor, mlp: "MlpLayer"):
         f = torch.float32
+        # the library trusts max_pos for the caches' sizes: the shapes are
+        # checked here, where they are known
+        if kcache.dim() != 3 or kcache.shape[2] != ATQ_D or tuple(vcache.shape) != tuple(
+                kcache.shape):
+            raise ValueError("kcache and vcache must both be [hkv, max_pos, %d]" % ATQ_D)
         self._keep = (qgkv, o, wa, wq, wk, kcache, vcache, mlp)
         self.kcache, self.vcache = kcache, vcache
         self._c = _AttnBlock(qgkv._c, o._c, _dev(wa, f, 2048, "wa"), _dev(wq, f, ATQ_D, "wq"),
@@ -452,6 +457,8 @@ class BlockStack:
             raise ValueError("no layers")
         self.blocks = blocks
         self.max_pos = int(blocks[0].kcache.shape[1])
+        if any(int(b.kcache.shape[1]) != self.max_pos for b in blocks):
+            raise ValueError("every layer's caches must hold the same number of positions")
         arr = (_AttnBlock * len(blocks))(*[b._c for b in blocks])
         h = _vp()
         _check("q4_block_stack_create",

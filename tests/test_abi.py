@@ -352,3 +352,17 @@ def test_block_stack_argument_checks(L):
     p = ctypes.c_void_p
     assert L.q4_decode_blocks(None, f, p(A), p(B), p(C), p(D), p(E), ctypes.c_size_t(1 << 21), 0,
                               None) == EINVAL
+
+
+
+def test_block_wrapper_checks_cache_shapes():
+    """AttnBlock checks what the C ABI takes on trust (the caches' shape
+    against max_pos) before touching anything else."""
+    import torch
+    import affine_q4_matvec_amd as q4
+    with pytest.raises(ValueError):
+        q4.AttnBlock(None, None, None, None, None, torch.zeros(4, 16, 64), torch.zeros(4, 16, 64),
+                     None)
+    with pytest.raises(ValueError):
+        q4.AttnBlock(None, None, None, None, None, torch.zeros(4, 16, 128), torch.zeros(4, 8, 128),
+                     None)

@@ -253,3 +253,17 @@ def test_block_chain_several_spans(max_pos, pos0, hkv):
         assert_bits_equal(host(chain.layers[l]["kc"]).ravel(), kc[l].ravel(), "layer %d kcache" % l)
         assert_bits_equal(host(chain.layers[l]["vc"]).ravel(), vc[l].ravel(), "layer %d vcache" % l)
     assert lib().q4_decode_block_status(chain.block_ws, s) == lib().Q4_OK
+
+
+def test_stack_rejects_caches_of_other_lengths():
+    from affine_q4_matvec_amd.chain import AttnDecodeChain
+    q4 = lib()
+    w = synth.attn_chain_weights(seed=70, layers=2, vocab=4096, max_pos=32)
+    chain = AttnDecodeChain(w, persistent=True)
+    lw = chain.layers[1]
+    short = q4.AttnBlock(lw["qgkv"], lw["o"], lw["wa"], lw["wq"], lw["wk"],
+                         torch.zeros(w["hkv"], 16, 128, device="cuda"),
+                         torch.zeros(w["hkv"], 16, 128, device="cuda"),
+                         q4.MlpLayer(lw["gu"], lw["down"], lw["wn"]))
+    with pytest.raises(ValueError):
+        q4.BlockStack([chain.layers[0]["blk"], short])
