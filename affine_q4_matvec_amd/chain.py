@@ -211,12 +211,12 @@ class AttnDecodeChain(DecodeChain):
       t' = argmax(head rmsq(h, wn_final));  p = p + 1
 
     Token and position live on the device, so one captured step is
-    replayed token after token; 2 + 5 per layer + 1 kernels.  The
+    replayed token after token; 4 + 5 per layer kernels.  The
     attention block is the product set's Q/K/V/O stages given their
     dataflow (the gate rows are an addition: the attention step gates its
     output).  persistent=True runs every layer in one persistent launch
     (q4_decode_blocks over stacks of at most 32 layers, caches of at most
-    4096 positions): 4 kernels for up to 32 layers, the same bits."""
+    4096 positions): 5 kernels for up to 32 layers, the same bits."""
 
     def __init__(self, weights: dict, mode: int = FIXED, layers: int | None = None,
                  device: str = "cuda", persistent: bool = False):
@@ -277,9 +277,11 @@ class AttnDecodeChain(DecodeChain):
         torch.cuda.synchronize()
 
     def kernels_per_token(self) -> int:
+        # embed, the layers, the head and argmax's final kernel, the
+        # position advance
         if self.persistent:
-            return 3 + len(self.stacks)
-        return 3 + 5 * len(self.layers)
+            return 4 + len(self.stacks)
+        return 4 + 5 * len(self.layers)
 
     def bytes_per_token(self) -> int:
         """Algorithmic bytes at position 0: every product's weights and
