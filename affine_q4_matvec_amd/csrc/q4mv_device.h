@@ -278,11 +278,17 @@ __device__ __forceinline__ void select_product(const ProdGroup &grp, Prod &P, in
 // Pre-scales the lane's activations for the pair decode when every
 // activation of the wave is below 2^118 in magnitude (NaN counts as large);
 // returns whether the wave may use the pair decode.
+// The test is one integer maximum over the magnitudes' bit patterns: with
+// the sign cleared, binary32 bits order like the magnitudes, and every NaN
+// and infinity lies above the bits of 2^118 (0x7A800000).
 __device__ __forceinline__ bool prescale_for_pairs(float *xv) {
-  bool large = false;
+  uint32_t m = 0;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) large |= !(__builtin_fabsf(xv[k]) < 0x1p118f);
-  if (__any(large)) return false;
+  for (int k = 0; k < 32; ++k) {
+    const uint32_t a = __float_as_uint(xv[k]) & 0x7FFFFFFFu;
+    m = a > m ? a : m;
+  }
+  if (__any(m >= 0x7A800000u)) return false;
   const float scale = 1.0f / fp8_unit();  // 2^9 or 2^10, exact
 #pragma unroll
   for (int k = 0; k < 32; ++k) xv[k] = xv[k] * scale;
@@ -362,9 +368,5 @@ __device__ __forceinline__ void swiglu_push(const Store &store, SwigluBatch &b, 
   if (b.count == kWave) swiglu_flush<FAST>(store, b);
 }
 
-// Blocks of R rows dealt round-robin to the waves: r0, r0 + stride, ...
-// Each block is loaded at the top of its iteration (issuing the next
-// block's loads while summing the current one would keep two blocks of
-// registers live); with PRELOAD, `a` holds the first block's loads on entry.
 }  // namespace dev
 }  // namespace q4

@@ -44,6 +44,13 @@
 #ifndef Q4_ROW64_OCC_PCT
 #define Q4_ROW64_OCC_PCT 100  // share of the resident workgroups launched
 #endif
+#ifndef Q4_ROW64_LOOP_WG_PER_CU
+// Workgroups per compute unit (waves per SIMD) of a row64 launch whose
+// waves loop over several blocks.  Measured on the 248320-row head: 4 is
+// 1-2 us faster than the 7 that fit (fixed order), the same in fast order;
+// 3 and 2 are slower.
+#define Q4_ROW64_LOOP_WG_PER_CU 4
+#endif
 #ifndef Q4_SPLIT_R
 #define Q4_SPLIT_R 4  // a multiple of 4
 #endif
@@ -115,6 +122,93 @@ struct RunningMax {
   }
 };
 
+// One block of rows [r, r + nrows) held in `a`: group terms, row sums in the
+// tree T, then the epilogue.  R a multiple of 4: four rows reduced at once,
+// row j of a quad ending in lane 16 j + 15; otherwise each row on its own,
+// ending in lane 63.
+template <int R, bool FAST, bool PAIRS, int EPI, class Store>
+__device__ __forceinline__ void row64_block(const Prod &P, const float *xv, float xsv, int lane,
+                                            int negz, int r, int nrows, const Row64Block<R> &a,
+                                            RunningMax &best, SwigluBatch &batch,
+                                            const Store &store_m) {
+  const bool odd = lane & 1;
+  constexpr bool kQuad = R % 4 == 0;
+  constexpr int kSums = kQuad ? R / 4 : R;
+  const int jq = kQuad ? lane >> 4 : 0;
+  const bool holder = kQuad ? (lane & 15) == 15 : lane == kWave - 1;
+  float tq[kSums];
+  if constexpr (kQuad) {
+#pragma unroll
+    for (int q = 0; q < R / 4; ++q) {
+      float gt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        gt[j] = group_term<FAST, PAIRS>(a.cw[4 * q + j], xv, a.sv[4 * q + j], a.bv[4 * q + j],
+                                        xsv, true, odd);
+      tq[q] = quad_row_sums(gt[0], gt[1], gt[2], gt[3]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      tq[j] = wave_sum_lane63(
+          group_term<FAST, PAIRS>(a.cw[j], xv, a.sv[j], a.bv[j], xsv, true, odd), negz);
+  }
+  if constexpr (EPI == kEpiSwiglu) {
+    // (gate, up) = rows (2i, 2i + 1) of the block
+#pragma unroll
+    for (int i = 0; 2 * i + 1 < R; ++i) {
+      if (2 * i + 1 < nrows) {
+        const int jg = 2 * i, ju = 2 * i + 1;
+        const int bg = __float_as_int(tq[kQuad ? jg / 4 : jg]);
+        const int bu = __float_as_int(tq[kQuad ? ju / 4 : ju]);
+        const float g = __int_as_float(__builtin_amdgcn_readlane(bg, kQuad ? 16 * (jg % 4) + 15 : 63));
+        const float u = __int_as_float(__builtin_amdgcn_readlane(bu, kQuad ? 16 * (ju % 4) + 15 : 63));
+        swiglu_push<FAST>(store_m, batch, lane, g, u, (r + jg) >> 1);
+      }
+    }
+  } else if (holder) {
+#pragma unroll
+    for (int k = 0; k < kSums; ++k) {
+      const int j = kQuad ? 4 * k + jq : k;
+      if (j < nrows) {
+        float v = tq[k];
+        if (P.res) v = P.res[r + j] + v;
+        P.y[r + j] = v;
+        if constexpr (EPI == kEpiArgmax) {
+          // a lane's rows arrive in increasing order: strictly greater
+          // keeps the lowest index of equal values (and -0 == +0)
+          const bool gt = (v > best.value) || best.index < 0;
+          best.value = gt ? v : best.value;
+          best.index = gt ? r + j : best.index;
+          best.nan |= v != v;
+        }
+      }
+    }
+  }
+}
+
+// Issue priority from a wave's progress: 3 over the first quarter of its
+// nblk blocks, then 2, 1 and 0.  A SIMD otherwise favours its oldest waves,
+// which then run out of blocks long before its youngest: the last part of
+// the launch would be left to one or two waves per SIMD, too few to hide
+// the loads' latency.  Waves that fall behind now get the issue slots, so
+// all of a SIMD's waves keep working until close to the end.
+__device__ __forceinline__ void progress_priority(int k, int nblk) {
+  const int q = (4 * k) / nblk;  // wave-uniform
+  if (q == 0)
+    __builtin_amdgcn_s_setprio(3);
+  else if (q == 1)
+    __builtin_amdgcn_s_setprio(2);
+  else if (q == 2)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
+// Blocks of R rows dealt round-robin to the waves: r0, r0 + stride, ...
+// Each block is loaded at the top of its iteration (issuing the next
+// block's loads while summing the current one would keep two blocks of
+// registers live); with PRELOAD, `a` holds the first block's loads on entry.
 template <int R, bool FAST, bool PAIRS, int EPI, bool PRELOAD>
 __device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, const float *xv,
                                            float xsv, int lane, int r0, int stride,
@@ -122,71 +216,65 @@ __device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, const
   const uint32_t voff_q = 16u * lane;
   const uint32_t voff_g = 4u * (lane >> 1);
   const int end = P.rows;
-  const bool odd = lane & 1;
   SwigluBatch batch;
   float *m_out = ex.m_out;
   const auto store_m = [m_out](int i, float v) { m_out[i] = v; };
-  // R a multiple of 4: four rows reduced at once, row j of a quad ending in
-  // lane 16 j + 15; otherwise each row on its own, ending in lane 63
-  constexpr bool kQuad = R % 4 == 0;
-  constexpr int kSums = kQuad ? R / 4 : R;
-  const int jq = kQuad ? lane >> 4 : 0;
-  const bool holder = kQuad ? (lane & 15) == 15 : lane == kWave - 1;
-  const int negz = neg_zero_reg();
-  for (int r = r0; r < end; r += stride) {
+  const int negz = R % 4 == 0 ? 0 : neg_zero_reg();  // only the one-row sums use it
+  const int nblk = r0 < end ? (end - r0 + stride - 1) / stride : 1;
+  int k = 0;
+  for (int r = r0; r < end; r += stride, ++k) {
+    progress_priority(k, nblk);
     const int nrows = min(R, end - r);
     if (!PRELOAD || r != r0) row64_load<R>(P, r, nrows, voff_q, voff_g, a);
-    float tq[kSums];
-    if constexpr (kQuad) {
-#pragma unroll
-      for (int q = 0; q < R / 4; ++q) {
-        float gt[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          gt[j] = group_term<FAST, PAIRS>(a.cw[4 * q + j], xv, a.sv[4 * q + j], a.bv[4 * q + j],
-                                          xsv, true, odd);
-        tq[q] = quad_row_sums(gt[0], gt[1], gt[2], gt[3]);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < R; ++j)
-        tq[j] = wave_sum_lane63(
-            group_term<FAST, PAIRS>(a.cw[j], xv, a.sv[j], a.bv[j], xsv, true, odd), negz);
-    }
-    if constexpr (EPI == kEpiSwiglu) {
-      // (gate, up) = rows (2i, 2i + 1) of the block
-#pragma unroll
-      for (int i = 0; 2 * i + 1 < R; ++i) {
-        if (2 * i + 1 < nrows) {
-          const int jg = 2 * i, ju = 2 * i + 1;
-          const int bg = __float_as_int(tq[kQuad ? jg / 4 : jg]);
-          const int bu = __float_as_int(tq[kQuad ? ju / 4 : ju]);
-          const float g = __int_as_float(__builtin_amdgcn_readlane(bg, kQuad ? 16 * (jg % 4) + 15 : 63));
-          const float u = __int_as_float(__builtin_amdgcn_readlane(bu, kQuad ? 16 * (ju % 4) + 15 : 63));
-          swiglu_push<FAST>(store_m, batch, lane, g, u, (r + jg) >> 1);
-        }
-      }
-    } else if (holder) {
-#pragma unroll
-      for (int k = 0; k < kSums; ++k) {
-        const int j = kQuad ? 4 * k + jq : k;
-        if (j < nrows) {
-          float v = tq[k];
-          if (P.res) v = P.res[r + j] + v;
-          P.y[r + j] = v;
-          if constexpr (EPI == kEpiArgmax) {
-            // a lane's rows arrive in increasing order: strictly greater
-            // keeps the lowest index of equal values (and -0 == +0)
-            const bool gt = (v > best.value) || best.index < 0;
-            best.value = gt ? v : best.value;
-            best.index = gt ? r + j : best.index;
-            best.nan |= v != v;
-          }
-        }
-      }
-    }
+    row64_block<R, FAST, PAIRS, EPI>(P, xv, xsv, lane, negz, r, nrows, a, best, batch, store_m);
   }
   if constexpr (EPI == kEpiSwiglu) swiglu_flush<FAST>(store_m, batch);
+}
+
+// The plain prologues (kProX, kProXsum) with the store epilogue: the
+// activations are read after the first block's loads have gone out, so
+// that those HBM loads are in flight while the activations arrive (every
+// wave reads the same 8 KB of them at the start, from L2).  The pair decode
+// is chosen per block (wave-uniform) since the activations come in inside
+// the loop.
+template <int R, bool FAST, int PRO>
+__device__ __forceinline__ void row64_rows_x_late(const Prod &P, int lane, int r0, int stride) {
+  const uint32_t voff_q = 16u * lane;
+  const uint32_t voff_g = 4u * (lane >> 1);
+  const int end = P.rows;
+  const int negz = R % 4 == 0 ? 0 : neg_zero_reg();  // only the one-row sums use it
+  const int nblk = r0 < end ? (end - r0 + stride - 1) / stride : 1;
+  // defined before the loop: a value first set inside it would be an
+  // undefined loop-carried value, which costs registers
+  float xv[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) xv[i] = 0.0f;
+  float xsv = 0.0f;
+  bool pairs = false;
+  RunningMax best;
+  SwigluBatch batch;
+  const auto no_store = [](int, float) {};
+  Row64Block<R> a;
+  int k = 0;
+  for (int r = r0; r < end; r += stride, ++k) {
+    progress_priority(k, nblk);
+    const int nrows = min(R, end - r);
+    row64_load<R>(P, r, nrows, voff_q, voff_g, a);
+    if (k == 0) {
+      // the lane index hidden from the optimiser, so that the activations'
+      // addresses are formed here and not held through the loop
+      int l = lane;
+      asm volatile("" : "+v"(l));
+      chunk_inputs<PRO>(P, l, true, xv, xsv);
+      pairs = prescale_for_pairs(xv);
+    }
+    if (pairs)
+      row64_block<R, FAST, true, kEpiStore>(P, xv, xsv, lane, negz, r, nrows, a, best, batch,
+                                            no_store);
+    else
+      row64_block<R, FAST, false, kEpiStore>(P, xv, xsv, lane, negz, r, nrows, a, best, batch,
+                                             no_store);
+  }
 }
 
 // PRELOAD: issue the first block's loads before the activations are formed
@@ -201,6 +289,11 @@ __global__ __launch_bounds__(kThreads) void q4mv_row64_kernel(ProdGroup grp, Ext
   const int wave = wave_index();
   const int wpg = kThreads / kWave;
   const int first = (lw * wpg + wave) * R, stride = nwg * wpg * R;
+
+  if constexpr (PRO != kProNorm && EPI == kEpiStore && !PRELOAD) {
+    row64_rows_x_late<R, FAST, PRO>(P, lane, first, stride);
+    return;
+  }
 
   Row64Block<R> a;
   if (PRELOAD && first < P.rows)
@@ -517,13 +610,13 @@ hipError_t dispatch_row64(const ProdGroup &g, const Shape &sh, const Extra &ex, 
 }
 
 // Workgroups of a row64 kernel variant that fit on the current device at
-// once: its occupancy per compute unit times the compute units, queried
-// once per device and variant.
+// once: its occupancy per compute unit (at most limit_per_cu if that is
+// positive) times the compute units, queried once per device and variant.
 constexpr int kMaxDevices = 64;
 constexpr int kVariantSlots = 2 * 2 * 3 * 3;  // mode x preload x prologue x epilogue
 std::atomic<int> g_resident[kMaxDevices][kVariantSlots];
 
-int resident_workgroups(const void *kernel, int slot) {
+int resident_workgroups(const void *kernel, int slot, int limit_per_cu) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev < 0 || dev >= kMaxDevices || slot < 0 || slot >= kVariantSlots) return 0;
@@ -533,6 +626,7 @@ int resident_workgroups(const void *kernel, int slot) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
+  if (limit_per_cu > 0 && per_cu > limit_per_cu) per_cu = limit_per_cu;
   int v = (per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
   v = v * Q4_ROW64_OCC_PCT / 100;
   if (v < 1) v = 1;
@@ -570,7 +664,8 @@ int32_t row64_capacity(const Shape &sh, int mode, bool preload) {
                        : (preload ? row64_ptr<false, true>(sh.pro, sh.epi)
                                   : row64_ptr<false, false>(sh.pro, sh.epi));
   if (!k) return 0;
-  return resident_workgroups(k, 18 * (fast ? 1 : 0) + 9 * (preload ? 1 : 0) + 3 * sh.pro + sh.epi);
+  return resident_workgroups(k, 18 * (fast ? 1 : 0) + 9 * (preload ? 1 : 0) + 3 * sh.pro + sh.epi,
+                             preload ? 0 : Q4_ROW64_LOOP_WG_PER_CU);
 }
 
 int32_t resident_capacity(const Shape &sh, int mode) {
@@ -583,8 +678,9 @@ int32_t workgroups_for(const Shape &sh, int32_t rows, int mode) {
   switch (sh.kind) {
     case Shape::kRow64: {
       // one block of R rows per wave if that fits on the device at once
-      // (the preloading variant then runs); otherwise as many workgroups as
-      // fit at once, none waiting for a second round
+      // (the preloading variant then runs); otherwise Q4_ROW64_LOOP_WG_PER_CU
+      // workgroups per compute unit (or fewer if fewer fit), all resident
+      // at once
       const long long need = (rows + wpg * Q4_ROW64_R - 1) / (wpg * Q4_ROW64_R);
       const int cap_pre = row64_capacity(sh, mode, true);
       if (cap_pre > 0 && need <= cap_pre) return clamp_wg(need, cap_pre);
