@@ -205,45 +205,74 @@ __device__ __forceinline__ void progress_priority(int k, int nblk) {
     __builtin_amdgcn_s_setprio(0);
 }
 
-// Blocks of R rows dealt round-robin to the waves: r0, r0 + stride, ...
-// Each block is loaded at the top of its iteration (issuing the next
-// block's loads while summing the current one would keep two blocks of
-// registers live); with PRELOAD, `a` holds the first block's loads on entry.
-template <int R, bool FAST, bool PAIRS, int EPI, bool PRELOAD>
-__device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, const float *xv,
-                                           float xsv, int lane, int r0, int stride,
-                                           Row64Block<R> &a, RunningMax &best) {
-  const uint32_t voff_q = 16u * lane;
-  const uint32_t voff_g = 4u * (lane >> 1);
-  const int end = P.rows;
+// x = rmsq(h, wn) over the workgroup into LDS (4 floats of padding after
+// every 32, so that the lanes' 16-byte reads of their 32 values hit
+// distinct banks); the lane's 32 values and its group's sum.  Every wave of
+// the workgroup must call it (two barriers).  The first workgroup also
+// publishes u and its group sums when asked.
+__device__ __forceinline__ void norm_prologue(const Extra &ex, int lw, int lane, float *xv,
+                                              float &xsv) {
+  __shared__ float red[17];
+  __shared__ float su[2048 + 2048 / 8];
+  __shared__ float sus[32];
+  float hv[8], wv[8];
+  const float rho = ops::rmsq_rho(ex.h, ex.wn, 2048, ex.eps, red, hv, wv);
+  ops::rmsq_u<4>(2048, rho, hv, wv, su, sus);
+  __syncthreads();
+  if (lw == 0 && ex.u_out) {
+    for (int i = threadIdx.x; i < 2048; i += kThreads) ex.u_out[i] = su[i + (i >> 5) * 4];
+    if (threadIdx.x < 32) ex.us_out[threadIdx.x] = sus[threadIdx.x];
+  }
+  load_x_values(su + 36 * lane, true, xv);
+  xsv = sus[lane >> 1];
+}
+
+// The activations of the lane: the prologue's.  `l` is the lane index.
+template <int PRO>
+__device__ __forceinline__ void row64_inputs(const Prod &P, const Extra &ex, int lw, int l,
+                                             float *xv, float &xsv) {
+  if constexpr (PRO == kProNorm)
+    norm_prologue(ex, lw, l, xv, xsv);
+  else
+    chunk_inputs<PRO>(P, l, true, xv, xsv);
+}
+
+// PRELOAD (every wave has at most one block): the block's loads were issued
+// before the prologue and `a` holds them.
+template <int R, bool FAST, bool PAIRS, int EPI>
+__device__ __forceinline__ void row64_single(const Prod &P, const Extra &ex, const float *xv,
+                                             float xsv, int lane, int r, Row64Block<R> &a,
+                                             RunningMax &best) {
+  if (r >= P.rows) return;
   SwigluBatch batch;
   float *m_out = ex.m_out;
   const auto store_m = [m_out](int i, float v) { m_out[i] = v; };
   const int negz = R % 4 == 0 ? 0 : neg_zero_reg();  // only the one-row sums use it
-  const int nblk = r0 < end ? (end - r0 + stride - 1) / stride : 1;
-  int k = 0;
-  for (int r = r0; r < end; r += stride, ++k) {
-    progress_priority(k, nblk);
-    const int nrows = min(R, end - r);
-    if (!PRELOAD || r != r0) row64_load<R>(P, r, nrows, voff_q, voff_g, a);
-    row64_block<R, FAST, PAIRS, EPI>(P, xv, xsv, lane, negz, r, nrows, a, best, batch, store_m);
-  }
+  row64_block<R, FAST, PAIRS, EPI>(P, xv, xsv, lane, negz, r, min(R, P.rows - r), a, best, batch,
+                                   store_m);
   if constexpr (EPI == kEpiSwiglu) swiglu_flush<FAST>(store_m, batch);
 }
 
-// The plain prologues (kProX, kProXsum) with the store epilogue: the
-// activations are read after the first block's loads have gone out, so
-// that those HBM loads are in flight while the activations arrive (every
-// wave reads the same 8 KB of them at the start, from L2).  The pair decode
-// is chosen per block (wave-uniform) since the activations come in inside
-// the loop.
-template <int R, bool FAST, int PRO>
-__device__ __forceinline__ void row64_rows_x_late(const Prod &P, int lane, int r0, int stride) {
+// Blocks of R rows dealt round-robin to the waves: r0, r0 + stride, ...
+// Each block is loaded at the top of its iteration (issuing the next
+// block's loads while summing the current one keeps two blocks of
+// registers live and measured no faster).  The activations are formed in
+// the first iteration, after its block's loads have gone out, so that
+// those HBM loads are in flight while the prologue runs (the activations
+// come from L2, or from rmsq over the workgroup).  Every wave runs the
+// first iteration, also one without rows (the rmsq prologue has
+// barriers); the pair decode is then chosen per block (wave-uniform).
+template <int R, bool FAST, int PRO, int EPI>
+__device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, int lw, int lane,
+                                           int r0, int stride, RunningMax &best) {
   const uint32_t voff_q = 16u * lane;
   const uint32_t voff_g = 4u * (lane >> 1);
   const int end = P.rows;
   const int negz = R % 4 == 0 ? 0 : neg_zero_reg();  // only the one-row sums use it
   const int nblk = r0 < end ? (end - r0 + stride - 1) / stride : 1;
+  SwigluBatch batch;
+  float *m_out = ex.m_out;
+  const auto store_m = [m_out](int i, float v) { m_out[i] = v; };
   // defined before the loop: a value first set inside it would be an
   // undefined loop-carried value, which costs registers
   float xv[32];
@@ -251,35 +280,34 @@ __device__ __forceinline__ void row64_rows_x_late(const Prod &P, int lane, int r
   for (int i = 0; i < 32; ++i) xv[i] = 0.0f;
   float xsv = 0.0f;
   bool pairs = false;
-  RunningMax best;
-  SwigluBatch batch;
-  const auto no_store = [](int, float) {};
   Row64Block<R> a;
   int k = 0;
-  for (int r = r0; r < end; r += stride, ++k) {
+  for (int r = r0; k == 0 || r < end; r += stride, ++k) {
     progress_priority(k, nblk);
-    const int nrows = min(R, end - r);
-    row64_load<R>(P, r, nrows, voff_q, voff_g, a);
+    // a wave without rows loads from a buffer of zero bytes: nothing
+    const int nrows = r < end ? min(R, end - r) : 0;
+    row64_load<R>(P, r < end ? r : 0, nrows, voff_q, voff_g, a);
     if (k == 0) {
       // the lane index hidden from the optimiser, so that the activations'
       // addresses are formed here and not held through the loop
       int l = lane;
       asm volatile("" : "+v"(l));
-      chunk_inputs<PRO>(P, l, true, xv, xsv);
+      row64_inputs<PRO>(P, ex, lw, l, xv, xsv);
       pairs = prescale_for_pairs(xv);
     }
-    if (pairs)
-      row64_block<R, FAST, true, kEpiStore>(P, xv, xsv, lane, negz, r, nrows, a, best, batch,
-                                            no_store);
-    else
-      row64_block<R, FAST, false, kEpiStore>(P, xv, xsv, lane, negz, r, nrows, a, best, batch,
-                                             no_store);
+    if (nrows > 0) {
+      if (pairs)
+        row64_block<R, FAST, true, EPI>(P, xv, xsv, lane, negz, r, nrows, a, best, batch, store_m);
+      else
+        row64_block<R, FAST, false, EPI>(P, xv, xsv, lane, negz, r, nrows, a, best, batch,
+                                         store_m);
+    }
   }
+  if constexpr (EPI == kEpiSwiglu) swiglu_flush<FAST>(store_m, batch);
 }
 
-// PRELOAD: issue the first block's loads before the activations are formed
-// (for launches where every wave has one block: the loads' latency then
-// overlaps the prologue).  Without it the kernel needs fewer registers.
+// PRELOAD: issue the first block's loads before the activations are formed,
+// for launches where every wave has one block at most.
 template <int R, bool FAST, int PRO, int EPI, bool PRELOAD>
 __global__ __launch_bounds__(kThreads) void q4mv_row64_kernel(ProdGroup grp, Extra ex) {
   Prod P;
@@ -290,42 +318,21 @@ __global__ __launch_bounds__(kThreads) void q4mv_row64_kernel(ProdGroup grp, Ext
   const int wpg = kThreads / kWave;
   const int first = (lw * wpg + wave) * R, stride = nwg * wpg * R;
 
-  if constexpr (PRO != kProNorm && EPI == kEpiStore && !PRELOAD) {
-    row64_rows_x_late<R, FAST, PRO>(P, lane, first, stride);
-    return;
-  }
-
-  Row64Block<R> a;
-  if (PRELOAD && first < P.rows)
-    row64_load<R>(P, first, min(R, P.rows - first), 16u * lane, 4u * (lane >> 1), a);
-
-  float xv[32];
-  float xsv;
-  if constexpr (PRO == kProNorm) {
-    // rmsq over the workgroup into LDS (4 floats of padding after every 32,
-    // so that the lanes' 16-byte reads of their 32 values hit distinct banks)
-    __shared__ float red[17];
-    __shared__ float su[2048 + 2048 / 8];
-    __shared__ float sus[32];
-    float hv[8], wv[8];
-    const float rho = ops::rmsq_rho(ex.h, ex.wn, 2048, ex.eps, red, hv, wv);
-    ops::rmsq_u<4>(2048, rho, hv, wv, su, sus);
-    __syncthreads();
-    if (lw == 0 && ex.u_out) {  // the first workgroup also publishes u
-      for (int i = threadIdx.x; i < 2048; i += kThreads) ex.u_out[i] = su[i + (i >> 5) * 4];
-      if (threadIdx.x < 32) ex.us_out[threadIdx.x] = sus[threadIdx.x];
-    }
-    load_x_values(su + 36 * lane, true, xv);
-    xsv = sus[lane >> 1];
-  } else {
-    chunk_inputs<PRO>(P, lane, true, xv, xsv);
-  }
-
   RunningMax best;
-  if (prescale_for_pairs(xv))
-    row64_rows<R, FAST, true, EPI, PRELOAD>(P, ex, xv, xsv, lane, first, stride, a, best);
-  else
-    row64_rows<R, FAST, false, EPI, PRELOAD>(P, ex, xv, xsv, lane, first, stride, a, best);
+  if constexpr (!PRELOAD) {
+    row64_rows<R, FAST, PRO, EPI>(P, ex, lw, lane, first, stride, best);
+  } else {
+    Row64Block<R> a;
+    if (first < P.rows)
+      row64_load<R>(P, first, min(R, P.rows - first), 16u * lane, 4u * (lane >> 1), a);
+    float xv[32];
+    float xsv;
+    row64_inputs<PRO>(P, ex, lw, lane, xv, xsv);
+    if (prescale_for_pairs(xv))
+      row64_single<R, FAST, true, EPI>(P, ex, xv, xsv, lane, first, a, best);
+    else
+      row64_single<R, FAST, false, EPI>(P, ex, xv, xsv, lane, first, a, best);
+  }
 
   if constexpr (EPI == kEpiArgmax) {
     // one key per workgroup; a second kernel reduces them (a single counter

@@ -189,6 +189,33 @@ def test_q4mv_head_248320x2048_full():
     assert_bits_equal(host(y), want, "head")
 
 
+@pytest.mark.parametrize("rows", [20483, 61447])
+@pytest.mark.parametrize("with_xsum", [True, False])
+def test_q4mv_looping_launch_ragged(rows, with_xsum):
+    """More rows than one 4-row block per resident wave, so that the waves
+    loop over 1-4 blocks each (the activations read after the first
+    block's loads, the issue priority stepped by progress), with a partial
+    last block; the group sums given, or formed in the kernel.  Fixed order
+    bit-exact; fast order within its bound."""
+    print("q4mv looping %dx2048 xsum %s" % (rows, with_xsum), flush=True)
+    m = synth.small_product(seed=21, rows=rows, cols=2048, name="loop%d" % rows)
+    xs = oracle.group_sums(m["x"])
+    q4 = lib()
+    W = q4.Q4Matrix.from_host(m)
+    xd = dev(m["x"])
+    xsd = dev(xs) if with_xsum else None
+    want = oracle.q4mv(m, m["x"], xs, NTHREADS)
+    y = q4.q4mv(W, xd, xsd, mode=0)
+    torch.cuda.synchronize()
+    assert_bits_equal(host(y), want, "looping fixed %d" % rows)
+    y = q4.q4mv(W, xd, xsd, mode=1)
+    torch.cuda.synchronize()
+    got, w64 = host(y).astype(np.float64), want.astype(np.float64)
+    rms = np.sqrt(np.mean(w64**2))
+    err = np.abs(got - w64)
+    assert np.all(err <= 1e-5 * np.abs(w64) + 1e-5 * rms), err.max()
+
+
 @pytest.mark.parametrize("rows,cols", [(13, 128), (1000, 2048), (31, 6144), (5, 192)])
 def test_q4mv_fast_within_tolerance(rows, cols):
     m = synth.small_product(seed=9, rows=rows, cols=cols, name="f%d_%d" % (rows, cols))
