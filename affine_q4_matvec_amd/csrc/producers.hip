@@ -30,6 +30,36 @@ __global__ __launch_bounds__(1024) void rmsq_kernel(const float *__restrict__ h,
   rmsq_block(h, w, n, eps, u, us, red);
 }
 
+// rmsq for n = 2048 by one wave, without LDS or barriers: lane l holds
+// values [32 l, 32 l + 32) of h and w.  The same trees as rmsq_block (the
+// balanced tree over the 2048 squares; per group, the balanced tree over
+// its 64 values: the lane's 32, then its partner's), so the same bits.
+__global__ __launch_bounds__(64) void rmsq2048_wave_kernel(const float *__restrict__ h,
+                                                           const float *__restrict__ w, float eps,
+                                                           float *__restrict__ u,
+                                                           float *__restrict__ us) {
+  const int lane = threadIdx.x;
+  const float4 *hp = reinterpret_cast<const float4 *>(h) + 8 * lane;
+  const float4 *wp = reinterpret_cast<const float4 *>(w) + 8 * lane;
+  float hv[32], wv[32];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float4 a = hp[k], c = wp[k];
+    hv[4 * k] = a.x, hv[4 * k + 1] = a.y, hv[4 * k + 2] = a.z, hv[4 * k + 3] = a.w;
+    wv[4 * k] = c.x, wv[4 * k + 1] = c.y, wv[4 * k + 2] = c.z, wv[4 * k + 3] = c.w;
+  }
+  const float rho = rmsq_rho_wave2048(hv, eps);
+  float uv[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) uv[k] = rmsq_value(hv[k], rho, wv[k]);
+  float4 *up = reinterpret_cast<float4 *>(u) + 8 * lane;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) up[k] = make_float4(uv[4 * k], uv[4 * k + 1], uv[4 * k + 2], uv[4 * k + 3]);
+  const float half = (tree8(uv) + tree8(uv + 8)) + (tree8(uv + 16) + tree8(uv + 24));
+  const float g = half + __shfl_xor(half, 1);
+  if ((lane & 1) == 0) us[lane >> 1] = g;
+}
+
 // One wave per 64-value group: lane i computes o[64g+i], then a butterfly
 // gives the group's balanced tree.
 template <bool FAST>
@@ -142,6 +172,13 @@ int next_pow2(int v) {
 
 hipError_t launch_rmsq(const float *h, const float *w, int32_t n, float eps, float *u, float *us,
                        hipStream_t st) {
+  // the one-wave kernel reads and writes 16 bytes at a time
+  const bool aligned16 = ((reinterpret_cast<uintptr_t>(h) | reinterpret_cast<uintptr_t>(w) |
+                           reinterpret_cast<uintptr_t>(u)) & 15u) == 0;
+  if (n == 2048 && aligned16) {
+    hipLaunchKernelGGL(rmsq2048_wave_kernel, dim3(1), dim3(kWave), 0, st, h, w, eps, u, us);
+    return hipGetLastError();
+  }
   int threads = next_pow2(n) / 8;
   if (threads < kWave) threads = kWave;
   hipLaunchKernelGGL(rmsq_kernel, dim3(1), dim3(threads), 0, st, h, w, n, eps, u, us);

@@ -37,6 +37,27 @@ def test_rmsq_edge_inputs():
         assert_bits_equal(host(usd), us, "rmsq sums " + name)
 
 
+def test_rmsq_2048_both_kernels():
+    """n = 2048 runs a one-wave kernel when h, w and u are 16-byte aligned
+    and the workgroup kernel otherwise: both give the oracle's bits."""
+    q4 = lib()
+    n = 2048
+    h = synth.normal_f32(5, "ah", (n,), 0.0, 1.0)
+    w = synth.normal_f32(5, "aw", (n,), 1.0, 0.1)
+    u, us = oracle.rmsq(h, w, 1e-6)
+    for off in (0, 1):
+        hb = torch.zeros(n + 4, device="cuda")
+        wb = torch.zeros(n + 4, device="cuda")
+        ub = torch.zeros(n + 4, device="cuda")
+        hb[off:off + n] = dev(h)
+        wb[off:off + n] = dev(w)
+        usd = torch.zeros(n // 64, device="cuda")
+        q4.rmsq(hb[off:off + n], wb[off:off + n], 1e-6, ub[off:off + n], usd)
+        torch.cuda.synchronize()
+        assert_bits_equal(host(ub[off:off + n]), u, "rmsq u offset %d" % off)
+        assert_bits_equal(host(usd), us, "rmsq usum offset %d" % off)
+
+
 @pytest.mark.parametrize("n", [64, 6144])
 def test_swq_fixed_bit_exact(n):
     q4 = lib()
