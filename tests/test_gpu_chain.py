@@ -54,6 +54,30 @@ def test_queue_product_set_two_layers_bit_exact():
     queue.close()
 
 
+def test_queue_stage_of_looping_products_bit_exact():
+    """One stage of three 2048-column products large enough that the
+    grouped launch loops (each product's waves take 1-4 blocks, with the
+    issue priority from their own progress), ragged row counts, one wait."""
+    q4 = lib()
+    x = synth.normal_f32(31, "lx", (2048,), 0.0, 1.0)
+    xs = oracle.group_sums(x)
+    xd, xsd = dev(x), dev(xs)
+    queue = q4.Queue()
+    ms, ys, Ws = [], [], []
+    for i, rows in enumerate((30001, 4099, 52223)):
+        m = synth.q4_matrix(31, "lp%d" % i, rows, 2048)
+        W = q4.Q4Matrix.from_host(m)
+        y = torch.full((rows,), 7.0, device="cuda")  # sentinel
+        queue.q4mv_queue(W, xd, xsd, y)
+        ms.append(m)
+        ys.append(y)
+        Ws.append(W)
+    queue.q4mv_wait()
+    for i, (m, y) in enumerate(zip(ms, ys)):
+        assert_bits_equal(host(y), oracle.q4mv(m, x, xs, NTHREADS), "looping product %d" % i)
+    queue.close()
+
+
 def test_queue_full_product_set_one_wait():
     """24 layers x 7 products + head, 97 stages, one host wait."""
     q4 = lib()
