@@ -227,11 +227,39 @@ __device__ __forceinline__ void norm_prologue(const Extra &ex, int lw, int lane,
   xsv = sus[lane >> 1];
 }
 
+// x = rmsq(h, wn) by each wave for itself, without LDS or barriers: lane l
+// holds values [32 l, 32 l + 32).  The same trees as norm_prologue (the
+// balanced tree over the 2048 squares; per group, the lane's 32 values and
+// then its partner's), so the same bits.  Wave 0 of the first workgroup
+// also publishes u and its group sums when asked.
+__device__ __forceinline__ void norm_prologue_wave(const Extra &ex, int lw, int lane, float *xv,
+                                                   float &xsv) {
+  float wv[32];
+  load_x_values(ex.h + 32 * lane, true, xv);
+  load_x_values(ex.wn + 32 * lane, true, wv);
+  const float rho = ops::rmsq_rho_wave2048(xv, ex.eps);
+#pragma unroll
+  for (int k = 0; k < 32; ++k) xv[k] = ops::rmsq_value(xv[k], rho, wv[k]);
+  xsv = pair_group_sum(xv);
+  if (lw == 0 && wave_index() == 0 && ex.u_out) {
+    float4 *up = reinterpret_cast<float4 *>(ex.u_out + 32 * lane);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      up[k] = make_float4(xv[4 * k], xv[4 * k + 1], xv[4 * k + 2], xv[4 * k + 3]);
+    if ((lane & 1) == 0) ex.us_out[lane >> 1] = xsv;
+  }
+}
+
 // The activations of the lane: the prologue's.  `l` is the lane index.
-template <int PRO>
+// WAVE_NORM: rmsq by each wave (the looping launches, where the workgroup's
+// barriers would hold back every wave's first block); otherwise over the
+// workgroup.
+template <int PRO, bool WAVE_NORM>
 __device__ __forceinline__ void row64_inputs(const Prod &P, const Extra &ex, int lw, int l,
                                              float *xv, float &xsv) {
-  if constexpr (PRO == kProNorm)
+  if constexpr (PRO == kProNorm && WAVE_NORM)
+    norm_prologue_wave(ex, lw, l, xv, xsv);
+  else if constexpr (PRO == kProNorm)
     norm_prologue(ex, lw, l, xv, xsv);
   else
     chunk_inputs<PRO>(P, l, true, xv, xsv);
@@ -292,7 +320,7 @@ __device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, int l
       // addresses are formed here and not held through the loop
       int l = lane;
       asm volatile("" : "+v"(l));
-      row64_inputs<PRO>(P, ex, lw, l, xv, xsv);
+      row64_inputs<PRO, true>(P, ex, lw, l, xv, xsv);
       pairs = prescale_for_pairs(xv);
     }
     if (nrows > 0) {
@@ -327,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void q4mv_row64_kernel(ProdGroup grp, Ext
       row64_load<R>(P, first, min(R, P.rows - first), 16u * lane, 4u * (lane >> 1), a);
     float xv[32];
     float xsv;
-    row64_inputs<PRO>(P, ex, lw, lane, xv, xsv);
+    row64_inputs<PRO, false>(P, ex, lw, lane, xv, xsv);
     if (prescale_for_pairs(xv))
       row64_single<R, FAST, true, EPI>(P, ex, xv, xsv, lane, first, a, best);
     else
