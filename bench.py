@@ -13,7 +13,8 @@ value = algorithmic bytes of a step / time per step (GB/s, 1e9 B/s), the
 steps timed back to back by one pair of HIP events on the launch stream.
 roofline = the q4mv kernel alone: its algorithmic bytes / its average
 duration, from one pair of HIP events around the same number of q4mv
-launches issued back to back on the launch stream.  Also reported: rmsq fused
+launches issued back to back on the launch stream (the median of three
+such rounds).  Also reported: rmsq fused
 into the product's prologue (one kernel per step).
 
 Also reported: the 24-layer decode chain (rmsq -> [gate;up] q4mv -> swq ->
@@ -43,6 +44,7 @@ METRIC = "q4mv achieved HBM GB/s (% of peak) on 248320x2048 head; ms per decode 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 ROWS, COLS = 248320, 2048
 SETTLE_S = 0.3  # untimed steps before the warm-up, to bring the GPU clocks up
+ROUNDS = {}  # the kernel-alone rounds of the head (ms per launch)
 
 
 def head_bytes(rows: int, cols: int) -> int:
@@ -162,17 +164,23 @@ def run_head(args, q4, torch, synth):
     step_ms = timed(step, args.steps)
     same = bool(np.array_equal(y.cpu().numpy().view(np.uint32), y_first.view(np.uint32)))
     # the q4mv kernel alone: the same launches back to back (an event between
-    # launches would itself add a gap)
-    kern_ms = timed(lambda i: q4.q4mv(mats[i % 2], x, xs, y, mode=mode, stream=stream), args.steps)
-    # for reference: rmsq fused into the product's prologue (one kernel)
-    fused_ms = timed(lambda i: q4.q4mv_norm(mats[i % 2], z, wn, eps, y, mode=mode, stream=stream),
-                     args.steps)
+    # launches would itself add a gap); for reference rmsq fused into the
+    # product's prologue (one kernel), and the kernel in the other mode.
+    # Three interleaved rounds each, the median reported: a single round
+    # moves by several microseconds with the clocks.
+    other = q4.FIXED if mode == q4.FAST else q4.FAST
+    kern, fused, oth = [], [], []
+    for _ in range(3):
+        kern.append(timed(lambda i: q4.q4mv(mats[i % 2], x, xs, y, mode=mode, stream=stream),
+                          args.steps))
+        fused.append(timed(lambda i: q4.q4mv_norm(mats[i % 2], z, wn, eps, y, mode=mode,
+                                                  stream=stream), args.steps))
+        oth.append(timed(lambda i: q4.q4mv(mats[i % 2], x, xs, y, mode=other, stream=stream),
+                         args.steps))
     torch.cuda.synchronize()
     same = same and bool(np.array_equal(y.cpu().numpy().view(np.uint32), y_first.view(np.uint32)))
-    # for reference: the q4mv kernel in the other mode, timed the same way
-    other = q4.FIXED if mode == q4.FAST else q4.FAST
-    other_ms = timed(lambda i: q4.q4mv(mats[i % 2], x, xs, y, mode=other, stream=stream),
-                     args.steps)
+    kern_ms, fused_ms, other_ms = (sorted(v)[1] for v in (kern, fused, oth))
+    ROUNDS.update(kernel=kern, fused=fused, other=oth)
     return step_ms, kern_ms, fused_ms, same, other_ms
 
 
@@ -527,10 +535,13 @@ def main() -> int:
                 "false" if args.mode == "fixed" else "true"),
             "algorithmic_bytes_per_launch": qb,
             "avg_launch_ms": round(kern_ms, 5),
-            "timing": "HIP events around %d back-to-back launches on the launch stream" % args.steps,
+            "avg_launch_ms_rounds": [round(v, 5) for v in ROUNDS["kernel"]],
+            "timing": "HIP events around %d back-to-back launches on the launch stream; median "
+                      "of 3 rounds interleaved with the other-mode and fused rounds" % args.steps,
             "other_mode": {
                 "mode": "fast" if args.mode == "fixed" else "fixed",
                 "avg_launch_ms": round(other_ms, 5),
+                "avg_launch_ms_rounds": [round(v, 5) for v in ROUNDS["other"]],
                 "achieved": round(qb / (other_ms * 1e-3) / 1e9, 1),
                 "frac": round(qb / (other_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             },
