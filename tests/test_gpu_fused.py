@@ -71,7 +71,9 @@ def test_q4mv_norm_other_width_runs_two_steps():
         q4.q4mv_norm(W, dev(h), dev(wn), 1e-6)
 
 
-@pytest.mark.parametrize("n", [64, 6144])
+# n = 20032: 40064 interleaved rows, more than one 4-row block per wave,
+# so the launch loops (the SwiGLU batches then span several blocks)
+@pytest.mark.parametrize("n", [64, 6144, 20032])
 def test_q4mv_norm_swiglu_equals_separate_steps(n):
     q4 = lib()
     from affine_q4_matvec_amd.chain import _interleave_rows
