@@ -1,9 +1,11 @@
 // Gated attention of one decode token over key/value caches (atq), for
 // gfx950: "Metal: queued rmsq, swq, gdn and atq kernels and a 4-row q4mv, so
-// a decode token is one command buffer with one wait" (#1440), Change (atq
-// bullet: q/k RMS norm and rotation, the new key and value into the caches,
-// scores, softmax, weighted values, sigmoid gate, group sums; a group of
-// query heads shares one key/value head).  The pages give no formulas; the
+// a decode token is one command buffer with one wait" (#1440), Change, atq
+// bullet: the step normalises and rotates the query and the new key, appends
+// the key and value to caches that stay on the GPU, weighs every cached
+// position by a softmax of its score, gates the weighted sum with a sigmoid
+// and emits the 64-value sums the next product needs; several query heads
+// read one key/value head.  The pages give no formulas; the
 // arithmetic read from them, operation by operation (D = 128, G = hq / hkv
 // query heads per key/value head j, n = pos + 1 positions):
 //   qn = rmsq(q_h, wq), kn = rmsq(k_j, wk) over D values

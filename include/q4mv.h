@@ -136,8 +136,9 @@ int q4mv_norm_argmax(const q4_mat *w, const float *h, const float *wn, float eps
                      int32_t *idx, void *ws, size_t ws_bytes, int mode, void *stream);
 
 /*
- * rmsq: RMS norm with float weights plus the 64-value group sums that q4mv
- * reads ([P1] Change, rmsq bullet; exact on the GPU there).
+ * rmsq: the RMS norm of h scaled by float weights, and the sum of each 64
+ * consecutive outputs, which is the xsum input of the next q4mv ([P1]
+ * Change, rmsq bullet; bit-exact on the pages' GPU).
  *   ss = T(h_i*h_i); rho = 1 / sqrt(ss/n + eps)  (correctly rounded);
  *   u_i = (h_i*rho)*w_i;  usum[g] = T(u[64g..64g+63]).
  *   h, w : device float[n];  u : device float[n];  usum : device float[n/64].
@@ -175,7 +176,9 @@ int q4_argmax(const float *v, int32_t n, int32_t *idx, void *ws,
               size_t ws_bytes, void *stream);
 
 /*
- * q4_embed: embedding lookup from a tied Q4 matrix: e[c] = (s[t,c/64] *
+ * q4_embed: the input row of the next greedy step ([P1] Verification: the
+ * greedy decode whose token ids are compared, one token feeding the next),
+ * looked up in a tied Q4 matrix: e[c] = (s[t,c/64] *
  * q(t,c)) + b[t,c/64] with t = *tok read on the device (so a captured graph
  * can feed argmax's output straight back).  A token outside [0, rows) fills
  * e with quiet NaNs.  tok: device int32[1]; e: device float[cols].
@@ -240,9 +243,10 @@ int q4_decode_layers_status(void *ws, void *stream);
 
 /*
  * Gated attention of one decode token over key/value caches ([P1] Change,
- * atq bullet: q/k RMS norm and rotation, the new key and value written to
- * the caches, scores, softmax, weighted values, sigmoid gate and group sums;
- * query heads in groups that share a key/value head).  The pages state no
+ * atq bullet, which lists the parts without formulas: normalise and rotate
+ * the query and new key, append key and value to the caches, softmax-weight
+ * the cached values by score, gate with a sigmoid, emit 64-value sums for
+ * the next product; several query heads per key/value head).  The pages state no
  * formulas; the operations as read, D = 128, G = hq / hkv, query head h
  * using key/value head j = h / G, n = pos + 1:
  *   qn = rmsq(q_h, wq), kn = rmsq(k_j, wk)          (rmsq over 128 values)

@@ -298,10 +298,13 @@ uint32_t orc_fnv1a32(const void *data, int64_t nbytes) {
 /* ------------------------------------------------------------------------
  * atq: one decode token of gated attention over key and value caches
  * ("Metal: queued rmsq, swq, gdn and atq kernels ..." (#1440), Change, atq
- * bullet: q/k RMS norm and rotation, the new k/v into the caches, scores,
- * softmax, weighted values, sigmoid gate and group sums; one threadgroup per
- * query head; a group of query heads shares one key/value head).  The
- * pages give no formulas; the readings (listed with the design notes):
+ * bullet).  That bullet names the parts only: the query and the new key are
+ * normalised and rotated, the new key and value are appended to the caches,
+ * each cached position is weighted by a softmax of its score, the weighted
+ * sum of values is gated by a sigmoid, and the 64-value sums are emitted;
+ * the Metal kernel runs a threadgroup per query head, and several query
+ * heads share one key/value head.  The pages give no formulas; the
+ * readings (listed with the design notes):
  *   D = 128 values per head; hq query heads, hkv key/value heads with
  *   hq % hkv == 0; query head h uses key/value head h / (hq / hkv).
  *   qn = rmsq(q_h, wq), kn = rmsq(k_j, wk)     (rmsq's definition over D)

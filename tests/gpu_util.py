@@ -46,9 +46,3 @@ def assert_bits_equal(got, want, what=""):
                              % (what, bad.size, g.size, i, float(np.asarray(got).ravel()[i]),
                                 float(np.asarray(want).ravel()[i])))
 
-
-def fnv1a32(a) -> int:
-    h = 2166136261
-    for byte in np.ascontiguousarray(a).tobytes():
-        h = ((h ^ byte) * 16777619) & 0xFFFFFFFF
-    return h

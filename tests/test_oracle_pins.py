@@ -727,3 +727,30 @@ def test_attn_chain_steps_against_binary64_forward():
         assert np.max(np.abs(kc[0][0, :pos + 1] - K64[0][0, :pos + 1])) < 1e-4 * np.max(
             np.abs(K64[0][0, :pos + 1]))
         tok = nxt
+
+
+# ---------------------------------------------------------------------------
+# FNV-1a (32 bit): the hash of an output's bytes that the 400-call product
+# check and the chains' per-step logits checks compare.  Pinned by the
+# algorithm's published test vectors (Fowler/Noll/Vo reference suite), not
+# by a second implementation of it.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("text,want", [
+    (b"", 0x811C9DC5),      # the offset basis itself
+    (b"a", 0xE40C292C),
+    (b"foobar", 0xBF9CF968),
+])
+def test_fnv1a32_published_vectors(text, want):
+    assert oracle.fnv1a32(np.frombuffer(text, dtype=np.uint8)) == want
+
+
+def test_fnv1a32_hashes_the_little_endian_bytes_of_floats():
+    # the same bytes give the same hash whatever the array's type; one
+    # flipped bit of one value changes it
+    y = synth.normal_f32(3, "fnv.y", (4096,), 0.0, 1.0)
+    h = oracle.fnv1a32(y)
+    assert h == oracle.fnv1a32(y.view(np.uint8))
+    assert h == oracle.fnv1a32(np.frombuffer(y.astype("<f4").tobytes(), dtype=np.uint8))
+    z = y.copy()
+    z.view(np.uint32)[1234] ^= 1
+    assert oracle.fnv1a32(z) != h
