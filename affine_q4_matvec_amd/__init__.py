@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "FIXED", "FAST", "Q4Error", "Q4Matrix", "q4mv", "q4mv_add", "q4mv_norm",
-    "q4mv_norm_swiglu", "q4mv_norm_argmax", "q4mv_argmax_ws_bytes", "rmsq", "swq",
+    "q4mv_norm_swiglu", "q4mv_norm_argmax", "q4mv_norm_argmax_noalloc", "q4mv_argmax_ws_bytes",
+    "rmsq", "swq",
     "q4_argmax", "q4_argmax_ws_bytes", "q4_embed", "Queue", "Graph", "q4_sync",
     "MlpLayer", "q4_decode_layers", "q4_decode_layers_ws_bytes", "q4_decode_layers_status",
     "Mailbox", "library_path", "q4_atq", "q4_atq_ws_bytes", "q4_atq_status", "q4_pos_advance",
@@ -73,6 +74,8 @@ _SIGS = {
     "q4mv_argmax_ws_bytes": ([], ctypes.c_size_t),
     "q4mv_norm_argmax": ([ctypes.POINTER(_Mat), _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
                           ctypes.c_size_t, ctypes.c_int, _vp], ctypes.c_int),
+    "q4mv_norm_argmax_noalloc": ([ctypes.POINTER(_Mat), _vp, _vp, ctypes.c_float, _vp, _vp,
+                                  ctypes.c_int, _vp], ctypes.c_int),
     "rmsq": ([_vp, _vp, _i32, ctypes.c_float, _vp, _vp, _vp], ctypes.c_int),
     "swq": ([_vp, _i32, _vp, _vp, ctypes.c_int, _vp], ctypes.c_int),
     "q4_argmax_ws_bytes": ([_i32], ctypes.c_size_t),
@@ -259,6 +262,21 @@ def q4mv_norm_argmax(w: Q4Matrix, h: torch.Tensor, wn: torch.Tensor, eps: float,
                                  _dev(idx, torch.int32, 1, "idx"),
                                  _dev(state, state.dtype, None, "state"),
                                  state.numel() * state.element_size(), mode, _stream(stream)))
+    return idx
+
+
+def q4mv_norm_argmax_noalloc(w: Q4Matrix, h: torch.Tensor, wn: torch.Tensor, eps: float,
+                             y: torch.Tensor, idx: torch.Tensor, mode: int = FIXED,
+                             stream=None) -> torch.Tensor:
+    """``q4mv_norm_argmax`` with the keys in the library's static device
+    array instead of a caller workspace (no allocation by the call); calls
+    on one GPU must not overlap in time."""
+    _check("q4mv_norm_argmax_noalloc",
+           _lib.q4mv_norm_argmax_noalloc(w.ref, _dev(h, torch.float32, w.cols, "h"),
+                                         _dev(wn, torch.float32, w.cols, "wn"), float(eps),
+                                         _dev(y, torch.float32, w.rows, "y"),
+                                         _dev(idx, torch.int32, 1, "idx"), mode,
+                                         _stream(stream)))
     return idx
 
 

@@ -6,7 +6,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <chrono>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -294,28 +296,32 @@ int q4mv_norm_swiglu(const q4_mat *w, const float *h, const float *wn, float eps
 // One 8-byte key per workgroup of the fused argmax launch.
 constexpr int32_t kArgmaxMaxWorkgroups = 4096;
 
-size_t q4mv_argmax_ws_bytes(void) { return sizeof(unsigned long long) * kArgmaxMaxWorkgroups; }
+namespace {
 
-int q4mv_norm_argmax(const q4_mat *w, const float *h, const float *wn, float eps, float *y,
-                     int32_t *idx, void *ws, size_t ws_bytes, int mode, void *stream) {
+// The checks of q4mv_norm_argmax other than those of its workspace.
+int check_norm_argmax(const q4_mat *w, const float *h, const float *wn, const float *y,
+                      const int32_t *idx, int mode) {
   if (mode != Q4_FIXED && mode != Q4_FAST) return Q4_EINVAL;
   int rc = check_mat(w);
   if (rc != Q4_OK) return rc;
   if ((rc = check_norm_inputs(h, wn)) != Q4_OK) return rc;
   if (w->cols != 2048) return Q4_EINVAL;
-  if (!y || !idx || !ws || !aligned(y, 4) || !aligned(idx, 4) || !aligned(ws, 8))
-    return Q4_EINVAL;
-  if (ws_bytes < sizeof(unsigned long long)) return Q4_EINVAL;
+  if (!y || !idx || !aligned(y, 4) || !aligned(idx, 4)) return Q4_EINVAL;
   const size_t nb = sizeof(float) * 2048, yb = sizeof(float) * (size_t)w->rows;
   if (overlap(y, yb, h, nb) || overlap(y, yb, wn, nb) || overlaps_mat(y, yb, w) ||
       overlap(idx, 4, y, yb) || overlap(idx, 4, h, nb) || overlap(idx, 4, wn, nb) ||
-      overlap(ws, ws_bytes, y, yb) || overlap(ws, ws_bytes, idx, 4) ||
-      overlap(ws, ws_bytes, h, nb) || overlap(ws, ws_bytes, wn, nb) || overlaps_mat(idx, 4, w) ||
-      overlaps_mat(ws, ws_bytes, w))
+      overlaps_mat(idx, 4, w))
     return Q4_EINVAL;
+  return Q4_OK;
+}
+
+// The product with its argmax epilogue, then the final pick over the
+// workgroups' keys; at most `slots` workgroups (one key each at keys[i]).
+int launch_norm_argmax(const q4_mat *w, const float *h, const float *wn, float eps, float *y,
+                       int32_t *idx, unsigned long long *keys, long long slots, int mode,
+                       hipStream_t st) {
   const Shape sh = q4::shape_of(2048, q4::kProNorm, q4::kEpiArgmax);
   long long nwg = q4::workgroups_for(sh, w->rows, mode);
-  const long long slots = (long long)(ws_bytes / sizeof(unsigned long long));
   if (nwg > slots) nwg = slots;
   if (nwg > kArgmaxMaxWorkgroups) nwg = kArgmaxMaxWorkgroups;
   ProdGroup g;
@@ -327,11 +333,68 @@ int q4mv_norm_argmax(const q4_mat *w, const float *h, const float *wn, float eps
   ex.h = h;
   ex.wn = wn;
   ex.eps = eps;
-  ex.amax = static_cast<unsigned long long *>(ws);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = hip_status(q4::launch_q4mv_group(g, sh, mode, ex, st));
+  ex.amax = keys;
+  const int rc = hip_status(q4::launch_q4mv_group(g, sh, mode, ex, st));
   if (rc != Q4_OK) return rc;
-  return hip_status(q4::launch_argmax_final(ex.amax, (int32_t)nwg, idx, st));
+  return hip_status(q4::launch_argmax_final(keys, (int32_t)nwg, idx, st));
+}
+
+// Device scratch of q4mv_norm_argmax_noalloc: the workgroups' argmax keys,
+// one array per GPU for the life of the process.  Its name is a host-side
+// stand-in: host code uses the device address that hipGetSymbolAddress
+// returns for the current device, never the name itself.
+static __device__ __align__(256) unsigned long long scratch[kArgmaxMaxWorkgroups];
+
+constexpr int kScratchDevices = 64;
+std::atomic<void *> g_scratch[kScratchDevices];
+std::mutex g_scratch_mu;
+
+// The address of `scratch` on the current device, looked up on the first
+// call for each device and kept.
+int scratch_address(unsigned long long **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return Q4_EHIP;
+  if (dev < 0 || dev >= kScratchDevices) return Q4_EINVAL;
+  void *p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return Q4_EHIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = static_cast<unsigned long long *>(p);
+  return Q4_OK;
+}
+
+}  // namespace
+
+size_t q4mv_argmax_ws_bytes(void) { return sizeof(unsigned long long) * kArgmaxMaxWorkgroups; }
+
+int q4mv_norm_argmax(const q4_mat *w, const float *h, const float *wn, float eps, float *y,
+                     int32_t *idx, void *ws, size_t ws_bytes, int mode, void *stream) {
+  int rc = check_norm_argmax(w, h, wn, y, idx, mode);
+  if (rc != Q4_OK) return rc;
+  if (!ws || !aligned(ws, 8) || ws_bytes < sizeof(unsigned long long)) return Q4_EINVAL;
+  const size_t nb = sizeof(float) * 2048, yb = sizeof(float) * (size_t)w->rows;
+  if (overlap(ws, ws_bytes, y, yb) || overlap(ws, ws_bytes, idx, 4) ||
+      overlap(ws, ws_bytes, h, nb) || overlap(ws, ws_bytes, wn, nb) ||
+      overlaps_mat(ws, ws_bytes, w))
+    return Q4_EINVAL;
+  return launch_norm_argmax(w, h, wn, eps, y, idx, static_cast<unsigned long long *>(ws),
+                            (long long)(ws_bytes / sizeof(unsigned long long)), mode,
+                            static_cast<hipStream_t>(stream));
+}
+
+int q4mv_norm_argmax_noalloc(const q4_mat *w, const float *h, const float *wn, float eps,
+                             float *y, int32_t *idx, int mode, void *stream) {
+  int rc = check_norm_argmax(w, h, wn, y, idx, mode);
+  if (rc != Q4_OK) return rc;
+  unsigned long long *keys = nullptr;
+  if ((rc = scratch_address(&keys)) != Q4_OK) return rc;
+  return launch_norm_argmax(w, h, wn, eps, y, idx, keys, kArgmaxMaxWorkgroups, mode,
+                            static_cast<hipStream_t>(stream));
 }
 
 int rmsq(const float *h, const float *w, int32_t n, float eps, float *u, float *usum,

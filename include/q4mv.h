@@ -136,6 +136,23 @@ int q4mv_norm_argmax(const q4_mat *w, const float *h, const float *wn, float eps
                      int32_t *idx, void *ws, size_t ws_bytes, int mode, void *stream);
 
 /*
+ * q4mv_norm_argmax_noalloc: q4mv_norm_argmax without a caller workspace, for
+ *   callers that cannot allocate device memory (code under stream capture,
+ *   tight serving loops, harnesses that forbid allocation).  The
+ *   workgroups' keys go to a static device array of the library (32 KiB per
+ *   GPU, held until the process ends; its address is looked up on the first
+ *   call on each device).  The call allocates nothing.  Same arguments,
+ *   results and errors as q4mv_norm_argmax with a full workspace; any rows
+ *   count is accepted (the product uses at most 4096 workgroups, one key
+ *   each).  Every call on one GPU shares that array: calls that overlap in
+ *   time on one GPU (other streams, other threads) race and must not be
+ *   issued.  Nothing in it needs to start at zero: each call writes every
+ *   key it reads.
+ */
+int q4mv_norm_argmax_noalloc(const q4_mat *w, const float *h, const float *wn, float eps,
+                             float *y, int32_t *idx, int mode, void *stream);
+
+/*
  * rmsq: the RMS norm of h scaled by float weights, and the sum of each 64
  * consecutive outputs, which is the xsum input of the next q4mv ([P1]
  * Change, rmsq bullet; bit-exact on the pages' GPU).
