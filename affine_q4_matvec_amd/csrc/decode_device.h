@@ -29,6 +29,7 @@ struct alignas(16) Lds {
   float x[NP * 64 * kChunkStride];  // x = rmsq(h) (stage A) or m (stage B)
   float xs[NP * 32];                // their group sums
   float red[kWaves];                // the waves' sums of squares
+  uint32_t flag[2];                 // stage B: a wait gave up / some |m| >= 2^118
 };
 
 // rmsq of h over the workgroup, with the arithmetic and tree of the rmsq

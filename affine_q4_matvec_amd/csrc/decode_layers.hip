@@ -45,11 +45,13 @@
 //
 // The weights of a stage do not depend on the previous one, so every wave
 // loads its next stage's rows ahead: the down row right after the wait for
-// h, the next layer's gate/up rows right after its gate/up products.  A
-// wave's loads complete in issue order for its wait counter, so a wait
-// issued after a prefetch also waits for the prefetch; the order above puts
-// each prefetch before the wait that is long anyway (for m), never before
-// the wait for h.
+// h, the next layer's gate/up rows as early as they can go.  A wave's loads
+// complete in issue order for its wait counter, so a poll issued after a
+// prefetch also waits for the prefetch (for the gate/up rows, about 16 MB
+// across the GPU).  Hence two kinds of waves: waves 0-3 poll h (at a
+// layer's start) and load their next gate/up rows right after their gate/up
+// products; waves 4-7 poll m (in stage B) and load theirs only once those
+// polls are done.  No poll then waits behind a fresh prefetch.
 //
 // Every value is computed by the same code as the per-stage kernels (rmsq
 // and SwiGLU from ops_device.h, group terms and row trees from
@@ -64,6 +66,9 @@ namespace {
 
 using namespace dev;
 using namespace decode;
+
+// Threads of the workgroup that poll m in stage B (the last four waves).
+constexpr int kPollThreads = 256;
 
 // e[c] of the embedding row tk (the embed kernel's arithmetic; NaN for a
 // token outside the vocabulary).
@@ -160,63 +165,77 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
       }
     }
 
-    // the next layer's gate/up rows: issued before this wave's next wait for
-    // m, which they would otherwise delay in the wait for h after it
-    if (l + 1 < A.nlayers && pb < pe)
+    // the next layer's gate/up rows, for the waves that do not poll m (they
+    // poll h at the next layer's start, long after these have landed)
+    const bool poller = t >= kThreads - kPollThreads;
+    if (!poller && l + 1 < A.nlayers && pb < pe)
       load_gu(A.layer[l + 1], pb, min(kGuPairs, pe - pb), lane, a);
     issue_order();
 
     // ---- stage B: m and its group sums into LDS; h = h + down m
-    // chunk c = 8 consecutive values of m; chunks t and t + kThreads
+    // chunk c = 8 consecutive values of m; poller thread p takes chunks
+    // p, p + kPollThreads, ...  The pollers are waves without fresh loads in
+    // flight: a wave's loads complete in issue order for its wait counter,
+    // so a poll behind a prefetch of the GPU's next gate/up rows (about 16
+    // MB) would wait for that prefetch to land.
     constexpr int kChunks = NP * kCols / 8;
-    float xm[2][8];
+    constexpr int kPerPoller = kChunks / kPollThreads;
+    static_assert(kChunks % kPollThreads == 0, "whole rounds of chunks");
     // the workgroup polls only once all its waves are done with stage A (a
     // poll that starts early only adds traffic at the lines being polled)
+    if (t == 0) S.flag[0] = S.flag[1] = 0u;
     __syncthreads();
-    // (one chunk at a time: polling both in the same rounds doubles the
-    // polled traffic while the wait lasts, which measured slower)
-    ok = true;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int c = t + r * kThreads;
-      if (c < kChunks)
-        ok &= poll_tagged<8>(mq + (size_t)copy * kDecodeMaxInter + 8 * c, tag0 + 2 * l + 1, xm[r],
-                             err, A.spin_ticks);
-    }
-    if (!__syncthreads_and(ok)) return;
-    // group sums: T over each chunk, then over 8 chunks by a butterfly
-    // (the balanced tree over the group's 64 values)
-    bool large = false;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int c = t + r * kThreads;
-      if (r * kThreads < kChunks) {  // uniform per round: 8 aligned chunks per group
-        float g = c < kChunks ? ops::tree8(xm[r]) : 0.0f;
+    if (poller) {
+      const int p = t - (kThreads - kPollThreads);
+      bool large = false;
+      // one chunk at a time: polling several in the same rounds multiplies
+      // the polled traffic while the wait lasts
+#pragma unroll 1
+      for (int r = 0; r < kPerPoller; ++r) {
+        const int c = p + r * kPollThreads;
+        float xm[8];
+        if (!poll_tagged<8>(mq + (size_t)copy * kDecodeMaxInter + 8 * c, tag0 + 2 * l + 1, xm,
+                            err, A.spin_ticks)) {
+          S.flag[0] = 1u;
+          break;
+        }
+        // group sums: T over each chunk, then over 8 chunks (8 consecutive
+        // lanes) by a butterfly: the balanced tree over the group's 64 values
+        float g = ops::tree8(xm);
         g = g + __shfl_xor(g, 1);
         g = g + __shfl_xor(g, 2);
         g = g + __shfl_xor(g, 4);
-        if (c < kChunks && (c & 7) == 0) S.xs[c >> 3] = g;
-        if (c < kChunks) {
+        if ((c & 7) == 0) S.xs[c >> 3] = g;
 #pragma unroll
-          for (int k = 0; k < 8; ++k) large |= !(__builtin_fabsf(xm[r][k]) < 0x1p118f);
-        }
+        for (int k = 0; k < 8; ++k) large |= !(__builtin_fabsf(xm[k]) < 0x1p118f);
+        // value i of m sits at i + 4 (i / 32) in the padded layout
+        float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * c + 4 * (c >> 2));
+        dst[0] = make_float4(xm[0], xm[1], xm[2], xm[3]);
+        dst[1] = make_float4(xm[4], xm[5], xm[6], xm[7]);
       }
+      if (large) S.flag[1] = 1u;
+      // this wave's gate/up rows of the next layer, now that its polls are done
+      if (l + 1 < A.nlayers && pb < pe)
+        load_gu(A.layer[l + 1], pb, min(kGuPairs, pe - pb), lane, a);
+      issue_order();
     }
+    __syncthreads();
+    if (S.flag[0] != 0u) return;
     // pre-scaled for the pair decode unless some value of the workgroup is
-    // large
-    const bool pairs = !__syncthreads_or(large);
-    {
-      const float scale = pairs ? 1.0f / fp8_unit() : 1.0f;
+    // large (the scaling of prescale_for_pairs, in place)
+    const bool pairs = S.flag[1] == 0u;
+    if (pairs) {
+      const float scale = 1.0f / fp8_unit();
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
+      for (int r = 0; r < kChunks / kThreads + 1; ++r) {
         const int c = t + r * kThreads;
         if (c < kChunks) {
-          // value i of m sits at i + 4 (i / 32) in the padded layout
-          float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * c + 4 * (c >> 2));
-          dst[0] = make_float4(xm[r][0] * scale, xm[r][1] * scale, xm[r][2] * scale,
-                               xm[r][3] * scale);
-          dst[1] = make_float4(xm[r][4] * scale, xm[r][5] * scale, xm[r][6] * scale,
-                               xm[r][7] * scale);
+          float4 *v = reinterpret_cast<float4 *>(S.x + 8 * c + 4 * (c >> 2));
+          float4 a0 = v[0], a1 = v[1];
+          a0.x = a0.x * scale; a0.y = a0.y * scale; a0.z = a0.z * scale; a0.w = a0.w * scale;
+          a1.x = a1.x * scale; a1.y = a1.y * scale; a1.z = a1.z * scale; a1.w = a1.w * scale;
+          v[0] = a0;
+          v[1] = a1;
         }
       }
     }
