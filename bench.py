@@ -45,6 +45,9 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
 ROWS, COLS = 248320, 2048
 SETTLE_S = 0.3  # untimed steps before the warm-up, to bring the GPU clocks up
 ROUNDS = {}  # the kernel-alone rounds of the head (ms per launch)
+HEAD_Y = {}  # the head's output in the timed mode (host copy) and its checks
+CHAIN_W = {}  # the decode chain's host weights, once generated
+SECTIONS = ("head", "product", "product_set", "chain", "atq", "attn_chain", "cpu")
 
 
 def head_bytes(rows: int, cols: int) -> int:
@@ -70,6 +73,39 @@ def log(msg: str) -> None:
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+def fnv1a32(a) -> int:
+    """FNV-1a (32 bit) of an array's bytes: the hash the golden files hold
+    for the oracle's outputs."""
+    import numpy as np
+
+    h = 0x811C9DC5
+    for b in np.ascontiguousarray(a).view(np.uint8).tobytes():
+        h = ((h ^ b) * 0x01000193) & 0xFFFFFFFF
+    return h
+
+
+def golden(kind: str, seed: int):
+    """The oracle's stored results for a workload (tests/golden), or None."""
+    path = os.path.join(ROOT, "tests", "golden", "%s_seed%d.json" % (kind, seed))
+    try:
+        return json.load(open(path))
+    except (OSError, ValueError):
+        return None
+
+
+def from_hexbits(bits) -> "np.ndarray":
+    import numpy as np
+
+    return np.array([int(b, 16) for b in bits], dtype=np.uint32).view(np.float32)
+
+
+def stats(v) -> dict:
+    import numpy as np
+
+    return {"min": round(float(np.min(v)), 5), "median": round(float(np.median(v)), 5),
+            "max": round(float(np.max(v)), 5), "n": len(v)}
+
+
 def kernel_source_hash() -> str:
     """Hash of the q4mv kernel sources (the counters are only valid for them)."""
     h = hashlib.sha256()
@@ -91,34 +127,88 @@ def measured_traffic(per_launch_alg_bytes: int):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(seed: int):
-    """The CPU oracle on the head workload, all host cores (at most 16)."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(seed: int, head_y=None, chain_w=None, budget_s: float = 6.0):
+    """The CPU oracle, timed on the host: single-threaded on the 13 x 128,
+    4096 x 2048 and head products; on all of the process's cores (at most
+    16, the CPU share a one-GPU job gets) on the head and on decode-chain
+    tokens.  The head figure (GB/s, all cores) is the headline value.  The
+    oracle's head output is also compared bit for bit with the GPU's."""
     import numpy as np
 
     import oracle
     import synth
 
     try:
-        cores = len(os.sched_getaffinity(0))
+        avail = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(16, cores))
+        avail = os.cpu_count() or 1
+    cores = max(1, min(16, avail))
+
+    def repeat(fn, seconds, lo=3, hi=200):
+        times = []
+        t_end = time.perf_counter() + seconds
+        while len(times) < lo or (time.perf_counter() < t_end and len(times) < hi):
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+        return times
+
+    single = {}
+    m = synth.small_product(seed=seed)
+    xs = oracle.group_sums(m["x"])
+    t = repeat(lambda: oracle.q4mv(m, m["x"], xs), 0.3, lo=20, hi=5000)
+    single["p13x128_us_per_call"] = round(float(np.median(t)) * 1e6, 2)
+    m = synth.small_product(seed=seed, rows=4096, cols=2048, name="p4096")
+    xs = oracle.group_sums(m["x"])
+    t = repeat(lambda: oracle.q4mv(m, m["x"], xs), 1.0, lo=5)
+    single["p4096x2048_ms_per_call"] = round(float(np.median(t)) * 1e3, 3)
+    single["p4096x2048_GBps"] = round(head_bytes(4096, 2048) / float(np.median(t)) / 1e9, 3)
     h = synth.head_inputs(seed=seed)
     u, us = oracle.rmsq(h["z"], h["wn"], h["eps"])
-    # about 10 s of CPU work: whole-head products repeated (at least 3, at
-    # most 200), the median run reported
-    times = []
-    t_end = time.perf_counter() + 10.0
-    while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 200):
-        t0 = time.perf_counter()
-        oracle.q4mv(h, u, us, nthreads=cores)
-        times.append(time.perf_counter() - t0)
+    t = repeat(lambda: oracle.q4mv(h, u, us), 0.0, lo=2, hi=2)
+    single["head_ms_per_call"] = round(float(np.median(t)) * 1e3, 1)
+    single["head_GBps"] = round(head_bytes(ROWS, COLS) / float(np.median(t)) / 1e9, 3)
+
+    ys = []
+    times = repeat(lambda: ys.append(oracle.q4mv(h, u, us, nthreads=cores)), budget_s)
     med = float(np.median(times))
-    return {"value": round(head_bytes(ROWS, COLS) / med / 1e9, 3), "unit": "GB/s",
-            "cores": cores, "kind": "oracle",
-            "sample": "full 248320x2048 head q4mv (fixed order), rows split over %d threads, "
-                      "%d runs in %.1f s, median %.3f s (best %.3f s)"
-                      % (cores, len(times), sum(times), med, min(times))}
+    y_oracle = ys[-1]
+    del ys
+    out = {"value": round(head_bytes(ROWS, COLS) / med / 1e9, 3), "unit": "GB/s",
+           "cores": cores, "kind": "oracle",
+           "sample": "full 248320x2048 head q4mv (fixed order), rows split over %d threads, "
+                     "%d runs in %.1f s, median %.3f s (best %.3f s)"
+                     % (cores, len(times), sum(times), med, min(times)),
+           "cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "affinity_cpus": avail,
+           "single_thread": single,
+           "all_cores": {"head_ms_per_call": round(med * 1e3, 2)}}
+    if head_y is not None:
+        out["gpu_head_bits_equal_oracle"] = bool(np.array_equal(
+            np.asarray(head_y, dtype=np.float32).view(np.uint32), y_oracle.view(np.uint32)))
+    if chain_w is not None:
+        # decode-chain tokens on all cores from the chain's start token
+        ref = golden("chain", seed)
+        tok, toks, tt = int(chain_w["tok0"]), [], []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            _, tok = oracle.chain_step(chain_w, tok, nthreads=cores)
+            tt.append(time.perf_counter() - t0)
+            toks.append(int(tok))
+        out["all_cores"]["chain_ms_per_token"] = round(float(np.median(tt)) * 1e3, 1)
+        out["all_cores"]["chain_tokens_timed"] = len(tt)
+        if ref is not None:
+            out["all_cores"]["chain_tokens_equal_golden"] = toks == ref["tokens"][:len(toks)]
+    return out
 
 
 def run_head(args, q4, torch, synth):
@@ -137,6 +227,10 @@ def run_head(args, q4, torch, synth):
     x = torch.empty(COLS, device="cuda")
     xs = torch.empty(COLS // 64, device="cuda")
     y = torch.empty(ROWS, device="cuda")
+    # the other-mode and fused rounds write elsewhere, so that y only ever
+    # holds the timed mode's output
+    y_other = torch.empty(ROWS, device="cuda")
+    y_fused = torch.empty(ROWS, device="cuda")
     mode = q4.FAST if args.mode == "fast" else q4.FIXED
     stream = torch.cuda.current_stream()
 
@@ -163,24 +257,35 @@ def run_head(args, q4, torch, synth):
     # the timed steps, back to back, one event pair around all of them
     step_ms = timed(step, args.steps)
     same = bool(np.array_equal(y.cpu().numpy().view(np.uint32), y_first.view(np.uint32)))
+    same_steps = same
     # the q4mv kernel alone: the same launches back to back (an event between
     # launches would itself add a gap); for reference rmsq fused into the
     # product's prologue (one kernel), and the kernel in the other mode.
-    # Three interleaved rounds each, the median reported: a single round
-    # moves by several microseconds with the clocks.
+    # args.rounds interleaved rounds each, the median reported: a single
+    # round moves by several microseconds with the clocks.
     other = q4.FIXED if mode == q4.FAST else q4.FAST
     kern, fused, oth = [], [], []
-    for _ in range(3):
+    for _ in range(args.rounds):
         kern.append(timed(lambda i: q4.q4mv(mats[i % 2], x, xs, y, mode=mode, stream=stream),
                           args.steps))
-        fused.append(timed(lambda i: q4.q4mv_norm(mats[i % 2], z, wn, eps, y, mode=mode,
+        fused.append(timed(lambda i: q4.q4mv_norm(mats[i % 2], z, wn, eps, y_fused, mode=mode,
                                                   stream=stream), args.steps))
-        oth.append(timed(lambda i: q4.q4mv(mats[i % 2], x, xs, y, mode=other, stream=stream),
-                         args.steps))
+        oth.append(timed(lambda i: q4.q4mv(mats[i % 2], x, xs, y_other, mode=other,
+                                           stream=stream), args.steps))
+    # one more step in the timed mode after the other rounds: the same bits
+    # as after the warm-up, and the fused kernel's bits equal to them too
+    step(1)
     torch.cuda.synchronize()
-    same = same and bool(np.array_equal(y.cpu().numpy().view(np.uint32), y_first.view(np.uint32)))
-    kern_ms, fused_ms, other_ms = (sorted(v)[1] for v in (kern, fused, oth))
+    y_last = y.cpu().numpy()
+    same = same and bool(np.array_equal(y_last.view(np.uint32), y_first.view(np.uint32)))
+    fused_same = bool(np.array_equal(y_fused.cpu().numpy().view(np.uint32),
+                                     y_first.view(np.uint32)))
+    kern_ms, fused_ms, other_ms = (float(np.median(v)) for v in (kern, fused, oth))
     ROUNDS.update(kernel=kern, fused=fused, other=oth)
+    HEAD_Y["y"] = y_last
+    HEAD_Y["checks"] = {"output_bits_stable_across_steps": same,
+                        "stable_over_timed_steps": same_steps,
+                        "fused_rmsq_q4mv_bits_equal": fused_same}
     return step_ms, kern_ms, fused_ms, same, other_ms
 
 
@@ -253,6 +358,7 @@ def run_chain(args, q4, torch, synth):
 
     log("generating decode-chain weights (24 layers, seed %d)" % args.seed)
     w = synth.chain_weights(seed=args.seed)
+    CHAIN_W["w"] = w  # kept for the CPU baseline's chain tokens
     mode = q4.FAST if args.mode == "fast" else q4.FIXED
     tok0 = chain_tok0(args.seed, synth)
     engines, bpt = {}, None
@@ -438,6 +544,226 @@ def run_attn_chain(args, q4, torch, synth):
     }
 
 
+def q4mv_bytes(rows: int, cols: int) -> int:
+    return head_bytes(rows, cols)
+
+
+def run_product(args, q4, torch, synth):
+    """The single 4096 x 2048 product (8.4M weights), timed three ways:
+    (i) the pages' per-call method, each call followed by a host wait:
+        (400-call run - 1-call run) / 400, six alternating rounds, with the
+        wait on the stream and through the queue's mailbox;
+    (ii) 400 calls back to back between two HIP events, one wait;
+    (iii) the same over 64 rotating weight copies (337 MB, more than the
+        256 MB Infinity Cache), so every call reads its weights from HBM.
+    (i) and (ii) re-read 5.3 MB that stay in the caches: cache rates, not
+    HBM rates.  Every one of the 400 outputs of (ii) is compared with the
+    first, and the hash of the last with the oracle's (golden file)."""
+    import numpy as np
+
+    g = golden("products", args.seed)
+    if g is None:
+        return {"skipped": "no golden file for seed %d" % args.seed}
+    gp = g["p4096x2048"]
+    m = synth.small_product(seed=args.seed, rows=4096, cols=2048, name=gp["name"])
+    W = q4.Q4Matrix.from_host(m)
+    x = torch.from_numpy(m["x"]).cuda()
+    xs = torch.from_numpy(from_hexbits(gp["xsum_bits"])).cuda()
+    mode = q4.FAST if args.mode == "fast" else q4.FIXED
+    stream = torch.cuda.current_stream()
+    y = torch.empty(4096, device="cuda")
+    n = 400
+
+    def call_sync(k):
+        for _ in range(k):
+            q4.q4mv(W, x, xs, y, mode=mode, stream=stream)
+            q4.q4_sync(stream)
+
+    queue = q4.Queue(mode=mode, stream=stream)
+    queue.set_wait(q4.WAIT_MAILBOX)
+
+    def call_mailbox(k):
+        for _ in range(k):
+            queue.q4mv_queue(W, x, xs, y)
+            queue.q4mv_wait()
+
+    def wall(fn, k):
+        t0 = time.perf_counter()
+        fn(k)
+        return time.perf_counter() - t0
+
+    settle(torch, lambda i: q4.q4mv(W, x, xs, y, mode=mode, stream=stream), args.settle / 3)
+    per_call = {"stream": [], "mailbox": []}
+    for _ in range(6):  # six alternating rounds, as the pages ran them
+        for name, fn in (("stream", call_sync), ("mailbox", call_mailbox)):
+            t400 = wall(fn, n)
+            t1 = wall(fn, 1)
+            per_call[name].append((t400 - t1) / n * 1e3)
+    queue.close()
+    hashes = {"per_call": fnv1a32(y.cpu().numpy())}
+
+    ys = torch.empty((n, 4096), device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    b2b = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(n):
+            q4.q4mv(W, x, xs, ys[i], mode=mode, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        b2b.append(ev[0].elapsed_time(ev[1]) / n)
+    yv = ys.view(torch.int32)
+    all_same = bool((yv == yv[0]).all().item())
+    hashes["back_to_back"] = fnv1a32(ys[n - 1].cpu().numpy())
+
+    copies = [W] + [q4.Q4Matrix(W.q.clone(), W.s.clone(), W.b.clone(), 4096, 2048)
+                    for _ in range(63)]
+    cold = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(n):
+            q4.q4mv(copies[i % 64], x, xs, ys[i], mode=mode, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        cold.append(ev[0].elapsed_time(ev[1]) / n)
+    all_same = all_same and bool((yv == yv[0]).all().item())
+    hashes["cold"] = fnv1a32(ys[n - 1].cpu().numpy())
+    del copies
+    nb = q4mv_bytes(4096, 2048)
+    want = gp["y_fnv1a32"] if mode == q4.FIXED else None
+    med = lambda v: float(np.median(v))
+    out = {
+        "workload": "q4mv 4096x2048 (8.4M weights), group 64, x ~ N(0,1), group sums from the "
+                    "oracle's golden file; %s order" % args.mode,
+        "algorithmic_bytes_per_call": nb,
+        "per_call_with_host_wait_ms": {k: stats(v) for k, v in per_call.items()},
+        "per_call_method": "(400-call run - 1-call run) / 400, wall clock, six alternating "
+                           "rounds; each call = one launch + one host wait (stream "
+                           "synchronise, or the queue's mailbox spin)",
+        "back_to_back_ms_per_call": stats(b2b),
+        "back_to_back_GBps_cache_resident": round(nb / (med(b2b) * 1e-3) / 1e9, 1),
+        "cold_64_copies_ms_per_call": stats(cold),
+        "cold_64_copies_GBps": round(nb / (med(cold) * 1e-3) / 1e9, 1),
+        "cold_64_copies_frac_of_peak": round(nb / (med(cold) * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "all_400_outputs_bit_identical": all_same,
+        "y_fnv1a32": hashes,
+        "y_fnv1a32_oracle": want,
+        "matches_oracle": (None if want is None else all(v == want for v in hashes.values())),
+    }
+    log("product 4096x2048: %s" % out)
+    return out
+
+
+def run_product_set(args, q4, torch, synth):
+    """One decode step's product set: 24 layers x {Q, K, V | O | gate, up |
+    down} + the head = 169 products in 97 stages, each product reading a
+    fixed seeded x of its width.  Per token: the stages as one captured
+    graph (one grouped launch per kernel shape and stage) with one host
+    wait; the device time of queued replays; and the stage queue driven
+    from the host with one wait per token, per stage and per product (the
+    pages' microbench of the same structure)."""
+    import numpy as np
+
+    g = golden("products", args.seed)
+    if g is None:
+        return {"skipped": "no golden file for seed %d" % args.seed}
+    gp = g["product_set"]
+    log("generating the product set (169 products, seed %d)" % args.seed)
+    ps = synth.product_set(seed=args.seed)
+    prods = ps["products"]
+    mats = [q4.Q4Matrix.from_host(p) for p in prods]
+    xd = {c: torch.from_numpy(x).cuda() for c, x in ps["x"].items()}
+    xsd = {int(c): torch.from_numpy(from_hexbits(v)).cuda() for c, v in gp["xsum_bits"].items()}
+    ys = [torch.full((p["rows"],), 7.0, device="cuda") for p in prods]
+    mode = q4.FAST if args.mode == "fast" else q4.FIXED
+    nb = sum(q4mv_bytes(p["rows"], p["cols"]) for p in prods)
+    del ps
+    torch.cuda.synchronize()
+
+    def enqueue(queue, wait):
+        stage = prods[0]["stage"]
+        for i, p in enumerate(prods):
+            if p["stage"] != stage:
+                if wait == "stage":
+                    queue.q4mv_wait()
+                else:
+                    queue.q4_stage()
+                stage = p["stage"]
+            queue.q4mv_queue(mats[i], xd[p["cols"]], xsd[p["cols"]], ys[i])
+            if wait == "product":
+                queue.q4mv_wait()
+        if wait == "graph":
+            queue.q4_stage()
+        else:
+            queue.q4mv_wait()
+
+    s = torch.cuda.Stream()
+    cap_queue = q4.Queue(mode=mode, stream=s)
+    graph = q4.Graph(s)
+    graph.begin()
+    try:
+        enqueue(cap_queue, "graph")
+    finally:
+        graph.end()
+    T = 20
+    settle(torch, lambda i: graph.launch(s), args.settle / 3, batch=1)
+    s.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(T):
+        graph.launch(s)
+        q4.q4_sync(s)
+    graph_wait = (time.perf_counter() - t0) * 1e3 / T
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(s)
+    for _ in range(T):
+        graph.launch(s)
+    ev[1].record(s)
+    s.synchronize()
+    graph_gpu = ev[0].elapsed_time(ev[1]) / T
+    got = [fnv1a32(y.cpu().numpy()) for y in ys]
+    graph_ok = mode != q4.FIXED or got == gp["y_fnv1a32"]
+    for y in ys:
+        y.fill_(7.0)
+    torch.cuda.synchronize()
+
+    eager = {}
+    for wait, how, tokens in (("token", q4.WAIT_STREAM, T), ("token", q4.WAIT_MAILBOX, T),
+                              ("stage", q4.WAIT_STREAM, 5), ("stage", q4.WAIT_MAILBOX, 5),
+                              ("product", q4.WAIT_STREAM, 3)):
+        queue = q4.Queue(mode=mode, stream=s)
+        queue.set_wait(how)
+        enqueue(queue, wait)  # one untimed token
+        t0 = time.perf_counter()
+        for _ in range(tokens):
+            enqueue(queue, wait)
+        ms = (time.perf_counter() - t0) * 1e3 / tokens
+        queue.close()
+        eager["wait_per_%s_%s_ms_per_token" % (wait, "mailbox" if how else "stream")] = round(ms, 4)
+    eager_ok = mode != q4.FIXED or [fnv1a32(y.cpu().numpy()) for y in ys] == gp["y_fnv1a32"]
+    graph.close()
+    cap_queue.close()
+    out = {
+        "workload": "product set of one decode step: 24 x {Q 2048x2048, K 512x2048, V 512x2048 | "
+                    "O 2048x2048 | gate, up 6144x2048 | down 2048x6144} + head 248320x2048; "
+                    "169 products, 97 stages; %s order" % args.mode,
+        "algorithmic_bytes_per_token": nb,
+        "graph_one_host_wait_ms_per_token": round(graph_wait, 4),
+        "graph_gpu_ms_per_token": round(graph_gpu, 4),
+        "graph_GBps": round(nb / (graph_gpu * 1e-3) / 1e9, 1),
+        "graph_frac_of_peak": round(nb / (graph_gpu * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "floor_ms_at_peak": round(nb / (PEAK_HBM_GBPS * 1e9) * 1e3, 4),
+        "eager_host_driven": eager,
+        "eager_note": "the queue API driven from Python: 169 q4mv_queue calls per token, so the "
+                      "host's own per-call cost is part of these figures",
+        "outputs_match_oracle_golden": {"graph": graph_ok, "eager": eager_ok},
+        "launches_per_token": "one grouped launch per kernel shape and stage (97)",
+    }
+    log("product set: %s" % out)
+    return out
+
+
 def chain_tok0(seed, synth):
     return synth.randint(seed, "ch.tok0", synth.VOCAB)
 
@@ -456,6 +782,11 @@ def main() -> int:
     ap.add_argument("--settle", type=float, default=SETTLE_S,
                     help="seconds of untimed steps before each section's warm-up (default %.1f)"
                     % SETTLE_S)
+    ap.add_argument("--rounds", type=int, default=7,
+                    help="interleaved kernel-alone rounds of the head (median reported)")
+    ap.add_argument("--sections", default=",".join(SECTIONS),
+                    help="comma-separated sections to run (default: all of %s); the head "
+                         "always runs" % ",".join(SECTIONS))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
                          "kernel that scales the HBM byte counters)")
@@ -466,9 +797,19 @@ def main() -> int:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(asked for --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
         return 2
-    if args.steps < 1:
-        print("--steps must be >= 1", file=sys.stderr)
+    if args.steps < 1 or args.rounds < 1:
+        print("--steps and --rounds must be >= 1", file=sys.stderr)
         return 2
+    want = {x.strip() for x in args.sections.split(",") if x.strip()}
+    if want - set(SECTIONS):
+        print("unknown sections: %s" % sorted(want - set(SECTIONS)), file=sys.stderr)
+        return 2
+    if args.no_chain:
+        want -= {"chain", "attn_chain"}
+    if args.no_atq:
+        want -= {"atq", "attn_chain"}
+    if args.no_cpu_baseline:
+        want.discard("cpu")
 
     import torch
 
@@ -496,13 +837,23 @@ def main() -> int:
     achieved = qb / (kern_ms * 1e-3) / 1e9
     log("head: %.4f ms/step; q4mv %.4f ms (%.1f GB/s); fused rmsq+q4mv %.4f ms"
         % (step_ms, kern_ms, achieved, fused_ms))
-    chain = None
-    if not args.no_chain:
-        chain = run_chain(args, q4, torch, synth)
-    atq = None if args.no_atq else run_atq(args, q4, torch, synth)
-    attn_chain = None if (args.no_chain or args.no_atq) else run_attn_chain(args, q4, torch, synth)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.seed)
+    product = run_product(args, q4, torch, synth) if "product" in want else None
+    product_set = run_product_set(args, q4, torch, synth) if "product_set" in want else None
+    torch.cuda.empty_cache()
+    chain = run_chain(args, q4, torch, synth) if "chain" in want else None
+    atq = run_atq(args, q4, torch, synth) if "atq" in want else None
+    attn_chain = run_attn_chain(args, q4, torch, synth) if "attn_chain" in want else None
+    cpu = None
+    if "cpu" in want:
+        cpu = cpu_baseline(args.seed, head_y=HEAD_Y.get("y") if args.mode == "fixed" else None,
+                           chain_w=CHAIN_W.get("w"))
     traffic = measured_traffic(qb)
+    gh = golden("products", args.seed)
+    head_checks = dict(HEAD_Y.get("checks", {}))
+    if gh is not None and args.mode == "fixed":
+        head_checks["y_fnv1a32"] = fnv1a32(HEAD_Y["y"])
+        head_checks["y_fnv1a32_oracle_golden"] = gh["head"]["y_fnv1a32"]
+        head_checks["matches_oracle_golden"] = head_checks["y_fnv1a32"] == gh["head"]["y_fnv1a32"]
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -524,6 +875,7 @@ def main() -> int:
             "untimed_settle_s_before_warmup": args.settle,
             "step_bytes": step_bytes,
             "output_bits_stable_across_steps": stable,
+            "output_checks": head_checks,
             "fused_rmsq_q4mv_ms": round(fused_ms, 5),
             "fused_rmsq_q4mv_GBps": round(norm_head_bytes(ROWS, COLS) / (fused_ms * 1e-3) / 1e9, 1),
         },
@@ -536,12 +888,19 @@ def main() -> int:
             "algorithmic_bytes_per_launch": qb,
             "avg_launch_ms": round(kern_ms, 5),
             "avg_launch_ms_rounds": [round(v, 5) for v in ROUNDS["kernel"]],
+            "avg_launch_ms_stats": stats(ROUNDS["kernel"]),
             "timing": "HIP events around %d back-to-back launches on the launch stream; median "
-                      "of 3 rounds interleaved with the other-mode and fused rounds" % args.steps,
+                      "of %d rounds interleaved with the other-mode and fused rounds"
+                      % (args.steps, args.rounds),
+            "traffic_source": "FETCH_SIZE + WRITE_SIZE per launch from rocprofv3 --pmc runs, "
+                              "scaled by the counters' reading of a 1 GiB copy; read from "
+                              "profiles/q4mv_head_hbm_counters.json while the kernel sources "
+                              "hash as when they were taken, else null",
             "other_mode": {
                 "mode": "fast" if args.mode == "fixed" else "fixed",
                 "avg_launch_ms": round(other_ms, 5),
                 "avg_launch_ms_rounds": [round(v, 5) for v in ROUNDS["other"]],
+                "avg_launch_ms_stats": stats(ROUNDS["other"]),
                 "achieved": round(qb / (other_ms * 1e-3) / 1e9, 1),
                 "frac": round(qb / (other_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             },
@@ -549,6 +908,8 @@ def main() -> int:
                                 "per launch; about 53 us with the weights L2-resident): "
                                 "profiles/q4mv_head_248320x2048_valu_counters.md",
         },
+        "product_4096x2048": product,
+        "product_set": product_set,
         "decode_chain": chain,
         "attention_step": atq,
         "attention_chain": attn_chain,
