@@ -19,6 +19,7 @@ import torch
 __all__ = [
     "FIXED", "FAST", "Q4Error", "Q4Matrix", "q4mv", "q4mv_add", "q4mv_norm",
     "q4mv_norm_swiglu", "q4mv_norm_argmax", "q4mv_norm_argmax_noalloc", "q4mv_argmax_ws_bytes",
+    "q4mv_variant", "VARIANTS",
     "rmsq", "swq",
     "q4_argmax", "q4_argmax_ws_bytes", "q4_embed", "Queue", "Graph", "q4_sync",
     "MlpLayer", "q4_decode_layers", "q4_decode_layers_ws_bytes", "q4_decode_layers_status",
@@ -76,6 +77,8 @@ _SIGS = {
                           ctypes.c_size_t, ctypes.c_int, _vp], ctypes.c_int),
     "q4mv_norm_argmax_noalloc": ([ctypes.POINTER(_Mat), _vp, _vp, ctypes.c_float, _vp, _vp,
                                   ctypes.c_int, _vp], ctypes.c_int),
+    "q4mv_variant": ([ctypes.POINTER(_Mat), _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, _vp],
+                     ctypes.c_int),
     "rmsq": ([_vp, _vp, _i32, ctypes.c_float, _vp, _vp, _vp], ctypes.c_int),
     "swq": ([_vp, _i32, _vp, _vp, ctypes.c_int, _vp], ctypes.c_int),
     "q4_argmax_ws_bytes": ([_i32], ctypes.c_size_t),
@@ -263,6 +266,22 @@ def q4mv_norm_argmax(w: Q4Matrix, h: torch.Tensor, wn: torch.Tensor, eps: float,
                                  _dev(state, state.dtype, None, "state"),
                                  state.numel() * state.element_size(), mode, _stream(stream)))
     return idx
+
+
+VARIANT_LANE_PER_ROW = 0
+VARIANTS = {"lane_per_row": 0, "wave_R1": 1, "wave_R2": 2, "wave_R4": 4, "wave_R8": 8}
+
+
+def q4mv_variant(w: Q4Matrix, x: torch.Tensor, xsum: torch.Tensor, y: torch.Tensor,
+                 variant: int, mode: int = FIXED, stream=None) -> torch.Tensor:
+    """``y = W x`` (2048 columns) by one of the kernel designs the pages
+    compare: ``variant`` 0 = one lane per row, 1/2/4/8 = one wave per row
+    with that many rows per block (4 is what ``q4mv`` runs)."""
+    _check("q4mv_variant", _lib.q4mv_variant(w.ref, _dev(x, torch.float32, w.cols, "x"),
+                                             _dev(xsum, torch.float32, w.cols // 64, "xsum"),
+                                             _dev(y, torch.float32, w.rows, "y"), int(variant),
+                                             mode, _stream(stream)))
+    return y
 
 
 def q4mv_norm_argmax_noalloc(w: Q4Matrix, h: torch.Tensor, wn: torch.Tensor, eps: float,

@@ -59,10 +59,11 @@ def _run(cmd: list, verbose: bool) -> None:
         print("\n".join(msgs), file=sys.stderr)
 
 
-def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=(), extra_flags=()) -> str:
     """Compile every source into affine_q4_matvec_amd/libq4mv.so (or `out`;
-    `defines` are extra -D tunables)."""
-    defs = ["-D" + d for d in defines]
+    `defines` are extra -D tunables, `extra_flags` extra compile and link
+    flags, e.g. host-only sanitizers for a test build)."""
+    defs = ["-D" + d for d in defines] + list(extra_flags)
     with tempfile.TemporaryDirectory(prefix="q4mv_build_") as tmpdir:
         objs = [os.path.join(tmpdir, s + ".o") for s in SOURCES]
         cmds = [[hipcc(), *FLAGS, *EXTRA_FLAGS.get(s, []), *defs, "-c", "-o", o,
@@ -72,7 +73,8 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
             for f in [ex.submit(_run, c, verbose) for c in cmds]:
                 f.result()
         tmp = out + ".tmp%d" % os.getpid()
-        _run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+        _run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *extra_flags, "-o", tmp, *objs],
+             verbose)
     os.replace(tmp, out)
     return out
 

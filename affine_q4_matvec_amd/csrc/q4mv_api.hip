@@ -387,6 +387,21 @@ int q4mv_norm_argmax(const q4_mat *w, const float *h, const float *wn, float eps
                             static_cast<hipStream_t>(stream));
 }
 
+int q4mv_variant(const q4_mat *w, const float *x, const float *xsum, float *y, int variant,
+                 int mode, void *stream) {
+  if (mode != Q4_FIXED && mode != Q4_FAST) return Q4_EINVAL;
+  if (variant != Q4_VARIANT_LANE_PER_ROW && variant != Q4_VARIANT_WAVE_R1 &&
+      variant != Q4_VARIANT_WAVE_R2 && variant != Q4_VARIANT_WAVE_R4 &&
+      variant != Q4_VARIANT_WAVE_R8)
+    return Q4_EINVAL;
+  if (!xsum) return Q4_EINVAL;
+  Prod p;
+  const int rc = make_prod(w, x, xsum, nullptr, y, &p);
+  if (rc != Q4_OK) return rc;
+  if (w->cols != 2048) return Q4_EINVAL;
+  return hip_status(q4::launch_q4mv_variant(p, variant, mode, static_cast<hipStream_t>(stream)));
+}
+
 int q4mv_norm_argmax_noalloc(const q4_mat *w, const float *h, const float *wn, float eps,
                              float *y, int32_t *idx, int mode, void *stream) {
   int rc = check_norm_argmax(w, h, wn, y, idx, mode);

@@ -78,6 +78,10 @@ int32_t resident_capacity(const Shape &sh, int mode);
 // the launch.
 hipError_t launch_q4mv_group(const ProdGroup &g, const Shape &sh, int mode, const Extra &ex,
                              hipStream_t st);
+// Measurement variants of a 2048-column product (see q4mv_variant in
+// q4mv.h): 0 = one lane per row, R = 1, 2, 4, 8 = one wave per row with R
+// rows per block.
+hipError_t launch_q4mv_variant(const Prod &p, int variant, int mode, hipStream_t st);
 hipError_t launch_rmsq(const float *h, const float *w, int32_t n, float eps, float *u,
                        float *us, hipStream_t st);
 hipError_t launch_swq(const float *a, int32_t n, float *o, float *os, int mode,

@@ -30,14 +30,13 @@
 //   epilogue kEpiArgmax  greedy argmax of y: each workgroup writes the key
 //                        of its best row; a one-workgroup kernel picks the
 //                        largest key
+#include <string.h>
+
 #include <atomic>
 
 #include "ops_device.h"
 #include "q4mv_device.h"
 
-#ifndef Q4_ROW64_R
-#define Q4_ROW64_R 4  // rows per wave iteration (loads in flight per lane)
-#endif
 #ifndef Q4_ROW64_MAX_WG
 #define Q4_ROW64_MAX_WG 2048  // cap when the occupancy query is unavailable
 #endif
@@ -68,11 +67,11 @@ using namespace dev;
 
 constexpr int kSegR = 4;
 constexpr int kThreads = 256;
-static_assert(Q4_ROW64_R == 1 || Q4_ROW64_R % 2 == 0, "rows per block: 1 or even");
-// The SwiGLU epilogue takes (gate, up) row pairs within a block: not with
-// one row per block (a build for measurements only; the fused call then
-// returns Q4_EINVAL).
-constexpr bool kRow64Swiglu = Q4_ROW64_R % 2 == 0;
+// Rows per block of the row64 kernel: four rows share each lane's
+// activations and are reduced together (quad_row_sums).  The measurement
+// variants (q4mv_variant) instantiate it for 1, 2 and 8 rows as well.
+constexpr int kRow64R = 4;
+static_assert(kRow64R % 2 == 0, "the SwiGLU epilogue takes (gate, up) row pairs of a block");
 
 // Activations of `chunk` and its group sum for prologues kProX / kProXsum.
 template <int PRO>
@@ -599,10 +598,10 @@ hipError_t launch_split(const ProdGroup &g, int passes, hipStream_t st) {
 template <bool FAST, int PRO, int EPI>
 hipError_t launch_row64(const ProdGroup &g, bool preload, const Extra &ex, hipStream_t st) {
   if (preload)
-    hipLaunchKernelGGL((q4mv_row64_kernel<Q4_ROW64_R, FAST, PRO, EPI, true>),
+    hipLaunchKernelGGL((q4mv_row64_kernel<kRow64R, FAST, PRO, EPI, true>),
                        dim3(g.wg_begin[g.n]), dim3(kThreads), 0, st, g, ex);
   else
-    hipLaunchKernelGGL((q4mv_row64_kernel<Q4_ROW64_R, FAST, PRO, EPI, false>),
+    hipLaunchKernelGGL((q4mv_row64_kernel<kRow64R, FAST, PRO, EPI, false>),
                        dim3(g.wg_begin[g.n]), dim3(kThreads), 0, st, g, ex);
   return hipGetLastError();
 }
@@ -619,7 +618,7 @@ template <bool FAST, bool PRELOAD>
 const void *row64_ptr(int pro, int epi) {
 #define Q4_PTR_CASE(P_, E_) \
   if (pro == P_ && epi == E_)   \
-    return reinterpret_cast<const void *>(&q4mv_row64_kernel<Q4_ROW64_R, FAST, P_, E_, PRELOAD>);
+    return reinterpret_cast<const void *>(&q4mv_row64_kernel<kRow64R, FAST, P_, E_, PRELOAD>);
   Q4_ROW64_VARIANTS(Q4_PTR_CASE)
 #undef Q4_PTR_CASE
   return nullptr;
@@ -629,7 +628,7 @@ const void *row64_ptr(int pro, int epi) {
 bool row64_single_pass(const ProdGroup &g) {
   for (int i = 0; i < g.n; ++i) {
     const long long waves = (long long)(g.wg_begin[i + 1] - g.wg_begin[i]) * (kThreads / kWave);
-    if ((long long)g.p[i].rows > waves * Q4_ROW64_R) return false;
+    if ((long long)g.p[i].rows > waves * kRow64R) return false;
   }
   return true;
 }
@@ -674,7 +673,179 @@ int32_t clamp_wg(long long need, long long cap) {
   return (int32_t)(need < cap ? need : cap);
 }
 
+// ---------------------------------------------------------------------------
+// Measurement variants of the 2048-column product (q4mv_variant).
+//
+// lane_row: one lane per row, the first Metal kernel of "Array.q4mv on
+// Metal: one kernel thread per row for products of 4M weights or more,
+// bit-identical" (#1435), Change.  Each lane walks its row's 32 groups in
+// order, 32 bytes of codes per group (two 16-byte loads 1 KiB from the next
+// lane's), with x and its group sums in LDS (every lane reads the same
+// address: a broadcast).  The sums keep the fixed tree: per group the
+// balanced tree over its 64 products (8-product word trees, then words,
+// then the two halves), and over the groups the balanced tree of 32, formed
+// as the groups arrive (a binary counter of partial sums: a left subtree is
+// always added before the right one, which is T).
+// ---------------------------------------------------------------------------
+constexpr int kLaneRowThreads = 256;
+
+// The term of group g of row r (fixed: T over its 64 products, then the
+// unfused affine step; fast: fused multiply-adds).
+template <bool FAST, bool PAIRS>
+__device__ __forceinline__ float lane_row_group(const u32x4 *qr, const float *sr, const float *br,
+                                                int g, const float *sx, const float *sxs) {
+  const u32x4 c0 = __builtin_nontemporal_load(qr + 2 * g);
+  const u32x4 c1 = __builtin_nontemporal_load(qr + 2 * g + 1);
+  const float sv = sr[g], bv = br[g];
+  float xv[64];
+#pragma unroll
+  for (int k = 0; k < 64; k += 4) {
+    const float4 v = *reinterpret_cast<const float4 *>(sx + 64 * g + k);
+    xv[k] = v.x;
+    xv[k + 1] = v.y;
+    xv[k + 2] = v.z;
+    xv[k + 3] = v.w;
+  }
+  if constexpr (!FAST) {
+    const float d = chunk_tree<PAIRS>(c0, xv) + chunk_tree<PAIRS>(c1, xv + 32);
+    const float sd = sv * d;
+    const float bx = bv * sxs[g];
+    return sd + bx;
+  } else {
+    const float dot = chunk_dot_fast<PAIRS>(c0, xv) + chunk_dot_fast<PAIRS>(c1, xv + 32);
+    return fmaf(sv, dot, bv * sxs[g]);
+  }
+}
+
+// Row r: the groups in 8 blocks of 4.  Fixed order: each block's balanced
+// tree, then the blocks' balanced tree formed as they arrive (a binary
+// counter: lv[k] holds the last complete run of 2^k blocks, always added as
+// the left operand), which is the balanced tree over the 32 groups, T.
+template <bool FAST, bool PAIRS>
+__device__ __forceinline__ float lane_row_sum(const Prod &P, int r, const float *sx,
+                                              const float *sxs) {
+  const u32x4 *qr = reinterpret_cast<const u32x4 *>(P.q) + (size_t)r * 64;  // 1 KiB per row
+  const float *sr = P.s + (size_t)r * 32;
+  const float *br = P.b + (size_t)r * 32;
+  float lv0 = 0.0f, lv1 = 0.0f, lv2 = 0.0f, acc = 0.0f;
+#pragma unroll 1
+  for (int j = 0; j < 8; ++j) {
+    float t[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t[k] = lane_row_group<FAST, PAIRS>(qr, sr, br, 4 * j + k, sx, sxs);
+    if constexpr (FAST) {
+      acc = ((acc + t[0]) + t[1]) + (t[2] + t[3]);
+    } else {
+      float b = (t[0] + t[1]) + (t[2] + t[3]);
+      if (j & 1) {
+        b = lv0 + b;
+        if (j & 2) {
+          b = lv1 + b;
+          if (j & 4)
+            b = lv2 + b;
+          else
+            lv2 = b;
+        } else {
+          lv1 = b;
+        }
+      } else {
+        lv0 = b;
+      }
+      acc = b;  // after the last block (j = 7): the sum of all 32 groups
+    }
+  }
+  return acc;
+}
+
+template <bool FAST>
+__global__ __launch_bounds__(kLaneRowThreads) void q4mv_lane_row_kernel(Prod P) {
+  __shared__ float sx[2048];
+  __shared__ float sxs[32];
+  // x (pre-scaled for the pair decode when every |x| < 2^118) and its sums
+  bool large = false;
+  for (int i = threadIdx.x; i < 2048; i += kLaneRowThreads)
+    large |= !(__builtin_fabsf(P.x[i]) < 0x1p118f);
+  const bool pairs = !__syncthreads_or(large);
+  const float scale = pairs ? 1.0f / fp8_unit() : 1.0f;
+  for (int i = threadIdx.x; i < 2048; i += kLaneRowThreads) sx[i] = P.x[i] * scale;
+  if (threadIdx.x < 32) sxs[threadIdx.x] = P.xs[threadIdx.x];
+  __syncthreads();
+  for (int r = blockIdx.x * kLaneRowThreads + threadIdx.x; r < P.rows;
+       r += gridDim.x * kLaneRowThreads) {
+    const float v = pairs ? lane_row_sum<FAST, true>(P, r, sx, sxs)
+                          : lane_row_sum<FAST, false>(P, r, sx, sxs);
+    P.y[r] = v;
+  }
+}
+
+// wave_R: the row64 kernel with R rows per block (R = 1, 2, 4, 8): the rows
+// of a block share the lane's activations in registers; [P1] (#1440), Change
+// and Verification, q4mv bullet, names the sharing of one activation group by
+// 4 rows of a SIMD group and found 2 and 8 rows no better.
+template <int R, bool FAST>
+hipError_t launch_wave_variant(const Prod &p, hipStream_t st) {
+  ProdGroup g;
+  memset(&g, 0, sizeof(g));
+  g.n = 1;
+  g.p[0] = p;
+  const int wpg = kThreads / kWave;
+  const long long need = (p.rows + (long long)wpg * R - 1) / ((long long)wpg * R);
+  int dev = 0, per_cu = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidValue;
+  const void *kpre = reinterpret_cast<const void *>(
+      &q4mv_row64_kernel<R, FAST, kProX, kEpiStore, true>);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kpre, kThreads, 0) != hipSuccess)
+    return hipErrorInvalidValue;
+  const Extra ex{};
+  if (need <= (long long)per_cu * cus) {
+    for (int i = 1; i <= kMaxGroup; ++i) g.wg_begin[i] = (int32_t)need;
+    hipLaunchKernelGGL((q4mv_row64_kernel<R, FAST, kProX, kEpiStore, true>), dim3((int)need),
+                       dim3(kThreads), 0, st, g, ex);
+    return hipGetLastError();
+  }
+  const void *kloop = reinterpret_cast<const void *>(
+      &q4mv_row64_kernel<R, FAST, kProX, kEpiStore, false>);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kloop, kThreads, 0) != hipSuccess)
+    return hipErrorInvalidValue;
+  if (per_cu > Q4_ROW64_LOOP_WG_PER_CU) per_cu = Q4_ROW64_LOOP_WG_PER_CU;
+  const int nwg = (per_cu < 1 ? 1 : per_cu) * cus;
+  for (int i = 1; i <= kMaxGroup; ++i) g.wg_begin[i] = nwg;
+  hipLaunchKernelGGL((q4mv_row64_kernel<R, FAST, kProX, kEpiStore, false>), dim3(nwg),
+                     dim3(kThreads), 0, st, g, ex);
+  return hipGetLastError();
+}
+
+template <bool FAST>
+hipError_t launch_variant(const Prod &p, int variant, hipStream_t st) {
+  switch (variant) {
+    case 0: {
+      // one lane per row: as many workgroups as the rows need (the pages'
+      // grid), at most 8 per compute unit's worth, looping beyond
+      int dev = 0, cus = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipErrorInvalidValue;
+      const long long need = (p.rows + kLaneRowThreads - 1) / kLaneRowThreads;
+      const long long cap = 8LL * (cus < 1 ? 1 : cus);
+      hipLaunchKernelGGL(q4mv_lane_row_kernel<FAST>, dim3((int)(need < cap ? need : cap)),
+                         dim3(kLaneRowThreads), 0, st, p);
+      return hipGetLastError();
+    }
+    case 1: return launch_wave_variant<1, FAST>(p, st);
+    case 2: return launch_wave_variant<2, FAST>(p, st);
+    case 4: return launch_wave_variant<4, FAST>(p, st);
+    case 8: return launch_wave_variant<8, FAST>(p, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_q4mv_variant(const Prod &p, int variant, int mode, hipStream_t st) {
+  return mode != 0 ? launch_variant<true>(p, variant, st) : launch_variant<false>(p, variant, st);
+}
 
 Shape shape_of(int32_t cols, int pro, int epi) {
   const int G = cols / 64;
@@ -687,7 +858,7 @@ Shape shape_of(int32_t cols, int pro, int epi) {
 }
 
 bool shape_supported(const Shape &sh) {
-  if (sh.kind == Shape::kRow64) return sh.epi != kEpiSwiglu || kRow64Swiglu;
+  if (sh.kind == Shape::kRow64) return true;
   return sh.epi == kEpiStore && sh.pro != kProNorm;
 }
 
@@ -716,7 +887,7 @@ int32_t workgroups_for(const Shape &sh, int32_t rows, int mode) {
       // (the preloading variant then runs); otherwise Q4_ROW64_LOOP_WG_PER_CU
       // workgroups per compute unit (or fewer if fewer fit), all resident
       // at once
-      const long long need = (rows + wpg * Q4_ROW64_R - 1) / (wpg * Q4_ROW64_R);
+      const long long need = (rows + wpg * kRow64R - 1) / (wpg * kRow64R);
       const int cap_pre = row64_capacity(sh, mode, true);
       if (cap_pre > 0 && need <= cap_pre) return clamp_wg(need, cap_pre);
       const int cap = row64_capacity(sh, mode, false);

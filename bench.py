@@ -47,7 +47,7 @@ SETTLE_S = 0.3  # untimed steps before the warm-up, to bring the GPU clocks up
 ROUNDS = {}  # the kernel-alone rounds of the head (ms per launch)
 HEAD_Y = {}  # the head's output in the timed mode (host copy) and its checks
 CHAIN_W = {}  # the decode chain's host weights, once generated
-SECTIONS = ("head", "product", "product_set", "chain", "atq", "attn_chain", "cpu")
+SECTIONS = ("head", "variants", "product", "product_set", "chain", "atq", "attn_chain", "cpu")
 
 
 def head_bytes(rows: int, cols: int) -> int:
@@ -656,6 +656,65 @@ def run_product(args, q4, torch, synth):
     return out
 
 
+def run_variants(args, q4, torch, synth):
+    """The kernel designs the pages compare, on the 248320 x 2048 head (two
+    weight copies alternating, x and its sums from rmsq): one lane per row
+    (the pages' first Metal kernel) and one wave per row with 1, 2, 4 or 8
+    rows per block sharing the activations (4 is what q4mv runs).  Each
+    variant is timed over args.rounds interleaved rounds of args.steps
+    back-to-back launches (min / median / max), and its output's hash is
+    compared with the oracle's."""
+    import numpy as np
+
+    g = golden("products", args.seed)
+    h = synth.head_inputs(seed=args.seed)
+    W0 = q4.Q4Matrix.from_host(h)
+    W1 = q4.Q4Matrix(W0.q.clone(), W0.s.clone(), W0.b.clone(), ROWS, COLS)
+    mats = [W0, W1]
+    z = torch.from_numpy(h["z"]).cuda()
+    wn = torch.from_numpy(h["wn"]).cuda()
+    del h
+    x = torch.empty(COLS, device="cuda")
+    xs = torch.empty(COLS // 64, device="cuda")
+    q4.rmsq(z, wn, float(synth.EPS), x, xs)
+    mode = q4.FAST if args.mode == "fast" else q4.FIXED
+    stream = torch.cuda.current_stream()
+    ys = {name: torch.empty(ROWS, device="cuda") for name in q4.VARIANTS}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(name):
+        v, y = q4.VARIANTS[name], ys[name]
+        ev[0].record(stream)
+        for i in range(args.steps):
+            q4.q4mv_variant(mats[i % 2], x, xs, y, v, mode=mode, stream=stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / args.steps
+
+    settle(torch, lambda i: q4.q4mv_variant(mats[i % 2], x, xs, ys["wave_R4"], 4, mode=mode,
+                                            stream=stream), args.settle)
+    times = {name: [] for name in q4.VARIANTS}
+    for _ in range(args.rounds):
+        for name in q4.VARIANTS:
+            times[name].append(timed(name))
+    nb = head_bytes(ROWS, COLS)
+    want = g["head"]["y_fnv1a32"] if (g is not None and mode == q4.FIXED) else None
+    out = {"workload": "248320x2048 head, x from rmsq, two weight copies; %s order" % args.mode,
+           "timing": "HIP events around %d back-to-back launches, %d interleaved rounds"
+                     % (args.steps, args.rounds)}
+    for name in q4.VARIANTS:
+        med = float(np.median(times[name]))
+        hsh = fnv1a32(ys[name].cpu().numpy())
+        out[name] = {"us_per_launch": {k: round(v * 1e3, 2) for k, v in stats(times[name]).items()
+                                       if k != "n"},
+                     "GBps": round(nb / (med * 1e-3) / 1e9, 1),
+                     "frac_of_peak": round(nb / (med * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "y_fnv1a32": hsh,
+                     "matches_oracle": None if want is None else hsh == want}
+    log("variants: %s" % out)
+    return out
+
+
 def run_product_set(args, q4, torch, synth):
     """One decode step's product set: 24 layers x {Q, K, V | O | gate, up |
     down} + the head = 169 products in 97 stages, each product reading a
@@ -837,6 +896,8 @@ def main() -> int:
     achieved = qb / (kern_ms * 1e-3) / 1e9
     log("head: %.4f ms/step; q4mv %.4f ms (%.1f GB/s); fused rmsq+q4mv %.4f ms"
         % (step_ms, kern_ms, achieved, fused_ms))
+    variants = run_variants(args, q4, torch, synth) if "variants" in want else None
+    torch.cuda.empty_cache()
     product = run_product(args, q4, torch, synth) if "product" in want else None
     product_set = run_product_set(args, q4, torch, synth) if "product_set" in want else None
     torch.cuda.empty_cache()
@@ -908,6 +969,7 @@ def main() -> int:
                                 "per launch; about 53 us with the weights L2-resident): "
                                 "profiles/q4mv_head_248320x2048_valu_counters.md",
         },
+        "head_kernel_variants": variants,
         "product_4096x2048": product,
         "product_set": product_set,
         "decode_chain": chain,

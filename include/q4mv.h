@@ -153,6 +153,29 @@ int q4mv_norm_argmax_noalloc(const q4_mat *w, const float *h, const float *wn, f
                              float *y, int32_t *idx, int mode, void *stream);
 
 /*
+ * q4mv_variant: q4mv of a 2048-column matrix by one of the kernel designs
+ * the pages compare, for measuring them side by side (same arguments as
+ * q4mv; xsum required; same results: bit-identical in Q4_FIXED).
+ *   Q4_VARIANT_LANE_PER_ROW  one lane per row, walking its row's groups in
+ *                            order ([P3] Change: one kernel thread per row;
+ *                            [P3] Limits: its strided reads stay below the
+ *                            memory bandwidth).
+ *   Q4_VARIANT_WAVE_R1 / R2 / R4 / R8
+ *                            one wave per row, 1, 2, 4 or 8 rows per block
+ *                            sharing each lane's activations ([P1] Change,
+ *                            q4mv bullet: 4 rows of a SIMD group share each
+ *                            activation group; Verification: 2 and 8 rows
+ *                            were no better).  R4 is the kernel q4mv runs.
+ */
+#define Q4_VARIANT_LANE_PER_ROW 0
+#define Q4_VARIANT_WAVE_R1 1
+#define Q4_VARIANT_WAVE_R2 2
+#define Q4_VARIANT_WAVE_R4 4
+#define Q4_VARIANT_WAVE_R8 8
+int q4mv_variant(const q4_mat *w, const float *x, const float *xsum, float *y, int variant,
+                 int mode, void *stream);
+
+/*
  * rmsq: the RMS norm of h scaled by float weights, and the sum of each 64
  * consecutive outputs, which is the xsum input of the next q4mv ([P1]
  * Change, rmsq bullet; bit-exact on the pages' GPU).

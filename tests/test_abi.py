@@ -9,7 +9,9 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "q4mv.h")
-LIB = os.path.join(ROOT, "affine_q4_matvec_amd", "libq4mv.so")
+# Q4MV_TEST_LIB: another build of the library to check (the sanitizer test
+# runs this module against a host-sanitized build)
+LIB = os.environ.get("Q4MV_TEST_LIB") or os.path.join(ROOT, "affine_q4_matvec_amd", "libq4mv.so")
 
 EINVAL = -1
 
@@ -366,3 +368,27 @@ def test_block_wrapper_checks_cache_shapes():
     with pytest.raises(ValueError):
         q4.AttnBlock(None, None, None, None, None, torch.zeros(4, 16, 128), torch.zeros(4, 8, 128),
                      None)
+
+
+def test_q4mv_variant_rejects_bad_arguments(L):
+    p = lambda v: ctypes.c_void_p(v)
+    m = mat(cols=2048)
+    assert L.q4mv_variant(ctypes.byref(m), p(D), p(E), p(F), 3, 0, None) == EINVAL   # no such variant
+    assert L.q4mv_variant(ctypes.byref(m), p(D), None, p(F), 4, 0, None) == EINVAL   # xsum required
+    assert L.q4mv_variant(ctypes.byref(m), p(D), p(E), p(F), 4, 2, None) == EINVAL   # mode
+    m1 = mat(cols=1024)
+    assert L.q4mv_variant(ctypes.byref(m1), p(D), p(E), p(F), 0, 0, None) == EINVAL  # 2048 columns only
+    assert L.q4mv_variant(ctypes.byref(m), p(D), p(E), p(D + 64), 4, 0, None) == EINVAL  # y overlaps x
+
+
+def test_q4mv_norm_argmax_noalloc_rejects_bad_arguments(L):
+    p = lambda v: ctypes.c_void_p(v)
+    m = mat(cols=2048)
+    f = ctypes.c_float(1e-6)
+    assert L.q4mv_norm_argmax_noalloc(ctypes.byref(m), p(D), p(E), f, p(F), None, 0, None) == EINVAL
+    assert L.q4mv_norm_argmax_noalloc(ctypes.byref(m), p(D + 4), p(E), f, p(F), p(F + 8192), 0,
+                                      None) == EINVAL  # h not 16-byte aligned
+    assert L.q4mv_norm_argmax_noalloc(ctypes.byref(mat(cols=1024)), p(D), p(E), f, p(F),
+                                      p(F + 8192), 0, None) == EINVAL
+    assert L.q4mv_norm_argmax_noalloc(ctypes.byref(m), p(D), p(E), f, p(F), p(F + 8192), 5,
+                                      None) == EINVAL  # mode

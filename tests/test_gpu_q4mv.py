@@ -245,3 +245,23 @@ def test_q4mv_argument_errors():
         q4.q4mv(W, x, xs, y, mode=7)
     q4.q4mv(W, x, xs, y)  # the library still works afterwards
     torch.cuda.synchronize()
+
+
+# Shapes whose kernels loop: the split kernel (rows over 2048-column passes)
+# takes more than one block of 4 rows per workgroup past 4 x 2048 rows, with
+# the next block's loads issued while the current one is summed; the seg
+# kernel (rows under 2048 columns) strides over its grid past 16384 rows at
+# 31 groups per row and past 32768 at 16.  Ragged tails in every case.
+@pytest.mark.parametrize("rows,cols", [(8197, 6144), (8195, 2112), (16411, 1984), (32771, 1024)])
+def test_q4mv_split_and_seg_loops(rows, cols):
+    print("q4mv loop path %dx%d" % (rows, cols), flush=True)
+    m = synth.small_product(seed=23, rows=rows, cols=cols, name="lp%d_%d" % (rows, cols))
+    xs = oracle.group_sums(m["x"])
+    want = oracle.q4mv(m, m["x"], xs, NTHREADS)
+    got = run_q4mv(m, m["x"], xs, mode=0)
+    assert_bits_equal(got, want, "loop path %dx%d" % (rows, cols))
+    r = synth.normal_f32(23, "lpr%d" % rows, (rows,), 0.0, 2.0)
+    q4 = lib()
+    y = q4.q4mv_add(q4.Q4Matrix.from_host(m), dev(m["x"]), dev(xs), dev(r))
+    torch.cuda.synchronize()
+    assert_bits_equal(host(y), oracle.add(r, want), "loop path with residual %dx%d" % (rows, cols))
