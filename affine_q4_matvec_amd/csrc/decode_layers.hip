@@ -68,6 +68,7 @@ using namespace dev;
 using namespace decode;
 
 // Threads of the workgroup that poll m in stage B (the last four waves).
+// Each polls NP chunks of 8 values (NP * 2048 values of m in all).
 constexpr int kPollThreads = 256;
 
 // e[c] of the embedding row tk (the embed kernel's arithmetic; NaN for a
@@ -185,33 +186,46 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
     // poll that starts early only adds traffic at the lines being polled)
     if (t == 0) S.flag[0] = S.flag[1] = 0u;
     __syncthreads();
+    // the pollers' chunks: c = p + r * kPollThreads, r < kPerPoller, one at
+    // a time.  The hand-offs are bound by the polled traffic: every
+    // workgroup reads all of m (NP * 16 KB of tagged words), and polling
+    // several chunks in the same rounds multiplies the traffic while the
+    // wait lasts (three at once: 0.369 -> 0.394 ms per token).
+    constexpr int kBatch = 1;
+    const uint64_t *mcopy = mq + (size_t)copy * kDecodeMaxInter;
     if (poller) {
       const int p = t - (kThreads - kPollThreads);
       bool large = false;
-      // one chunk at a time: polling several in the same rounds multiplies
-      // the polled traffic while the wait lasts
+      // values pre-scaled for the pair decode (the scaling of
+      // prescale_for_pairs), unless some value of the workgroup turns out
+      // to be large: then the raw values are written over them below
+      const float scale = 1.0f / fp8_unit();
 #pragma unroll 1
-      for (int r = 0; r < kPerPoller; ++r) {
-        const int c = p + r * kPollThreads;
-        float xm[8];
-        if (!poll_tagged<8>(mq + (size_t)copy * kDecodeMaxInter + 8 * c, tag0 + 2 * l + 1, xm,
-                            err, A.spin_ticks)) {
+      for (int r0 = 0; r0 < kPerPoller; r0 += kBatch) {
+        float xm[kBatch * 8];
+        if (!poll_tagged<8>(mcopy + 8 * (p + r0 * kPollThreads), tag0 + 2 * l + 1, xm, err,
+                            A.spin_ticks)) {
           S.flag[0] = 1u;
           break;
         }
-        // group sums: T over each chunk, then over 8 chunks (8 consecutive
-        // lanes) by a butterfly: the balanced tree over the group's 64 values
-        float g = ops::tree8(xm);
-        g = g + __shfl_xor(g, 1);
-        g = g + __shfl_xor(g, 2);
-        g = g + __shfl_xor(g, 4);
-        if ((c & 7) == 0) S.xs[c >> 3] = g;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) large |= !(__builtin_fabsf(xm[k]) < 0x1p118f);
-        // value i of m sits at i + 4 (i / 32) in the padded layout
-        float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * c + 4 * (c >> 2));
-        dst[0] = make_float4(xm[0], xm[1], xm[2], xm[3]);
-        dst[1] = make_float4(xm[4], xm[5], xm[6], xm[7]);
+        for (int r = 0; r < kBatch; ++r) {
+          const int c = p + (r0 + r) * kPollThreads;
+          const float *v = xm + 8 * r;
+          // group sums: T over each chunk, then over 8 chunks (8 consecutive
+          // lanes) by a butterfly: the balanced tree over the group's 64
+          float g = ops::tree8(v);
+          g = g + __shfl_xor(g, 1);
+          g = g + __shfl_xor(g, 2);
+          g = g + __shfl_xor(g, 4);
+          if ((c & 7) == 0) S.xs[c >> 3] = g;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) large |= !(__builtin_fabsf(v[k]) < 0x1p118f);
+          // value i of m sits at i + 4 (i / 32) in the padded layout
+          float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * c + 4 * (c >> 2));
+          dst[0] = make_float4(v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale);
+          dst[1] = make_float4(v[4] * scale, v[5] * scale, v[6] * scale, v[7] * scale);
+        }
       }
       if (large) S.flag[1] = 1u;
       // this wave's gate/up rows of the next layer, now that its polls are done
@@ -221,25 +235,28 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
     }
     __syncthreads();
     if (S.flag[0] != 0u) return;
-    // pre-scaled for the pair decode unless some value of the workgroup is
-    // large (the scaling of prescale_for_pairs, in place)
     const bool pairs = S.flag[1] == 0u;
-    if (pairs) {
-      const float scale = 1.0f / fp8_unit();
+    if (!pairs) {
+      // some |m| >= 2^118: the plain decode, on the raw values read again
+      // from the tagged words (they carry this layer's tag until every
+      // workgroup, this one included, has done this layer's down rows)
+      if (poller) {
+        const int p = t - (kThreads - kPollThreads);
+#pragma unroll 1
+        for (int r = 0; r < kPerPoller; ++r) {
+          const int c = p + r * kPollThreads;
+          float v[8];
 #pragma unroll
-      for (int r = 0; r < kChunks / kThreads + 1; ++r) {
-        const int c = t + r * kThreads;
-        if (c < kChunks) {
-          float4 *v = reinterpret_cast<float4 *>(S.x + 8 * c + 4 * (c >> 2));
-          float4 a0 = v[0], a1 = v[1];
-          a0.x = a0.x * scale; a0.y = a0.y * scale; a0.z = a0.z * scale; a0.w = a0.w * scale;
-          a1.x = a1.x * scale; a1.y = a1.y * scale; a1.z = a1.z * scale; a1.w = a1.w * scale;
-          v[0] = a0;
-          v[1] = a1;
+          for (int k = 0; k < 8; ++k)
+            v[k] = __uint_as_float((uint32_t)__hip_atomic_load(
+                mcopy + 8 * c + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * c + 4 * (c >> 2));
+          dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+          dst[1] = make_float4(v[4], v[5], v[6], v[7]);
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
     if (has_row) {
       const float v = pairs ? down_row<NP, FAST, true>(S, lane, d)
                             : down_row<NP, FAST, false>(S, lane, d);

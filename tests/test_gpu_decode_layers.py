@@ -58,6 +58,25 @@ def test_decode_layers_bit_exact(inter, nlayers):
         assert_bits_equal(got, want, "h inter=%d layers=%d tok=%d" % (inter, nlayers, tok))
 
 
+def test_decode_layers_large_m_takes_the_plain_decode():
+    """One value of m near 2^120 (gate and up of one pair near 2^60): the
+    workgroups cannot pre-scale m for the pair decode and must sum the down
+    rows from the raw values; every h bit as the oracle's."""
+    q4 = lib()
+    w = synth.chain_weights(seed=47, layers=1, inter=2048, vocab=300)
+    tok = 11
+    w["head"]["s"][tok, :] = 0.0  # h = the embedding row = all ones
+    w["head"]["b"][tok, :] = 1.0
+    lw = w["layers"][0]
+    for name in ("gate", "up"):
+        lw[name]["s"][5, :] = 0.0
+        lw[name]["b"][5, :] = np.float32(2.0**49)
+    want = oracle.chain_hidden(w, tok, NTHREADS)
+    assert np.all(np.isfinite(want)) and np.max(np.abs(want)) > 2.0**100
+    got, _ = run_layers(q4, q4.Q4Matrix.from_host(w["head"]), mlp_layers(q4, w), w, tok)
+    assert_bits_equal(got, want, "h with m near 2^120")
+
+
 def test_decode_layers_token_out_of_range_gives_nan():
     q4 = lib()
     w = synth.chain_weights(seed=45, layers=1, vocab=500)
