@@ -211,6 +211,47 @@ def cpu_baseline(seed: int, head_y=None, chain_w=None, budget_s: float = 6.0):
     return out
 
 
+def record_traffic(paths) -> int:
+    """Writes profiles/q4mv_head_hbm_counters.json from four rocprofv3 --pmc
+    counter_collection.csv files: FETCH_SIZE and WRITE_SIZE of a head run
+    (bench.py --sections head), then of --calibrate-copy.  The copy kernel
+    reads and writes a known 1 GiB per dispatch, which scales each counter
+    to bytes."""
+    import csv
+
+    def mean_kib(path, kernel_part, counter):
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                if kernel_part in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        if not vals:
+            raise SystemExit("no %s rows for %s in %s" % (counter, kernel_part, path))
+        return sum(vals) / len(vals), len(vals)
+
+    head = "q4mv_row64_kernel<4, false, 0, 0, false>"
+    fh, nf = mean_kib(paths[0], head, "FETCH_SIZE")
+    wh, nw = mean_kib(paths[1], head, "WRITE_SIZE")
+    fc, _ = mean_kib(paths[2], "copyBuffer", "FETCH_SIZE")
+    wc, _ = mean_kib(paths[3], "copyBuffer", "WRITE_SIZE")
+    gib = 1 << 30
+    ff, wf = gib / (fc * 1024), gib / (wc * 1024)
+    total = round(fh * 1024 * ff + wh * 1024 * wf)
+    rec = {"kernel": "q4mv_row64_kernel<4,false,kProX,kEpiStore,no preload> (fixed order), "
+                     "248320x2048 head",
+           "kernel_source_sha256_16": kernel_source_hash(),
+           "fetch_size_kib_per_dispatch": round(fh, 3), "write_size_kib_per_dispatch": round(wh, 3),
+           "dispatches": [nf, nw],
+           "copy_calibration": {"bytes_read": gib, "bytes_written": gib,
+                                "fetch_size_kib": round(fc, 3), "write_size_kib": round(wc, 3),
+                                "fetch_factor": round(ff, 6), "write_factor": round(wf, 6)},
+           "hbm_bytes_per_launch": total,
+           "algorithmic_bytes_per_launch": head_bytes(ROWS, COLS),
+           "traffic_over_algorithmic": round(total / head_bytes(ROWS, COLS), 5)}
+    out = os.path.join(ROOT, "profiles", "q4mv_head_hbm_counters.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+    return 0
+
+
 def run_head(args, q4, torch, synth):
     import numpy as np
 
@@ -849,7 +890,13 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the known-size "
                          "kernel that scales the HBM byte counters)")
+    ap.add_argument("--record-traffic", nargs=4, metavar="CSV",
+                    help="write profiles/q4mv_head_hbm_counters.json from the rocprofv3 "
+                         "counter_collection.csv files of FETCH_SIZE and WRITE_SIZE runs of "
+                         "the head, then of --calibrate-copy (no GPU needed)")
     args = ap.parse_args()
+    if args.record_traffic:
+        return record_traffic(args.record_traffic)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
