@@ -56,7 +56,7 @@ def test_attn_chain_steps_bit_exact(use_graph):
 
 
 def test_attn_chain_24_layers_golden_tokens():
-    """64 tokens of the 24-layer chain with attention through one captured
+    """200 tokens of the 24-layer chain with attention through one captured
     graph with the mailbox wait: tokens and logits hashes as the oracle
     wrote them."""
     from affine_q4_matvec_amd.chain import AttnDecodeChain

@@ -3,7 +3,7 @@ q4_decode_block: the attention block and the MLP block of every layer in
 one launch whose stages hand their outputs to each other through tagged
 words), driven through AttnDecodeChain(persistent=True): step by step and
 as graph replays against the oracle's attn_chain_step, bit for bit, for 1
-to 16 key/value heads; 64 tokens of the 24-layer chain against the
+to 16 key/value heads; 200 tokens of the 24-layer chain against the
 oracle's golden file; the hidden state after a stack of layers and after
 single-layer launches against the oracle's; the bounded waits; positions
 outside the cache."""
@@ -267,3 +267,30 @@ def test_stack_rejects_caches_of_other_lengths():
                          q4.MlpLayer(lw["gu"], lw["down"], lw["wn"]))
     with pytest.raises(ValueError):
         q4.BlockStack([chain.layers[0]["blk"], short])
+
+
+LONG_GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                           "attn_chain_long_seed20261202.json")
+
+
+@pytest.mark.parametrize("persistent", [False, True])
+def test_attn_chain_long_cache_golden_tokens(persistent):
+    """200 tokens at positions 3896..4095 of a 4096-position cache (all 16
+    spans of a head in use; earlier rows zero, as the oracle's fresh
+    caches), both engines: tokens and logits hashes as the oracle wrote
+    them."""
+    from affine_q4_matvec_amd.chain import AttnDecodeChain
+    g = json.load(open(LONG_GOLDEN))
+    print("attention chain at the end of a %d cache, persistent %s, %d golden tokens"
+          % (g["max_pos"], persistent, len(g["tokens"])), flush=True)
+    w = synth.attn_chain_weights(seed=g["seed"], max_pos=g["max_pos"])
+    chain = AttnDecodeChain(w, persistent=persistent)
+    s = torch.cuda.Stream()
+    hashes = []
+    toks = chain.run(g["tok0"], len(g["tokens"]), s, wait="mailbox", pos0=g["pos0"],
+                     on_step=lambda i, c: hashes.append(oracle.fnv1a32(host(c.logits))))
+    assert toks == g["tokens"]
+    assert hashes == g["logits_fnv1a32"]
+    assert lib().q4_atq_status(chain.atq_ws, w["hq"], w["hkv"], s) == lib().Q4_OK
+    if persistent:
+        assert lib().q4_decode_block_status(chain.block_ws, s) == lib().Q4_OK
