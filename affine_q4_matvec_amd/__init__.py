@@ -23,6 +23,7 @@ __all__ = [
     "rmsq", "swq",
     "q4_argmax", "q4_argmax_ws_bytes", "q4_embed", "Queue", "Graph", "q4_sync",
     "MlpLayer", "q4_decode_layers", "q4_decode_layers_ws_bytes", "q4_decode_layers_status",
+    "q4_decode_token",
     "Mailbox", "library_path", "q4_atq", "q4_atq_ws_bytes", "q4_atq_status", "q4_pos_advance",
     "AttnBlock", "BlockStack", "q4_decode_block", "q4_decode_blocks", "q4_decode_block_ws_bytes",
     "q4_decode_block_status",
@@ -89,6 +90,9 @@ _SIGS = {
                           ctypes.c_float, _vp, _vp, ctypes.c_size_t, ctypes.c_int, _vp],
                          ctypes.c_int),
     "q4_decode_layers_status": ([_vp, _vp], ctypes.c_int),
+    "q4_decode_token": ([ctypes.POINTER(_Mat), _vp, ctypes.POINTER(_MlpLayer), _i32, _vp,
+                         ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, ctypes.c_int, _vp],
+                        ctypes.c_int),
     "q4_atq_ws_bytes": ([_i32, _i32], ctypes.c_size_t),
     "q4_atq": ([_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _i32,
                 _i32, _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
@@ -386,6 +390,25 @@ def q4_decode_layers(emb: Q4Matrix, tok: torch.Tensor, layers: list, eps: float,
                                  _dev(ws, ws.dtype, None, "ws"), ws.numel() * ws.element_size(),
                                  mode, _stream(stream)))
     return h
+
+
+def q4_decode_token(emb: Q4Matrix, tok: torch.Tensor, layers: list, wn_final: torch.Tensor,
+                    eps: float, h: torch.Tensor, logits: torch.Tensor, ws: torch.Tensor,
+                    mode: int = FIXED, stream=None) -> torch.Tensor:
+    """One greedy decode step in one persistent launch: ``h`` after every
+    layer, ``logits = emb rmsq(h, wn_final)`` and the next token written
+    over ``tok`` (device int32[1]).  ``ws`` as for ``q4_decode_layers``."""
+    if not layers:
+        raise ValueError("at least one layer required")
+    arr = (_MlpLayer * len(layers))(*[L._c for L in layers])
+    _check("q4_decode_token",
+           _lib.q4_decode_token(emb.ref, _dev(tok, torch.int32, 1, "tok"), arr, len(layers),
+                                _dev(wn_final, torch.float32, 2048, "wn_final"), float(eps),
+                                _dev(h, torch.float32, 2048, "h"),
+                                _dev(logits, torch.float32, emb.rows, "logits"),
+                                _dev(ws, ws.dtype, None, "ws"), ws.numel() * ws.element_size(),
+                                mode, _stream(stream)))
+    return tok
 
 
 def q4_decode_layers_status(ws: torch.Tensor, stream=None) -> int:

@@ -17,6 +17,8 @@ the same chain with an attention block in every layer):
                    in the head product's epilogue: 1 + 2 per layer + 2 kernels
   persistent=True  the embedding and every layer in one persistent kernel
                    (q4_decode_layers), then the fused head: 3 kernels
+  one_launch=True  the whole step, the head and its argmax included, in one
+                   persistent kernel (q4_decode_token)
 
 The token lives on the device: argmax writes it where the next step's embed
 reads it, so a step captured once as a graph can be replayed token after
@@ -35,6 +37,7 @@ import torch
 from . import (ATQ_D, BLOCK_MAX_LAYERS, BLOCK_MAX_POS, FIXED, AttnBlock, BlockStack, Graph,
                Mailbox, MlpLayer, Q4Matrix, q4_argmax, q4_argmax_ws_bytes, q4_atq,
                q4_atq_ws_bytes, q4_decode_block_ws_bytes, q4_decode_blocks, q4_decode_layers,
+               q4_decode_token,
                q4_decode_layers_ws_bytes, q4_embed, q4_pos_advance, q4mv, q4mv_add,
                q4mv_argmax_ws_bytes, q4mv_norm, q4mv_norm_argmax, q4mv_norm_swiglu, rmsq, swq)
 
@@ -57,10 +60,12 @@ def _interleave_rows(a: dict, b: dict) -> dict:
 
 class DecodeChain:
     def __init__(self, weights: dict, mode: int = FIXED, layers: int | None = None,
-                 device: str = "cuda", fused: bool = True, persistent: bool = False):
+                 device: str = "cuda", fused: bool = True, persistent: bool = False,
+                 one_launch: bool = False):
         self.mode = mode
-        self.persistent = persistent
-        self.fused = fused or persistent
+        self.persistent = persistent or one_launch
+        self.one_launch = one_launch
+        self.fused = fused or self.persistent
         self.hidden = int(weights["hidden"])
         self.inter = int(weights["inter"])
         self.vocab = int(weights["vocab"])
@@ -97,6 +102,8 @@ class DecodeChain:
         torch.cuda.synchronize()
 
     def kernels_per_token(self) -> int:
+        if self.one_launch:
+            return 1
         if self.persistent:
             return 3
         return 3 + 2 * len(self.layers) if self.fused else 5 + 4 * len(self.layers)
@@ -116,6 +123,10 @@ class DecodeChain:
 
     def enqueue_step(self, stream) -> None:
         """Every kernel of one step, in order, on `stream`."""
+        if self.one_launch:
+            q4_decode_token(self.head, self.tok, self.mlp, self.wn_final, self.eps, self.h,
+                            self.logits, self.stack_ws, mode=self.mode, stream=stream)
+            return
         if self.persistent:
             q4_decode_layers(self.head, self.tok, self.mlp, self.eps, self.h, self.stack_ws,
                              mode=self.mode, stream=stream)

@@ -227,5 +227,118 @@ __device__ __forceinline__ float down_row(const Lds<NP> &S, int lane, const Down
 }
 
 
+// ---------------------------------------------------------------------------
+// The head inside the persistent launch: blocks of 4 rows of the tied
+// embedding matrix (2048 columns), summed with the head kernel's group
+// terms and four-row tree (q4mv_device.h), so the same bits.
+// ---------------------------------------------------------------------------
+constexpr int kHeadR = 4;
+
+struct HeadBlock {
+  u32x4 cw[kHeadR];
+  float sv[kHeadR], bv[kHeadR];
+};
+
+// Rows [4 blk, 4 blk + 4) of the head that exist; a block past the last row
+// reads a zero-byte buffer (no memory access, zeros).
+__device__ __forceinline__ void head_load(const DecodeArgs &A, int blk, int lane, HeadBlock &b) {
+  const long long r0 = (long long)kHeadR * blk;
+  const long long left = (long long)A.vocab - r0;
+  const int nrows = left <= 0 ? 0 : (left < kHeadR ? (int)left : kHeadR);
+  const size_t r = nrows > 0 ? (size_t)r0 : 0;
+  const auto qr = buffer(A.eq + r * 256, nrows * 1024);
+  const auto sr = buffer(A.es + r * 32, nrows * 128);
+  const auto br = buffer(A.eb + r * 32, nrows * 128);
+#pragma unroll
+  for (int j = 0; j < kHeadR; ++j) {
+    b.cw[j] = load_codes(qr, 16u * lane, j * 1024);
+    b.sv[j] = load_f32(sr, 4u * (lane >> 1), j * 128);
+    b.bv[j] = load_f32(br, 4u * (lane >> 1), j * 128);
+  }
+}
+
+// The same rows into the first four rows of a gate/up block (whose
+// registers are free after the last layer's gate/up products), and back.
+__device__ __forceinline__ void head_load_into(const DecodeArgs &A, int blk, int lane,
+                                               GuBlock &a) {
+  HeadBlock b;
+  head_load(A, blk, lane, b);
+#pragma unroll
+  for (int j = 0; j < kHeadR; ++j) {
+    a.cw[j] = b.cw[j];
+    a.sv[j] = b.sv[j];
+    a.bv[j] = b.bv[j];
+  }
+}
+
+__device__ __forceinline__ void head_from(const GuBlock &a, HeadBlock &b) {
+  static_assert(kGuR >= kHeadR, "a head block fits in a gate/up block");
+#pragma unroll
+  for (int j = 0; j < kHeadR; ++j) {
+    b.cw[j] = a.cw[j];
+    b.sv[j] = a.sv[j];
+    b.bv[j] = a.bv[j];
+  }
+}
+
+// Greedy pick over the rows a lane has stored (rows in increasing order).
+struct HeadMax {
+  float value = 0.0f;
+  int index = -1;  // -1: no row yet
+  bool nan = false;
+  __device__ unsigned long long key() const {
+    if (nan) return ops::kNanKey;
+    return index < 0 ? 0ull : ops::argmax_key(value, index);
+  }
+};
+
+// Block blk held in b: the four rows' sums (row j in lanes [16 j, 16 j +
+// 16), as in the head kernel), stored to logits and folded into the lane's
+// running maximum (holder lanes 15, 31, 47, 63).
+template <bool FAST, bool PAIRS>
+__device__ __forceinline__ void head_block(const DecodeArgs &A, const float *xv, float xsv,
+                                           int lane, int blk, const HeadBlock &b, HeadMax &best) {
+  const long long r0 = (long long)kHeadR * blk;
+  if (r0 >= A.vocab) return;  // wave-uniform
+  const int nrows = A.vocab - r0 < kHeadR ? (int)(A.vocab - r0) : kHeadR;
+  const bool odd = lane & 1;
+  float gt[kHeadR];
+#pragma unroll
+  for (int j = 0; j < kHeadR; ++j)
+    gt[j] = group_term<FAST, PAIRS>(b.cw[j], xv, b.sv[j], b.bv[j], xsv, true, odd);
+  const float v = quad_row_sums(gt[0], gt[1], gt[2], gt[3]);
+  const int j = lane >> 4;
+  if ((lane & 15) == 15 && j < nrows) {
+    const int r = (int)r0 + j;
+    A.logits[r] = v;
+    // strictly greater keeps the lowest index of equal values (-0 == +0)
+    const bool gt_ = (v > best.value) || best.index < 0;
+    best.value = gt_ ? v : best.value;
+    best.index = gt_ ? r : best.index;
+    best.nan |= v != v;
+  }
+}
+
+// The wave's head blocks first, first + stride, ... (nblk of them), three
+// in registers at a time: b0 and b1 hold the loads of the first two on
+// entry; each block's loads go out two blocks ahead.  (Two blocks summed
+// together for more independent work per wave measured slower: 0.3694
+// against 0.3664 ms per token.)
+template <bool FAST, bool PAIRS>
+__device__ __forceinline__ void head_rows(const DecodeArgs &A, const float *xv, float xsv,
+                                          int lane, int first, int stride, int nblk,
+                                          HeadBlock &b0, HeadBlock &b1, HeadMax &best) {
+  HeadBlock b2;
+#pragma unroll 1
+  for (int k = 0; k < nblk; k += 3) {
+    head_load(A, first + (k + 2) * stride, lane, b2);
+    head_block<FAST, PAIRS>(A, xv, xsv, lane, first + k * stride, b0, best);
+    head_load(A, first + (k + 3) * stride, lane, b0);
+    if (k + 1 < nblk) head_block<FAST, PAIRS>(A, xv, xsv, lane, first + (k + 1) * stride, b1, best);
+    head_load(A, first + (k + 4) * stride, lane, b1);
+    if (k + 2 < nblk) head_block<FAST, PAIRS>(A, xv, xsv, lane, first + (k + 2) * stride, b2, best);
+  }
+}
+
 }  // namespace decode
 }  // namespace q4

@@ -110,6 +110,12 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
   GuBlock a;
   DownRow<NP> d;
   if (pb < pe) load_gu(A.layer[0], pb, min(kGuPairs, pe - pb), lane, a);
+  // the head (q4_decode_token): blocks of 4 rows gw, gw + stride, ...; the
+  // first is loaded during the last layer, into the registers of the gate/up
+  // block (free by then: there is no next layer)
+  const bool head = A.wf != nullptr;
+  const int head_blocks = (A.vocab + kHeadR - 1) / kHeadR;
+  const int head_nblk = gw < head_blocks ? (head_blocks - gw + stride - 1) / stride : 0;
   // the residual of the wave's row (lane 63): h before the layer
   float res = has_row && lane == kWave - 1 ? embed_value(A, tk, row) : 0.0f;
 
@@ -171,6 +177,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
     const bool poller = t >= kThreads - kPollThreads;
     if (!poller && l + 1 < A.nlayers && pb < pe)
       load_gu(A.layer[l + 1], pb, min(kGuPairs, pe - pb), lane, a);
+    if (!poller && l + 1 == A.nlayers && head) head_load_into(A, gw, lane, a);
     issue_order();
 
     // ---- stage B: m and its group sums into LDS; h = h + down m
@@ -228,9 +235,11 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
         }
       }
       if (large) S.flag[1] = 1u;
-      // this wave's gate/up rows of the next layer, now that its polls are done
+      // this wave's gate/up rows of the next layer (or its first head
+      // blocks after the last layer), now that its polls are done
       if (l + 1 < A.nlayers && pb < pe)
         load_gu(A.layer[l + 1], pb, min(kGuPairs, pe - pb), lane, a);
+      if (l + 1 == A.nlayers && head) head_load_into(A, gw, lane, a);
       issue_order();
     }
     __syncthreads();
@@ -262,17 +271,93 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
                             : down_row<NP, FAST, false>(S, lane, d);
       if (lane == kWave - 1) {
         res = res + v;
-        if (l + 1 < A.nlayers)
+        if (l + 1 < A.nlayers || head)
 #pragma unroll
           for (int c = 0; c < kDecodeCopies; ++c)
             store_tagged(A.hq + ((size_t)(l & 1) * kDecodeCopies + c) * kCols + row, res,
                          tag0 + 2 * l + 2);
-        else
-          A.h[row] = res;
+        if (l + 1 == A.nlayers) A.h[row] = res;
       }
     }
     // the next stage A writes S.x (all reads of it above are done)
     __syncthreads();
+  }
+
+  if (head) {
+    // ---- the head: x = rmsq(h, wf) over the workgroup, as a layer's
+    // stage A; logits = emb x, every wave over its blocks of 4 rows
+    const int L = A.nlayers;
+    bool ok = true;
+    float h8[8] = {}, w8[8] = {};
+    if (mine) {
+      const float4 *wp = reinterpret_cast<const float4 *>(A.wf + 8 * t);
+      const float4 w0 = wp[0], w1 = wp[1];
+      w8[0] = w0.x; w8[1] = w0.y; w8[2] = w0.z; w8[3] = w0.w;
+      w8[4] = w1.x; w8[5] = w1.y; w8[6] = w1.z; w8[7] = w1.w;
+      ok = poll_tagged<8>(A.hq + ((size_t)((L - 1) & 1) * kDecodeCopies + copy) * kCols + 8 * t,
+                          tag0 + 2 * L, h8, err, A.spin_ticks);
+    }
+    // the second block's loads, after the wait for h (a poll issued behind
+    // them would wait for them too)
+    HeadBlock hb0, hb1;
+    head_from(a, hb0);
+    issue_order();
+    head_load(A, gw + stride, lane, hb1);
+    const int rq = workgroup_rmsq(S, h8, w8, A.eps, ok);
+    if (rq < 0) return;
+    HeadMax best;
+    {
+      float xv[32];
+      const float xsv = load_rmsq_x(S, lane, rq != 0, xv);
+      if (rq != 0)
+        head_rows<FAST, true>(A, xv, xsv, lane, gw, stride, head_nblk, hb0, hb1, best);
+      else
+        head_rows<FAST, false>(A, xv, xsv, lane, gw, stride, head_nblk, hb0, hb1, best);
+    }
+    // the workgroup's best key (holder lanes 15, 31, 47, 63 of each wave;
+    // other lanes hold key 0) to workgroup 0 as two tagged words
+    __shared__ unsigned long long wkey[kWaves];
+    unsigned long long k = best.key();
+    unsigned long long o = __shfl_xor(k, 16);
+    k = o > k ? o : k;
+    o = __shfl_xor(k, 32);
+    k = o > k ? o : k;
+    if (lane == kWave - 1) wkey[wave] = k;
+    __syncthreads();
+    const uint32_t ktag = call + 1;  // never 0, the workspace's initial contents
+    if (t == 0) {
+      k = wkey[0];
+#pragma unroll
+      for (int i = 1; i < kWaves; ++i) k = wkey[i] > k ? wkey[i] : k;
+      store_tagged(A.kq + 2 * wg, __uint_as_float((uint32_t)(k >> 32)), ktag);
+      store_tagged(A.kq + 2 * wg + 1, __uint_as_float((uint32_t)k), ktag);
+    }
+    if (wg == 0) {
+      // every workgroup's key; the largest names the token (the lowest
+      // index of the largest logit, -1 if any logit is NaN)
+      unsigned long long best_key = 0ull;
+      ok = true;
+      for (int i = t; i < nwg; i += kThreads) {
+        float kv[2];
+        ok &= poll_tagged<2>(A.kq + 2 * i, ktag, kv, err, A.spin_ticks);
+        const unsigned long long c =
+            ((unsigned long long)__float_as_uint(kv[0]) << 32) | __float_as_uint(kv[1]);
+        best_key = c > best_key ? c : best_key;
+      }
+#pragma unroll
+      for (int m = 1; m < kWave; m *= 2) {
+        o = __shfl_xor(best_key, m);
+        best_key = o > best_key ? o : best_key;
+      }
+      __syncthreads();  // wkey is free again (every reader is past it)
+      if (lane == 0) wkey[wave] = best_key;
+      if (!__syncthreads_and(ok)) return;
+      if (t == 0) {
+#pragma unroll
+        for (int i = 1; i < kWaves; ++i) best_key = wkey[i] > best_key ? wkey[i] : best_key;
+        *A.tok_out = ops::argmax_index(best_key);
+      }
+    }
   }
   if (t == 0) store_word(A.ctl + wg, call + 1);
 }

@@ -459,9 +459,16 @@ int q4_embed(const q4_mat *w, const int32_t *tok, float *e, void *stream) {
 
 size_t q4_decode_layers_ws_bytes(void) { return q4::kDecodeWsBytes; }
 
-int q4_decode_layers(const q4_mat *emb, const int32_t *tok, const q4_mlp_layer *layers,
-                     int32_t nlayers, float eps, float *h, void *ws, size_t ws_bytes, int mode,
-                     void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of q4_decode_layers and q4_decode_token and the kernel's arguments;
+// `outs` are the arrays the call writes (h, ws and, for the token, logits):
+// none may overlap an input.
+int decode_args(const q4_mat *emb, const int32_t *tok, const q4_mlp_layer *layers,
+                int32_t nlayers, float eps, float *h, void *ws, size_t ws_bytes, int mode,
+                const void *const *outs, const size_t *outb, int nouts, q4::DecodeArgs *a) {
   if (mode != Q4_FIXED && mode != Q4_FAST) return Q4_EINVAL;
   int rc = check_mat(emb);
   if (rc != Q4_OK) return rc;
@@ -472,42 +479,78 @@ int q4_decode_layers(const q4_mat *emb, const int32_t *tok, const q4_mlp_layer *
   const int32_t inter = layers[0].down.cols;
   if (inter < 2048 || inter % 2048 != 0 || inter > q4::kDecodeMaxInter) return Q4_EINVAL;
   const size_t hb = sizeof(float) * 2048;
-  // h and ws are written: they may overlap nothing else
-  const void *outs[2] = {h, ws};
-  const size_t outb[2] = {hb, q4::kDecodeWsBytes};
-  if (overlap(h, hb, ws, q4::kDecodeWsBytes)) return Q4_EINVAL;
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < nouts; ++i) {
+    for (int k = i + 1; k < nouts; ++k)
+      if (overlap(outs[i], outb[i], outs[k], outb[k])) return Q4_EINVAL;
     if (overlaps_mat(outs[i], outb[i], emb) || overlap(outs[i], outb[i], tok, 4)) return Q4_EINVAL;
-  q4::DecodeArgs a;
-  memset(&a, 0, sizeof(a));
+  }
+  memset(a, 0, sizeof(*a));
   for (int l = 0; l < nlayers; ++l) {
     const q4_mlp_layer &L = layers[l];
     if (check_mat(&L.gate_up) != Q4_OK || check_mat(&L.down) != Q4_OK) return Q4_EINVAL;
     if (L.gate_up.cols != 2048 || L.gate_up.rows != 2 * inter) return Q4_EINVAL;
     if (L.down.rows != 2048 || L.down.cols != inter) return Q4_EINVAL;
     if (!L.wn || !aligned(L.wn, 16)) return Q4_EINVAL;
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < nouts; ++i)
       if (overlaps_mat(outs[i], outb[i], &L.gate_up) || overlaps_mat(outs[i], outb[i], &L.down) ||
           overlap(outs[i], outb[i], L.wn, hb))
         return Q4_EINVAL;
-    a.layer[l] = q4::DecodeLayer{L.gate_up.q, L.gate_up.s, L.gate_up.b, L.wn,
-                                 L.down.q,    L.down.s,    L.down.b};
+    a->layer[l] = q4::DecodeLayer{L.gate_up.q, L.gate_up.s, L.gate_up.b, L.wn,
+                                  L.down.q,    L.down.s,    L.down.b};
   }
-  a.nlayers = nlayers;
-  a.inter = inter;
-  a.eq = emb->q;
-  a.es = emb->s;
-  a.eb = emb->b;
-  a.vocab = emb->rows;
-  a.tok = tok;
-  a.h = h;
+  a->nlayers = nlayers;
+  a->inter = inter;
+  a->eq = emb->q;
+  a->es = emb->s;
+  a->eb = emb->b;
+  a->vocab = emb->rows;
+  a->tok = tok;
+  a->h = h;
   char *w = static_cast<char *>(ws);
-  a.hq = reinterpret_cast<uint64_t *>(w + q4::kDecodeHqOffset);
-  a.mq = reinterpret_cast<uint64_t *>(w + q4::kDecodeMqOffset);
-  a.ctl = reinterpret_cast<uint32_t *>(w + q4::kDecodeCtlOffset);
-  a.eps = eps;
-  if (wait_ticks(&a.spin_ticks) != Q4_OK) return Q4_EHIP;
+  a->hq = reinterpret_cast<uint64_t *>(w + q4::kDecodeHqOffset);
+  a->mq = reinterpret_cast<uint64_t *>(w + q4::kDecodeMqOffset);
+  a->ctl = reinterpret_cast<uint32_t *>(w + q4::kDecodeCtlOffset);
+  a->kq = reinterpret_cast<uint64_t *>(w + q4::kDecodeKqOffset);
+  a->eps = eps;
+  if (wait_ticks(&a->spin_ticks) != Q4_OK) return Q4_EHIP;
   if (q4::decode_layers_grid(mode, inter) < 1) return Q4_EINVAL;  // too few compute units
+  return Q4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q4_decode_layers(const q4_mat *emb, const int32_t *tok, const q4_mlp_layer *layers,
+                     int32_t nlayers, float eps, float *h, void *ws, size_t ws_bytes, int mode,
+                     void *stream) {
+  const void *outs[2] = {h, ws};
+  const size_t outb[2] = {sizeof(float) * 2048, q4::kDecodeWsBytes};
+  q4::DecodeArgs a;
+  const int rc = decode_args(emb, tok, layers, nlayers, eps, h, ws, ws_bytes, mode, outs, outb, 2,
+                             &a);
+  if (rc != Q4_OK) return rc;
+  return hip_status(q4::launch_decode_layers(a, mode, static_cast<hipStream_t>(stream)));
+}
+
+int q4_decode_token(const q4_mat *emb, int32_t *tok, const q4_mlp_layer *layers, int32_t nlayers,
+                    const float *wn_final, float eps, float *h, float *logits, void *ws,
+                    size_t ws_bytes, int mode, void *stream) {
+  if (!wn_final || !aligned(wn_final, 16) || !logits || !aligned(logits, 4)) return Q4_EINVAL;
+  if (check_mat(emb) != Q4_OK) return Q4_EINVAL;
+  const void *outs[3] = {h, ws, logits};
+  const size_t outb[3] = {sizeof(float) * 2048, q4::kDecodeWsBytes,
+                          sizeof(float) * (size_t)emb->rows};
+  q4::DecodeArgs a;
+  const int rc = decode_args(emb, tok, layers, nlayers, eps, h, ws, ws_bytes, mode, outs, outb, 3,
+                             &a);
+  if (rc != Q4_OK) return rc;
+  // wn_final is read, the outputs must not overlap it
+  for (int i = 0; i < 3; ++i)
+    if (overlap(outs[i], outb[i], wn_final, sizeof(float) * 2048)) return Q4_EINVAL;
+  a.wf = wn_final;
+  a.logits = logits;
+  a.tok_out = tok;
   return hip_status(q4::launch_decode_layers(a, mode, static_cast<hipStream_t>(stream)));
 }
 

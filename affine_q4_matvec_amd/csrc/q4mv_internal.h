@@ -120,10 +120,19 @@ struct DecodeArgs {
   uint32_t *ctl;        // workspace: call counters and error word
   float eps;
   long long spin_ticks; // bound of one wait in wall-clock ticks
+  // The head, when wf is not null (q4_decode_token): logits = emb
+  // rmsq(h, wf), *tok_out = argmax(logits), with the workgroups' best keys
+  // handed to workgroup 0 through tagged words in kq.
+  const float *wf;      // [2048] final norm weights, or nullptr
+  float *logits;        // [vocab]
+  int32_t *tok_out;     // [1] the next token (may be tok)
+  uint64_t *kq;         // workspace: [max groups][2] tagged argmax keys
 };
 // Workspace layout (bytes): tagged h and tagged m of the widest inter, each
-// twice (by layer parity) in kDecodeCopies copies, then the control words: one call counter per workgroup (at most
-// kDecodeMaxGroups) and the error word on a 128-byte line of its own.
+// twice (by layer parity) in kDecodeCopies copies; two tagged words per
+// workgroup for the head's argmax keys; then the control words: one call
+// counter per workgroup (at most kDecodeMaxGroups) and the error word on a
+// 128-byte line of its own (32 words before the end).
 constexpr int kDecodeMaxInter = 8192;
 constexpr int kDecodeMaxGroups = 1024;
 // Each tagged value is written in kDecodeCopies copies; workgroup i reads
@@ -132,8 +141,9 @@ constexpr int kDecodeMaxGroups = 1024;
 constexpr int kDecodeCopies = 8;
 constexpr size_t kDecodeHqOffset = 0;
 constexpr size_t kDecodeMqOffset = 2 * kDecodeCopies * 8 * 2048;
-constexpr size_t kDecodeCtlOffset =
+constexpr size_t kDecodeKqOffset =
     kDecodeMqOffset + 2 * kDecodeCopies * 8 * (size_t)kDecodeMaxInter;
+constexpr size_t kDecodeCtlOffset = kDecodeKqOffset + 2 * 8 * (size_t)kDecodeMaxGroups;
 constexpr int kDecodeErrorWord = kDecodeMaxGroups + 32;
 constexpr size_t kDecodeWsBytes = kDecodeCtlOffset + 4 * (kDecodeErrorWord + 32);
 // Workgroups of the persistent launch for this mode and width (0: none fit).

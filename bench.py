@@ -23,8 +23,11 @@ HIP graph, in ms per token over 200 tokens, for two engines: the fused
 per-stage kernels (2 per layer) and the persistent layer kernel (one launch
 for all layers); the attention step at positions 204 and 4095 of a 4096
 cache; the chain with an attention block in every layer (200 tokens from
-position 0; fused stages, and one persistent launch per layer); and the
-CPU oracle timed on the host's cores on the head workload.
+position 0, and 200 at the end of a 4096-position cache; fused stages, and
+every layer in one persistent launch), its tokens checked against the
+oracle's golden files; the kernel designs the pages compare on the head;
+the 4096 x 2048 product and the 169-product set; and the CPU oracle timed
+on the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -403,8 +406,9 @@ def run_chain(args, q4, torch, synth):
     mode = q4.FAST if args.mode == "fast" else q4.FIXED
     tok0 = chain_tok0(args.seed, synth)
     engines, bpt = {}, None
-    for name in ("fused", "persistent"):
-        chain = DecodeChain(w, mode=mode, persistent=(name == "persistent"))
+    for name in ("fused", "persistent", "one_launch"):
+        chain = DecodeChain(w, mode=mode, persistent=(name == "persistent"),
+                            one_launch=(name == "one_launch"))
         engines[name], bpt = time_chain(args, q4, torch, chain, tok0)
         log("chain %s: %s" % (name, engines[name]))
         del chain
@@ -548,7 +552,8 @@ def run_attn_chain(args, q4, torch, synth):
         r, tokens = time_attn_chain(args, q4, torch, chain, tok0, steps)
         if ref is not None:
             n = min(len(ref["tokens"]), len(tokens))
-            r["tokens_match_oracle_golden_prefix"] = bool(ref["tokens"][:n] == tokens[:n])
+            r["tokens_match_oracle_golden"] = bool(ref["tokens"][:n] == tokens[:n])
+            r["tokens_checked"] = n
         engines[name] = r
         log("attention chain %s: %s" % (name, r))
         del chain
@@ -569,6 +574,13 @@ def run_attn_chain(args, q4, torch, synth):
         log("attention chain %s, positions %d..%d: %s" % (name, pos0, long_pos - 1, r))
         del chain
         torch.cuda.synchronize()
+    long_ref = golden("attn_chain_long", args.seed) if mode == q4.FIXED else None
+    if long_ref is not None and long_ref["pos0"] == pos0 and long_ref["max_pos"] == long_pos:
+        for name in long_engines:
+            n = min(len(long_ref["tokens"]), len(long_tokens[name]))
+            long_engines[name]["tokens_match_oracle_golden"] = (
+                long_ref["tokens"][:n] == long_tokens[name][:n])
+            long_engines[name]["tokens_checked"] = n
     long_best = min(long_engines, key=lambda k: long_engines[k]["ms_per_token_gpu"])
     return {
         "tokens": steps, "layers": len(w["layers"]), "positions": "0..%d" % (steps - 1),

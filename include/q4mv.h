@@ -274,6 +274,34 @@ int q4_decode_layers(const q4_mat *emb, const int32_t *tok, const q4_mlp_layer *
                      void *stream);
 
 /*
+ * A whole greedy decode step in one persistent launch ([P1] Change and
+ * Verification: a decode token as one command buffer with one wait, greedy
+ * token ids): q4_decode_layers, then the final RMS norm, the head product
+ * over the same tied matrix and its argmax, with the bits of
+ *   q4_decode_layers(emb, tok, layers, nlayers, eps, h, ...);
+ *   q4mv_norm_argmax(emb, h, wn_final, eps, logits, tok, ...)
+ * The token is read at the start and the next one written over it at the
+ * end, so a graph of this one call replays token after token.  After the
+ * last layer h is handed to every workgroup as between layers; each forms
+ * rmsq(h, wn_final) once and every wave sums its blocks of 4 head rows (the
+ * first loaded during the last layer); workgroup 0 gathers the workgroups'
+ * best (value, index) keys through tagged words and writes the token.
+ *   emb     : as for q4_decode_layers; also the head (vocab = emb->rows).
+ *   tok     : device int32[1], read, then overwritten with the next token
+ *             (-1 when a logit is NaN).
+ *   wn_final: device float[2048], 16-byte aligned.
+ *   h       : device float[2048]: the hidden state after the last layer.
+ *   logits  : device float[emb->rows].
+ *   ws      : as for q4_decode_layers (the same size and status call).
+ * h, logits and ws must overlap each other and no input.  Errors and
+ * bounded waits as for q4_decode_layers; a wait that runs out leaves the
+ * token unwritten.
+ */
+int q4_decode_token(const q4_mat *emb, int32_t *tok, const q4_mlp_layer *layers, int32_t nlayers,
+                    const float *wn_final, float eps, float *h, float *logits, void *ws,
+                    size_t ws_bytes, int mode, void *stream);
+
+/*
  * Waits for `stream` on the host, then returns Q4_ETIMEOUT if a wait of a
  * q4_decode_layers call using `ws` ran out since the workspace was last
  * cleared (and clears the whole workspace), else Q4_OK.  Q4_ESTATE during

@@ -171,14 +171,15 @@ def oracle_chain(w, tok, steps, layers=None):
     return toks, logits
 
 
-@pytest.mark.parametrize("persistent", [False, True])
+@pytest.mark.parametrize("persistent", [False, True, "one_launch"])
 def test_chain_two_layers_every_step_bit_exact(persistent):
     DecodeChain = chain_cls()
     w = synth.chain_weights(seed=7, layers=2, vocab=8192)
     want_toks, want_logits = oracle_chain(w, w["tok0"], 12)
     assert len(set(want_toks)) > 3
     for use_graph in (False, True):
-        chain = DecodeChain(w, persistent=persistent)
+        chain = DecodeChain(w, persistent=persistent is True,
+                            one_launch=persistent == "one_launch")
         got_logits = []
         toks = chain.run(w["tok0"], 12, torch.cuda.Stream(), use_graph=use_graph,
                          on_step=lambda i, c: got_logits.append(host(c.logits)))
@@ -223,8 +224,8 @@ def test_chain_full_depth_first_steps_bit_exact():
         assert_bits_equal(got[i], want_logits[i], "full chain logits step %d" % i)
 
 
-@pytest.mark.parametrize("persistent", [False, True])
-def test_chain_200_tokens_against_oracle_golden(persistent):
+@pytest.mark.parametrize("engine", ["fused", "persistent", "one_launch"])
+def test_chain_200_tokens_against_oracle_golden(engine):
     """200 greedy steps of the 24-layer chain in one captured graph; every
     token and every step's logits hash equal the oracle's (tests/golden,
     written by tests/golden/make_chain_golden.py from the oracle only)."""
@@ -232,7 +233,7 @@ def test_chain_200_tokens_against_oracle_golden(persistent):
     ref = json.load(open(GOLDEN))
     w = synth.chain_weights(seed=ref["seed"])
     assert w["tok0"] == ref["tok0"]
-    chain = DecodeChain(w, persistent=persistent)
+    chain = DecodeChain(w, persistent=engine == "persistent", one_launch=engine == "one_launch")
     hashes = []
     toks = chain.run(ref["tok0"], len(ref["tokens"]), torch.cuda.Stream(),
                      on_step=lambda i, c: hashes.append(oracle.fnv1a32(host(c.logits))))
@@ -259,3 +260,44 @@ def test_two_chains_interleaved_equal_solo_runs():
         got_a.append(ta)
         got_b.append(tb)
     assert got_a == solo_a and got_b == solo_b
+
+
+@pytest.mark.parametrize("mailbox", [False, True])
+def test_queue_wait_trace_reports_each_wait(capfd, mailbox):
+    """With Q4MV_TRACE=1 each q4mv_wait prints the products it waited for,
+    their GPU time and the wall time since the first of them was launched
+    ('Array.q4go/Array.q4wait queue Metal Q4 products ...' (#1437), Change:
+    the trace of every wait); the products' results are unchanged."""
+    import re
+    q4 = lib()
+    os.environ["Q4MV_TRACE"] = "1"
+    try:
+        queue = q4.Queue(stream=torch.cuda.Stream())
+    finally:
+        del os.environ["Q4MV_TRACE"]
+    if mailbox:
+        queue.set_wait(q4.WAIT_MAILBOX)
+    m = synth.small_product(seed=5, rows=4099, cols=2048, name="tr")
+    xs = oracle.group_sums(m["x"])
+    W = q4.Q4Matrix.from_host(m)
+    xd, xsd = dev(m["x"]), dev(xs)
+    want = oracle.q4mv(m, m["x"], xs, NTHREADS)
+    ys = [torch.empty(4099, device="cuda") for _ in range(6)]
+    capfd.readouterr()
+    for y in ys[:3]:  # stage 1: three products
+        queue.q4mv_queue(W, xd, xsd, y)
+    queue.q4_stage()
+    for y in ys[3:5]:  # stage 2: two more, then one wait for all five
+        queue.q4mv_queue(W, xd, xsd, y)
+    queue.q4mv_wait()
+    queue.q4mv_queue(W, xd, xsd, ys[5])  # a second wait for one product
+    queue.q4mv_wait()
+    err = capfd.readouterr().err
+    lines = re.findall(r"q4mv_wait: (\d+) products, gpu ([0-9.]+) ms, wall ([0-9.]+) ms", err)
+    assert [int(n) for n, _, _ in lines] == [5, 1], err
+    for _, gpu, wall in lines:
+        assert 0.0 < float(gpu) < 1000.0 and 0.0 < float(wall) < 10000.0
+        assert float(wall) >= 0.5 * float(gpu)  # the wall time spans the GPU work
+    for y in ys:
+        assert_bits_equal(host(y), want, "traced queue product")
+    queue.close()

@@ -198,3 +198,113 @@ def test_decode_layers_wait_timeout_is_reported_and_cleared():
     assert int(np.abs(host(ws)).max()) == 0
     got, _ = run_layers(q4, emb, layers[:2], {**w, "layers": w["layers"][:2]}, 3, ws=ws)
     assert_bits_equal(got, oracle.chain_hidden(w, 3, NTHREADS, layers=2), "after a timeout")
+
+
+@pytest.mark.parametrize("inter,nlayers,vocab", [(2048, 1, 3001), (6144, 2, 20003), (8192, 1, 7),
+                                                 (4096, 3, 9000)])
+def test_decode_token_matches_separate_calls_and_oracle(inter, nlayers, vocab):
+    """q4_decode_token (the layers, the final norm, the head and its argmax
+    in one launch) against q4_decode_layers + q4mv_norm_argmax and the
+    oracle: h, every logit and the token bit for bit, over several steps
+    on one workspace (the token fed back in place); vocab sizes with a
+    ragged last block, fewer blocks than waves, and several per wave."""
+    q4 = lib()
+    w = synth.chain_weights(seed=60 + nlayers, layers=nlayers, inter=inter, vocab=vocab)
+    emb = q4.Q4Matrix.from_host(w["head"])
+    layers = mlp_layers(q4, w)
+    wf = dev(w["wn_final"])
+    tok = torch.tensor([int(w["tok0"])], dtype=torch.int32, device="cuda")
+    h = torch.full((2048,), 7.0, device="cuda")
+    logits = torch.full((vocab,), 7.0, device="cuda")
+    ws = new_ws(q4)
+    t_host = int(w["tok0"])
+    for step in range(3):
+        print("decode_token inter=%d layers=%d vocab=%d step %d" % (inter, nlayers, vocab, step),
+              flush=True)
+        want_logits, want_tok = oracle.chain_step(w, t_host, NTHREADS)
+        q4.q4_decode_token(emb, tok, layers, wf, w["eps"], h, logits, ws)
+        assert q4.q4_decode_layers_status(ws) == q4.Q4_OK
+        assert_bits_equal(host(h), oracle.chain_hidden(w, t_host, NTHREADS), "h step %d" % step)
+        assert_bits_equal(host(logits), want_logits, "logits step %d" % step)
+        assert int(host(tok)[0]) == want_tok, step
+        # the separate calls give the same
+        t2 = torch.tensor([t_host], dtype=torch.int32, device="cuda")
+        h2 = torch.empty(2048, device="cuda")
+        y2 = torch.empty(vocab, device="cuda")
+        q4.q4_decode_layers(emb, t2, layers, w["eps"], h2, new_ws(q4))
+        q4.q4mv_norm_argmax(emb, h2, wf, w["eps"], y2, t2)
+        torch.cuda.synchronize()
+        assert_bits_equal(host(y2), host(logits), "separate calls step %d" % step)
+        assert int(host(t2)[0]) == want_tok
+        t_host = want_tok
+
+
+def test_decode_token_nan_logits_give_minus_one():
+    q4 = lib()
+    w = synth.chain_weights(seed=64, layers=1, inter=2048, vocab=500)
+    emb = q4.Q4Matrix.from_host(w["head"])
+    tok = torch.tensor([500], dtype=torch.int32, device="cuda")  # outside: h is NaN
+    h = torch.empty(2048, device="cuda")
+    logits = torch.empty(500, device="cuda")
+    ws = new_ws(q4)
+    q4.q4_decode_token(emb, tok, mlp_layers(q4, w), dev(w["wn_final"]), w["eps"], h, logits, ws)
+    assert q4.q4_decode_layers_status(ws) == q4.Q4_OK
+    assert np.all(np.isnan(host(logits)))
+    assert int(host(tok)[0]) == -1
+
+
+def test_decode_token_wait_timeout_is_reported_and_cleared():
+    """No waiting allowed: the launch leaves early, the status reports it
+    and clears the workspace, and the token is left as it was."""
+    q4 = lib()
+    w = synth.chain_weights(seed=65, layers=6, vocab=1000)
+    emb = q4.Q4Matrix.from_host(w["head"])
+    layers = mlp_layers(q4, w)
+    tok = torch.tensor([3], dtype=torch.int32, device="cuda")
+    h = torch.empty(2048, device="cuda")
+    logits = torch.empty(1000, device="cuda")
+    ws = new_ws(q4)
+    os.environ["Q4_DECODE_TIMEOUT_MS"] = "-1"
+    try:
+        q4.q4_decode_token(emb, tok, layers, dev(w["wn_final"]), w["eps"], h, logits, ws)
+    finally:
+        del os.environ["Q4_DECODE_TIMEOUT_MS"]
+    assert q4.q4_decode_layers_status(ws) == q4.Q4_ETIMEOUT
+    assert int(host(tok)[0]) == 3
+    assert int(np.abs(host(ws)).max()) == 0
+    q4.q4_decode_token(emb, tok, layers[:1], dev(w["wn_final"]), w["eps"], h, logits, ws)
+    assert q4.q4_decode_layers_status(ws) == q4.Q4_OK
+    _, want = oracle.chain_step({**w, "layers": w["layers"][:1]}, 3, NTHREADS)
+    assert int(host(tok)[0]) == want
+
+
+def test_decode_token_planted_maxima_every_wave_position():
+    """The largest logit placed in rows of the first wave of a workgroup
+    (block 5: rows 20..23) and of the last wave (block 2047: rows 8188..8191),
+    then in two identical rows (a tie: the lower index wins)."""
+    q4 = lib()
+    w = synth.chain_weights(seed=66, layers=1, inter=2048, vocab=9000)
+    tok = 3
+    h = oracle.chain_hidden(w, tok, NTHREADS)
+    _, us = oracle.rmsq(h, w["wn_final"], w["eps"])
+    lift = np.where(us >= 0, np.float32(64.0), np.float32(-64.0))
+    layers = mlp_layers(q4, w)
+    wf = dev(w["wn_final"])
+    for rows, want in (([21], 21), ([8189], 8189), ([8190, 22], 22)):
+        head = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in w["head"].items()}
+        for r in rows:
+            head["q"][r] = head["q"][rows[0]]
+            head["s"][r] = head["s"][rows[0]]
+            head["b"][r] = lift
+        wm = {**w, "head": head}
+        want_logits, want_tok = oracle.chain_step(wm, tok, NTHREADS)
+        assert want_tok == want
+        emb = q4.Q4Matrix.from_host(head)
+        t = torch.tensor([tok], dtype=torch.int32, device="cuda")
+        hd = torch.empty(2048, device="cuda")
+        logits = torch.empty(9000, device="cuda")
+        ws = new_ws(q4)
+        q4.q4_decode_token(emb, t, layers, wf, w["eps"], hd, logits, ws)
+        assert q4.q4_decode_layers_status(ws) == q4.Q4_OK
+        assert_bits_equal(host(logits), want_logits, "planted %s" % rows)
+        assert int(host(t)[0]) == want, rows
