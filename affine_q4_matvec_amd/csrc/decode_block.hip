@@ -631,34 +631,77 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
       }
 
       // ---- stage B: h = h + down m ---------------------------------------------
+      // chunk c = 8 consecutive values of m; the last four waves poll them
+      // (poller p: chunks p, p + 256, ...) and write them to LDS scaled for
+      // the pair decode.  A wave's loads complete in issue order for its
+      // wait counter, so a poll behind a fresh prefetch would wait for it:
+      // the first four waves (which poll h in the next stage Q) load their
+      // next Q rows now, the pollers once their polls are done.
       constexpr int kChunks = NP * kCols / 8;
-      float xm[2][8] = {};
+      constexpr int kPollThreads = 256;
+      constexpr int kPerPoller = kChunks / kPollThreads;
+      static_assert(kChunks % kPollThreads == 0, "whole rounds of chunks");
+      const bool poller = t >= kThreads - kPollThreads;
+      if (!poller && l + 1 < A.nlayers && qb < qe)
+        load_qrows(layer_at(A, l + 1), qb, qe - qb, lane, qa);
+      issue_order();
+      if (t == 0) S.flag[0] = S.flag[1] = 0u;
       __syncthreads();  // every wave of the workgroup is done with stage A
-      // (one chunk at a time: polling both in the same rounds doubles the
-      // polled traffic while the wait lasts, which measured slower)
-      ok = true;
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const int c = t + rr * kThreads;
-        if (c < kChunks)
-          ok &= poll_tagged<8>(A.mq + (size_t)copy * kDecodeMaxInter + 8 * c, tag + 4, xm[rr], err,
-                               A.spin_ticks);
-      }
-      if (!__syncthreads_and(ok)) return;
-      // group sums: T over each chunk, then over 8 chunks by a butterfly
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        const int c = t + rr * kThreads;
-        if (rr * kThreads < kChunks) {  // uniform per round
-          float gs = c < kChunks ? ops::tree8(xm[rr]) : 0.0f;
+      const uint64_t *mcopy = A.mq + (size_t)copy * kDecodeMaxInter;
+      if (poller) {
+        const int p = t - (kThreads - kPollThreads);
+        bool large = false;
+        const float scale = 1.0f / fp8_unit();
+        // one chunk at a time: polling several in the same rounds multiplies
+        // the polled traffic while the wait lasts
+#pragma unroll 1
+        for (int r = 0; r < kPerPoller; ++r) {
+          const int c = p + r * kPollThreads;
+          float xm[8];
+          if (!poll_tagged<8>(mcopy + 8 * c, tag + 4, xm, err, A.spin_ticks)) {
+            S.flag[0] = 1u;
+            break;
+          }
+          // group sums: T over each chunk, then over 8 chunks by a butterfly
+          float gs = ops::tree8(xm);
           gs = gs + __shfl_xor(gs, 1);
           gs = gs + __shfl_xor(gs, 2);
           gs = gs + __shfl_xor(gs, 4);
-          if (c < kChunks && (c & 7) == 0) S.xs[c >> 3] = gs;
+          if ((c & 7) == 0) S.xs[c >> 3] = gs;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) large |= !(__builtin_fabsf(xm[k]) < 0x1p118f);
+          float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * c + 4 * (c >> 2));
+          dst[0] = make_float4(xm[0] * scale, xm[1] * scale, xm[2] * scale, xm[3] * scale);
+          dst[1] = make_float4(xm[4] * scale, xm[5] * scale, xm[6] * scale, xm[7] * scale);
         }
+        if (large) S.flag[1] = 1u;
+        if (l + 1 < A.nlayers && qb < qe) load_qrows(layer_at(A, l + 1), qb, qe - qb, lane, qa);
+        issue_order();
       }
-      const bool pairs = stage_rows_input<NP>(S, xm, kChunks);
       __syncthreads();
+      if (S.flag[0] != 0u) return;
+      const bool pairs = S.flag[1] == 0u;
+      if (!pairs) {
+        // some |m| >= 2^118: the raw values for the plain decode, read again
+        // from the tagged words (they keep this layer's tag until every
+        // workgroup has done this layer's down rows)
+        if (poller) {
+          const int p = t - (kThreads - kPollThreads);
+#pragma unroll 1
+          for (int r = 0; r < kPerPoller; ++r) {
+            const int c = p + r * kPollThreads;
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              v[k] = __uint_as_float((uint32_t)__hip_atomic_load(
+                  mcopy + 8 * c + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * c + 4 * (c >> 2));
+            dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+            dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+          }
+        }
+        __syncthreads();
+      }
       if (has_row) {
         const float v =
             pairs ? down_row<NP, FAST, true>(S, lane, d) : down_row<NP, FAST, false>(S, lane, d);
@@ -674,8 +717,6 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
         }
       }
     }
-    // the next layer's [Q; gate; K; V] rows, in flight during the wait for h
-    if (l + 1 < A.nlayers && qb < qe) load_qrows(layer_at(A, l + 1), qb, qe - qb, lane, qa);
   }  // layers
   __syncthreads();
   if (threadIdx.x == 0) store_word(A.ctl + wg, call + 1);

@@ -370,10 +370,9 @@ def time_chain(args, q4, torch, chain, tok0):
     stream.synchronize()
     gpu_ms = e0.elapsed_time(e1) / args.chain_tokens
     last = int(chain.tok.cpu().numpy()[0])
-    golden = os.path.join(ROOT, "tests", "golden", "chain_seed%d.json" % args.seed)
     match = None
-    if os.path.exists(golden):
-        ref = json.load(open(golden))
+    ref = golden("chain", args.seed)
+    if ref is not None:
         n = min(len(ref["tokens"]), len(tokens))
         match = bool(ref["tokens"][:n] == tokens[:n])
     bpt = chain.bytes_per_token()
@@ -544,8 +543,7 @@ def run_attn_chain(args, q4, torch, synth):
     mode = q4.FAST if args.mode == "fast" else q4.FIXED
     tok0 = int(w["tok0"])
     steps = min(args.chain_tokens, int(w["max_pos"]))
-    golden = os.path.join(ROOT, "tests", "golden", "attn_chain_seed%d.json" % args.seed)
-    ref = json.load(open(golden)) if os.path.exists(golden) and mode == q4.FIXED else None
+    ref = golden("attn_chain", args.seed) if mode == q4.FIXED else None
     engines = {}
     for name in ("fused", "persistent"):
         chain = AttnDecodeChain(w, mode=mode, persistent=(name == "persistent"))
