@@ -26,6 +26,15 @@
 // fences costs about 10 us, a fence-free one about 4 us; a dependent
 // device-scope load about 2 us.)
 //
+// h goes on through the L2 of each XCD instead: its producers write one
+// device-scope copy; on each XCD, each workgroup relays a 64-value slice of
+// it into that XCD's copy (non-temporal stores), and the XCD's workgroups
+// poll that copy with non-temporal loads, which the XCD's shared L2 serves
+// (0.55 us for a round trip between two workgroups of one XCD against 0.99
+// us at device scope).  A workgroup that no relay serves falls back to the
+// device-scope copy after a bounded time.  Chain: 0.366 -> 0.362 ms per
+// token; m, with three times the values per workgroup, was slower this way.
+//
 // Tags: call c (each workgroup counts its calls in a word of its own in the
 // workspace; the grid has the same size in every call, so after a
 // completed call all counters agree) gives m of layer l the tag
@@ -105,7 +114,33 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
   const bool has_row = row < kCols;
   const bool mine = 8 * t < kCols;  // threads 0..255 own 8 values of h each
   const int tk = *A.tok;
-  const int copy = wg % kDecodeCopies;  // the copy of m and h this workgroup reads
+  const int copy = wg % kDecodeCopies;  // the copy of m this workgroup reads
+  // h goes through the L2 of each XCD: the workgroups wg = x, x + 8, ...
+  // run on XCD x when the grid is dealt out round robin; workgroup wg
+  // relays slice wg / 8 of h from the producers' copy (kDecodeXcds) into
+  // its XCD's copy and reads that copy.  (The same for m, with 3 times the
+  // words, was slower: 0.381 against 0.366 ms per token.)
+  const uint32_t xcd = xcd_id();
+  const int nslot = nwg / kDecodeXcds;
+  const bool relay = nwg % kDecodeXcds == 0 && xcd < (uint32_t)kDecodeXcds && kCols <= kWave * nslot;
+  const int slot = wg / kDecodeXcds;
+  const int near_copy = relay ? (int)xcd : 0;
+  bool use_near = relay;
+  // h after layer l - 1 (tag 64 c + 2 l): the relay of this workgroup's
+  // slice (wave 0), then 8 values per thread into h8
+  const auto poll_h = [&](int l, float *h8) {
+    const uint32_t th = tag0 + 2 * l;
+    uint64_t *hb = A.hq + (size_t)((l - 1) & 1) * kDecodeSlots * kCols;
+    const uint64_t *far = hb + kDecodeXcds * kCols;
+    bool ok = true;
+    if (relay && wave == 0) {
+      const int i = slot * kCols / nslot + lane;
+      if (i < (slot + 1) * kCols / nslot)
+        ok = relay_word(far, hb + near_copy * kCols, i, th, err, A.spin_ticks);
+    }
+    return ok && poll_tagged_near<8>(hb + near_copy * kCols + 8 * t, far + 8 * t, th, h8, err,
+                                     use_near, A.near_ticks, A.spin_ticks);
+  };
 
   GuBlock a;
   DownRow<NP> d;
@@ -149,8 +184,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
       }
     } else if (mine) {
       // h after the previous layer, 8 values per thread
-      ok = poll_tagged<8>(A.hq + ((size_t)((l - 1) & 1) * kDecodeCopies + copy) * kCols + 8 * t,
-                          tag0 + 2 * l, h8, err, A.spin_ticks);
+      ok = poll_h(l, h8);
     }
     issue_order();
     if (has_row) load_down<NP>(L, row, lane, d);
@@ -179,6 +213,8 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
       load_gu(A.layer[l + 1], pb, min(kGuPairs, pe - pb), lane, a);
     if (!poller && l + 1 == A.nlayers && head) head_load_into(A, gw, lane, a);
     issue_order();
+    const uint32_t tag_m = tag0 + 2 * l + 1;
+    const uint64_t *mcopy = mq + (size_t)copy * kDecodeMaxInter;
 
     // ---- stage B: m and its group sums into LDS; h = h + down m
     // chunk c = 8 consecutive values of m; poller thread p takes chunks
@@ -199,7 +235,6 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
     // several chunks in the same rounds multiplies the traffic while the
     // wait lasts (three at once: 0.369 -> 0.394 ms per token).
     constexpr int kBatch = 1;
-    const uint64_t *mcopy = mq + (size_t)copy * kDecodeMaxInter;
     if (poller) {
       const int p = t - (kThreads - kPollThreads);
       bool large = false;
@@ -210,8 +245,8 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
 #pragma unroll 1
       for (int r0 = 0; r0 < kPerPoller; r0 += kBatch) {
         float xm[kBatch * 8];
-        if (!poll_tagged<8>(mcopy + 8 * (p + r0 * kPollThreads), tag0 + 2 * l + 1, xm, err,
-                            A.spin_ticks)) {
+        const int c0 = p + r0 * kPollThreads;
+        if (!poll_tagged<8>(mcopy + 8 * c0, tag_m, xm, err, A.spin_ticks)) {
           S.flag[0] = 1u;
           break;
         }
@@ -271,11 +306,10 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
                             : down_row<NP, FAST, false>(S, lane, d);
       if (lane == kWave - 1) {
         res = res + v;
+        // h to the producers' copy, from which each XCD relays it
         if (l + 1 < A.nlayers || head)
-#pragma unroll
-          for (int c = 0; c < kDecodeCopies; ++c)
-            store_tagged(A.hq + ((size_t)(l & 1) * kDecodeCopies + c) * kCols + row, res,
-                         tag0 + 2 * l + 2);
+          store_tagged(A.hq + ((size_t)(l & 1) * kDecodeSlots + kDecodeXcds) * kCols + row, res,
+                       tag0 + 2 * l + 2);
         if (l + 1 == A.nlayers) A.h[row] = res;
       }
     }
@@ -294,8 +328,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
       const float4 w0 = wp[0], w1 = wp[1];
       w8[0] = w0.x; w8[1] = w0.y; w8[2] = w0.z; w8[3] = w0.w;
       w8[4] = w1.x; w8[5] = w1.y; w8[6] = w1.z; w8[7] = w1.w;
-      ok = poll_tagged<8>(A.hq + ((size_t)((L - 1) & 1) * kDecodeCopies + copy) * kCols + 8 * t,
-                          tag0 + 2 * L, h8, err, A.spin_ticks);
+      ok = poll_h(L, h8);
     }
     // the second block's loads, after the wait for h (a poll issued behind
     // them would wait for them too)

@@ -99,6 +99,24 @@ int wait_ticks(long long *ticks) {
   return Q4_OK;
 }
 
+// How long a wait for h reads its XCD's copy before it turns to the
+// producers' copy: 50 us by default (every relay of a launch is done well
+// within that; only a workgroup that no relay serves runs it out), or
+// Q4_DECODE_NEAR_US microseconds (0: after one round), at most the whole
+// bound.
+long long near_ticks(long long spin_ticks) {
+  long long us = 50;
+  if (const char *v = getenv("Q4_DECODE_NEAR_US")) us = atoll(v);
+  if (us < 0) us = 0;
+  if (us > 60000000) us = 60000000;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    khz = 100000;
+  const long long t = us * (khz > 0 ? khz : 100000) / 1000;
+  return spin_ticks < t ? spin_ticks : t;
+}
+
 // Host wait on `stream`, then the error word at byte offset err_off of a
 // workspace: Q4_OK, or Q4_ETIMEOUT after clearing the first `clear` bytes
 // of the workspace (a wait ran out and left its words in an unknown state).
@@ -513,6 +531,7 @@ int decode_args(const q4_mat *emb, const int32_t *tok, const q4_mlp_layer *layer
   a->kq = reinterpret_cast<uint64_t *>(w + q4::kDecodeKqOffset);
   a->eps = eps;
   if (wait_ticks(&a->spin_ticks) != Q4_OK) return Q4_EHIP;
+  a->near_ticks = near_ticks(a->spin_ticks);
   if (q4::decode_layers_grid(mode, inter) < 1) return Q4_EINVAL;  // too few compute units
   return Q4_OK;
 }

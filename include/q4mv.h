@@ -251,7 +251,7 @@ int q4_embed(const q4_mat *w, const int32_t *tok, float *e, void *stream);
  *   h       : device float[2048]: the output (its prior contents are not
  *             read).
  *   ws      : device workspace of q4_decode_layers_ws_bytes() bytes (about
- *             1.3 MB), 16-byte aligned, zero-filled before its first use;
+ *             1.4 MB), 16-byte aligned, zero-filled before its first use;
  *             each call leaves it ready for the next.  Calls that overlap in
  *             time must not share it, and no other kernel should hold the
  *             device's compute units while this one runs.
@@ -261,6 +261,10 @@ int q4_embed(const q4_mat *w, const int32_t *tok, float *e, void *stream);
  * one runs out, every workgroup leaves the kernel and h is undefined;
  * q4_decode_layers_status reports it.  A workspace whose error word is set
  * makes the kernel return at once until the status call clears it.
+ * h between layers goes through the L2 of each XCD (the XCD's workgroups
+ * relay slices of it); a wait for h that its XCD's copy has not served
+ * within Q4_DECODE_NEAR_US microseconds (env, default 50) reads the
+ * device-scope copy from then on in that call.
  * Q4_EINVAL also when the device has fewer than 256 compute units.
  */
 typedef struct q4_mlp_layer {

@@ -1,8 +1,10 @@
 """GPU parity of the persistent decode-layers kernel (q4_decode_layers):
 the embedding and every MLP layer of a decode step in one launch whose
-workgroups hand m and h to each other through tagged words, against the
-oracle's separate steps (bit-exact in fixed mode), against the per-stage
-kernels in fast mode, inside a captured graph, and its bounded waits."""
+workgroups hand m and h to each other through tagged words (h relayed
+through each XCD's L2, with a fallback to the device-scope copy), against
+the oracle's separate steps (bit-exact in fixed mode), against the
+per-stage kernels in fast mode, inside a captured graph, and its bounded
+waits."""
 import os
 
 import numpy as np
@@ -123,6 +125,27 @@ def test_decode_layers_full_depth_matches_oracle():
     for _ in range(3):
         again, ws = run_layers(q4, emb, layers, w, w["tok0"], ws=ws)
         assert_bits_equal(again, want, "h after 24 layers, again")
+
+
+def test_decode_layers_relay_fallback_gives_the_same_bits():
+    """Q4_DECODE_NEAR_US=0: a wait for h reads its XCD's copy for one round
+    only, then the producers' device-scope copy (the path of a workgroup
+    that no relay serves); the result must not change."""
+    q4 = lib()
+    w = synth.chain_weights(seed=46, layers=4, vocab=3000)
+    emb = q4.Q4Matrix.from_host(w["head"])
+    layers = mlp_layers(q4, w)
+    want = oracle.chain_hidden(w, w["tok0"], NTHREADS)
+    os.environ["Q4_DECODE_NEAR_US"] = "0"
+    try:
+        ws = None
+        for i in range(3):
+            got, ws = run_layers(q4, emb, layers, w, w["tok0"], ws=ws)
+            assert_bits_equal(got, want, "h after 4 layers, relay fallback, call %d" % i)
+    finally:
+        del os.environ["Q4_DECODE_NEAR_US"]
+    got, ws = run_layers(q4, emb, layers, w, w["tok0"], ws=ws)
+    assert_bits_equal(got, want, "h after 4 layers, relay")
 
 
 def test_decode_layers_in_graph_replays():
