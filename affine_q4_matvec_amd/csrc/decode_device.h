@@ -30,7 +30,22 @@ struct alignas(16) Lds {
   float xs[NP * 32];                // their group sums
   float red[kWaves];                // the waves' sums of squares
   uint32_t flag[2];                 // stage B: a wait gave up / some |m| >= 2^118
+  alignas(16) uint32_t wflag[2][kWaves];  // workgroup_rmsq: per wave, a wait gave up / a large x
 };
+
+// Whether `p` holds in any thread of the workgroup, with one barrier: each
+// wave's vote goes to slot[wave], then every thread reads all of them.
+// (HIP's __syncthreads_or takes three barriers and an LDS atomic.)  The
+// caller must not use the same slots again before a further barrier.
+__device__ __forceinline__ bool workgroup_any(uint32_t *slot, bool p) {
+  static_assert(kWaves == 8, "two 16-byte reads of the slots");
+  const bool w = __any(p);
+  if ((threadIdx.x & (kWave - 1)) == 0) slot[threadIdx.x / kWave] = w ? 1u : 0u;
+  __syncthreads();
+  const uint4 a = reinterpret_cast<const uint4 *>(slot)[0];
+  const uint4 b = reinterpret_cast<const uint4 *>(slot)[1];
+  return ((a.x | a.y | a.z | a.w) | (b.x | b.y | b.z | b.w)) != 0u;
+}
 
 // rmsq of h over the workgroup, with the arithmetic and tree of the rmsq
 // kernel (ops_device.h), so the bits of every wave forming it alone:
@@ -55,7 +70,7 @@ __device__ __forceinline__ int workgroup_rmsq(Lds<NP> &L, const float *h8, const
 #pragma unroll
   for (int m = 1; m < kWave; m *= 2) s = s + __shfl_xor(s, m);
   if (lane == 0) L.red[wave] = s;
-  if (!__syncthreads_and(ok)) return -1;
+  if (workgroup_any(L.wflag[0], !ok)) return -1;
   const float *r = L.red;
   static_assert(kWaves == 8, "the tree over the wave sums");
   const float ss = ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
@@ -77,7 +92,7 @@ __device__ __forceinline__ int workgroup_rmsq(Lds<NP> &L, const float *h8, const
   g = g + __shfl_xor(g, 2);
   g = g + __shfl_xor(g, 4);
   if (mine && (t & 7) == 0) L.xs[t >> 3] = g;
-  return __syncthreads_or(large) ? 0 : 1;
+  return workgroup_any(L.wflag[1], large) ? 0 : 1;
 }
 
 // A wave's 32 values of x from L (lane l: columns [32 l, 32 l + 32)) and
