@@ -148,6 +148,45 @@ def test_decode_layers_relay_fallback_gives_the_same_bits():
     assert_bits_equal(got, want, "h after 4 layers, relay")
 
 
+def test_two_persistent_launches_at_once_end_and_stay_exact():
+    """The persistent kernel needs every compute unit (one workgroup each);
+    two launches on two streams at once may each get only part of the
+    device.  Each must then either finish with the oracle's bits or give up
+    through its bounded waits (Q4_ETIMEOUT, here after 200 ms) and leave a
+    workspace that the status call makes usable again: never a hang, never
+    other bits."""
+    q4 = lib()
+    w = synth.chain_weights(seed=48, layers=2, vocab=3000)
+    emb = q4.Q4Matrix.from_host(w["head"])
+    layers = mlp_layers(q4, w)
+    want = oracle.chain_hidden(w, w["tok0"], NTHREADS)
+    t = torch.tensor([w["tok0"]], dtype=torch.int32, device="cuda")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    hs = [torch.full((2048,), 7.0, device="cuda") for _ in streams]
+    wss = [new_ws(q4) for _ in streams]
+    seen = set()
+    os.environ["Q4_DECODE_TIMEOUT_MS"] = "200"
+    try:
+        for rep in range(6):
+            torch.cuda.synchronize()
+            for s, h, ws in zip(streams, hs, wss):
+                q4.q4_decode_layers(emb, t, layers, w["eps"], h, ws, stream=s)
+            for i, (s, h, ws) in enumerate(zip(streams, hs, wss)):
+                st = q4.q4_decode_layers_status(ws, stream=s)
+                print("concurrent launches, round %d, stream %d: status %d" % (rep, i, st),
+                      flush=True)
+                assert st in (q4.Q4_OK, q4.Q4_ETIMEOUT)
+                seen.add(st)
+                if st == q4.Q4_OK:
+                    assert_bits_equal(host(h), want, "h, concurrent launch %d/%d" % (rep, i))
+    finally:
+        del os.environ["Q4_DECODE_TIMEOUT_MS"]
+    print("statuses seen:", sorted(seen), flush=True)
+    for h, ws in zip(hs, wss):
+        got, _ = run_layers(q4, emb, layers, w, w["tok0"], ws=ws)
+        assert_bits_equal(got, want, "h after the concurrent launches")
+
+
 def test_decode_layers_in_graph_replays():
     q4 = lib()
     w = synth.chain_weights(seed=47, layers=3, vocab=3000)
