@@ -663,10 +663,7 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
             break;
           }
           // group sums: T over each chunk, then over 8 chunks by a butterfly
-          float gs = ops::tree8(xm);
-          gs = gs + __shfl_xor(gs, 1);
-          gs = gs + __shfl_xor(gs, 2);
-          gs = gs + __shfl_xor(gs, 4);
+          const float gs = ops::lane_sum8(ops::tree8(xm));
           if ((c & 7) == 0) S.xs[c >> 3] = gs;
 #pragma unroll
           for (int k = 0; k < 8; ++k) large |= !(__builtin_fabsf(xm[k]) < 0x1p118f);

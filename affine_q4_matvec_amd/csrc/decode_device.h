@@ -66,9 +66,7 @@ __device__ __forceinline__ int workgroup_rmsq(Lds<NP> &L, const float *h8, const
   float v[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) v[k] = mine ? h8[k] * h8[k] : kNegZero;
-  float s = ops::tree8(v);
-#pragma unroll
-  for (int m = 1; m < kWave; m *= 2) s = s + __shfl_xor(s, m);
+  const float s = ops::lane_sum64(ops::tree8(v));
   if (lane == 0) L.red[wave] = s;
   if (workgroup_any(L.wflag[0], !ok)) return -1;
   const float *r = L.red;
@@ -87,10 +85,7 @@ __device__ __forceinline__ int workgroup_rmsq(Lds<NP> &L, const float *h8, const
     dst[0] = make_float4(u[0], u[1], u[2], u[3]);
     dst[1] = make_float4(u[4], u[5], u[6], u[7]);
   }
-  float g = ops::tree8(u);
-  g = g + __shfl_xor(g, 1);
-  g = g + __shfl_xor(g, 2);
-  g = g + __shfl_xor(g, 4);
+  const float g = ops::lane_sum8(ops::tree8(u));
   if (mine && (t & 7) == 0) L.xs[t >> 3] = g;
   return workgroup_any(L.wflag[1], large) ? 0 : 1;
 }

@@ -256,10 +256,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
           const float *v = xm + 8 * r;
           // group sums: T over each chunk, then over 8 chunks (8 consecutive
           // lanes) by a butterfly: the balanced tree over the group's 64
-          float g = ops::tree8(v);
-          g = g + __shfl_xor(g, 1);
-          g = g + __shfl_xor(g, 2);
-          g = g + __shfl_xor(g, 4);
+          const float g = ops::lane_sum8(ops::tree8(v));
           if ((c & 7) == 0) S.xs[c >> 3] = g;
 #pragma unroll
           for (int k = 0; k < 8; ++k) large |= !(__builtin_fabsf(v[k]) < 0x1p118f);

@@ -24,6 +24,40 @@ __device__ __forceinline__ float tree8(const float *v) {
   return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
 }
 
+// Lane butterflies with DPP and the gfx950 lane swaps instead of shuffles
+// routed through LDS (a ds_bpermute each, whose latency sits on the
+// critical path of every reduction).  Steps: xor 1 and xor 2 within quads;
+// then, once every aligned block of 4 (8) lanes holds one value, the mirror
+// within 8 (16) lanes pairs the same blocks as xor 4 (8); then the 16- and
+// 32-lane swaps pair 16-lane rows 0/1, 2/3 and then halves 0/1, as xor 16
+// and xor 32 do.  Each step adds the same two operands as the xor
+// butterfly (in the other order in half the lanes, which IEEE addition does
+// not see), so the result is the balanced tree over the lanes, in every
+// lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned block of 8 lanes.
+__device__ __forceinline__ float lane_sum8(float s) {
+  s = s + dpp_move<0xB1>(s);   // quad_perm [1,0,3,2]: xor 1
+  s = s + dpp_move<0x4E>(s);   // quad_perm [2,3,0,1]: xor 2
+  return s + dpp_move<0x141>(s);  // row_half_mirror: xor 4 here
+}
+
+// Sum over the 64 lanes of the wave.
+__device__ __forceinline__ float lane_sum64(float s) {
+  s = lane_sum8(s);
+  s = s + dpp_move<0x140>(s);  // row_mirror: xor 8 here
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false,
+                                                  false);
+  s = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false,
+                                                  false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // RMS norm of n values with weights, plus group sums, by one workgroup of
 // blockDim.x = max(64, P/8) threads (P = next power of two >= n, n % 64 ==
 // 0, at most 1024 threads).  Thread t owns the contiguous slots [8t, 8t+8);
@@ -49,9 +83,7 @@ __device__ __forceinline__ float rmsq_rho_regs(const float *hv, int n, float eps
   float v[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) v[k] = 8 * t + k < n ? hv[k] * hv[k] : kNegZero;
-  float s = tree8(v);
-#pragma unroll
-  for (int m = 1; m < kWave; m *= 2) s = s + __shfl_xor(s, m);
+  const float s = lane_sum64(tree8(v));
   if (lane == 0) red[wave] = s;
   __syncthreads();
   if (t == 0) {
@@ -86,9 +118,7 @@ __device__ __forceinline__ float rmsq_rho_wave2048(const float *hv, float eps) {
   float sq[32];
 #pragma unroll
   for (int k = 0; k < 32; ++k) sq[k] = hv[k] * hv[k];
-  float s = (tree8(sq) + tree8(sq + 8)) + (tree8(sq + 16) + tree8(sq + 24));
-#pragma unroll
-  for (int m = 1; m < kWave; m *= 2) s = s + __shfl_xor(s, m);
+  const float s = lane_sum64((tree8(sq) + tree8(sq + 8)) + (tree8(sq + 16) + tree8(sq + 24)));
   return rmsq_rho_from_ss(s, 2048, eps);
 }
 
@@ -113,10 +143,7 @@ __device__ __forceinline__ void rmsq_u(int n, float rho, const float *hv, const 
     uv[k] = i < n ? rmsq_value(hv[k], rho, wv[k]) : kNegZero;
     if (i < n) u[i + (i >> 5) * PAD] = uv[k];
   }
-  float gsum = tree8(uv);
-  gsum = gsum + __shfl_xor(gsum, 1);
-  gsum = gsum + __shfl_xor(gsum, 2);
-  gsum = gsum + __shfl_xor(gsum, 4);
+  const float gsum = lane_sum8(tree8(uv));
   if ((t & 7) == 0 && 8 * t < n) us[t >> 3] = gsum;
 }
 

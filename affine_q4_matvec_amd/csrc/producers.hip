@@ -56,7 +56,7 @@ __global__ __launch_bounds__(64) void rmsq2048_wave_kernel(const float *__restri
 #pragma unroll
   for (int k = 0; k < 8; ++k) up[k] = make_float4(uv[4 * k], uv[4 * k + 1], uv[4 * k + 2], uv[4 * k + 3]);
   const float half = (tree8(uv) + tree8(uv + 8)) + (tree8(uv + 16) + tree8(uv + 24));
-  const float g = half + __shfl_xor(half, 1);
+  const float g = half + ops::dpp_move<0xB1>(half);  // xor 1
   if ((lane & 1) == 0) us[lane >> 1] = g;
 }
 
@@ -72,9 +72,7 @@ __global__ __launch_bounds__(256) void swq_kernel(const float *__restrict__ a, i
   const int i = 64 * g + lane;
   const float ov = swiglu_value<FAST>(a[i], a[n + i]);
   o[i] = ov;
-  float s = ov;
-#pragma unroll
-  for (int m = 1; m < kWave; m *= 2) s = s + __shfl_xor(s, m);
+  const float s = ops::lane_sum64(ov);
   if (lane == 0) os[g] = s;
 }
 

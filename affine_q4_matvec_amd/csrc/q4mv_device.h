@@ -83,8 +83,16 @@ __device__ __forceinline__ float segment_sum(float t) {
   if constexpr (LPR >= 4) t = t + dpp<kDppQuadXor2>(t);
   if constexpr (LPR >= 8) t = t + dpp<kDppRowHalfMirror>(t);
   if constexpr (LPR >= 16) t = t + dpp<kDppRowMirror>(t);
-  if constexpr (LPR >= 32) t = t + __shfl_xor(t, 16);
-  if constexpr (LPR >= 64) t = t + __shfl_xor(t, 32);
+  if constexpr (LPR >= 32) {  // the 16-lane rows are uniform: rows 0/1, 2/3 (xor 16)
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(t), __float_as_uint(t), false,
+                                                    false);
+    t = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  if constexpr (LPR >= 64) {  // halves 0/1 (xor 32)
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false,
+                                                    false);
+    t = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  }
   return t;
 }
 
