@@ -97,11 +97,7 @@ __device__ __forceinline__ float sum64(float s) {
   return segment_sum<64>(s);
 }
 
-__device__ __forceinline__ float max64(float s) {
-#pragma unroll
-  for (int m = 1; m < kWave; m *= 2) s = fmaxf(s, __shfl_xor(s, m));
-  return s;
-}
+__device__ __forceinline__ float max64(float s) { return ops::lane_max64(s); }
 
 __device__ __forceinline__ void load8(const float *p, float *v) {
   const float4 a = reinterpret_cast<const float4 *>(p)[0];
@@ -297,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void atq_kernel(AtqArgs a) {
         pr[k] = pb + k < n ? S.e[8 * pg + k] * vk : kNegZero;
       }
       const float b8 = tree8(pr);
-      w4[col] = b8 + __shfl_xor(b8, 32);
+      w4[col] = ops::half_sum32(b8);
     }
     if (lane < 32)
       *reinterpret_cast<float4 *>(&S.part[wave][4 * cq]) = make_float4(w4[0], w4[1], w4[2], w4[3]);

@@ -103,11 +103,7 @@ __device__ __forceinline__ float sum64(float s) {
   return segment_sum<64>(s);
 }
 
-__device__ __forceinline__ float max64(float s) {
-#pragma unroll
-  for (int m = 1; m < kWave; m *= 2) s = fmaxf(s, __shfl_xor(s, m));
-  return s;
-}
+__device__ __forceinline__ float max64(float s) { return ops::lane_max64(s); }
 
 struct AttnLds {
   float in[4][kD];          // q, gate, k, v of the head

@@ -347,11 +347,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
     // the workgroup's best key (holder lanes 15, 31, 47, 63 of each wave;
     // other lanes hold key 0) to workgroup 0 as two tagged words
     __shared__ unsigned long long wkey[kWaves];
-    unsigned long long k = best.key();
-    unsigned long long o = __shfl_xor(k, 16);
-    k = o > k ? o : k;
-    o = __shfl_xor(k, 32);
-    k = o > k ? o : k;
+    unsigned long long k = ops::key_max_rows(best.key());
     if (lane == kWave - 1) wkey[wave] = k;
     __syncthreads();
     const uint32_t ktag = call + 1;  // never 0, the workspace's initial contents
@@ -374,11 +370,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
             ((unsigned long long)__float_as_uint(kv[0]) << 32) | __float_as_uint(kv[1]);
         best_key = c > best_key ? c : best_key;
       }
-#pragma unroll
-      for (int m = 1; m < kWave; m *= 2) {
-        o = __shfl_xor(best_key, m);
-        best_key = o > best_key ? o : best_key;
-      }
+      best_key = ops::lane_key_max64(best_key);
       __syncthreads();  // wkey is free again (every reader is past it)
       if (lane == 0) wkey[wave] = best_key;
       if (!__syncthreads_and(ok)) return;

@@ -46,6 +46,61 @@ __device__ __forceinline__ float lane_sum8(float s) {
   return s + dpp_move<0x141>(s);  // row_half_mirror: xor 4 here
 }
 
+// Sum of the two 32-lane halves (xor 32), in every lane.
+__device__ __forceinline__ float half_sum32(float s) {
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false,
+                                                  false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// Largest of the 64 lanes (fmaxf: any order gives the same value).
+__device__ __forceinline__ float lane_max64(float s) {
+  s = fmaxf(s, dpp_move<0xB1>(s));
+  s = fmaxf(s, dpp_move<0x4E>(s));
+  s = fmaxf(s, dpp_move<0x141>(s));
+  s = fmaxf(s, dpp_move<0x140>(s));
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false,
+                                                  false);
+  s = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false,
+                                                  false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
+// 64-bit (value, index) keys: the largest over lanes, by the same steps on
+// the two 32-bit halves (a maximum, so the order of the steps does not
+// matter).
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_move_key(unsigned long long v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+__device__ __forceinline__ unsigned long long key_max(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+
+// The larger key of lanes i and i ^ 16, then of i and i ^ 32, in every lane.
+__device__ __forceinline__ unsigned long long key_max_rows(unsigned long long k) {
+  auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)k, (uint32_t)k, false, false);
+  auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(k >> 32), (uint32_t)(k >> 32), false, false);
+  k = key_max(((unsigned long long)hi[0] << 32) | lo[0], ((unsigned long long)hi[1] << 32) | lo[1]);
+  lo = __builtin_amdgcn_permlane32_swap((uint32_t)k, (uint32_t)k, false, false);
+  hi = __builtin_amdgcn_permlane32_swap((uint32_t)(k >> 32), (uint32_t)(k >> 32), false, false);
+  return key_max(((unsigned long long)hi[0] << 32) | lo[0], ((unsigned long long)hi[1] << 32) | lo[1]);
+}
+
+// The largest key of the 64 lanes, in every lane.
+__device__ __forceinline__ unsigned long long lane_key_max64(unsigned long long k) {
+  k = key_max(k, dpp_move_key<0xB1>(k));
+  k = key_max(k, dpp_move_key<0x4E>(k));
+  k = key_max(k, dpp_move_key<0x141>(k));
+  k = key_max(k, dpp_move_key<0x140>(k));
+  return key_max_rows(k);
+}
+
 // Sum over the 64 lanes of the wave.
 __device__ __forceinline__ float lane_sum64(float s) {
   s = lane_sum8(s);

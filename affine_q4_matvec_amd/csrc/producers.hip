@@ -83,11 +83,7 @@ constexpr int kArgmaxMaxBlocks = 1024;
 
 __device__ __forceinline__ unsigned long long block_max_key(unsigned long long k) {
   __shared__ unsigned long long wk[16];
-#pragma unroll
-  for (int m = 1; m < kWave; m *= 2) {
-    const unsigned long long o = __shfl_xor(k, m);
-    k = o > k ? o : k;
-  }
+  k = lane_key_max64(k);
   const int wave = threadIdx.x / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) wk[wave] = k;
   __syncthreads();

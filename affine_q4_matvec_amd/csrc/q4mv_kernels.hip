@@ -366,11 +366,7 @@ __global__ __launch_bounds__(kThreads) void q4mv_row64_kernel(ProdGroup grp, Ext
     // or maximum shared by every workgroup would serialise their atomics)
     __shared__ unsigned long long wbest[kThreads / kWave];
     // the best of the four holder lanes (other lanes hold key 0)
-    unsigned long long k = best.key();
-    unsigned long long o = __shfl_xor(k, 16);
-    k = o > k ? o : k;
-    o = __shfl_xor(k, 32);
-    k = o > k ? o : k;
+    const unsigned long long k = ops::key_max_rows(best.key());
     if (lane == kWave - 1) wbest[wave] = k;
     __syncthreads();
     if (threadIdx.x == 0) {
