@@ -104,17 +104,21 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
   const uint32_t tag0 = call << 6;
 
   // wave gw = wave * nwg + wg (consecutive gw on different compute units)
-  // takes a balanced contiguous range of the inter (gate, up) pairs and
-  // the down row gw (the launch has at least 2048 waves)
+  // takes the head's blocks gw, gw + stride, ...
   const int gw = wave * nwg + wg;
   const int stride = kWaves * nwg;
-  const int pb = (int)(((long long)A.inter * gw) / stride);
-  const int pe = (int)(((long long)A.inter * (gw + 1)) / stride);
-  const int row = gw;
-  const bool has_row = row < kCols;
   const bool mine = 8 * t < kCols;  // threads 0..255 own 8 values of h each
+  // the (gate, up) pairs and the down groups by XCD (the grid has 8 x 32
+  // workgroups): XCD x = wg mod 8, k = wg / 8; wave 8 k + wave of XCD x
+  // takes pairs 2048 q + base (q < NP); the workgroup's down slice is rows
+  // [64 k, 64 k + 64) of groups 32 q + 4 x .. + 3; it owns rows [8 wg, 8 wg
+  // + 8) (threads 0..7: the residual, the pass sums' gather, h)
+  const int x = wg % kDecodeXcds, k = wg / kDecodeXcds;
+  const int base = 256 * x + 8 * k + wave;
+  const int drow = 64 * k + 8 * wave + lane / 8;
+  const bool owner = t < 8;
+  const int orow = 8 * wg + t;
   const int tk = *A.tok;
-  const int copy = wg % kDecodeCopies;  // the copy of m this workgroup reads
   // h goes through the L2 of each XCD: the workgroups wg = x, x + 8, ...
   // run on XCD x when the grid is dealt out round robin; workgroup wg
   // relays slice wg / 8 of h from the producers' copy (kDecodeXcds) into
@@ -126,6 +130,10 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
   const int slot = wg / kDecodeXcds;
   const int near_copy = relay ? (int)xcd : 0;
   bool use_near = relay;
+  // m through the XCD's L2 when this workgroup runs on the XCD the dealing
+  // assumes (else only the device-scope copy)
+  const bool local_m = relay && (int)xcd == wg % kDecodeXcds;
+  bool use_near_m = local_m;
   // h after layer l - 1 (tag 64 c + 2 l): the relay of this workgroup's
   // slice (wave 0), then 8 values per thread into h8
   const auto poll_h = [&](int l, float *h8) {
@@ -144,19 +152,21 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
 
   GuBlock a;
   DownRow<NP> d;
-  if (pb < pe) load_gu(A.layer[0], pb, min(kGuPairs, pe - pb), lane, a);
+  load_gu_strided(A.layer[0], A.inter, base, 0, min(kGuPairs, NP), lane, a);
   // the head (q4_decode_token): blocks of 4 rows gw, gw + stride, ...; the
   // first is loaded during the last layer, into the registers of the gate/up
   // block (free by then: there is no next layer)
   const bool head = A.wf != nullptr;
   const int head_blocks = (A.vocab + kHeadR - 1) / kHeadR;
   const int head_nblk = gw < head_blocks ? (head_blocks - gw + stride - 1) / stride : 0;
-  // the residual of the wave's row (lane 63): h before the layer
-  float res = has_row && lane == kWave - 1 ? embed_value(A, tk, row) : 0.0f;
+  // the residual of an owned row: h before the layer
+  float res = owner ? embed_value(A, tk, orow) : 0.0f;
 
   for (int l = 0; l < A.nlayers; ++l) {
     const DecodeLayer &L = A.layer[l];
-    uint64_t *mq = A.mq + (size_t)(l & 1) * kDecodeCopies * kDecodeMaxInter;  // copy 0
+    uint64_t *mq = A.mq + (size_t)(l & 1) * kDecodeSlots * kDecodeMaxInter;  // copy 0
+    uint64_t *mfar = mq + (size_t)kDecodeXcds * kDecodeMaxInter;
+    uint64_t *mnear = mq + (size_t)x * kDecodeMaxInter;
 
     // ---- stage A: x = rmsq(h, wn) over the workgroup (threads 0..255: 8
     // columns each); m = SwiGLU of the gate/up rows
@@ -187,90 +197,79 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
       ok = poll_h(l, h8);
     }
     issue_order();
-    if (has_row) load_down<NP>(L, row, lane, d);
+    load_down_slice<NP>(L, drow, x, lane, d);
     {
       const int rq = workgroup_rmsq(S, h8, w8, A.eps, ok);
       if (rq < 0) return;
       float xv[32];
       const float xsv = load_rmsq_x(S, lane, rq != 0, xv);
       const uint32_t tag = tag0 + 2 * l + 1;
-      const auto store_m = [mq, tag](int i, float v) {
-#pragma unroll
-        for (int c = 0; c < kDecodeCopies; ++c) store_tagged(mq + c * kDecodeMaxInter + i, v, tag);
+      // m[2048 q + base] to the XCD's copy (non-temporal: its L2) and the
+      // device-scope one
+      const auto store_m = [mfar, mnear, tag, base, local_m](int q, float v) {
+        const int i = 2048 * q + base;
+        if (local_m)
+          __builtin_nontemporal_store(((uint64_t)tag << 32) | __float_as_uint(v), mnear + i);
+        store_tagged(mfar + i, v, tag);
       };
-      if (pb < pe) {
-        if (rq != 0)
-          gu_stage<FAST, true>(L, xv, xsv, lane, pb, pe, a, store_m);
-        else
-          gu_stage<FAST, false>(L, xv, xsv, lane, pb, pe, a, store_m);
-      }
+      if (rq != 0)
+        gu_stage_strided<FAST, true>(L, A.inter, xv, xsv, lane, base, NP, a, store_m);
+      else
+        gu_stage_strided<FAST, false>(L, A.inter, xv, xsv, lane, base, NP, a, store_m);
     }
 
     // the next layer's gate/up rows, for the waves that do not poll m (they
     // poll h at the next layer's start, long after these have landed)
     const bool poller = t >= kThreads - kPollThreads;
-    if (!poller && l + 1 < A.nlayers && pb < pe)
-      load_gu(A.layer[l + 1], pb, min(kGuPairs, pe - pb), lane, a);
+    if (!poller && l + 1 < A.nlayers)
+      load_gu_strided(A.layer[l + 1], A.inter, base, 0, min(kGuPairs, NP), lane, a);
     if (!poller && l + 1 == A.nlayers && head) head_load_into(A, gw, lane, a);
     issue_order();
     const uint32_t tag_m = tag0 + 2 * l + 1;
-    const uint64_t *mcopy = mq + (size_t)copy * kDecodeMaxInter;
 
-    // ---- stage B: m and its group sums into LDS; h = h + down m
-    // chunk c = 8 consecutive values of m; poller thread p takes chunks
-    // p, p + kPollThreads, ...  The pollers are waves without fresh loads in
+    // ---- stage B: this XCD's m (its workgroup's 4 NP groups) and their
+    // group sums into LDS; the slice's pass sums to the rows' owners; h =
+    // h + down m for the owned rows.  Poller thread p < 64 NP takes local
+    // values [4 p, 4 p + 4): block q = p / 64, m[2048 q + 256 x + 4 (p %
+    // 64) ..], group p / 16.  The pollers are waves without fresh loads in
     // flight: a wave's loads complete in issue order for its wait counter,
-    // so a poll behind a prefetch of the GPU's next gate/up rows (about 16
-    // MB) would wait for that prefetch to land.
-    constexpr int kChunks = NP * kCols / 8;
-    constexpr int kPerPoller = kChunks / kPollThreads;
-    static_assert(kChunks % kPollThreads == 0, "whole rounds of chunks");
-    // the workgroup polls only once all its waves are done with stage A (a
-    // poll that starts early only adds traffic at the lines being polled)
+    // so a poll behind a prefetch of the GPU's next gate/up rows would wait
+    // for that prefetch to land.
+    // the workgroup polls only once all its waves are done with stage A (the
+    // values go to S.x, which stage A reads)
     if (t == 0) S.flag[0] = S.flag[1] = 0u;
     __syncthreads();
-    // the pollers' chunks: c = p + r * kPollThreads, r < kPerPoller, one at
-    // a time.  The hand-offs are bound by the polled traffic: every
-    // workgroup reads all of m (NP * 16 KB of tagged words), and polling
-    // several chunks in the same rounds multiplies the traffic while the
-    // wait lasts (three at once: 0.369 -> 0.394 ms per token).
-    constexpr int kBatch = 1;
+    const int p = t - (kThreads - kPollThreads);
+    const bool mpoll = poller && p < 64 * NP;  // wave-uniform
     if (poller) {
-      const int p = t - (kThreads - kPollThreads);
-      bool large = false;
-      // values pre-scaled for the pair decode (the scaling of
-      // prescale_for_pairs), unless some value of the workgroup turns out
-      // to be large: then the raw values are written over them below
-      const float scale = 1.0f / fp8_unit();
-#pragma unroll 1
-      for (int r0 = 0; r0 < kPerPoller; r0 += kBatch) {
-        float xm[kBatch * 8];
-        const int c0 = p + r0 * kPollThreads;
-        if (!poll_tagged<8>(mcopy + 8 * c0, tag_m, xm, err, A.spin_ticks)) {
+      if (mpoll) {
+        const int lv = 4 * p;
+        const int i = 2048 * (lv / 256) + 256 * x + lv % 256;
+        float v[4];
+        if (!poll_tagged_near<4>(mnear + i, mfar + i, tag_m, v, err, use_near_m, A.near_ticks,
+                                 A.spin_ticks))
           S.flag[0] = 1u;
-          break;
-        }
+        // group sums: the balanced tree over the group's 64 values (4 per
+        // lane, 16 lanes)
+        float gs = (v[0] + v[1]) + (v[2] + v[3]);
+        gs = ops::lane_sum8(gs);
+        gs = gs + ops::dpp_move<0x140>(gs);  // row_mirror: xor 8 here
+        if ((p & 15) == 0) S.xs[p >> 4] = gs;
+        bool large = false;
 #pragma unroll
-        for (int r = 0; r < kBatch; ++r) {
-          const int c = p + (r0 + r) * kPollThreads;
-          const float *v = xm + 8 * r;
-          // group sums: T over each chunk, then over 8 chunks (8 consecutive
-          // lanes) by a butterfly: the balanced tree over the group's 64
-          const float g = ops::lane_sum8(ops::tree8(v));
-          if ((c & 7) == 0) S.xs[c >> 3] = g;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) large |= !(__builtin_fabsf(v[k]) < 0x1p118f);
-          // value i of m sits at i + 4 (i / 32) in the padded layout
-          float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * c + 4 * (c >> 2));
-          dst[0] = make_float4(v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale);
-          dst[1] = make_float4(v[4] * scale, v[5] * scale, v[6] * scale, v[7] * scale);
-        }
+        for (int kk = 0; kk < 4; ++kk) large |= !(__builtin_fabsf(v[kk]) < 0x1p118f);
+        if (large) S.flag[1] = 1u;
+        // pre-scaled for the pair decode (the scaling of
+        // prescale_for_pairs), unless some value of the workgroup is large:
+        // then the raw values are written over them below
+        const float scale = 1.0f / fp8_unit();
+        *reinterpret_cast<float4 *>(S.x + lv + 4 * (lv >> 5)) =
+            make_float4(v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale);
       }
-      if (large) S.flag[1] = 1u;
       // this wave's gate/up rows of the next layer (or its first head
       // blocks after the last layer), now that its polls are done
-      if (l + 1 < A.nlayers && pb < pe)
-        load_gu(A.layer[l + 1], pb, min(kGuPairs, pe - pb), lane, a);
+      if (l + 1 < A.nlayers)
+        load_gu_strided(A.layer[l + 1], A.inter, base, 0, min(kGuPairs, NP), lane, a);
       if (l + 1 == A.nlayers && head) head_load_into(A, gw, lane, a);
       issue_order();
     }
@@ -279,35 +278,54 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
     const bool pairs = S.flag[1] == 0u;
     if (!pairs) {
       // some |m| >= 2^118: the plain decode, on the raw values read again
-      // from the tagged words (they carry this layer's tag until every
-      // workgroup, this one included, has done this layer's down rows)
-      if (poller) {
-        const int p = t - (kThreads - kPollThreads);
-#pragma unroll 1
-        for (int r = 0; r < kPerPoller; ++r) {
-          const int c = p + r * kPollThreads;
-          float v[8];
+      // from the device-scope copy (it keeps this layer's tag until every
+      // workgroup, this one included, has done this layer's down slice)
+      if (mpoll) {
+        const int lv = 4 * p;
+        const int i = 2048 * (lv / 256) + 256 * x + lv % 256;
+        float v[4];
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
-            v[k] = __uint_as_float((uint32_t)__hip_atomic_load(
-                mcopy + 8 * c + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-          float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * c + 4 * (c >> 2));
-          dst[0] = make_float4(v[0], v[1], v[2], v[3]);
-          dst[1] = make_float4(v[4], v[5], v[6], v[7]);
-        }
+        for (int kk = 0; kk < 4; ++kk)
+          v[kk] = __uint_as_float((uint32_t)__hip_atomic_load(mfar + i + kk, __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT));
+        *reinterpret_cast<float4 *>(S.x + lv + 4 * (lv >> 5)) = make_float4(v[0], v[1], v[2], v[3]);
       }
       __syncthreads();
     }
-    if (has_row) {
-      const float v = pairs ? down_row<NP, FAST, true>(S, lane, d)
-                            : down_row<NP, FAST, false>(S, lane, d);
-      if (lane == kWave - 1) {
-        res = res + v;
+    {
+      // the slice: the row's 4-group sums of every pass, to the row's owner
+      float sj[NP];
+      if (pairs)
+        down_slice<NP, FAST, true>(S, lane, d, sj);
+      else
+        down_slice<NP, FAST, false>(S, lane, d, sj);
+      if ((lane & 7) == 0)
+#pragma unroll
+        for (int j = 0; j < NP; ++j)
+          store_tagged(A.pq + ((size_t)drow * NP + j) * kDecodeXcds + x, sj[j], tag_m);
+    }
+    if (wave == 0) {
+      // thread t < 8 NP: owned row 8 wg + t % 8, pass t / 8: the 8 XCDs'
+      // sums in order (the balanced tree over the pass's 32 group terms)
+      bool okp = true;
+      if (t < 8 * NP) {
+        float v8[8];
+        okp = poll_tagged<8>(A.pq + ((size_t)(8 * wg + (t & 7)) * NP + (t >> 3)) * kDecodeXcds,
+                             tag_m, v8, err, A.spin_ticks);
+        S.own[t] = ops::tree8(v8);
+      }
+      const bool all_ok = __all(okp);
+      issue_order();  // the same wave reads them back below
+      if (owner && all_ok) {
+        float pj[NP];
+#pragma unroll
+        for (int jj = 0; jj < NP; ++jj) pj[jj] = S.own[t + 8 * jj];
+        res = res + combine_passes<NP>(pj);
         // h to the producers' copy, from which each XCD relays it
         if (l + 1 < A.nlayers || head)
-          store_tagged(A.hq + ((size_t)(l & 1) * kDecodeSlots + kDecodeXcds) * kCols + row, res,
+          store_tagged(A.hq + ((size_t)(l & 1) * kDecodeSlots + kDecodeXcds) * kCols + orow, res,
                        tag0 + 2 * l + 2);
-        if (l + 1 == A.nlayers) A.h[row] = res;
+        if (l + 1 == A.nlayers) A.h[orow] = res;
       }
     }
     // the next stage A writes S.x (all reads of it above are done)
@@ -410,9 +428,10 @@ int32_t decode_layers_grid(int mode, int32_t inter) {
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  // one workgroup per compute unit, and a wave for every down row
-  if (per_cu < 1 || cus * kWaves < kCols || cus > kDecodeMaxGroups) return 0;
-  return cus;
+  // one workgroup per compute unit; the work is dealt to 8 XCDs of 32
+  // workgroups (further compute units stay idle)
+  if (per_cu < 1 || cus < kDecodeGroups) return 0;
+  return kDecodeGroups;
 }
 
 hipError_t launch_decode_layers(const DecodeArgs &a, int mode, hipStream_t st) {

@@ -527,6 +527,7 @@ int decode_args(const q4_mat *emb, const int32_t *tok, const q4_mlp_layer *layer
   char *w = static_cast<char *>(ws);
   a->hq = reinterpret_cast<uint64_t *>(w + q4::kDecodeHqOffset);
   a->mq = reinterpret_cast<uint64_t *>(w + q4::kDecodeMqOffset);
+  a->pq = reinterpret_cast<uint64_t *>(w + q4::kDecodePqOffset);
   a->ctl = reinterpret_cast<uint32_t *>(w + q4::kDecodeCtlOffset);
   a->kq = reinterpret_cast<uint64_t *>(w + q4::kDecodeKqOffset);
   a->eps = eps;

@@ -116,7 +116,8 @@ struct DecodeArgs {
   const int32_t *tok;   // [1] token read on the device
   float *h;             // [2048] hidden state after the last layer (output)
   uint64_t *hq;         // workspace: [2][slots][2048] tagged h between layers
-  uint64_t *mq;         // workspace: [2][copies][max inter] tagged m
+  uint64_t *mq;         // workspace: [2][slots][max inter] tagged m
+  uint64_t *pq;         // workspace: [2048][4][8] tagged down partial sums
   uint32_t *ctl;        // workspace: call counters and error word
   float eps;
   long long spin_ticks; // bound of one wait in wall-clock ticks
@@ -129,28 +130,33 @@ struct DecodeArgs {
   int32_t *tok_out;     // [1] the next token (may be tok)
   uint64_t *kq;         // workspace: [max groups][2] tagged argmax keys
 };
-// Workspace layout (bytes): tagged h (in kDecodeSlots copies) and tagged m
-// of the widest inter (in kDecodeCopies copies), each twice (by layer
-// parity); two tagged words per workgroup for the head's argmax keys; then
-// the control words: one call counter per workgroup (at most
-// kDecodeMaxGroups) and the error word on a 128-byte line of its own (32
-// words before the end).
+// Workspace layout (bytes): tagged h and tagged m of the widest inter (each
+// in kDecodeSlots copies, twice by layer parity); the down product's
+// partial sums (per row, pass and XCD); two tagged words per workgroup for
+// the head's argmax keys; then the control words: one call counter per
+// workgroup (at most kDecodeMaxGroups) and the error word on a 128-byte
+// line of its own (32 words before the end).
 constexpr int kDecodeMaxInter = 8192;
 constexpr int kDecodeMaxGroups = 1024;
 // The decode-block kernels write each tagged value in kDecodeCopies copies;
 // workgroup i reads copy i % kDecodeCopies, so that each cache line is
 // polled by a fraction of the grid only.
 constexpr int kDecodeCopies = 8;
-// The decode-layers kernel hands h on through the L2 of each XCD: the
-// producers write copy kDecodeXcds (device scope); the workgroups of XCD x
-// relay it, a slice each, into copy x, which they then read from their
-// XCD's L2.  m goes in kDecodeCopies copies.
+// The decode-layers kernel hands h and m on through the L2 of each XCD:
+// copy x of each is read by the workgroups of XCD x, copy kDecodeXcds (the
+// device-scope one) by any workgroup that its XCD's copy does not serve.
+// h's producers write copy kDecodeXcds and the workgroups of XCD x relay it
+// into copy x; m's producers write both copies (each XCD produces the m
+// values its own workgroups read).
 constexpr int kDecodeXcds = 8;
 constexpr int kDecodeSlots = kDecodeXcds + 1;
+// The persistent grid: 8 XCDs of 32 workgroups.
+constexpr int kDecodeGroups = 256;
 constexpr size_t kDecodeHqOffset = 0;
 constexpr size_t kDecodeMqOffset = 2 * kDecodeSlots * 8 * 2048;
-constexpr size_t kDecodeKqOffset =
-    kDecodeMqOffset + 2 * kDecodeCopies * 8 * (size_t)kDecodeMaxInter;
+constexpr size_t kDecodePqOffset =
+    kDecodeMqOffset + 2 * kDecodeSlots * 8 * (size_t)kDecodeMaxInter;
+constexpr size_t kDecodeKqOffset = kDecodePqOffset + 8 * (size_t)2048 * 4 * kDecodeXcds;
 constexpr size_t kDecodeCtlOffset = kDecodeKqOffset + 2 * 8 * (size_t)kDecodeMaxGroups;
 constexpr int kDecodeErrorWord = kDecodeMaxGroups + 32;
 constexpr size_t kDecodeWsBytes = kDecodeCtlOffset + 4 * (kDecodeErrorWord + 32);
