@@ -10,42 +10,54 @@
 //   h = embed(tok)                          (8 columns per thread, from the weights)
 //   per layer:  u = rmsq(h, wn)              (once per workgroup, into LDS)
 //               m = SwiGLU([gate; up] u)     (rows in (gate, up) pairs)
-//               h = h + down m               (m staged in LDS per workgroup)
+//               h = h + down m               (by slices, see below)
 //
 // Dataflow instead of grid barriers.  Every value one workgroup hands to
-// another (m of each layer, h between layers) is stored as a 64-bit word:
-// the float's bits and a 32-bit tag naming the call and the stage that
-// produced it, with device-scope stores (the sc1 cache policy: written
-// through to the memory side, where device-scope loads read it), in
-// kDecodeCopies copies of which each workgroup reads one (a cache line that
-// the whole grid polls at once serialises its readers).  A
-// consumer polls the words it needs with device-scope 64-bit loads until
-// each carries the expected tag: the wait and the data arrive in the same
-// load, and no cache write-back, invalidation or barrier is needed.  (On
-// this device a grid barrier built on the memory model's agent-scope
-// fences costs about 10 us, a fence-free one about 4 us; a dependent
-// device-scope load about 2 us.)
+// another is stored as a 64-bit word: the float's bits and a 32-bit tag
+// naming the call and the stage that produced it.  A consumer polls the
+// words it needs until each carries the expected tag: the wait and the data
+// arrive in the same load, and no cache write-back, invalidation or barrier
+// is needed.  (On this device a grid barrier built on the memory model's
+// agent-scope fences costs about 10 us, a fence-free one about 4 us.)  Two
+// kinds of copies: a device-scope one (sc1 stores and loads: written
+// through to the memory side, where device-scope loads read it), and one
+// per XCD, written and polled with non-temporal stores and loads, which the
+// XCD's shared L2 serves (a round trip between two workgroups of one XCD:
+// 0.55 us, against 0.99 us at device scope; across XCDs these words are not
+// seen).  A wait that its XCD's copy does not serve within a bounded time
+// turns to the device-scope copy, so a workgroup not on the XCD the dealing
+// assumes costs time, not correctness.
 //
-// h goes on through the L2 of each XCD instead: its producers write one
-// device-scope copy; on each XCD, each workgroup relays a 64-value slice of
-// it into that XCD's copy (non-temporal stores), and the XCD's workgroups
-// poll that copy with non-temporal loads, which the XCD's shared L2 serves
-// (0.55 us for a round trip between two workgroups of one XCD against 0.99
-// us at device scope).  A workgroup that no relay serves falls back to the
-// device-scope copy after a bounded time.  Chain: 0.366 -> 0.362 ms per
-// token; m, with three times the values per workgroup, was slower this way.
+// The work is dealt by XCD.  The grid is 8 XCDs x 32 workgroups
+// (workgroup w runs on XCD w mod 8 when the grid is dealt out round
+// robin); for x = w mod 8, k = w / 8:
+//   - stage A: wave 8 k + i of XCD x takes (gate, up) pair 2048 q + 256 x +
+//     8 k + i of each 2048-pair block q, so XCD x produces m[2048 q + 256 x,
+//     + 256): groups 32 q + 4 x .. + 3 of every pass q of the down product;
+//   - m of those groups goes through the XCD's copy to its workgroups;
+//   - stage B: workgroup w sums rows [64 k, 64 k + 64) over its XCD's 4
+//     groups of each pass (a node of the balanced tree over the pass's 32
+//     group terms) and publishes those sums (device scope);
+//   - the owner of row r (workgroup r / 8, threads 0..7) gathers the 8
+//     XCDs' sums of each pass in order, forms the passes' tree, adds the
+//     residual and publishes h[r] (device scope);
+//   - on each XCD, each workgroup relays a 64-value slice of h into the
+//     XCD's copy, which the XCD's workgroups read for the next rmsq.
+// Every workgroup used to read all of m at device scope (12.6 MB across
+// the GPU per poll round, 0.3452 ms per token); now the device-scope
+// polls of a layer are the sums (0.4 MB) and h's slices (0.13 MB): 0.3389.
 //
 // Tags: call c (each workgroup counts its calls in a word of its own in the
 // workspace; the grid has the same size in every call, so after a
-// completed call all counters agree) gives m of layer l the tag
-// 64 c + 2 l + 1 and h after layer l the tag 64 c + 2 l + 2 (at most 32
-// layers).  m and h alternate between two buffers each by layer; with that,
-// no word is overwritten while a reader may still need it.  Writing m of
-// layer l + 2 needs h after layer l + 1 complete, and writing h after layer
-// l + 2 needs m of layer l + 2 complete, hence h after layer l + 1; h after
-// layer l + 1 is complete only when every workgroup (each owns at least one
-// row) has finished layer l + 1's down stage, which follows its reads of m
-// of layer l and of h after layer l.
+// completed call all counters agree) gives m of layer l and the down sums
+// of layer l the tag 64 c + 2 l + 1 and h after layer l the tag 64 c +
+// 2 l + 2 (at most 32 layers).  m and h alternate between two buffers each
+// by layer; the sums need one.  No word is overwritten while a reader may
+// still need it: writing the sums of layer l + 1 needs h after layer l
+// complete, hence every owner done with the sums of layer l; writing m of
+// layer l + 2 needs h after layer l + 1 complete, which needs every
+// workgroup's sums of layer l + 1, which follow its reads of m of layer l
+// + 1 and, before them, of layer l; likewise for h.
 //
 // Every wait is bounded by spin_ticks of the wall clock; a wait that runs
 // out sets the error word, and every workgroup leaves at its next wait, so
@@ -53,18 +65,19 @@
 // the launch is resident.
 //
 // The weights of a stage do not depend on the previous one, so every wave
-// loads its next stage's rows ahead: the down row right after the wait for
-// h, the next layer's gate/up rows as early as they can go.  A wave's loads
-// complete in issue order for its wait counter, so a poll issued after a
-// prefetch also waits for the prefetch (for the gate/up rows, about 16 MB
-// across the GPU).  Hence two kinds of waves: waves 0-3 poll h (at a
+// loads its next stage's rows ahead: the down slice right after the wait
+// for h, the next layer's gate/up rows as early as they can go.  A wave's
+// loads complete in issue order for its wait counter, so a poll issued
+// after a prefetch also waits for the prefetch (for the gate/up rows, about
+// 16 MB across the GPU).  Hence two kinds of waves: waves 0-3 poll h (at a
 // layer's start) and load their next gate/up rows right after their gate/up
 // products; waves 4-7 poll m (in stage B) and load theirs only once those
 // polls are done.  No poll then waits behind a fresh prefetch.
 //
 // Every value is computed by the same code as the per-stage kernels (rmsq
 // and SwiGLU from ops_device.h, group terms and row trees from
-// q4mv_device.h), so the result has the bits of the unfused chain.
+// q4mv_device.h), in the same trees, so the result has the bits of the
+// unfused chain.
 #include "decode_device.h"
 #include "tagged_device.h"
 
@@ -76,8 +89,8 @@ namespace {
 using namespace dev;
 using namespace decode;
 
-// Threads of the workgroup that poll m in stage B (the last four waves).
-// Each polls NP chunks of 8 values (NP * 2048 values of m in all).
+// Threads of the workgroup that may poll m in stage B (the last four
+// waves); 64 NP of them poll 4 values each (the XCD's 256 NP values).
 constexpr int kPollThreads = 256;
 
 // e[c] of the embedding row tk (the embed kernel's arithmetic; NaN for a
@@ -119,11 +132,11 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
   const bool owner = t < 8;
   const int orow = 8 * wg + t;
   const int tk = *A.tok;
-  // h goes through the L2 of each XCD: the workgroups wg = x, x + 8, ...
-  // run on XCD x when the grid is dealt out round robin; workgroup wg
-  // relays slice wg / 8 of h from the producers' copy (kDecodeXcds) into
-  // its XCD's copy and reads that copy.  (The same for m, with 3 times the
-  // words, was slower: 0.381 against 0.366 ms per token.)
+  // h goes through the L2 of each XCD: workgroup wg relays slice wg / 8 of
+  // h from the device-scope copy (kDecodeXcds) into its XCD's copy and reads
+  // that copy.  (The earlier dealing relayed m the same way, from producers
+  // on every XCD: 0.381 against 0.366 ms per token without; forming h from
+  // the sums on every XCD instead of the owners: 0.374 against 0.340.)
   const uint32_t xcd = xcd_id();
   const int nslot = nwg / kDecodeXcds;
   const bool relay = nwg % kDecodeXcds == 0 && xcd < (uint32_t)kDecodeXcds && kCols <= kWave * nslot;
