@@ -209,10 +209,11 @@ __device__ __forceinline__ void gu_stage(const DecodeLayer &L, const float *xv, 
 }
 
 // The persistent layers kernel deals the (gate, up) pairs and the down
-// groups by XCD (workgroup w on XCD w mod 8, k = w / 8): wave i = 8 k +
-// wave of XCD x takes pair 2048 q + 256 x + i of every 2048-pair block q,
-// so XCD x produces m[2048 q + 256 x, +256): the 4 groups 32 q + 4 x .. + 3
-// of each block, which are the down groups it reads.
+// groups by XCD (workgroups w = x, x + 8, ... share an XCD; k = w / 8):
+// wave i = 8 k + wave of XCD x takes pair 2048 q + 256 x + i of every
+// 2048-pair block q, so XCD x produces m[2048 q + 256 x, +256): the 4
+// groups 32 q + 4 x .. + 3 of each block, which are the down groups it
+// reads.
 __device__ __forceinline__ void load_gu_strided(const DecodeLayer &L, int inter, int base, int q0,
                                                 int np, int lane, GuBlock &a) {
   const auto qr = buffer(L.gq, 2u * (uint32_t)inter * 1024u);

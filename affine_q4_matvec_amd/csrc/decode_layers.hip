@@ -28,9 +28,9 @@
 // turns to the device-scope copy, so a workgroup not on the XCD the dealing
 // assumes costs time, not correctness.
 //
-// The work is dealt by XCD.  The grid is 8 XCDs x 32 workgroups
-// (workgroup w runs on XCD w mod 8 when the grid is dealt out round
-// robin); for x = w mod 8, k = w / 8:
+// The work is dealt by XCD.  The grid is 8 XCDs x 32 workgroups (the
+// dispatcher deals them round robin: workgroups w = x, x + 8, ... share one
+// XCD); for x = w mod 8, k = w / 8:
 //   - stage A: wave 8 k + i of XCD x takes (gate, up) pair 2048 q + 256 x +
 //     8 k + i of each 2048-pair block q, so XCD x produces m[2048 q + 256 x,
 //     + 256): groups 32 q + 4 x .. + 3 of every pass q of the down product;
@@ -143,9 +143,13 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
   const int slot = wg / kDecodeXcds;
   const int near_copy = relay ? (int)xcd : 0;
   bool use_near = relay;
-  // m through the XCD's L2 when this workgroup runs on the XCD the dealing
-  // assumes (else only the device-scope copy)
-  const bool local_m = relay && (int)xcd == wg % kDecodeXcds;
+  // m through the XCD's L2.  The dispatcher deals the grid to the XCDs
+  // round robin but not always from the first XCD (one launch in a long run
+  // started at XCD 7: every workgroup on XCD (w + 7) mod 8), so the check
+  // is not xcd == wg mod 8: the workgroups w = x, x + 8, ... still share one
+  // XCD, which is all the producers and readers of copy x need.  If they do
+  // not, the readers' waits turn to the device-scope copy after near_ticks.
+  const bool local_m = relay;
   bool use_near_m = local_m;
   // h after layer l - 1 (tag 64 c + 2 l): the relay of this workgroup's
   // slice (wave 0), then 8 values per thread into h8
