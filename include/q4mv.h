@@ -251,7 +251,7 @@ int q4_embed(const q4_mat *w, const int32_t *tok, float *e, void *stream);
  *   h       : device float[2048]: the output (its prior contents are not
  *             read).
  *   ws      : device workspace of q4_decode_layers_ws_bytes() bytes (about
- *             1.4 MB), 16-byte aligned, zero-filled before its first use;
+ *             2.0 MB), 16-byte aligned, zero-filled before its first use;
  *             each call leaves it ready for the next.  Calls that overlap in
  *             time must not share it, and no other kernel should hold the
  *             device's compute units while this one runs.
