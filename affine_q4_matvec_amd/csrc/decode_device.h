@@ -208,51 +208,10 @@ __device__ __forceinline__ void gu_stage(const DecodeLayer &L, const float *xv, 
   swiglu_flush<FAST>(store, batch);
 }
 
-// The persistent layers kernel deals the (gate, up) pairs and the down
-// groups by XCD (workgroups w = x, x + 8, ... share an XCD; k = w / 8):
-// wave i = 8 k + wave of XCD x takes pair 2048 q + 256 x + i of every
-// 2048-pair block q, so XCD x produces m[2048 q + 256 x, +256): the 4
-// groups 32 q + 4 x .. + 3 of each block, which are the down groups it
-// reads.
-__device__ __forceinline__ void load_gu_strided(const DecodeLayer &L, int inter, int base, int q0,
-                                                int np, int lane, GuBlock &a) {
-  const auto qr = buffer(L.gq, 2u * (uint32_t)inter * 1024u);
-  const auto sr = buffer(L.gs, 2u * (uint32_t)inter * 128u);
-  const auto br = buffer(L.gb, 2u * (uint32_t)inter * 128u);
-#pragma unroll
-  for (int j = 0; j < kGuPairs; ++j) {
-    if (j < np) {
-      const uint32_t row = 2u * (2048u * (uint32_t)(q0 + j) + (uint32_t)base);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        a.cw[2 * j + h] = load_codes(qr, 16u * lane, (row + h) * 1024u);
-        a.sv[2 * j + h] = load_f32(sr, 4u * (lane >> 1), (row + h) * 128u);
-        a.bv[2 * j + h] = load_f32(br, 4u * (lane >> 1), (row + h) * 128u);
-      }
-    }
-  }
-}
-
-// Stage A over the wave's np pairs 2048 q + base (q < np), in blocks of
-// kGuPairs; `a` holds the first block's loads.  The store receives q.
-template <bool FAST, bool PAIRS, class Store>
-__device__ __forceinline__ void gu_stage_strided(const DecodeLayer &L, int inter, const float *xv,
-                                                 float xsv, int lane, int base, int np_all,
-                                                 GuBlock &a, const Store &store) {
-  const int negz = neg_zero_reg();
-  SwigluBatch batch;
-  for (int q = 0; q < np_all; q += kGuPairs) {
-    const int np = min(kGuPairs, np_all - q);
-    if (q != 0) load_gu_strided(L, inter, base, q, np, lane, a);
-    gu_block<FAST, PAIRS>(a, xv, xsv, lane, q, np, store, batch, negz);
-  }
-  swiglu_flush<FAST>(store, batch);
-}
-
 // Stage B's slice of the down product: lane l of a wave covers row `row`
-// (8 rows per wave, 8 lanes per row) and, in pass j < NP, half l % 2 of
-// group 32 j + 4 x + (l / 2) % 4: the 8 lanes of a row read the 128
-// contiguous bytes of its 4 groups.
+// (8 rows per wave, 8 lanes per row) and, in local pass j < NP, half l % 2
+// of group 4 (NP x + j) + (l / 2) % 4: the 8 lanes of a row read the 128
+// contiguous bytes of its 4 groups, and the XCD's NP passes are contiguous.
 template <int NP>
 __device__ __forceinline__ void load_down_slice(const DecodeLayer &L, int row, int x, int lane,
                                                 DownRow<NP> &d) {
@@ -261,18 +220,19 @@ __device__ __forceinline__ void load_down_slice(const DecodeLayer &L, int row, i
   const auto br = buffer(L.db, 2048u * NP * 128u);
   const uint32_t vq = (uint32_t)row * (NP * 1024u) + 16u * (uint32_t)(lane & 7);
   const uint32_t vs = (uint32_t)row * (NP * 128u) + 4u * (uint32_t)((lane >> 1) & 3);
+  const uint32_t n0 = (uint32_t)(NP * x);
 #pragma unroll
   for (int j = 0; j < NP; ++j) {
-    d.cw[j] = load_codes(qr, vq, 1024u * j + 128u * (uint32_t)x);
-    d.sv[j] = load_f32(sr, vs, 128u * j + 16u * (uint32_t)x);
-    d.bv[j] = load_f32(br, vs, 128u * j + 16u * (uint32_t)x);
+    d.cw[j] = load_codes(qr, vq, 128u * (n0 + j));
+    d.sv[j] = load_f32(sr, vs, 16u * (n0 + j));
+    d.bv[j] = load_f32(br, vs, 16u * (n0 + j));
   }
 }
 
-// The slice's sums: for each pass j, T over the row's 4 group terms (the
-// lane pairs of the row's 8 lanes: xor 2 within quads, then the mirror
-// within 8 lanes), a node of the balanced tree over the pass's 32 groups;
-// every lane of the row ends with it.  m (local group 4 j + g: values
+// The slice's sums: for each local pass j, T over the row's 4 group terms
+// (the lane pairs of the row's 8 lanes: xor 2 within quads, then the mirror
+// within 8 lanes), a node of the balanced tree over the 32 groups of the
+// pass holding them; every lane of the row ends with it.  m (local group 4 j + g: values
 // [256 j + 64 g, +64)) and its group sums are in LDS.
 template <int NP, bool FAST, bool PAIRS>
 __device__ __forceinline__ void down_slice(const Lds<NP> &S, int lane, const DownRow<NP> &d,

@@ -31,21 +31,26 @@
 // The work is dealt by XCD.  The grid is 8 XCDs x 32 workgroups (the
 // dispatcher deals them round robin: workgroups w = x, x + 8, ... share one
 // XCD); for x = w mod 8, k = w / 8:
-//   - stage A: wave 8 k + i of XCD x takes (gate, up) pair 2048 q + 256 x +
-//     8 k + i of each 2048-pair block q, so XCD x produces m[2048 q + 256 x,
-//     + 256): groups 32 q + 4 x .. + 3 of every pass q of the down product;
+//   - stage A: wave 8 k + i of XCD x takes (gate, up) pairs [256 NP x +
+//     NP (8 k + i), + NP), so XCD x produces m[256 NP x, + 256 NP): the
+//     down product's column groups [4 NP x, 4 NP x + 4 NP);
 //   - m of those groups goes through the XCD's copy to its workgroups;
-//   - stage B: workgroup w sums rows [64 k, 64 k + 64) over its XCD's 4
-//     groups of each pass (a node of the balanced tree over the pass's 32
-//     group terms) and publishes those sums (device scope);
+//   - stage B: workgroup w sums rows [64 k, 64 k + 64) over each 4 of its
+//     XCD's groups (node NP x + j of the row's 8 NP nodes: the balanced
+//     tree over the 32 group terms of pass n / 8 has node n % 8 of that
+//     pass as a subtree) and publishes those sums (device scope);
 //   - the owner of row r (workgroup r / 8, threads 0..7) gathers the 8
-//     XCDs' sums of each pass in order, forms the passes' tree, adds the
+//     node sums of each pass in order, forms the passes' tree, adds the
 //     residual and publishes h[r] (device scope);
 //   - on each XCD, each workgroup relays a 64-value slice of h into the
 //     XCD's copy, which the XCD's workgroups read for the next rmsq.
 // Every workgroup used to read all of m at device scope (12.6 MB across
 // the GPU per poll round, 0.3452 ms per token); now the device-scope
 // polls of a layer are the sums (0.4 MB) and h's slices (0.13 MB): 0.3389.
+// Each XCD's groups are contiguous, so its share of a down row's codes is
+// whole 128-byte lines and its scales and biases span 1 or 2 lines; with 4
+// groups of every pass instead, every XCD read 16 bytes of every line of
+// them, and the 8 L2s fetched 1.5x the weights' bytes.
 //
 // Tags: call c (each workgroup counts its calls in a word of its own in the
 // workspace; the grid has the same size in every call, so after a
@@ -123,11 +128,11 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
   const bool mine = 8 * t < kCols;  // threads 0..255 own 8 values of h each
   // the (gate, up) pairs and the down groups by XCD (the grid has 8 x 32
   // workgroups): XCD x = wg mod 8, k = wg / 8; wave 8 k + wave of XCD x
-  // takes pairs 2048 q + base (q < NP); the workgroup's down slice is rows
-  // [64 k, 64 k + 64) of groups 32 q + 4 x .. + 3; it owns rows [8 wg, 8 wg
+  // takes pairs [pb, pb + NP); the workgroup's down slice is rows [64 k,
+  // 64 k + 64) of groups [4 NP x, 4 NP x + 4 NP); it owns rows [8 wg, 8 wg
   // + 8) (threads 0..7: the residual, the pass sums' gather, h)
   const int x = wg % kDecodeXcds, k = wg / kDecodeXcds;
-  const int base = 256 * x + 8 * k + wave;
+  const int pb = 256 * NP * x + NP * (8 * k + wave);
   const int drow = 64 * k + 8 * wave + lane / 8;
   const bool owner = t < 8;
   const int orow = 8 * wg + t;
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
 
   GuBlock a;
   DownRow<NP> d;
-  load_gu_strided(A.layer[0], A.inter, base, 0, min(kGuPairs, NP), lane, a);
+  load_gu(A.layer[0], pb, min(kGuPairs, NP), lane, a);
   // the head (q4_decode_token): blocks of 4 rows gw, gw + stride, ...; the
   // first is loaded during the last layer, into the registers of the gate/up
   // block (free by then: there is no next layer)
@@ -221,25 +226,24 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
       float xv[32];
       const float xsv = load_rmsq_x(S, lane, rq != 0, xv);
       const uint32_t tag = tag0 + 2 * l + 1;
-      // m[2048 q + base] to the XCD's copy (non-temporal: its L2) and the
-      // device-scope one
-      const auto store_m = [mfar, mnear, tag, base, local_m](int q, float v) {
-        const int i = 2048 * q + base;
+      // m[i] to the XCD's copy (non-temporal: its L2) and the device-scope
+      // one
+      const auto store_m = [mfar, mnear, tag, local_m](int i, float v) {
         if (local_m)
           __builtin_nontemporal_store(((uint64_t)tag << 32) | __float_as_uint(v), mnear + i);
         store_tagged(mfar + i, v, tag);
       };
       if (rq != 0)
-        gu_stage_strided<FAST, true>(L, A.inter, xv, xsv, lane, base, NP, a, store_m);
+        gu_stage<FAST, true>(L, xv, xsv, lane, pb, pb + NP, a, store_m);
       else
-        gu_stage_strided<FAST, false>(L, A.inter, xv, xsv, lane, base, NP, a, store_m);
+        gu_stage<FAST, false>(L, xv, xsv, lane, pb, pb + NP, a, store_m);
     }
 
     // the next layer's gate/up rows, for the waves that do not poll m (they
     // poll h at the next layer's start, long after these have landed)
     const bool poller = t >= kThreads - kPollThreads;
     if (!poller && l + 1 < A.nlayers)
-      load_gu_strided(A.layer[l + 1], A.inter, base, 0, min(kGuPairs, NP), lane, a);
+      load_gu(A.layer[l + 1], pb, min(kGuPairs, NP), lane, a);
     if (!poller && l + 1 == A.nlayers && head) head_load_into(A, gw, lane, a);
     issue_order();
     const uint32_t tag_m = tag0 + 2 * l + 1;
@@ -247,8 +251,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
     // ---- stage B: this XCD's m (its workgroup's 4 NP groups) and their
     // group sums into LDS; the slice's pass sums to the rows' owners; h =
     // h + down m for the owned rows.  Poller thread p < 64 NP takes local
-    // values [4 p, 4 p + 4): block q = p / 64, m[2048 q + 256 x + 4 (p %
-    // 64) ..], group p / 16.  The pollers are waves without fresh loads in
+    // values [4 p, 4 p + 4): m[256 NP x + 4 p ..], local group p / 16.  The pollers are waves without fresh loads in
     // flight: a wave's loads complete in issue order for its wait counter,
     // so a poll behind a prefetch of the GPU's next gate/up rows would wait
     // for that prefetch to land.
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
     if (poller) {
       if (mpoll) {
         const int lv = 4 * p;
-        const int i = 2048 * (lv / 256) + 256 * x + lv % 256;
+        const int i = 256 * NP * x + lv;
         float v[4];
         if (!poll_tagged_near<4>(mnear + i, mfar + i, tag_m, v, err, use_near_m, A.near_ticks,
                                  A.spin_ticks))
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
       // this wave's gate/up rows of the next layer (or its first head
       // blocks after the last layer), now that its polls are done
       if (l + 1 < A.nlayers)
-        load_gu_strided(A.layer[l + 1], A.inter, base, 0, min(kGuPairs, NP), lane, a);
+        load_gu(A.layer[l + 1], pb, min(kGuPairs, NP), lane, a);
       if (l + 1 == A.nlayers && head) head_load_into(A, gw, lane, a);
       issue_order();
     }
@@ -299,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
       // workgroup, this one included, has done this layer's down slice)
       if (mpoll) {
         const int lv = 4 * p;
-        const int i = 2048 * (lv / 256) + 256 * x + lv % 256;
+        const int i = 256 * NP * x + lv;
         float v[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
@@ -310,7 +313,8 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
       __syncthreads();
     }
     {
-      // the slice: the row's 4-group sums of every pass, to the row's owner
+      // the slice: the row's 4-group sums (nodes NP x + j of the row's 8 NP
+      // nodes), to the row's owner
       float sj[NP];
       if (pairs)
         down_slice<NP, FAST, true>(S, lane, d, sj);
@@ -319,11 +323,11 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
       if ((lane & 7) == 0)
 #pragma unroll
         for (int j = 0; j < NP; ++j)
-          store_tagged(A.pq + ((size_t)drow * NP + j) * kDecodeXcds + x, sj[j], tag_m);
+          store_tagged(A.pq + (size_t)drow * (8 * NP) + NP * x + j, sj[j], tag_m);
     }
     if (wave == 0) {
-      // thread t < 8 NP: owned row 8 wg + t % 8, pass t / 8: the 8 XCDs'
-      // sums in order (the balanced tree over the pass's 32 group terms)
+      // thread t < 8 NP: owned row 8 wg + t % 8, pass t / 8: the pass's 8
+      // node sums in order (the balanced tree over its 32 group terms)
       bool okp = true;
       if (t < 8 * NP) {
         float v8[8];
