@@ -32,6 +32,7 @@ struct alignas(16) Lds {
   uint32_t flag[2];                 // stage B: a wait gave up / some |m| >= 2^118
   alignas(16) uint32_t wflag[2][kWaves];  // workgroup_rmsq: per wave, a wait gave up / a large x
   float own[8 * 4];                 // stage B: the owned rows' pass sums
+  float ownw[8 * 8 * 4];            // stage B: the owned rows' node sums
 };
 
 // Whether `p` holds in any thread of the workgroup, with one barrier: each

@@ -157,7 +157,11 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
   const bool local_m = relay;
   bool use_near_m = local_m;
   // h after layer l - 1 (tag 64 c + 2 l): the relay of this workgroup's
-  // slice (wave 0), then 8 values per thread into h8
+  // slice (wave 0); then every thread polls words t + 512 k (each wave's
+  // load is 64 consecutive words, a few cache lines; polling 8 consecutive
+  // words per thread made each load touch a line per lane) into S.x, and
+  // after a barrier threads 0..255 take their 8 consecutive values into h8.
+  // Every thread of the workgroup calls it; S.x must be free.
   const auto poll_h = [&](int l, float *h8) {
     const uint32_t th = tag0 + 2 * l;
     uint64_t *hb = A.hq + (size_t)((l - 1) & 1) * kDecodeSlots * kCols;
@@ -168,8 +172,20 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
       if (i < (slot + 1) * kCols / nslot)
         ok = relay_word(far, hb + near_copy * kCols, i, th, err, A.spin_ticks);
     }
-    return ok && poll_tagged_near<8>(hb + near_copy * kCols + 8 * t, far + 8 * t, th, h8, err,
-                                     use_near, A.near_ticks, A.spin_ticks);
+    static_assert(kCols == 4 * kThreads, "4 words of h per thread");
+    float hv[4];
+    ok = ok && poll_tagged_near<4, kThreads>(hb + near_copy * kCols + t, far + t, th, hv, err,
+                                             use_near, A.near_ticks, A.spin_ticks);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) S.x[t + kThreads * k] = hv[k];
+    __syncthreads();
+    if (mine) {
+      const float4 *src = reinterpret_cast<const float4 *>(S.x + 8 * t);
+      const float4 a0 = src[0], a1 = src[1];
+      h8[0] = a0.x; h8[1] = a0.y; h8[2] = a0.z; h8[3] = a0.w;
+      h8[4] = a1.x; h8[5] = a1.y; h8[6] = a1.z; h8[7] = a1.w;
+    }
+    return ok;
   };
 
   GuBlock a;
@@ -214,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
           h8[i] = valid ? sq + bg : __builtin_nanf("");
         }
       }
-    } else if (mine) {
+    } else {
       // h after the previous layer, 8 values per thread
       ok = poll_h(l, h8);
     }
@@ -326,13 +342,23 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
           store_tagged(A.pq + (size_t)drow * (8 * NP) + NP * x + j, sj[j], tag_m);
     }
     if (wave == 0) {
-      // thread t < 8 NP: owned row 8 wg + t % 8, pass t / 8: the pass's 8
-      // node sums in order (the balanced tree over its 32 group terms)
-      bool okp = true;
+      // the owned rows' 64 NP node sums (rows [8 wg, 8 wg + 8) x 8 NP
+      // nodes, contiguous): lane l polls words l + 64 i (coalesced) into
+      // S.ownw; then thread t < 8 NP, for owned row 8 wg + t % 8 and pass
+      // t / 8, reads the pass's 8 node sums in order (the balanced tree over
+      // its 32 group terms).  One wave writes and reads S.ownw: its LDS
+      // accesses are done in order.
+      float pv[NP];
+      const bool okp = poll_tagged<NP, kWave>(A.pq + (size_t)wg * (64 * NP) + lane, tag_m, pv,
+                                               err, A.spin_ticks);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) S.ownw[lane + kWave * i] = pv[i];
+      issue_order();
       if (t < 8 * NP) {
+        const float *q = S.ownw + (t & 7) * (8 * NP) + 8 * (t >> 3);
         float v8[8];
-        okp = poll_tagged<8>(A.pq + ((size_t)(8 * wg + (t & 7)) * NP + (t >> 3)) * kDecodeXcds,
-                             tag_m, v8, err, A.spin_ticks);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v8[k] = q[k];
         S.own[t] = ops::tree8(v8);
       }
       const bool all_ok = __all(okp);
@@ -364,8 +390,8 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
       const float4 w0 = wp[0], w1 = wp[1];
       w8[0] = w0.x; w8[1] = w0.y; w8[2] = w0.z; w8[3] = w0.w;
       w8[4] = w1.x; w8[5] = w1.y; w8[6] = w1.z; w8[7] = w1.w;
-      ok = poll_h(L, h8);
     }
+    ok = poll_h(L, h8);
     // the second block's loads, after the wait for h (a poll issued behind
     // them would wait for them too)
     HeadBlock hb0, hb1;

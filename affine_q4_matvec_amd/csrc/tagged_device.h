@@ -27,10 +27,12 @@ __device__ __forceinline__ void store_tagged(uint64_t *p, float v, uint32_t tag)
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Polls the N tagged words at p until each carries `tag`; their floats go to
-// v.  False when the wait ran out (the error word is then set) or another
-// wait did.
-template <int N>
+// Polls the N tagged words p[STRIDE k] (k < N) until each carries `tag`;
+// their floats go to v.  False when the wait ran out (the error word is
+// then set) or another wait did.  (With STRIDE the wave's width, a wave's
+// load covers 64 consecutive words: a few cache lines per load instead of
+// up to one per lane.)
+template <int N, int STRIDE = 1>
 __device__ __forceinline__ bool poll_tagged(const uint64_t *p, uint32_t tag, float *v,
                                             uint32_t *err, long long spin_ticks) {
   const long long t0 = wall_clock64();
@@ -38,7 +40,8 @@ __device__ __forceinline__ bool poll_tagged(const uint64_t *p, uint32_t tag, flo
     bool ready = true;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-      const uint64_t w = __hip_atomic_load(p + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t w =
+          __hip_atomic_load(p + STRIDE * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       v[k] = __uint_as_float((uint32_t)w);
       ready &= (uint32_t)(w >> 32) == tag;
     }
@@ -80,13 +83,13 @@ __device__ __forceinline__ bool relay_word(const uint64_t *far, uint64_t *near, 
   return true;
 }
 
-// Polls the N words at near (this XCD's copy) until each carries `tag`,
-// for at most near_ticks, then the same words at far (the producers' copy)
-// as poll_tagged does; with use_near false (or once near_ticks has run out,
-// which clears it), only far.  A relay that never comes (a workgroup not
-// where the relay expects it) costs time, not correctness: both copies
-// hold the same values under the same tag.
-template <int N>
+// Polls the N words near[STRIDE k] (this XCD's copy) until each carries
+// `tag`, for at most near_ticks, then the same words at far (the
+// producers' copy) as poll_tagged does; with use_near false (or once
+// near_ticks has run out, which clears it), only far.  A relay that never
+// comes (a workgroup not where the relay expects it) costs time, not
+// correctness: both copies hold the same values under the same tag.
+template <int N, int STRIDE = 1>
 __device__ __forceinline__ bool poll_tagged_near(const uint64_t *near, const uint64_t *far,
                                                  uint32_t tag, float *v, uint32_t *err,
                                                  bool &use_near, long long near_ticks,
@@ -97,7 +100,7 @@ __device__ __forceinline__ bool poll_tagged_near(const uint64_t *near, const uin
       bool ready = true;
 #pragma unroll
       for (int k = 0; k < N; ++k) {
-        const uint64_t w = __builtin_nontemporal_load(near + k);
+        const uint64_t w = __builtin_nontemporal_load(near + STRIDE * k);
         v[k] = __uint_as_float((uint32_t)w);
         ready &= (uint32_t)(w >> 32) == tag;
       }
@@ -110,7 +113,7 @@ __device__ __forceinline__ bool poll_tagged_near(const uint64_t *near, const uin
       __builtin_amdgcn_s_sleep(1);
     }
   }
-  return poll_tagged<N>(far, tag, v, err, spin_ticks);
+  return poll_tagged<N, STRIDE>(far, tag, v, err, spin_ticks);
 }
 
 // Polls `groups` (at most M) groups of N consecutive words, group g at
