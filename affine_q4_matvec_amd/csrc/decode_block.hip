@@ -112,38 +112,27 @@ struct AttnLds {
   float rot[2][kD];         // rotated q, k
   float s[kBlockSpan];      // scores of the span
   float e[kBlockSpan];      // weights of the span
-  float part[16][kD];       // value sums over 16 positions
+  alignas(16) float part[16][kD];  // value sums over 16 positions (stage B: m as polled)
   float sw[kBlockMaxSpans][kD];  // the spans' value sums (span 0 of a head)
   float sz[kBlockMaxSpans];      // the spans' weight sums
   float wsum[4];            // weight sums over 64 positions
   float m;                  // largest score
 };
 
-// Stages m (or o) into LDS for a down (or O) row: `vals` are this thread's
-// chunks (8 values each, chunk c of the padded layout), the group sums
-// are written by the caller.  Returns whether the pair decode may be used.
-template <int NP>
-__device__ __forceinline__ bool stage_rows_input(Lds<NP> &L, const float (*vals)[8], int nchunks) {
+// Stages o into LDS for the O rows (the padded layout, scaled for the
+// pair decode unless some |o| >= 2^118; the group sums are written by the
+// caller): v[k] is value t + 512 k of thread t.  Returns whether the pair
+// decode may be used.
+__device__ __forceinline__ bool stage_o_input(Lds<1> &L, const float *v) {
   bool large = false;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int c = threadIdx.x + r * kThreads;
-    if (c < nchunks)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) large |= !(__builtin_fabsf(vals[r][k]) < 0x1p118f);
-  }
+  for (int k = 0; k < 4; ++k) large |= !(__builtin_fabsf(v[k]) < 0x1p118f);
   const bool pairs = !__syncthreads_or(large);
   const float scale = pairs ? 1.0f / fp8_unit() : 1.0f;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int c = threadIdx.x + r * kThreads;
-    if (c < nchunks) {
-      float4 *dst = reinterpret_cast<float4 *>(L.x + 8 * c + 4 * (c >> 2));
-      dst[0] = make_float4(vals[r][0] * scale, vals[r][1] * scale, vals[r][2] * scale,
-                           vals[r][3] * scale);
-      dst[1] = make_float4(vals[r][4] * scale, vals[r][5] * scale, vals[r][6] * scale,
-                           vals[r][7] * scale);
-    }
+  for (int k = 0; k < 4; ++k) {
+    const int c = threadIdx.x + kThreads * k;
+    L.x[c + 4 * (c >> 5)] = v[k] * scale;
   }
   return pairs;
 }
@@ -264,14 +253,17 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
       if (l == 0) {
         load_x_values(A.h + 32 * lane, true, hv);
       } else {
-        bool ok = true;
-        if (mine) {
-          float h8[8];
-          ok = poll_tagged<8>(A.hb + (size_t)copy * kCols + 8 * t, stage_tag(call, l - 1) + 5, h8,
-                              err, A.spin_ticks);
-          float4 *dst = reinterpret_cast<float4 *>(SO.x + 8 * t + 4 * (t >> 2));
-          dst[0] = make_float4(h8[0], h8[1], h8[2], h8[3]);
-          dst[1] = make_float4(h8[4], h8[5], h8[6], h8[7]);
+        // every thread polls words t + 512 k (each wave's load: 64
+        // consecutive words, a few cache lines) into the padded layout
+        static_assert(kCols == 4 * kThreads, "4 words of h per thread");
+        float h4[4];
+        const bool ok = poll_tagged<4, kThreads>(A.hb + (size_t)copy * kCols + t,
+                                                 stage_tag(call, l - 1) + 5, h4, err,
+                                                 A.spin_ticks);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int c = t + kThreads * k;
+          SO.x[c + 4 * (c >> 5)] = h4[k];
         }
         if (!__syncthreads_and(ok)) return;
         load_x_values(SO.x + kChunkStride * lane, true, hv);
@@ -551,32 +543,25 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
     if (pb < pe) load_gu(Y.mlp, pb, min(kGuPairs, pe - pb), lane, a);
     issue_order();
     {
-      float ov[2][8] = {};
       // the wait for the attention stage is long: wave 0 alone polls (the
       // group sums of every head) until it ends, then every thread takes its
       // words
       bool ok = wave != 0 || await_words(A.ov + (size_t)copy * kBlockORows + kCols, 2 * kHeads,
                                          tag + 2, err, A.spin_ticks);
       if (!__syncthreads_and(ok)) return;
-      if (mine)
-        ok = poll_tagged<8>(A.ov + (size_t)copy * kBlockORows + 8 * t, tag + 2, ov[0], err,
-                            A.spin_ticks);
-      if (t >= 256 && t < 260)  // the 32 group sums, 8 per thread
-        ok = poll_tagged<8>(A.ov + (size_t)copy * kBlockORows + kCols + 8 * (t - 256), tag + 2,
-                            ov[1], err, A.spin_ticks);
-      if (!__syncthreads_and(ok)) return;
-      if (t >= 256 && t < 260)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) SO.xs[8 * (t - 256) + k] = ov[1][k];
-      // stage_rows_input looks at chunks t and t + 512 only: chunk t is this
-      // thread's 8 values of o
-      float vals[2][8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        vals[0][k] = mine ? ov[0][k] : 0.0f;
-        vals[1][k] = 0.0f;
+      // every thread polls words t + 512 k of o (lane-contiguous loads);
+      // threads t < 32 also the group sum t (the others poll word t again
+      // in its place)
+      float o5[5];
+      {
+        const int off[5] = {t, t + kThreads, t + 2 * kThreads, t + 3 * kThreads,
+                            t < 2 * kHeads ? kCols + t : t};
+        ok = poll_tagged_at<5>(A.ov + (size_t)copy * kBlockORows, off, tag + 2, o5, err,
+                               A.spin_ticks);
       }
-      const bool pairs = stage_rows_input<1>(SO, vals, kCols / 8);
+      if (!__syncthreads_and(ok)) return;
+      if (t < 2 * kHeads) SO.xs[t] = o5[4];
+      const bool pairs = stage_o_input(SO, o5);
       __syncthreads();
       if (has_row) {
         Lds<1> &L = SO;
@@ -600,13 +585,27 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
       // x = rmsq(h, wn) over the workgroup: threads 0..255 take 8 columns
       bool ok = true;
       float h8[8] = {}, w8[8] = {};
-      if (mine) {
-        load8(Y.mlp.wn + 8 * t, w8);
-        ok = poll_tagged<8>(A.hv + (size_t)copy * kCols + 8 * t, tag + 3, h8, err, A.spin_ticks);
+      // every thread polls words t + 512 k of h into S.x (free: its last
+      // readers, the previous layer's down rows, are past several
+      // barriers); after a barrier threads 0..255 take their 8 values
+      if (mine) load8(Y.mlp.wn + 8 * t, w8);
+      {
+        float h4[4];
+        ok = poll_tagged<4, kThreads>(A.hv + (size_t)copy * kCols + t, tag + 3, h4, err,
+                                      A.spin_ticks);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) S.x[t + kThreads * k] = h4[k];
       }
       issue_order();
       DownRow<NP> d{};
       if (has_row) load_down<NP>(Y.mlp, row, lane, d);
+      __syncthreads();
+      if (mine) {
+        const float4 *src = reinterpret_cast<const float4 *>(S.x + 8 * t);
+        const float4 a0 = src[0], a1 = src[1];
+        h8[0] = a0.x; h8[1] = a0.y; h8[2] = a0.z; h8[3] = a0.w;
+        h8[4] = a1.x; h8[5] = a1.y; h8[6] = a1.z; h8[7] = a1.w;
+      }
       const int rq = workgroup_rmsq(S, h8, w8, A.eps, ok);
       if (rq < 0) return;
       {
@@ -648,15 +647,32 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
         const int p = t - (kThreads - kPollThreads);
         bool large = false;
         const float scale = 1.0f / fp8_unit();
+        // the poller wave's 64 chunks of a round (512 consecutive words)
+        // polled lane-contiguous (words lane + 64 k: 4 cache lines per
+        // load), then through the wave's slice of T.part (free in this
+        // stage; one wave writes and reads it, and its LDS accesses are done
+        // in order) to chunk c = 8 consecutive values per lane
+        float *stg = &T.part[0][0] + 512 * (p / kWave);
+        static_assert(sizeof(T.part) >= 4 * 512 * sizeof(float), "4 poller waves");
         // one chunk at a time: polling several in the same rounds multiplies
         // the polled traffic while the wait lasts
 #pragma unroll 1
         for (int r = 0; r < kPerPoller; ++r) {
           const int c = p + r * kPollThreads;
           float xm[8];
-          if (!poll_tagged<8>(mcopy + 8 * c, tag + 4, xm, err, A.spin_ticks)) {
+          if (!poll_tagged<8, kWave>(mcopy + 2048 * r + 512 * (p / kWave) + lane, tag + 4, xm,
+                                     err, A.spin_ticks)) {
             S.flag[0] = 1u;
             break;
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) stg[lane + kWave * k] = xm[k];
+          issue_order();
+          {
+            const float4 *src = reinterpret_cast<const float4 *>(stg + 8 * lane);
+            const float4 a0 = src[0], a1 = src[1];
+            xm[0] = a0.x; xm[1] = a0.y; xm[2] = a0.z; xm[3] = a0.w;
+            xm[4] = a1.x; xm[5] = a1.y; xm[6] = a1.z; xm[7] = a1.w;
           }
           // group sums: T over each chunk, then over 8 chunks by a butterfly
           const float gs = ops::lane_sum8(ops::tree8(xm));

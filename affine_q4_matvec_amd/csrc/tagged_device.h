@@ -55,6 +55,32 @@ __device__ __forceinline__ bool poll_tagged(const uint64_t *p, uint32_t tag, flo
   }
 }
 
+// Polls the N tagged words p[off[k]] until each carries `tag`, as
+// poll_tagged does.
+template <int N>
+__device__ __forceinline__ bool poll_tagged_at(const uint64_t *p, const int (&off)[N],
+                                               uint32_t tag, float *v, uint32_t *err,
+                                               long long spin_ticks) {
+  const long long t0 = wall_clock64();
+  for (int it = 1;; ++it) {
+    bool ready = true;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const uint64_t w =
+          __hip_atomic_load(p + off[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      v[k] = __uint_as_float((uint32_t)w);
+      ready &= (uint32_t)(w >> 32) == tag;
+    }
+    if (ready) return true;
+    if ((it & 63) == 0 && load_word(err) != 0) return false;
+    if (wall_clock64() - t0 > spin_ticks) {
+      store_word(err, 1u);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 // A hand-off through the L2 of each XCD.  The producers' words (device
 // scope) are read by one workgroup per XCD only, which stores them again
 // into its XCD's copy; the other workgroups of that XCD poll that copy.
