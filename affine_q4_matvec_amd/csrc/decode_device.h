@@ -51,44 +51,50 @@ __device__ __forceinline__ bool workgroup_any(uint32_t *slot, bool p) {
 
 // rmsq of h over the workgroup, with the arithmetic and tree of the rmsq
 // kernel (ops_device.h), so the bits of every wave forming it alone:
-// threads 0..255 hold h and the weights of columns [8t, 8t+8) (h8, w8);
-// the sum of squares goes over the 64 lanes of each wave, then every
-// thread adds the 8 wave sums in the balanced tree.  x goes to L.x in the
-// row stages' padded layout, its group sums to L.xs.  Returns -1 when `ok`
-// is false in any thread (a wait gave up), else 1 when every |x| < 2^118
-// (the pair decode may be used; the callers scale x as they load it), else
-// 0.  Two workgroup barriers; L must be free (every earlier reader past a
-// barrier).
+// threads 0..255 (waves 0..3) hold h and the weights of columns [8t, 8t+8)
+// (h8, w8); the sum of squares goes over the 64 lanes of each wave, then
+// the 4 wave sums in a balanced tree: the balanced tree over the 2048
+// squares in index order.  Waves 4..7 only vote: each shares a SIMD with
+// one of waves 0..3, and when they formed the same sums (over -0 in place
+// of h: four -0 wave sums more in the tree, which change nothing) their
+// copy of the arithmetic delayed both at the barriers.  x goes to L.x in the row stages' padded layout, its group sums
+// to L.xs.  Returns -1 when `ok` is false in any thread (a wait gave up),
+// else 1 when every |x| < 2^118 (the pair decode may be used; the callers
+// scale x as they load it), else 0.  Two workgroup barriers; L must be
+// free (every earlier reader past a barrier).
 template <int NP>
 __device__ __forceinline__ int workgroup_rmsq(Lds<NP> &L, const float *h8, const float *w8,
                                               float eps, bool ok) {
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1), wave = t / kWave;
-  const bool mine = 8 * t < kCols;
-  float v[8];
+  constexpr int kHWaves = kCols / (8 * kWave);
+  static_assert(kHWaves == 4, "the tree over the wave sums");
+  const bool hw = wave < kHWaves;  // wave-uniform: the 8 t < kCols threads
+  if (hw) {
+    float v[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) v[k] = mine ? h8[k] * h8[k] : kNegZero;
-  const float s = ops::lane_sum64(ops::tree8(v));
-  if (lane == 0) L.red[wave] = s;
-  if (workgroup_any(L.wflag[0], !ok)) return -1;
-  const float *r = L.red;
-  static_assert(kWaves == 8, "the tree over the wave sums");
-  const float ss = ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
-  const float rho = ops::rmsq_rho_from_ss(ss, kCols, eps);
-  float u[8];
-  bool large = false;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    u[k] = mine ? ops::rmsq_value(h8[k], rho, w8[k]) : kNegZero;
-    large |= mine && !(__builtin_fabsf(u[k]) < 0x1p118f);
+    for (int k = 0; k < 8; ++k) v[k] = h8[k] * h8[k];
+    const float s = ops::lane_sum64(ops::tree8(v));
+    if (lane == 0) L.red[wave] = s;
   }
-  if (mine) {
+  if (workgroup_any(L.wflag[0], !ok)) return -1;
+  bool large = false;
+  if (hw) {
+    const float *r = L.red;
+    const float ss = (r[0] + r[1]) + (r[2] + r[3]);
+    const float rho = ops::rmsq_rho_from_ss(ss, kCols, eps);
+    float u[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      u[k] = ops::rmsq_value(h8[k], rho, w8[k]);
+      large |= !(__builtin_fabsf(u[k]) < 0x1p118f);
+    }
     float4 *dst = reinterpret_cast<float4 *>(L.x + 8 * t + 4 * (t >> 2));
     dst[0] = make_float4(u[0], u[1], u[2], u[3]);
     dst[1] = make_float4(u[4], u[5], u[6], u[7]);
+    const float g = ops::lane_sum8(ops::tree8(u));
+    if ((t & 7) == 0) L.xs[t >> 3] = g;
   }
-  const float g = ops::lane_sum8(ops::tree8(u));
-  if (mine && (t & 7) == 0) L.xs[t >> 3] = g;
   return workgroup_any(L.wflag[1], large) ? 0 : 1;
 }
 
