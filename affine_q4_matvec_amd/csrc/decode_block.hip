@@ -119,22 +119,14 @@ struct AttnLds {
   float m;                  // largest score
 };
 
-// Stages o into LDS for the O rows (the padded layout, scaled for the
-// pair decode unless some |o| >= 2^118; the group sums are written by the
-// caller): v[k] is value t + 512 k of thread t.  Returns whether the pair
-// decode may be used.
-__device__ __forceinline__ bool stage_o_input(Lds<1> &L, const float *v) {
-  bool large = false;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) large |= !(__builtin_fabsf(v[k]) < 0x1p118f);
-  const bool pairs = !__syncthreads_or(large);
-  const float scale = pairs ? 1.0f / fp8_unit() : 1.0f;
+// Stages o into LDS for the O rows (the padded layout; the group sums are
+// written by the caller): v[k] is value t + 512 k of thread t.
+__device__ __forceinline__ void stage_o_input(Lds<1> &L, const float *v) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int c = threadIdx.x + kThreads * k;
-    L.x[c + 4 * (c >> 5)] = v[k] * scale;
+    L.x[c + 4 * (c >> 5)] = v[k];
   }
-  return pairs;
 }
 
 // v, through an empty asm the optimiser cannot see through.
@@ -273,13 +265,10 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
 #pragma unroll
       for (int k = 0; k < 32; ++k) xv[k] = ops::rmsq_value(hv[k], rho, wv[k]);
       const float xsv = pair_group_sum(xv);
-      const bool pairs = prescale_for_pairs(xv);
 #pragma unroll
       for (int i = 0; i < kQRowsPerWave; ++i) {
         if (qb + i < qe) {  // uniform per wave
-          const float tv =
-              pairs ? group_term<FAST, true>(qa.cw[i], xv, qa.sv[i], qa.bv[i], xsv, true, odd)
-                    : group_term<FAST, false>(qa.cw[i], xv, qa.sv[i], qa.bv[i], xsv, true, odd);
+          const float tv = group_term<FAST>(qa.cw[i], xv, qa.sv[i], qa.bv[i], xsv, true, odd);
           const float v = wave_sum_lane63(tv, negz);
           if (lane == kWave - 1)
 #pragma unroll
@@ -561,15 +550,14 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
       }
       if (!__syncthreads_and(ok)) return;
       if (t < 2 * kHeads) SO.xs[t] = o5[4];
-      const bool pairs = stage_o_input(SO, o5);
+      stage_o_input(SO, o5);
       __syncthreads();
       if (has_row) {
         Lds<1> &L = SO;
         float xv[32];
         load_x_values(L.x + lane * kChunkStride, true, xv);
         const float xsv = L.xs[lane >> 1];
-        const float tv = pairs ? group_term<FAST, true>(od.cw, xv, od.sv, od.bv, xsv, true, odd)
-                               : group_term<FAST, false>(od.cw, xv, od.sv, od.bv, xsv, true, odd);
+        const float tv = group_term<FAST>(od.cw, xv, od.sv, od.bv, xsv, true, odd);
         const float v = wave_sum_lane63(tv, negz);
         if (lane == kWave - 1) {
           res = res + v;
@@ -606,29 +594,23 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
         h8[0] = a0.x; h8[1] = a0.y; h8[2] = a0.z; h8[3] = a0.w;
         h8[4] = a1.x; h8[5] = a1.y; h8[6] = a1.z; h8[7] = a1.w;
       }
-      const int rq = workgroup_rmsq(S, h8, w8, A.eps, ok);
-      if (rq < 0) return;
+      if (!workgroup_rmsq(S, h8, w8, A.eps, ok)) return;
       {
         float xv[32];
-        const float xsv = load_rmsq_x(S, lane, rq != 0, xv);
+        const float xsv = load_rmsq_x(S, lane, xv);
         uint64_t *mq = A.mq;
         const uint32_t tm = tag + 4;
         const auto store_m = [mq, tm](int i, float v) {
 #pragma unroll
           for (int c = 0; c < kDecodeCopies; ++c) store_tagged(mq + c * kDecodeMaxInter + i, v, tm);
         };
-        if (pb < pe) {
-          if (rq != 0)
-            gu_stage<FAST, true>(Y.mlp, xv, xsv, lane, pb, pe, a, store_m);
-          else
-            gu_stage<FAST, false>(Y.mlp, xv, xsv, lane, pb, pe, a, store_m);
-        }
+        if (pb < pe) gu_stage<FAST>(Y.mlp, xv, xsv, lane, pb, pe, a, store_m);
       }
 
       // ---- stage B: h = h + down m ---------------------------------------------
       // chunk c = 8 consecutive values of m; the last four waves poll them
-      // (poller p: chunks p, p + 256, ...) and write them to LDS scaled for
-      // the pair decode.  A wave's loads complete in issue order for its
+      // (poller p: chunks p, p + 256, ...) and write them to LDS.  A wave's
+      // loads complete in issue order for its
       // wait counter, so a poll behind a fresh prefetch would wait for it:
       // the first four waves (which poll h in the next stage Q) load their
       // next Q rows now, the pollers once their polls are done.
@@ -640,13 +622,11 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
       if (!poller && l + 1 < A.nlayers && qb < qe)
         load_qrows(layer_at(A, l + 1), qb, qe - qb, lane, qa);
       issue_order();
-      if (t == 0) S.flag[0] = S.flag[1] = 0u;
+      if (t == 0) S.flag = 0u;
       __syncthreads();  // every wave of the workgroup is done with stage A
       const uint64_t *mcopy = A.mq + (size_t)copy * kDecodeMaxInter;
       if (poller) {
         const int p = t - (kThreads - kPollThreads);
-        bool large = false;
-        const float scale = 1.0f / fp8_unit();
         // the poller wave's 64 chunks of a round (512 consecutive words)
         // polled lane-contiguous (words lane + 64 k: 4 cache lines per
         // load), then through the wave's slice of T.part (free in this
@@ -662,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
           float xm[8];
           if (!poll_tagged<8, kWave>(mcopy + 2048 * r + 512 * (p / kWave) + lane, tag + 4, xm,
                                      err, A.spin_ticks)) {
-            S.flag[0] = 1u;
+            S.flag = 1u;
             break;
           }
 #pragma unroll
@@ -677,43 +657,17 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
           // group sums: T over each chunk, then over 8 chunks by a butterfly
           const float gs = ops::lane_sum8(ops::tree8(xm));
           if ((c & 7) == 0) S.xs[c >> 3] = gs;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) large |= !(__builtin_fabsf(xm[k]) < 0x1p118f);
           float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * c + 4 * (c >> 2));
-          dst[0] = make_float4(xm[0] * scale, xm[1] * scale, xm[2] * scale, xm[3] * scale);
-          dst[1] = make_float4(xm[4] * scale, xm[5] * scale, xm[6] * scale, xm[7] * scale);
+          dst[0] = make_float4(xm[0], xm[1], xm[2], xm[3]);
+          dst[1] = make_float4(xm[4], xm[5], xm[6], xm[7]);
         }
-        if (large) S.flag[1] = 1u;
         if (l + 1 < A.nlayers && qb < qe) load_qrows(layer_at(A, l + 1), qb, qe - qb, lane, qa);
         issue_order();
       }
       __syncthreads();
-      if (S.flag[0] != 0u) return;
-      const bool pairs = S.flag[1] == 0u;
-      if (!pairs) {
-        // some |m| >= 2^118: the raw values for the plain decode, read again
-        // from the tagged words (they keep this layer's tag until every
-        // workgroup has done this layer's down rows)
-        if (poller) {
-          const int p = t - (kThreads - kPollThreads);
-#pragma unroll 1
-          for (int r = 0; r < kPerPoller; ++r) {
-            const int c = p + r * kPollThreads;
-            float v[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-              v[k] = __uint_as_float((uint32_t)__hip_atomic_load(
-                  mcopy + 8 * c + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            float4 *dst = reinterpret_cast<float4 *>(S.x + 8 * c + 4 * (c >> 2));
-            dst[0] = make_float4(v[0], v[1], v[2], v[3]);
-            dst[1] = make_float4(v[4], v[5], v[6], v[7]);
-          }
-        }
-        __syncthreads();
-      }
+      if (S.flag != 0u) return;
       if (has_row) {
-        const float v =
-            pairs ? down_row<NP, FAST, true>(S, lane, d) : down_row<NP, FAST, false>(S, lane, d);
+        const float v = down_row<NP, FAST>(S, lane, d);
         if (lane == kWave - 1) {
           res = res + v;
           if (l + 1 < A.nlayers) {

@@ -29,8 +29,8 @@ struct alignas(16) Lds {
   float x[NP * 64 * kChunkStride];  // x = rmsq(h) (stage A) or m (stage B)
   float xs[NP * 32];                // their group sums
   float red[kWaves];                // the waves' sums of squares
-  uint32_t flag[2];                 // stage B: a wait gave up / some |m| >= 2^118
-  alignas(16) uint32_t wflag[2][kWaves];  // workgroup_rmsq: per wave, a wait gave up / a large x
+  uint32_t flag;                    // stage B: a wait gave up
+  alignas(16) uint32_t wflag[kWaves];     // workgroup_rmsq: per wave, a wait gave up
   float own[8 * 4];                 // stage B: the owned rows' pass sums
   float ownw[8 * 8 * 4];            // stage B: the owned rows' node sums
 };
@@ -57,13 +57,12 @@ __device__ __forceinline__ bool workgroup_any(uint32_t *slot, bool p) {
 // squares in index order.  Waves 4..7 only vote: each shares a SIMD with
 // one of waves 0..3, and when they formed the same sums (over -0 in place
 // of h: four -0 wave sums more in the tree, which change nothing) their
-// copy of the arithmetic delayed both at the barriers.  x goes to L.x in the row stages' padded layout, its group sums
-// to L.xs.  Returns -1 when `ok` is false in any thread (a wait gave up),
-// else 1 when every |x| < 2^118 (the pair decode may be used; the callers
-// scale x as they load it), else 0.  Two workgroup barriers; L must be
-// free (every earlier reader past a barrier).
+// copy of the arithmetic delayed both at the barriers.  x goes to L.x in
+// the row stages' padded layout, its group sums to L.xs.  Returns false
+// when `ok` is false in any thread (a wait gave up).  Two workgroup
+// barriers; L must be free (every earlier reader past a barrier).
 template <int NP>
-__device__ __forceinline__ int workgroup_rmsq(Lds<NP> &L, const float *h8, const float *w8,
+__device__ __forceinline__ bool workgroup_rmsq(Lds<NP> &L, const float *h8, const float *w8,
                                               float eps, bool ok) {
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1), wave = t / kWave;
@@ -77,38 +76,29 @@ __device__ __forceinline__ int workgroup_rmsq(Lds<NP> &L, const float *h8, const
     const float s = ops::lane_sum64(ops::tree8(v));
     if (lane == 0) L.red[wave] = s;
   }
-  if (workgroup_any(L.wflag[0], !ok)) return -1;
-  bool large = false;
+  if (workgroup_any(L.wflag, !ok)) return false;
   if (hw) {
     const float *r = L.red;
     const float ss = (r[0] + r[1]) + (r[2] + r[3]);
     const float rho = ops::rmsq_rho_from_ss(ss, kCols, eps);
     float u[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      u[k] = ops::rmsq_value(h8[k], rho, w8[k]);
-      large |= !(__builtin_fabsf(u[k]) < 0x1p118f);
-    }
+    for (int k = 0; k < 8; ++k) u[k] = ops::rmsq_value(h8[k], rho, w8[k]);
     float4 *dst = reinterpret_cast<float4 *>(L.x + 8 * t + 4 * (t >> 2));
     dst[0] = make_float4(u[0], u[1], u[2], u[3]);
     dst[1] = make_float4(u[4], u[5], u[6], u[7]);
     const float g = ops::lane_sum8(ops::tree8(u));
     if ((t & 7) == 0) L.xs[t >> 3] = g;
   }
-  return workgroup_any(L.wflag[1], large) ? 0 : 1;
+  __syncthreads();
+  return true;
 }
 
 // A wave's 32 values of x from L (lane l: columns [32 l, 32 l + 32)) and
-// the group sum of its lane pair, scaled for the pair decode if `pairs`
-// (the scaling of prescale_for_pairs).
+// the group sum of its lane pair.
 template <int NP>
-__device__ __forceinline__ float load_rmsq_x(const Lds<NP> &L, int lane, bool pairs, float *xv) {
+__device__ __forceinline__ float load_rmsq_x(const Lds<NP> &L, int lane, float *xv) {
   load_x_values(L.x + kChunkStride * lane, true, xv);
-  if (pairs) {
-    const float scale = 1.0f / fp8_unit();
-#pragma unroll
-    for (int k = 0; k < 32; ++k) xv[k] = xv[k] * scale;
-  }
   return L.xs[lane >> 1];
 }
 
@@ -176,7 +166,7 @@ __device__ __forceinline__ void swiglu_push_uniform(const Store &store, SwigluBa
 // [16 j, 16 j + 16); rows 4 and 5 in lane 63: the same tree as
 // wave_sum_lane63), then each (gate, up) pair goes into the wave's SwiGLU
 // batch (m[p0 + i]).
-template <bool FAST, bool PAIRS, class Store>
+template <bool FAST, class Store>
 __device__ __forceinline__ void gu_block(const GuBlock &a, const float *xv, float xsv, int lane,
                                          int p0, int np, const Store &store, SwigluBatch &batch,
                                          int negz) {
@@ -185,7 +175,7 @@ __device__ __forceinline__ void gu_block(const GuBlock &a, const float *xv, floa
   float t[kGuR];
 #pragma unroll
   for (int j = 0; j < kGuR; ++j)
-    t[j] = j < 2 * np ? group_term<FAST, PAIRS>(a.cw[j], xv, a.sv[j], a.bv[j], xsv, true, odd)
+    t[j] = j < 2 * np ? group_term<FAST>(a.cw[j], xv, a.sv[j], a.bv[j], xsv, true, odd)
                       : kNegZero;
   const float q = quad_row_sums(t[0], t[1], t[2], t[3]);
   const float r4 = wave_sum_lane63(t[4], negz);
@@ -202,7 +192,7 @@ __device__ __forceinline__ void gu_block(const GuBlock &a, const float *xv, floa
 
 // Stage A over the wave's pairs [pb, pe) in blocks of kGuPairs; `a` holds
 // the first block's loads.
-template <bool FAST, bool PAIRS, class Store>
+template <bool FAST, class Store>
 __device__ __forceinline__ void gu_stage(const DecodeLayer &L, const float *xv, float xsv, int lane,
                                          int pb, int pe, GuBlock &a, const Store &store) {
   const int negz = neg_zero_reg();
@@ -210,7 +200,7 @@ __device__ __forceinline__ void gu_stage(const DecodeLayer &L, const float *xv, 
   for (int p = pb; p < pe; p += kGuPairs) {
     const int np = min(kGuPairs, pe - p);
     if (p != pb) load_gu(L, p, np, lane, a);
-    gu_block<FAST, PAIRS>(a, xv, xsv, lane, p, np, store, batch, negz);
+    gu_block<FAST>(a, xv, xsv, lane, p, np, store, batch, negz);
   }
   swiglu_flush<FAST>(store, batch);
 }
@@ -241,7 +231,7 @@ __device__ __forceinline__ void load_down_slice(const DecodeLayer &L, int row, i
 // within 8 lanes), a node of the balanced tree over the 32 groups of the
 // pass holding them; every lane of the row ends with it.  m (local group 4 j + g: values
 // [256 j + 64 g, +64)) and its group sums are in LDS.
-template <int NP, bool FAST, bool PAIRS>
+template <int NP, bool FAST>
 __device__ __forceinline__ void down_slice(const Lds<NP> &S, int lane, const DownRow<NP> &d,
                                            float *sj) {
   const bool odd = lane & 1;
@@ -251,7 +241,7 @@ __device__ __forceinline__ void down_slice(const Lds<NP> &S, int lane, const Dow
     float xv[32];
     load_x_values(S.x + (8 * j + (lane & 7)) * kChunkStride, true, xv);
     const float xsv = S.xs[4 * j + g];
-    float t = group_term<FAST, PAIRS>(d.cw[j], xv, d.sv[j], d.bv[j], xsv, true, odd);
+    float t = group_term<FAST>(d.cw[j], xv, d.sv[j], d.bv[j], xsv, true, odd);
     t = t + dpp<kDppQuadXor2>(t);
     sj[j] = t + dpp<kDppRowHalfMirror>(t);
     issue_order();  // one pass's activations in registers at a time
@@ -276,7 +266,7 @@ __device__ __forceinline__ float combine_passes(const float *p) {
 // Stage B: the wave's down row from `d` and the activations in LDS: T over
 // each pass's 32 group terms, then the -0-padded balanced tree over the
 // passes (T over all groups); valid in lane 63.
-template <int NP, bool FAST, bool PAIRS>
+template <int NP, bool FAST>
 __device__ __forceinline__ float down_row(const Lds<NP> &S, int lane, const DownRow<NP> &d) {
   constexpr int PP = NP == 1 ? 1 : NP == 2 ? 2 : 4;
   const int negz = neg_zero_reg();
@@ -288,7 +278,7 @@ __device__ __forceinline__ float down_row(const Lds<NP> &S, int lane, const Down
       float xv[32];
       load_x_values(S.x + (p * 64 + lane) * kChunkStride, true, xv);
       const float xsv = S.xs[p * 32 + (lane >> 1)];
-      v[p] = wave_sum_lane63(group_term<FAST, PAIRS>(d.cw[p], xv, d.sv[p], d.bv[p], xsv, true, odd),
+      v[p] = wave_sum_lane63(group_term<FAST>(d.cw[p], xv, d.sv[p], d.bv[p], xsv, true, odd),
                              negz);
       issue_order();  // one pass's activations in registers at a time
     } else {
@@ -371,7 +361,7 @@ struct HeadMax {
 // Block blk held in b: the four rows' sums (row j in lanes [16 j, 16 j +
 // 16), as in the head kernel), stored to logits and folded into the lane's
 // running maximum (holder lanes 15, 31, 47, 63).
-template <bool FAST, bool PAIRS>
+template <bool FAST>
 __device__ __forceinline__ void head_block(const DecodeArgs &A, const float *xv, float xsv,
                                            int lane, int blk, const HeadBlock &b, HeadMax &best) {
   const long long r0 = (long long)kHeadR * blk;
@@ -381,7 +371,7 @@ __device__ __forceinline__ void head_block(const DecodeArgs &A, const float *xv,
   float gt[kHeadR];
 #pragma unroll
   for (int j = 0; j < kHeadR; ++j)
-    gt[j] = group_term<FAST, PAIRS>(b.cw[j], xv, b.sv[j], b.bv[j], xsv, true, odd);
+    gt[j] = group_term<FAST>(b.cw[j], xv, b.sv[j], b.bv[j], xsv, true, odd);
   const float v = quad_row_sums(gt[0], gt[1], gt[2], gt[3]);
   const int j = lane >> 4;
   if ((lane & 15) == 15 && j < nrows) {
@@ -400,7 +390,7 @@ __device__ __forceinline__ void head_block(const DecodeArgs &A, const float *xv,
 // entry; each block's loads go out two blocks ahead.  (Two blocks summed
 // together for more independent work per wave measured slower: 0.3694
 // against 0.3664 ms per token.)
-template <bool FAST, bool PAIRS>
+template <bool FAST>
 __device__ __forceinline__ void head_rows(const DecodeArgs &A, const float *xv, float xsv,
                                           int lane, int first, int stride, int nblk,
                                           HeadBlock &b0, HeadBlock &b1, HeadMax &best) {
@@ -408,11 +398,11 @@ __device__ __forceinline__ void head_rows(const DecodeArgs &A, const float *xv, 
 #pragma unroll 1
   for (int k = 0; k < nblk; k += 3) {
     head_load(A, first + (k + 2) * stride, lane, b2);
-    head_block<FAST, PAIRS>(A, xv, xsv, lane, first + k * stride, b0, best);
+    head_block<FAST>(A, xv, xsv, lane, first + k * stride, b0, best);
     head_load(A, first + (k + 3) * stride, lane, b0);
-    if (k + 1 < nblk) head_block<FAST, PAIRS>(A, xv, xsv, lane, first + (k + 1) * stride, b1, best);
+    if (k + 1 < nblk) head_block<FAST>(A, xv, xsv, lane, first + (k + 1) * stride, b1, best);
     head_load(A, first + (k + 4) * stride, lane, b1);
-    if (k + 2 < nblk) head_block<FAST, PAIRS>(A, xv, xsv, lane, first + (k + 2) * stride, b2, best);
+    if (k + 2 < nblk) head_block<FAST>(A, xv, xsv, lane, first + (k + 2) * stride, b2, best);
   }
 }
 

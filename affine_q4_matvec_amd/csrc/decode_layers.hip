@@ -237,10 +237,9 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
     issue_order();
     load_down_slice<NP>(L, drow, x, lane, d);
     {
-      const int rq = workgroup_rmsq(S, h8, w8, A.eps, ok);
-      if (rq < 0) return;
+      if (!workgroup_rmsq(S, h8, w8, A.eps, ok)) return;
       float xv[32];
-      const float xsv = load_rmsq_x(S, lane, rq != 0, xv);
+      const float xsv = load_rmsq_x(S, lane, xv);
       const uint32_t tag = tag0 + 2 * l + 1;
       // m[i] to the XCD's copy (non-temporal: its L2) and the device-scope
       // one
@@ -249,10 +248,7 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
           __builtin_nontemporal_store(((uint64_t)tag << 32) | __float_as_uint(v), mnear + i);
         store_tagged(mfar + i, v, tag);
       };
-      if (rq != 0)
-        gu_stage<FAST, true>(L, xv, xsv, lane, pb, pb + NP, a, store_m);
-      else
-        gu_stage<FAST, false>(L, xv, xsv, lane, pb, pb + NP, a, store_m);
+      gu_stage<FAST>(L, xv, xsv, lane, pb, pb + NP, a, store_m);
     }
 
     // the next layer's gate/up rows, for the waves that do not poll m (they
@@ -267,13 +263,14 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
     // ---- stage B: this XCD's m (its workgroup's 4 NP groups) and their
     // group sums into LDS; the slice's pass sums to the rows' owners; h =
     // h + down m for the owned rows.  Poller thread p < 64 NP takes local
-    // values [4 p, 4 p + 4): m[256 NP x + 4 p ..], local group p / 16.  The pollers are waves without fresh loads in
+    // values [4 p, 4 p + 4): m[256 NP x + 4 p ..], local group p / 16.  The
+    // pollers are waves without fresh loads in
     // flight: a wave's loads complete in issue order for its wait counter,
     // so a poll behind a prefetch of the GPU's next gate/up rows would wait
     // for that prefetch to land.
     // the workgroup polls only once all its waves are done with stage A (the
     // values go to S.x, which stage A reads)
-    if (t == 0) S.flag[0] = S.flag[1] = 0u;
+    if (t == 0) S.flag = 0u;
     __syncthreads();
     const int p = t - (kThreads - kPollThreads);
     const bool mpoll = poller && p < 64 * NP;  // wave-uniform
@@ -284,23 +281,14 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
         float v[4];
         if (!poll_tagged_near<4>(mnear + i, mfar + i, tag_m, v, err, use_near_m, A.near_ticks,
                                  A.spin_ticks))
-          S.flag[0] = 1u;
+          S.flag = 1u;
         // group sums: the balanced tree over the group's 64 values (4 per
         // lane, 16 lanes)
         float gs = (v[0] + v[1]) + (v[2] + v[3]);
         gs = ops::lane_sum8(gs);
         gs = gs + ops::dpp_move<0x140>(gs);  // row_mirror: xor 8 here
         if ((p & 15) == 0) S.xs[p >> 4] = gs;
-        bool large = false;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) large |= !(__builtin_fabsf(v[kk]) < 0x1p118f);
-        if (large) S.flag[1] = 1u;
-        // pre-scaled for the pair decode (the scaling of
-        // prescale_for_pairs), unless some value of the workgroup is large:
-        // then the raw values are written over them below
-        const float scale = 1.0f / fp8_unit();
-        *reinterpret_cast<float4 *>(S.x + lv + 4 * (lv >> 5)) =
-            make_float4(v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale);
+        *reinterpret_cast<float4 *>(S.x + lv + 4 * (lv >> 5)) = make_float4(v[0], v[1], v[2], v[3]);
       }
       // this wave's gate/up rows of the next layer (or its first head
       // blocks after the last layer), now that its polls are done
@@ -310,32 +298,12 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
       issue_order();
     }
     __syncthreads();
-    if (S.flag[0] != 0u) return;
-    const bool pairs = S.flag[1] == 0u;
-    if (!pairs) {
-      // some |m| >= 2^118: the plain decode, on the raw values read again
-      // from the device-scope copy (it keeps this layer's tag until every
-      // workgroup, this one included, has done this layer's down slice)
-      if (mpoll) {
-        const int lv = 4 * p;
-        const int i = 256 * NP * x + lv;
-        float v[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          v[kk] = __uint_as_float((uint32_t)__hip_atomic_load(mfar + i + kk, __ATOMIC_RELAXED,
-                                                              __HIP_MEMORY_SCOPE_AGENT));
-        *reinterpret_cast<float4 *>(S.x + lv + 4 * (lv >> 5)) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-      __syncthreads();
-    }
+    if (S.flag != 0u) return;
     {
       // the slice: the row's 4-group sums (nodes NP x + j of the row's 8 NP
       // nodes), to the row's owner
       float sj[NP];
-      if (pairs)
-        down_slice<NP, FAST, true>(S, lane, d, sj);
-      else
-        down_slice<NP, FAST, false>(S, lane, d, sj);
+      down_slice<NP, FAST>(S, lane, d, sj);
       if ((lane & 7) == 0)
 #pragma unroll
         for (int j = 0; j < NP; ++j)
@@ -398,16 +366,12 @@ __global__ __launch_bounds__(kThreads) void decode_layers_kernel(DecodeArgs A) {
     head_from(a, hb0);
     issue_order();
     head_load(A, gw + stride, lane, hb1);
-    const int rq = workgroup_rmsq(S, h8, w8, A.eps, ok);
-    if (rq < 0) return;
+    if (!workgroup_rmsq(S, h8, w8, A.eps, ok)) return;
     HeadMax best;
     {
       float xv[32];
-      const float xsv = load_rmsq_x(S, lane, rq != 0, xv);
-      if (rq != 0)
-        head_rows<FAST, true>(A, xv, xsv, lane, gw, stride, head_nblk, hb0, hb1, best);
-      else
-        head_rows<FAST, false>(A, xv, xsv, lane, gw, stride, head_nblk, hb0, hb1, best);
+      const float xsv = load_rmsq_x(S, lane, xv);
+      head_rows<FAST>(A, xv, xsv, lane, gw, stride, head_nblk, hb0, hb1, best);
     }
     // the workgroup's best key (holder lanes 15, 31, 47, 63 of each wave;
     // other lanes hold key 0) to workgroup 0 as two tagged words

@@ -30,7 +30,6 @@ constexpr int kWave = 64;
 constexpr float kNegZero = -0.0f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // DPP controls of the gfx9 family.
 constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
@@ -146,66 +145,43 @@ __device__ __forceinline__ float quad_row_sums(float t0, float t1, float t2, flo
 // Codes -> products.  Word bits 4k..4k+3 hold code k; p_k = code_k * x_k.
 // ---------------------------------------------------------------------------
 
+// Byte k of v (0..255) as binary32, exactly: v_cvt_f32_ubyte0..3.  These
+// conversions issue at the rate of a plain add and let two waves of a SIMD
+// issue together, unlike v_cvt_pk_f32_fp8 (which holds the SIMD's VALU for
+// about two issue cycles and issues alone), and unlike a bit-field extract
+// followed by ubyte0 (two VOP3-class instructions per code).
+template <int K>
+__device__ __forceinline__ float byte_f32(uint32_t v) {
+  float f;
+  if constexpr (K == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(v));
+  if constexpr (K == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(v));
+  if constexpr (K == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(v));
+  if constexpr (K == 3) asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(v));
+  return f;
+}
+
 // Plain decode: every code converted to binary32 exactly.
 __device__ __forceinline__ float word_tree(uint32_t w, const float *xk) {
   const uint32_t lo = w & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6
   const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
-  const float p0 = (float)(lo & 0xFFu) * xk[0];
-  const float p1 = (float)(hi & 0xFFu) * xk[1];
-  const float p2 = (float)((lo >> 8) & 0xFFu) * xk[2];
-  const float p3 = (float)((hi >> 8) & 0xFFu) * xk[3];
-  const float p4 = (float)((lo >> 16) & 0xFFu) * xk[4];
-  const float p5 = (float)((hi >> 16) & 0xFFu) * xk[5];
-  const float p6 = (float)(lo >> 24) * xk[6];
-  const float p7 = (float)(hi >> 24) * xk[7];
-  return ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7));
-}
-
-// Pair decode: a byte 0x0q read as an 8-bit float (4 exponent bits, 3
-// mantissa bits) is exactly q * u for q = 0..15, where u (2^-9 in the OCP
-// format, 2^-10 in the FNUZ one) is the value of byte 0x01: 0x01..0x07 are
-// subnormals m*u and 0x08..0x0F the first binade (8+m)*u.  One
-// v_cvt_pk_f32_fp8 decodes two codes.  With activations pre-scaled to
-// x' = x / u (exact: a power-of-two scale that cannot overflow while
-// |x| < 2^118), (q u) * x' equals q * x as a real number, so its rounding
-// is the rounding of q * x: the same bits as the plain decode.
-__device__ __forceinline__ float fp8_unit() {
-  const f32x2 one = __builtin_amdgcn_cvt_pk_f32_fp8(0x0101, false);
-  return one.x;
-}
-
-__device__ __forceinline__ float word_tree_pairs(uint32_t w, const float *xk) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-  const f32x2 c02 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-  const f32x2 c46 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-  const f32x2 c13 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-  const f32x2 c57 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-  const float p0 = c02.x * xk[0];
-  const float p1 = c13.x * xk[1];
-  const float p2 = c02.y * xk[2];
-  const float p3 = c13.y * xk[3];
-  const float p4 = c46.x * xk[4];
-  const float p5 = c57.x * xk[5];
-  const float p6 = c46.y * xk[6];
-  const float p7 = c57.y * xk[7];
+  const float p0 = byte_f32<0>(lo) * xk[0];
+  const float p1 = byte_f32<0>(hi) * xk[1];
+  const float p2 = byte_f32<1>(lo) * xk[2];
+  const float p3 = byte_f32<1>(hi) * xk[3];
+  const float p4 = byte_f32<2>(lo) * xk[4];
+  const float p5 = byte_f32<2>(hi) * xk[5];
+  const float p6 = byte_f32<3>(lo) * xk[6];
+  const float p7 = byte_f32<3>(hi) * xk[7];
   return ((p0 + p1) + (p2 + p3)) + ((p4 + p5) + (p6 + p7));
 }
 
 // Tree of one lane's 32-code chunk (four words, contiguous columns).
-template <bool PAIRS>
 __device__ __forceinline__ float chunk_tree(u32x4 c, const float *xv) {
-  if constexpr (PAIRS) {
-    return (word_tree_pairs(c.x, xv) + word_tree_pairs(c.y, xv + 8)) +
-           (word_tree_pairs(c.z, xv + 16) + word_tree_pairs(c.w, xv + 24));
-  } else {
-    return (word_tree(c.x, xv) + word_tree(c.y, xv + 8)) +
-           (word_tree(c.z, xv + 16) + word_tree(c.w, xv + 24));
-  }
+  return (word_tree(c.x, xv) + word_tree(c.y, xv + 8)) +
+         (word_tree(c.z, xv + 16) + word_tree(c.w, xv + 24));
 }
 
 // Q4_FAST: the chunk's dot product accumulated with fused multiply-adds.
-template <bool PAIRS>
 __device__ __forceinline__ float chunk_dot_fast(u32x4 c, const float *xv) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
   float acc = 0.0f;
@@ -214,29 +190,14 @@ __device__ __forceinline__ float chunk_dot_fast(u32x4 c, const float *xv) {
     const uint32_t lo = w[k] & 0x0F0F0F0Fu;
     const uint32_t hi = (w[k] >> 4) & 0x0F0F0F0Fu;
     const float *xk = xv + 8 * k;
-    if constexpr (PAIRS) {
-      const f32x2 c02 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-      const f32x2 c46 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-      const f32x2 c13 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-      const f32x2 c57 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-      acc = fmaf(c02.x, xk[0], acc);
-      acc = fmaf(c13.x, xk[1], acc);
-      acc = fmaf(c02.y, xk[2], acc);
-      acc = fmaf(c13.y, xk[3], acc);
-      acc = fmaf(c46.x, xk[4], acc);
-      acc = fmaf(c57.x, xk[5], acc);
-      acc = fmaf(c46.y, xk[6], acc);
-      acc = fmaf(c57.y, xk[7], acc);
-    } else {
-      acc = fmaf((float)(lo & 0xFFu), xk[0], acc);
-      acc = fmaf((float)(hi & 0xFFu), xk[1], acc);
-      acc = fmaf((float)((lo >> 8) & 0xFFu), xk[2], acc);
-      acc = fmaf((float)((hi >> 8) & 0xFFu), xk[3], acc);
-      acc = fmaf((float)((lo >> 16) & 0xFFu), xk[4], acc);
-      acc = fmaf((float)((hi >> 16) & 0xFFu), xk[5], acc);
-      acc = fmaf((float)(lo >> 24), xk[6], acc);
-      acc = fmaf((float)(hi >> 24), xk[7], acc);
-    }
+    acc = fmaf(byte_f32<0>(lo), xk[0], acc);
+    acc = fmaf(byte_f32<0>(hi), xk[1], acc);
+    acc = fmaf(byte_f32<1>(lo), xk[2], acc);
+    acc = fmaf(byte_f32<1>(hi), xk[3], acc);
+    acc = fmaf(byte_f32<2>(lo), xk[4], acc);
+    acc = fmaf(byte_f32<2>(hi), xk[5], acc);
+    acc = fmaf(byte_f32<3>(lo), xk[6], acc);
+    acc = fmaf(byte_f32<3>(hi), xk[7], acc);
   }
   return acc;
 }
@@ -246,11 +207,11 @@ __device__ __forceinline__ float chunk_dot_fast(u32x4 c, const float *xv) {
 //          pair end with the same t
 //   fast : each lane adds s*dot (+ b*xs on the even lane), then the pair is
 //          summed, so both lanes again hold the group's term.
-template <bool FAST, bool PAIRS>
+template <bool FAST>
 __device__ __forceinline__ float group_term(u32x4 c, const float *xv, float sv, float bv,
                                             float xsv, bool active, bool odd) {
   if constexpr (!FAST) {
-    float L = chunk_tree<PAIRS>(c, xv);
+    float L = chunk_tree(c, xv);
     L = active ? L : kNegZero;
     const float d = L + dpp<kDppQuadXor1>(L);
     const float sd = sv * d;
@@ -258,7 +219,7 @@ __device__ __forceinline__ float group_term(u32x4 c, const float *xv, float sv, 
     const float t = sd + bx;
     return active ? t : kNegZero;
   } else {
-    const float acc = chunk_dot_fast<PAIRS>(c, xv);
+    const float acc = chunk_dot_fast(c, xv);
     float t = fmaf(sv, acc, odd ? 0.0f : bv * xsv);
     t = active ? t : 0.0f;
     return t + dpp<kDppQuadXor1>(t);
@@ -281,26 +242,6 @@ __device__ __forceinline__ void select_product(const ProdGroup &grp, Prod &P, in
       nwg = grp.wg_begin[i + 1] - grp.wg_begin[i];
     }
   }
-}
-
-// Pre-scales the lane's activations for the pair decode when every
-// activation of the wave is below 2^118 in magnitude (NaN counts as large);
-// returns whether the wave may use the pair decode.
-// The test is one integer maximum over the magnitudes' bit patterns: with
-// the sign cleared, binary32 bits order like the magnitudes, and every NaN
-// and infinity lies above the bits of 2^118 (0x7A800000).
-__device__ __forceinline__ bool prescale_for_pairs(float *xv) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const uint32_t a = __float_as_uint(xv[k]) & 0x7FFFFFFFu;
-    m = a > m ? a : m;
-  }
-  if (__any(m >= 0x7A800000u)) return false;
-  const float scale = 1.0f / fp8_unit();  // 2^9 or 2^10, exact
-#pragma unroll
-  for (int k = 0; k < 32; ++k) xv[k] = xv[k] * scale;
-  return true;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer(const void *base, uint32_t bytes) {

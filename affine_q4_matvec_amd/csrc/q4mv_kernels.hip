@@ -125,7 +125,7 @@ struct RunningMax {
 // tree T, then the epilogue.  R a multiple of 4: four rows reduced at once,
 // row j of a quad ending in lane 16 j + 15; otherwise each row on its own,
 // ending in lane 63.
-template <int R, bool FAST, bool PAIRS, int EPI, class Store>
+template <int R, bool FAST, int EPI, class Store>
 __device__ __forceinline__ void row64_block(const Prod &P, const float *xv, float xsv, int lane,
                                             int negz, int r, int nrows, const Row64Block<R> &a,
                                             RunningMax &best, SwigluBatch &batch,
@@ -142,15 +142,15 @@ __device__ __forceinline__ void row64_block(const Prod &P, const float *xv, floa
       float gt[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        gt[j] = group_term<FAST, PAIRS>(a.cw[4 * q + j], xv, a.sv[4 * q + j], a.bv[4 * q + j],
-                                        xsv, true, odd);
+        gt[j] = group_term<FAST>(a.cw[4 * q + j], xv, a.sv[4 * q + j], a.bv[4 * q + j], xsv,
+                                 true, odd);
       tq[q] = quad_row_sums(gt[0], gt[1], gt[2], gt[3]);
     }
   } else {
 #pragma unroll
     for (int j = 0; j < R; ++j)
       tq[j] = wave_sum_lane63(
-          group_term<FAST, PAIRS>(a.cw[j], xv, a.sv[j], a.bv[j], xsv, true, odd), negz);
+          group_term<FAST>(a.cw[j], xv, a.sv[j], a.bv[j], xsv, true, odd), negz);
   }
   if constexpr (EPI == kEpiSwiglu) {
     // (gate, up) = rows (2i, 2i + 1) of the block
@@ -266,7 +266,7 @@ __device__ __forceinline__ void row64_inputs(const Prod &P, const Extra &ex, int
 
 // PRELOAD (every wave has at most one block): the block's loads were issued
 // before the prologue and `a` holds them.
-template <int R, bool FAST, bool PAIRS, int EPI>
+template <int R, bool FAST, int EPI>
 __device__ __forceinline__ void row64_single(const Prod &P, const Extra &ex, const float *xv,
                                              float xsv, int lane, int r, Row64Block<R> &a,
                                              RunningMax &best) {
@@ -275,7 +275,7 @@ __device__ __forceinline__ void row64_single(const Prod &P, const Extra &ex, con
   float *m_out = ex.m_out;
   const auto store_m = [m_out](int i, float v) { m_out[i] = v; };
   const int negz = R % 4 == 0 ? 0 : neg_zero_reg();  // only the one-row sums use it
-  row64_block<R, FAST, PAIRS, EPI>(P, xv, xsv, lane, negz, r, min(R, P.rows - r), a, best, batch,
+  row64_block<R, FAST, EPI>(P, xv, xsv, lane, negz, r, min(R, P.rows - r), a, best, batch,
                                    store_m);
   if constexpr (EPI == kEpiSwiglu) swiglu_flush<FAST>(store_m, batch);
 }
@@ -288,7 +288,7 @@ __device__ __forceinline__ void row64_single(const Prod &P, const Extra &ex, con
 // those HBM loads are in flight while the prologue runs (the activations
 // come from L2, or from rmsq over the workgroup).  Every wave runs the
 // first iteration, also one without rows (the rmsq prologue has
-// barriers); the pair decode is then chosen per block (wave-uniform).
+// barriers).
 template <int R, bool FAST, int PRO, int EPI>
 __device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, int lw, int lane,
                                            int r0, int stride, RunningMax &best) {
@@ -306,7 +306,6 @@ __device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, int l
 #pragma unroll
   for (int i = 0; i < 32; ++i) xv[i] = 0.0f;
   float xsv = 0.0f;
-  bool pairs = false;
   Row64Block<R> a;
   int k = 0;
   for (int r = r0; k == 0 || r < end; r += stride, ++k) {
@@ -320,15 +319,9 @@ __device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, int l
       int l = lane;
       asm volatile("" : "+v"(l));
       row64_inputs<PRO, true>(P, ex, lw, l, xv, xsv);
-      pairs = prescale_for_pairs(xv);
     }
-    if (nrows > 0) {
-      if (pairs)
-        row64_block<R, FAST, true, EPI>(P, xv, xsv, lane, negz, r, nrows, a, best, batch, store_m);
-      else
-        row64_block<R, FAST, false, EPI>(P, xv, xsv, lane, negz, r, nrows, a, best, batch,
-                                         store_m);
-    }
+    if (nrows > 0)
+      row64_block<R, FAST, EPI>(P, xv, xsv, lane, negz, r, nrows, a, best, batch, store_m);
   }
   if constexpr (EPI == kEpiSwiglu) swiglu_flush<FAST>(store_m, batch);
 }
@@ -355,10 +348,7 @@ __global__ __launch_bounds__(kThreads) void q4mv_row64_kernel(ProdGroup grp, Ext
     float xv[32];
     float xsv;
     row64_inputs<PRO, false>(P, ex, lw, lane, xv, xsv);
-    if (prescale_for_pairs(xv))
-      row64_single<R, FAST, true, EPI>(P, ex, xv, xsv, lane, first, a, best);
-    else
-      row64_single<R, FAST, false, EPI>(P, ex, xv, xsv, lane, first, a, best);
+    row64_single<R, FAST, EPI>(P, ex, xv, xsv, lane, first, a, best);
   }
 
   if constexpr (EPI == kEpiArgmax) {
@@ -425,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void q4mv_seg_kernel(ProdGroup grp) {
 #pragma unroll
     for (int j = 0; j < R; ++j)
       tot[j] = segment_sum<LPR>(
-          group_term<FAST, false>(cw[j], xv, sv[j], bv[j], xsv, active, chunk & 1));
+          group_term<FAST>(cw[j], xv, sv[j], bv[j], xsv, active, chunk & 1));
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const int r = rb * RB + j * RPW + seg;
@@ -468,7 +458,7 @@ __device__ __forceinline__ void split_load(const Prod &P, int r0, int nrows, uin
   }
 }
 
-template <int PP, int R, bool FAST, bool PAIRS>
+template <int PP, int R, bool FAST>
 __device__ __forceinline__ void split_rows(const Prod &P, const float *xv, float xsv, int lane,
                                            int wave, int passes, int begin, int end,
                                            SplitBlock<R> &a, float (*part)[16]) {
@@ -486,8 +476,8 @@ __device__ __forceinline__ void split_rows(const Prod &P, const float *xv, float
       float gt[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        gt[j] = group_term<FAST, PAIRS>(a.cw[4 * q + j], xv, a.sv[4 * q + j], a.bv[4 * q + j], xsv,
-                                        active, odd);
+        gt[j] = group_term<FAST>(a.cw[4 * q + j], xv, a.sv[4 * q + j], a.bv[4 * q + j], xsv,
+                                 active, odd);
       // row 4 q + j's pass sum in lanes [16 j, 16 j + 16)
       const float tq = quad_row_sums(gt[0], gt[1], gt[2], gt[3]);
       if ((lane & 15) == 15) part[4 * q + (lane >> 4)][wave] = tq;
@@ -542,19 +532,8 @@ __global__ __launch_bounds__(1024) void q4mv_split_kernel(ProdGroup grp) {
   float xv[32];
   float xsv;
   chunk_inputs<PRO>(P, chunk, active, xv, xsv);
-  // one decode choice for the whole workgroup (the loop has barriers)
-  bool large = false;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) large |= !(__builtin_fabsf(xv[k]) < 0x1p118f);
   __shared__ float part[R][16];
-  if (!__syncthreads_or(large)) {
-    const float scale = 1.0f / fp8_unit();
-#pragma unroll
-    for (int k = 0; k < 32; ++k) xv[k] = xv[k] * scale;
-    split_rows<PP, R, FAST, true>(P, xv, xsv, lane, wave, passes, begin, end, a, part);
-  } else {
-    split_rows<PP, R, FAST, false>(P, xv, xsv, lane, wave, passes, begin, end, a, part);
-  }
+  split_rows<PP, R, FAST>(P, xv, xsv, lane, wave, passes, begin, end, a, part);
 }
 
 int next_pow2(int v) {
@@ -687,7 +666,7 @@ constexpr int kLaneRowThreads = 256;
 
 // The term of group g of row r (fixed: T over its 64 products, then the
 // unfused affine step; fast: fused multiply-adds).
-template <bool FAST, bool PAIRS>
+template <bool FAST>
 __device__ __forceinline__ float lane_row_group(const u32x4 *qr, const float *sr, const float *br,
                                                 int g, const float *sx, const float *sxs) {
   const u32x4 c0 = __builtin_nontemporal_load(qr + 2 * g);
@@ -703,12 +682,12 @@ __device__ __forceinline__ float lane_row_group(const u32x4 *qr, const float *sr
     xv[k + 3] = v.w;
   }
   if constexpr (!FAST) {
-    const float d = chunk_tree<PAIRS>(c0, xv) + chunk_tree<PAIRS>(c1, xv + 32);
+    const float d = chunk_tree(c0, xv) + chunk_tree(c1, xv + 32);
     const float sd = sv * d;
     const float bx = bv * sxs[g];
     return sd + bx;
   } else {
-    const float dot = chunk_dot_fast<PAIRS>(c0, xv) + chunk_dot_fast<PAIRS>(c1, xv + 32);
+    const float dot = chunk_dot_fast(c0, xv) + chunk_dot_fast(c1, xv + 32);
     return fmaf(sv, dot, bv * sxs[g]);
   }
 }
@@ -717,7 +696,7 @@ __device__ __forceinline__ float lane_row_group(const u32x4 *qr, const float *sr
 // tree, then the blocks' balanced tree formed as they arrive (a binary
 // counter: lv[k] holds the last complete run of 2^k blocks, always added as
 // the left operand), which is the balanced tree over the 32 groups, T.
-template <bool FAST, bool PAIRS>
+template <bool FAST>
 __device__ __forceinline__ float lane_row_sum(const Prod &P, int r, const float *sx,
                                               const float *sxs) {
   const u32x4 *qr = reinterpret_cast<const u32x4 *>(P.q) + (size_t)r * 64;  // 1 KiB per row
@@ -728,7 +707,7 @@ __device__ __forceinline__ float lane_row_sum(const Prod &P, int r, const float 
   for (int j = 0; j < 8; ++j) {
     float t[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) t[k] = lane_row_group<FAST, PAIRS>(qr, sr, br, 4 * j + k, sx, sxs);
+    for (int k = 0; k < 4; ++k) t[k] = lane_row_group<FAST>(qr, sr, br, 4 * j + k, sx, sxs);
     if constexpr (FAST) {
       acc = ((acc + t[0]) + t[1]) + (t[2] + t[3]);
     } else {
@@ -757,20 +736,13 @@ template <bool FAST>
 __global__ __launch_bounds__(kLaneRowThreads) void q4mv_lane_row_kernel(Prod P) {
   __shared__ float sx[2048];
   __shared__ float sxs[32];
-  // x (pre-scaled for the pair decode when every |x| < 2^118) and its sums
-  bool large = false;
-  for (int i = threadIdx.x; i < 2048; i += kLaneRowThreads)
-    large |= !(__builtin_fabsf(P.x[i]) < 0x1p118f);
-  const bool pairs = !__syncthreads_or(large);
-  const float scale = pairs ? 1.0f / fp8_unit() : 1.0f;
-  for (int i = threadIdx.x; i < 2048; i += kLaneRowThreads) sx[i] = P.x[i] * scale;
+  // x and its group sums
+  for (int i = threadIdx.x; i < 2048; i += kLaneRowThreads) sx[i] = P.x[i];
   if (threadIdx.x < 32) sxs[threadIdx.x] = P.xs[threadIdx.x];
   __syncthreads();
   for (int r = blockIdx.x * kLaneRowThreads + threadIdx.x; r < P.rows;
        r += gridDim.x * kLaneRowThreads) {
-    const float v = pairs ? lane_row_sum<FAST, true>(P, r, sx, sxs)
-                          : lane_row_sum<FAST, false>(P, r, sx, sxs);
-    P.y[r] = v;
+    P.y[r] = lane_row_sum<FAST>(P, r, sx, sxs);
   }
 }
 

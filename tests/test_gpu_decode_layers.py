@@ -60,10 +60,10 @@ def test_decode_layers_bit_exact(inter, nlayers):
         assert_bits_equal(got, want, "h inter=%d layers=%d tok=%d" % (inter, nlayers, tok))
 
 
-def test_decode_layers_large_m_takes_the_plain_decode():
-    """One value of m near 2^120 (gate and up of one pair near 2^60): the
-    workgroups cannot pre-scale m for the pair decode and must sum the down
-    rows from the raw values; every h bit as the oracle's."""
+def test_decode_layers_large_m():
+    """One value of m near 2^120 (gate and up of one pair near 2^60): down
+    products near the top of the binary32 range; every h bit as the
+    oracle's."""
     q4 = lib()
     w = synth.chain_weights(seed=47, layers=1, inter=2048, vocab=300)
     tok = 11

@@ -105,8 +105,8 @@ def test_q4mv_tree_order_adversarial():
 
 @pytest.mark.parametrize("cols", [128, 2048, 6144])
 def test_q4mv_special_values(cols):
-    """Zeros of both signs and subnormal activations (pair decode), and
-    activations of 2^118 and more, which send a wave to the plain decode."""
+    """Zeros of both signs, subnormal activations, and activations of 2^117
+    and more (products up to 15 times those, near binary32 overflow)."""
     rows = 16
     m = synth.small_product(seed=3, rows=rows, cols=cols, name="spec%d" % cols)
     x = m["x"].copy()
@@ -122,7 +122,7 @@ def test_q4mv_special_values(cols):
         xs = oracle.group_sums(xb)
         assert_bits_equal(run_q4mv(m, xb, xs), oracle.q4mv(m, xb, xs), "large %r %d" % (big, cols))
     xb = x.copy()
-    xb[cols // 2] = np.float32(2.0**117)  # largest scale the pair decode keeps
+    xb[cols // 2] = np.float32(2.0**117)
     xs = oracle.group_sums(xb)
     assert_bits_equal(run_q4mv(m, xb, xs), oracle.q4mv(m, xb, xs), "2^117 %d" % cols)
 

@@ -49,9 +49,9 @@ def test_variant_matches_oracle(variant, rows):
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-def test_variant_large_activations_take_the_plain_decode(variant):
-    # an activation of 2^120 rules out the pre-scaled pair decode; the
-    # plain decode must give the same bits as the oracle
+def test_variant_large_activations(variant):
+    # an activation of 2^120: products near binary32 overflow, the same bits
+    # as the oracle
     q4 = lib()
     m = synth.small_product(seed=42, rows=515, cols=2048, name="varbig")
     x = m["x"].copy()
