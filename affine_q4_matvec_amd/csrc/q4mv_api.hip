@@ -137,29 +137,18 @@ int ws_status(void *ws, size_t err_off, size_t clear, void *stream) {
 }
 
 // Launches a list of products of one shape as grouped kernels (up to
-// kMaxGroup products per launch).  When the products of a launch together
-// want more workgroups than fit on the device at once, each one's share is
-// cut in proportion (at least one workgroup each).
+// kMaxGroup products per launch), each launch's workgroups planned by
+// plan_group.
 int launch_products(const Prod *prods, int count, const Shape &sh, int mode, hipStream_t st,
                     const q4::Extra &ex = q4::Extra{}) {
   if (!q4::shape_supported(sh)) return Q4_EINVAL;
-  const int cap = q4::resident_capacity(sh, mode);
   for (int at = 0; at < count; at += q4::kMaxGroup) {
     ProdGroup g;
     memset(&g, 0, sizeof(g));
     g.n = count - at < q4::kMaxGroup ? count - at : q4::kMaxGroup;
-    int32_t want[q4::kMaxGroup];
-    long long total = 0;
-    for (int i = 0; i < g.n; ++i) {
-      want[i] = q4::workgroups_for(sh, prods[at + i].rows, mode);
-      total += want[i];
-    }
-    if (cap > 0 && total > cap) {
-      for (int i = 0; i < g.n; ++i) {
-        const long long w = (long long)want[i] * cap / total;
-        want[i] = (int32_t)(w < 1 ? 1 : w);
-      }
-    }
+    int32_t rows[q4::kMaxGroup], want[q4::kMaxGroup];
+    for (int i = 0; i < g.n; ++i) rows[i] = prods[at + i].rows;
+    q4::plan_group(sh, mode, rows, g.n, want);
     g.wg_begin[0] = 0;
     for (int i = 0; i < g.n; ++i) {
       g.p[i] = prods[at + i];

@@ -70,9 +70,11 @@ Shape shape_of(int32_t cols, int pro = kProX, int epi = kEpiStore);
 bool shape_supported(const Shape &sh);
 // Workgroups a product of this shape gets when launched alone.
 int32_t workgroups_for(const Shape &sh, int32_t rows, int mode);
-// Workgroups of this shape that fit on the current device at once (0: no
-// limit from occupancy).
-int32_t resident_capacity(const Shape &sh, int mode);
+// Workgroups of the products of one grouped launch (want[0..n)), in the
+// units of the kernel that will run: for row64 shapes the preloading kernel
+// when every product's blocks fit on the device at once, else the looping
+// kernel with the device's workgroups shared in proportion.
+void plan_group(const Shape &sh, int mode, const int32_t *rows, int n, int32_t *want);
 
 // Launchers.  They assume validated arguments and return the HIP status of
 // the launch.

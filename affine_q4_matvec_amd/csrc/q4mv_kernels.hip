@@ -43,13 +43,10 @@
 #ifndef Q4_ROW64_OCC_PCT
 #define Q4_ROW64_OCC_PCT 100  // share of the resident workgroups launched
 #endif
-#ifndef Q4_ROW64_LOOP_WG_PER_CU
-// Workgroups per compute unit (waves per SIMD) of a row64 launch whose
-// waves loop over several blocks.  Measured on the 248320-row head: 4 is
-// 1-2 us faster than the 7 that fit (fixed order), the same in fast order;
-// 3 and 2 are slower.
-#define Q4_ROW64_LOOP_WG_PER_CU 4
-#endif
+// A row64 launch whose waves loop over several blocks runs one workgroup of
+// 16 waves per compute unit (4 per SIMD).
+constexpr int kLoopThreads = 1024;
+constexpr int kLoopWaves = kLoopThreads / 64;
 #ifndef Q4_SPLIT_R
 #define Q4_SPLIT_R 4  // a multiple of 4
 #endif
@@ -186,24 +183,6 @@ __device__ __forceinline__ void row64_block(const Prod &P, const float *xv, floa
   }
 }
 
-// Issue priority from a wave's progress: 3 over the first quarter of its
-// nblk blocks, then 2, 1 and 0.  A SIMD otherwise favours its oldest waves,
-// which then run out of blocks long before its youngest: the last part of
-// the launch would be left to one or two waves per SIMD, too few to hide
-// the loads' latency.  Waves that fall behind now get the issue slots, so
-// all of a SIMD's waves keep working until close to the end.
-__device__ __forceinline__ void progress_priority(int k, int nblk) {
-  const int q = (4 * k) / nblk;  // wave-uniform
-  if (q == 0)
-    __builtin_amdgcn_s_setprio(3);
-  else if (q == 1)
-    __builtin_amdgcn_s_setprio(2);
-  else if (q == 2)
-    __builtin_amdgcn_s_setprio(1);
-  else
-    __builtin_amdgcn_s_setprio(0);
-}
-
 // x = rmsq(h, wn) over the workgroup into LDS (4 floats of padding after
 // every 32, so that the lanes' 16-byte reads of their 32 values hit
 // distinct banks); the lane's 32 values and its group's sum.  Every wave of
@@ -280,23 +259,32 @@ __device__ __forceinline__ void row64_single(const Prod &P, const Extra &ex, con
   if constexpr (EPI == kEpiSwiglu) swiglu_flush<FAST>(store_m, batch);
 }
 
-// Blocks of R rows dealt round-robin to the waves: r0, r0 + stride, ...
-// Each block is loaded at the top of its iteration (issuing the next
-// block's loads while summing the current one keeps two blocks of
-// registers live and measured no faster).  The activations are formed in
-// the first iteration, after its block's loads have gone out, so that
-// those HBM loads are in flight while the prologue runs (the activations
-// come from L2, or from rmsq over the workgroup).  Every wave runs the
-// first iteration, also one without rows (the rmsq prologue has
-// barriers).
+// The blocks of workgroup lw of nwg: blocks lw, lw + nwg, lw + 2 nwg, ...
+// of R rows each, taken by its 16 waves as they become free.  Ticket t
+// names the workgroup's block t; waves take tickets 0..15 first and then
+// one at a time from a counter in LDS, fetched while the current block is
+// summed.  (Dealt statically, one block in four per wave, the first waves a
+// SIMD received finished several microseconds before its last: a SIMD
+// favours its oldest waves.  Here the waves that are served more take more
+// blocks, and a workgroup's waves finish within about one block of each
+// other; dealing a workgroup's last blocks one row per ticket, to finish
+// closer together, was slower: 50.9 us on the head with whole blocks, 53.0
+// with the last 4 blocks by rows, 54.5 with 8.)  A wave's tickets, and so its rows, increase.  Each block is
+// loaded at the top of its iteration (issuing the next block's loads while
+// summing the current one keeps two blocks of registers live and measured
+// no faster).  The activations are formed in the first iteration, after
+// its block's loads have gone out, so that those HBM loads are in flight
+// while the prologue runs; every wave runs that first iteration, also one
+// without a block.
 template <int R, bool FAST, int PRO, int EPI>
-__device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, int lw, int lane,
-                                           int r0, int stride, RunningMax &best) {
+__device__ __forceinline__ void row64_loop_rows(const Prod &P, const Extra &ex, int lw, int nwg,
+                                                int lane, int wave, uint32_t *ticket,
+                                                RunningMax &best) {
   const uint32_t voff_q = 16u * lane;
   const uint32_t voff_g = 4u * (lane >> 1);
-  const int end = P.rows;
+  const int blocks = (P.rows + R - 1) / R;
+  const int nblk = lw < blocks ? (blocks - lw + nwg - 1) / nwg : 0;  // this workgroup's
   const int negz = R % 4 == 0 ? 0 : neg_zero_reg();  // only the one-row sums use it
-  const int nblk = r0 < end ? (end - r0 + stride - 1) / stride : 1;
   SwigluBatch batch;
   float *m_out = ex.m_out;
   const auto store_m = [m_out](int i, float v) { m_out[i] = v; };
@@ -307,28 +295,60 @@ __device__ __forceinline__ void row64_rows(const Prod &P, const Extra &ex, int l
   for (int i = 0; i < 32; ++i) xv[i] = 0.0f;
   float xsv = 0.0f;
   Row64Block<R> a;
-  int k = 0;
-  for (int r = r0; k == 0 || r < end; r += stride, ++k) {
-    progress_priority(k, nblk);
-    // a wave without rows loads from a buffer of zero bytes: nothing
-    const int nrows = r < end ? min(R, end - r) : 0;
-    row64_load<R>(P, r < end ? r : 0, nrows, voff_q, voff_g, a);
-    if (k == 0) {
+  int t = wave;
+  for (bool first = true; first || t < nblk; first = false) {
+    const int r = (lw + nwg * t) * R;
+    // a wave without a block loads from a buffer of zero bytes: nothing
+    const int nrows = t < nblk ? min(R, P.rows - r) : 0;
+    row64_load<R>(P, nrows > 0 ? r : 0, nrows, voff_q, voff_g, a);
+    if (first) {
       // the lane index hidden from the optimiser, so that the activations'
       // addresses are formed here and not held through the loop
       int l = lane;
       asm volatile("" : "+v"(l));
       row64_inputs<PRO, true>(P, ex, lw, l, xv, xsv);
     }
-    if (nrows > 0)
-      row64_block<R, FAST, EPI>(P, xv, xsv, lane, negz, r, nrows, a, best, batch, store_m);
+    if (nrows == 0) break;
+    uint32_t tn = 0;
+    if (lane == 0) tn = atomicAdd(ticket, 1u);
+    tn = __builtin_amdgcn_readfirstlane(tn);
+    row64_block<R, FAST, EPI>(P, xv, xsv, lane, negz, r, nrows, a, best, batch, store_m);
+    t = (int)tn;
   }
   if constexpr (EPI == kEpiSwiglu) swiglu_flush<FAST>(store_m, batch);
 }
 
-// PRELOAD: issue the first block's loads before the activations are formed,
-// for launches where every wave has one block at most.
-template <int R, bool FAST, int PRO, int EPI, bool PRELOAD>
+// One workgroup of 16 waves per compute unit, looping over its blocks.
+template <int R, bool FAST, int PRO, int EPI>
+__global__ __launch_bounds__(kLoopThreads) void q4mv_row64_loop_kernel(ProdGroup grp, Extra ex) {
+  __shared__ uint32_t ticket;
+  Prod P;
+  int lw = 0, nwg = 1;
+  select_product(grp, P, lw, nwg);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = wave_index();
+  if (threadIdx.x == 0) ticket = kLoopWaves;
+  __syncthreads();
+  RunningMax best;
+  row64_loop_rows<R, FAST, PRO, EPI>(P, ex, lw, nwg, lane, wave, &ticket, best);
+  if constexpr (EPI == kEpiArgmax) {
+    // one key per workgroup; a second kernel reduces them
+    __shared__ unsigned long long wbest[kLoopWaves];
+    const unsigned long long k = ops::key_max_rows(best.key());
+    if (lane == kWave - 1) wbest[wave] = k;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long k = wbest[0];
+#pragma unroll
+      for (int i = 1; i < kLoopWaves; ++i) k = wbest[i] > k ? wbest[i] : k;
+      ex.amax[lw] = k;
+    }
+  }
+}
+
+// Launches where every wave has one block at most: the block's loads go out
+// before the activations are formed.
+template <int R, bool FAST, int PRO, int EPI>
 __global__ __launch_bounds__(kThreads) void q4mv_row64_kernel(ProdGroup grp, Extra ex) {
   Prod P;
   int lw = 0, nwg = 1;
@@ -336,12 +356,10 @@ __global__ __launch_bounds__(kThreads) void q4mv_row64_kernel(ProdGroup grp, Ext
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = wave_index();
   const int wpg = kThreads / kWave;
-  const int first = (lw * wpg + wave) * R, stride = nwg * wpg * R;
+  const int first = (lw * wpg + wave) * R;
 
   RunningMax best;
-  if constexpr (!PRELOAD) {
-    row64_rows<R, FAST, PRO, EPI>(P, ex, lw, lane, first, stride, best);
-  } else {
+  {
     Row64Block<R> a;
     if (first < P.rows)
       row64_load<R>(P, first, min(R, P.rows - first), 16u * lane, 4u * (lane >> 1), a);
@@ -573,11 +591,11 @@ hipError_t launch_split(const ProdGroup &g, int passes, hipStream_t st) {
 template <bool FAST, int PRO, int EPI>
 hipError_t launch_row64(const ProdGroup &g, bool preload, const Extra &ex, hipStream_t st) {
   if (preload)
-    hipLaunchKernelGGL((q4mv_row64_kernel<kRow64R, FAST, PRO, EPI, true>),
-                       dim3(g.wg_begin[g.n]), dim3(kThreads), 0, st, g, ex);
+    hipLaunchKernelGGL((q4mv_row64_kernel<kRow64R, FAST, PRO, EPI>), dim3(g.wg_begin[g.n]),
+                       dim3(kThreads), 0, st, g, ex);
   else
-    hipLaunchKernelGGL((q4mv_row64_kernel<kRow64R, FAST, PRO, EPI, false>),
-                       dim3(g.wg_begin[g.n]), dim3(kThreads), 0, st, g, ex);
+    hipLaunchKernelGGL((q4mv_row64_loop_kernel<kRow64R, FAST, PRO, EPI>), dim3(g.wg_begin[g.n]),
+                       dim3(kLoopThreads), 0, st, g, ex);
   return hipGetLastError();
 }
 
@@ -593,7 +611,8 @@ template <bool FAST, bool PRELOAD>
 const void *row64_ptr(int pro, int epi) {
 #define Q4_PTR_CASE(P_, E_) \
   if (pro == P_ && epi == E_)   \
-    return reinterpret_cast<const void *>(&q4mv_row64_kernel<kRow64R, FAST, P_, E_, PRELOAD>);
+    return PRELOAD ? reinterpret_cast<const void *>(&q4mv_row64_kernel<kRow64R, FAST, P_, E_>)  \
+                   : reinterpret_cast<const void *>(&q4mv_row64_loop_kernel<kRow64R, FAST, P_, E_>);
   Q4_ROW64_VARIANTS(Q4_PTR_CASE)
 #undef Q4_PTR_CASE
   return nullptr;
@@ -625,14 +644,14 @@ constexpr int kMaxDevices = 64;
 constexpr int kVariantSlots = 2 * 2 * 3 * 3;  // mode x preload x prologue x epilogue
 std::atomic<int> g_resident[kMaxDevices][kVariantSlots];
 
-int resident_workgroups(const void *kernel, int slot, int limit_per_cu) {
+int resident_workgroups(const void *kernel, int threads, int slot, int limit_per_cu) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev < 0 || dev >= kMaxDevices || slot < 0 || slot >= kVariantSlots) return 0;
   const int cached = g_resident[dev][slot].load(std::memory_order_relaxed);
   if (cached > 0) return cached;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   if (limit_per_cu > 0 && per_cu > limit_per_cu) per_cu = limit_per_cu;
@@ -762,26 +781,21 @@ hipError_t launch_wave_variant(const Prod &p, hipStream_t st) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipErrorInvalidValue;
-  const void *kpre = reinterpret_cast<const void *>(
-      &q4mv_row64_kernel<R, FAST, kProX, kEpiStore, true>);
+  const void *kpre = reinterpret_cast<const void *>(&q4mv_row64_kernel<R, FAST, kProX, kEpiStore>);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kpre, kThreads, 0) != hipSuccess)
     return hipErrorInvalidValue;
   const Extra ex{};
   if (need <= (long long)per_cu * cus) {
     for (int i = 1; i <= kMaxGroup; ++i) g.wg_begin[i] = (int32_t)need;
-    hipLaunchKernelGGL((q4mv_row64_kernel<R, FAST, kProX, kEpiStore, true>), dim3((int)need),
+    hipLaunchKernelGGL((q4mv_row64_kernel<R, FAST, kProX, kEpiStore>), dim3((int)need),
                        dim3(kThreads), 0, st, g, ex);
     return hipGetLastError();
   }
-  const void *kloop = reinterpret_cast<const void *>(
-      &q4mv_row64_kernel<R, FAST, kProX, kEpiStore, false>);
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kloop, kThreads, 0) != hipSuccess)
-    return hipErrorInvalidValue;
-  if (per_cu > Q4_ROW64_LOOP_WG_PER_CU) per_cu = Q4_ROW64_LOOP_WG_PER_CU;
-  const int nwg = (per_cu < 1 ? 1 : per_cu) * cus;
+  // the looping kernel: one workgroup per compute unit
+  const int nwg = cus < 1 ? 1 : cus;
   for (int i = 1; i <= kMaxGroup; ++i) g.wg_begin[i] = nwg;
-  hipLaunchKernelGGL((q4mv_row64_kernel<R, FAST, kProX, kEpiStore, false>), dim3(nwg),
-                     dim3(kThreads), 0, st, g, ex);
+  hipLaunchKernelGGL((q4mv_row64_loop_kernel<R, FAST, kProX, kEpiStore>), dim3(nwg),
+                     dim3(kLoopThreads), 0, st, g, ex);
   return hipGetLastError();
 }
 
@@ -838,13 +852,42 @@ int32_t row64_capacity(const Shape &sh, int mode, bool preload) {
                        : (preload ? row64_ptr<false, true>(sh.pro, sh.epi)
                                   : row64_ptr<false, false>(sh.pro, sh.epi));
   if (!k) return 0;
-  return resident_workgroups(k, 18 * (fast ? 1 : 0) + 9 * (preload ? 1 : 0) + 3 * sh.pro + sh.epi,
-                             preload ? 0 : Q4_ROW64_LOOP_WG_PER_CU);
+  // the looping kernel: one workgroup of kLoopThreads per compute unit
+  return resident_workgroups(k, preload ? kThreads : kLoopThreads,
+                             18 * (fast ? 1 : 0) + 9 * (preload ? 1 : 0) + 3 * sh.pro + sh.epi,
+                             preload ? 0 : 1);
 }
 
-int32_t resident_capacity(const Shape &sh, int mode) {
-  if (sh.kind != Shape::kRow64) return 0;  // no cap from occupancy
-  return row64_capacity(sh, mode, false);
+void plan_group(const Shape &sh, int mode, const int32_t *rows, int n, int32_t *want) {
+  long long total = 0;
+  for (int i = 0; i < n; ++i) {
+    want[i] = workgroups_for(sh, rows[i], mode);
+    total += want[i];
+  }
+  if (sh.kind != Shape::kRow64) return;  // no cap from occupancy
+  // every product one block per wave, all resident at once: the preloading
+  // kernel; otherwise the looping kernel for all of them, its workgroups
+  // (one per compute unit) shared in proportion to the wants
+  const int wpg = kThreads / kWave;
+  long long need_pre = 0;
+  for (int i = 0; i < n; ++i) need_pre += (rows[i] + wpg * kRow64R - 1) / (wpg * kRow64R);
+  const int cap_pre = row64_capacity(sh, mode, true);
+  if (cap_pre > 0 && need_pre <= cap_pre) {
+    for (int i = 0; i < n; ++i) want[i] = (rows[i] + wpg * kRow64R - 1) / (wpg * kRow64R);
+    return;
+  }
+  total = 0;
+  for (int i = 0; i < n; ++i) {
+    want[i] = clamp_wg((rows[i] + kLoopWaves * kRow64R - 1) / (kLoopWaves * kRow64R),
+                       Q4_ROW64_MAX_WG);
+    total += want[i];
+  }
+  const int cap = row64_capacity(sh, mode, false);
+  if (cap > 0 && total > cap)
+    for (int i = 0; i < n; ++i) {
+      const long long w = (long long)want[i] * cap / total;
+      want[i] = (int32_t)(w < 1 ? 1 : w);
+    }
 }
 
 int32_t workgroups_for(const Shape &sh, int32_t rows, int mode) {
@@ -852,14 +895,15 @@ int32_t workgroups_for(const Shape &sh, int32_t rows, int mode) {
   switch (sh.kind) {
     case Shape::kRow64: {
       // one block of R rows per wave if that fits on the device at once
-      // (the preloading variant then runs); otherwise Q4_ROW64_LOOP_WG_PER_CU
-      // workgroups per compute unit (or fewer if fewer fit), all resident
-      // at once
+      // (the preloading kernel then runs, workgroups of kThreads);
+      // otherwise the looping kernel, one workgroup of kLoopThreads per
+      // compute unit
       const long long need = (rows + wpg * kRow64R - 1) / (wpg * kRow64R);
       const int cap_pre = row64_capacity(sh, mode, true);
       if (cap_pre > 0 && need <= cap_pre) return clamp_wg(need, cap_pre);
+      const long long need_loop = (rows + kLoopWaves * kRow64R - 1) / (kLoopWaves * kRow64R);
       const int cap = row64_capacity(sh, mode, false);
-      return clamp_wg(need, cap > 0 ? cap : Q4_ROW64_MAX_WG);
+      return clamp_wg(need_loop, cap > 0 ? cap : Q4_ROW64_MAX_WG);
     }
     case Shape::kSeg: {
       const long long per_wg = (long long)wpg * kSegR * (kWave / sh.lpr);
