@@ -259,9 +259,17 @@ __device__ __forceinline__ void row64_single(const Prod &P, const Extra &ex, con
   if constexpr (EPI == kEpiSwiglu) swiglu_flush<FAST>(store_m, batch);
 }
 
-// The blocks of workgroup lw of nwg: blocks lw, lw + nwg, lw + 2 nwg, ...
-// of R rows each, taken by its 16 waves as they become free.  Ticket t
-// names the workgroup's block t; waves take tickets 0..15 first and then
+// Items [begin, end) of part `k` when `rows` items are split into `parts` balanced
+// contiguous ranges.
+__device__ __forceinline__ void balanced_range(int rows, int k, int parts, int &begin, int &end) {
+  begin = (int)(((long long)rows * k) / parts);
+  end = (int)(((long long)rows * (k + 1)) / parts);
+}
+
+// The blocks of workgroup lw of nwg: a contiguous, balanced range of the
+// product's blocks of R rows (so that each 128-byte line of y is written
+// from one XCD's L2), taken by its 16 waves as they become free.  Ticket t
+// names the range's block t; waves take tickets 0..15 first and then
 // one at a time from a counter in LDS, fetched while the current block is
 // summed.  (Dealt statically, one block in four per wave, the first waves a
 // SIMD received finished several microseconds before its last: a SIMD
@@ -282,8 +290,9 @@ __device__ __forceinline__ void row64_loop_rows(const Prod &P, const Extra &ex, 
                                                 RunningMax &best) {
   const uint32_t voff_q = 16u * lane;
   const uint32_t voff_g = 4u * (lane >> 1);
-  const int blocks = (P.rows + R - 1) / R;
-  const int nblk = lw < blocks ? (blocks - lw + nwg - 1) / nwg : 0;  // this workgroup's
+  int b0, b1;  // this workgroup's blocks
+  balanced_range((P.rows + R - 1) / R, lw, nwg, b0, b1);
+  const int nblk = b1 - b0;
   const int negz = R % 4 == 0 ? 0 : neg_zero_reg();  // only the one-row sums use it
   SwigluBatch batch;
   float *m_out = ex.m_out;
@@ -297,7 +306,7 @@ __device__ __forceinline__ void row64_loop_rows(const Prod &P, const Extra &ex, 
   Row64Block<R> a;
   int t = wave;
   for (bool first = true; first || t < nblk; first = false) {
-    const int r = (lw + nwg * t) * R;
+    const int r = (b0 + t) * R;
     // a wave without a block loads from a buffer of zero bytes: nothing
     const int nrows = t < nblk ? min(R, P.rows - r) : 0;
     row64_load<R>(P, nrows > 0 ? r : 0, nrows, voff_q, voff_g, a);
@@ -519,13 +528,6 @@ __device__ __forceinline__ void split_rows(const Prod &P, const float *xv, float
     }
     __syncthreads();
   }
-}
-
-// Rows [begin, end) of part `k` when `rows` are split into `parts` balanced
-// contiguous ranges.
-__device__ __forceinline__ void balanced_range(int rows, int k, int parts, int &begin, int &end) {
-  begin = (int)(((long long)rows * k) / parts);
-  end = (int)(((long long)rows * (k + 1)) / parts);
 }
 
 template <int PP, int R, bool FAST, int PRO>

@@ -229,7 +229,7 @@ def record_traffic(paths) -> int:
             raise SystemExit("no %s rows for %s in %s" % (counter, kernel_part, path))
         return sum(vals) / len(vals), len(vals)
 
-    head = "q4mv_row64_kernel<4, false, 0, 0, false>"
+    head = "q4mv_row64_loop_kernel<4, false, 0, 0>"
     fh, nf = mean_kib(paths[0], head, "FETCH_SIZE")
     wh, nw = mean_kib(paths[1], head, "WRITE_SIZE")
     fc, _ = mean_kib(paths[2], "copyBuffer", "FETCH_SIZE")
@@ -237,7 +237,7 @@ def record_traffic(paths) -> int:
     gib = 1 << 30
     ff, wf = gib / (fc * 1024), gib / (wc * 1024)
     total = round(fh * 1024 * ff + wh * 1024 * wf)
-    rec = {"kernel": "q4mv_row64_kernel<4,false,kProX,kEpiStore,no preload> (fixed order), "
+    rec = {"kernel": "q4mv_row64_loop_kernel<4,false,kProX,kEpiStore> (fixed order), "
                      "248320x2048 head",
            "kernel_source_sha256_16": kernel_source_hash(),
            "fetch_size_kib_per_dispatch": round(fh, 3), "write_size_kib_per_dispatch": round(wh, 3),
@@ -1001,7 +1001,7 @@ def main() -> int:
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-            "kernel": "q4mv_row64_kernel<4,%s,kProX,kEpiStore,no preload>" % (
+            "kernel": "q4mv_row64_loop_kernel<4,%s,kProX,kEpiStore>" % (
                 "false" if args.mode == "fixed" else "true"),
             "algorithmic_bytes_per_launch": qb,
             "avg_launch_ms": round(kern_ms, 5),
@@ -1022,9 +1022,10 @@ def main() -> int:
                 "achieved": round(qb / (other_ms * 1e-3) / 1e9, 1),
                 "frac": round(qb / (other_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             },
-            "fixed_order_note": "the fixed order is bound by VALU issue (25.6M wave instructions "
-                                "per launch; about 53 us with the weights L2-resident): "
-                                "profiles/q4mv_head_248320x2048_valu_counters.md",
+            "bound_note": "both orders bound by HBM: the arithmetic alone (weights "
+                          "L2-resident) about 41 us fixed, the loads alone about 47 us; 59% of "
+                          "the fixed order's VALU instructions issue paired: "
+                          "profiles/q4mv_head_248320x2048_valu_counters.md",
         },
         "head_kernel_variants": variants,
         "product_4096x2048": product,

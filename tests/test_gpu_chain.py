@@ -56,8 +56,9 @@ def test_queue_product_set_two_layers_bit_exact():
 
 def test_queue_stage_of_looping_products_bit_exact():
     """One stage of three 2048-column products large enough that the
-    grouped launch loops (each product's waves take 1-4 blocks, with the
-    issue priority from their own progress), ragged row counts, one wait."""
+    grouped launch loops (the device's 16-wave workgroups shared among the
+    products in proportion, each workgroup's waves taking its blocks by
+    tickets), ragged row counts, one wait."""
     q4 = lib()
     x = synth.normal_f32(31, "lx", (2048,), 0.0, 1.0)
     xs = oracle.group_sums(x)

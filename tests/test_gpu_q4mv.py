@@ -192,11 +192,11 @@ def test_q4mv_head_248320x2048_full():
 @pytest.mark.parametrize("rows", [20483, 61447])
 @pytest.mark.parametrize("with_xsum", [True, False])
 def test_q4mv_looping_launch_ragged(rows, with_xsum):
-    """More rows than one 4-row block per resident wave, so that the waves
-    loop over 1-4 blocks each (the activations read after the first
-    block's loads, the issue priority stepped by progress), with a partial
-    last block; the group sums given, or formed in the kernel.  Fixed order
-    bit-exact; fast order within its bound."""
+    """More rows than one 4-row block per resident wave, so that the
+    looping kernel runs (each workgroup's 16 waves take its blocks by
+    tickets; the activations read after the first block's loads), with a
+    partial last block; the group sums given, or formed in the kernel.
+    Fixed order bit-exact; fast order within its bound."""
     print("q4mv looping %dx2048 xsum %s" % (rows, with_xsum), flush=True)
     m = synth.small_product(seed=21, rows=rows, cols=2048, name="loop%d" % rows)
     xs = oracle.group_sums(m["x"])
