@@ -189,6 +189,29 @@ def test_q4mv_head_248320x2048_full():
     assert_bits_equal(host(y), want, "head")
 
 
+def test_q4mv_looping_launches_on_two_streams_at_once():
+    """Two looping launches (41011 and 20483 rows) issued on two streams so
+    that they can run at the same time, each with its own activations:
+    the looping kernel's tickets live in each workgroup's LDS, so the
+    launches share no state; both fixed-order outputs bit-exact."""
+    q4 = lib()
+    ms = [synth.small_product(seed=61 + i, rows=rows, cols=2048, name="two%d" % i)
+          for i, rows in enumerate((41011, 20483))]
+    wants = [oracle.q4mv(m, m["x"], oracle.group_sums(m["x"]), NTHREADS) for m in ms]
+    Ws = [q4.Q4Matrix.from_host(m) for m in ms]
+    xs = [(dev(m["x"]), dev(oracle.group_sums(m["x"]))) for m in ms]
+    ys = [torch.full((m["rows"],), 7.0, device="cuda") for m in ms]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                q4.q4mv(Ws[i], xs[i][0], xs[i][1], ys[i], stream=streams[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert_bits_equal(host(ys[i]), wants[i], "stream %d rep %d" % (i, rep))
+
+
 @pytest.mark.parametrize("rows", [20483, 61447])
 @pytest.mark.parametrize("with_xsum", [True, False])
 def test_q4mv_looping_launch_ragged(rows, with_xsum):
