@@ -235,36 +235,35 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
     const uint32_t tag = stage_tag(call, l);
 
     // ---- stage Q --------------------------------------------------------------
-    // x = rmsq(h, wa), each wave for itself: h is the layer's input, or the
-    // previous layer's tagged output staged in LDS.  (Forming it once per
-    // workgroup, as stage A does, measured slower in this stage, which
-    // leads to the attention stage.)
+    // x = rmsq(h, wa) over the workgroup, as in stage A (threads 0..255
+    // take 8 columns): h is the layer's input, or the previous layer's
+    // tagged output, polled as words t + 512 k (each wave's load: 64
+    // consecutive words) into SO.x; after a barrier threads 0..255 take
+    // their 8 values
     {
-      float hv[32], wv[32];
-      load_x_values(Y.wa + 32 * lane, true, wv);
+      bool ok = true;
+      float h8[8] = {}, w8[8] = {};
+      if (mine) load8(Y.wa + 8 * t, w8);
       if (l == 0) {
-        load_x_values(A.h + 32 * lane, true, hv);
+        if (mine) load8(A.h + 8 * t, h8);
       } else {
-        // every thread polls words t + 512 k (each wave's load: 64
-        // consecutive words, a few cache lines) into the padded layout
         static_assert(kCols == 4 * kThreads, "4 words of h per thread");
         float h4[4];
-        const bool ok = poll_tagged<4, kThreads>(A.hb + (size_t)copy * kCols + t,
-                                                 stage_tag(call, l - 1) + 5, h4, err,
-                                                 A.spin_ticks);
+        ok = poll_tagged<4, kThreads>(A.hb + (size_t)copy * kCols + t, stage_tag(call, l - 1) + 5,
+                                      h4, err, A.spin_ticks);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int c = t + kThreads * k;
-          SO.x[c + 4 * (c >> 5)] = h4[k];
+        for (int k = 0; k < 4; ++k) SO.x[t + kThreads * k] = h4[k];
+        __syncthreads();
+        if (mine) {
+          const float4 *src = reinterpret_cast<const float4 *>(SO.x + 8 * t);
+          const float4 a0 = src[0], a1 = src[1];
+          h8[0] = a0.x; h8[1] = a0.y; h8[2] = a0.z; h8[3] = a0.w;
+          h8[4] = a1.x; h8[5] = a1.y; h8[6] = a1.z; h8[7] = a1.w;
         }
-        if (!__syncthreads_and(ok)) return;
-        load_x_values(SO.x + kChunkStride * lane, true, hv);
       }
-      const float rho = ops::rmsq_rho_wave2048(hv, A.eps);
+      if (!workgroup_rmsq(SO, h8, w8, A.eps, ok)) return;
       float xv[32];
-#pragma unroll
-      for (int k = 0; k < 32; ++k) xv[k] = ops::rmsq_value(hv[k], rho, wv[k]);
-      const float xsv = pair_group_sum(xv);
+      const float xsv = load_rmsq_x(SO, lane, xv);
 #pragma unroll
       for (int i = 0; i < kQRowsPerWave; ++i) {
         if (qb + i < qe) {  // uniform per wave
