@@ -362,23 +362,22 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
         for (int k = 0; k < 8; ++k)
           T.un[r][8 * lq + k] = ops::rmsq_value(x[k], rho, T.tab[kD * r + 8 * lq + k]);
       }
-      __syncthreads();
+      // the same 32 threads of wave 0 read T.un back: the wave's LDS
+      // accesses are done in order, so no barrier
+      issue_order();
       if (t < 32) {
+        // value d < 64: a c - b s with a = un[d], b = un[d + 64]; value
+        // d >= 64: a s + b c with a = un[d - 64], b = un[d]; as one
+        // expression, own c + (-/+ partner s): the same sums, no branch
         const float *ct = T.tab + 2 * kD + 8 * (lq & 7), *st = ct + kD / 2;
+        const float *own = T.un[r] + 8 * lq, *partner = T.un[r] + 8 * (lq ^ 8);
+        const bool first_half = lq < 8;
         float rv[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const int d = 8 * lq + k;
-          if (lq < 8) {
-            const float a = T.un[r][d], b = T.un[r][d + kD / 2];
-            const float ac = a * ct[k], bs = b * st[k];
-            rv[k] = ac - bs;
-          } else {
-            const float a = T.un[r][d - kD / 2], b = T.un[r][d];
-            const float as = a * st[k], bc = b * ct[k];
-            rv[k] = as + bc;
-          }
-          T.rot[r][d] = rv[k];
+          const float pc = own[k] * ct[k], ps = partner[k] * st[k];
+          rv[k] = pc + (first_half ? -ps : ps);
+          T.rot[r][8 * lq + k] = rv[k];
         }
         if (r == 1 && hd % G == 0 && owns_pos) {  // the new cache rows
           const size_t at = ((size_t)j * A.max_pos + pos) * kD + 8 * lq;
@@ -392,7 +391,18 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
         }
       }
       __syncthreads();
-      // scores
+      // scores (the rotated q and new k read once: a select between the new
+      // k and a cache row, not a branch around an LDS read)
+      float rq[8], rk[8];
+      {
+        const float4 *q4p = reinterpret_cast<const float4 *>(&T.rot[0][8 * lq]);
+        const float4 *k4p = reinterpret_cast<const float4 *>(&T.rot[1][8 * lq]);
+        const float4 a0 = q4p[0], a1 = q4p[1], b0 = k4p[0], b1 = k4p[1];
+        rq[0] = a0.x; rq[1] = a0.y; rq[2] = a0.z; rq[3] = a0.w;
+        rq[4] = a1.x; rq[5] = a1.y; rq[6] = a1.z; rq[7] = a1.w;
+        rk[0] = b0.x; rk[1] = b0.y; rk[2] = b0.z; rk[3] = b0.w;
+        rk[4] = b1.x; rk[5] = b1.y; rk[6] = b1.z; rk[7] = b1.w;
+      }
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
         const int tp = 32 * p + r;
@@ -400,8 +410,7 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
           const bool at_pos = p0 + tp == pos;
           float pr[8];
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
-            pr[k] = T.rot[0][8 * lq + k] * (at_pos ? T.rot[1][8 * lq + k] : kv[p][k]);
+          for (int k = 0; k < 8; ++k) pr[k] = rq[k] * (at_pos ? rk[k] : kv[p][k]);
           const float sc = sum16(ops::tree8(pr)) * kScale;
           if (lq == 0) T.s[tp] = sc;
         }
@@ -443,13 +452,12 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
         if (kp >= 0 && kp < 16) {
           const float4 nv = *reinterpret_cast<const float4 *>(&T.in[3][4 * cq]);
 #pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            if (k == kp) {
-              v0[k] = nv.x;
-              v1[k] = nv.y;
-              v2[k] = nv.z;
-              v3[k] = nv.w;
-            }
+          for (int k = 0; k < 16; ++k) {  // selects, not branches
+            const bool at = k == kp;
+            v0[k] = at ? nv.x : v0[k];
+            v1[k] = at ? nv.y : v1[k];
+            v2[k] = at ? nv.z : v2[k];
+            v3[k] = at ? nv.w : v3[k];
           }
         }
         float ek[16];
