@@ -200,22 +200,21 @@ __global__ __launch_bounds__(kThreads) void atq_kernel(AtqArgs a) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) S.un[r][8 * l + k] = rmsq_value(xv[k], rho, wv[k]);
   }
-  __syncthreads();
+  // the same threads of wave 0 read S.un back: the wave's LDS accesses are
+  // done in order, so a compiler barrier is enough
+  asm volatile("" ::: "memory");
   if (nrow) {
+    // value d < 64: A c - B s with A = un[d], B = un[d + 64]; value d >= 64:
+    // A s + B c with A = un[d - 64], B = un[d]; as one expression, own c +
+    // (-/+ partner s): the same products and sum, no branch
+    const float *own = S.un[r] + 8 * l, *partner = S.un[r] + 8 * (l ^ 8);
+    const bool first_half = l < 8;
     float rv[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int d = 8 * l + k;
-      if (l < 8) {  // d < 64: the first of the pair
-        const float A = S.un[r][d], B = S.un[r][d + kD / 2];
-        const float ac = A * ct[k], bs = B * st[k];
-        rv[k] = ac - bs;
-      } else {
-        const float A = S.un[r][d - kD / 2], B = S.un[r][d];
-        const float as = A * st[k], bc = B * ct[k];
-        rv[k] = as + bc;
-      }
-      S.rot[r][d] = rv[k];
+      const float pc = own[k] * ct[k], ps = partner[k] * st[k];
+      rv[k] = pc + (first_half ? -ps : ps);
+      S.rot[r][8 * l + k] = rv[k];
     }
     if (r == 1 && writes_rows) {  // the new cache rows
       float4 *kd = reinterpret_cast<float4 *>(a.kc + ((size_t)j * a.max_pos + pos) * kD + 8 * l);
@@ -229,17 +228,21 @@ __global__ __launch_bounds__(kThreads) void atq_kernel(AtqArgs a) {
   __syncthreads();
 
   // ---- scores ---------------------------------------------------------------
-  float qv[8];
+  // (the rotated q and new k read once; the new k is chosen by a select,
+  // not a branch around an LDS read)
+  float qv[8], nk[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) qv[k] = S.rot[0][8 * l + k];
+  for (int k = 0; k < 8; ++k) {
+    qv[k] = S.rot[0][8 * l + k];
+    nk[k] = S.rot[1][8 * l + k];
+  }
 #pragma unroll
   for (int pass = 0; pass < kSpan / 64; ++pass) {
     const int tp = base + 64 * pass + r;
     if (tp < n) {  // uniform over the 16 lanes of the position
-      if (tp == pos) {
+      const bool at_pos = tp == pos;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) kv[pass][k] = S.rot[1][8 * l + k];
-      }
+      for (int k = 0; k < 8; ++k) kv[pass][k] = at_pos ? nk[k] : kv[pass][k];
       float pr[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) pr[k] = qv[k] * kv[pass][k];
