@@ -64,9 +64,9 @@ struct Row {
 
 __device__ __forceinline__ void load_qrows(const BlockLayer &Y, int r0, int nrows, int lane,
                                            QBlock &a) {
-  const auto qr = buffer(Y.qq + (size_t)r0 * 256, nrows * 1024);
-  const auto sr = buffer(Y.qs + (size_t)r0 * 32, nrows * 128);
-  const auto br = buffer(Y.qb + (size_t)r0 * 32, nrows * 128);
+  const auto qr = buffer_uniform(Y.qq + (size_t)r0 * 256, nrows * 1024);
+  const auto sr = buffer_uniform(Y.qs + (size_t)r0 * 32, nrows * 128);
+  const auto br = buffer_uniform(Y.qb + (size_t)r0 * 32, nrows * 128);
 #pragma unroll
   for (int j = 0; j < kQRowsPerWave; ++j) {
     a.cw[j] = load_codes(qr, 16u * lane, j * 1024);
@@ -76,9 +76,9 @@ __device__ __forceinline__ void load_qrows(const BlockLayer &Y, int r0, int nrow
 }
 
 __device__ __forceinline__ void load_orow(const BlockLayer &Y, int r, int lane, Row &d) {
-  const auto qr = buffer(Y.oq + (size_t)r * 256, 1024);
-  const auto sr = buffer(Y.os + (size_t)r * 32, 128);
-  const auto br = buffer(Y.ob + (size_t)r * 32, 128);
+  const auto qr = buffer_uniform(Y.oq + (size_t)r * 256, 1024);
+  const auto sr = buffer_uniform(Y.os + (size_t)r * 32, 128);
+  const auto br = buffer_uniform(Y.ob + (size_t)r * 32, 128);
   d.cw = load_codes(qr, 16u * lane, 0);
   d.sv = load_f32(sr, 4u * (lane >> 1), 0);
   d.bv = load_f32(br, 4u * (lane >> 1), 0);
@@ -310,8 +310,8 @@ __global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockArgs 
       // buffer loads: zeros from n on; row pos is stale here and not used)
       const size_t hb = ((size_t)j * A.max_pos + p0) * kD;
       const uint32_t span_bytes = (uint32_t)max(pn, 0) * kD * 4u;
-      const auto kr = buffer(Y.kc + hb, span_bytes);
-      const auto vr = buffer(Y.vc + hb, span_bytes);
+      const auto kr = buffer_uniform(Y.kc + hb, span_bytes);
+      const auto vr = buffer_uniform(Y.vc + hb, span_bytes);
       float kv[8][8];
 #pragma unroll
       for (int p = 0; p < 8; ++p) {

@@ -102,6 +102,19 @@ __device__ __forceinline__ float load_rmsq_x(const Lds<NP> &L, int lane, float *
   return L.xs[lane >> 1];
 }
 
+// A buffer descriptor from a base and size that are the same in every
+// lane of the wave (a wave's rows, a task's cache span), taken from the
+// first lane: the compiler then keeps the descriptor in scalar registers.
+// Built from values it cannot prove uniform (pointers read from the layer
+// table), a descriptor would cost a waterfall loop around every load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_uniform(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return buffer(reinterpret_cast<const void *>(((uint64_t)hi << 32) | lo),
+                __builtin_amdgcn_readfirstlane(bytes));
+}
+
 struct GuBlock {
   u32x4 cw[kGuR];
   float sv[kGuR], bv[kGuR];
@@ -118,9 +131,9 @@ struct DownRow {
 __device__ __forceinline__ void load_gu(const DecodeLayer &L, int p0, int np, int lane,
                                         GuBlock &a) {
   const size_t r0 = 2 * (size_t)p0;
-  const auto qr = buffer(L.gq + r0 * 256, 2 * np * 1024);
-  const auto sr = buffer(L.gs + r0 * 32, 2 * np * 128);
-  const auto br = buffer(L.gb + r0 * 32, 2 * np * 128);
+  const auto qr = buffer_uniform(L.gq + r0 * 256, 2 * np * 1024);
+  const auto sr = buffer_uniform(L.gs + r0 * 32, 2 * np * 128);
+  const auto br = buffer_uniform(L.gb + r0 * 32, 2 * np * 128);
 #pragma unroll
   for (int j = 0; j < kGuR; ++j) {
     a.cw[j] = load_codes(qr, 16u * lane, j * 1024);
@@ -132,9 +145,9 @@ __device__ __forceinline__ void load_gu(const DecodeLayer &L, int p0, int np, in
 // Row r of the down matrix: pass p covers columns [2048 p, 2048 p + 2048).
 template <int NP>
 __device__ __forceinline__ void load_down(const DecodeLayer &L, int r, int lane, DownRow<NP> &d) {
-  const auto qr = buffer(L.dq + (size_t)r * (NP * 256), NP * 1024);
-  const auto sr = buffer(L.ds + (size_t)r * (NP * 32), NP * 128);
-  const auto br = buffer(L.db + (size_t)r * (NP * 32), NP * 128);
+  const auto qr = buffer_uniform(L.dq + (size_t)r * (NP * 256), NP * 1024);
+  const auto sr = buffer_uniform(L.ds + (size_t)r * (NP * 32), NP * 128);
+  const auto br = buffer_uniform(L.db + (size_t)r * (NP * 32), NP * 128);
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     d.cw[p] = load_codes(qr, 16u * lane, p * 1024);
